@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the TurboQuant KV-cache path on one MI355X.
+
+One step = append-encode of the newest tokens + one decode-attention step
+over the whole packed context (the two calls a generation step makes). The
+default workload is the long-context decode: batch 1, 32 query / 8 KV heads,
+d = 128, 524288-token context, 3-bit keys / 4-bit values with fp16 norms,
+4096 tokens appended per step, bf16 N(0,1) inputs.
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value     KV-tokens/s of the whole step (B * N / step time)
+  roofline  the decode call's algorithmic bytes / its measured duration
+            against the 8 TB/s HBM peak
+  cpu_baseline  the CPU oracle timed on a bounded sample, scaled
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "packed decode-attention KV-tokens/s and achieved HBM GB/s as % of peak"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "decode_attention_seeded_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(wid):
+    """HBM bytes per decode launch from the committed counter summary, if it
+    was taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", f"decode_hbm_traffic_workload{wid}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def to_dev_bf16(torch, raw):
+    import numpy as np
+    return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def cpu_baseline(w, sample_tokens):
+    """The oracle (NumPy fp64, as it stands) on a bounded sample of the same
+    step: the append-encode of the newest tokens for one KV head and the
+    decode of that KV head's query heads over `sample_tokens` tokens; both
+    scaled linearly to the whole step."""
+    import numpy as np
+    import oracle as o
+    import seeded_inputs as si
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    n = min(sample_tokens, w.N)
+    A = min(w.append or 4096, n)
+    _, fk = si.kv_rows(w, si.T_K, 0, 0, 0, n)
+    _, fv = si.kv_rows(w, si.T_V, 0, 0, 0, n)
+    fk = fk.astype(np.float64)[None, None]
+    fv = fv.astype(np.float64)[None, None]
+    kw = dict(seed=w.seed, bits_k=w.bits_k, bits_v=w.bits_v, norm_dtype=w.norm_dtype,
+              qjl=w.qjl, qjl_seed=w.qjl_seed)
+    cache = o.encode_kv(fk, fv, **kw)                      # setup, untimed
+    t0 = time.perf_counter()
+    o.encode_kv(fk[:, :, n - A:], fv[:, :, n - A:], **kw)  # the step's append
+    t_enc = time.perf_counter() - t0
+    _, qf = si.queries(w)
+    q = qf[:1, :w.G].astype(np.float64)
+    t0 = time.perf_counter()
+    o.attend(q, cache, n, d=w.d, seed=w.seed, bits_k=w.bits_k, bits_v=w.bits_v, Hkv=1,
+             qjl=w.qjl, qjl_seed=w.qjl_seed)
+    t_dec = time.perf_counter() - t0
+    units = w.B * w.Hkv
+    step_s = t_enc * units * (w.append or A) / A + t_dec * units * w.N / n
+    return {
+        "value": w.B * w.N / step_s,
+        "unit": "KV-tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"1 of {units} KV heads: {A}-token append encode ({t_enc:.2f} s) and "
+                   f"decode of {w.G} query heads over {n} of {w.N} tokens ({t_dec:.2f} s), "
+                   f"scaled linearly to the full step ({step_s:.1f} s)"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import decode_attention_seeded_amd as tq
+    import seeded_inputs as si
+
+    w = si.WORKLOADS[args.workload]
+    A = w.append if w.append else 0
+    log(f"workload {w.wid}: {w.name}")
+    torch.cuda.set_device(0)
+
+    # ---------------- inputs (seeded, host-generated, uploaded once)
+    t0 = time.time()
+    k_host = si.kv_full(w, si.T_K)
+    v_host = si.kv_full(w, si.T_V)
+    q_raw, _ = si.queries(w)
+    log(f"generated inputs in {time.time() - t0:.1f} s")
+    if w.in_dtype == "bf16":
+        K, V, q = to_dev_bf16(torch, k_host), to_dev_bf16(torch, v_host), to_dev_bf16(torch, q_raw)
+    else:
+        K = torch.from_numpy(k_host).cuda()
+        V = torch.from_numpy(v_host).cuda()
+        q = torch.from_numpy(q_raw).cuda()
+    del k_host, v_host
+
+    cfg = tq.Config(d=w.d, bits_k=w.bits_k, bits_v=w.bits_v, norm_dtype=w.norm_dtype,
+                    qjl=w.qjl, seed=w.seed, qjl_seed=w.qjl_seed)
+    cache = tq.PackedCache(cfg, w.B, w.Hkv, w.N)
+    n_bulk = w.N - A
+    k_bulk, v_bulk = K[:, :, :n_bulk].contiguous(), V[:, :, :n_bulk].contiguous()
+    k_app, v_app = K[:, :, n_bulk:].contiguous(), V[:, :, n_bulk:].contiguous()
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    splits = tq.tq_num_splits(cfg, w.B, w.Hq, w.Hkv, w.N)
+    ws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N))
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    e0.record()
+    tq.tq_encode_kv(cfg, k_bulk, v_bulk, 0, cache)
+    e1.record()
+    torch.cuda.synchronize()
+    bulk_ms = e0.elapsed_time(e1)
+    del k_bulk, v_bulk
+    log(f"bulk encode of {n_bulk} tokens x {w.B * w.Hkv} heads: {bulk_ms:.3f} ms")
+
+    def step(dec_events=None):
+        if A:
+            tq.tq_encode_kv(cfg, k_app, v_app, n_bulk, cache)
+        if dec_events:
+            dec_events[0].record()
+        tq.tq_attend_decode(cfg, q, cache, w.N, out, ws)
+        if dec_events:
+            dec_events[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
+
+    dec_ev = [(ev(), ev()) for _ in range(args.steps)]
+    s0, s1 = ev(), ev()
+    torch.cuda.synchronize()
+    s0.record()
+    for i in range(args.steps):
+        step(dec_ev[i])
+    s1.record()
+    torch.cuda.synchronize()
+    total_ms = s0.elapsed_time(s1)
+    ms_per_step = total_ms / args.steps
+    dec_us = [a.elapsed_time(b) * 1e3 for a, b in dec_ev]
+    dec_avg_us = float(np.mean(dec_us))
+    log(f"step {ms_per_step * 1e3:.1f} us; decode call avg {dec_avg_us:.1f} us "
+        f"(p10 {np.percentile(dec_us, 10):.1f}, p90 {np.percentile(dec_us, 90):.1f})")
+
+    # append-encode alone
+    enc_us = None
+    if A:
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(20):
+            tq.tq_encode_kv(cfg, k_app, v_app, n_bulk, cache)
+        b.record()
+        torch.cuda.synchronize()
+        enc_us = a.elapsed_time(b) * 1e3 / 20
+
+    # algorithmic bytes of one decode call: every packed plane over N tokens,
+    # plus q in and out
+    cache_bytes, _ = tq.tq_cache_bytes(cfg, w.B, w.Hkv, w.N)
+    qbytes = q.numel() * q.element_size()
+    alg_bytes = cache_bytes + qbytes + out.numel() * 4
+    achieved = alg_bytes / (dec_avg_us * 1e-6) / 1e9
+    traffic = traffic_from_profile(w.wid)
+
+    # dense bf16 decode on the same GPU (same split-K skeleton, bf16 rows)
+    dense = None
+    if not args.no_dense and w.in_dtype == "bf16":
+        dws = tq.workspace(tq.tq_dense_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.N))
+        dout = torch.empty_like(out)
+        for _ in range(3):
+            tq.tq_dense_decode_bf16(q, K, V, dout, dws)
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(20):
+            tq.tq_dense_decode_bf16(q, K, V, dout, dws)
+        b.record()
+        torch.cuda.synchronize()
+        dus = a.elapsed_time(b) * 1e3 / 20
+        dbytes = 2 * K.numel() * 2 + qbytes + out.numel() * 4
+        dense = {"decode_us": round(dus, 2), "achieved_gbps": round(dbytes / dus / 1e3, 1),
+                 "packed_speedup": round(dus / dec_avg_us, 3)}
+        log(f"dense bf16 decode {dus:.1f} us ({dense['achieved_gbps']} GB/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(w, args.cpu_sample_tokens)
+        log(f"oracle: {cpu['value']:.3e} KV-tokens/s ({cpu['sample']})")
+
+    cfg_desc = {
+        "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
+        "context": w.N, "bits_k": w.bits_k, "bits_v": w.bits_v, "norms": w.norm_dtype,
+        "qjl": w.qjl, "append_tokens_per_step": A, "inputs": f"{w.in_dtype} seeded synthetic",
+        "splits": splits,
+    }
+    rec = {
+        "metric": METRIC,
+        "value": round(w.B * w.N / (ms_per_step * 1e-3), 1),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": cfg_desc,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "decode_call_us": round(dec_avg_us, 2),
+        "decode_kv_tokens_per_s": round(w.B * w.N / (dec_avg_us * 1e-6), 1),
+        "append_encode_us": round(enc_us, 2) if enc_us else None,
+        "bulk_encode_ms": round(bulk_ms, 3),
+        "algorithmic_bytes_per_decode": alg_bytes,
+        "dense_bf16": dense,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

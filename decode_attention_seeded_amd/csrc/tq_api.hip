@@ -1,0 +1,312 @@
+// Public entry points of libtq.so: host-side validation, launch planning and
+// kernel launches. Every argument is checked before the first HIP call.
+
+#include <cmath>
+
+#include "tq_internal.h"
+#include "tq_kernels.h"
+
+namespace tq {
+
+using DecodeLauncher = int (*)(int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d128_k2(int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d128_k3(int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d128_k4(int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d128_k16(int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d256_k2(int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d256_k3(int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d256_k4(int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d256_k16(int, int, int, const DecodeArgs&, dim3, hipStream_t);
+
+namespace {
+
+DecodeLauncher decode_launcher(int d, int bk) {
+  if (d == 128) {
+    switch (bk) {
+      case 2: return launch_decode_d128_k2;
+      case 3: return launch_decode_d128_k3;
+      case 4: return launch_decode_d128_k4;
+      case 16: return launch_decode_d128_k16;
+    }
+  } else if (d == 256) {
+    switch (bk) {
+      case 2: return launch_decode_d256_k2;
+      case 3: return launch_decode_d256_k3;
+      case 4: return launch_decode_d256_k4;
+      case 16: return launch_decode_d256_k16;
+    }
+  }
+  return nullptr;
+}
+
+int device_ready() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n < 1) return TQ_ERR_NO_DEVICE;
+  return TQ_OK;
+}
+
+int last_launch() { return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP; }
+
+unsigned row_grid(int64_t rows) {
+  const int64_t g = (rows + 15) / 16;
+  return unsigned(g < 16384 ? g : 16384);
+}
+
+template <int D, int BITS, bool QJL>
+int launch_encode(const EncodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_encode<D, BITS, QJL>), dim3(row_grid(a.rows)), dim3(256), 0, st, a);
+  return last_launch();
+}
+
+template <int D>
+int launch_encode_bits(int bits, bool qjl, const EncodeArgs& a, hipStream_t st) {
+  switch (bits) {
+    case 2: return qjl ? launch_encode<D, 2, true>(a, st) : launch_encode<D, 2, false>(a, st);
+    case 3: return qjl ? launch_encode<D, 3, true>(a, st) : launch_encode<D, 3, false>(a, st);
+    case 4: return qjl ? launch_encode<D, 4, true>(a, st) : launch_encode<D, 4, false>(a, st);
+  }
+  return TQ_ERR_UNSUPPORTED;
+}
+
+void fill_codebook_f64(int bits, double* thr, double* cen) {
+  const Codebook& cb = codebook(bits);
+  const int L = 1 << bits;
+  for (int k = 0; k < 15; ++k) thr[k] = k < L - 1 ? cb.t[k] : INFINITY;
+  for (int k = 0; k < 16; ++k) cen[k] = k < L ? cb.c[k] : 0.0;
+}
+
+void fill_codebook_f32(int bits, float* cen) {
+  const Codebook& cb = codebook(bits);
+  const int L = 1 << bits;
+  for (int k = 0; k < 16; ++k) cen[k] = k < L ? float(cb.c[k]) : 0.f;
+}
+
+int launch_qprep(int d, const QPrepArgs& a, hipStream_t st) {
+  const unsigned grid = unsigned((a.heads + 15) / 16);
+  if (d == 128)
+    hipLaunchKernelGGL(k_qprep<128>, dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_qprep<256>, dim3(grid), dim3(256), 0, st, a);
+  return last_launch();
+}
+
+int launch_merge(int d, const MergeArgs& a, hipStream_t st) {
+  if (d == 128)
+    hipLaunchKernelGGL(k_merge<128>, dim3(unsigned(a.heads)), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_merge<256>, dim3(unsigned(a.heads)), dim3(256), 0, st, a);
+  return last_launch();
+}
+
+// Shared tail of the packed and dense decode paths: q preparation, split-K
+// kernel, merge.
+int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs da,
+               QPrepArgs qa, int B, int Hq, int Hkv, void* ws, float* out, int rotate,
+               uint64_t seed, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  qa.qp = reinterpret_cast<float*>(w + p.off_qp);
+  qa.qq = qjl ? reinterpret_cast<float*>(w + p.off_qq) : nullptr;
+  da.qp = qa.qp;
+  da.qq = qa.qq;
+  da.ml = reinterpret_cast<float*>(w + p.off_ml);
+  da.acc = reinterpret_cast<float*>(w + p.off_acc);
+  da.tps = p.tps;
+  da.Hkv = Hkv;
+  da.Hq = Hq;
+  da.G = p.G;
+  da.chunks = p.chunks;
+  da.S = p.splits;
+  int st1 = launch_qprep(d, qa, st);
+  if (st1 != TQ_OK) return st1;
+  DecodeLauncher fn = decode_launcher(d, bk);
+  if (!fn) return TQ_ERR_UNSUPPORTED;
+  dim3 grid(unsigned(p.splits), unsigned(int64_t(B) * Hkv * p.chunks));
+  st1 = fn(bv, p.gk, qjl, da, grid, st);
+  if (st1 != TQ_OK) return st1;
+  MergeArgs ma;
+  ma.ml = da.ml;
+  ma.acc = da.acc;
+  ma.out = out;
+  ma.heads = int64_t(B) * Hq;
+  ma.S = p.splits;
+  ma.rotate = rotate;
+  ma.seed = seed;
+  return launch_merge(d, ma, st);
+}
+
+}  // namespace
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+int tq_rht(const void* x, int x_dtype, float* y, int64_t rows, int d, uint64_t seed,
+           int inverse, hipStream_t stream) {
+  if (rows < 0) return TQ_ERR_ARG;
+  if (!valid_d(d) || !valid_in_dtype(x_dtype)) return TQ_ERR_UNSUPPORTED;
+  if (inverse != 0 && inverse != 1) return TQ_ERR_ARG;
+  if (rows == 0) return TQ_OK;
+  if (!x || !y) return TQ_ERR_ARG;
+  if (!aligned16(x) || !aligned16(y)) return TQ_ERR_ALIGN;
+  int st = device_ready();
+  if (st != TQ_OK) return st;
+  RhtArgs a{x, y, rows, x_dtype, inverse, seed};
+  if (d == 128)
+    hipLaunchKernelGGL(k_rht<128>, dim3(row_grid(rows)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_rht<256>, dim3(row_grid(rows)), dim3(256), 0, stream, a);
+  return last_launch();
+}
+
+int tq_encode_kv(const tq_config* cfg, const void* k, const void* v, int in_dtype,
+                 int64_t offset, int64_t n_new, const tq_cache* cache, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  st = check_cache(cfg, cache);
+  if (st != TQ_OK) return st;
+  if (!valid_in_dtype(in_dtype)) return TQ_ERR_UNSUPPORTED;
+  if (offset < 0 || n_new < 0) return TQ_ERR_ARG;
+  if (offset + n_new > cache->capacity) return TQ_ERR_CAPACITY;
+  const int64_t rows = int64_t(cache->B) * cache->Hkv * n_new;
+  if (rows == 0) return TQ_OK;
+  if (!k || !v) return TQ_ERR_ARG;
+  if (!aligned16(k) || !aligned16(v)) return TQ_ERR_ALIGN;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+
+  EncodeArgs a{};
+  a.rows = rows;
+  a.n_new = n_new;
+  a.offset = offset;
+  a.capacity = cache->capacity;
+  a.in_dtype = in_dtype;
+  a.norm_f16 = cfg->norm_dtype == TQ_F16;
+  a.seed = cfg->seed;
+  a.qjl_seed = cfg->qjl_seed;
+
+  EncodeArgs ak = a;
+  ak.x = k;
+  ak.codes = static_cast<uint8_t*>(cache->kc);
+  ak.norms = cache->kn;
+  ak.qbits = static_cast<uint8_t*>(cache->kq);
+  ak.rnorm = static_cast<uint16_t*>(cache->kr);
+  fill_codebook_f64(cfg->bits_k, ak.thr, ak.cen);
+  const bool q = cfg->qjl != 0;
+  st = cfg->d == 128 ? launch_encode_bits<128>(cfg->bits_k, q, ak, stream)
+                     : launch_encode_bits<256>(cfg->bits_k, q, ak, stream);
+  if (st != TQ_OK) return st;
+
+  EncodeArgs av = a;
+  av.x = v;
+  av.codes = static_cast<uint8_t*>(cache->vc);
+  av.norms = cache->vn;
+  fill_codebook_f64(cfg->bits_v, av.thr, av.cen);
+  return cfg->d == 128 ? launch_encode_bits<128>(cfg->bits_v, false, av, stream)
+                       : launch_encode_bits<256>(cfg->bits_v, false, av, stream);
+}
+
+int tq_qjl_sketch(const float* r, int64_t rows, int d, uint64_t qjl_seed, uint32_t* bits,
+                  uint16_t* rnorm_f16, hipStream_t stream) {
+  if (rows < 0) return TQ_ERR_ARG;
+  if (!valid_d(d)) return TQ_ERR_UNSUPPORTED;
+  if (rows == 0) return TQ_OK;
+  if (!r || !bits || !rnorm_f16) return TQ_ERR_ARG;
+  if (!aligned16(r) || !aligned16(bits) || !aligned16(rnorm_f16)) return TQ_ERR_ALIGN;
+  int st = device_ready();
+  if (st != TQ_OK) return st;
+  QjlArgs a{r, bits, rnorm_f16, rows, qjl_seed};
+  if (d == 128)
+    hipLaunchKernelGGL(k_qjl<128>, dim3(row_grid(rows)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_qjl<256>, dim3(row_grid(rows)), dim3(256), 0, stream, a);
+  return last_launch();
+}
+
+int tq_attend_decode(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
+                     const tq_cache* cache, int64_t n_ctx, float scale, int splits, float* out,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  st = check_cache(cfg, cache);
+  if (st != TQ_OK) return st;
+  if (!valid_in_dtype(q_dtype)) return TQ_ERR_UNSUPPORTED;
+  if (B != cache->B || Hq < 1 || Hq % cache->Hkv != 0 || splits < 0) return TQ_ERR_ARG;
+  if (!std::isfinite(scale)) return TQ_ERR_ARG;
+  if (n_ctx < 1) return TQ_ERR_ARG;
+  if (n_ctx > cache->capacity) return TQ_ERR_CAPACITY;
+  if (B == 0) return TQ_OK;
+  if (!q || !out || !ws) return TQ_ERR_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return TQ_ERR_ALIGN;
+  DecodePlan p;
+  st = plan_decode(cfg->d, cfg->qjl, B, Hq, cache->Hkv, n_ctx, splits, &p);
+  if (st != TQ_OK) return st;
+  if (ws_bytes < p.total) return TQ_ERR_WORKSPACE;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+
+  const float tau = scale == 0.f ? 1.0f / std::sqrt(float(cfg->d)) : scale;
+  QPrepArgs qa{};
+  qa.q = q;
+  qa.heads = int64_t(B) * Hq;
+  qa.q_dtype = q_dtype;
+  qa.rotate = 1;
+  qa.qjl = cfg->qjl;
+  qa.mult = tau * dev::kLog2e;
+  qa.seed = cfg->seed;
+  qa.qjl_seed = cfg->qjl_seed;
+
+  DecodeArgs da{};
+  da.kc = static_cast<const uint8_t*>(cache->kc);
+  da.vc = static_cast<const uint8_t*>(cache->vc);
+  da.kn = cache->kn;
+  da.vn = cache->vn;
+  da.kq = static_cast<const uint32_t*>(cache->kq);
+  da.kr = static_cast<const uint16_t*>(cache->kr);
+  da.capacity = cache->capacity;
+  da.n_ctx = n_ctx;
+  da.norm_f16 = cfg->norm_dtype == TQ_F16;
+  da.inv_sqrt_d = float(1.0 / std::sqrt(double(cfg->d)));
+  da.qjl_c = float(std::sqrt(M_PI / (2.0 * cfg->d)));
+  fill_codebook_f32(cfg->bits_k, da.cbk);
+  fill_codebook_f32(cfg->bits_v, da.cbv);
+  return run_decode(cfg->d, cfg->bits_k, cfg->bits_v, cfg->qjl, p, da, qa, B, Hq, cache->Hkv,
+                    ws, out, 1, cfg->seed, stream);
+}
+
+int tq_dense_decode_bf16(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                         int d, int64_t n_ctx, float scale, int splits, float* out, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  if (!valid_d(d)) return TQ_ERR_UNSUPPORTED;
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || splits < 0 || n_ctx < 1)
+    return TQ_ERR_ARG;
+  if (!std::isfinite(scale)) return TQ_ERR_ARG;
+  if (B == 0) return TQ_OK;
+  if (!q || !k || !v || !out || !ws) return TQ_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(ws))
+    return TQ_ERR_ALIGN;
+  DecodePlan p;
+  int st = plan_dense(d, B, Hq, Hkv, n_ctx, splits, &p);
+  if (st != TQ_OK) return st;
+  if (ws_bytes < p.total) return TQ_ERR_WORKSPACE;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+
+  const float tau = scale == 0.f ? 1.0f / std::sqrt(float(d)) : scale;
+  QPrepArgs qa{};
+  qa.q = q;
+  qa.heads = int64_t(B) * Hq;
+  qa.q_dtype = TQ_BF16;
+  qa.rotate = 0;
+  qa.qjl = 0;
+  qa.mult = tau * dev::kLog2e;
+
+  DecodeArgs da{};
+  da.kc = static_cast<const uint8_t*>(k);
+  da.vc = static_cast<const uint8_t*>(v);
+  da.capacity = n_ctx;
+  da.n_ctx = n_ctx;
+  return run_decode(d, 16, 16, 0, p, da, qa, B, Hq, Hkv, ws, out, 0, 0, stream);
+}
+
+}  // extern "C"

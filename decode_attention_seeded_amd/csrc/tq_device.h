@@ -1,0 +1,245 @@
+// Device code of libtq.so for gfx950 (CDNA4, wave64): helpers and kernel
+// templates. Included by the kernel translation units only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace tq {
+namespace dev {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Pointer into the constant address space: wave-uniform loads through it
+// become scalar (SMEM) loads into SGPRs. Only for data the kernel never
+// writes.
+typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+__device__ __forceinline__ const_f32_ptr as_const(const float* p) {
+  return (const_f32_ptr)(p);
+}
+
+// ---------------------------------------------------------------------------
+// Element conversions (inputs are fp32, bf16 or fp16; bf16/fp16 arrive as
+// raw 16-bit patterns).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return float(__builtin_bit_cast(_Float16, uint16_t(bits16)));
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, _Float16(x));
+}
+
+// Nearest-even rounding of a double to IEEE binary16, from the bit fields
+// (one rounding step, so no double-rounding through fp32).
+__device__ __forceinline__ uint16_t f64_to_f16_bits(double x) {
+  const uint64_t b = uint64_t(__double_as_longlong(x));
+  const uint16_t sign = uint16_t((b >> 48) & 0x8000u);
+  const int e = int((b >> 52) & 0x7FF);
+  const uint64_t m = b & ((uint64_t(1) << 52) - 1);
+  if (e == 0x7FF) return sign | 0x7C00u | (m ? 0x200u : 0u);
+  if (e == 0) return sign;
+  const int E = e - 1023;
+  if (E > 15) return sign | 0x7C00u;
+  const uint64_t sig = m | (uint64_t(1) << 52);
+  const int shift = (E >= -14) ? 42 : 28 - E;
+  if (shift >= 54) return sign;
+  uint64_t hs = sig >> shift;
+  const uint64_t rem = sig & ((uint64_t(1) << shift) - 1);
+  const uint64_t half = uint64_t(1) << (shift - 1);
+  if (rem > half || (rem == half && (hs & 1))) ++hs;
+  if (E >= -14) {
+    int he = E + 15;
+    if (hs == 2048) { hs = 1024; ++he; }
+    if (he >= 31) return sign | 0x7C00u;
+    return uint16_t(sign | (he << 10) | (hs & 0x3FF));
+  }
+  return uint16_t(sign | hs);
+}
+
+__device__ __forceinline__ double f16_bits_to_f64(uint16_t h) {
+  return double(__builtin_bit_cast(_Float16, h));
+}
+
+// ---------------------------------------------------------------------------
+// SplitMix64 as a counter-based generator: output i of the stream started at
+// state `seed` (Steele, Lea, Flood, OOPSLA 2014). Rotation sign i is -1 when
+// the top bit of output i is set.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t i) {
+  uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Bit i of the result is 1 when sign(first + i) is negative, i < n <= 32.
+__device__ __forceinline__ uint32_t sign_mask(uint64_t seed, int first, int n) {
+  uint32_t m = 0;
+  for (int i = 0; i < n; ++i)
+    m |= uint32_t(splitmix64_at(seed, uint64_t(first + i)) >> 63) << i;
+  return m;
+}
+
+// ---------------------------------------------------------------------------
+// Walsh-Hadamard transform of one row held by a group of 16 consecutive
+// lanes, E consecutive elements per lane (row length 16*E). Element index
+// l16*E + i; butterflies on index bit 0 first. Unnormalized (H_d x).
+// ---------------------------------------------------------------------------
+
+template <int E, typename T>
+__device__ __forceinline__ void fwht16(T (&v)[E], int l16) {
+#pragma unroll
+  for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if (!(i & h)) {
+        const T a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const T o = __shfl_xor(v[i], m, 16);
+      v[i] = (l16 & m) ? (o - v[i]) : (v[i] + o);
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ T group16_sum(T x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 16);
+  return x;
+}
+
+// Loads E consecutive elements of dtype `dt` (0 f32, 1 bf16, 2 f16) starting
+// at element `idx` of `p` into floats. 16-byte aligned for E*size >= 16.
+template <int E>
+__device__ __forceinline__ void load_row_part(const void* p, int dt, int64_t idx,
+                                              float (&f)[E]) {
+  if (dt == 0) {
+    const float4* s = reinterpret_cast<const float4*>(static_cast<const float*>(p) + idx);
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k) {
+      const float4 q = s[k];
+      f[4 * k + 0] = q.x; f[4 * k + 1] = q.y; f[4 * k + 2] = q.z; f[4 * k + 3] = q.w;
+    }
+  } else {
+    const uint4* s = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + idx);
+#pragma unroll
+    for (int k = 0; k < E / 8; ++k) {
+      const uint4 q = s[k];
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = w[j] & 0xFFFFu, hi = w[j] >> 16;
+        f[8 * k + 2 * j + 0] = dt == 1 ? bf16_to_f32(lo) : f16_to_f32(lo);
+        f[8 * k + 2 * j + 1] = dt == 1 ? bf16_to_f32(hi) : f16_to_f32(hi);
+      }
+    }
+  }
+}
+
+// Field i (width BITS) of a little-endian bitstream held in dwords w[].
+template <int BITS, int NW>
+__device__ __forceinline__ uint32_t field(const uint32_t (&w)[NW], int i) {
+  const int bit = i * BITS;
+  const int wi = bit >> 5, sh = bit & 31;
+  uint32_t x = w[wi] >> sh;
+  if (sh + BITS > 32) x |= w[wi + 1] << (32 - sh);
+  return BITS == 32 ? x : (x & ((1u << BITS) - 1u));
+}
+
+// Stores `nbytes` low bytes of v at byte address p (alignment as stated).
+__device__ __forceinline__ void store_bytes(uint8_t* p, uint64_t v, int nbytes) {
+  switch (nbytes) {
+    case 1: *p = uint8_t(v); break;
+    case 2: *reinterpret_cast<uint16_t*>(p) = uint16_t(v); break;
+    case 3: p[0] = uint8_t(v); p[1] = uint8_t(v >> 8); p[2] = uint8_t(v >> 16); break;
+    case 4: *reinterpret_cast<uint32_t*>(p) = uint32_t(v); break;
+    case 6: {
+      uint16_t* q = reinterpret_cast<uint16_t*>(p);
+      q[0] = uint16_t(v); q[1] = uint16_t(v >> 16); q[2] = uint16_t(v >> 32);
+      break;
+    }
+    case 8: *reinterpret_cast<uint64_t*>(p) = v; break;
+    default: break;
+  }
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Sums NV per-lane values over the 64 lanes of a wave, leaving the sums
+// spread over the lanes ("transpose-reduce"). At lane-offset O the lane keeps
+// the half of its CUR live values selected by (lane & O) and adds the
+// partner's copy of that half; once one value is left, plain butterflies
+// finish. reduce_index() gives the original index of each kept value.
+template <int NV, int CUR, int O>
+__device__ __forceinline__ void transpose_reduce_step(float (&v)[NV], int lane) {
+  if constexpr (O >= 1) {
+    if constexpr (CUR > 1) {
+      constexpr int H = CUR / 2;
+      const bool up = (lane & O) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float send = up ? v[i] : v[i + H];
+        const float keep = up ? v[i + H] : v[i];
+        v[i] = keep + __shfl_xor(send, O);
+      }
+      transpose_reduce_step<NV, H, O / 2>(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], O);
+      transpose_reduce_step<NV, 1, O / 2>(v, lane);
+    }
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void wave_transpose_reduce(float (&v)[NV], int lane) {
+  transpose_reduce_step<NV, NV, 32>(v, lane);
+}
+
+// Values left per lane by wave_transpose_reduce<NV>.
+template <int NV>
+constexpr int reduce_kept() { return NV >= 64 ? NV / 64 : 1; }
+
+// Original index of kept value i on `lane`, and whether this lane is the
+// designated writer of it (several lanes hold copies when NV < 64).
+template <int NV>
+__device__ __forceinline__ int reduce_index(int lane, int i, bool* writer) {
+  int cur = NV, idx = i;
+  bool w = true;
+  for (int o = 32; o >= 1; o >>= 1) {
+    if (cur > 1) {
+      const int half = cur >> 1;
+      if (lane & o) idx += half;
+      cur = half;
+    } else if (lane & o) {
+      w = false;
+    }
+  }
+  *writer = w;
+  return idx;
+}
+
+}  // namespace dev
+}  // namespace tq

@@ -1,0 +1,235 @@
+// Host-only part of libtq.so: argument validation, the Lloyd-Max codebook,
+// the rotation signs, fractional-bit rule, cache sizes and launch plans.
+// Nothing here touches the GPU.
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+namespace {
+
+// P(Z >= x) and the standard normal density.
+double upper_tail(double x) { return std::isinf(x) ? 0.0 : 0.5 * std::erfc(x / std::sqrt(2.0)); }
+double density(double x) {
+  return std::isinf(x) ? 0.0 : std::exp(-0.5 * x * x) / std::sqrt(2.0 * M_PI);
+}
+
+// Lloyd iteration for the N(0,1) quantizer with 2^bits levels. The
+// positive half is iterated (cells [a_k, a_{k+1}) with a_0 = 0, a_m = inf,
+// centroid = E[Z | cell]) and mirrored, which keeps the codebook exactly
+// antisymmetric with a zero middle threshold.
+Codebook build_codebook(int bits) {
+  Codebook cb;
+  cb.bits = bits;
+  const int m = 1 << (bits - 1);
+  double pos[kMaxLevels / 2];
+  // start: evenly spaced on (0, 3]
+  for (int k = 0; k < m; ++k) pos[k] = 3.0 * (k + 0.5) / m;
+  for (int it = 0; it < 1000000; ++it) {
+    double edge[kMaxLevels / 2 + 1];
+    edge[0] = 0.0;
+    for (int k = 1; k < m; ++k) edge[k] = 0.5 * (pos[k - 1] + pos[k]);
+    edge[m] = INFINITY;
+    double change = 0.0;
+    for (int k = 0; k < m; ++k) {
+      const double mass = upper_tail(edge[k]) - upper_tail(edge[k + 1]);
+      const double mean = (density(edge[k]) - density(edge[k + 1])) / mass;
+      change = std::fmax(change, std::fabs(mean - pos[k]));
+      pos[k] = mean;
+    }
+    if (change < 1e-16) break;
+  }
+  const int L = 2 * m;
+  for (int k = 0; k < m; ++k) {
+    cb.c[m + k] = pos[k];
+    cb.c[m - 1 - k] = -pos[k];
+  }
+  for (int k = 1; k < L; ++k) cb.t[k - 1] = 0.5 * (cb.c[k - 1] + cb.c[k]);
+  cb.t[m - 1] = 0.0;
+  return cb;
+}
+
+std::once_flag g_once[5];
+Codebook g_cb[5];
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+const Codebook& codebook(int bits) {
+  std::call_once(g_once[bits], [bits] { g_cb[bits] = build_codebook(bits); });
+  return g_cb[bits];
+}
+
+int check_config(const tq_config* cfg) {
+  if (!cfg) return TQ_ERR_ARG;
+  if (!valid_d(cfg->d) || !valid_bits(cfg->bits_k) || !valid_bits(cfg->bits_v))
+    return TQ_ERR_UNSUPPORTED;
+  if (cfg->norm_dtype != TQ_F16 && cfg->norm_dtype != TQ_F32) return TQ_ERR_UNSUPPORTED;
+  if (cfg->qjl != 0 && cfg->qjl != 1) return TQ_ERR_ARG;
+  return TQ_OK;
+}
+
+int check_cache(const tq_config* cfg, const tq_cache* c) {
+  if (!c) return TQ_ERR_ARG;
+  if (c->B < 0 || c->Hkv < 1 || c->capacity < 0) return TQ_ERR_ARG;
+  if (!c->kc || !c->vc || !c->kn || !c->vn) return TQ_ERR_ARG;
+  if (cfg->qjl && (!c->kq || !c->kr)) return TQ_ERR_ARG;
+  if (!aligned16(c->kc) || !aligned16(c->vc) || !aligned16(c->kn) || !aligned16(c->vn))
+    return TQ_ERR_ALIGN;
+  if (cfg->qjl && (!aligned16(c->kq) || !aligned16(c->kr))) return TQ_ERR_ALIGN;
+  return TQ_OK;
+}
+
+static int decode_tile(int d) { return d == 128 ? 256 : 512; }
+
+static int finish_plan(int d, int B, int Hq, int Hkv, int64_t n_ctx, int splits,
+                       int units_per_kv, int tile, DecodePlan* p) {
+  const int64_t tiles = (n_ctx + tile - 1) / tile;
+  int64_t s;
+  if (splits > 0) {
+    s = splits;
+  } else {
+    // aim for ~8 workgroups per compute unit on a 256-CU part
+    int64_t units = int64_t(B) * Hkv * units_per_kv;
+    if (units < 1) units = 1;
+    s = (2048 + units - 1) / units;
+  }
+  if (s > tiles) s = tiles;
+  if (s < 1) s = 1;
+  const int64_t tiles_per_split = (tiles + s - 1) / s;
+  p->tps = tiles_per_split * tile;
+  p->splits = int((n_ctx + p->tps - 1) / p->tps);
+  p->tile = tile;
+  return TQ_OK;
+}
+
+int plan_decode(int d, int qjl, int B, int Hq, int Hkv, int64_t n_ctx, int splits,
+                DecodePlan* p) {
+  if (!valid_d(d)) return TQ_ERR_UNSUPPORTED;
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || splits < 0) return TQ_ERR_ARG;
+  if (n_ctx < 1) return TQ_ERR_ARG;
+  *p = DecodePlan();
+  p->G = Hq / Hkv;
+  p->gk = (p->G % 4 == 0) ? 4 : (p->G % 2 == 0) ? 2 : 1;
+  p->chunks = p->G / p->gk;
+  finish_plan(d, B, Hq, Hkv, n_ctx, splits, p->chunks, decode_tile(d), p);
+  const size_t heads = size_t(B) * Hq;
+  size_t off = 0;
+  p->off_qp = off;  off = align256(off + heads * d * sizeof(float));
+  p->off_qq = off;  if (qjl) off = align256(off + heads * d * sizeof(float));
+  p->off_ml = off;  off = align256(off + heads * p->splits * 2 * sizeof(float));
+  p->off_acc = off; off = align256(off + heads * p->splits * size_t(d) * sizeof(float));
+  p->total = off;
+  return TQ_OK;
+}
+
+int plan_dense(int d, int B, int Hq, int Hkv, int64_t n_ctx, int splits, DecodePlan* p) {
+  // the dense baseline runs the same split-K skeleton with bf16 rows
+  return plan_decode(d, 0, B, Hq, Hkv, n_ctx, splits, p);
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+const char* tq_strerror(int s) {
+  switch (s) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_ARG: return "TQ_ERR_ARG: invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED: unsupported d, bit width or dtype";
+    case TQ_ERR_ALIGN: return "TQ_ERR_ALIGN: device pointer not 16-byte aligned";
+    case TQ_ERR_CAPACITY: return "TQ_ERR_CAPACITY: token range exceeds cache capacity";
+    case TQ_ERR_WORKSPACE: return "TQ_ERR_WORKSPACE: workspace too small";
+    case TQ_ERR_NO_DEVICE: return "TQ_ERR_NO_DEVICE: no HIP device";
+    case TQ_ERR_HIP: return "TQ_ERR_HIP: HIP runtime error";
+    default: return "unknown tq_status";
+  }
+}
+
+int tq_bits_split(double kv_bits, int force_turboquant, int* enabled, int* bits_k,
+                  int* bits_v) {
+  if (!enabled || !bits_k || !bits_v || !std::isfinite(kv_bits)) return TQ_ERR_ARG;
+  const double nearest = std::nearbyint(kv_bits);
+  const bool integral = std::fabs(kv_bits - nearest) <= 1e-6;
+  if (integral && !force_turboquant) {
+    *enabled = 0;
+    return TQ_OK;
+  }
+  int bk, bv;
+  if (integral) {
+    bk = bv = int(nearest);
+  } else {
+    bk = int(std::floor(kv_bits));
+    bv = int(std::ceil(kv_bits));
+  }
+  *enabled = 1;
+  if (!valid_bits(bk) || !valid_bits(bv)) return TQ_ERR_UNSUPPORTED;
+  *bits_k = bk;
+  *bits_v = bv;
+  return TQ_OK;
+}
+
+int tq_codebook(int bits, double* centroids, double* thresholds) {
+  if (bits < 1 || bits > 4) return TQ_ERR_UNSUPPORTED;
+  const Codebook& cb = codebook(bits);
+  const int L = 1 << bits;
+  if (centroids) std::memcpy(centroids, cb.c, sizeof(double) * L);
+  if (thresholds) std::memcpy(thresholds, cb.t, sizeof(double) * (L - 1));
+  return TQ_OK;
+}
+
+int tq_signs(uint64_t seed, int d, int8_t* out) {
+  if (!out || d < 1) return TQ_ERR_ARG;
+  for (int i = 0; i < d; ++i) out[i] = (splitmix64_at(seed, uint64_t(i)) >> 63) ? -1 : 1;
+  return TQ_OK;
+}
+
+int64_t tq_cache_bytes(const tq_config* cfg, int B, int Hkv, int64_t capacity,
+                       int64_t* plane_bytes) {
+  int st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  if (B < 0 || Hkv < 1 || capacity < 0) return TQ_ERR_ARG;
+  const int64_t rows = int64_t(B) * Hkv * capacity;
+  int64_t p[6] = {
+      rows * cfg->d * cfg->bits_k / 8, rows * cfg->d * cfg->bits_v / 8,
+      rows * norm_bytes(cfg),          rows * norm_bytes(cfg),
+      cfg->qjl ? rows * cfg->d / 8 : 0, cfg->qjl ? rows * 2 : 0};
+  int64_t total = 0;
+  for (int i = 0; i < 6; ++i) {
+    if (plane_bytes) plane_bytes[i] = p[i];
+    total += p[i];
+  }
+  return total;
+}
+
+int tq_num_splits(const tq_config* cfg, int B, int Hq, int Hkv, int64_t n_ctx, int splits) {
+  int st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  DecodePlan p;
+  st = plan_decode(cfg->d, cfg->qjl, B, Hq, Hkv, n_ctx, splits, &p);
+  return st != TQ_OK ? st : p.splits;
+}
+
+int64_t tq_workspace_bytes(const tq_config* cfg, int B, int Hq, int Hkv, int64_t n_ctx,
+                           int splits) {
+  int st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  DecodePlan p;
+  st = plan_decode(cfg->d, cfg->qjl, B, Hq, Hkv, n_ctx, splits, &p);
+  return st != TQ_OK ? st : int64_t(p.total);
+}
+
+int64_t tq_dense_workspace_bytes(int B, int Hq, int Hkv, int d, int64_t n_ctx, int splits) {
+  DecodePlan p;
+  int st = plan_dense(d, B, Hq, Hkv, n_ctx, splits, &p);
+  return st != TQ_OK ? st : int64_t(p.total);
+}
+
+}  // extern "C"

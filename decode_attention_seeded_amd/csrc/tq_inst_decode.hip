@@ -1,0 +1,61 @@
+// Instantiates the split-K decode kernel for one (D, key bits) pair, chosen
+// at compile time with -DTQ_D=... -DTQ_BK=... (BK = 16: dense bf16 baseline),
+// and exposes one launcher that dispatches over value bits, heads per
+// workgroup and QJL.
+#include "tq_internal.h"
+#include "tq_kernels.h"
+
+#ifndef TQ_D
+#error "TQ_D must be defined"
+#endif
+#ifndef TQ_BK
+#error "TQ_BK must be defined"
+#endif
+
+#define TQ_CAT2(a, b, c, d) a##b##c##d
+#define TQ_CAT(a, b, c, d) TQ_CAT2(a, b, c, d)
+#define TQ_LAUNCHER TQ_CAT(launch_decode_d, TQ_D, _k, TQ_BK)
+
+namespace tq {
+
+template <int BV, int GK, bool QJL>
+static int go(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_decode<TQ_D, TQ_BK, BV, GK, QJL>), grid, dim3(TQ_D / 32 * 64), 0, st,
+                     a, a.qp, a.qq);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+template <int BV, int GK>
+static int go_q(int qjl, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+#if TQ_BK == 16
+  (void)qjl;
+  return go<BV, GK, false>(a, grid, st);
+#else
+  return qjl ? go<BV, GK, true>(a, grid, st) : go<BV, GK, false>(a, grid, st);
+#endif
+}
+
+template <int BV>
+static int go_g(int gk, int qjl, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+  switch (gk) {
+    case 1: return go_q<BV, 1>(qjl, a, grid, st);
+    case 2: return go_q<BV, 2>(qjl, a, grid, st);
+    case 4: return go_q<BV, 4>(qjl, a, grid, st);
+    default: return TQ_ERR_UNSUPPORTED;
+  }
+}
+
+int TQ_LAUNCHER(int bv, int gk, int qjl, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+#if TQ_BK == 16
+  return bv == 16 ? go_g<16>(gk, 0, a, grid, st) : TQ_ERR_UNSUPPORTED;
+#else
+  switch (bv) {
+    case 2: return go_g<2>(gk, qjl, a, grid, st);
+    case 3: return go_g<3>(gk, qjl, a, grid, st);
+    case 4: return go_g<4>(gk, qjl, a, grid, st);
+    default: return TQ_ERR_UNSUPPORTED;
+  }
+#endif
+}
+
+}  // namespace tq

@@ -1,0 +1,66 @@
+// Internal helpers shared by the host part (tq_host.cpp) and the kernel
+// launchers (tq_kernels.hip) of libtq.so. Not part of the public ABI.
+#pragma once
+
+#include <cstdint>
+#include <cstddef>
+
+#include "tq.h"
+
+namespace tq {
+
+constexpr int kMaxLevels = 16;  // 2^4
+
+// Codebook tables in the precisions the kernels consume.
+struct Codebook {
+  int bits = 0;
+  double c[kMaxLevels];      // ascending centroids
+  double t[kMaxLevels - 1];  // thresholds
+};
+
+// Lloyd-Max codebook for N(0,1), cached per bit width (thread-safe).
+const Codebook& codebook(int bits);
+
+// SplitMix64 output i (0-based) of the stream started at state `seed`.
+inline uint64_t splitmix64_at(uint64_t seed, uint64_t i) {
+  uint64_t z = seed + (i + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+inline bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+inline bool valid_d(int d) { return d == 128 || d == 256; }
+inline bool valid_bits(int b) { return b >= 2 && b <= 4; }
+inline bool valid_in_dtype(int t) { return t == TQ_F32 || t == TQ_BF16 || t == TQ_F16; }
+
+// Validates a tq_config (shape/format fields only).
+int check_config(const tq_config* cfg);
+// Validates a cache against a config (pointers, alignment, shape).
+int check_cache(const tq_config* cfg, const tq_cache* cache);
+
+inline int norm_bytes(const tq_config* cfg) { return cfg->norm_dtype == TQ_F16 ? 2 : 4; }
+
+// Decode launch geometry.
+//   gk:     query heads handled by one workgroup (1, 2 or 4)
+//   chunks: G / gk workgroup groups per KV head
+//   tile:   tokens per tile (= threads per workgroup)
+//   splits: split-K count; every split holds >= 1 token
+//   tps:    tokens per split (multiple of tile)
+struct DecodePlan {
+  int G = 0, gk = 0, chunks = 0, tile = 0, splits = 0;
+  int64_t tps = 0;
+  // workspace section offsets (bytes)
+  size_t off_qp = 0, off_qq = 0, off_ml = 0, off_acc = 0, total = 0;
+};
+
+// Fills a plan; returns TQ_OK or a negative status.
+int plan_decode(int d, int qjl, int B, int Hq, int Hkv, int64_t n_ctx,
+                int splits, DecodePlan* plan);
+int plan_dense(int d, int B, int Hq, int Hkv, int64_t n_ctx, int splits,
+               DecodePlan* plan);
+
+}  // namespace tq

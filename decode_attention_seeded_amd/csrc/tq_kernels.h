@@ -1,0 +1,601 @@
+// Kernel templates of libtq.so (gfx950, wave64). Instantiated by the
+// tq_inst_*.hip translation units and launched from tq_api.hip.
+#pragma once
+
+#include "tq_device.h"
+
+namespace tq {
+
+// ---------------------------------------------------------------------------
+// Arguments
+// ---------------------------------------------------------------------------
+
+struct RhtArgs {
+  const void* x;
+  float* y;
+  int64_t rows;
+  int x_dtype;
+  int inverse;
+  uint64_t seed;
+};
+
+struct EncodeArgs {
+  const void* x;          // [B*Hkv][n_new][D] rows of K or V
+  uint8_t* codes;         // packed code plane
+  void* norms;            // fp16 or fp32 norm plane
+  uint8_t* qbits;         // QJL sign plane (keys with QJL only)
+  uint16_t* rnorm;        // QJL residual-norm plane
+  int64_t rows;           // B*Hkv*n_new
+  int64_t n_new, offset, capacity;
+  int in_dtype;
+  int norm_f16;
+  uint64_t seed, qjl_seed;
+  double thr[15];         // thresholds, ascending
+  double cen[16];         // centroids, ascending
+};
+
+struct QjlArgs {
+  const float* r;
+  uint32_t* bits;
+  uint16_t* rnorm;
+  int64_t rows;
+  uint64_t qjl_seed;
+};
+
+struct QPrepArgs {
+  const void* q;          // [B*Hq][D]
+  float* qp;              // [B*Hq][D]: scale*log2(e) * R q   (or unrotated)
+  float* qq;              // [B*Hq][D]: R_2 qp (QJL only)
+  int64_t heads;
+  int q_dtype;
+  int rotate;             // 0: dense baseline, no rotation
+  int qjl;
+  float mult;             // scale * log2(e)
+  uint64_t seed, qjl_seed;
+};
+
+struct DecodeArgs {
+  const uint8_t* kc;
+  const uint8_t* vc;
+  const void* kn;
+  const void* vn;
+  const uint32_t* kq;
+  const uint16_t* kr;
+  const float* qp;
+  const float* qq;
+  float* ml;              // [B*Hq][S][2]  (max in log2 units, sum)
+  float* acc;             // [B*Hq][S][D]
+  int64_t capacity, n_ctx, tps;
+  int Hkv, Hq, G, chunks, S;
+  int norm_f16;
+  float inv_sqrt_d;
+  float qjl_c;            // sqrt(pi / (2 d))
+  float cbk[16];
+  float cbv[16];
+};
+
+struct MergeArgs {
+  const float* ml;
+  const float* acc;
+  float* out;
+  int64_t heads;
+  int S;
+  int rotate;
+  uint64_t seed;
+};
+
+// ---------------------------------------------------------------------------
+// tq_rht: 16 lanes per row, E = D/16 elements per lane, fp32.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ void __launch_bounds__(256) k_rht(RhtArgs a) {
+  constexpr int E = D / 16;
+  const int l16 = threadIdx.x & 15;
+  const int grp = threadIdx.x >> 4;
+  const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
+  const float norm = 1.0f / sqrtf(float(D));
+  for (int64_t row = int64_t(blockIdx.x) * 16 + grp; row < a.rows;
+       row += int64_t(gridDim.x) * 16) {
+    float v[E];
+    dev::load_row_part<E>(a.x, a.x_dtype, row * D + l16 * E, v);
+    if (!a.inverse) {
+#pragma unroll
+      for (int i = 0; i < E; ++i) if (smask >> i & 1) v[i] = -v[i];
+    }
+    dev::fwht16<E, float>(v, l16);
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      v[i] *= norm;
+      if (a.inverse && (smask >> i & 1)) v[i] = -v[i];
+    }
+    float4* dst = reinterpret_cast<float4*>(a.y + row * D + l16 * E);
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k)
+      dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Encode: rotation, norm, quantization and packing of one K or V plane.
+// 16 lanes per row. The transform and the comparisons run in double: the
+// Hadamard sums of bf16 inputs are then exact, so the codes equal the
+// definition except for values lying exactly on a threshold.
+// ---------------------------------------------------------------------------
+
+template <int D, int BITS, bool QJL>
+__global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
+  constexpr int E = D / 16;
+  constexpr int L = 1 << BITS;
+  constexpr int REC = D * BITS / 8;          // bytes per packed row
+  constexpr int LANE_BYTES = E * BITS / 8;    // bytes of the row per lane
+  const int l16 = threadIdx.x & 15;
+  const int grp = threadIdx.x >> 4;
+  const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
+  const uint32_t qmask = QJL ? dev::sign_mask(a.qjl_seed, l16 * E, E) : 0u;
+  const double inv_sqrt_d = 1.0 / sqrt(double(D));
+
+  for (int64_t row = int64_t(blockIdx.x) * 16 + grp; row < a.rows;
+       row += int64_t(gridDim.x) * 16) {
+    const int64_t bh = row / a.n_new;
+    const int64_t t = row - bh * a.n_new;
+    const int64_t rec = bh * a.capacity + a.offset + t;
+
+    float f[E];
+    dev::load_row_part<E>(a.x, a.in_dtype, row * D + l16 * E, f);
+    double u[E];
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const double x = f[i];
+      ss += x * x;
+      u[i] = (smask >> i & 1) ? -x : x;
+    }
+    dev::fwht16<E, double>(u, l16);
+    ss = dev::group16_sum(ss);
+    const double n = sqrt(ss);
+
+    double nstored;
+    if (a.norm_f16) {
+      const uint16_t h = dev::f64_to_f16_bits(n);
+      nstored = dev::f16_bits_to_f64(h);
+      if (l16 == 0) static_cast<uint16_t*>(a.norms)[rec] = h;
+    } else {
+      const float nf = float(n);
+      nstored = nf;
+      if (l16 == 0) static_cast<float*>(a.norms)[rec] = nf;
+    }
+
+    uint64_t packed = 0;
+    uint32_t code[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const double z = n > 0.0 ? u[i] / n : 0.0;
+      uint32_t c = 0;
+#pragma unroll
+      for (int k = 0; k < L - 1; ++k) c += (z >= a.thr[k]) ? 1u : 0u;
+      code[i] = c;
+      packed |= uint64_t(c) << (BITS * i);
+    }
+    dev::store_bytes(a.codes + rec * REC + l16 * LANE_BYTES, packed, LANE_BYTES);
+
+    if constexpr (QJL) {
+      // residual in the rotated frame: r = (u - n_stored * c[code]) / sqrt(d)
+      double r[E];
+      double rr = 0.0;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        double ci = 0.0;
+#pragma unroll
+        for (int k = 0; k < L; ++k) ci = (code[i] == uint32_t(k)) ? a.cen[k] : ci;
+        const double ri = (u[i] - nstored * ci) * inv_sqrt_d;
+        rr += ri * ri;
+        r[i] = (qmask >> i & 1) ? -ri : ri;
+      }
+      rr = dev::group16_sum(rr);
+      dev::fwht16<E, double>(r, l16);
+      uint32_t bits = 0;
+#pragma unroll
+      for (int i = 0; i < E; ++i) bits |= (r[i] < 0.0 ? 1u : 0u) << i;
+      dev::store_bytes(a.qbits + rec * (D / 8) + l16 * (E / 8), bits, E / 8);
+      if (l16 == 0) a.rnorm[rec] = dev::f64_to_f16_bits(sqrt(rr));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Standalone QJL sketch of fp32 residual rows.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ void __launch_bounds__(256) k_qjl(QjlArgs a) {
+  constexpr int E = D / 16;
+  const int l16 = threadIdx.x & 15;
+  const int grp = threadIdx.x >> 4;
+  const uint32_t qmask = dev::sign_mask(a.qjl_seed, l16 * E, E);
+  for (int64_t row = int64_t(blockIdx.x) * 16 + grp; row < a.rows;
+       row += int64_t(gridDim.x) * 16) {
+    float f[E];
+    dev::load_row_part<E>(a.r, 0, row * D + l16 * E, f);
+    double r[E];
+    double rr = 0.0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const double x = f[i];
+      rr += x * x;
+      r[i] = (qmask >> i & 1) ? -x : x;
+    }
+    rr = dev::group16_sum(rr);
+    dev::fwht16<E, double>(r, l16);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) bits |= (r[i] < 0.0 ? 1u : 0u) << i;
+    dev::store_bytes(reinterpret_cast<uint8_t*>(a.bits) + row * (D / 8) + l16 * (E / 8),
+                     bits, E / 8);
+    if (l16 == 0) a.rnorm[row] = dev::f64_to_f16_bits(sqrt(rr));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query preparation: qp = mult * R q (mult = scale * log2 e), and for QJL
+// qq = R_2 qp. The dense baseline only scales.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ void __launch_bounds__(256) k_qprep(QPrepArgs a) {
+  constexpr int E = D / 16;
+  const int l16 = threadIdx.x & 15;
+  const int grp = threadIdx.x >> 4;
+  const int64_t row = int64_t(blockIdx.x) * 16 + grp;
+  if (row >= a.heads) return;   // whole 16-lane groups exit together
+  float v[E];
+  dev::load_row_part<E>(a.q, a.q_dtype, row * D + l16 * E, v);
+  if (a.rotate) {
+    const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
+#pragma unroll
+    for (int i = 0; i < E; ++i) if (smask >> i & 1) v[i] = -v[i];
+    dev::fwht16<E, float>(v, l16);
+  }
+  const float mult = a.rotate ? a.mult / sqrtf(float(D)) : a.mult;
+#pragma unroll
+  for (int i = 0; i < E; ++i) v[i] *= mult;
+  float4* dst = reinterpret_cast<float4*>(a.qp + row * D + l16 * E);
+#pragma unroll
+  for (int k = 0; k < E / 4; ++k)
+    dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  if (a.qjl) {
+    const uint32_t qmask = dev::sign_mask(a.qjl_seed, l16 * E, E);
+#pragma unroll
+    for (int i = 0; i < E; ++i) if (qmask >> i & 1) v[i] = -v[i];
+    dev::fwht16<E, float>(v, l16);
+    const float nn = 1.0f / sqrtf(float(D));
+    float4* dq = reinterpret_cast<float4*>(a.qq + row * D + l16 * E);
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k)
+      dq[k] = make_float4(v[4 * k] * nn, v[4 * k + 1] * nn, v[4 * k + 2] * nn,
+                          v[4 * k + 3] * nn);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K decode over packed codes (BK, BV in {2,3,4}) or, with BK = BV = 16,
+// over dense bf16 rows (the comparison baseline).
+//
+// One workgroup per (split, b, kv head, head chunk); W = D/32 waves, one
+// tile = 64*W tokens.
+//   K phase  : thread = token. Scores for the GK query heads of the chunk,
+//              qp read as wave-uniform values (scalar loads).
+//   softmax  : tile max per head across the workgroup, online rescale.
+//   V phase  : wave w owns coordinates [32w, 32w+32); lane = token (the
+//              tile's tokens are spread over the 64 lanes), accumulating
+//              GK x 32 weighted values per lane.
+//   epilogue : lane sums by transpose-reduce; write (max, sum, acc[D]) of
+//              the split in the rotated frame.
+// ---------------------------------------------------------------------------
+
+template <int D, int BK, int BV, int GK, bool QJL>
+__global__ void __launch_bounds__(D / 32 * 64)
+k_decode(DecodeArgs a, const float* __restrict__ qp_all, const float* __restrict__ qq_all) {
+  constexpr int W = D / 32;
+  constexpr int T = W * 64;
+  constexpr int CW = 32;
+  constexpr bool DENSE = (BK == 16);
+  constexpr int KREC = D * BK / 8;
+  constexpr int VREC = D * BV / 8;
+  constexpr int KCW = BK;                      // dwords per 32-coordinate key chunk
+  constexpr int VW = CW * BV / 32;             // dwords per value slice
+
+  __shared__ float lut_k[16 * 32];
+  __shared__ float lut_v[16 * 32];
+  __shared__ float pv[T * GK];
+  __shared__ float red[W * GK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int split = blockIdx.x;
+  const int unit = blockIdx.y;                 // (b * Hkv + kvh) * chunks + chunk
+  const int chunk = unit % a.chunks;
+  const int bkv = unit / a.chunks;             // b * Hkv + kvh
+  const int b = bkv / a.Hkv;
+  const int kvh = bkv - b * a.Hkv;
+  const int h0 = kvh * a.G + chunk * GK;       // first query head of this chunk
+  const int64_t head0 = int64_t(b) * a.Hq + h0;
+
+  if constexpr (!DENSE) {
+    for (int i = tid; i < 16 * 32; i += T) {
+      lut_k[i] = a.cbk[i >> 5];
+      lut_v[i] = a.cbv[i >> 5];
+    }
+  }
+
+  const int64_t t_begin = int64_t(split) * a.tps;
+  const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
+  const int64_t row0 = int64_t(bkv) * a.capacity;
+
+  const float* qp_base = qp_all + head0 * D;
+  const float* qq_base = QJL ? qq_all + head0 * D : qp_base;
+
+  float m_run[GK], lpart[GK];
+  float acc[GK][CW];
+#pragma unroll
+  for (int g = 0; g < GK; ++g) {
+    m_run[g] = -INFINITY;
+    lpart[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) acc[g][c] = 0.f;
+  }
+  __syncthreads();
+
+  for (int64_t base = t_begin; base < t_end; base += T) {
+    // The query rows are re-read every tile as wave-uniform (scalar) loads.
+    // An empty asm makes the pointers opaque so the compiler cannot hoist
+    // all G*D values into vector registers for the whole loop.
+    const float* qpr = qp_base;
+    const float* qqr = qq_base;
+    asm volatile("" : "+s"(qpr));
+    if constexpr (QJL) asm volatile("" : "+s"(qqr));
+    const dev::const_f32_ptr qp = dev::as_const(qpr);
+    const dev::const_f32_ptr qq = dev::as_const(qqr);
+    // ---------------- K phase: one token per thread
+    const int64_t j = base + tid;
+    const bool valid = j < t_end;
+    float s[GK];
+#pragma unroll
+    for (int g = 0; g < GK; ++g) s[g] = 0.f;
+    float nv = 0.f;
+    if (valid) {
+      // 32 coordinates per chunk: BK dwords of codes (16 for dense bf16)
+      const uint32_t* krow = reinterpret_cast<const uint32_t*>(a.kc + (row0 + j) * KREC);
+#pragma unroll 1
+      for (int ch = 0; ch < D / 32; ++ch) {
+        uint32_t kw[KCW];
+        const uint32_t* src = krow + ch * KCW;
+        if constexpr (KCW % 4 == 0) {
+#pragma unroll
+          for (int k = 0; k < KCW / 4; ++k) {
+            const uint4 q4 = reinterpret_cast<const uint4*>(src)[k];
+            kw[4 * k] = q4.x; kw[4 * k + 1] = q4.y; kw[4 * k + 2] = q4.z; kw[4 * k + 3] = q4.w;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < KCW; ++k) kw[k] = src[k];
+        }
+        const dev::const_f32_ptr qc = qp + ch * 32;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+          float c;
+          if constexpr (DENSE) {
+            c = dev::bf16_to_f32(dev::field<16>(kw, e));
+          } else {
+            c = lut_k[(dev::field<BK>(kw, e) << 5) | (lane & 31)];
+          }
+#pragma unroll
+          for (int g = 0; g < GK; ++g) s[g] = fmaf(qc[g * D + e], c, s[g]);
+        }
+      }
+      if constexpr (!DENSE) {
+        const float knrm = a.norm_f16
+            ? dev::f16_to_f32(static_cast<const uint16_t*>(a.kn)[row0 + j])
+            : static_cast<const float*>(a.kn)[row0 + j];
+        const float ks = knrm * a.inv_sqrt_d;
+#pragma unroll
+        for (int g = 0; g < GK; ++g) s[g] *= ks;
+        nv = (a.norm_f16 ? dev::f16_to_f32(static_cast<const uint16_t*>(a.vn)[row0 + j])
+                         : static_cast<const float*>(a.vn)[row0 + j]) * a.inv_sqrt_d;
+      } else {
+        nv = 1.f;
+      }
+      if constexpr (QJL) {
+        uint32_t sw[D / 32];
+        const uint4* qs = reinterpret_cast<const uint4*>(a.kq + (row0 + j) * (D / 32));
+#pragma unroll
+        for (int k = 0; k < D / 128; ++k) {
+          const uint4 q4 = qs[k];
+          sw[4 * k] = q4.x; sw[4 * k + 1] = q4.y; sw[4 * k + 2] = q4.z; sw[4 * k + 3] = q4.w;
+        }
+        float tq[GK];
+#pragma unroll
+        for (int g = 0; g < GK; ++g) tq[g] = 0.f;
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+          const bool neg = (sw[i >> 5] >> (i & 31)) & 1u;
+#pragma unroll
+          for (int g = 0; g < GK; ++g) tq[g] += neg ? -qq[g * D + i] : qq[g * D + i];
+        }
+        const float rho = dev::f16_to_f32(a.kr[row0 + j]) * a.qjl_c;
+#pragma unroll
+        for (int g = 0; g < GK; ++g) s[g] = fmaf(rho, tq[g], s[g]);
+      }
+    }
+
+    // ---------------- online softmax over the tile
+#pragma unroll
+    for (int g = 0; g < GK; ++g) {
+      const float mx = dev::wave_max(valid ? s[g] : -INFINITY);
+      if (lane == 0) red[wave * GK + g] = mx;
+    }
+    __syncthreads();
+    float alpha[GK];
+#pragma unroll
+    for (int g = 0; g < GK; ++g) {
+      float tmax = red[g];
+#pragma unroll
+      for (int w = 1; w < W; ++w) tmax = fmaxf(tmax, red[w * GK + g]);
+      const float m_new = fmaxf(m_run[g], tmax);
+      alpha[g] = exp2f(m_run[g] - m_new);
+      m_run[g] = m_new;
+      const float p = valid ? exp2f(s[g] - m_new) : 0.f;
+      lpart[g] = fmaf(lpart[g], alpha[g], p);
+      pv[tid * GK + g] = p * nv;
+#pragma unroll
+      for (int c = 0; c < CW; ++c) acc[g][c] *= alpha[g];
+    }
+    __syncthreads();
+
+    // ---------------- V phase: wave owns 32 coordinates, lane = token
+#pragma unroll 1
+    for (int m = 0; m < T / 64; ++m) {
+      const int tl = m * 64 + lane;
+      const int64_t jj = base + tl;
+      if (jj < t_end) {
+        uint32_t vw[VW];
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(
+            a.vc + (row0 + jj) * VREC + wave * (CW * BV / 8));
+        if constexpr (VW % 4 == 0) {
+#pragma unroll
+          for (int k = 0; k < VW / 4; ++k) {
+            const uint4 q4 = reinterpret_cast<const uint4*>(src)[k];
+            vw[4 * k] = q4.x; vw[4 * k + 1] = q4.y; vw[4 * k + 2] = q4.z; vw[4 * k + 3] = q4.w;
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < VW; ++k) vw[k] = src[k];
+        }
+        float p[GK];
+#pragma unroll
+        for (int g = 0; g < GK; ++g) p[g] = pv[tl * GK + g];
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+          float val;
+          if constexpr (DENSE) {
+            val = dev::bf16_to_f32(dev::field<16>(vw, c));
+          } else {
+            val = lut_v[(dev::field<BV>(vw, c) << 5) | (lane & 31)];
+          }
+#pragma unroll
+          for (int g = 0; g < GK; ++g) acc[g][c] = fmaf(p[g], val, acc[g][c]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---------------- epilogue: write the split's partial results
+#pragma unroll
+  for (int g = 0; g < GK; ++g) {
+    const float l = dev::wave_sum(lpart[g]);
+    if (lane == 0) red[wave * GK + g] = l;
+  }
+  __syncthreads();
+  if (tid < GK) {
+    float l = 0.f;
+    for (int w = 0; w < W; ++w) l += red[w * GK + tid];
+    float* ml = a.ml + ((head0 + tid) * a.S + split) * 2;
+    ml[0] = m_run[tid];
+    ml[1] = l;
+  }
+  constexpr int NV = GK * CW;
+  float flat[NV];
+#pragma unroll
+  for (int g = 0; g < GK; ++g)
+#pragma unroll
+    for (int c = 0; c < CW; ++c) flat[g * CW + c] = acc[g][c];
+  dev::wave_transpose_reduce<NV>(flat, lane);
+#pragma unroll
+  for (int i = 0; i < dev::reduce_kept<NV>(); ++i) {
+    bool writer;
+    const int idx = dev::reduce_index<NV>(lane, i, &writer);
+    if (writer) {
+      const int g = idx / CW, c = idx % CW;
+      a.acc[((head0 + g) * a.S + split) * D + wave * CW + c] = flat[i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of split partials (exact log-sum-exp, fixed order), 1/l, inverse
+// rotation. One workgroup (256 threads) per query head.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ void __launch_bounds__(256) k_merge(MergeArgs a) {
+  constexpr int Q = D / 4;                 // float4 columns
+  constexpr int SG = 256 / Q;              // split groups
+  constexpr int E = D / 16;
+  __shared__ float red[256];
+  __shared__ float4 part[SG][Q];
+  __shared__ float orot[D];
+  const int tid = threadIdx.x;
+  const int64_t head = blockIdx.x;
+  const float* ml = a.ml + head * a.S * 2;
+
+  float mx = -INFINITY;
+  for (int s = tid; s < a.S; s += 256) mx = fmaxf(mx, ml[2 * s]);
+  red[tid] = mx;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  const float M = red[0];
+  __syncthreads();
+  float l = 0.f;
+  for (int s = tid; s < a.S; s += 256) l += ml[2 * s + 1] * exp2f(ml[2 * s] - M);
+  red[tid] = l;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  const float inv_l = 1.f / red[0];
+
+  const int q = tid % Q, sg = tid / Q;
+  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = sg; s < a.S; s += SG) {
+    const float w = exp2f(ml[2 * s] - M);
+    const float4 v = reinterpret_cast<const float4*>(a.acc + (head * a.S + s) * D)[q];
+    sum.x = fmaf(w, v.x, sum.x); sum.y = fmaf(w, v.y, sum.y);
+    sum.z = fmaf(w, v.z, sum.z); sum.w = fmaf(w, v.w, sum.w);
+  }
+  part[sg][q] = sum;
+  __syncthreads();
+  if (tid < Q) {
+    float4 t = part[0][tid];
+    for (int g = 1; g < SG; ++g) {
+      const float4 u = part[g][tid];
+      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+    }
+    orot[4 * tid + 0] = t.x * inv_l; orot[4 * tid + 1] = t.y * inv_l;
+    orot[4 * tid + 2] = t.z * inv_l; orot[4 * tid + 3] = t.w * inv_l;
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float v[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = orot[tid * E + i];
+    if (a.rotate) {
+      dev::fwht16<E, float>(v, tid);
+      const uint32_t smask = dev::sign_mask(a.seed, tid * E, E);
+      const float nn = 1.0f / sqrtf(float(D));
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[i] = (smask >> i & 1) ? -v[i] * nn : v[i] * nn;
+    }
+    float4* dst = reinterpret_cast<float4*>(a.out + head * D + tid * E);
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k)
+      dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  }
+}
+
+}  // namespace tq

@@ -1,0 +1,219 @@
+/*
+ * tq.h - TurboQuant KV-cache decode path for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libtq.so. Plain pointers and sizes only.
+ *
+ * The method (see the pages "TurboQuant Performance Benefits: Memory
+ * Reduction and Speed Optimization in MLX-VLM", "How to Use TurboQuant with
+ * the MLX-VLM Python API: A Complete Guide" and the mlx-turboquant README):
+ *   - K and V rows are rotated by a seeded randomized Hadamard transform
+ *     R = H_d diag(s) / sqrt(d) (sign flip, then a normalized Walsh-Hadamard
+ *     transform in Sylvester order; s from SplitMix64 seeded with `seed`,
+ *     s_i = -1 when the top bit of the i-th output is set);
+ *   - each row is normalized (one norm per row, stored rounded to the norm
+ *     dtype) and every coordinate of z = sqrt(d) R x / ||x|| is quantized
+ *     against the N(0,1) Lloyd-Max codebook: code = #{k : z >= t_k};
+ *   - codes are bit-packed: code i of a row sits at bits [b*i, b*i + b) of the
+ *     row's little-endian byte string;
+ *   - decode attention runs on the packed codes: the query is rotated into
+ *     the same frame, scores come from codebook lookups, the softmax is
+ *     online, values are dequantized and accumulated in the same pass;
+ *   - optionally a 1-bit QJL sketch of the key residual r = R k - k_hat
+ *     (sign bits of R_2 r, R_2 built like R from `qjl_seed`, plus ||r|| in
+ *     fp16) corrects the score by sqrt(pi/(2d)) ||r|| <R_2 R q, sign(R_2 r)>.
+ *
+ * Conventions shared by every entry point:
+ *   - Device buffers are allocated and owned by the caller. The library never
+ *     allocates, frees or synchronizes; every call only enqueues work on
+ *     `stream` (0 = the null stream) and returns.
+ *   - Every argument is validated on the host before any HIP call. A failed
+ *     validation returns a negative tq_status and touches no memory.
+ *   - Device pointers must be 16-byte aligned (TQ_ERR_ALIGN otherwise).
+ *   - Functions are stateless and may be called from several host threads.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_ARG = -1,          /* null pointer, negative size, inconsistent shape  */
+  TQ_ERR_UNSUPPORTED = -2,  /* d not in {128,256}, bits not in {2,3,4}, dtype   */
+  TQ_ERR_ALIGN = -3,        /* a device pointer is not 16-byte aligned          */
+  TQ_ERR_CAPACITY = -4,     /* offset + n_new > capacity, or n_ctx > capacity   */
+  TQ_ERR_WORKSPACE = -5,    /* workspace smaller than tq_workspace_bytes()      */
+  TQ_ERR_NO_DEVICE = -6,    /* no HIP device visible                           */
+  TQ_ERR_HIP = -7           /* a HIP launch or runtime call failed              */
+} tq_status;
+
+/* Element types of inputs (q, k, v, x) and of the per-row norms. */
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+/* Static description of one quantized cache format. */
+typedef struct {
+  int d;              /* head dimension: 128 or 256                           */
+  int bits_k;         /* key code width: 2, 3 or 4                            */
+  int bits_v;         /* value code width: 2, 3 or 4                          */
+  int norm_dtype;     /* TQ_F16 or TQ_F32: storage of the per-row norms       */
+  int qjl;            /* 1: keys also carry the 1-bit QJL residual sketch     */
+  uint64_t seed;      /* SplitMix64 seed of the rotation signs s              */
+  uint64_t qjl_seed;  /* SplitMix64 seed of the QJL rotation R_2              */
+} tq_config;
+
+/*
+ * Caller-owned device planes of a packed cache with B batch entries, Hkv KV
+ * heads and room for `capacity` tokens. Row (b, h, t) is record
+ * (b * Hkv + h) * capacity + t of every plane:
+ *   kc : d*bits_k/8 bytes per record (packed key codes)
+ *   vc : d*bits_v/8 bytes per record (packed value codes)
+ *   kn : key norm   (2 bytes if norm_dtype == TQ_F16, else 4)
+ *   vn : value norm (same dtype as kn)
+ *   kq : d/8 bytes per record, QJL sign bits; as little-endian uint32 words,
+ *        coordinate 32m + j is bit j of word m; bit = 1 where (R_2 r)_i < 0
+ *        (only when qjl, else may be NULL)
+ *   kr : fp16 ||r|| per record (only when qjl, else may be NULL)
+ * tq_cache_bytes() gives each plane's size.
+ */
+typedef struct {
+  void* kc;
+  void* vc;
+  void* kn;
+  void* vn;
+  void* kq;
+  void* kr;
+  int B;
+  int Hkv;
+  int64_t capacity;
+} tq_cache;
+
+/*
+ * Fractional bit widths (performance page, "Fractional-Bit Precision
+ * Support"; API page, "How TurboQuant Activation Works").
+ * *enabled = 0 when TurboQuant is not selected: kv_bits is not finite-and-
+ * fractional and force_turboquant is 0 (the uniform fallback, not provided
+ * here); bits_k / bits_v are then left untouched. Otherwise *enabled = 1 and
+ * bits_k = floor(kv_bits), bits_v = ceil(kv_bits) for a fractional width
+ * (3.5 -> 3/4), or both = kv_bits for an integer width. A width within 1e-6
+ * of an integer counts as that integer.
+ * Returns TQ_OK, TQ_ERR_ARG (null output pointer, non-finite kv_bits) or
+ * TQ_ERR_UNSUPPORTED (a resulting width outside 2..4). Host only.
+ */
+int tq_bits_split(double kv_bits, int force_turboquant, int* enabled,
+                  int* bits_k, int* bits_v);
+
+/*
+ * N(0,1) Lloyd-Max codebook for `bits` in 1..4 (performance page, "What Is
+ * TurboQuant?": MSE code-book; README: Lloyd-Max LUT). Writes 2^bits
+ * ascending centroids and 2^bits - 1 thresholds t_k = (c_{k-1} + c_k) / 2
+ * (host arrays, either may be NULL). Computed in double on the host.
+ */
+int tq_codebook(int bits, double* centroids, double* thresholds);
+
+/* The +-1 rotation signs for (seed, d) as int8 (host array of d). Host only. */
+int tq_signs(uint64_t seed, int d, int8_t* out);
+
+/*
+ * Bytes of each plane of a cache (capacity tokens) written to
+ * plane_bytes[6] in the order kc, vc, kn, vn, kq, kr (may be NULL).
+ * Returns the total, or a negative tq_status.
+ */
+int64_t tq_cache_bytes(const tq_config* cfg, int B, int Hkv, int64_t capacity,
+                       int64_t* plane_bytes);
+
+/*
+ * Rotate rows: y = R x (inverse = 0) or y = R^T x (inverse = 1).
+ * x: [rows][d] of x_dtype (device); y: [rows][d] fp32 (device), may alias x
+ * only when x_dtype == TQ_F32. d in {128, 256}. rows == 0 is a no-op.
+ * (API page: _rht_forward / _rht_inverse; README: randomized Hadamard.)
+ */
+int tq_rht(const void* x, int x_dtype, float* y, int64_t rows, int d,
+           uint64_t seed, int inverse, hipStream_t stream);
+
+/*
+ * Encode n_new tokens of K and V into the cache at token positions
+ * [offset, offset + n_new) of every (b, h) row (performance page, "What Is
+ * TurboQuant?"; README, "The 1-bit QJL residual").
+ * k, v: [B][Hkv][n_new][d] contiguous, in_dtype TQ_F32/TQ_BF16/TQ_F16.
+ * Writes kc, vc, kn, vn (and kq, kr when cfg->qjl) of those positions only.
+ * Converting a dense cache is offset = 0, n_new = length; a decode-time
+ * append is offset = length, n_new = 1. n_new == 0 is a no-op.
+ * Codes are computed in double precision, so they equal the exact
+ * definition except where z lies exactly on a threshold.
+ */
+int tq_encode_kv(const tq_config* cfg, const void* k, const void* v,
+                 int in_dtype, int64_t offset, int64_t n_new,
+                 const tq_cache* cache, hipStream_t stream);
+
+/*
+ * Standalone QJL sketch of residual rows (README, "The 1-bit QJL residual").
+ * r: [rows][d] fp32 (device). Writes bits: [rows][d/32] uint32 words
+ * (coordinate 32m + j at bit j of word m; 1 where (R_2 r)_i < 0) and
+ * rnorm_f16: [rows] fp16 bit patterns of ||r||. d in {128, 256}.
+ * tq_encode_kv with qjl = 1 produces the same bits as encoding without QJL,
+ * forming r = R k - k_hat_rot, and calling this.
+ */
+int tq_qjl_sketch(const float* r, int64_t rows, int d, uint64_t qjl_seed,
+                  uint32_t* bits, uint16_t* rnorm_f16, hipStream_t stream);
+
+/*
+ * Split count tq_attend_decode uses for these sizes (splits = 0 means the
+ * library's choice). Returns >= 1, or a negative tq_status.
+ */
+int tq_num_splits(const tq_config* cfg, int B, int Hq, int Hkv, int64_t n_ctx,
+                  int splits);
+
+/* Workspace bytes tq_attend_decode needs; negative tq_status on bad args. */
+int64_t tq_workspace_bytes(const tq_config* cfg, int B, int Hq, int Hkv,
+                           int64_t n_ctx, int splits);
+
+/*
+ * One decode step of attention over the first n_ctx tokens of the cache
+ * (performance page, "Custom Metal Kernel Implementation": scores on packed
+ * codes fused with value aggregation; README, "How it plugs in": the query
+ * is rotated and the QJL correction added).
+ *   q:   [B][Hq][d] of q_dtype (device). Hq must be a multiple of cache->Hkv;
+ *        query head h reads KV head h / (Hq / Hkv).
+ *   out: [B][Hq][d] fp32 (device):
+ *        out = softmax_j(scale * <q, k_hat_j> [+ QJL term]) . v_hat_j
+ *        with k_hat / v_hat the dequantized rows in the original frame.
+ *   scale: 0 selects 1/sqrt(d).
+ *   splits: 0 lets the library choose (see tq_num_splits).
+ *   ws:  device workspace of at least tq_workspace_bytes() bytes.
+ * n_ctx must be in [1, capacity]. The result does not depend on host
+ * threads or on timing: partials are merged in a fixed order.
+ */
+int tq_attend_decode(const tq_config* cfg, const void* q, int q_dtype, int B,
+                     int Hq, const tq_cache* cache, int64_t n_ctx, float scale,
+                     int splits, float* out, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/*
+ * Dense bf16 decode attention for comparison on the same GPU (not part of
+ * the method): out = softmax(scale q K^T) V over k, v: [B][Hkv][n_ctx][d]
+ * bf16, q: [B][Hq][d] bf16, out fp32. Same workspace rules
+ * (tq_dense_workspace_bytes).
+ */
+int64_t tq_dense_workspace_bytes(int B, int Hq, int Hkv, int d, int64_t n_ctx,
+                                 int splits);
+int tq_dense_decode_bf16(const void* q, const void* k, const void* v, int B,
+                         int Hq, int Hkv, int d, int64_t n_ctx, float scale,
+                         int splits, float* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* Human-readable name of a tq_status. Never NULL. */
+const char* tq_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

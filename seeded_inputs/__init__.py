@@ -51,7 +51,7 @@ class Workload:
     bits_v: int
     norm_dtype: str          # "f16" | "f32"
     qjl: bool
-    in_dtype: str            # "f32" | "bf16"
+    in_dtype: str            # "f32" | "bf16" | "f16"
     structure: str           # "iid" | "outlier" | "correlated"
     append: int = 0          # tokens appended at the end of the context
     seed: int = 0            # RHT sign seed
@@ -125,9 +125,16 @@ def kv_rows(w: Workload, tensor: int, b: int, h: int, t0: int, t1: int,
         hi = min(t1 - blk * BLOCK, x.shape[0])
         parts.append(x[lo:hi])
     x = np.concatenate(parts) if parts else np.zeros((0, w.d), np.float32)
-    if w.in_dtype == "bf16":
+    return _round_input(x, w.in_dtype)
+
+
+def _round_input(x: np.ndarray, in_dtype: str):
+    if in_dtype == "bf16":
         raw = f32_to_bf16_bits(x)
         return raw, bf16_bits_to_f32(raw)
+    if in_dtype == "f16":
+        raw = x.astype(np.float16)
+        return raw, raw.astype(np.float32)
     return x, x
 
 
@@ -146,10 +153,7 @@ def queries(w: Workload, data_seed=DATA_SEED):
                 j = int(js[b, hq])
                 _, kj = kv_rows(w, T_K, b, hq // w.G, j, j + 1, data_seed)
                 x[b, hq] = np.float32(0.8) * kj[0] + np.float32(0.6) * eps[b, hq]
-    if w.in_dtype == "bf16":
-        raw = f32_to_bf16_bits(x)
-        return raw, bf16_bits_to_f32(raw)
-    return x, x
+    return _round_input(x, w.in_dtype)
 
 
 def correlated_tokens(w: Workload, data_seed=DATA_SEED):
@@ -163,7 +167,7 @@ def kv_full(w: Workload, tensor: int, data_seed=DATA_SEED, workers=None):
     Blocks are generated on a thread pool (NumPy releases the GIL in its
     generators), so a 1 GiB tensor takes seconds.
     """
-    dt = np.uint16 if w.in_dtype == "bf16" else np.float32
+    dt = {"bf16": np.uint16, "f16": np.float16}.get(w.in_dtype, np.float32)
     out = np.empty((w.B, w.Hkv, w.N, w.d), dt)
     jobs = [(b, h, blk) for b in range(w.B) for h in range(w.Hkv)
             for blk in range((w.N + BLOCK - 1) // BLOCK)]

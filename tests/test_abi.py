@@ -1,0 +1,193 @@
+"""C-ABI tests that need no GPU: the library loads, exports what include/tq.h
+declares, host helpers agree with the independent oracle, and every argument
+check returns its status before any device work. No test here launches a
+kernel; paths that would pass validation are only taken with B = 0 or
+n_new = 0 (documented no-ops)."""
+
+import ctypes
+import json
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_attention_seeded_amd as tq
+from decode_attention_seeded_amd import binding as bd
+import oracle as o
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    with open(os.path.join(ROOT, "include", "tq.h")) as f:
+        header = f.read()
+    declared = set(re.findall(r"^\s*(?:const char\*|int64_t|int)\s+(tq_\w+)\s*\(", header, re.M))
+    assert declared == set(tq.EXPORTS)
+    lib = tq.lib()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_host_codebook_matches_oracle(bits):
+    c, t = tq.tq_codebook(bits)
+    oc, ot = o.lloyd_max(bits)
+    np.testing.assert_allclose(c, oc, atol=1e-13, rtol=0)
+    np.testing.assert_allclose(t, ot, atol=1e-13, rtol=0)
+    assert t[len(t) // 2] == 0.0
+
+
+@pytest.mark.parametrize("seed,d", [(0, 128), (1, 256), (12345, 128)])
+def test_host_signs_match_oracle(seed, d):
+    assert tq.tq_signs(seed, d) == list(o.signs(seed, d).astype(int))
+
+
+def test_bits_split_matches_truth_table():
+    with open(os.path.join(ROOT, "tests", "golden", "enable_rule.json")) as f:
+        g = json.load(f)
+    for bits, scheme, want in g["enabled"]:
+        if bits is None:
+            continue
+        got = tq.tq_bits_split(bits, scheme == "turboquant")
+        assert (got is not None) == want, (bits, scheme)
+        if want:
+            assert got == o.bits_split(bits, scheme)
+    assert tq.tq_bits_split(3.5) == (3, 4)
+    with pytest.raises(tq.TqError) as e:
+        tq.tq_bits_split(5.5)
+    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+    with pytest.raises(tq.TqError):
+        tq.tq_bits_split(float("nan"))
+
+
+@pytest.mark.parametrize("bk,bv,nd,qjl,d", [(3, 4, "f16", False, 128), (4, 4, "f32", False, 128),
+                                            (2, 2, "f16", False, 256), (3, 4, "f16", True, 128)])
+def test_cache_bytes_match_format(bk, bv, nd, qjl, d):
+    cfg = tq.Config(d=d, bits_k=bk, bits_v=bv, norm_dtype=nd, qjl=qjl)
+    total, planes = tq.tq_cache_bytes(cfg, 2, 3, 100)
+    nb = 2 if nd == "f16" else 4
+    assert total == 600 * o.tq_bytes_per_token(d, bk, bv, nb, qjl)
+    assert planes[0] == 600 * d * bk // 8 and planes[1] == 600 * d * bv // 8
+
+
+def test_split_plan_and_workspace():
+    cfg = tq.Config(d=128, bits_k=3, bits_v=4)
+    s = tq.tq_num_splits(cfg, 1, 32, 8, 524288)
+    assert s >= 8
+    assert tq.tq_num_splits(cfg, 1, 32, 8, 1) == 1
+    assert tq.tq_num_splits(cfg, 1, 32, 8, 300, splits=7) == 2     # clamped to tiles
+    ws = tq.tq_workspace_bytes(cfg, 1, 32, 8, 524288)
+    assert ws >= 32 * 128 * 4 + 32 * s * (128 + 2) * 4
+    with pytest.raises(tq.TqError) as e:
+        tq.tq_num_splits(cfg, 1, 30, 8, 100)
+    assert e.value.status == tq.TQ_ERR_ARG
+
+
+def test_strerror_names_every_status():
+    for s in range(0, -8, -1):
+        assert tq.tq_strerror(s).startswith("TQ_")
+    assert tq.tq_strerror(-99) == "unknown tq_status"
+
+
+# ---------------------------------------------------------------- validation
+# Fake device addresses: aligned (0x1000...) and misaligned (+4). They are
+# never dereferenced: every call below fails validation or is a no-op.
+
+A = 0x10000
+MIS = 0x10004
+
+
+def _cfg(**kw):
+    base = dict(d=128, bits_k=3, bits_v=4, norm_dtype=tq.TQ_F16, qjl=0, seed=0, qjl_seed=1)
+    base.update(kw)
+    return bd.tq_config(**base)
+
+
+def _cache(B=1, Hkv=2, cap=64, **kw):
+    c = bd.tq_cache(A, A, A, A, A, A, B, Hkv, cap)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _enc(cfg=None, k=A, v=A, dt=tq.TQ_BF16, off=0, n=4, cache=None):
+    lib = tq.lib()
+    cfg = _cfg() if cfg is None else cfg
+    cache = _cache() if cache is None else cache
+    return lib.tq_encode_kv(ctypes.byref(cfg) if cfg != "null" else None, k, v, dt, off, n,
+                            ctypes.byref(cache) if cache != "null" else None, None)
+
+
+def test_encode_validation():
+    assert _enc(cfg="null") == tq.TQ_ERR_ARG
+    assert _enc(cfg=_cfg(d=64)) == tq.TQ_ERR_UNSUPPORTED
+    assert _enc(cfg=_cfg(bits_k=5)) == tq.TQ_ERR_UNSUPPORTED
+    assert _enc(cfg=_cfg(bits_v=1)) == tq.TQ_ERR_UNSUPPORTED
+    assert _enc(cfg=_cfg(norm_dtype=tq.TQ_BF16)) == tq.TQ_ERR_UNSUPPORTED
+    assert _enc(cfg=_cfg(qjl=2)) == tq.TQ_ERR_ARG
+    assert _enc(cache="null") == tq.TQ_ERR_ARG
+    assert _enc(cache=_cache(kc=None)) == tq.TQ_ERR_ARG
+    assert _enc(cache=_cache(vn=MIS)) == tq.TQ_ERR_ALIGN
+    assert _enc(cfg=_cfg(qjl=1), cache=_cache(kq=None)) == tq.TQ_ERR_ARG
+    assert _enc(cfg=_cfg(qjl=1), cache=_cache(kr=MIS)) == tq.TQ_ERR_ALIGN
+    assert _enc(dt=7) == tq.TQ_ERR_UNSUPPORTED
+    assert _enc(off=-1) == tq.TQ_ERR_ARG
+    assert _enc(n=-1) == tq.TQ_ERR_ARG
+    assert _enc(off=60, n=5) == tq.TQ_ERR_CAPACITY
+    assert _enc(k=None) == tq.TQ_ERR_ARG
+    assert _enc(v=MIS) == tq.TQ_ERR_ALIGN
+    assert _enc(cache=_cache(Hkv=0)) == tq.TQ_ERR_ARG
+    assert _enc(n=0) == tq.TQ_OK                       # empty append: no-op
+    assert _enc(cache=_cache(B=0)) == tq.TQ_OK         # empty batch: no-op
+
+
+def _dec(cfg=None, q=A, qdt=tq.TQ_BF16, B=1, Hq=4, cache=None, n_ctx=10, scale=0.0,
+         splits=0, out=A, ws=A, ws_bytes=1 << 30):
+    lib = tq.lib()
+    cfg = _cfg() if cfg is None else cfg
+    cache = _cache() if cache is None else cache
+    return lib.tq_attend_decode(ctypes.byref(cfg), q, qdt, B, Hq, ctypes.byref(cache), n_ctx,
+                                scale, splits, out, ws, ws_bytes, None)
+
+
+def test_decode_validation():
+    assert _dec(cfg=_cfg(d=96)) == tq.TQ_ERR_UNSUPPORTED
+    assert _dec(qdt=5) == tq.TQ_ERR_UNSUPPORTED
+    assert _dec(B=2) == tq.TQ_ERR_ARG                  # B must match the cache
+    assert _dec(Hq=3) == tq.TQ_ERR_ARG                 # Hq % Hkv
+    assert _dec(splits=-1) == tq.TQ_ERR_ARG
+    assert _dec(scale=float("nan")) == tq.TQ_ERR_ARG
+    assert _dec(n_ctx=0) == tq.TQ_ERR_ARG
+    assert _dec(n_ctx=65) == tq.TQ_ERR_CAPACITY
+    assert _dec(q=None) == tq.TQ_ERR_ARG
+    assert _dec(out=MIS) == tq.TQ_ERR_ALIGN
+    assert _dec(ws=MIS) == tq.TQ_ERR_ALIGN
+    assert _dec(ws_bytes=64) == tq.TQ_ERR_WORKSPACE
+    assert _dec(cache=_cache(kn=MIS)) == tq.TQ_ERR_ALIGN
+    assert _dec(B=0, cache=_cache(B=0)) == tq.TQ_OK    # empty batch: no-op
+
+
+def test_rht_qjl_dense_validation():
+    lib = tq.lib()
+    assert lib.tq_rht(A, tq.TQ_F32, A, -1, 128, 0, 0, None) == tq.TQ_ERR_ARG
+    assert lib.tq_rht(A, tq.TQ_F32, A, 4, 64, 0, 0, None) == tq.TQ_ERR_UNSUPPORTED
+    assert lib.tq_rht(A, 9, A, 4, 128, 0, 0, None) == tq.TQ_ERR_UNSUPPORTED
+    assert lib.tq_rht(A, tq.TQ_F32, A, 4, 128, 0, 3, None) == tq.TQ_ERR_ARG
+    assert lib.tq_rht(None, tq.TQ_F32, A, 4, 128, 0, 0, None) == tq.TQ_ERR_ARG
+    assert lib.tq_rht(MIS, tq.TQ_F32, A, 4, 128, 0, 0, None) == tq.TQ_ERR_ALIGN
+    assert lib.tq_rht(A, tq.TQ_F32, A, 0, 128, 0, 0, None) == tq.TQ_OK
+    assert lib.tq_qjl_sketch(A, 4, 100, 1, A, A, None) == tq.TQ_ERR_UNSUPPORTED
+    assert lib.tq_qjl_sketch(A, -2, 128, 1, A, A, None) == tq.TQ_ERR_ARG
+    assert lib.tq_qjl_sketch(A, 4, 128, 1, None, A, None) == tq.TQ_ERR_ARG
+    assert lib.tq_qjl_sketch(A, 4, 128, 1, A, MIS, None) == tq.TQ_ERR_ALIGN
+    assert lib.tq_qjl_sketch(A, 0, 128, 1, A, A, None) == tq.TQ_OK
+    bad_d = (A, A, A, 1, 4, 2, 100, 10, 0.0, 0, A, A, 1 << 30, None)
+    assert lib.tq_dense_decode_bf16(*bad_d) == tq.TQ_ERR_UNSUPPORTED
+    bad_g = (A, A, A, 1, 5, 2, 128, 10, 0.0, 0, A, A, 1 << 30, None)
+    assert lib.tq_dense_decode_bf16(*bad_g) == tq.TQ_ERR_ARG
+    small = (A, A, A, 1, 4, 2, 128, 10, 0.0, 0, A, A, 8, None)
+    assert lib.tq_dense_decode_bf16(*small) == tq.TQ_ERR_WORKSPACE
+    mis = (A, MIS, A, 1, 4, 2, 128, 10, 0.0, 0, A, A, 1 << 30, None)
+    assert lib.tq_dense_decode_bf16(*mis) == tq.TQ_ERR_ALIGN

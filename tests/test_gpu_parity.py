@@ -1,0 +1,209 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle on
+the same seeded inputs: small shapes that span several tiles plus a ragged
+tail, every bit-width combination, GQA group sizes 1/2/3/4/8, d = 128/256,
+QJL, fp32/fp16 norms, appends, explicit scale, split counts, edge cases.
+
+Bars: packed codes, norms and QJL sign bits bit-exact except the counted
+boundary cases; attention output max row-relative error <= 2e-3."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as o
+import seeded_inputs as si
+from gpu_helpers import (TOL, compare_codes, config_of, gpu_decode, gpu_encode, kv_host,
+                         log, oracle_encode, rel_err, to_device, torch_cuda)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # name: small_workload kwargs
+    "d128_k4v4_f32norm_f32in_g1": dict(B=1, Hq=1, Hkv=1, N=700, bits_k=4, bits_v=4,
+                                       norm_dtype="f32", in_dtype="f32", wid=101),
+    "d128_k3v4_gqa4": dict(B=2, Hq=8, Hkv=2, N=1000, bits_k=3, bits_v=4, wid=102),
+    "d256_k2v2_outlier": dict(B=2, Hq=4, Hkv=1, d=256, N=1100, bits_k=2, bits_v=2,
+                              structure="outlier", wid=103),
+    "d128_k3qjl_v4_corr": dict(B=2, Hq=8, Hkv=2, N=900, bits_k=3, bits_v=4, qjl=True,
+                               structure="correlated", wid=104),
+    "d128_k2v3_g2_f16in": dict(B=1, Hq=4, Hkv=2, N=513, bits_k=2, bits_v=3,
+                               in_dtype="f16", wid=105),
+    "d128_k4v2_g8": dict(B=1, Hq=8, Hkv=1, N=600, bits_k=4, bits_v=2, wid=106),
+    "d128_k3v3_g3": dict(B=1, Hq=6, Hkv=2, N=450, bits_k=3, bits_v=3, wid=107),
+    "d256_k3qjl_v4": dict(B=1, Hq=4, Hkv=2, d=256, N=1300, bits_k=3, bits_v=4, qjl=True,
+                          structure="correlated", wid=108),
+    "d256_k4v3_f32norm": dict(B=1, Hq=2, Hkv=1, d=256, N=520, bits_k=4, bits_v=3,
+                              norm_dtype="f32", wid=109),
+    "d128_n1": dict(B=2, Hq=4, Hkv=2, N=1, bits_k=3, bits_v=4, wid=110),
+}
+
+
+def _run_case(w, scale=0.0, splits=0):
+    torch_cuda()
+    log(f"case {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} N={w.N} "
+        f"K{w.bits_k}/V{w.bits_v} qjl={w.qjl} norm={w.norm_dtype} in={w.in_dtype}")
+    cfg, cache = gpu_encode(w)
+    ref = oracle_encode(w)
+    stats = compare_codes(w, cache, ref)
+    qraw, qf = si.queries(w)
+    got = gpu_decode(w, cfg, cache, to_device(qraw, w.in_dtype), w.N, scale=scale,
+                     splits=splits)
+    want = o.attend(qf.astype(np.float64), ref, w.N, d=w.d, seed=w.seed, bits_k=w.bits_k,
+                    bits_v=w.bits_v, Hkv=w.Hkv, scale=scale, qjl=w.qjl,
+                    qjl_seed=w.qjl_seed)
+    err, abs_err = rel_err(got, want)
+    log(f"  boundary stats {stats}; max row-relative error {err:.3e} (abs {abs_err:.3e})")
+    assert np.isfinite(got).all()
+    assert err <= TOL
+    return got
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_encode_and_decode_match_oracle(name):
+    _run_case(si.small_workload(**SMALL[name]))
+
+
+def test_explicit_scale():
+    _run_case(si.small_workload(B=1, Hq=4, Hkv=2, N=777, wid=120), scale=0.37)
+
+
+def test_split_count_invariance_and_determinism():
+    torch = torch_cuda()
+    w = si.small_workload(B=1, Hq=8, Hkv=2, N=3000, bits_k=3, bits_v=4, wid=121)
+    cfg, cache = gpu_encode(w)
+    qraw, _ = si.queries(w)
+    q = to_device(qraw, w.in_dtype)
+    base = gpu_decode(w, cfg, cache, q, w.N, splits=1)
+    for s in (2, 5, 12, 0):
+        other = gpu_decode(w, cfg, cache, q, w.N, splits=s)
+        err, _ = rel_err(other, base)
+        log(f"splits={s}: rel diff vs 1 split {err:.2e}")
+        assert err <= 1e-5
+    again = gpu_decode(w, cfg, cache, q, w.N)
+    assert np.array_equal(again, gpu_decode(w, cfg, cache, q, w.N))
+
+
+def test_append_chunks_equal_bulk_encode():
+    """Encoding as several appends writes the same planes as one encode."""
+    torch = torch_cuda()
+    w = si.small_workload(B=2, Hq=4, Hkv=2, N=700, bits_k=3, bits_v=4, qjl=True, wid=122)
+    _, bulk = gpu_encode(w)
+    _, parts = gpu_encode(w, chunks=[(0, 1), (1, 300), (300, 301), (301, 700)])
+    for name in ("kc", "vc", "kn", "vn", "kq", "kr"):
+        assert torch.equal(getattr(bulk, name), getattr(parts, name)), name
+
+
+def test_decode_prefix_of_larger_cache():
+    """n_ctx < capacity attends to the first n_ctx tokens only."""
+    w = si.small_workload(B=1, Hq=4, Hkv=2, N=800, wid=123)
+    cfg, cache = gpu_encode(w, capacity=1000)
+    qraw, qf = si.queries(w)
+    n = 517
+    got = gpu_decode(w, cfg, cache, to_device(qraw, w.in_dtype), n)
+    ref = oracle_encode(w, 0, n)
+    want = o.attend(qf.astype(np.float64), ref, n, d=w.d, seed=0, bits_k=3, bits_v=4, Hkv=2)
+    assert rel_err(got, want)[0] <= TOL
+
+
+def test_zero_vectors_encode_and_decode():
+    """All-zero key/value rows: norm 0, middle code, zero contribution."""
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.small_workload(B=1, Hq=2, Hkv=1, N=64, wid=124)
+    rk, rv, fk, fv = kv_host(w, 0, w.N)
+    rk[:, :, 5] = 0
+    rv[:, :, 5] = 0
+    rk[:, :, 9] = 0
+    fk[:, :, 5] = 0; fv[:, :, 5] = 0; fk[:, :, 9] = 0
+    cfg = config_of(w)
+    cache = tq.PackedCache(cfg, w.B, w.Hkv, w.N)
+    tq.tq_encode_kv(cfg, to_device(rk, "bf16"), to_device(rv, "bf16"), 0, cache)
+    torch.cuda.synchronize()
+    ref = o.encode_kv(fk, fv, seed=0, bits_k=3, bits_v=4, norm_dtype="f16")
+    compare_codes(w, cache, ref)
+    assert cache.kn[0, 0, 5].item() == 0 and cache.vn[0, 0, 5].item() == 0
+    qraw, qf = si.queries(w)
+    got = gpu_decode(w, cfg, cache, to_device(qraw, "bf16"), w.N)
+    want = o.attend(qf.astype(np.float64), ref, w.N, d=w.d, seed=0, bits_k=3, bits_v=4, Hkv=1)
+    assert rel_err(got, want)[0] <= TOL
+
+
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("inverse", [False, True])
+def test_rht_matches_oracle(d, dtype, inverse):
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    rows = 37
+    rng = np.random.default_rng(d + len(dtype))
+    x32 = rng.standard_normal((rows, d)).astype(np.float32)
+    raw, xf = si._round_input(x32, dtype)
+    y = torch.empty((rows, d), dtype=torch.float32, device="cuda")
+    tq.tq_rht(to_device(raw, dtype), y, seed=7, inverse=inverse)
+    torch.cuda.synchronize()
+    fn = o.rht_inverse if inverse else o.rht
+    want = fn(xf.astype(np.float64), 7)
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.abs(got - want).max() <= 1e-6 * np.abs(want).max()
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_qjl_sketch_matches_oracle_and_encode(d):
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    rows = 50
+    rng = np.random.default_rng(d)
+    r = (0.2 * rng.standard_normal((rows, d))).astype(np.float32)
+    r[3] = 0.0
+    bits = torch.empty((rows, d // 32), dtype=torch.int32, device="cuda")
+    rn = torch.empty((rows,), dtype=torch.float16, device="cuda")
+    tq.tq_qjl_sketch(to_device(r, "f32"), 5, bits, rn)
+    torch.cuda.synchronize()
+    ref = o.qjl_sketch(r.astype(np.float64), 5)
+    got = o.unpack_signs(bits.cpu().numpy().view(np.uint8).reshape(rows, d // 8), d)
+    bnd = o.qjl_boundary_mask(ref["w"], ref["rnorm_exact"])
+    assert not ((got != ref["bits"]) & ~bnd).any()
+    gr = rn.float().cpu().numpy().astype(np.float64)
+    amb = o.norm_ambiguous(ref["rnorm_exact"], "f16")
+    assert not ((gr != ref["rnorm"]) & ~amb).any()
+    assert gr[3] == 0 and not got[3].any()
+
+    # encode with QJL == encode, form the residual, sketch it
+    w = si.small_workload(B=1, Hq=2, Hkv=1, d=d, N=40, qjl=True, qjl_seed=5, wid=125)
+    cfg, cache = gpu_encode(w)
+    _, _, fk, _ = kv_host(w, 0, w.N)
+    codes = o.unpack_codes(cache.kc.cpu().numpy(), w.bits_k, d)
+    norms = cache.kn.float().cpu().numpy().astype(np.float64)
+    res = o.rht(fk, 0) - o.dequant_rot(codes, norms, w.bits_k)
+    bits2 = torch.empty((w.N, d // 32), dtype=torch.int32, device="cuda")
+    rn2 = torch.empty((w.N,), dtype=torch.float16, device="cuda")
+    tq.tq_qjl_sketch(to_device(res.reshape(-1, d).astype(np.float32), "f32"), 5, bits2, rn2)
+    torch.cuda.synchronize()
+    a = o.unpack_signs(cache.kq.cpu().numpy().reshape(w.N, d // 8), d)
+    b = o.unpack_signs(bits2.cpu().numpy().view(np.uint8).reshape(w.N, d // 8), d)
+    wv = o.rht(res.reshape(-1, d), 5)
+    near = np.abs(wv) < 1e-5 * np.linalg.norm(res.reshape(-1, d), axis=-1, keepdims=True)
+    assert not ((a != b) & ~near).any()
+
+
+def test_dense_bf16_baseline_matches_fp64_attention():
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.small_workload(B=2, Hq=8, Hkv=2, N=900, wid=126)
+    rk, rv, fk, fv = kv_host(w, 0, w.N)
+    qraw, qf = si.queries(w)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    ws = tq.workspace(tq.tq_dense_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.N))
+    tq.tq_dense_decode_bf16(to_device(qraw, "bf16"), to_device(rk, "bf16"), to_device(rv, "bf16"),
+                            out, ws)
+    torch.cuda.synchronize()
+    G = w.G
+    want = np.zeros((w.B, w.Hq, w.d))
+    for b in range(w.B):
+        for h in range(w.Hq):
+            lg = fk[b, h // G] @ qf[b, h].astype(np.float64) / math.sqrt(w.d)
+            p = np.exp(lg - lg.max())
+            want[b, h] = (p / p.sum()) @ fv[b, h // G]
+    err, _ = rel_err(out.cpu().numpy().astype(np.float64), want)
+    assert err <= 1e-4
