@@ -91,10 +91,11 @@ int launch_qprep(int d, const QPrepArgs& a, hipStream_t st) {
 }
 
 int launch_merge(int d, const MergeArgs& a, hipStream_t st) {
+  const dim3 grid(unsigned(a.heads), unsigned(d / 32));
   if (d == 128)
-    hipLaunchKernelGGL(k_merge<128>, dim3(unsigned(a.heads)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_merge<128>, grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL(k_merge<256>, dim3(unsigned(a.heads)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(k_merge<256>, grid, dim3(256), 0, st, a);
   return last_launch();
 }
 
@@ -116,6 +117,8 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
   da.G = p.G;
   da.chunks = p.chunks;
   da.S = p.splits;
+  da.seed = seed;
+  (void)rotate;
   int st1 = launch_qprep(d, qa, st);
   if (st1 != TQ_OK) return st1;
   DecodeLauncher fn = decode_launcher(d, bk);
@@ -129,8 +132,6 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
   ma.out = out;
   ma.heads = int64_t(B) * Hq;
   ma.S = p.splits;
-  ma.rotate = rotate;
-  ma.seed = seed;
   return launch_merge(d, ma, st);
 }
 
@@ -251,6 +252,7 @@ int tq_attend_decode(const tq_config* cfg, const void* q, int q_dtype, int B, in
   qa.heads = int64_t(B) * Hq;
   qa.q_dtype = q_dtype;
   qa.rotate = 1;
+  qa.pairs = 1;
   qa.qjl = cfg->qjl;
   qa.mult = tau * dev::kLog2e;
   qa.seed = cfg->seed;

@@ -15,8 +15,24 @@ constexpr float kLog2e = 1.4426950408889634f;
 // become scalar (SMEM) loads into SGPRs. Only for data the kernel never
 // writes.
 typedef const __attribute__((address_space(4))) float* const_f32_ptr;
+typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
 __device__ __forceinline__ const_f32_ptr as_const(const float* p) {
   return (const_f32_ptr)(p);
+}
+__device__ __forceinline__ const_u32_ptr as_const(const uint32_t* p) {
+  return (const_u32_ptr)(p);
+}
+
+// Two fp16 values in one dword (low half first) and their dot product with
+// fp32 accumulation: v_dot2c_f32_f16.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
+                                c, false);
+}
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return uint32_t(__builtin_bit_cast(uint16_t, _Float16(lo))) |
+         (uint32_t(__builtin_bit_cast(uint16_t, _Float16(hi))) << 16);
 }
 
 // ---------------------------------------------------------------------------

@@ -100,6 +100,7 @@ static int finish_plan(int d, int B, int Hq, int Hkv, int64_t n_ctx, int splits,
     s = (2048 + units - 1) / units;
   }
   if (s > tiles) s = tiles;
+  if (s > kMaxSplitCount) s = kMaxSplitCount;
   if (s < 1) s = 1;
   const int64_t tiles_per_split = (tiles + s - 1) / s;
   p->tps = tiles_per_split * tile;

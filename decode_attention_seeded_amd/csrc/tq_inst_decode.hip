@@ -20,8 +20,13 @@ namespace tq {
 
 template <int BV, int GK, bool QJL>
 static int go(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+#if TQ_BK == 16
   hipLaunchKernelGGL((k_decode<TQ_D, TQ_BK, BV, GK, QJL>), grid, dim3(TQ_D / 32 * 64), 0, st,
                      a, a.qp, a.qq);
+#else
+  hipLaunchKernelGGL((k_decode_pk<TQ_D, TQ_BK, BV, GK, QJL>), grid, dim3(TQ_D / 32 * 64), 0,
+                     st, a, reinterpret_cast<const uint32_t*>(a.qp), a.qq);
+#endif
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 

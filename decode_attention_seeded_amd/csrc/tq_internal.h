@@ -10,6 +10,7 @@
 namespace tq {
 
 constexpr int kMaxLevels = 16;  // 2^4
+constexpr int kMaxSplitCount = 4096;  // split-K partials per query head
 
 // Codebook tables in the precisions the kernels consume.
 struct Codebook {

@@ -49,6 +49,7 @@ struct QPrepArgs {
   int64_t heads;
   int q_dtype;
   int rotate;             // 0: dense baseline, no rotation
+  int pairs;              // 1: write qp as fp16 pairs (packed decode)
   int qjl;
   float mult;             // scale * log2(e)
   uint64_t seed, qjl_seed;
@@ -72,6 +73,7 @@ struct DecodeArgs {
   float qjl_c;            // sqrt(pi / (2 d))
   float cbk[16];
   float cbv[16];
+  uint64_t seed;          // rotation seed: partials are rotated back (R^T)
 };
 
 struct MergeArgs {
@@ -80,8 +82,6 @@ struct MergeArgs {
   float* out;
   int64_t heads;
   int S;
-  int rotate;
-  uint64_t seed;
 };
 
 // ---------------------------------------------------------------------------
@@ -259,10 +259,22 @@ __global__ void __launch_bounds__(256) k_qprep(QPrepArgs a) {
   const float mult = a.rotate ? a.mult / sqrtf(float(D)) : a.mult;
 #pragma unroll
   for (int i = 0; i < E; ++i) v[i] *= mult;
-  float4* dst = reinterpret_cast<float4*>(a.qp + row * D + l16 * E);
+  if (a.pairs) {
+    // fp16 pairs (v_2m, v_2m+1), D/2 dwords per head
+    uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint32_t*>(a.qp) + row * (D / 2) +
+                                          l16 * (E / 2));
 #pragma unroll
-  for (int k = 0; k < E / 4; ++k)
-    dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    for (int k = 0; k < E / 8; ++k)
+      dst[k] = make_uint4(dev::pack_f16x2(v[8 * k], v[8 * k + 1]),
+                          dev::pack_f16x2(v[8 * k + 2], v[8 * k + 3]),
+                          dev::pack_f16x2(v[8 * k + 4], v[8 * k + 5]),
+                          dev::pack_f16x2(v[8 * k + 6], v[8 * k + 7]));
+  } else {
+    float4* dst = reinterpret_cast<float4*>(a.qp + row * D + l16 * E);
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k)
+      dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  }
   if (a.qjl) {
     const uint32_t qmask = dev::sign_mask(a.qjl_seed, l16 * E, E);
 #pragma unroll
@@ -524,20 +536,324 @@ k_decode(DecodeArgs a, const float* __restrict__ qp_all, const float* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Merge of split partials (exact log-sum-exp, fixed order), 1/l, inverse
-// rotation. One workgroup (256 threads) per query head.
+// Split-K decode over packed codes, pair tables and fp16 dot products.
+//
+// Same workgroup layout as k_decode. Differences:
+//   * the rotated query arrives as fp16 pairs (q_2m, q_2m+1) in dwords; a key
+//     pair index (two consecutive codes, 2*BK bits) selects an fp16 pair
+//     (c[code_2m], c[code_2m+1]) from an LDS table replicated RK times across
+//     banks, and one v_dot2c_f32_f16 per head adds both products into the
+//     fp32 score;
+//   * in the V phase a lane holds two tokens (t, t+64); the pair index
+//     (code_t | code_{t+64} << BV) of one coordinate selects
+//     (c[code_t], c[code_{t+64}]) and one dot2 with the fp16 weight pair
+//     (p_t, p_{t+64}) adds both tokens' contributions to the fp32 sum;
+//   * the running max is refreshed only when a tile's max exceeds it by more
+//     than 8 (log2 units), so weights stay <= 2^8 and the accumulators are
+//     rarely rescaled.
 // ---------------------------------------------------------------------------
+
+template <int D, int BK, int BV, int NP, bool QJL>
+struct PkTile {
+  uint32_t kw[D * BK / 32];        // this thread's key row (K phase token)
+  uint32_t kn, vn;                 // raw norm bits of that token
+  uint32_t sw[QJL ? D / 32 : 1];   // QJL sign words
+  uint32_t kr;                     // QJL residual norm (fp16 bits)
+  uint32_t X[NP][BV], Y[NP][BV];   // value slices of the V-phase token pairs
+};
+
+template <int D, int BK, int BV, int GK, bool QJL>
+__global__ void __launch_bounds__(D / 32 * 64)
+k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
+            const float* __restrict__ qq_all) {
+  constexpr int W = D / 32;
+  constexpr int T = W * 64;
+  constexpr int CW = 32;
+  constexpr int KREC = D * BK / 8;
+  constexpr int VREC = D * BV / 8;
+  constexpr int KW = D * BK / 32;              // dwords per key row
+  constexpr int VW = BV;                       // dwords per 32 value coordinates
+  constexpr int KE = 1 << (2 * BK);            // key pair-table entries
+  constexpr int VE = 1 << (2 * BV);            // value pair-table entries
+  constexpr int RK = (KE + VE) * 32 * 4 <= 48 * 1024 ? 32 : 16;   // replicas
+  constexpr int RSH = RK == 32 ? 5 : 4;
+  constexpr int NP = T / 128;                  // token pairs per lane (V phase)
+  constexpr float kRescale = 8.0f;
+  using Tile = PkTile<D, BK, BV, NP, QJL>;
+
+  __shared__ uint32_t lutk[KE * RK];
+  __shared__ uint32_t lutv[VE * RK];
+  __shared__ uint32_t pv2[(T / 2) * GK];
+  __shared__ float red[W * GK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int rl = lane & (RK - 1);
+  const int split = blockIdx.x;
+  const int unit = blockIdx.y;
+  const int chunk = unit % a.chunks;
+  const int bkv = unit / a.chunks;
+  const int b = bkv / a.Hkv;
+  const int kvh = bkv - b * a.Hkv;
+  const int h0 = kvh * a.G + chunk * GK;
+  const int64_t head0 = int64_t(b) * a.Hq + h0;
+
+  for (int i = tid; i < KE * RK; i += T) {
+    const int e = i >> RSH;
+    lutk[i] = dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
+  }
+  for (int i = tid; i < VE * RK; i += T) {
+    const int e = i >> RSH;
+    lutv[i] = dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
+  }
+
+  const int64_t t_begin = int64_t(split) * a.tps;
+  const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
+  const int64_t row0 = int64_t(bkv) * a.capacity;
+  const uint32_t* qp_base = qp2_all + head0 * (D / 2);
+  const float* qq_base = QJL ? qq_all + head0 * D : nullptr;
+  const bool nf16 = a.norm_f16 != 0;
+
+  // Issues every global load one tile needs; consumed one tile later.
+  auto load_tile = [&](int64_t base, Tile& t) {
+    const int64_t j = base + tid;
+    if (j < t_end) {
+      const uint32_t* kr_ = reinterpret_cast<const uint32_t*>(a.kc + (row0 + j) * KREC);
+      if constexpr (KW % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < KW / 4; ++k) {
+          const uint4 q4 = reinterpret_cast<const uint4*>(kr_)[k];
+          t.kw[4 * k] = q4.x; t.kw[4 * k + 1] = q4.y; t.kw[4 * k + 2] = q4.z;
+          t.kw[4 * k + 3] = q4.w;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < KW; ++k) t.kw[k] = kr_[k];
+      }
+      t.kn = nf16 ? uint32_t(static_cast<const uint16_t*>(a.kn)[row0 + j])
+                  : static_cast<const uint32_t*>(a.kn)[row0 + j];
+      t.vn = nf16 ? uint32_t(static_cast<const uint16_t*>(a.vn)[row0 + j])
+                  : static_cast<const uint32_t*>(a.vn)[row0 + j];
+      if constexpr (QJL) {
+        const uint4* qs = reinterpret_cast<const uint4*>(a.kq + (row0 + j) * (D / 32));
+#pragma unroll
+        for (int k = 0; k < D / 128; ++k) {
+          const uint4 q4 = qs[k];
+          t.sw[4 * k] = q4.x; t.sw[4 * k + 1] = q4.y; t.sw[4 * k + 2] = q4.z;
+          t.sw[4 * k + 3] = q4.w;
+        }
+        t.kr = a.kr[row0 + j];
+      }
+    }
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      const int64_t jj = base + pr * 128 + lane;
+      const uint32_t* sx = reinterpret_cast<const uint32_t*>(
+          a.vc + (row0 + jj) * VREC + wave * (CW * BV / 8));
+      const uint32_t* sy = sx + 64 * (VREC / 4);
+      const bool hx = jj < t_end, hy = jj + 64 < t_end;
+      if constexpr (VW % 4 == 0) {
+        uint4 x4 = make_uint4(0u, 0u, 0u, 0u), y4 = x4;
+        if (hx) x4 = reinterpret_cast<const uint4*>(sx)[0];
+        if (hy) y4 = reinterpret_cast<const uint4*>(sy)[0];
+        t.X[pr][0] = x4.x; t.X[pr][1] = x4.y; t.X[pr][2] = x4.z; t.X[pr][3] = x4.w;
+        t.Y[pr][0] = y4.x; t.Y[pr][1] = y4.y; t.Y[pr][2] = y4.z; t.Y[pr][3] = y4.w;
+      } else {
+#pragma unroll
+        for (int k = 0; k < VW; ++k) {
+          t.X[pr][k] = hx ? sx[k] : 0u;
+          t.Y[pr][k] = hy ? sy[k] : 0u;
+        }
+      }
+    }
+  };
+
+  float m_run[GK], lpart[GK];
+  float acc[GK][CW];
+#pragma unroll
+  for (int g = 0; g < GK; ++g) {
+    m_run[g] = -INFINITY;
+    lpart[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) acc[g][c] = 0.f;
+  }
+  // d = 128: the next tile's loads are issued before this tile's math
+  // (double buffer). d = 256 has no register room for that; the whole
+  // tile's loads are issued together at its start instead.
+  constexpr bool kDouble = (D == 128);
+  Tile cur, nxt;
+  if constexpr (kDouble) load_tile(t_begin, cur);
+  __syncthreads();
+
+  for (int64_t base = t_begin; base < t_end; base += T) {
+    if constexpr (kDouble) {
+      if (base + T < t_end) load_tile(base + T, nxt);
+    } else {
+      load_tile(base, cur);
+    }
+
+    const uint32_t* qpr = qp_base;
+    const float* qqr = qq_base;
+    asm volatile("" : "+s"(qpr));
+    if constexpr (QJL) asm volatile("" : "+s"(qqr));
+    const dev::const_u32_ptr qp = dev::as_const(qpr);
+
+    // ---------------- K phase: thread = token
+    const int64_t j = base + tid;
+    const bool valid = j < t_end;
+    float s[GK];
+#pragma unroll
+    for (int g = 0; g < GK; ++g) s[g] = 0.f;
+    float nv = 0.f;
+    if (valid) {
+#pragma unroll
+      for (int ch = 0; ch < D / 32; ++ch) {
+        const dev::const_u32_ptr qc = qp + ch * 16;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          const uint32_t cp = lutk[(dev::field<2 * BK>(cur.kw, ch * 16 + m) << RSH) | rl];
+#pragma unroll
+          for (int g = 0; g < GK; ++g) s[g] = dev::dot2(qc[g * (D / 2) + m], cp, s[g]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const float knrm = nf16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
+      const float ks = knrm * a.inv_sqrt_d;
+#pragma unroll
+      for (int g = 0; g < GK; ++g) s[g] *= ks;
+      nv = (nf16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn)) * a.inv_sqrt_d;
+      if constexpr (QJL) {
+        const dev::const_f32_ptr qq = dev::as_const(qqr);
+        float tq[GK];
+#pragma unroll
+        for (int g = 0; g < GK; ++g) tq[g] = 0.f;
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+          const bool neg = (cur.sw[i >> 5] >> (i & 31)) & 1u;
+#pragma unroll
+          for (int g = 0; g < GK; ++g) tq[g] += neg ? -qq[g * D + i] : qq[g * D + i];
+        }
+        const float rho = dev::f16_to_f32(cur.kr) * a.qjl_c;
+#pragma unroll
+        for (int g = 0; g < GK; ++g) s[g] = fmaf(rho, tq[g], s[g]);
+      }
+    }
+
+    // ---------------- online softmax, lazy rescale
+#pragma unroll
+    for (int g = 0; g < GK; ++g) {
+      const float mx = dev::wave_max(valid ? s[g] : -INFINITY);
+      if (lane == 0) red[wave * GK + g] = mx;
+    }
+    __syncthreads();
+    uint16_t* pv16 = reinterpret_cast<uint16_t*>(pv2);
+    const int pslot = ((tid >> 7) * 64 + (tid & 63)) * GK;
+    const int phalf = (tid >> 6) & 1;
+#pragma unroll
+    for (int g = 0; g < GK; ++g) {
+      float tmax = red[g];
+#pragma unroll
+      for (int w = 1; w < W; ++w) tmax = fmaxf(tmax, red[w * GK + g]);
+      if (tmax > m_run[g] + kRescale) {          // uniform across the workgroup
+        const float alpha = exp2f(m_run[g] - tmax);
+        m_run[g] = tmax;
+        lpart[g] *= alpha;
+#pragma unroll
+        for (int c = 0; c < CW; ++c) acc[g][c] *= alpha;
+      }
+      const float p = valid ? exp2f(s[g] - m_run[g]) : 0.f;
+      lpart[g] += p;
+      pv16[(pslot + g) * 2 + phalf] = __builtin_bit_cast(uint16_t, _Float16(p * nv));
+    }
+    __syncthreads();
+
+    // ---------------- V phase: wave owns 32 coordinates, lane = 2 tokens
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      if (base + pr * 128 + lane < t_end) {
+        uint32_t p2[GK];
+#pragma unroll
+        for (int g = 0; g < GK; ++g) p2[g] = pv2[(pr * 64 + lane) * GK + g];
+#pragma unroll
+        for (int c = 0; c < CW; ++c) {
+          const uint32_t idx = dev::field<BV>(cur.X[pr], c) |
+                               (dev::field<BV>(cur.Y[pr], c) << BV);
+          const uint32_t vp = lutv[(idx << RSH) | rl];
+#pragma unroll
+          for (int g = 0; g < GK; ++g) acc[g][c] = dev::dot2(p2[g], vp, acc[g][c]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    if constexpr (kDouble) cur = nxt;
+  }
+
+  // ---------------- epilogue: (max, sum) and R^T of the weighted sum
+#pragma unroll
+  for (int g = 0; g < GK; ++g) {
+    const float l = dev::wave_sum(lpart[g]);
+    if (lane == 0) red[wave * GK + g] = l;
+  }
+  constexpr int NV = GK * CW;
+  float flat[NV];
+#pragma unroll
+  for (int g = 0; g < GK; ++g)
+#pragma unroll
+    for (int c = 0; c < CW; ++c) flat[g * CW + c] = acc[g][c];
+  dev::wave_transpose_reduce<NV>(flat, lane);
+  // pv2 (D*GK dwords) is free now: stage the partial rows [GK][D] there
+  float* obuf = reinterpret_cast<float*>(pv2);
+#pragma unroll
+  for (int i = 0; i < dev::reduce_kept<NV>(); ++i) {
+    bool writer;
+    const int idx = dev::reduce_index<NV>(lane, i, &writer);
+    if (writer) obuf[(idx / CW) * D + wave * CW + idx % CW] = flat[i];
+  }
+  __syncthreads();
+  if (tid < GK) {
+    float l = 0.f;
+    for (int w = 0; w < W; ++w) l += red[w * GK + tid];
+    float* ml = a.ml + ((head0 + tid) * a.S + split) * 2;
+    ml[0] = m_run[tid];
+    ml[1] = l;
+  }
+  if (tid < 16 * GK) {
+    constexpr int E = D / 16;
+    const int g = tid >> 4, l16 = tid & 15;
+    float v[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = obuf[g * D + l16 * E + i];
+    dev::fwht16<E, float>(v, l16);
+    const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
+    const float nn = 1.0f / sqrtf(float(D));
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (smask >> i & 1) ? -v[i] * nn : v[i] * nn;
+    float4* dst = reinterpret_cast<float4*>(a.acc + ((head0 + g) * a.S + split) * D + l16 * E);
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k)
+      dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of split partials (exact log-sum-exp in a fixed order) and 1/l.
+// The partials are already in the original frame, so every coordinate is
+// independent: grid (query head, block of 32 coordinates), 256 threads =
+// 32 coordinates x 8 split groups.
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxSplits = 4096;
 
 template <int D>
 __global__ void __launch_bounds__(256) k_merge(MergeArgs a) {
-  constexpr int Q = D / 4;                 // float4 columns
-  constexpr int SG = 256 / Q;              // split groups
-  constexpr int E = D / 16;
+  __shared__ float wts[kMaxSplits];
   __shared__ float red[256];
-  __shared__ float4 part[SG][Q];
-  __shared__ float orot[D];
+  __shared__ float part[8][32];
   const int tid = threadIdx.x;
   const int64_t head = blockIdx.x;
+  const int cb = blockIdx.y;
   const float* ml = a.ml + head * a.S * 2;
 
   float mx = -INFINITY;
@@ -551,7 +867,11 @@ __global__ void __launch_bounds__(256) k_merge(MergeArgs a) {
   const float M = red[0];
   __syncthreads();
   float l = 0.f;
-  for (int s = tid; s < a.S; s += 256) l += ml[2 * s + 1] * exp2f(ml[2 * s] - M);
+  for (int s = tid; s < a.S; s += 256) {
+    const float w = exp2f(ml[2 * s] - M);
+    wts[s] = w;
+    l = fmaf(ml[2 * s + 1], w, l);
+  }
   red[tid] = l;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
@@ -560,41 +880,25 @@ __global__ void __launch_bounds__(256) k_merge(MergeArgs a) {
   }
   const float inv_l = 1.f / red[0];
 
-  const int q = tid % Q, sg = tid / Q;
-  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = sg; s < a.S; s += SG) {
-    const float w = exp2f(ml[2 * s] - M);
-    const float4 v = reinterpret_cast<const float4*>(a.acc + (head * a.S + s) * D)[q];
-    sum.x = fmaf(w, v.x, sum.x); sum.y = fmaf(w, v.y, sum.y);
-    sum.z = fmaf(w, v.z, sum.z); sum.w = fmaf(w, v.w, sum.w);
+  const int c = tid & 31, sg = tid >> 5;
+  const float* col = a.acc + head * int64_t(a.S) * D + cb * 32 + c;
+  float sum = 0.f;
+  int s = sg;
+  for (; s + 7 * 8 < a.S; s += 8 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = col[int64_t(s + 8 * u) * D];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum = fmaf(wts[s + 8 * u], v[u], sum);
   }
-  part[sg][q] = sum;
+  for (; s < a.S; s += 8) sum = fmaf(wts[s], col[int64_t(s) * D], sum);
+  part[sg][c] = sum;
   __syncthreads();
-  if (tid < Q) {
-    float4 t = part[0][tid];
-    for (int g = 1; g < SG; ++g) {
-      const float4 u = part[g][tid];
-      t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-    }
-    orot[4 * tid + 0] = t.x * inv_l; orot[4 * tid + 1] = t.y * inv_l;
-    orot[4 * tid + 2] = t.z * inv_l; orot[4 * tid + 3] = t.w * inv_l;
-  }
-  __syncthreads();
-  if (tid < 16) {
-    float v[E];
+  if (tid < 32) {
+    float t = part[0][tid];
 #pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = orot[tid * E + i];
-    if (a.rotate) {
-      dev::fwht16<E, float>(v, tid);
-      const uint32_t smask = dev::sign_mask(a.seed, tid * E, E);
-      const float nn = 1.0f / sqrtf(float(D));
-#pragma unroll
-      for (int i = 0; i < E; ++i) v[i] = (smask >> i & 1) ? -v[i] * nn : v[i] * nn;
-    }
-    float4* dst = reinterpret_cast<float4*>(a.out + head * D + tid * E);
-#pragma unroll
-    for (int k = 0; k < E / 4; ++k)
-      dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    for (int g = 1; g < 8; ++g) t += part[g][tid];
+    a.out[head * D + cb * 32 + tid] = t * inv_l;
   }
 }
 

@@ -79,7 +79,9 @@ def test_split_count_invariance_and_determinism():
         other = gpu_decode(w, cfg, cache, q, w.N, splits=s)
         err, _ = rel_err(other, base)
         log(f"splits={s}: rel diff vs 1 split {err:.2e}")
-        assert err <= 1e-5
+        # the weights enter the value sum as fp16, rounded relative to the
+        # running max, and the running max depends on where a split starts
+        assert err <= 1e-3
     again = gpu_decode(w, cfg, cache, q, w.N)
     assert np.array_equal(again, gpu_decode(w, cfg, cache, q, w.N))
 
