@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 namespace tq {
 namespace dev {
@@ -174,6 +175,82 @@ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[NW], int i) {
   uint32_t x = w[wi] >> sh;
   if (sh + BITS > 32) x |= w[wi + 1] << (32 - sh);
   return BITS == 32 ? x : (x & ((1u << BITS) - 1u));
+}
+
+// Field i (width BITS) of the bitstream w[], already shifted left by P
+// (result = field << P). Two VALU ops: one shift (or a funnel shift when the
+// field straddles two dwords) and the mask. Needs P <= 32 - BITS... the
+// straddling case needs the field to start at bit >= P of its dword.
+template <int BITS, int P, int NW>
+__device__ __forceinline__ uint32_t field_at(const uint32_t (&w)[NW], int i) {
+  const int bit = i * BITS;
+  const int wi = bit >> 5, sh = bit & 31;
+  uint32_t x;
+  if (sh + BITS > 32) {
+    x = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], uint32_t(sh - P));
+  } else if (sh >= P) {
+    x = w[wi] >> (sh - P);
+  } else {
+    x = w[wi] << (P - sh);
+  }
+  return x & (((1u << BITS) - 1u) << P);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// s[g] += dot2(q_g broadcast from lane L of every 16-lane row, c) for the
+// G accumulators: v_dot2c_f32_f16 with a DPP row_newbcast source, so the
+// query operand comes straight from a VGPR that only lane L of the row
+// holds. The leading s_nop covers the DPP read-after-VALU-write hazard,
+// which the compiler does not check inside inline assembly. EXEC must be
+// full when this runs.
+template <int L, int G>
+__device__ __forceinline__ void dot2_bcast(float (&s)[G], const uint32_t (&q)[G], uint32_t c) {
+  static_assert(G == 1 || G == 2 || G == 4, "G");
+  if constexpr (G == 1) {
+    asm("s_nop 1\n\t"
+        "v_dot2c_f32_f16_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(s[0]) : "v"(q[0]), "v"(c), "n"(L));
+  } else if constexpr (G == 2) {
+    asm("s_nop 1\n\t"
+        "v_dot2c_f32_f16_dpp %0, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %1, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
+        : "+v"(s[0]), "+v"(s[1]) : "v"(q[0]), "v"(q[1]), "v"(c), "n"(L));
+  } else {
+    asm("s_nop 1\n\t"
+        "v_dot2c_f32_f16_dpp %0, %4, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %1, %5, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %2, %6, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
+        "v_dot2c_f32_f16_dpp %3, %7, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf"
+        : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3])
+        : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(c), "n"(L));
+  }
+}
+
+// Wave-wide max with DPP row operations (quad swaps, half-row and row
+// mirrors, then row broadcasts); the result is taken from lane 63.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max_step(float x) {
+  const int o = __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL,
+                                            ROW_MASK, 0xF, false);
+  return fmaxf(x, __int_as_float(o));
+}
+
+__device__ __forceinline__ float dpp_wave_max(float v) {
+  v = dpp_max_step<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max_step<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max_step<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max_step<0x140, 0xF>(v);  // row_mirror
+  v = dpp_max_step<0x142, 0xA>(v);  // row_bcast:15
+  v = dpp_max_step<0x143, 0xC>(v);  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Stores `nbytes` low bytes of v at byte address p (alignment as stated).

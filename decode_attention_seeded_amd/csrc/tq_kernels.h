@@ -553,17 +553,21 @@ k_decode(DecodeArgs a, const float* __restrict__ qp_all, const float* __restrict
 //     rarely rescaled.
 // ---------------------------------------------------------------------------
 
-template <int D, int BK, int BV, int NP, bool QJL>
-struct PkTile {
+template <int D, int BK, bool QJL>
+struct PkKeys {
   uint32_t kw[D * BK / 32];        // this thread's key row (K phase token)
   uint32_t kn, vn;                 // raw norm bits of that token
   uint32_t sw[QJL ? D / 32 : 1];   // QJL sign words
   uint32_t kr;                     // QJL residual norm (fp16 bits)
+};
+
+template <int BV, int NP>
+struct PkVals {
   uint32_t X[NP][BV], Y[NP][BV];   // value slices of the V-phase token pairs
 };
 
 template <int D, int BK, int BV, int GK, bool QJL>
-__global__ void __launch_bounds__(D / 32 * 64)
+__global__ void __launch_bounds__(D / 32 * 64) __attribute__((amdgpu_waves_per_eu(2)))
 k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
             const float* __restrict__ qq_all) {
   constexpr int W = D / 32;
@@ -575,21 +579,29 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   constexpr int VW = BV;                       // dwords per 32 value coordinates
   constexpr int KE = 1 << (2 * BK);            // key pair-table entries
   constexpr int VE = 1 << (2 * BV);            // value pair-table entries
-  constexpr int RK = (KE + VE) * 32 * 4 <= 48 * 1024 ? 32 : 16;   // replicas
-  constexpr int RSH = RK == 32 ? 5 : 4;
+  // Key table: 32 copies of every entry, 128-byte entry stride, so that lane
+  // l reads copy (l & 31) and the 32 lanes of a half-wave hit 32 banks.
+  constexpr int KT_BYTES = KE * 128;
+  // Value table: 256-byte entry stride, 64 copies; the address of entry e
+  // for lane l is (e << 8) | 4l, which one v_perm_b32 assembles from the
+  // entry byte. Without room for it (QJL), 128-byte stride and 32 copies.
+  constexpr bool WIDE_V = !QJL && (KT_BYTES + VE * 256 <= 76 * 1024);
+  constexpr int VSH = WIDE_V ? 8 : 7;
+  constexpr int VT_BYTES = VE << VSH;
   constexpr int NP = T / 128;                  // token pairs per lane (V phase)
   constexpr float kRescale = 8.0f;
-  using Tile = PkTile<D, BK, BV, NP, QJL>;
+  using KTile = PkKeys<D, BK, QJL>;
+  using VTile = PkVals<BV, NP>;
 
-  __shared__ uint32_t lutk[KE * RK];
-  __shared__ uint32_t lutv[VE * RK];
+  __shared__ __attribute__((aligned(16))) uint8_t tabs[KT_BYTES + VT_BYTES];
   __shared__ uint32_t pv2[(T / 2) * GK];
   __shared__ float red[W * GK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rl = lane & (RK - 1);
+  const uint32_t rl4 = uint32_t(lane & 31) << 2;           // key-table copy
+  const uint32_t vl4 = uint32_t(WIDE_V ? lane : (lane & 31)) << 2;
   const int split = blockIdx.x;
   const int unit = blockIdx.y;
   const int chunk = unit % a.chunks;
@@ -599,24 +611,38 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   const int h0 = kvh * a.G + chunk * GK;
   const int64_t head0 = int64_t(b) * a.Hq + h0;
 
-  for (int i = tid; i < KE * RK; i += T) {
-    const int e = i >> RSH;
-    lutk[i] = dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
+  for (int i = tid; i < KE * 32; i += T) {
+    const int e = i >> 5;
+    *reinterpret_cast<uint32_t*>(tabs + (e << 7) + ((i & 31) << 2)) =
+        dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
   }
-  for (int i = tid; i < VE * RK; i += T) {
-    const int e = i >> RSH;
-    lutv[i] = dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
+  constexpr int VCOPIES = WIDE_V ? 64 : 32;
+  for (int i = tid; i < VE * VCOPIES; i += T) {
+    const int e = i / VCOPIES;
+    *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << VSH) + ((i % VCOPIES) << 2)) =
+        dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
   }
+  const uint8_t* vtab = tabs + KT_BYTES;
 
   const int64_t t_begin = int64_t(split) * a.tps;
   const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
   const int64_t row0 = int64_t(bkv) * a.capacity;
-  const uint32_t* qp_base = qp2_all + head0 * (D / 2);
   const float* qq_base = QJL ? qq_all + head0 * D : nullptr;
   const bool nf16 = a.norm_f16 != 0;
 
-  // Issues every global load one tile needs; consumed one tile later.
-  auto load_tile = [&](int64_t base, Tile& t) {
+  // The GK x D/2 rotated query pairs stay in VGPRs for the whole split:
+  // register r of lane l holds pair 16 r + (l & 15), so every 16-lane row
+  // has all of them and the K phase broadcasts one per dot2.
+  constexpr int NQR = GK * D / 32;
+  uint32_t vq[NQR];
+  {
+    const uint32_t* qsrc = qp2_all + head0 * (D / 2) + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < NQR; ++r) vq[r] = qsrc[16 * r];
+  }
+
+  // Global loads of one tile: key rows and norms (issued a tile ahead) ...
+  auto load_keys = [&](int64_t base, KTile& t) {
     const int64_t j = base + tid;
     if (j < t_end) {
       const uint32_t* kr_ = reinterpret_cast<const uint32_t*>(a.kc + (row0 + j) * KREC);
@@ -646,6 +672,10 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
         t.kr = a.kr[row0 + j];
       }
     }
+  };
+  // ... and value slices (issued at the start of their own tile, consumed
+  // after the K phase).
+  auto load_vals = [&](int64_t base, VTile& t) {
 #pragma unroll
     for (int pr = 0; pr < NP; ++pr) {
       const int64_t jj = base + pr * 128 + lane;
@@ -678,46 +708,37 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 #pragma unroll
     for (int c = 0; c < CW; ++c) acc[g][c] = 0.f;
   }
-  // d = 128: the next tile's loads are issued before this tile's math
-  // (double buffer). d = 256 has no register room for that; the whole
-  // tile's loads are issued together at its start instead.
-  constexpr bool kDouble = (D == 128);
-  Tile cur, nxt;
-  if constexpr (kDouble) load_tile(t_begin, cur);
-  __syncthreads();
 
-  for (int64_t base = t_begin; base < t_end; base += T) {
-    if constexpr (kDouble) {
-      if (base + T < t_end) load_tile(base + T, nxt);
-    } else {
-      load_tile(base, cur);
-    }
-
-    const uint32_t* qpr = qp_base;
+  // One tile of T tokens from registers `cur` (keys) and `vals`.
+  auto process = [&](int64_t base, const KTile& cur, const VTile& vals) {
     const float* qqr = qq_base;
-    asm volatile("" : "+s"(qpr));
     if constexpr (QJL) asm volatile("" : "+s"(qqr));
-    const dev::const_u32_ptr qp = dev::as_const(qpr);
 
-    // ---------------- K phase: thread = token
+    // ---------------- K phase: thread = token. Runs on every lane (EXEC
+    // full for the DPP broadcasts); lanes past the end are masked below.
     const int64_t j = base + tid;
     const bool valid = j < t_end;
     float s[GK];
 #pragma unroll
     for (int g = 0; g < GK; ++g) s[g] = 0.f;
     float nv = 0.f;
-    if (valid) {
+    {
 #pragma unroll
       for (int ch = 0; ch < D / 32; ++ch) {
-        const dev::const_u32_ptr qc = qp + ch * 16;
+        uint32_t qg[GK];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-          const uint32_t cp = lutk[(dev::field<2 * BK>(cur.kw, ch * 16 + m) << RSH) | rl];
-#pragma unroll
-          for (int g = 0; g < GK; ++g) s[g] = dev::dot2(qc[g * (D / 2) + m], cp, s[g]);
-        }
+        for (int g = 0; g < GK; ++g) qg[g] = vq[g * (D / 32) + ch];
+        dev::static_for<0, 16>([&](auto mc) {
+          constexpr int m = decltype(mc)::value;
+          const uint32_t ka = dev::field_at<2 * BK, 7>(cur.kw, ch * 16 + m) | rl4;
+          const uint32_t cp = *reinterpret_cast<const uint32_t*>(tabs + ka);
+          dev::dot2_bcast<m, GK>(s, qg, cp);
+          if constexpr (m == 7) __builtin_amdgcn_sched_barrier(0);
+        });
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    if (valid) {
       const float knrm = nf16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
       const float ks = knrm * a.inv_sqrt_d;
 #pragma unroll
@@ -743,7 +764,7 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     // ---------------- online softmax, lazy rescale
 #pragma unroll
     for (int g = 0; g < GK; ++g) {
-      const float mx = dev::wave_max(valid ? s[g] : -INFINITY);
+      const float mx = dev::dpp_wave_max(valid ? s[g] : -INFINITY);
       if (lane == 0) red[wave * GK + g] = mx;
     }
     __syncthreads();
@@ -775,19 +796,71 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
         uint32_t p2[GK];
 #pragma unroll
         for (int g = 0; g < GK; ++g) p2[g] = pv2[(pr * 64 + lane) * GK + g];
+        if constexpr (BV == 4) {
+          // byte b of lo/hi = (code of token t) | (code of token t+64) << 4
+          // for coordinate 8k + 2b (lo) and 8k + 2b + 1 (hi)
 #pragma unroll
-        for (int c = 0; c < CW; ++c) {
-          const uint32_t idx = dev::field<BV>(cur.X[pr], c) |
-                               (dev::field<BV>(cur.Y[pr], c) << BV);
-          const uint32_t vp = lutv[(idx << RSH) | rl];
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t x = vals.X[pr][k], y = vals.Y[pr][k];
+            const uint32_t lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
+            const uint32_t hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
 #pragma unroll
-          for (int g = 0; g < GK; ++g) acc[g][c] = dev::dot2(p2[g], vp, acc[g][c]);
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t word = (e & 1) ? hi : lo;
+              const int bsel = e >> 1;
+              uint32_t va;
+              if constexpr (WIDE_V) {
+                va = __builtin_amdgcn_perm(word, vl4, 0x0C0C0000u | uint32_t(4 + bsel) << 8);
+              } else {
+                va = ((bsel * 8 >= 7 ? (word >> (bsel * 8 - 7)) : (word << 7)) & 0x7F80u) | vl4;
+              }
+              const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
+              const int c = 8 * k + e;
+#pragma unroll
+              for (int g = 0; g < GK; ++g) acc[g][c] = dev::dot2(p2[g], vp, acc[g][c]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < CW; ++c) {
+            const uint32_t va = dev::field_at<BV, VSH>(vals.X[pr], c) |
+                                dev::field_at<BV, VSH + BV>(vals.Y[pr], c) | vl4;
+            const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
+#pragma unroll
+            for (int g = 0; g < GK; ++g) acc[g][c] = dev::dot2(p2[g], vp, acc[g][c]);
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-    if constexpr (kDouble) cur = nxt;
+  };
+
+  // d = 128: key rows are loaded one tile ahead into two alternating
+  // register buffers; d = 256 has no register room for that and loads its
+  // key rows at the tile start. Value slices always load at the tile start.
+  __syncthreads();
+  VTile vals;
+  if constexpr (D == 128) {
+    KTile ka, kb;
+    load_keys(t_begin, ka);
+    for (int64_t base = t_begin; base < t_end; base += 2 * T) {
+      load_vals(base, vals);
+      if (base + T < t_end) load_keys(base + T, kb);
+      process(base, ka, vals);
+      if (base + T >= t_end) break;
+      load_vals(base + T, vals);
+      if (base + 2 * T < t_end) load_keys(base + 2 * T, ka);
+      process(base + T, kb, vals);
+    }
+  } else {
+    KTile ka;
+    for (int64_t base = t_begin; base < t_end; base += T) {
+      load_keys(base, ka);
+      load_vals(base, vals);
+      process(base, ka, vals);
+    }
   }
 
   // ---------------- epilogue: (max, sum) and R^T of the weighted sum
