@@ -75,10 +75,12 @@ void fill_codebook_f64(int bits, double* thr, double* cen) {
   for (int k = 0; k < 16; ++k) cen[k] = k < L ? cb.c[k] : 0.0;
 }
 
-void fill_codebook_f32(int bits, float* cen) {
+// alpha * centroids for the fp16 decode tables; returns alpha.
+double fill_codebook_f32(int bits, float* cen) {
   const Codebook& cb = codebook(bits);
   const int L = 1 << bits;
-  for (int k = 0; k < 16; ++k) cen[k] = k < L ? float(cb.c[k]) : 0.f;
+  for (int k = 0; k < 16; ++k) cen[k] = k < L ? float(cb.alpha * cb.c[k]) : 0.f;
+  return cb.alpha;
 }
 
 int launch_qprep(int d, const QPrepArgs& a, hipStream_t st) {
@@ -270,8 +272,10 @@ int tq_attend_decode(const tq_config* cfg, const void* q, int q_dtype, int B, in
   da.norm_f16 = cfg->norm_dtype == TQ_F16;
   da.inv_sqrt_d = float(1.0 / std::sqrt(double(cfg->d)));
   da.qjl_c = float(std::sqrt(M_PI / (2.0 * cfg->d)));
-  fill_codebook_f32(cfg->bits_k, da.cbk);
-  fill_codebook_f32(cfg->bits_v, da.cbv);
+  const double ak = fill_codebook_f32(cfg->bits_k, da.cbk);
+  const double av = fill_codebook_f32(cfg->bits_v, da.cbv);
+  da.kscale = float(1.0 / (std::sqrt(double(cfg->d)) * ak));
+  da.vscale = float(1.0 / (std::sqrt(double(cfg->d)) * av));
   return run_decode(cfg->d, cfg->bits_k, cfg->bits_v, cfg->qjl, p, da, qa, B, Hq, cache->Hkv,
                     ws, out, 1, cfg->seed, stream);
 }

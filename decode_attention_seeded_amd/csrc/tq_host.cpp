@@ -53,6 +53,36 @@ Codebook build_codebook(int bits) {
   return cb;
 }
 
+// Nearest-even rounding of a positive double to binary16, returned as a
+// double (normal range only; the centroids here are in [0.1, 3]).
+double round_f16(double x) {
+  int e;
+  const double m = std::frexp(x, &e);          // x = m * 2^e, m in [0.5, 1)
+  const double scaled = std::ldexp(m, 11);     // 11 significant bits
+  return std::ldexp(std::nearbyint(scaled), e - 11);
+}
+
+// Scale alpha in [1, 2) (steps of 2^-20) minimizing the largest relative
+// fp16 rounding error of alpha * c over the positive centroids.
+void fit_alpha(Codebook& cb) {
+  const int m = 1 << (cb.bits - 1);
+  double best = 1e9, best_a = 1.0;
+  for (int i = 0; i < (1 << 20); ++i) {
+    const double a = 1.0 + std::ldexp(double(i), -20);
+    double worst = 0.0;
+    for (int k = 0; k < m && worst < best; ++k) {
+      const double v = a * cb.c[m + k];
+      worst = std::fmax(worst, std::fabs(round_f16(v) - v) / v);
+    }
+    if (worst < best) {
+      best = worst;
+      best_a = a;
+    }
+  }
+  cb.alpha = best_a;
+  cb.alpha_err = best;
+}
+
 std::once_flag g_once[5];
 Codebook g_cb[5];
 
@@ -61,7 +91,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
 const Codebook& codebook(int bits) {
-  std::call_once(g_once[bits], [bits] { g_cb[bits] = build_codebook(bits); });
+  std::call_once(g_once[bits], [bits] {
+    g_cb[bits] = build_codebook(bits);
+    fit_alpha(g_cb[bits]);
+  });
   return g_cb[bits];
 }
 

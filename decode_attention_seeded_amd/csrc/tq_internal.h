@@ -17,6 +17,11 @@ struct Codebook {
   int bits = 0;
   double c[kMaxLevels];      // ascending centroids
   double t[kMaxLevels - 1];  // thresholds
+  // Scale in [1, 2) that puts every alpha * c_k as close as possible to an
+  // fp16 value (decode tables hold fp16 alpha * c; 1/alpha is applied in
+  // fp32 with the row norm), and the residual max relative error.
+  double alpha = 1.0;
+  double alpha_err = 0.0;
 };
 
 // Lloyd-Max codebook for N(0,1), cached per bit width (thread-safe).

@@ -70,9 +70,11 @@ struct DecodeArgs {
   int Hkv, Hq, G, chunks, S;
   int norm_f16;
   float inv_sqrt_d;
+  float kscale;           // 1 / (sqrt(d) * alpha_k): fp32 part of the key scale
+  float vscale;           // 1 / (sqrt(d) * alpha_v)
   float qjl_c;            // sqrt(pi / (2 d))
-  float cbk[16];
-  float cbv[16];
+  float cbk[16];          // alpha_k * key centroids (exact in fp16 to ~1e-4)
+  float cbv[16];          // alpha_v * value centroids
   uint64_t seed;          // rotation seed: partials are rotated back (R^T)
 };
 
@@ -740,10 +742,10 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     }
     if (valid) {
       const float knrm = nf16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
-      const float ks = knrm * a.inv_sqrt_d;
+      const float ks = knrm * a.kscale;
 #pragma unroll
       for (int g = 0; g < GK; ++g) s[g] *= ks;
-      nv = (nf16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn)) * a.inv_sqrt_d;
+      nv = (nf16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn)) * a.vscale;
       if constexpr (QJL) {
         const dev::const_f32_ptr qq = dev::as_const(qqr);
         float tq[GK];
