@@ -75,7 +75,7 @@ def cpu_baseline(w, sample_tokens):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    n = min(sample_tokens, w.N)
+    n = min(sample_tokens, w.N) if sample_tokens > 0 else w.N
     A = min(w.append or 4096, n)
     _, fk = si.kv_rows(w, si.T_K, 0, 0, 0, n)
     _, fv = si.kv_rows(w, si.T_V, 0, 0, 0, n)
@@ -83,7 +83,9 @@ def cpu_baseline(w, sample_tokens):
     fv = fv.astype(np.float64)[None, None]
     kw = dict(seed=w.seed, bits_k=w.bits_k, bits_v=w.bits_v, norm_dtype=w.norm_dtype,
               qjl=w.qjl, qjl_seed=w.qjl_seed)
+    t0 = time.perf_counter()
     cache = o.encode_kv(fk, fv, **kw)                      # setup, untimed
+    t_setup = time.perf_counter() - t0
     t0 = time.perf_counter()
     o.encode_kv(fk[:, :, n - A:], fv[:, :, n - A:], **kw)  # the step's append
     t_enc = time.perf_counter() - t0
@@ -102,7 +104,8 @@ def cpu_baseline(w, sample_tokens):
         "kind": "oracle",
         "sample": (f"1 of {units} KV heads: {A}-token append encode ({t_enc:.2f} s) and "
                    f"decode of {w.G} query heads over {n} of {w.N} tokens ({t_dec:.2f} s), "
-                   f"scaled linearly to the full step ({step_s:.1f} s)"),
+                   f"scaled linearly to the full step ({step_s:.1f} s); encoding the "
+                   f"sample's cache first took {t_setup:.1f} s (not part of the step)"),
     }
 
 
@@ -114,7 +117,12 @@ def main():
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=131072)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
+                    help="context tokens of the CPU-oracle sample (0: the whole context "
+                         "of one KV head)")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="copy a buffer of this many MiB once before timing (a kernel of "
+                         "known traffic, for calibrating HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -175,6 +183,14 @@ def main():
         tq.tq_attend_decode(cfg, q, cache, w.N, out, ws)
         if dec_events:
             dec_events[1].record()
+
+    if args.copy_probe_mb:
+        src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"copy probe: {args.copy_probe_mb} MiB read + written")
 
     for _ in range(args.warmup):
         step()
