@@ -8,15 +8,15 @@
 
 namespace tq {
 
-using DecodeLauncher = int (*)(int, int, int, const DecodeArgs&, dim3, hipStream_t);
-int launch_decode_d128_k2(int, int, int, const DecodeArgs&, dim3, hipStream_t);
-int launch_decode_d128_k3(int, int, int, const DecodeArgs&, dim3, hipStream_t);
-int launch_decode_d128_k4(int, int, int, const DecodeArgs&, dim3, hipStream_t);
-int launch_decode_d128_k16(int, int, int, const DecodeArgs&, dim3, hipStream_t);
-int launch_decode_d256_k2(int, int, int, const DecodeArgs&, dim3, hipStream_t);
-int launch_decode_d256_k3(int, int, int, const DecodeArgs&, dim3, hipStream_t);
-int launch_decode_d256_k4(int, int, int, const DecodeArgs&, dim3, hipStream_t);
-int launch_decode_d256_k16(int, int, int, const DecodeArgs&, dim3, hipStream_t);
+using DecodeLauncher = int (*)(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d128_k2(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d128_k3(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d128_k4(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d128_k16(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d256_k2(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d256_k3(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d256_k4(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
+int launch_decode_d256_k16(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
 
 namespace {
 
@@ -126,7 +126,7 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
   DecodeLauncher fn = decode_launcher(d, bk);
   if (!fn) return TQ_ERR_UNSUPPORTED;
   dim3 grid(unsigned(p.splits), unsigned(int64_t(B) * Hkv * p.chunks));
-  st1 = fn(bv, p.gk, qjl, da, grid, st);
+  st1 = fn(bv, p.gk, qjl, p.wide, da, grid, st);
   if (st1 != TQ_OK) return st1;
   MergeArgs ma;
   ma.ml = da.ml;
@@ -242,7 +242,7 @@ int tq_attend_decode(const tq_config* cfg, const void* q, int q_dtype, int B, in
   if (!q || !out || !ws) return TQ_ERR_ARG;
   if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return TQ_ERR_ALIGN;
   DecodePlan p;
-  st = plan_decode(cfg->d, cfg->qjl, B, Hq, cache->Hkv, n_ctx, splits, &p);
+  st = plan_decode(cfg->d, cfg->bits_v, cfg->qjl, B, Hq, cache->Hkv, n_ctx, splits, &p);
   if (st != TQ_OK) return st;
   if (ws_bytes < p.total) return TQ_ERR_WORKSPACE;
   st = device_ready();

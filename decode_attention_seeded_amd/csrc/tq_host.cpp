@@ -120,17 +120,18 @@ int check_cache(const tq_config* cfg, const tq_cache* c) {
 
 static int decode_tile(int d) { return d == 128 ? 256 : 512; }
 
-static int finish_plan(int d, int B, int Hq, int Hkv, int64_t n_ctx, int splits,
-                       int units_per_kv, int tile, DecodePlan* p) {
+// Default split count: about `target` workgroups over the chip (256 CUs).
+// The wide kernel holds a whole compute unit per workgroup, so it aims at one
+// round of 256 workgroups; the narrow kernels at ~8 workgroups per CU.
+static int finish_plan(int64_t n_ctx, int splits, int64_t units, int tile, int64_t target,
+                       DecodePlan* p) {
   const int64_t tiles = (n_ctx + tile - 1) / tile;
   int64_t s;
   if (splits > 0) {
     s = splits;
   } else {
-    // aim for ~8 workgroups per compute unit on a 256-CU part
-    int64_t units = int64_t(B) * Hkv * units_per_kv;
     if (units < 1) units = 1;
-    s = (2048 + units - 1) / units;
+    s = (target + units - 1) / units;
   }
   if (s > tiles) s = tiles;
   if (s > kMaxSplitCount) s = kMaxSplitCount;
@@ -142,7 +143,7 @@ static int finish_plan(int d, int B, int Hq, int Hkv, int64_t n_ctx, int splits,
   return TQ_OK;
 }
 
-int plan_decode(int d, int qjl, int B, int Hq, int Hkv, int64_t n_ctx, int splits,
+int plan_decode(int d, int bits_v, int qjl, int B, int Hq, int Hkv, int64_t n_ctx, int splits,
                 DecodePlan* p) {
   if (!valid_d(d)) return TQ_ERR_UNSUPPORTED;
   if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || splits < 0) return TQ_ERR_ARG;
@@ -151,7 +152,12 @@ int plan_decode(int d, int qjl, int B, int Hq, int Hkv, int64_t n_ctx, int split
   p->G = Hq / Hkv;
   p->gk = (p->G % 4 == 0) ? 4 : (p->G % 2 == 0) ? 2 : 1;
   p->chunks = p->G / p->gk;
-  finish_plan(d, B, Hq, Hkv, n_ctx, splits, p->chunks, decode_tile(d), p);
+  p->wide = use_wide(d, bits_v, qjl) ? 1 : 0;
+  const int64_t units = int64_t(B) * Hkv * p->chunks;
+  if (p->wide)
+    finish_plan(n_ctx, splits, units, 512, 256, p);
+  else
+    finish_plan(n_ctx, splits, units, decode_tile(d), 2048, p);
   const size_t heads = size_t(B) * Hq;
   size_t off = 0;
   p->off_qp = off;  off = align256(off + heads * d * sizeof(float));
@@ -164,7 +170,7 @@ int plan_decode(int d, int qjl, int B, int Hq, int Hkv, int64_t n_ctx, int split
 
 int plan_dense(int d, int B, int Hq, int Hkv, int64_t n_ctx, int splits, DecodePlan* p) {
   // the dense baseline runs the same split-K skeleton with bf16 rows
-  return plan_decode(d, 0, B, Hq, Hkv, n_ctx, splits, p);
+  return plan_decode(d, 16, 0, B, Hq, Hkv, n_ctx, splits, p);
 }
 
 }  // namespace tq
@@ -247,7 +253,7 @@ int tq_num_splits(const tq_config* cfg, int B, int Hq, int Hkv, int64_t n_ctx, i
   int st = check_config(cfg);
   if (st != TQ_OK) return st;
   DecodePlan p;
-  st = plan_decode(cfg->d, cfg->qjl, B, Hq, Hkv, n_ctx, splits, &p);
+  st = plan_decode(cfg->d, cfg->bits_v, cfg->qjl, B, Hq, Hkv, n_ctx, splits, &p);
   return st != TQ_OK ? st : p.splits;
 }
 
@@ -256,7 +262,7 @@ int64_t tq_workspace_bytes(const tq_config* cfg, int B, int Hq, int Hkv, int64_t
   int st = check_config(cfg);
   if (st != TQ_OK) return st;
   DecodePlan p;
-  st = plan_decode(cfg->d, cfg->qjl, B, Hq, Hkv, n_ctx, splits, &p);
+  st = plan_decode(cfg->d, cfg->bits_v, cfg->qjl, B, Hq, Hkv, n_ctx, splits, &p);
   return st != TQ_OK ? st : int64_t(p.total);
 }
 

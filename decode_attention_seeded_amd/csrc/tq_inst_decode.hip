@@ -1,7 +1,7 @@
 // Instantiates the split-K decode kernel for one (D, key bits) pair, chosen
 // at compile time with -DTQ_D=... -DTQ_BK=... (BK = 16: dense bf16 baseline),
 // and exposes one launcher that dispatches over value bits, heads per
-// workgroup and QJL.
+// workgroup, QJL and the wide (8-wave) variant.
 #include "tq_internal.h"
 #include "tq_kernels.h"
 
@@ -19,11 +19,21 @@
 namespace tq {
 
 template <int BV, int GK, bool QJL>
-static int go(const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static int go(int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
 #if TQ_BK == 16
+  if (wide) return TQ_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((k_decode<TQ_D, TQ_BK, BV, GK, QJL>), grid, dim3(TQ_D / 32 * 64), 0, st,
                      a, a.qp, a.qq);
 #else
+  if constexpr (TQ_D == 128 && !QJL && (BV == 2 || BV == 4)) {
+    if (wide) {
+      hipLaunchKernelGGL((k_decode_wide<TQ_BK, BV, GK, QJL>), grid, dim3(512), 0, st, a,
+                         reinterpret_cast<const uint32_t*>(a.qp), a.qq);
+      return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+    }
+  } else {
+    if (wide) return TQ_ERR_UNSUPPORTED;
+  }
   hipLaunchKernelGGL((k_decode_pk<TQ_D, TQ_BK, BV, GK, QJL>), grid, dim3(TQ_D / 32 * 64), 0,
                      st, a, reinterpret_cast<const uint32_t*>(a.qp), a.qq);
 #endif
@@ -31,33 +41,34 @@ static int go(const DecodeArgs& a, dim3 grid, hipStream_t st) {
 }
 
 template <int BV, int GK>
-static int go_q(int qjl, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static int go_q(int qjl, int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
 #if TQ_BK == 16
   (void)qjl;
-  return go<BV, GK, false>(a, grid, st);
+  return go<BV, GK, false>(wide, a, grid, st);
 #else
-  return qjl ? go<BV, GK, true>(a, grid, st) : go<BV, GK, false>(a, grid, st);
+  return qjl ? go<BV, GK, true>(wide, a, grid, st) : go<BV, GK, false>(wide, a, grid, st);
 #endif
 }
 
 template <int BV>
-static int go_g(int gk, int qjl, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static int go_g(int gk, int qjl, int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
   switch (gk) {
-    case 1: return go_q<BV, 1>(qjl, a, grid, st);
-    case 2: return go_q<BV, 2>(qjl, a, grid, st);
-    case 4: return go_q<BV, 4>(qjl, a, grid, st);
+    case 1: return go_q<BV, 1>(qjl, wide, a, grid, st);
+    case 2: return go_q<BV, 2>(qjl, wide, a, grid, st);
+    case 4: return go_q<BV, 4>(qjl, wide, a, grid, st);
     default: return TQ_ERR_UNSUPPORTED;
   }
 }
 
-int TQ_LAUNCHER(int bv, int gk, int qjl, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+int TQ_LAUNCHER(int bv, int gk, int qjl, int wide, const DecodeArgs& a, dim3 grid,
+                hipStream_t st) {
 #if TQ_BK == 16
-  return bv == 16 ? go_g<16>(gk, 0, a, grid, st) : TQ_ERR_UNSUPPORTED;
+  return bv == 16 ? go_g<16>(gk, 0, wide, a, grid, st) : TQ_ERR_UNSUPPORTED;
 #else
   switch (bv) {
-    case 2: return go_g<2>(gk, qjl, a, grid, st);
-    case 3: return go_g<3>(gk, qjl, a, grid, st);
-    case 4: return go_g<4>(gk, qjl, a, grid, st);
+    case 2: return go_g<2>(gk, qjl, wide, a, grid, st);
+    case 3: return go_g<3>(gk, qjl, wide, a, grid, st);
+    case 4: return go_g<4>(gk, qjl, wide, a, grid, st);
     default: return TQ_ERR_UNSUPPORTED;
   }
 #endif

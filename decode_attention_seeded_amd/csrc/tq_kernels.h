@@ -913,6 +913,344 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 }
 
 // ---------------------------------------------------------------------------
+// Split-K decode, wide variant for d = 128 with 2- or 4-bit values (no QJL).
+//
+// 8 waves, 512-token tiles: in the K phase a thread is a token, in the V
+// phase wave w owns 16 coordinates and a lane holds 4 token pairs
+// (t, t+64). Meant to run one workgroup per compute unit over long splits:
+//   * key rows are loaded two tiles ahead into three register buffers (the
+//     tile loop is unrolled 3x, so no copies) and value slices one tile
+//     ahead, which keeps about 80-110 KB per compute unit in flight;
+//   * accumulators are GK x 16 fp32 per lane;
+//   * the softmax max is lazy: each wave votes whether any score exceeds the
+//     running max by more than 8 (log2 units); only then is a wave max
+//     taken. Weights are written with the old max and the tile pays one
+//     barrier; when a vote fired, all threads rescale, recompute the weights
+//     and pay one more barrier. Weight and vote buffers alternate between
+//     tiles, so no barrier is needed at the end of a tile.
+// ---------------------------------------------------------------------------
+
+template <int BK, bool QJL>
+struct WideKeys {
+  uint32_t kw[128 * BK / 32];
+  uint32_t kn, vn;
+};
+
+template <int BV>
+struct WideVals {
+  uint32_t X[4][BV / 2], Y[4][BV / 2];   // 16 coordinates x BV bits per slice
+};
+
+template <int BK, int BV, int GK, bool QJL>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
+              const float* __restrict__ qq_all) {
+  static_assert(BV == 2 || BV == 4, "wide decode: 2- or 4-bit values");
+  static_assert(!QJL, "wide decode: no QJL");
+  constexpr int D = 128;
+  constexpr int W = 8;
+  constexpr int T = 512;
+  constexpr int CW = 16;
+  constexpr int NP = 4;                        // token pairs per lane
+  constexpr int KREC = D * BK / 8;
+  constexpr int VREC = D * BV / 8;
+  constexpr int KW = D * BK / 32;
+  constexpr int VW = BV / 2;                   // dwords per 16-coordinate slice
+  constexpr int KE = 1 << (2 * BK);
+  constexpr int VE = 1 << (2 * BV);
+  constexpr int KT_BYTES = KE * 128;           // 32 copies, 128-B entry stride
+  constexpr int VT_BYTES = VE * 256;           // 64 copies, 256-B entry stride
+  constexpr float kRescale = 8.0f;
+  using KTile = WideKeys<BK, QJL>;
+  using VTile = WideVals<BV>;
+
+  __shared__ __attribute__((aligned(16))) uint8_t tabs[KT_BYTES + VT_BYTES];
+  __shared__ uint32_t pv2[2][(T / 2) * GK];
+  __shared__ __attribute__((aligned(16))) float red[2][W * GK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const uint32_t rl4 = uint32_t(lane & 31) << 2;
+  const uint32_t vl4 = uint32_t(lane) << 2;
+  const int split = blockIdx.x;
+  const int unit = blockIdx.y;
+  const int chunk = unit % a.chunks;
+  const int bkv = unit / a.chunks;
+  const int b = bkv / a.Hkv;
+  const int kvh = bkv - b * a.Hkv;
+  const int h0 = kvh * a.G + chunk * GK;
+  const int64_t head0 = int64_t(b) * a.Hq + h0;
+
+  for (int i = tid; i < KE * 32; i += T) {
+    const int e = i >> 5;
+    *reinterpret_cast<uint32_t*>(tabs + (e << 7) + ((i & 31) << 2)) =
+        dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
+  }
+  for (int i = tid; i < VE * 64; i += T) {
+    const int e = i >> 6;
+    *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << 8) + ((i & 63) << 2)) =
+        dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
+  }
+  const uint8_t* vtab = tabs + KT_BYTES;
+
+  const int64_t t_begin = int64_t(split) * a.tps;
+  const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
+  const int64_t row0 = int64_t(bkv) * a.capacity;
+  const bool nf16 = a.norm_f16 != 0;
+
+  constexpr int NQR = GK * D / 32;
+  uint32_t vq[NQR];
+  {
+    const uint32_t* qsrc = qp2_all + head0 * (D / 2) + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < NQR; ++r) vq[r] = qsrc[16 * r];
+  }
+
+  auto load_keys = [&](int64_t base, KTile& t) {
+    const int64_t j = base + tid;
+    if (j < t_end) {
+      const uint32_t* kr_ = reinterpret_cast<const uint32_t*>(a.kc + (row0 + j) * KREC);
+      if constexpr (KW % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < KW / 4; ++k) {
+          const uint4 q4 = reinterpret_cast<const uint4*>(kr_)[k];
+          t.kw[4 * k] = q4.x; t.kw[4 * k + 1] = q4.y; t.kw[4 * k + 2] = q4.z;
+          t.kw[4 * k + 3] = q4.w;
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < KW; ++k) t.kw[k] = kr_[k];
+      }
+      t.kn = nf16 ? uint32_t(static_cast<const uint16_t*>(a.kn)[row0 + j])
+                  : static_cast<const uint32_t*>(a.kn)[row0 + j];
+      t.vn = nf16 ? uint32_t(static_cast<const uint16_t*>(a.vn)[row0 + j])
+                  : static_cast<const uint32_t*>(a.vn)[row0 + j];
+    } else {
+      t.kn = 0u;    // rows past the split: finite norms, weight forced to 0 below
+      t.vn = 0u;
+    }
+  };
+  auto load_vals = [&](int64_t base, VTile& t) {
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      const int64_t jj = base + pr * 128 + lane;
+      const uint8_t* sx = a.vc + (row0 + jj) * VREC + wave * (CW * BV / 8);
+      const uint8_t* sy = sx + 64 * VREC;
+      const bool hx = jj < t_end, hy = jj + 64 < t_end;
+      if constexpr (VW == 2) {
+        uint2 x2 = make_uint2(0u, 0u), y2 = x2;
+        if (hx) x2 = *reinterpret_cast<const uint2*>(sx);
+        if (hy) y2 = *reinterpret_cast<const uint2*>(sy);
+        t.X[pr][0] = x2.x; t.X[pr][1] = x2.y;
+        t.Y[pr][0] = y2.x; t.Y[pr][1] = y2.y;
+      } else {
+        t.X[pr][0] = hx ? *reinterpret_cast<const uint32_t*>(sx) : 0u;
+        t.Y[pr][0] = hy ? *reinterpret_cast<const uint32_t*>(sy) : 0u;
+      }
+    }
+  };
+
+  float m_run[GK], lpart[GK];
+  float acc[GK][CW];
+#pragma unroll
+  for (int g = 0; g < GK; ++g) {
+    m_run[g] = -INFINITY;
+    lpart[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) acc[g][c] = 0.f;
+  }
+
+  auto process = [&](int64_t base, int buf, const KTile& cur, const VTile& vals) {
+    // ---------------- K phase: thread = token (EXEC full for the DPP)
+    const int64_t j = base + tid;
+    const bool valid = j < t_end;
+    float s[GK];
+#pragma unroll
+    for (int g = 0; g < GK; ++g) s[g] = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < D / 32; ++ch) {
+      uint32_t qg[GK];
+#pragma unroll
+      for (int g = 0; g < GK; ++g) qg[g] = vq[g * (D / 32) + ch];
+      dev::static_for<0, 16>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        const uint32_t ka = dev::field_at<2 * BK, 7>(cur.kw, ch * 16 + m) | rl4;
+        const uint32_t cp = *reinterpret_cast<const uint32_t*>(tabs + ka);
+        dev::dot2_bcast<m, GK>(s, qg, cp);
+        if constexpr (m == 7) __builtin_amdgcn_sched_barrier(0);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const float knrm = nf16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
+    const float ks = knrm * a.kscale;
+    const float nv = (nf16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn)) * a.vscale;
+#pragma unroll
+    for (int g = 0; g < GK; ++g) s[g] *= ks;
+
+    // ---------------- lazy softmax max: vote, optimistic weights
+#pragma unroll
+    for (int g = 0; g < GK; ++g) {
+      const bool ex = valid && (s[g] > m_run[g] + kRescale);
+      float wmax = -INFINITY;
+      if (__ballot(ex)) wmax = dev::dpp_wave_max(valid ? s[g] : -INFINITY);
+      if (lane == 0) red[buf][wave * GK + g] = wmax;
+    }
+    uint16_t* pv16 = reinterpret_cast<uint16_t*>(pv2[buf]);
+    const int pslot = ((tid >> 7) * 64 + (tid & 63)) * GK;
+    const int phalf = (tid >> 6) & 1;
+    float p[GK];
+#pragma unroll
+    for (int g = 0; g < GK; ++g) {
+      p[g] = valid ? exp2f(s[g] - m_run[g]) : 0.f;
+      pv16[(pslot + g) * 2 + phalf] =
+          valid ? __builtin_bit_cast(uint16_t, _Float16(p[g] * nv)) : uint16_t(0);
+    }
+    __syncthreads();
+    bool any = false;
+    float M[GK];
+#pragma unroll
+    for (int g = 0; g < GK; ++g) {
+      M[g] = red[buf][g];
+#pragma unroll
+      for (int w = 1; w < W; ++w) M[g] = fmaxf(M[g], red[buf][w * GK + g]);
+      any = any || (M[g] > -INFINITY);
+    }
+    if (any) {                                   // uniform across the workgroup
+#pragma unroll
+      for (int g = 0; g < GK; ++g) {
+        if (M[g] > -INFINITY) {
+          const float m_new = fmaxf(m_run[g], M[g]);
+          const float alpha = exp2f(m_run[g] - m_new);
+          m_run[g] = m_new;
+          lpart[g] *= alpha;
+#pragma unroll
+          for (int c = 0; c < CW; ++c) acc[g][c] *= alpha;
+        }
+        p[g] = valid ? exp2f(s[g] - m_run[g]) : 0.f;
+        pv16[(pslot + g) * 2 + phalf] =
+            valid ? __builtin_bit_cast(uint16_t, _Float16(p[g] * nv)) : uint16_t(0);
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int g = 0; g < GK; ++g) lpart[g] += p[g];
+
+    // ---------------- V phase: wave owns 16 coordinates, lane = 4 token pairs
+#pragma unroll
+    for (int pr = 0; pr < NP; ++pr) {
+      if (base + pr * 128 + lane < t_end) {
+        uint32_t p2[GK];
+#pragma unroll
+        for (int g = 0; g < GK; ++g) p2[g] = pv2[buf][(pr * 64 + lane) * GK + g];
+        if constexpr (BV == 4) {
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const uint32_t x = vals.X[pr][k], y = vals.Y[pr][k];
+            const uint32_t lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
+            const uint32_t hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t word = (e & 1) ? hi : lo;
+              const uint32_t va =
+                  __builtin_amdgcn_perm(word, vl4, 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8);
+              const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
+              const int c = 8 * k + e;
+#pragma unroll
+              for (int g = 0; g < GK; ++g) acc[g][c] = dev::dot2(p2[g], vp, acc[g][c]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < CW; ++c) {
+            const uint32_t va = dev::field_at<2, 8>(vals.X[pr], c) |
+                                dev::field_at<2, 10>(vals.Y[pr], c) | vl4;
+            const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
+#pragma unroll
+            for (int g = 0; g < GK; ++g) acc[g][c] = dev::dot2(p2[g], vp, acc[g][c]);
+            if (c == 7) __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // keys two tiles ahead in three rotating buffers (tile loop unrolled 3x),
+  // values one tile ahead
+  __syncthreads();
+  {
+    KTile ka, kb, kc;
+    VTile vnext;
+    load_keys(t_begin, ka);
+    load_vals(t_begin, vnext);
+    if (t_begin + T < t_end) load_keys(t_begin + T, kb);
+    int buf = 0;
+    auto step = [&](int64_t base, const KTile& cur, KTile& ahead2) {
+      if (base + 2 * T < t_end) load_keys(base + 2 * T, ahead2);
+      const VTile vcur = vnext;
+      if (base + T < t_end) load_vals(base + T, vnext);
+      process(base, buf, cur, vcur);
+      buf ^= 1;
+    };
+    for (int64_t base = t_begin; base < t_end; base += 3 * T) {
+      step(base, ka, kc);
+      if (base + T >= t_end) break;
+      step(base + T, kb, ka);
+      if (base + 2 * T >= t_end) break;
+      step(base + 2 * T, kc, kb);
+    }
+  }
+
+  // ---------------- epilogue: (max, sum) and R^T of the weighted sum
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < GK; ++g) {
+    const float l = dev::wave_sum(lpart[g]);
+    if (lane == 0) red[0][wave * GK + g] = l;
+  }
+  constexpr int NV = GK * CW;
+  float flat[NV];
+#pragma unroll
+  for (int g = 0; g < GK; ++g)
+#pragma unroll
+    for (int c = 0; c < CW; ++c) flat[g * CW + c] = acc[g][c];
+  dev::wave_transpose_reduce<NV>(flat, lane);
+  float* obuf = reinterpret_cast<float*>(pv2[0]);   // GK x D floats fit in one buffer
+#pragma unroll
+  for (int i = 0; i < dev::reduce_kept<NV>(); ++i) {
+    bool writer;
+    const int idx = dev::reduce_index<NV>(lane, i, &writer);
+    if (writer) obuf[(idx / CW) * D + wave * CW + idx % CW] = flat[i];
+  }
+  __syncthreads();
+  if (tid < GK) {
+    float l = 0.f;
+    for (int w = 0; w < W; ++w) l += red[0][w * GK + tid];
+    float* ml = a.ml + ((head0 + tid) * a.S + split) * 2;
+    ml[0] = m_run[tid];
+    ml[1] = l;
+  }
+  if (tid < 16 * GK) {
+    constexpr int E = D / 16;
+    const int g = tid >> 4, l16 = tid & 15;
+    float v[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = obuf[g * D + l16 * E + i];
+    dev::fwht16<E, float>(v, l16);
+    const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
+    const float nn = 1.0f / sqrtf(float(D));
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (smask >> i & 1) ? -v[i] * nn : v[i] * nn;
+    float4* dst = reinterpret_cast<float4*>(a.acc + ((head0 + g) * a.S + split) * D + l16 * E);
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k)
+      dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge of split partials (exact log-sum-exp in a fixed order) and 1/l.
 // The partials are already in the original frame, so every coordinate is
 // independent: grid (query head, block of 32 coordinates), 256 threads =

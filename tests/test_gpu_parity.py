@@ -86,6 +86,15 @@ def test_split_count_invariance_and_determinism():
     assert np.array_equal(again, gpu_decode(w, cfg, cache, q, w.N))
 
 
+@pytest.mark.parametrize("splits,scale", [(1, 0.0), (3, 0.0), (1, 0.35), (2, 0.35)])
+def test_many_tiles_per_split(splits, scale):
+    """Long splits (up to 10 tiles of 512 tokens in one workgroup, every
+    rotation of the prefetch buffers, ragged tail) against the oracle; scale
+    0.35 widens the score range ~4x so the running max is raised often."""
+    _run_case(si.small_workload(B=1, Hq=4, Hkv=1, N=5037, bits_k=3, bits_v=4,
+                                structure="correlated", wid=127), scale=scale, splits=splits)
+
+
 def test_append_chunks_equal_bulk_encode():
     """Encoding as several appends writes the same planes as one encode."""
     torch = torch_cuda()
