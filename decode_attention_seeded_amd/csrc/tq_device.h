@@ -196,6 +196,13 @@ __device__ __forceinline__ uint32_t field_at(const uint32_t (&w)[NW], int i) {
   return x & (((1u << BITS) - 1u) << P);
 }
 
+// Raw buffer descriptor over [p, p + bytes): loads at byte offsets past the
+// range return zero without touching memory (stride 0, 32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), short(0), int(bytes),
+                                           0x00020000);
+}
+
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {

@@ -913,64 +913,81 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 }
 
 // ---------------------------------------------------------------------------
-// Split-K decode, wide variant for d = 128 with 2- or 4-bit values (no QJL).
-//
-// 8 waves, 512-token tiles: in the K phase a thread is a token, in the V
-// phase wave w owns 16 coordinates and a lane holds 4 token pairs
-// (t, t+64). Meant to run one workgroup per compute unit over long splits:
-//   * key rows are loaded two tiles ahead into three register buffers (the
-//     tile loop is unrolled 3x, so no copies) and value slices one tile
-//     ahead, which keeps about 80-110 KB per compute unit in flight;
-//   * accumulators are GK x 16 fp32 per lane;
-//   * the softmax max is lazy: each wave votes whether any score exceeds the
-//     running max by more than 8 (log2 units); only then is a wave max
-//     taken. Weights are written with the old max and the tile pays one
-//     barrier; when a vote fired, all threads rescale, recompute the weights
-//     and pay one more barrier. Weight and vote buffers alternate between
-//     tiles, so no barrier is needed at the end of a tile.
+// Split-K decode, wave-private variant for d = 128 with 2- or 4-bit values
+// (no QJL). One workgroup of 8 waves holds a compute unit and shares the
+// codebook pair tables in LDS; each wave runs its own online-softmax pass
+// over interleaved 64-token tiles of the split (wave w takes tiles w, w+8,
+// ...), so the tile loop has no workgroup barrier. The waves' partial
+// results are combined once, at the end of the split.
+//   K phase: lane = token; the key row is in VGPRs, each coordinate pair is
+//            one LDS pair-table lookup feeding GK DPP-broadcast dot2s.
+//   V phase: lane = (row class q = lane & 7, coordinate slice d = lane >> 3):
+//            the lane holds rows 16k+q and 16k+q+8 (k = 0..3) of its 16
+//            coordinates, so each lookup yields a (token, token) value pair
+//            for one coordinate, weighted by the matching fp16 weight pair.
+//            Weights move from the K layout to the V layout through a
+//            wave-private LDS slot.
+//   Loads: key rows, norms and value slices of a tile are fetched two tiles
+//          ahead into three register buffers used in rotation (tile loop
+//          unrolled 3x), through buffer descriptors whose range ends at the
+//          split's last token (rows past it read as zero).
+//   Softmax: the running max is raised only when some lane's score exceeds
+//            it by more than 8 (log2 units): then a DPP wave max, a rescale
+//            of that head's accumulators, and the weights use the new max.
 // ---------------------------------------------------------------------------
 
-template <int BK, bool QJL>
-struct WideKeys {
-  uint32_t kw[128 * BK / 32];
-  uint32_t kn, vn;
+template <int BK, int BV>
+struct WvTile {
+  uint32_t kw[128 * BK / 32];   // key row of the lane's token
+  uint32_t kn[2], vn[2];        // its key and value norms as 16-bit halves
+  uint32_t vx[8][BV / 2];       // value slices: row 8i+q, coordinates 16d..16d+15
 };
 
-template <int BV>
-struct WideVals {
-  uint32_t X[4][BV / 2], Y[4][BV / 2];   // 16 coordinates x BV bits per slice
-};
+// Spreads the eight 2-bit fields of the low 16 bits of x to the low two bits
+// of eight nibbles.
+__device__ __forceinline__ uint32_t spread2to4(uint32_t x) {
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  return x;
+}
 
 template <int BK, int BV, int GK, bool QJL>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
               const float* __restrict__ qq_all) {
-  static_assert(BV == 2 || BV == 4, "wide decode: 2- or 4-bit values");
-  static_assert(!QJL, "wide decode: no QJL");
+  static_assert(BV == 2 || BV == 4, "wave-private decode: 2- or 4-bit values");
+  static_assert(!QJL, "wave-private decode: no QJL");
   constexpr int D = 128;
-  constexpr int W = 8;
-  constexpr int T = 512;
-  constexpr int CW = 16;
-  constexpr int NP = 4;                        // token pairs per lane
+  constexpr int W = 8;                         // waves per workgroup
+  constexpr int TW = 64;                       // tokens per wave tile
+  constexpr int T = W * TW;                    // tokens per workgroup round
   constexpr int KREC = D * BK / 8;
   constexpr int VREC = D * BV / 8;
   constexpr int KW = D * BK / 32;
-  constexpr int VW = BV / 2;                   // dwords per 16-coordinate slice
   constexpr int KE = 1 << (2 * BK);
   constexpr int VE = 1 << (2 * BV);
   constexpr int KT_BYTES = KE * 128;           // 32 copies, 128-B entry stride
   constexpr int VT_BYTES = VE * 256;           // 64 copies, 256-B entry stride
+  constexpr int PX = TW / 2 * GK;              // weight pairs per wave tile
   constexpr float kRescale = 8.0f;
-  using KTile = WideKeys<BK, QJL>;
-  using VTile = WideVals<BV>;
+  using Tile = WvTile<BK, BV>;
+  static_assert(KW % 4 == 0, "key rows are whole 16-byte loads");
 
-  __shared__ __attribute__((aligned(16))) uint8_t tabs[KT_BYTES + VT_BYTES];
-  __shared__ uint32_t pv2[2][(T / 2) * GK];
-  __shared__ __attribute__((aligned(16))) float red[2][W * GK];
+  constexpr int SLAB_BYTES = W * GK * D * 4;   // per-wave partials, after the loop
+  constexpr int TAB_BYTES = KT_BYTES + VT_BYTES;
+  __shared__ __attribute__((aligned(16)))
+  uint8_t tabs[TAB_BYTES > SLAB_BYTES ? TAB_BYTES : SLAB_BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t pex[W][3][PX];
+  __shared__ uint32_t qs[GK * (D / 2)];
+  __shared__ float mlx[W][GK][2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave index as a scalar, so tile bases and buffer descriptors stay in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane & 7;
+  const int dsl = lane >> 3;
   const uint32_t rl4 = uint32_t(lane & 31) << 2;
   const uint32_t vl4 = uint32_t(lane) << 2;
   const int split = blockIdx.x;
@@ -993,78 +1010,74 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
         dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
   }
   const uint8_t* vtab = tabs + KT_BYTES;
+  // query fp16 pairs of the GK heads; each K-phase chunk reads its 16 pairs
+  // per head into VGPRs for the DPP broadcast
+  if (tid < GK * (D / 2)) qs[tid] = qp2_all[head0 * (D / 2) + tid];
+  const uint32_t* qrow = qs + (lane & 15);
 
   const int64_t t_begin = int64_t(split) * a.tps;
   const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
   const int64_t row0 = int64_t(bkv) * a.capacity;
   const bool nf16 = a.norm_f16 != 0;
+  const int nb = nf16 ? 2 : 4;
+  const int iters = int((t_end - t_begin + T - 1) / T);
 
-  constexpr int NQR = GK * D / 32;
-  uint32_t vq[NQR];
-  {
-    const uint32_t* qsrc = qp2_all + head0 * (D / 2) + (lane & 15);
-#pragma unroll
-    for (int r = 0; r < NQR; ++r) vq[r] = qsrc[16 * r];
-  }
-
-  auto load_keys = [&](int64_t base, KTile& t) {
-    const int64_t j = base + tid;
-    if (j < t_end) {
-      const uint32_t* kr_ = reinterpret_cast<const uint32_t*>(a.kc + (row0 + j) * KREC);
-      if constexpr (KW % 4 == 0) {
-#pragma unroll
-        for (int k = 0; k < KW / 4; ++k) {
-          const uint4 q4 = reinterpret_cast<const uint4*>(kr_)[k];
-          t.kw[4 * k] = q4.x; t.kw[4 * k + 1] = q4.y; t.kw[4 * k + 2] = q4.z;
-          t.kw[4 * k + 3] = q4.w;
-        }
-      } else {
-#pragma unroll
-        for (int k = 0; k < KW; ++k) t.kw[k] = kr_[k];
-      }
-      t.kn = nf16 ? uint32_t(static_cast<const uint16_t*>(a.kn)[row0 + j])
-                  : static_cast<const uint32_t*>(a.kn)[row0 + j];
-      t.vn = nf16 ? uint32_t(static_cast<const uint16_t*>(a.vn)[row0 + j])
-                  : static_cast<const uint32_t*>(a.vn)[row0 + j];
-    } else {
-      t.kn = 0u;    // rows past the split: finite norms, weight forced to 0 below
-      t.vn = 0u;
-    }
+  auto rows_left = [&](int64_t base) -> uint32_t {
+    const int64_t n = t_end - base;
+    return uint32_t(n <= 0 ? 0 : (n < TW ? n : TW));
   };
-  auto load_vals = [&](int64_t base, VTile& t) {
+  // voffsets: the lane's key row, its norms, and its value slices (row q,
+  // coordinates 16*dsl..16*dsl+15). Norms are read as two 16-bit halves; the
+  // high half's descriptor is empty for f16 norms, so the load count per
+  // tile does not depend on the norm type.
+  const uint32_t ko0 = uint32_t(lane) * KREC;
+  const uint32_t no_lo0 = nf16 ? uint32_t(lane) * 2 : uint32_t(lane) * 4;
+  const uint32_t no_hi0 = uint32_t(lane) * 4 + 2;
+  const uint32_t vo0 = uint32_t(q) * VREC + uint32_t(dsl) * (2 * BV);
+  // per-load constants go in the scalar offset operand, so they cost neither
+  // VALU work nor loop-invariant VGPRs
+  auto load = [&](int64_t base, Tile& t) {
+    const uint32_t n = rows_left(base);
+    const auto rk = dev::buffer_rsrc(a.kc + (row0 + base) * KREC, n * KREC);
 #pragma unroll
-    for (int pr = 0; pr < NP; ++pr) {
-      const int64_t jj = base + pr * 128 + lane;
-      const uint8_t* sx = a.vc + (row0 + jj) * VREC + wave * (CW * BV / 8);
-      const uint8_t* sy = sx + 64 * VREC;
-      const bool hx = jj < t_end, hy = jj + 64 < t_end;
-      if constexpr (VW == 2) {
-        uint2 x2 = make_uint2(0u, 0u), y2 = x2;
-        if (hx) x2 = *reinterpret_cast<const uint2*>(sx);
-        if (hy) y2 = *reinterpret_cast<const uint2*>(sy);
-        t.X[pr][0] = x2.x; t.X[pr][1] = x2.y;
-        t.Y[pr][0] = y2.x; t.Y[pr][1] = y2.y;
+    for (int k = 0; k < KW / 4; ++k) {
+      const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rk, ko0, 16 * k, 0);
+      t.kw[4 * k] = q4[0]; t.kw[4 * k + 1] = q4[1]; t.kw[4 * k + 2] = q4[2];
+      t.kw[4 * k + 3] = q4[3];
+    }
+    const uint8_t* kn_p = static_cast<const uint8_t*>(a.kn) + (row0 + base) * nb;
+    const uint8_t* vn_p = static_cast<const uint8_t*>(a.vn) + (row0 + base) * nb;
+    const uint32_t nbytes = n * nb, hbytes = nf16 ? 0u : nbytes;
+    t.kn[0] = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(kn_p, nbytes), no_lo0, 0, 0);
+    t.kn[1] = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(kn_p, hbytes), no_hi0, 0, 0);
+    t.vn[0] = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(vn_p, nbytes), no_lo0, 0, 0);
+    t.vn[1] = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(vn_p, hbytes), no_hi0, 0, 0);
+    const auto rv = dev::buffer_rsrc(a.vc + (row0 + base) * VREC, n * VREC);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (BV == 4) {
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rv, vo0, i * 8 * VREC, 0);
+        t.vx[i][0] = v2[0];
+        t.vx[i][1] = v2[1];
       } else {
-        t.X[pr][0] = hx ? *reinterpret_cast<const uint32_t*>(sx) : 0u;
-        t.Y[pr][0] = hy ? *reinterpret_cast<const uint32_t*>(sy) : 0u;
+        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo0, i * 8 * VREC, 0);
       }
     }
   };
 
   float m_run[GK], lpart[GK];
-  float acc[GK][CW];
+  float acc[GK][16];
 #pragma unroll
   for (int g = 0; g < GK; ++g) {
     m_run[g] = -INFINITY;
     lpart[g] = 0.f;
 #pragma unroll
-    for (int c = 0; c < CW; ++c) acc[g][c] = 0.f;
+    for (int c = 0; c < 16; ++c) acc[g][c] = 0.f;
   }
 
-  auto process = [&](int64_t base, int buf, const KTile& cur, const VTile& vals) {
-    // ---------------- K phase: thread = token (EXEC full for the DPP)
-    const int64_t j = base + tid;
-    const bool valid = j < t_end;
+  auto process = [&](int64_t base, uint32_t* px, const Tile& cur) {
+    // ---------------- K phase: lane = token (EXEC full for the DPP)
+    const bool valid = base + lane < t_end;
     float s[GK];
 #pragma unroll
     for (int g = 0; g < GK; ++g) s[g] = 0.f;
@@ -1072,7 +1085,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     for (int ch = 0; ch < D / 32; ++ch) {
       uint32_t qg[GK];
 #pragma unroll
-      for (int g = 0; g < GK; ++g) qg[g] = vq[g * (D / 32) + ch];
+      for (int g = 0; g < GK; ++g) qg[g] = qrow[g * (D / 2) + ch * 16];
       dev::static_for<0, 16>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         const uint32_t ka = dev::field_at<2 * BK, 7>(cur.kw, ch * 16 + m) | rl4;
@@ -1082,154 +1095,159 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
       });
       __builtin_amdgcn_sched_barrier(0);
     }
-    const float knrm = nf16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
+    const uint32_t kn32 = cur.kn[0] | (cur.kn[1] << 16);
+    const uint32_t vn32 = cur.vn[0] | (cur.vn[1] << 16);
+    const float knrm = nf16 ? dev::f16_to_f32(kn32) : __uint_as_float(kn32);
+    const float vnrm = nf16 ? dev::f16_to_f32(vn32) : __uint_as_float(vn32);
     const float ks = knrm * a.kscale;
-    const float nv = (nf16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn)) * a.vscale;
-#pragma unroll
-    for (int g = 0; g < GK; ++g) s[g] *= ks;
+    const float nv = vnrm * a.vscale;
 
-    // ---------------- lazy softmax max: vote, optimistic weights
+    // ---------------- online softmax with a lazily raised running max
+    uint16_t* p16 = reinterpret_cast<uint16_t*>(px);
+    const int pslot = (((lane >> 4) * 8 + (lane & 7)) * GK) * 2 + ((lane >> 3) & 1);
 #pragma unroll
     for (int g = 0; g < GK; ++g) {
-      const bool ex = valid && (s[g] > m_run[g] + kRescale);
-      float wmax = -INFINITY;
-      if (__ballot(ex)) wmax = dev::dpp_wave_max(valid ? s[g] : -INFINITY);
-      if (lane == 0) red[buf][wave * GK + g] = wmax;
-    }
-    uint16_t* pv16 = reinterpret_cast<uint16_t*>(pv2[buf]);
-    const int pslot = ((tid >> 7) * 64 + (tid & 63)) * GK;
-    const int phalf = (tid >> 6) & 1;
-    float p[GK];
+      s[g] *= ks;
+      if (__ballot(valid && s[g] > m_run[g] + kRescale)) {     // wave-uniform
+        const float mx = dev::dpp_wave_max(valid ? s[g] : -INFINITY);
+        const float m_new = fmaxf(m_run[g], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+        m_run[g] = m_new;
+        lpart[g] *= alpha;
 #pragma unroll
-    for (int g = 0; g < GK; ++g) {
-      p[g] = valid ? exp2f(s[g] - m_run[g]) : 0.f;
-      pv16[(pslot + g) * 2 + phalf] =
-          valid ? __builtin_bit_cast(uint16_t, _Float16(p[g] * nv)) : uint16_t(0);
-    }
-    __syncthreads();
-    bool any = false;
-    float M[GK];
-#pragma unroll
-    for (int g = 0; g < GK; ++g) {
-      M[g] = red[buf][g];
-#pragma unroll
-      for (int w = 1; w < W; ++w) M[g] = fmaxf(M[g], red[buf][w * GK + g]);
-      any = any || (M[g] > -INFINITY);
-    }
-    if (any) {                                   // uniform across the workgroup
-#pragma unroll
-      for (int g = 0; g < GK; ++g) {
-        if (M[g] > -INFINITY) {
-          const float m_new = fmaxf(m_run[g], M[g]);
-          const float alpha = exp2f(m_run[g] - m_new);
-          m_run[g] = m_new;
-          lpart[g] *= alpha;
-#pragma unroll
-          for (int c = 0; c < CW; ++c) acc[g][c] *= alpha;
-        }
-        p[g] = valid ? exp2f(s[g] - m_run[g]) : 0.f;
-        pv16[(pslot + g) * 2 + phalf] =
-            valid ? __builtin_bit_cast(uint16_t, _Float16(p[g] * nv)) : uint16_t(0);
+        for (int c = 0; c < 16; ++c) acc[g][c] *= alpha;
       }
-      __syncthreads();
+      // branch-free: rows past the split have s = 0 and zero norms
+      const float e = __builtin_amdgcn_exp2f(s[g] - m_run[g]);
+      const float p = valid ? e : 0.f;
+      lpart[g] += p;
+      p16[pslot + 2 * g] = __builtin_bit_cast(uint16_t, _Float16(p * nv));
     }
-#pragma unroll
-    for (int g = 0; g < GK; ++g) lpart[g] += p[g];
+    // the weights written above are read back by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---------------- V phase: wave owns 16 coordinates, lane = 4 token pairs
+    // ---------------- V phase: lane = (row class q, coordinate slice dsl)
 #pragma unroll
-    for (int pr = 0; pr < NP; ++pr) {
-      if (base + pr * 128 + lane < t_end) {
-        uint32_t p2[GK];
+    for (int k = 0; k < 4; ++k) {
+      uint32_t p2[GK];
+      const uint32_t* pp = px + (k * 8 + q) * GK;
+      if constexpr (GK == 4) {
+        const uint4 v4 = *reinterpret_cast<const uint4*>(pp);
+        p2[0] = v4.x; p2[1] = v4.y; p2[2] = v4.z; p2[3] = v4.w;
+      } else if constexpr (GK == 2) {
+        const uint2 v2 = *reinterpret_cast<const uint2*>(pp);
+        p2[0] = v2.x; p2[1] = v2.y;
+      } else {
+        p2[0] = pp[0];
+      }
 #pragma unroll
-        for (int g = 0; g < GK; ++g) p2[g] = pv2[buf][(pr * 64 + lane) * GK + g];
+      for (int hw = 0; hw < 2; ++hw) {        // coordinates 8hw..8hw+7 of the slice
+        uint32_t lo, hi;  // byte b: (x code, y code) of coordinate 2b (lo), 2b+1 (hi)
         if constexpr (BV == 4) {
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const uint32_t x = vals.X[pr][k], y = vals.Y[pr][k];
-            const uint32_t lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
-            const uint32_t hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t word = (e & 1) ? hi : lo;
-              const uint32_t va =
-                  __builtin_amdgcn_perm(word, vl4, 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8);
-              const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
-              const int c = 8 * k + e;
-#pragma unroll
-              for (int g = 0; g < GK; ++g) acc[g][c] = dev::dot2(p2[g], vp, acc[g][c]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
+          const uint32_t x = cur.vx[2 * k][hw], y = cur.vx[2 * k + 1][hw];
+          lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
+          hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
         } else {
-#pragma unroll
-          for (int c = 0; c < CW; ++c) {
-            const uint32_t va = dev::field_at<2, 8>(vals.X[pr], c) |
-                                dev::field_at<2, 10>(vals.Y[pr], c) | vl4;
-            const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
-#pragma unroll
-            for (int g = 0; g < GK; ++g) acc[g][c] = dev::dot2(p2[g], vp, acc[g][c]);
-            if (c == 7) __builtin_amdgcn_sched_barrier(0);
-          }
+          const uint32_t x = cur.vx[2 * k][0] >> (16 * hw), y = cur.vx[2 * k + 1][0] >> (16 * hw);
+          const uint32_t w = spread2to4(x & 0xFFFFu) | (spread2to4(y & 0xFFFFu) << 2);
+          lo = w & 0x0F0F0F0Fu;
+          hi = (w >> 4) & 0x0F0F0F0Fu;
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = (e & 1) ? hi : lo;
+          const uint32_t va =
+              __builtin_amdgcn_perm(word, vl4, 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8);
+          const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
+#pragma unroll
+          for (int g = 0; g < GK; ++g)
+            acc[g][8 * hw + e] = dev::dot2(p2[g], vp, acc[g][8 * hw + e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // keys two tiles ahead in three rotating buffers (tile loop unrolled 3x),
-  // values one tile ahead
+  // two tiles ahead in three rotating buffers; all waves run `iters` rounds
+  // (tiles past the split read as zero and carry zero weight)
   __syncthreads();
   {
-    KTile ka, kb, kc;
-    VTile vnext;
-    load_keys(t_begin, ka);
-    load_vals(t_begin, vnext);
-    if (t_begin + T < t_end) load_keys(t_begin + T, kb);
-    int buf = 0;
-    auto step = [&](int64_t base, const KTile& cur, KTile& ahead2) {
-      if (base + 2 * T < t_end) load_keys(base + 2 * T, ahead2);
-      const VTile vcur = vnext;
-      if (base + T < t_end) load_vals(base + T, vnext);
-      process(base, buf, cur, vcur);
-      buf ^= 1;
-    };
-    for (int64_t base = t_begin; base < t_end; base += 3 * T) {
-      step(base, ka, kc);
-      if (base + T >= t_end) break;
-      step(base + T, kb, ka);
-      if (base + 2 * T >= t_end) break;
-      step(base + 2 * T, kc, kb);
+    Tile ta, tb, tc;
+    const int64_t wb = t_begin + int64_t(wave) * TW;
+    // issue order matters: the loop's waits count loads issued after ta
+    load(wb, ta);
+    __builtin_amdgcn_sched_barrier(0);
+    load(wb + T, tb);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t* px0 = pex[wave][0];
+    uint32_t* px1 = pex[wave][1];
+    uint32_t* px2 = pex[wave][2];
+    for (int it = 0; it < iters; it += 3) {
+      const int64_t base = wb + int64_t(it) * T;
+      load(base + 2 * T, tc);
+      process(base, px0, ta);
+      if (it + 1 >= iters) break;
+      load(base + 3 * T, ta);
+      process(base + T, px1, tb);
+      if (it + 2 >= iters) break;
+      load(base + 4 * T, tb);
+      process(base + 2 * T, px2, tc);
     }
   }
 
-  // ---------------- epilogue: (max, sum) and R^T of the weighted sum
-  __syncthreads();
+  // ---------------- combine the waves, then R^T of the weighted sum
+  float lw[GK];
 #pragma unroll
   for (int g = 0; g < GK; ++g) {
-    const float l = dev::wave_sum(lpart[g]);
-    if (lane == 0) red[0][wave * GK + g] = l;
+    lw[g] = dev::wave_sum(lpart[g]);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      acc[g][c] += __shfl_xor(acc[g][c], 1);
+      acc[g][c] += __shfl_xor(acc[g][c], 2);
+      acc[g][c] += __shfl_xor(acc[g][c], 4);
+    }
   }
-  constexpr int NV = GK * CW;
-  float flat[NV];
+  __syncthreads();                       // tables are dead: reuse them below
+  if (lane == 0) {
 #pragma unroll
-  for (int g = 0; g < GK; ++g)
+    for (int g = 0; g < GK; ++g) {
+      mlx[wave][g][0] = m_run[g];
+      mlx[wave][g][1] = lw[g];
+    }
+  }
+  __syncthreads();
+  float* slab = reinterpret_cast<float*>(tabs);          // [W][GK][D]
+  float M[GK];
 #pragma unroll
-    for (int c = 0; c < CW; ++c) flat[g * CW + c] = acc[g][c];
-  dev::wave_transpose_reduce<NV>(flat, lane);
-  float* obuf = reinterpret_cast<float*>(pv2[0]);   // GK x D floats fit in one buffer
+  for (int g = 0; g < GK; ++g) {
+    M[g] = mlx[0][g][0];
 #pragma unroll
-  for (int i = 0; i < dev::reduce_kept<NV>(); ++i) {
-    bool writer;
-    const int idx = dev::reduce_index<NV>(lane, i, &writer);
-    if (writer) obuf[(idx / CW) * D + wave * CW + idx % CW] = flat[i];
+    for (int w = 1; w < W; ++w) M[g] = fmaxf(M[g], mlx[w][g][0]);
+    const float f = m_run[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - M[g]);
+    if (q == 0) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) slab[(wave * GK + g) * D + dsl * 16 + c] = acc[g][c] * f;
+    }
+  }
+  __syncthreads();
+  float* obuf = reinterpret_cast<float*>(pex);            // [GK][D]
+  if (tid < GK * D) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) sum += slab[w * GK * D + tid];
+    obuf[tid] = sum;
   }
   __syncthreads();
   if (tid < GK) {
     float l = 0.f;
-    for (int w = 0; w < W; ++w) l += red[0][w * GK + tid];
+    for (int w = 0; w < W; ++w) {
+      const float mw = mlx[w][tid][0];
+      if (mw != -INFINITY) l += mlx[w][tid][1] * __builtin_amdgcn_exp2f(mw - M[tid]);
+    }
     float* ml = a.ml + ((head0 + tid) * a.S + split) * 2;
-    ml[0] = m_run[tid];
+    ml[0] = M[tid];
     ml[1] = l;
   }
   if (tid < 16 * GK) {
