@@ -27,7 +27,7 @@ static int go(int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
 #else
   if constexpr (TQ_D == 128 && !QJL && (BV == 2 || BV == 4)) {
     if (wide) {
-      hipLaunchKernelGGL((k_decode_wide<TQ_BK, BV, GK, QJL>), grid, dim3(512), 0, st, a,
+      hipLaunchKernelGGL((k_decode_wide<TQ_BK, BV, GK, QJL>), grid, dim3(64 * kWideWaves), 0, st, a,
                          reinterpret_cast<const uint32_t*>(a.qp), a.qq);
       return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
     }

@@ -58,11 +58,15 @@ inline int norm_bytes(const tq_config* cfg) { return cfg->norm_dtype == TQ_F16 ?
 //   tps:    tokens per split (multiple of tile)
 struct DecodePlan {
   int G = 0, gk = 0, chunks = 0, tile = 0, splits = 0;
-  int wide = 0;      // 1: the 8-wave, 512-token-tile kernel (d 128, 2/4-bit values, no QJL)
+  int wide = 0;      // 1: the wave-private wide kernel (d 128, 2/4-bit values, no QJL)
   int64_t tps = 0;
   // workspace section offsets (bytes)
   size_t off_qp = 0, off_qq = 0, off_ml = 0, off_acc = 0, total = 0;
 };
+
+// Waves per workgroup of the wide kernel; one workgroup round covers
+// 64 * kWideWaves tokens.
+constexpr int kWideWaves = 12;
 
 // Whether the packed decode runs the wide kernel for this format.
 inline bool use_wide(int d, int bits_v, int qjl) {

@@ -914,23 +914,23 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 
 // ---------------------------------------------------------------------------
 // Split-K decode, wave-private variant for d = 128 with 2- or 4-bit values
-// (no QJL). One workgroup of 8 waves holds a compute unit and shares the
-// codebook pair tables in LDS; each wave runs its own online-softmax pass
-// over interleaved 64-token tiles of the split (wave w takes tiles w, w+8,
-// ...), so the tile loop has no workgroup barrier. The waves' partial
-// results are combined once, at the end of the split.
+// (no QJL). One workgroup of kWideWaves (12) waves holds a compute unit (3
+// waves per SIMD) and shares the codebook pair tables in LDS; each wave runs
+// its own online-softmax pass over interleaved 64-token tiles of the split
+// (wave w takes tiles w, w+12, ...), so the tile loop has no workgroup
+// barrier. The waves' partial results are combined once, at the end.
 //   K phase: lane = token; the key row is in VGPRs, each coordinate pair is
 //            one LDS pair-table lookup feeding GK DPP-broadcast dot2s.
-//   V phase: lane = (row class q = lane & 7, coordinate slice d = lane >> 3):
-//            the lane holds rows 16k+q and 16k+q+8 (k = 0..3) of its 16
+//   V phase: lane = (row class q = lane & 3, coordinate slice d = lane >> 2):
+//            the lane holds rows 8k+q and 8k+q+4 (k = 0..7) of its 8
 //            coordinates, so each lookup yields a (token, token) value pair
 //            for one coordinate, weighted by the matching fp16 weight pair.
 //            Weights move from the K layout to the V layout through a
 //            wave-private LDS slot.
-//   Loads: key rows, norms and value slices of a tile are fetched two tiles
-//          ahead into three register buffers used in rotation (tile loop
-//          unrolled 3x), through buffer descriptors whose range ends at the
-//          split's last token (rows past it read as zero).
+//   Loads: key rows, norms and value slices of the next tile are fetched
+//          while the current one is processed (two register buffers, tile
+//          loop unrolled 2x), through buffer descriptors whose range ends at
+//          the split's last token (rows past it read as zero).
 //   Softmax: the running max is raised only when some lane's score exceeds
 //            it by more than 8 (log2 units): then a DPP wave max, a rescale
 //            of that head's accumulators, and the weights use the new max.
@@ -940,7 +940,7 @@ template <int BK, int BV>
 struct WvTile {
   uint32_t kw[128 * BK / 32];   // key row of the lane's token
   uint32_t kn[2], vn[2];        // its key and value norms as 16-bit halves
-  uint32_t vx[8][BV / 2];       // value slices: row 8i+q, coordinates 16d..16d+15
+  uint32_t vx[16];              // value slices: row 4i+q, coordinates 8d..8d+7
 };
 
 // Spreads the eight 2-bit fields of the low 16 bits of x to the low two bits
@@ -953,15 +953,17 @@ __device__ __forceinline__ uint32_t spread2to4(uint32_t x) {
 }
 
 template <int BK, int BV, int GK, bool QJL>
-__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64 * kWideWaves)
+    __attribute__((amdgpu_waves_per_eu(kWideWaves / 4)))
 k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
               const float* __restrict__ qq_all) {
   static_assert(BV == 2 || BV == 4, "wave-private decode: 2- or 4-bit values");
   static_assert(!QJL, "wave-private decode: no QJL");
   constexpr int D = 128;
-  constexpr int W = 8;                         // waves per workgroup
+  constexpr int W = kWideWaves;                // waves per workgroup
   constexpr int TW = 64;                       // tokens per wave tile
   constexpr int T = W * TW;                    // tokens per workgroup round
+  constexpr int NT = 64 * W;                   // threads
   constexpr int KREC = D * BK / 8;
   constexpr int VREC = D * BV / 8;
   constexpr int KW = D * BK / 32;
@@ -978,7 +980,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   constexpr int TAB_BYTES = KT_BYTES + VT_BYTES;
   __shared__ __attribute__((aligned(16)))
   uint8_t tabs[TAB_BYTES > SLAB_BYTES ? TAB_BYTES : SLAB_BYTES];
-  __shared__ __attribute__((aligned(16))) uint32_t pex[W][3][PX];
+  __shared__ __attribute__((aligned(16))) uint32_t pex[W][2][PX];
   __shared__ uint32_t qs[GK * (D / 2)];
   __shared__ float mlx[W][GK][2];
 
@@ -986,8 +988,8 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   const int lane = tid & 63;
   // wave index as a scalar, so tile bases and buffer descriptors stay in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int q = lane & 7;
-  const int dsl = lane >> 3;
+  const int q = lane & 3;
+  const int dsl = lane >> 2;
   const uint32_t rl4 = uint32_t(lane & 31) << 2;
   const uint32_t vl4 = uint32_t(lane) << 2;
   const int split = blockIdx.x;
@@ -999,12 +1001,12 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   const int h0 = kvh * a.G + chunk * GK;
   const int64_t head0 = int64_t(b) * a.Hq + h0;
 
-  for (int i = tid; i < KE * 32; i += T) {
+  for (int i = tid; i < KE * 32; i += NT) {
     const int e = i >> 5;
     *reinterpret_cast<uint32_t*>(tabs + (e << 7) + ((i & 31) << 2)) =
         dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
   }
-  for (int i = tid; i < VE * 64; i += T) {
+  for (int i = tid; i < VE * 64; i += NT) {
     const int e = i >> 6;
     *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << 8) + ((i & 63) << 2)) =
         dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
@@ -1027,13 +1029,13 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     return uint32_t(n <= 0 ? 0 : (n < TW ? n : TW));
   };
   // voffsets: the lane's key row, its norms, and its value slices (row q,
-  // coordinates 16*dsl..16*dsl+15). Norms are read as two 16-bit halves; the
+  // coordinates 8*dsl..8*dsl+7). Norms are read as two 16-bit halves; the
   // high half's descriptor is empty for f16 norms, so the load count per
   // tile does not depend on the norm type.
   const uint32_t ko0 = uint32_t(lane) * KREC;
   const uint32_t no_lo0 = nf16 ? uint32_t(lane) * 2 : uint32_t(lane) * 4;
   const uint32_t no_hi0 = uint32_t(lane) * 4 + 2;
-  const uint32_t vo0 = uint32_t(q) * VREC + uint32_t(dsl) * (2 * BV);
+  const uint32_t vo0 = uint32_t(q) * VREC + uint32_t(dsl) * BV;
   // per-load constants go in the scalar offset operand, so they cost neither
   // VALU work nor loop-invariant VGPRs
   auto load = [&](int64_t base, Tile& t) {
@@ -1054,25 +1056,22 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     t.vn[1] = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(vn_p, hbytes), no_hi0, 0, 0);
     const auto rv = dev::buffer_rsrc(a.vc + (row0 + base) * VREC, n * VREC);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if constexpr (BV == 4) {
-        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rv, vo0, i * 8 * VREC, 0);
-        t.vx[i][0] = v2[0];
-        t.vx[i][1] = v2[1];
-      } else {
-        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo0, i * 8 * VREC, 0);
-      }
+    for (int i = 0; i < 16; ++i) {
+      if constexpr (BV == 4)
+        t.vx[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo0, i * 4 * VREC, 0);
+      else
+        t.vx[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, vo0, i * 4 * VREC, 0);
     }
   };
 
   float m_run[GK], lpart[GK];
-  float acc[GK][16];
+  float acc[GK][8];
 #pragma unroll
   for (int g = 0; g < GK; ++g) {
     m_run[g] = -INFINITY;
     lpart[g] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) acc[g][c] = 0.f;
+    for (int c = 0; c < 8; ++c) acc[g][c] = 0.f;
   }
 
   auto process = [&](int64_t base, uint32_t* px, const Tile& cur) {
@@ -1104,7 +1103,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 
     // ---------------- online softmax with a lazily raised running max
     uint16_t* p16 = reinterpret_cast<uint16_t*>(px);
-    const int pslot = (((lane >> 4) * 8 + (lane & 7)) * GK) * 2 + ((lane >> 3) & 1);
+    const int pslot = (((lane >> 3) * 4 + (lane & 3)) * GK) * 2 + ((lane >> 2) & 1);
 #pragma unroll
     for (int g = 0; g < GK; ++g) {
       s[g] *= ks;
@@ -1115,7 +1114,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
         m_run[g] = m_new;
         lpart[g] *= alpha;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) acc[g][c] *= alpha;
+        for (int c = 0; c < 8; ++c) acc[g][c] *= alpha;
       }
       // branch-free: rows past the split have s = 0 and zero norms
       const float e = __builtin_amdgcn_exp2f(s[g] - m_run[g]);
@@ -1130,9 +1129,9 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 
     // ---------------- V phase: lane = (row class q, coordinate slice dsl)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 8; ++k) {
       uint32_t p2[GK];
-      const uint32_t* pp = px + (k * 8 + q) * GK;
+      const uint32_t* pp = px + (k * 4 + q) * GK;
       if constexpr (GK == 4) {
         const uint4 v4 = *reinterpret_cast<const uint4*>(pp);
         p2[0] = v4.x; p2[1] = v4.y; p2[2] = v4.z; p2[3] = v4.w;
@@ -1142,58 +1141,46 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
       } else {
         p2[0] = pp[0];
       }
-#pragma unroll
-      for (int hw = 0; hw < 2; ++hw) {        // coordinates 8hw..8hw+7 of the slice
-        uint32_t lo, hi;  // byte b: (x code, y code) of coordinate 2b (lo), 2b+1 (hi)
-        if constexpr (BV == 4) {
-          const uint32_t x = cur.vx[2 * k][hw], y = cur.vx[2 * k + 1][hw];
-          lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
-          hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
-        } else {
-          const uint32_t x = cur.vx[2 * k][0] >> (16 * hw), y = cur.vx[2 * k + 1][0] >> (16 * hw);
-          const uint32_t w = spread2to4(x & 0xFFFFu) | (spread2to4(y & 0xFFFFu) << 2);
-          lo = w & 0x0F0F0F0Fu;
-          hi = (w >> 4) & 0x0F0F0F0Fu;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t word = (e & 1) ? hi : lo;
-          const uint32_t va =
-              __builtin_amdgcn_perm(word, vl4, 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8);
-          const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
-#pragma unroll
-          for (int g = 0; g < GK; ++g)
-            acc[g][8 * hw + e] = dev::dot2(p2[g], vp, acc[g][8 * hw + e]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      const uint32_t x = cur.vx[2 * k], y = cur.vx[2 * k + 1];   // rows 8k+q, 8k+q+4
+      uint32_t lo, hi;      // byte b: (x code, y code) of coordinate 2b (lo), 2b+1 (hi)
+      if constexpr (BV == 4) {
+        lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
+        hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
+      } else {
+        const uint32_t w = spread2to4(x) | (spread2to4(y) << 2);   // nibble c: coord c
+        lo = w & 0x0F0F0F0Fu;
+        hi = (w >> 4) & 0x0F0F0F0Fu;
       }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t word = (e & 1) ? hi : lo;
+        const uint32_t va =
+            __builtin_amdgcn_perm(word, vl4, 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8);
+        const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
+#pragma unroll
+        for (int g = 0; g < GK; ++g) acc[g][e] = dev::dot2(p2[g], vp, acc[g][e]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // two tiles ahead in three rotating buffers; all waves run `iters` rounds
-  // (tiles past the split read as zero and carry zero weight)
+  // the next tile is loaded while the current one is processed; all waves
+  // run `iters` rounds (tiles past the split read as zero, zero weight)
   __syncthreads();
   {
-    Tile ta, tb, tc;
+    Tile ta, tb;
     const int64_t wb = t_begin + int64_t(wave) * TW;
-    // issue order matters: the loop's waits count loads issued after ta
     load(wb, ta);
-    __builtin_amdgcn_sched_barrier(0);
-    load(wb + T, tb);
     __builtin_amdgcn_sched_barrier(0);
     uint32_t* px0 = pex[wave][0];
     uint32_t* px1 = pex[wave][1];
-    uint32_t* px2 = pex[wave][2];
-    for (int it = 0; it < iters; it += 3) {
+    for (int it = 0; it < iters; it += 2) {
       const int64_t base = wb + int64_t(it) * T;
-      load(base + 2 * T, tc);
+      load(base + T, tb);
       process(base, px0, ta);
       if (it + 1 >= iters) break;
-      load(base + 3 * T, ta);
+      load(base + 2 * T, ta);
       process(base + T, px1, tb);
-      if (it + 2 >= iters) break;
-      load(base + 4 * T, tb);
-      process(base + 2 * T, px2, tc);
     }
   }
 
@@ -1203,10 +1190,9 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   for (int g = 0; g < GK; ++g) {
     lw[g] = dev::wave_sum(lpart[g]);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < 8; ++c) {
       acc[g][c] += __shfl_xor(acc[g][c], 1);
       acc[g][c] += __shfl_xor(acc[g][c], 2);
-      acc[g][c] += __shfl_xor(acc[g][c], 4);
     }
   }
   __syncthreads();                       // tables are dead: reuse them below
@@ -1228,7 +1214,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     const float f = m_run[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - M[g]);
     if (q == 0) {
 #pragma unroll
-      for (int c = 0; c < 16; ++c) slab[(wave * GK + g) * D + dsl * 16 + c] = acc[g][c] * f;
+      for (int c = 0; c < 8; ++c) slab[(wave * GK + g) * D + dsl * 8 + c] = acc[g][c] * f;
     }
   }
   __syncthreads();
