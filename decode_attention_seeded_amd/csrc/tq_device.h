@@ -215,31 +215,49 @@ __device__ __forceinline__ void static_for(F&& f) {
 // s[g] += dot2(q_g broadcast from lane L of every 16-lane row, c) for the
 // G accumulators: v_dot2c_f32_f16 with a DPP row_newbcast source, so the
 // query operand comes straight from a VGPR that only lane L of the row
-// holds. The leading s_nop covers the DPP read-after-VALU-write hazard,
-// which the compiler does not check inside inline assembly. EXEC must be
-// full when this runs.
-template <int L, int G>
+// holds. The compiler checks no hazards inside inline assembly, so the
+// block carries its own wait states:
+//  * the leading s_nop 1 covers the DPP read of a VGPR written by a recent
+//    VALU instruction (2 wait states);
+//  * with TAIL, a trailing s_nop 4 covers a dot result read by a following
+//    non-dot VALU instruction (CDNA3 asks for 3 wait states; only a dot that
+//    takes it as its accumulator is interlocked). Chained calls accumulate
+//    into s, so only the last call before s is read needs TAIL.
+// EXEC must be full when this runs.
+#define TQ_DOT2_DPP(D, Q, C, L) \
+  "v_dot2c_f32_f16_dpp " D ", " Q ", " C " row_newbcast:" L " row_mask:0xf bank_mask:0xf\n\t"
+template <int L, int G, bool TAIL = false>
 __device__ __forceinline__ void dot2_bcast(float (&s)[G], const uint32_t (&q)[G], uint32_t c) {
   static_assert(G == 1 || G == 2 || G == 4, "G");
   if constexpr (G == 1) {
-    asm("s_nop 1\n\t"
-        "v_dot2c_f32_f16_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-        : "+v"(s[0]) : "v"(q[0]), "v"(c), "n"(L));
+    if constexpr (TAIL)
+      asm("s_nop 1\n\t" TQ_DOT2_DPP("%0", "%1", "%2", "%3") "s_nop 4"
+          : "+v"(s[0]) : "v"(q[0]), "v"(c), "n"(L));
+    else
+      asm("s_nop 1\n\t" TQ_DOT2_DPP("%0", "%1", "%2", "%3")
+          : "+v"(s[0]) : "v"(q[0]), "v"(c), "n"(L));
   } else if constexpr (G == 2) {
-    asm("s_nop 1\n\t"
-        "v_dot2c_f32_f16_dpp %0, %2, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %3, %4 row_newbcast:%5 row_mask:0xf bank_mask:0xf"
-        : "+v"(s[0]), "+v"(s[1]) : "v"(q[0]), "v"(q[1]), "v"(c), "n"(L));
+    if constexpr (TAIL)
+      asm("s_nop 1\n\t" TQ_DOT2_DPP("%0", "%2", "%4", "%5") TQ_DOT2_DPP("%1", "%3", "%4", "%5")
+          "s_nop 4"
+          : "+v"(s[0]), "+v"(s[1]) : "v"(q[0]), "v"(q[1]), "v"(c), "n"(L));
+    else
+      asm("s_nop 1\n\t" TQ_DOT2_DPP("%0", "%2", "%4", "%5") TQ_DOT2_DPP("%1", "%3", "%4", "%5")
+          : "+v"(s[0]), "+v"(s[1]) : "v"(q[0]), "v"(q[1]), "v"(c), "n"(L));
   } else {
-    asm("s_nop 1\n\t"
-        "v_dot2c_f32_f16_dpp %0, %4, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %1, %5, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %2, %6, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf\n\t"
-        "v_dot2c_f32_f16_dpp %3, %7, %8 row_newbcast:%9 row_mask:0xf bank_mask:0xf"
-        : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3])
-        : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(c), "n"(L));
+    if constexpr (TAIL)
+      asm("s_nop 1\n\t" TQ_DOT2_DPP("%0", "%4", "%8", "%9") TQ_DOT2_DPP("%1", "%5", "%8", "%9")
+          TQ_DOT2_DPP("%2", "%6", "%8", "%9") TQ_DOT2_DPP("%3", "%7", "%8", "%9") "s_nop 4"
+          : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3])
+          : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(c), "n"(L));
+    else
+      asm("s_nop 1\n\t" TQ_DOT2_DPP("%0", "%4", "%8", "%9") TQ_DOT2_DPP("%1", "%5", "%8", "%9")
+          TQ_DOT2_DPP("%2", "%6", "%8", "%9") TQ_DOT2_DPP("%3", "%7", "%8", "%9")
+          : "+v"(s[0]), "+v"(s[1]), "+v"(s[2]), "+v"(s[3])
+          : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(c), "n"(L));
   }
 }
+#undef TQ_DOT2_DPP
 
 // Wave-wide max with DPP row operations (quad swaps, half-row and row
 // mirrors, then row broadcasts); the result is taken from lane 63.

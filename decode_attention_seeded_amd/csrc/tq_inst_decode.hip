@@ -27,8 +27,13 @@ static int go(int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
 #else
   if constexpr (TQ_D == 128 && !QJL && (BV == 2 || BV == 4)) {
     if (wide) {
-      hipLaunchKernelGGL((k_decode_wide<TQ_BK, BV, GK, QJL>), grid, dim3(64 * kWideWaves), 0, st, a,
-                         reinterpret_cast<const uint32_t*>(a.qp), a.qq);
+      const uint32_t* qp2 = reinterpret_cast<const uint32_t*>(a.qp);
+      if (a.norm_f16)
+        hipLaunchKernelGGL((k_decode_wide<TQ_BK, BV, GK, QJL, true>), grid, dim3(64 * kWideWaves),
+                           0, st, a, qp2, a.qq);
+      else
+        hipLaunchKernelGGL((k_decode_wide<TQ_BK, BV, GK, QJL, false>), grid,
+                           dim3(64 * kWideWaves), 0, st, a, qp2, a.qq);
       return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
     }
   } else {

@@ -66,7 +66,7 @@ struct DecodePlan {
 
 // Waves per workgroup of the wide kernel; one workgroup round covers
 // 64 * kWideWaves tokens.
-constexpr int kWideWaves = 12;
+constexpr int kWideWaves = 16;
 
 // Whether the packed decode runs the wide kernel for this format.
 inline bool use_wide(int d, int bits_v, int qjl) {

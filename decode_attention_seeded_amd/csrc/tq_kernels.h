@@ -734,7 +734,7 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
           constexpr int m = decltype(mc)::value;
           const uint32_t ka = dev::field_at<2 * BK, 7>(cur.kw, ch * 16 + m) | rl4;
           const uint32_t cp = *reinterpret_cast<const uint32_t*>(tabs + ka);
-          dev::dot2_bcast<m, GK>(s, qg, cp);
+          dev::dot2_bcast<m, GK, m == 15>(s, qg, cp);
           if constexpr (m == 7) __builtin_amdgcn_sched_barrier(0);
         });
         __builtin_amdgcn_sched_barrier(0);
@@ -939,7 +939,7 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 template <int BK, int BV>
 struct WvTile {
   uint32_t kw[128 * BK / 32];   // key row of the lane's token
-  uint32_t kn[2], vn[2];        // its key and value norms as 16-bit halves
+  uint32_t kn, vn;              // its key and value norms (f16 or f32 bits)
   uint32_t vx[16];              // value slices: row 4i+q, coordinates 8d..8d+7
 };
 
@@ -952,7 +952,7 @@ __device__ __forceinline__ uint32_t spread2to4(uint32_t x) {
   return x;
 }
 
-template <int BK, int BV, int GK, bool QJL>
+template <int BK, int BV, int GK, bool QJL, bool NF16>
 __global__ void __launch_bounds__(64 * kWideWaves)
     __attribute__((amdgpu_waves_per_eu(kWideWaves / 4)))
 k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
@@ -1020,8 +1020,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   const int64_t t_begin = int64_t(split) * a.tps;
   const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
   const int64_t row0 = int64_t(bkv) * a.capacity;
-  const bool nf16 = a.norm_f16 != 0;
-  const int nb = nf16 ? 2 : 4;
+  constexpr int nb = NF16 ? 2 : 4;
   const int iters = int((t_end - t_begin + T - 1) / T);
 
   auto rows_left = [&](int64_t base) -> uint32_t {
@@ -1029,12 +1028,9 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     return uint32_t(n <= 0 ? 0 : (n < TW ? n : TW));
   };
   // voffsets: the lane's key row, its norms, and its value slices (row q,
-  // coordinates 8*dsl..8*dsl+7). Norms are read as two 16-bit halves; the
-  // high half's descriptor is empty for f16 norms, so the load count per
-  // tile does not depend on the norm type.
+  // coordinates 8*dsl..8*dsl+7)
   const uint32_t ko0 = uint32_t(lane) * KREC;
-  const uint32_t no_lo0 = nf16 ? uint32_t(lane) * 2 : uint32_t(lane) * 4;
-  const uint32_t no_hi0 = uint32_t(lane) * 4 + 2;
+  const uint32_t no0 = uint32_t(lane) * nb;
   const uint32_t vo0 = uint32_t(q) * VREC + uint32_t(dsl) * BV;
   // per-load constants go in the scalar offset operand, so they cost neither
   // VALU work nor loop-invariant VGPRs
@@ -1049,11 +1045,13 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     }
     const uint8_t* kn_p = static_cast<const uint8_t*>(a.kn) + (row0 + base) * nb;
     const uint8_t* vn_p = static_cast<const uint8_t*>(a.vn) + (row0 + base) * nb;
-    const uint32_t nbytes = n * nb, hbytes = nf16 ? 0u : nbytes;
-    t.kn[0] = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(kn_p, nbytes), no_lo0, 0, 0);
-    t.kn[1] = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(kn_p, hbytes), no_hi0, 0, 0);
-    t.vn[0] = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(vn_p, nbytes), no_lo0, 0, 0);
-    t.vn[1] = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(vn_p, hbytes), no_hi0, 0, 0);
+    if constexpr (NF16) {
+      t.kn = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(kn_p, n * nb), no0, 0, 0);
+      t.vn = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(vn_p, n * nb), no0, 0, 0);
+    } else {
+      t.kn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(kn_p, n * nb), no0, 0, 0);
+      t.vn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(vn_p, n * nb), no0, 0, 0);
+    }
     const auto rv = dev::buffer_rsrc(a.vc + (row0 + base) * VREC, n * VREC);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -1089,15 +1087,13 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
         constexpr int m = decltype(mc)::value;
         const uint32_t ka = dev::field_at<2 * BK, 7>(cur.kw, ch * 16 + m) | rl4;
         const uint32_t cp = *reinterpret_cast<const uint32_t*>(tabs + ka);
-        dev::dot2_bcast<m, GK>(s, qg, cp);
+        dev::dot2_bcast<m, GK, m == 15>(s, qg, cp);
         if constexpr (m == 7) __builtin_amdgcn_sched_barrier(0);
       });
       __builtin_amdgcn_sched_barrier(0);
     }
-    const uint32_t kn32 = cur.kn[0] | (cur.kn[1] << 16);
-    const uint32_t vn32 = cur.vn[0] | (cur.vn[1] << 16);
-    const float knrm = nf16 ? dev::f16_to_f32(kn32) : __uint_as_float(kn32);
-    const float vnrm = nf16 ? dev::f16_to_f32(vn32) : __uint_as_float(vn32);
+    const float knrm = NF16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
+    const float vnrm = NF16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn);
     const float ks = knrm * a.kscale;
     const float nv = vnrm * a.vscale;
 

@@ -36,6 +36,10 @@ SMALL = {
     "d256_k4v3_f32norm": dict(B=1, Hq=2, Hkv=1, d=256, N=520, bits_k=4, bits_v=3,
                               norm_dtype="f32", wid=109),
     "d128_n1": dict(B=2, Hq=4, Hkv=2, N=1, bits_k=3, bits_v=4, wid=110),
+    # one query head per KV head with f32 norms: the score scaling follows the
+    # last DPP dot of the K phase closely (dot-result wait states)
+    "d128_k3v4_f32norm_g1": dict(B=2, Hq=2, Hkv=2, N=1500, bits_k=3, bits_v=4,
+                                 norm_dtype="f32", wid=111),
 }
 
 
