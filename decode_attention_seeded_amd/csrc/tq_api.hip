@@ -52,20 +52,48 @@ unsigned row_grid(int64_t rows) {
   return unsigned(g < 16384 ? g : 16384);
 }
 
-template <int D, int BITS, bool QJL>
+// grid of the encode kernel: 16 tokens per workgroup in x, (batch, KV head)
+// in y (the kernel strides y past 65535), K and V in z
+template <int D, int BK, int BV, bool QJL>
 int launch_encode(const EncodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_encode<D, BITS, QJL>), dim3(row_grid(a.rows)), dim3(256), 0, st, a);
+  const unsigned gx = unsigned((a.n_new + 15) / 16);
+  const unsigned gy = unsigned(a.BH < 65535 ? a.BH : 65535);
+  hipLaunchKernelGGL((k_encode<D, BK, BV, QJL>), dim3(gx, gy, 2), dim3(256), 0, st, a);
   return last_launch();
 }
 
-template <int D>
-int launch_encode_bits(int bits, bool qjl, const EncodeArgs& a, hipStream_t st) {
-  switch (bits) {
-    case 2: return qjl ? launch_encode<D, 2, true>(a, st) : launch_encode<D, 2, false>(a, st);
-    case 3: return qjl ? launch_encode<D, 3, true>(a, st) : launch_encode<D, 3, false>(a, st);
-    case 4: return qjl ? launch_encode<D, 4, true>(a, st) : launch_encode<D, 4, false>(a, st);
+template <int D, int BK>
+int launch_encode_v(int bv, bool qjl, const EncodeArgs& a, hipStream_t st) {
+  switch (bv) {
+    case 2: return qjl ? launch_encode<D, BK, 2, true>(a, st) : launch_encode<D, BK, 2, false>(a, st);
+    case 3: return qjl ? launch_encode<D, BK, 3, true>(a, st) : launch_encode<D, BK, 3, false>(a, st);
+    case 4: return qjl ? launch_encode<D, BK, 4, true>(a, st) : launch_encode<D, BK, 4, false>(a, st);
   }
   return TQ_ERR_UNSUPPORTED;
+}
+
+template <int D>
+int launch_encode_kv(int bk, int bv, bool qjl, const EncodeArgs& a, hipStream_t st) {
+  switch (bk) {
+    case 2: return launch_encode_v<D, 2>(bv, qjl, a, st);
+    case 3: return launch_encode_v<D, 3>(bv, qjl, a, st);
+    case 4: return launch_encode_v<D, 4>(bv, qjl, a, st);
+  }
+  return TQ_ERR_UNSUPPORTED;
+}
+
+// Bit i set when rotation sign i (SplitMix64 stream `seed`) is negative.
+void sign_bitmap(uint64_t seed, int d, uint32_t (&w)[8]) {
+  for (int k = 0; k < 8; ++k) w[k] = 0;
+  for (int i = 0; i < d; ++i)
+    if (splitmix64_at(seed, uint64_t(i)) >> 63) w[i >> 5] |= 1u << (i & 31);
+}
+
+// t_{L/2} .. t_{L-2}: the positive thresholds of the antisymmetric codebook.
+void fill_positive_thresholds(int bits, double* tpos) {
+  const Codebook& cb = codebook(bits);
+  const int H = 1 << (bits - 1);
+  for (int j = 0; j < 7; ++j) tpos[j] = j < H - 1 ? cb.t[H + j] : INFINITY;
 }
 
 void fill_codebook_f64(int bits, double* thr, double* cen) {
@@ -179,34 +207,29 @@ int tq_encode_kv(const tq_config* cfg, const void* k, const void* v, int in_dtyp
   if (st != TQ_OK) return st;
 
   EncodeArgs a{};
-  a.rows = rows;
+  a.x[0] = k;
+  a.x[1] = v;
+  a.codes[0] = static_cast<uint8_t*>(cache->kc);
+  a.codes[1] = static_cast<uint8_t*>(cache->vc);
+  a.norms[0] = cache->kn;
+  a.norms[1] = cache->vn;
+  a.qbits = static_cast<uint8_t*>(cache->kq);
+  a.rnorm = static_cast<uint16_t*>(cache->kr);
   a.n_new = n_new;
   a.offset = offset;
   a.capacity = cache->capacity;
+  a.BH = cache->B * cache->Hkv;
   a.in_dtype = in_dtype;
   a.norm_f16 = cfg->norm_dtype == TQ_F16;
-  a.seed = cfg->seed;
-  a.qjl_seed = cfg->qjl_seed;
-
-  EncodeArgs ak = a;
-  ak.x = k;
-  ak.codes = static_cast<uint8_t*>(cache->kc);
-  ak.norms = cache->kn;
-  ak.qbits = static_cast<uint8_t*>(cache->kq);
-  ak.rnorm = static_cast<uint16_t*>(cache->kr);
-  fill_codebook_f64(cfg->bits_k, ak.thr, ak.cen);
+  sign_bitmap(cfg->seed, cfg->d, a.sbits);
+  sign_bitmap(cfg->qjl_seed, cfg->d, a.qsbits);
+  fill_positive_thresholds(cfg->bits_k, a.tpos[0]);
+  fill_positive_thresholds(cfg->bits_v, a.tpos[1]);
+  double thr_unused[15];
+  fill_codebook_f64(cfg->bits_k, thr_unused, a.cen_k);
   const bool q = cfg->qjl != 0;
-  st = cfg->d == 128 ? launch_encode_bits<128>(cfg->bits_k, q, ak, stream)
-                     : launch_encode_bits<256>(cfg->bits_k, q, ak, stream);
-  if (st != TQ_OK) return st;
-
-  EncodeArgs av = a;
-  av.x = v;
-  av.codes = static_cast<uint8_t*>(cache->vc);
-  av.norms = cache->vn;
-  fill_codebook_f64(cfg->bits_v, av.thr, av.cen);
-  return cfg->d == 128 ? launch_encode_bits<128>(cfg->bits_v, false, av, stream)
-                       : launch_encode_bits<256>(cfg->bits_v, false, av, stream);
+  return cfg->d == 128 ? launch_encode_kv<128>(cfg->bits_k, cfg->bits_v, q, a, stream)
+                       : launch_encode_kv<256>(cfg->bits_k, cfg->bits_v, q, a, stream);
 }
 
 int tq_qjl_sketch(const float* r, int64_t rows, int d, uint64_t qjl_seed, uint32_t* bits,

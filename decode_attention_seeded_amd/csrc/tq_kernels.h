@@ -19,19 +19,22 @@ struct RhtArgs {
   uint64_t seed;
 };
 
+// Encode of one token range of K and V into the packed cache (one launch,
+// blockIdx.z selects the tensor).
 struct EncodeArgs {
-  const void* x;          // [B*Hkv][n_new][D] rows of K or V
-  uint8_t* codes;         // packed code plane
-  void* norms;            // fp16 or fp32 norm plane
+  const void* x[2];       // K rows, V rows: [B*Hkv][n_new][D]
+  uint8_t* codes[2];      // packed code planes
+  void* norms[2];         // fp16 or fp32 norm planes
   uint8_t* qbits;         // QJL sign plane (keys with QJL only)
   uint16_t* rnorm;        // QJL residual-norm plane
-  int64_t rows;           // B*Hkv*n_new
   int64_t n_new, offset, capacity;
+  int BH;                 // B * Hkv
   int in_dtype;
   int norm_f16;
-  uint64_t seed, qjl_seed;
-  double thr[15];         // thresholds, ascending
-  double cen[16];         // centroids, ascending
+  uint32_t sbits[8];      // rotation signs, bit i set when sign i is negative
+  uint32_t qsbits[8];     // QJL rotation signs, same layout
+  double tpos[2][7];      // thresholds t_{L/2} .. t_{L-2} of K and V (t_{L/2-1} = 0)
+  double cen_k[16];       // key centroids, ascending (QJL residual)
 };
 
 struct QjlArgs {
@@ -125,83 +128,113 @@ __global__ void __launch_bounds__(256) k_rht(RhtArgs a) {
 // definition except for values lying exactly on a threshold.
 // ---------------------------------------------------------------------------
 
-template <int D, int BITS, bool QJL>
-__global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
+// Bits [first, first + n) of a little-endian bitmap held in 8 uniform
+// dwords, n <= 16 and first a multiple of n: a select chain over the dwords,
+// so a lane-dependent index needs no private memory.
+__device__ __forceinline__ uint32_t bitmap_bits(const uint32_t (&w)[8], int first, int n) {
+  const int wi = first >> 5;
+  uint32_t x = w[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) x = (wi == k) ? w[k] : x;
+  return (x >> (first & 31)) & ((1u << n) - 1u);
+}
+
+// One row (16 lanes, E = D/16 coordinates each) of tensor TS (0 = K, 1 = V):
+// sign flip + FWHT in fp64 (exact for bf16/fp16 inputs), norm, codes, pack.
+// The code of z = u / n is #{k : z >= t_k}; with the antisymmetric codebook
+// (t_{L/2-1} = 0, t_k = -t_{L-2-k}) it is L/2 + #{j : |u| >= n t_{L/2+j}} for
+// u >= 0 and L/2 - 1 - #{j : |u| >= n t_{L/2+j}} for u < 0 (exact ties aside),
+// which needs neither a division nor the negative half of the thresholds.
+template <int D, int BITS, bool QJL, int TS>
+__device__ __forceinline__ void encode_row(const EncodeArgs& a, int64_t bh, int64_t t,
+                                           int l16) {
   constexpr int E = D / 16;
   constexpr int L = 1 << BITS;
+  constexpr int H = L / 2;
   constexpr int REC = D * BITS / 8;          // bytes per packed row
   constexpr int LANE_BYTES = E * BITS / 8;    // bytes of the row per lane
+  const int64_t row = bh * a.n_new + t;
+  const int64_t rec = bh * a.capacity + a.offset + t;
+  const uint32_t smask = bitmap_bits(a.sbits, l16 * E, E);
+
+  float f[E];
+  dev::load_row_part<E>(a.x[TS], a.in_dtype, row * D + l16 * E, f);
+  double u[E];
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const double x = f[i];
+    ss += x * x;
+    u[i] = (smask >> i & 1) ? -x : x;
+  }
+  dev::fwht16<E, double>(u, l16);
+  ss = dev::group16_sum(ss);
+  const double n = sqrt(ss);
+
+  double nstored;
+  if (a.norm_f16) {
+    const uint16_t h = dev::f64_to_f16_bits(n);
+    nstored = dev::f16_bits_to_f64(h);
+    if (l16 == 0) static_cast<uint16_t*>(a.norms[TS])[rec] = h;
+  } else {
+    const float nf = float(n);
+    nstored = nf;
+    if (l16 == 0) static_cast<float*>(a.norms[TS])[rec] = nf;
+  }
+
+  // thresholds scaled by the norm; a zero row gets the middle code L/2
+  double T[H - 1];
+#pragma unroll
+  for (int j = 0; j < H - 1; ++j) T[j] = n > 0.0 ? a.tpos[TS][j] * n : INFINITY;
+  uint64_t packed = 0;
+  uint32_t code[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const double au = fabs(u[i]);
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < H - 1; ++j) c += (au >= T[j]) ? 1u : 0u;
+    code[i] = u[i] >= 0.0 ? uint32_t(H) + c : uint32_t(H - 1) - c;
+    packed |= uint64_t(code[i]) << (BITS * i);
+  }
+  dev::store_bytes(a.codes[TS] + rec * REC + l16 * LANE_BYTES, packed, LANE_BYTES);
+
+  if constexpr (QJL) {
+    // residual in the rotated frame: r = (u - n_stored * c[code]) / sqrt(d)
+    const uint32_t qmask = bitmap_bits(a.qsbits, l16 * E, E);
+    const double inv_sqrt_d = 1.0 / sqrt(double(D));
+    double r[E];
+    double rr = 0.0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      double ci = 0.0;
+#pragma unroll
+      for (int k = 0; k < L; ++k) ci = (code[i] == uint32_t(k)) ? a.cen_k[k] : ci;
+      const double ri = (u[i] - nstored * ci) * inv_sqrt_d;
+      rr += ri * ri;
+      r[i] = (qmask >> i & 1) ? -ri : ri;
+    }
+    rr = dev::group16_sum(rr);
+    dev::fwht16<E, double>(r, l16);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) bits |= (r[i] < 0.0 ? 1u : 0u) << i;
+    dev::store_bytes(a.qbits + rec * (D / 8) + l16 * (E / 8), bits, E / 8);
+    if (l16 == 0) a.rnorm[rec] = dev::f64_to_f16_bits(sqrt(rr));
+  }
+}
+
+// grid: x = 16-token groups, y = (batch, KV head) (strided), z = tensor.
+template <int D, int BK, int BV, bool QJL>
+__global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
   const int l16 = threadIdx.x & 15;
-  const int grp = threadIdx.x >> 4;
-  const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
-  const uint32_t qmask = QJL ? dev::sign_mask(a.qjl_seed, l16 * E, E) : 0u;
-  const double inv_sqrt_d = 1.0 / sqrt(double(D));
-
-  for (int64_t row = int64_t(blockIdx.x) * 16 + grp; row < a.rows;
-       row += int64_t(gridDim.x) * 16) {
-    const int64_t bh = row / a.n_new;
-    const int64_t t = row - bh * a.n_new;
-    const int64_t rec = bh * a.capacity + a.offset + t;
-
-    float f[E];
-    dev::load_row_part<E>(a.x, a.in_dtype, row * D + l16 * E, f);
-    double u[E];
-    double ss = 0.0;
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const double x = f[i];
-      ss += x * x;
-      u[i] = (smask >> i & 1) ? -x : x;
-    }
-    dev::fwht16<E, double>(u, l16);
-    ss = dev::group16_sum(ss);
-    const double n = sqrt(ss);
-
-    double nstored;
-    if (a.norm_f16) {
-      const uint16_t h = dev::f64_to_f16_bits(n);
-      nstored = dev::f16_bits_to_f64(h);
-      if (l16 == 0) static_cast<uint16_t*>(a.norms)[rec] = h;
-    } else {
-      const float nf = float(n);
-      nstored = nf;
-      if (l16 == 0) static_cast<float*>(a.norms)[rec] = nf;
-    }
-
-    uint64_t packed = 0;
-    uint32_t code[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      const double z = n > 0.0 ? u[i] / n : 0.0;
-      uint32_t c = 0;
-#pragma unroll
-      for (int k = 0; k < L - 1; ++k) c += (z >= a.thr[k]) ? 1u : 0u;
-      code[i] = c;
-      packed |= uint64_t(c) << (BITS * i);
-    }
-    dev::store_bytes(a.codes + rec * REC + l16 * LANE_BYTES, packed, LANE_BYTES);
-
-    if constexpr (QJL) {
-      // residual in the rotated frame: r = (u - n_stored * c[code]) / sqrt(d)
-      double r[E];
-      double rr = 0.0;
-#pragma unroll
-      for (int i = 0; i < E; ++i) {
-        double ci = 0.0;
-#pragma unroll
-        for (int k = 0; k < L; ++k) ci = (code[i] == uint32_t(k)) ? a.cen[k] : ci;
-        const double ri = (u[i] - nstored * ci) * inv_sqrt_d;
-        rr += ri * ri;
-        r[i] = (qmask >> i & 1) ? -ri : ri;
-      }
-      rr = dev::group16_sum(rr);
-      dev::fwht16<E, double>(r, l16);
-      uint32_t bits = 0;
-#pragma unroll
-      for (int i = 0; i < E; ++i) bits |= (r[i] < 0.0 ? 1u : 0u) << i;
-      dev::store_bytes(a.qbits + rec * (D / 8) + l16 * (E / 8), bits, E / 8);
-      if (l16 == 0) a.rnorm[rec] = dev::f64_to_f16_bits(sqrt(rr));
-    }
+  const int64_t t = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  if (t >= a.n_new) return;                  // a whole 16-lane group leaves together
+  for (int64_t bh = blockIdx.y; bh < a.BH; bh += gridDim.y) {
+    if (blockIdx.z == 0)
+      encode_row<D, BK, QJL, 0>(a, bh, t, l16);
+    else
+      encode_row<D, BV, false, 1>(a, bh, t, l16);
   }
 }
 
