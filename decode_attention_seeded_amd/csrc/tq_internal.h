@@ -64,13 +64,16 @@ struct DecodePlan {
   size_t off_qp = 0, off_qq = 0, off_ml = 0, off_acc = 0, total = 0;
 };
 
-// Waves per workgroup of the wide kernel; one workgroup round covers
-// 64 * kWideWaves tokens.
-constexpr int kWideWaves = 16;
+// Waves per workgroup of the wide decode kernel (one workgroup holds a
+// compute unit; a workgroup round covers 64 tokens per wave). d = 256 keeps
+// twice the accumulators per lane, so it runs fewer, larger waves.
+constexpr int wide_waves(int d, int bits_v) { return d == 128 ? 16 : 8 + 0 * bits_v; }
+// Tiles each wave loads ahead of the one it processes (1 or 2).
+constexpr int wide_prefetch(int d, int bits_v) { return 1 + 0 * (d + bits_v); }
 
 // Whether the packed decode runs the wide kernel for this format.
 inline bool use_wide(int d, int bits_v, int qjl) {
-  return d == 128 && !qjl && (bits_v == 2 || bits_v == 4);
+  return (d == 128 || d == 256) && !qjl && (bits_v == 2 || bits_v == 4);
 }
 
 // Fills a plan; returns TQ_OK or a negative status.

@@ -946,34 +946,35 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 }
 
 // ---------------------------------------------------------------------------
-// Split-K decode, wave-private variant for d = 128 with 2- or 4-bit values
-// (no QJL). One workgroup of kWideWaves (12) waves holds a compute unit (3
-// waves per SIMD) and shares the codebook pair tables in LDS; each wave runs
-// its own online-softmax pass over interleaved 64-token tiles of the split
-// (wave w takes tiles w, w+12, ...), so the tile loop has no workgroup
-// barrier. The waves' partial results are combined once, at the end.
+// Split-K decode, wave-private variant for d = 128 or 256 with 2- or 4-bit
+// values (no QJL). One workgroup of W waves (wide_waves) holds a compute
+// unit and shares the codebook pair tables in LDS; each wave runs its own
+// online-softmax pass over interleaved 64-token tiles of the split (wave w
+// takes tiles w, w+W, ...), so the tile loop has no workgroup barrier. The
+// waves' partial results are combined once, at the end.
 //   K phase: lane = token; the key row is in VGPRs, each coordinate pair is
 //            one LDS pair-table lookup feeding GK DPP-broadcast dot2s.
 //   V phase: lane = (row class q = lane & 3, coordinate slice d = lane >> 2):
-//            the lane holds rows 8k+q and 8k+q+4 (k = 0..7) of its 8
-//            coordinates, so each lookup yields a (token, token) value pair
-//            for one coordinate, weighted by the matching fp16 weight pair.
-//            Weights move from the K layout to the V layout through a
+//            the lane holds rows 8k+q and 8k+q+4 (k = 0..7) of its CPL =
+//            D/16 coordinates, so each lookup yields a (token, token) value
+//            pair for one coordinate, weighted by the matching fp16 weight
+//            pair. Weights move from the K layout to the V layout through a
 //            wave-private LDS slot.
-//   Loads: key rows, norms and value slices of the next tile are fetched
-//          while the current one is processed (two register buffers, tile
-//          loop unrolled 2x), through buffer descriptors whose range ends at
-//          the split's last token (rows past it read as zero).
+//   Loads: key rows, norms and value slices of the next tiles are fetched
+//          while the current one is processed (PF + 1 register buffers used
+//          in rotation), through buffer descriptors whose range ends at the
+//          split's last token (rows past it read as zero).
 //   Softmax: the running max is raised only when some lane's score exceeds
 //            it by more than 8 (log2 units): then a DPP wave max, a rescale
 //            of that head's accumulators, and the weights use the new max.
 // ---------------------------------------------------------------------------
 
-template <int BK, int BV>
+template <int D, int BK, int BV>
 struct WvTile {
-  uint32_t kw[128 * BK / 32];   // key row of the lane's token
+  static constexpr int SW = (D / 16 * BV + 31) / 32;   // dwords per value slice
+  uint32_t kw[D * BK / 32];     // key row of the lane's token
   uint32_t kn, vn;              // its key and value norms (f16 or f32 bits)
-  uint32_t vx[16];              // value slices: row 4i+q, coordinates 8d..8d+7
+  uint32_t vx[16][SW];          // value slices: row 4i+q, coordinates CPL*d ..
 };
 
 // Spreads the eight 2-bit fields of the low 16 bits of x to the low two bits
@@ -985,29 +986,34 @@ __device__ __forceinline__ uint32_t spread2to4(uint32_t x) {
   return x;
 }
 
-template <int BK, int BV, int GK, bool QJL, bool NF16>
-__global__ void __launch_bounds__(64 * kWideWaves)
-    __attribute__((amdgpu_waves_per_eu(kWideWaves / 4)))
+template <int D, int BK, int BV, int GK, bool QJL, bool NF16>
+__global__ void __launch_bounds__(64 * wide_waves(D, BV))
+    __attribute__((amdgpu_waves_per_eu(wide_waves(D, BV) / 4)))
 k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
               const float* __restrict__ qq_all) {
+  static_assert(D == 128 || D == 256, "wave-private decode: d 128 or 256");
   static_assert(BV == 2 || BV == 4, "wave-private decode: 2- or 4-bit values");
   static_assert(!QJL, "wave-private decode: no QJL");
-  constexpr int D = 128;
-  constexpr int W = kWideWaves;                // waves per workgroup
+  constexpr int W = wide_waves(D, BV);         // waves per workgroup
+  constexpr int PF = wide_prefetch(D, BV);     // tiles loaded ahead
   constexpr int TW = 64;                       // tokens per wave tile
   constexpr int T = W * TW;                    // tokens per workgroup round
   constexpr int NT = 64 * W;                   // threads
+  constexpr int CPL = D / 16;                  // value coordinates per lane
   constexpr int KREC = D * BK / 8;
   constexpr int VREC = D * BV / 8;
   constexpr int KW = D * BK / 32;
+  constexpr int SBYTES = CPL * BV / 8;         // bytes per value slice
+  constexpr int SW = (SBYTES + 3) / 4;
   constexpr int KE = 1 << (2 * BK);
   constexpr int VE = 1 << (2 * BV);
   constexpr int KT_BYTES = KE * 128;           // 32 copies, 128-B entry stride
   constexpr int VT_BYTES = VE * 256;           // 64 copies, 256-B entry stride
   constexpr int PX = TW / 2 * GK;              // weight pairs per wave tile
   constexpr float kRescale = 8.0f;
-  using Tile = WvTile<BK, BV>;
+  using Tile = WvTile<D, BK, BV>;
   static_assert(KW % 4 == 0, "key rows are whole 16-byte loads");
+  static_assert(SBYTES == 2 || SBYTES == 4 || SBYTES == 8, "value slice width");
 
   constexpr int SLAB_BYTES = W * GK * D * 4;   // per-wave partials, after the loop
   constexpr int TAB_BYTES = KT_BYTES + VT_BYTES;
@@ -1047,7 +1053,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   const uint8_t* vtab = tabs + KT_BYTES;
   // query fp16 pairs of the GK heads; each K-phase chunk reads its 16 pairs
   // per head into VGPRs for the DPP broadcast
-  if (tid < GK * (D / 2)) qs[tid] = qp2_all[head0 * (D / 2) + tid];
+  for (int i = tid; i < GK * (D / 2); i += NT) qs[i] = qp2_all[head0 * (D / 2) + i];
   const uint32_t* qrow = qs + (lane & 15);
 
   const int64_t t_begin = int64_t(split) * a.tps;
@@ -1061,10 +1067,10 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     return uint32_t(n <= 0 ? 0 : (n < TW ? n : TW));
   };
   // voffsets: the lane's key row, its norms, and its value slices (row q,
-  // coordinates 8*dsl..8*dsl+7)
+  // coordinates CPL*dsl .. CPL*dsl + CPL - 1)
   const uint32_t ko0 = uint32_t(lane) * KREC;
   const uint32_t no0 = uint32_t(lane) * nb;
-  const uint32_t vo0 = uint32_t(q) * VREC + uint32_t(dsl) * BV;
+  const uint32_t vo0 = uint32_t(q) * VREC + uint32_t(dsl) * SBYTES;
   // per-load constants go in the scalar offset operand, so they cost neither
   // VALU work nor loop-invariant VGPRs
   auto load = [&](int64_t base, Tile& t) {
@@ -1088,21 +1094,26 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     const auto rv = dev::buffer_rsrc(a.vc + (row0 + base) * VREC, n * VREC);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if constexpr (BV == 4)
-        t.vx[i] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo0, i * 4 * VREC, 0);
-      else
-        t.vx[i] = __builtin_amdgcn_raw_buffer_load_b16(rv, vo0, i * 4 * VREC, 0);
+      if constexpr (SBYTES == 8) {
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rv, vo0, i * 4 * VREC, 0);
+        t.vx[i][0] = v2[0];
+        t.vx[i][SW - 1] = v2[1];
+      } else if constexpr (SBYTES == 4) {
+        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo0, i * 4 * VREC, 0);
+      } else {
+        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b16(rv, vo0, i * 4 * VREC, 0);
+      }
     }
   };
 
   float m_run[GK], lpart[GK];
-  float acc[GK][8];
+  float acc[GK][CPL];
 #pragma unroll
   for (int g = 0; g < GK; ++g) {
     m_run[g] = -INFINITY;
     lpart[g] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[g][c] = 0.f;
+    for (int c = 0; c < CPL; ++c) acc[g][c] = 0.f;
   }
 
   auto process = [&](int64_t base, uint32_t* px, const Tile& cur) {
@@ -1143,7 +1154,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
         m_run[g] = m_new;
         lpart[g] *= alpha;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[g][c] *= alpha;
+        for (int c = 0; c < CPL; ++c) acc[g][c] *= alpha;
       }
       // branch-free: rows past the split have s = 0 and zero norms
       const float e = __builtin_amdgcn_exp2f(s[g] - m_run[g]);
@@ -1170,46 +1181,74 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
       } else {
         p2[0] = pp[0];
       }
-      const uint32_t x = cur.vx[2 * k], y = cur.vx[2 * k + 1];   // rows 8k+q, 8k+q+4
-      uint32_t lo, hi;      // byte b: (x code, y code) of coordinate 2b (lo), 2b+1 (hi)
-      if constexpr (BV == 4) {
-        lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
-        hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
-      } else {
-        const uint32_t w = spread2to4(x) | (spread2to4(y) << 2);   // nibble c: coord c
-        lo = w & 0x0F0F0F0Fu;
-        hi = (w >> 4) & 0x0F0F0F0Fu;
-      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t word = (e & 1) ? hi : lo;
-        const uint32_t va =
-            __builtin_amdgcn_perm(word, vl4, 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8);
-        const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
+      for (int hw = 0; hw < CPL / 8; ++hw) {   // coordinates 8hw .. 8hw+7 of the slice
+        uint32_t lo, hi;  // byte b: (x code, y code) of coordinate 2b (lo), 2b+1 (hi)
+        if constexpr (BV == 4) {
+          const uint32_t x = cur.vx[2 * k][hw], y = cur.vx[2 * k + 1][hw];  // rows 8k+q, +4
+          lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
+          hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
+        } else {
+          const uint32_t x = (cur.vx[2 * k][0] >> (16 * hw)) & 0xFFFFu;
+          const uint32_t y = (cur.vx[2 * k + 1][0] >> (16 * hw)) & 0xFFFFu;
+          const uint32_t w = spread2to4(x) | (spread2to4(y) << 2);   // nibble c: coord c
+          lo = w & 0x0F0F0F0Fu;
+          hi = (w >> 4) & 0x0F0F0F0Fu;
+        }
 #pragma unroll
-        for (int g = 0; g < GK; ++g) acc[g][e] = dev::dot2(p2[g], vp, acc[g][e]);
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t word = (e & 1) ? hi : lo;
+          const uint32_t va =
+              __builtin_amdgcn_perm(word, vl4, 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8);
+          const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
+#pragma unroll
+          for (int g = 0; g < GK; ++g)
+            acc[g][8 * hw + e] = dev::dot2(p2[g], vp, acc[g][8 * hw + e]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // the next tile is loaded while the current one is processed; all waves
-  // run `iters` rounds (tiles past the split read as zero, zero weight)
+  // tiles are loaded PF tiles ahead of the one being processed (register
+  // buffers used in rotation, loop unrolled PF + 1 times); all waves run
+  // `iters` rounds (tiles past the split read as zero, zero weight)
   __syncthreads();
   {
-    Tile ta, tb;
     const int64_t wb = t_begin + int64_t(wave) * TW;
-    load(wb, ta);
-    __builtin_amdgcn_sched_barrier(0);
     uint32_t* px0 = pex[wave][0];
     uint32_t* px1 = pex[wave][1];
-    for (int it = 0; it < iters; it += 2) {
-      const int64_t base = wb + int64_t(it) * T;
-      load(base + T, tb);
-      process(base, px0, ta);
-      if (it + 1 >= iters) break;
-      load(base + 2 * T, ta);
-      process(base + T, px1, tb);
+    if constexpr (PF == 1) {
+      Tile ta, tb;
+      load(wb, ta);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int it = 0; it < iters; it += 2) {
+        const int64_t base = wb + int64_t(it) * T;
+        load(base + T, tb);
+        process(base, px0, ta);
+        if (it + 1 >= iters) break;
+        load(base + 2 * T, ta);
+        process(base + T, px1, tb);
+      }
+    } else {
+      static_assert(PF == 2, "prefetch depth 1 or 2");
+      Tile ta, tb, tc;
+      // issue order matters: the loop's waits count loads issued after ta
+      load(wb, ta);
+      __builtin_amdgcn_sched_barrier(0);
+      load(wb + T, tb);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int it = 0; it < iters; it += 3) {
+        const int64_t base = wb + int64_t(it) * T;
+        load(base + 2 * T, tc);
+        process(base, px0, ta);
+        if (it + 1 >= iters) break;
+        load(base + 3 * T, ta);
+        process(base + T, px1, tb);
+        if (it + 2 >= iters) break;
+        load(base + 4 * T, tb);
+        process(base + 2 * T, px0, tc);
+      }
     }
   }
 
@@ -1219,7 +1258,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   for (int g = 0; g < GK; ++g) {
     lw[g] = dev::wave_sum(lpart[g]);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < CPL; ++c) {
       acc[g][c] += __shfl_xor(acc[g][c], 1);
       acc[g][c] += __shfl_xor(acc[g][c], 2);
     }
@@ -1243,16 +1282,17 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     const float f = m_run[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - M[g]);
     if (q == 0) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) slab[(wave * GK + g) * D + dsl * 8 + c] = acc[g][c] * f;
+      for (int c = 0; c < CPL; ++c) slab[(wave * GK + g) * D + dsl * CPL + c] = acc[g][c] * f;
     }
   }
   __syncthreads();
   float* obuf = reinterpret_cast<float*>(pex);            // [GK][D]
-  if (tid < GK * D) {
+  static_assert(sizeof(pex) >= GK * D * 4, "output staging fits the weight slots");
+  for (int i = tid; i < GK * D; i += NT) {
     float sum = 0.f;
 #pragma unroll
-    for (int w = 0; w < W; ++w) sum += slab[w * GK * D + tid];
-    obuf[tid] = sum;
+    for (int w = 0; w < W; ++w) sum += slab[w * GK * D + i];
+    obuf[i] = sum;
   }
   __syncthreads();
   if (tid < GK) {
