@@ -155,7 +155,7 @@ int plan_decode(int d, int bits_v, int qjl, int B, int Hq, int Hkv, int64_t n_ct
   p->wide = use_wide(d, bits_v, qjl) ? 1 : 0;
   const int64_t units = int64_t(B) * Hkv * p->chunks;
   if (p->wide)
-    finish_plan(n_ctx, splits, units, 64 * wide_waves(d, bits_v), 256, p);
+    finish_plan(n_ctx, splits, units, 64 * wide_waves(d, bits_v, qjl), 256, p);
   else
     finish_plan(n_ctx, splits, units, decode_tile(d), 2048, p);
   const size_t heads = size_t(B) * Hq;

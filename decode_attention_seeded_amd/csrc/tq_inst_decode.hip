@@ -25,10 +25,10 @@ static int go(int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((k_decode<TQ_D, TQ_BK, BV, GK, QJL>), grid, dim3(TQ_D / 32 * 64), 0, st,
                      a, a.qp, a.qq);
 #else
-  if constexpr (!QJL && (BV == 2 || BV == 4)) {
+  if constexpr (BV == 2 || BV == 4) {
     if (wide) {
       const uint32_t* qp2 = reinterpret_cast<const uint32_t*>(a.qp);
-      const dim3 block(64 * wide_waves(TQ_D, BV));
+      const dim3 block(64 * wide_waves(TQ_D, BV, QJL));
       if (a.norm_f16)
         hipLaunchKernelGGL((k_decode_wide<TQ_D, TQ_BK, BV, GK, QJL, true>), grid, block, 0, st,
                            a, qp2, a.qq);

@@ -66,14 +66,18 @@ struct DecodePlan {
 
 // Waves per workgroup of the wide decode kernel (one workgroup holds a
 // compute unit; a workgroup round covers 64 tokens per wave). d = 256 keeps
-// twice the accumulators per lane, so it runs fewer, larger waves.
-constexpr int wide_waves(int d, int bits_v) { return d == 128 ? 16 : 8 + 0 * bits_v; }
+// twice the accumulators per lane and QJL adds the sign words, so those run
+// fewer waves with more registers each.
+constexpr int wide_waves(int d, int bits_v, int qjl) {
+  return d == 256 ? 8 : (qjl ? 12 : 16 + 0 * bits_v);
+}
 // Tiles each wave loads ahead of the one it processes (1 or 2).
 constexpr int wide_prefetch(int d, int bits_v) { return 1 + 0 * (d + bits_v); }
 
 // Whether the packed decode runs the wide kernel for this format.
 inline bool use_wide(int d, int bits_v, int qjl) {
-  return (d == 128 || d == 256) && !qjl && (bits_v == 2 || bits_v == 4);
+  (void)qjl;
+  return (d == 128 || d == 256) && (bits_v == 2 || bits_v == 4);
 }
 
 // Fills a plan; returns TQ_OK or a negative status.

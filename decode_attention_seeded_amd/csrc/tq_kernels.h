@@ -54,6 +54,7 @@ struct QPrepArgs {
   int rotate;             // 0: dense baseline, no rotation
   int pairs;              // 1: write qp as fp16 pairs (packed decode)
   int qjl;
+  int qq_pairs;           // 1: write qq as fp16 pairs too (wide decode)
   float mult;             // scale * log2(e)
   uint64_t seed, qjl_seed;
 };
@@ -316,11 +317,23 @@ __global__ void __launch_bounds__(256) k_qprep(QPrepArgs a) {
     for (int i = 0; i < E; ++i) if (qmask >> i & 1) v[i] = -v[i];
     dev::fwht16<E, float>(v, l16);
     const float nn = 1.0f / sqrtf(float(D));
-    float4* dq = reinterpret_cast<float4*>(a.qq + row * D + l16 * E);
 #pragma unroll
-    for (int k = 0; k < E / 4; ++k)
-      dq[k] = make_float4(v[4 * k] * nn, v[4 * k + 1] * nn, v[4 * k + 2] * nn,
-                          v[4 * k + 3] * nn);
+    for (int i = 0; i < E; ++i) v[i] *= nn;
+    if (a.qq_pairs) {
+      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint32_t*>(a.qq) + row * (D / 2) +
+                                            l16 * (E / 2));
+#pragma unroll
+      for (int k = 0; k < E / 8; ++k)
+        dst[k] = make_uint4(dev::pack_f16x2(v[8 * k], v[8 * k + 1]),
+                            dev::pack_f16x2(v[8 * k + 2], v[8 * k + 3]),
+                            dev::pack_f16x2(v[8 * k + 4], v[8 * k + 5]),
+                            dev::pack_f16x2(v[8 * k + 6], v[8 * k + 7]));
+    } else {
+      float4* dq = reinterpret_cast<float4*>(a.qq + row * D + l16 * E);
+#pragma unroll
+      for (int k = 0; k < E / 4; ++k)
+        dq[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    }
   }
 }
 
@@ -947,7 +960,7 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 
 // ---------------------------------------------------------------------------
 // Split-K decode, wave-private variant for d = 128 or 256 with 2- or 4-bit
-// values (no QJL). One workgroup of W waves (wide_waves) holds a compute
+// values, with or without the QJL score correction. One workgroup of W waves (wide_waves) holds a compute
 // unit and shares the codebook pair tables in LDS; each wave runs its own
 // online-softmax pass over interleaved 64-token tiles of the split (wave w
 // takes tiles w, w+W, ...), so the tile loop has no workgroup barrier. The
@@ -969,12 +982,14 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 //            of that head's accumulators, and the weights use the new max.
 // ---------------------------------------------------------------------------
 
-template <int D, int BK, int BV>
+template <int D, int BK, int BV, bool QJL>
 struct WvTile {
   static constexpr int SW = (D / 16 * BV + 31) / 32;   // dwords per value slice
   uint32_t kw[D * BK / 32];     // key row of the lane's token
   uint32_t kn, vn;              // its key and value norms (f16 or f32 bits)
   uint32_t vx[16][SW];          // value slices: row 4i+q, coordinates CPL*d ..
+  uint32_t sw[QJL ? D / 32 : 1];  // QJL sign bits of the key (bit set: negative)
+  uint32_t kr;                  // QJL residual norm (f16 bits)
 };
 
 // Spreads the eight 2-bit fields of the low 16 bits of x to the low two bits
@@ -987,14 +1002,13 @@ __device__ __forceinline__ uint32_t spread2to4(uint32_t x) {
 }
 
 template <int D, int BK, int BV, int GK, bool QJL, bool NF16>
-__global__ void __launch_bounds__(64 * wide_waves(D, BV))
-    __attribute__((amdgpu_waves_per_eu(wide_waves(D, BV) / 4)))
+__global__ void __launch_bounds__(64 * wide_waves(D, BV, QJL))
+    __attribute__((amdgpu_waves_per_eu(wide_waves(D, BV, QJL) / 4)))
 k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
               const float* __restrict__ qq_all) {
   static_assert(D == 128 || D == 256, "wave-private decode: d 128 or 256");
   static_assert(BV == 2 || BV == 4, "wave-private decode: 2- or 4-bit values");
-  static_assert(!QJL, "wave-private decode: no QJL");
-  constexpr int W = wide_waves(D, BV);         // waves per workgroup
+  constexpr int W = wide_waves(D, BV, QJL);    // waves per workgroup
   constexpr int PF = wide_prefetch(D, BV);     // tiles loaded ahead
   constexpr int TW = 64;                       // tokens per wave tile
   constexpr int T = W * TW;                    // tokens per workgroup round
@@ -1009,18 +1023,20 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   constexpr int VE = 1 << (2 * BV);
   constexpr int KT_BYTES = KE * 128;           // 32 copies, 128-B entry stride
   constexpr int VT_BYTES = VE * 256;           // 64 copies, 256-B entry stride
+  constexpr int ST_BYTES = QJL ? 16 * 512 : 0; // QJL sign quads: 64 copies of 8 B
   constexpr int PX = TW / 2 * GK;              // weight pairs per wave tile
   constexpr float kRescale = 8.0f;
-  using Tile = WvTile<D, BK, BV>;
+  using Tile = WvTile<D, BK, BV, QJL>;
   static_assert(KW % 4 == 0, "key rows are whole 16-byte loads");
   static_assert(SBYTES == 2 || SBYTES == 4 || SBYTES == 8, "value slice width");
 
   constexpr int SLAB_BYTES = W * GK * D * 4;   // per-wave partials, after the loop
-  constexpr int TAB_BYTES = KT_BYTES + VT_BYTES;
+  constexpr int TAB_BYTES = KT_BYTES + VT_BYTES + ST_BYTES;
   __shared__ __attribute__((aligned(16)))
   uint8_t tabs[TAB_BYTES > SLAB_BYTES ? TAB_BYTES : SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t pex[W][2][PX];
   __shared__ uint32_t qs[GK * (D / 2)];
+  __shared__ uint32_t qs2[QJL ? GK * (D / 2) : 1];
   __shared__ float mlx[W][GK][2];
 
   const int tid = threadIdx.x;
@@ -1051,10 +1067,27 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
         dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
   }
   const uint8_t* vtab = tabs + KT_BYTES;
-  // query fp16 pairs of the GK heads; each K-phase chunk reads its 16 pairs
-  // per head into VGPRs for the DPP broadcast
-  for (int i = tid; i < GK * (D / 2); i += NT) qs[i] = qp2_all[head0 * (D / 2) + i];
+  const uint8_t* stab = tabs + KT_BYTES + VT_BYTES;
+  if constexpr (QJL) {
+    // entry e: the fp16 pairs (s0, s1), (s2, s3) with s_k = -1 where bit k
+    // of e is set, else +1
+    for (int i = tid; i < 16 * 64; i += NT) {
+      const int e = i >> 6;
+      const float s0 = (e & 1) ? -1.f : 1.f, s1 = (e & 2) ? -1.f : 1.f;
+      const float s2 = (e & 4) ? -1.f : 1.f, s3 = (e & 8) ? -1.f : 1.f;
+      *reinterpret_cast<uint2*>(tabs + KT_BYTES + VT_BYTES + (e << 9) + ((i & 63) << 3)) =
+          make_uint2(dev::pack_f16x2(s0, s1), dev::pack_f16x2(s2, s3));
+    }
+  }
+  // query fp16 pairs of the GK heads (and the QJL query R_2 q'); each K-phase
+  // chunk reads its 16 pairs per head into VGPRs for the DPP broadcast
+  for (int i = tid; i < GK * (D / 2); i += NT) {
+    qs[i] = qp2_all[head0 * (D / 2) + i];
+    if constexpr (QJL) qs2[i] = reinterpret_cast<const uint32_t*>(qq_all)[head0 * (D / 2) + i];
+  }
   const uint32_t* qrow = qs + (lane & 15);
+  const uint32_t* qrow2 = qs2 + (lane & 15);
+  const uint32_t sl8 = uint32_t(lane) << 3;
 
   const int64_t t_begin = int64_t(split) * a.tps;
   const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
@@ -1071,6 +1104,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   const uint32_t ko0 = uint32_t(lane) * KREC;
   const uint32_t no0 = uint32_t(lane) * nb;
   const uint32_t vo0 = uint32_t(q) * VREC + uint32_t(dsl) * SBYTES;
+  const uint32_t so0 = uint32_t(lane) * (D / 8);
   // per-load constants go in the scalar offset operand, so they cost neither
   // VALU work nor loop-invariant VGPRs
   auto load = [&](int64_t base, Tile& t) {
@@ -1090,6 +1124,18 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     } else {
       t.kn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(kn_p, n * nb), no0, 0, 0);
       t.vn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(vn_p, n * nb), no0, 0, 0);
+    }
+    if constexpr (QJL) {
+      const auto rs = dev::buffer_rsrc(reinterpret_cast<const uint8_t*>(a.kq) +
+                                           (row0 + base) * (D / 8), n * (D / 8));
+#pragma unroll
+      for (int k = 0; k < D / 128; ++k) {
+        const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rs, so0, 16 * k, 0);
+        t.sw[4 * k] = q4[0]; t.sw[4 * k + 1] = q4[1]; t.sw[4 * k + 2] = q4[2];
+        t.sw[4 * k + 3] = q4[3];
+      }
+      t.kr = __builtin_amdgcn_raw_buffer_load_b16(
+          dev::buffer_rsrc(a.kr + (row0 + base), n * 2), uint32_t(lane) * 2, 0, 0);
     }
     const auto rv = dev::buffer_rsrc(a.vc + (row0 + base) * VREC, n * VREC);
 #pragma unroll
@@ -1136,10 +1182,31 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
       });
       __builtin_amdgcn_sched_barrier(0);
     }
+    // QJL: sum of +-q'' over the key's sign bits, four signs per lookup
+    float tq[QJL ? GK : 1];
+    if constexpr (QJL) {
+#pragma unroll
+      for (int g = 0; g < GK; ++g) tq[g] = 0.f;
+#pragma unroll
+      for (int ch = 0; ch < D / 32; ++ch) {
+        uint32_t qg[GK];
+#pragma unroll
+        for (int g = 0; g < GK; ++g) qg[g] = qrow2[g * (D / 2) + ch * 16];
+        dev::static_for<0, 8>([&](auto jc) {
+          constexpr int j = decltype(jc)::value;
+          const uint32_t sa = dev::field_at<4, 9>(cur.sw, ch * 8 + j) | sl8;
+          const uint2 sp = *reinterpret_cast<const uint2*>(stab + sa);
+          dev::dot2_bcast<2 * j, GK>(tq, qg, sp.x);
+          dev::dot2_bcast<2 * j + 1, GK, j == 7>(tq, qg, sp.y);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     const float knrm = NF16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
     const float vnrm = NF16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn);
     const float ks = knrm * a.kscale;
     const float nv = vnrm * a.vscale;
+    const float rho = QJL ? dev::f16_to_f32(cur.kr) * a.qjl_c : 0.f;
 
     // ---------------- online softmax with a lazily raised running max
     uint16_t* p16 = reinterpret_cast<uint16_t*>(px);
@@ -1147,6 +1214,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 #pragma unroll
     for (int g = 0; g < GK; ++g) {
       s[g] *= ks;
+      if constexpr (QJL) s[g] = fmaf(rho, tq[g], s[g]);
       if (__ballot(valid && s[g] > m_run[g] + kRescale)) {     // wave-uniform
         const float mx = dev::dpp_wave_max(valid ? s[g] : -INFINITY);
         const float m_new = fmaxf(m_run[g], mx);
