@@ -3,8 +3,8 @@
     python -m decode_attention_seeded_amd.build
 
 Objects go to decode_attention_seeded_amd/_build/, the library to
-decode_attention_seeded_amd/libtq.so. The split-K decode kernel is compiled
-once per (head dim, key bits) pair in parallel processes.
+decode_attention_seeded_amd/libtq.so. The split-K decode and the encode
+kernels are compiled once per (head dim, key bits) pair in parallel processes.
 """
 
 from __future__ import annotations
@@ -32,6 +32,7 @@ HIP_FLAGS = [
 ]
 
 DECODE_VARIANTS = [(d, bk) for d in (128, 256) for bk in (2, 3, 4, 16)]
+ENCODE_VARIANTS = [(d, bk) for d in (128, 256) for bk in (2, 3, 4)]
 
 
 def _jobs():
@@ -45,6 +46,10 @@ def _jobs():
         jobs.append((f"tq_decode_d{d}_k{bk}.o",
                      [HIPCC, *HIP_FLAGS, f"-DTQ_D={d}", f"-DTQ_BK={bk}",
                       "-c", os.path.join(CSRC, "tq_inst_decode.hip")]))
+    for d, bk in ENCODE_VARIANTS:
+        jobs.append((f"tq_encode_d{d}_k{bk}.o",
+                     [HIPCC, *HIP_FLAGS, f"-DTQ_D={d}", f"-DTQ_BK={bk}",
+                      "-c", os.path.join(CSRC, "tq_inst_encode.hip")]))
     return jobs
 
 

@@ -18,6 +18,14 @@ int launch_decode_d256_k3(int, int, int, int, const DecodeArgs&, dim3, hipStream
 int launch_decode_d256_k4(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
 int launch_decode_d256_k16(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
 
+using EncodeLauncher = int (*)(int, bool, const EncodeArgs&, hipStream_t);
+int launch_encode_d128_k2(int, bool, const EncodeArgs&, hipStream_t);
+int launch_encode_d128_k3(int, bool, const EncodeArgs&, hipStream_t);
+int launch_encode_d128_k4(int, bool, const EncodeArgs&, hipStream_t);
+int launch_encode_d256_k2(int, bool, const EncodeArgs&, hipStream_t);
+int launch_encode_d256_k3(int, bool, const EncodeArgs&, hipStream_t);
+int launch_encode_d256_k4(int, bool, const EncodeArgs&, hipStream_t);
+
 namespace {
 
 DecodeLauncher decode_launcher(int d, int bk) {
@@ -39,6 +47,15 @@ DecodeLauncher decode_launcher(int d, int bk) {
   return nullptr;
 }
 
+EncodeLauncher encode_launcher(int d, int bk) {
+  switch (bk) {
+    case 2: return d == 128 ? launch_encode_d128_k2 : launch_encode_d256_k2;
+    case 3: return d == 128 ? launch_encode_d128_k3 : launch_encode_d256_k3;
+    case 4: return d == 128 ? launch_encode_d128_k4 : launch_encode_d256_k4;
+  }
+  return nullptr;
+}
+
 int device_ready() {
   int n = 0;
   if (hipGetDeviceCount(&n) != hipSuccess || n < 1) return TQ_ERR_NO_DEVICE;
@@ -50,36 +67,6 @@ int last_launch() { return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 unsigned row_grid(int64_t rows) {
   const int64_t g = (rows + 15) / 16;
   return unsigned(g < 16384 ? g : 16384);
-}
-
-// grid of the encode kernel: 16 tokens per workgroup in x, (batch, KV head)
-// in y (the kernel strides y past 65535), K and V in z
-template <int D, int BK, int BV, bool QJL>
-int launch_encode(const EncodeArgs& a, hipStream_t st) {
-  const unsigned gx = unsigned((a.n_new + 15) / 16);
-  const unsigned gy = unsigned(a.BH < 65535 ? a.BH : 65535);
-  hipLaunchKernelGGL((k_encode<D, BK, BV, QJL>), dim3(gx, gy, 2), dim3(256), 0, st, a);
-  return last_launch();
-}
-
-template <int D, int BK>
-int launch_encode_v(int bv, bool qjl, const EncodeArgs& a, hipStream_t st) {
-  switch (bv) {
-    case 2: return qjl ? launch_encode<D, BK, 2, true>(a, st) : launch_encode<D, BK, 2, false>(a, st);
-    case 3: return qjl ? launch_encode<D, BK, 3, true>(a, st) : launch_encode<D, BK, 3, false>(a, st);
-    case 4: return qjl ? launch_encode<D, BK, 4, true>(a, st) : launch_encode<D, BK, 4, false>(a, st);
-  }
-  return TQ_ERR_UNSUPPORTED;
-}
-
-template <int D>
-int launch_encode_kv(int bk, int bv, bool qjl, const EncodeArgs& a, hipStream_t st) {
-  switch (bk) {
-    case 2: return launch_encode_v<D, 2>(bv, qjl, a, st);
-    case 3: return launch_encode_v<D, 3>(bv, qjl, a, st);
-    case 4: return launch_encode_v<D, 4>(bv, qjl, a, st);
-  }
-  return TQ_ERR_UNSUPPORTED;
 }
 
 // Bit i set when rotation sign i (SplitMix64 stream `seed`) is negative.
@@ -228,9 +215,9 @@ int tq_encode_kv(const tq_config* cfg, const void* k, const void* v, int in_dtyp
   fill_positive_thresholds(cfg->bits_v, a.tpos[1]);
   double thr_unused[15];
   fill_codebook_f64(cfg->bits_k, thr_unused, a.cen_k);
-  const bool q = cfg->qjl != 0;
-  return cfg->d == 128 ? launch_encode_kv<128>(cfg->bits_k, cfg->bits_v, q, a, stream)
-                       : launch_encode_kv<256>(cfg->bits_k, cfg->bits_v, q, a, stream);
+  EncodeLauncher fn = encode_launcher(cfg->d, cfg->bits_k);
+  if (!fn) return TQ_ERR_UNSUPPORTED;
+  return fn(cfg->bits_v, cfg->qjl != 0, a, stream);
 }
 
 int tq_qjl_sketch(const float* r, int64_t rows, int d, uint64_t qjl_seed, uint32_t* bits,

@@ -129,65 +129,185 @@ __global__ void __launch_bounds__(256) k_rht(RhtArgs a) {
 // definition except for values lying exactly on a threshold.
 // ---------------------------------------------------------------------------
 
-// Bits [first, first + n) of a little-endian bitmap held in 8 uniform
-// dwords, n <= 16 and first a multiple of n: a select chain over the dwords,
-// so a lane-dependent index needs no private memory.
-__device__ __forceinline__ uint32_t bitmap_bits(const uint32_t (&w)[8], int first, int n) {
-  const int wi = first >> 5;
+// Dword k (k < 8) of 8 uniform dwords for a lane-dependent k: a select
+// chain, so the index needs no private memory.
+__device__ __forceinline__ uint32_t pick8(const uint32_t (&w)[8], int k) {
   uint32_t x = w[0];
 #pragma unroll
-  for (int k = 1; k < 8; ++k) x = (wi == k) ? w[k] : x;
-  return (x >> (first & 31)) & ((1u << n) - 1u);
+  for (int j = 1; j < 8; ++j) x = (k == j) ? w[j] : x;
+  return x;
 }
 
-// One row (16 lanes, E = D/16 coordinates each) of tensor TS (0 = K, 1 = V):
-// sign flip + FWHT in fp64 (exact for bf16/fp16 inputs), norm, codes, pack.
-// The code of z = u / n is #{k : z >= t_k}; with the antisymmetric codebook
+// x from lane (lane ^ M) of the same quad (M = 1 or 2), through DPP
+// quad_perm on the two halves of the double.
+template <int M>
+__device__ __forceinline__ double quad_xor_f64(double x) {
+  constexpr int CTRL = M == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+  const uint64_t bits = uint64_t(__double_as_longlong(x));
+  const int lo = __builtin_amdgcn_mov_dpp(int(uint32_t(bits)), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp(int(uint32_t(bits >> 32)), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double(int64_t((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo)));
+}
+
+template <int M>
+__device__ __forceinline__ double lane_xor_f64(double x) {
+  if constexpr (M <= 2) return quad_xor_f64<M>(x);
+  else return __shfl_xor(x, M, 2 * M);
+}
+
+// Walsh-Hadamard transform (unnormalized, Sylvester order) of a row spread
+// over P consecutive lanes, 32 coordinates each (coordinate = lane_in_row *
+// 32 + i): five butterfly stages inside the lane, log2(P) across lanes. In a
+// cross-lane stage the lower lane of a pair keeps x + y and the upper one
+// x - y, so each lane computes partner + sg * own with sg[s] = +1 or -1.
+template <int P>
+__device__ __forceinline__ void fwht32xP(double (&v)[32], const double (&sg)[3]) {
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (!(i & h)) {
+        const double x = v[i], y = v[i + h];
+        v[i] = x + y;
+        v[i + h] = x - y;
+      }
+    }
+  }
+  // eight coordinates at a time, so that at most 16 partner registers are
+  // live on top of the row
+  dev::static_for<0, (P == 8 ? 3 : 2)>([&](auto sc) {
+    constexpr int st = decltype(sc)::value;
+#pragma unroll
+    for (int i0 = 0; i0 < 32; i0 += 8) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = i0; i < i0 + 8; ++i) v[i] = fma(v[i], sg[st], lane_xor_f64<(1 << st)>(v[i]));
+    }
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  // pin the results here: otherwise the last stage is sunk past the norm
+  // branches to its uses and its 32 partner values stay live meanwhile
+#pragma unroll
+  for (int i = 0; i < 32; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+template <int P>
+__device__ __forceinline__ double group_sum_f64(double x) {
+  x += lane_xor_f64<1>(x);
+  x += lane_xor_f64<2>(x);
+  if constexpr (P == 8) x += lane_xor_f64<4>(x);
+  return x;
+}
+
+// One lane's 32 input coordinates as raw 16-byte words: 4 for 16-bit inputs
+// (IW = 2 bytes per element), 8 for fp32.
+template <int IW>
+struct RowWords {
+  uint4 q[2 * IW];
+};
+
+// Per-lane constants of the encode kernel: the rotation signs of the lane's
+// 32 coordinates (for 16-bit inputs as XOR masks on the packed element
+// pairs: bit 15 and bit 31), and the cross-lane butterfly signs.
+template <int IW>
+struct EncodeLane {
+  uint32_t smask;
+  uint32_t pm[IW == 2 ? 16 : 1];
+  uint32_t qmask;
+  double sg[3];
+  int lp;
+};
+
+template <int D, int IW>
+__device__ __forceinline__ void load_words(const EncodeArgs& a, int z, int bh, int64_t t, int lp,
+                                           RowWords<IW>& r) {
+  const int64_t tc = t < a.n_new ? t : a.n_new - 1;   // rows past the end re-read the last one
+  const int64_t row = int64_t(bh) * a.n_new + tc;
+  const uint4* s = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(a.x[z]) +
+                                                  (row * D + lp * 32) * IW);
+#pragma unroll
+  for (int k = 0; k < 2 * IW; ++k) r.q[k] = s[k];
+}
+
+// Sign-flipped coordinates x_i * s_i as doubles, and sum of squares (DT:
+// 0 fp32, 1 bf16, 2 fp16).
+template <int DT, int IW = (DT == 0 ? 4 : 2)>
+__device__ __forceinline__ double words_to_f64(const RowWords<IW>& r, const EncodeLane<IW>& el,
+                                               double (&u)[32]) {
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < 2 * IW; ++k) {
+    const uint32_t w4[4] = {r.q[k].x, r.q[k].y, r.q[k].z, r.q[k].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (IW == 2) {
+        const int e = 8 * k + 2 * j;
+        const uint32_t w = w4[j] ^ el.pm[4 * k + j];
+        float lo, hi;
+        if constexpr (DT == 1) {
+          lo = __uint_as_float(w << 16);
+          hi = __uint_as_float(w & 0xFFFF0000u);
+        } else {
+          lo = dev::f16_to_f32(w & 0xFFFFu);
+          hi = dev::f16_to_f32(w >> 16);
+        }
+        u[e] = lo;
+        u[e + 1] = hi;
+        ss = fma(u[e], u[e], ss);
+        ss = fma(u[e + 1], u[e + 1], ss);
+      } else {
+        const int e = 4 * k + j;
+        const uint32_t w = w4[j] ^ ((el.smask << (31 - e)) & 0x80000000u);
+        u[e] = __uint_as_float(w);
+        ss = fma(u[e], u[e], ss);
+      }
+    }
+  }
+  return ss;
+}
+
+// One row of tensor TS (0 = K, 1 = V) on P = D/32 lanes, from its
+// sign-flipped coordinates u and their sum of squares: FWHT in fp64 (exact
+// for bf16/fp16 inputs), norm, codes, pack. The code of
+// z = u / n is #{k : z >= t_k}; with the antisymmetric codebook
 // (t_{L/2-1} = 0, t_k = -t_{L-2-k}) it is L/2 + #{j : |u| >= n t_{L/2+j}} for
 // u >= 0 and L/2 - 1 - #{j : |u| >= n t_{L/2+j}} for u < 0 (exact ties aside),
 // which needs neither a division nor the negative half of the thresholds.
-template <int D, int BITS, bool QJL, int TS>
-__device__ __forceinline__ void encode_row(const EncodeArgs& a, int64_t bh, int64_t t,
-                                           int l16) {
-  constexpr int E = D / 16;
+// Lanes of rows past the end (valid = false) compute but store nothing.
+template <int D, int BITS, bool QJL, int TS, int IW>
+__device__ __forceinline__ void encode_row(const EncodeArgs& a, int bh, int64_t t, bool valid,
+                                           const EncodeLane<IW>& el, double (&u)[32], double ss) {
+  constexpr int P = D / 32;
+  constexpr int E = 32;
   constexpr int L = 1 << BITS;
   constexpr int H = L / 2;
   constexpr int REC = D * BITS / 8;          // bytes per packed row
-  constexpr int LANE_BYTES = E * BITS / 8;    // bytes of the row per lane
-  const int64_t row = bh * a.n_new + t;
-  const int64_t rec = bh * a.capacity + a.offset + t;
-  const uint32_t smask = bitmap_bits(a.sbits, l16 * E, E);
+  constexpr int LW = BITS;                    // dwords of the row per lane (32 codes)
+  const int lp = el.lp;
+  const int64_t rec = int64_t(bh) * a.capacity + a.offset + t;
 
-  float f[E];
-  dev::load_row_part<E>(a.x[TS], a.in_dtype, row * D + l16 * E, f);
-  double u[E];
-  double ss = 0.0;
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const double x = f[i];
-    ss += x * x;
-    u[i] = (smask >> i & 1) ? -x : x;
-  }
-  dev::fwht16<E, double>(u, l16);
-  ss = dev::group16_sum(ss);
+  fwht32xP<P>(u, el.sg);
+  ss = group_sum_f64<P>(ss);
   const double n = sqrt(ss);
 
   double nstored;
   if (a.norm_f16) {
     const uint16_t h = dev::f64_to_f16_bits(n);
     nstored = dev::f16_bits_to_f64(h);
-    if (l16 == 0) static_cast<uint16_t*>(a.norms[TS])[rec] = h;
+    if (valid && lp == 0) static_cast<uint16_t*>(a.norms[TS])[rec] = h;
   } else {
     const float nf = float(n);
     nstored = nf;
-    if (l16 == 0) static_cast<float*>(a.norms[TS])[rec] = nf;
+    if (valid && lp == 0) static_cast<float*>(a.norms[TS])[rec] = nf;
   }
 
   // thresholds scaled by the norm; a zero row gets the middle code L/2
   double T[H - 1];
 #pragma unroll
   for (int j = 0; j < H - 1; ++j) T[j] = n > 0.0 ? a.tpos[TS][j] * n : INFINITY;
-  uint64_t packed = 0;
+  uint32_t w[LW];
+#pragma unroll
+  for (int k = 0; k < LW; ++k) w[k] = 0u;
   uint32_t code[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) {
@@ -196,13 +316,19 @@ __device__ __forceinline__ void encode_row(const EncodeArgs& a, int64_t bh, int6
 #pragma unroll
     for (int j = 0; j < H - 1; ++j) c += (au >= T[j]) ? 1u : 0u;
     code[i] = u[i] >= 0.0 ? uint32_t(H) + c : uint32_t(H - 1) - c;
-    packed |= uint64_t(code[i]) << (BITS * i);
+    // LSB-first bitstream: code i at bit BITS*i of the lane's LW dwords
+    const int pos = BITS * i;
+    w[pos >> 5] |= code[i] << (pos & 31);
+    if ((pos & 31) + BITS > 32) w[(pos >> 5) + 1] |= code[i] >> (32 - (pos & 31));
   }
-  dev::store_bytes(a.codes[TS] + rec * REC + l16 * LANE_BYTES, packed, LANE_BYTES);
+  if (valid) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes[TS] + rec * REC + lp * (4 * LW));
+#pragma unroll
+    for (int k = 0; k < LW; ++k) dst[k] = w[k];
+  }
 
   if constexpr (QJL) {
     // residual in the rotated frame: r = (u - n_stored * c[code]) / sqrt(d)
-    const uint32_t qmask = bitmap_bits(a.qsbits, l16 * E, E);
     const double inv_sqrt_d = 1.0 / sqrt(double(D));
     double r[E];
     double rr = 0.0;
@@ -213,29 +339,83 @@ __device__ __forceinline__ void encode_row(const EncodeArgs& a, int64_t bh, int6
       for (int k = 0; k < L; ++k) ci = (code[i] == uint32_t(k)) ? a.cen_k[k] : ci;
       const double ri = (u[i] - nstored * ci) * inv_sqrt_d;
       rr += ri * ri;
-      r[i] = (qmask >> i & 1) ? -ri : ri;
+      r[i] = (el.qmask >> i & 1) ? -ri : ri;
     }
-    rr = dev::group16_sum(rr);
-    dev::fwht16<E, double>(r, l16);
+    rr = group_sum_f64<P>(rr);
+    fwht32xP<P>(r, el.sg);
     uint32_t bits = 0;
 #pragma unroll
     for (int i = 0; i < E; ++i) bits |= (r[i] < 0.0 ? 1u : 0u) << i;
-    dev::store_bytes(a.qbits + rec * (D / 8) + l16 * (E / 8), bits, E / 8);
-    if (l16 == 0) a.rnorm[rec] = dev::f64_to_f16_bits(sqrt(rr));
+    if (valid) {
+      reinterpret_cast<uint32_t*>(a.qbits + rec * (D / 8))[lp] = bits;
+      if (lp == 0) a.rnorm[rec] = dev::f64_to_f16_bits(sqrt(rr));
+    }
   }
 }
 
-// grid: x = 16-token groups, y = (batch, KV head) (strided), z = tensor.
-template <int D, int BK, int BV, bool QJL>
+// Persistent encode of K and V: a work item is 64/P consecutive rows (one
+// wave) of one (tensor, batch*KV head) pair, numbered
+// (tensor * BH + bh) * groups + group. Each wave walks the items with the
+// grid's wave count as stride and loads the next item's input while it
+// encodes the current one.
+template <int D, int BK, int BV, bool QJL, int DT>
 __global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
-  const int l16 = threadIdx.x & 15;
-  const int64_t t = int64_t(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  if (t >= a.n_new) return;                  // a whole 16-lane group leaves together
-  for (int64_t bh = blockIdx.y; bh < a.BH; bh += gridDim.y) {
-    if (blockIdx.z == 0)
-      encode_row<D, BK, QJL, 0>(a, bh, t, l16);
+  constexpr int IW = DT == 0 ? 4 : 2;        // input bytes per coordinate
+  constexpr int P = D / 32;
+  constexpr int RPW = 64 / P;                // rows per work item
+  const int lane = threadIdx.x & 63;
+  const uint32_t groups = uint32_t((a.n_new + RPW - 1) / RPW);
+  const uint32_t per_tensor = uint32_t(a.BH) * groups;
+  const uint32_t items = 2 * per_tensor;
+  const uint32_t nwave = gridDim.x * (blockDim.x >> 6);
+  uint32_t item = blockIdx.x * (blockDim.x >> 6) +
+                  uint32_t(__builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)));
+  if (item >= items) return;
+
+  EncodeLane<IW> el;
+  el.lp = lane & (P - 1);
+  el.smask = pick8(a.sbits, el.lp);
+  el.qmask = QJL ? pick8(a.qsbits, el.lp) : 0u;
+  if constexpr (IW == 2) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      el.pm[j] = ((el.smask >> (2 * j) & 1u) << 15) | ((el.smask >> (2 * j + 1) & 1u) << 31);
+  }
+#pragma unroll
+  for (int s = 0; s < 3; ++s) el.sg[s] = (el.lp >> s & 1) ? -1.0 : 1.0;
+  const int rl = lane / P;
+
+  struct Where { int z, bh; int64_t t; };
+  auto where = [&](uint32_t it) {
+    Where w;
+    w.z = it >= per_tensor ? 1 : 0;
+    const uint32_t rem = it - (w.z ? per_tensor : 0u);
+    w.bh = int(rem / groups);
+    w.t = int64_t(rem - uint32_t(w.bh) * groups) * RPW + rl;
+    return w;
+  };
+  auto fetch = [&](uint32_t it, RowWords<IW>& rw) {
+    const uint32_t c = it < items ? it : items - 1;    // past the last item: reload it
+    const Where w = where(c);
+    load_words<D, IW>(a, w.z, w.bh, w.t, el.lp, rw);
+  };
+
+  // one input buffer: it is converted to doubles before the next item's
+  // loads are issued into it
+  RowWords<IW> rw;
+  fetch(item, rw);
+  for (;;) {
+    double u[32];
+    const double ss = words_to_f64<DT>(rw, el, u);
+    const Where w = where(item);
+    item += nwave;
+    fetch(item, rw);
+    const bool valid = w.t < a.n_new;
+    if (w.z == 0)
+      encode_row<D, BK, QJL, 0, IW>(a, w.bh, w.t, valid, el, u, ss);
     else
-      encode_row<D, BV, false, 1>(a, bh, t, l16);
+      encode_row<D, BV, false, 1, IW>(a, w.bh, w.t, valid, el, u, ss);
+    if (item >= items) break;
   }
 }
 
