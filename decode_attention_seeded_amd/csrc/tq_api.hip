@@ -136,7 +136,7 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
   da.S = p.splits;
   da.seed = seed;
   (void)rotate;
-  qa.qq_pairs = p.wide;
+  qa.qq_pairs = p.wide != 0;
   int st1 = launch_qprep(d, qa, st);
   if (st1 != TQ_OK) return st1;
   DecodeLauncher fn = decode_launcher(d, bk);

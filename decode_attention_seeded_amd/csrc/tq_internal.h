@@ -58,7 +58,7 @@ inline int norm_bytes(const tq_config* cfg) { return cfg->norm_dtype == TQ_F16 ?
 //   tps:    tokens per split (multiple of tile)
 struct DecodePlan {
   int G = 0, gk = 0, chunks = 0, tile = 0, splits = 0;
-  int wide = 0;      // 1: the wave-private wide kernel (d 128, 2/4-bit values, no QJL)
+  int wide = 0;      // 1: wave-private kernel on the VALU, 2: on the matrix cores
   int64_t tps = 0;
   // workspace section offsets (bytes)
   size_t off_qp = 0, off_qq = 0, off_ml = 0, off_acc = 0, total = 0;
@@ -79,6 +79,11 @@ inline bool use_wide(int d, int bits_v, int qjl) {
   (void)qjl;
   return (d == 128 || d == 256) && (bits_v == 2 || bits_v == 4);
 }
+
+// Waves per workgroup of the matrix-core decode kernel, and whether a format
+// runs it (2- or 4-bit values, no QJL correction).
+constexpr int mx_waves(int d) { return 8 + 0 * d; }
+inline bool use_mx(int d, int bits_v, int qjl) { return use_wide(d, bits_v, qjl) && !qjl; }
 
 // Fills a plan; returns TQ_OK or a negative status.
 int plan_decode(int d, int bits_v, int qjl, int B, int Hq, int Hkv, int64_t n_ctx,

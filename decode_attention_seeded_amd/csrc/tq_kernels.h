@@ -1572,6 +1572,355 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 }
 
 // ---------------------------------------------------------------------------
+// Split-K decode on the matrix cores, d = 128 or 256 with 2- or 4-bit values
+// and no QJL correction. Workgroup, tile and softmax structure are those of
+// k_decode_wide (W waves, each with its own online-softmax pass over
+// interleaved 64-token tiles, combined once at the end); the two
+// contractions of a tile run as MFMAs on fp16 operands dequantized through
+// the pair tables:
+//   scores  S[g][t] = q_g . k_t with v_mfma_f32_4x4x4_16b_f16: 16 blocks of
+//           4 tokens, so lane t supplies 4 coordinates of its own key (two
+//           pair lookups) as the B operand and receives the GK scores of
+//           token t. The query is the A operand, broadcast from one block
+//           (CBSZ 4, ABID j mod 16): lane (block b, row m) keeps only the
+//           quads j = b, b + 16, ... of head m.
+//   values  O[g][c] += sum_t p[g][t] v_t[c] with v_mfma_f32_16x16x16_f16 per
+//           16 tokens: A = weights (row = head, rows past GK zero), B =
+//           value pair lookups; lane (kq = lane / 16, column n = lane % 16)
+//           holds tokens 4kq .. 4kq + 3 of the block for coordinates
+//           VJ*n .. VJ*n + VJ - 1, one instruction per offset j < VJ. The
+//           sums land in lanes 0..15 (register g = head g).
+// ---------------------------------------------------------------------------
+
+typedef _Float16 mx_h4 __attribute__((ext_vector_type(4)));
+typedef float mx_f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t mx_u2 __attribute__((ext_vector_type(2)));
+
+template <int D, int BK, int BV>
+struct MxTile {
+  static constexpr int SB = D * BV / 128;       // value bytes per (token, lane column)
+  static constexpr int SW = (SB + 3) / 4;
+  uint32_t kw[D * BK / 32];     // key row of the lane's token
+  uint32_t kn, vn;              // its key and value norms (f16 or f32 bits)
+  uint32_t vx[16][SW];          // value slices: token 16*(i/4) + 4*kq + i%4
+};
+
+// For two tokens' slices x, y of 8 coordinates: byte b of *lo is the value
+// pair-table index (x code, y code) of coordinate 2b, of *hi of 2b + 1.
+template <int BV>
+__device__ __forceinline__ void mx_pair_words(uint32_t x, uint32_t y, uint32_t* lo,
+                                              uint32_t* hi) {
+  if constexpr (BV == 4) {
+    *lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
+    *hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
+  } else {
+    const uint32_t w = spread2to4(x & 0xFFFFu) | (spread2to4(y & 0xFFFFu) << 2);
+    *lo = w & 0x0F0F0F0Fu;
+    *hi = (w >> 4) & 0x0F0F0F0Fu;
+  }
+}
+
+template <int D, int BK, int BV, int GK, bool NF16>
+__global__ void __launch_bounds__(64 * mx_waves(D))
+    __attribute__((amdgpu_waves_per_eu(mx_waves(D) / 4)))
+k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
+  static_assert(D == 128 || D == 256, "matrix-core decode: d 128 or 256");
+  static_assert(BV == 2 || BV == 4, "matrix-core decode: 2- or 4-bit values");
+  static_assert(GK == 1 || GK == 2 || GK == 4, "heads per workgroup");
+  constexpr int W = mx_waves(D);
+  constexpr int TW = 64;                       // tokens per wave tile
+  constexpr int T = W * TW;                    // tokens per workgroup round
+  constexpr int NT = 64 * W;
+  constexpr int KREC = D * BK / 8;
+  constexpr int VREC = D * BV / 8;
+  constexpr int KW = D * BK / 32;
+  constexpr int VJ = D / 16;                   // coordinates per lane column
+  constexpr int SB = MxTile<D, BK, BV>::SB;
+  constexpr int KE = 1 << (2 * BK);
+  constexpr int VE = 1 << (2 * BV);
+  constexpr int KT_BYTES = KE * 128;           // 32 copies, 128-B entry stride
+  constexpr int VT_BYTES = VE * 256;           // 64 copies, 256-B entry stride
+  constexpr int NQ = D / 64;                   // query quads kept per lane
+  constexpr int PX = GK * TW / 2;              // weight dwords per wave tile
+  constexpr float kRescale = 8.0f;
+  using Tile = MxTile<D, BK, BV>;
+  static_assert(KW % 4 == 0, "key rows are whole 16-byte loads");
+  static_assert(SB == 2 || SB == 4 || SB == 8, "value slice width");
+
+  constexpr int SLAB_BYTES = W * GK * D * 4;   // per-wave partials, after the loop
+  constexpr int TAB_BYTES = KT_BYTES + VT_BYTES;
+  __shared__ __attribute__((aligned(16)))
+  uint8_t tabs[TAB_BYTES > SLAB_BYTES ? TAB_BYTES : SLAB_BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t pex[W][2][PX];
+  __shared__ uint32_t qs[GK * (D / 2)];
+  __shared__ float mlx[W][GK][2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;                   // V phase: lane column / A row
+  const int kq = lane >> 4;                    // V phase: token quad
+  const uint32_t rl4 = uint32_t(lane & 31) << 2;
+  const uint32_t vl4 = uint32_t(lane) << 2;
+  const int split = blockIdx.x;
+  const int unit = blockIdx.y;
+  const int chunk = unit % a.chunks;
+  const int bkv = unit / a.chunks;
+  const int b = bkv / a.Hkv;
+  const int kvh = bkv - b * a.Hkv;
+  const int h0 = kvh * a.G + chunk * GK;
+  const int64_t head0 = int64_t(b) * a.Hq + h0;
+
+  for (int i = tid; i < KE * 32; i += NT) {
+    const int e = i >> 5;
+    *reinterpret_cast<uint32_t*>(tabs + (e << 7) + ((i & 31) << 2)) =
+        dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
+  }
+  for (int i = tid; i < VE * 64; i += NT) {
+    const int e = i >> 6;
+    *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << 8) + ((i & 63) << 2)) =
+        dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
+  }
+  const uint8_t* vtab = tabs + KT_BYTES;
+  for (int i = tid; i < GK * (D / 2); i += NT) qs[i] = qp2_all[head0 * (D / 2) + i];
+  __syncthreads();
+
+  // query quads for the broadcast A operand: lane (block lane/4, row lane%4)
+  // keeps coordinates 4j .. 4j+3 of head lane%4 for j = lane/4 + 16*i
+  mx_u2 qa[NQ];
+  {
+    const int qm = lane & 3, qb = lane >> 2;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int j = qb + 16 * i;
+      if (qm < GK) {
+        qa[i][0] = qs[qm * (D / 2) + 2 * j];
+        qa[i][1] = qs[qm * (D / 2) + 2 * j + 1];
+      } else {
+        qa[i][0] = 0u;
+        qa[i][1] = 0u;
+      }
+    }
+  }
+
+  const int64_t t_begin = int64_t(split) * a.tps;
+  const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
+  const int64_t row0 = int64_t(bkv) * a.capacity;
+  constexpr int nb = NF16 ? 2 : 4;
+  const int iters = int((t_end - t_begin + T - 1) / T);
+
+  auto rows_left = [&](int64_t base) -> uint32_t {
+    const int64_t n = t_end - base;
+    return uint32_t(n <= 0 ? 0 : (n < TW ? n : TW));
+  };
+  const uint32_t ko0 = uint32_t(lane) * KREC;
+  const uint32_t no0 = uint32_t(lane) * nb;
+  const uint32_t vo0 = uint32_t(4 * kq) * VREC + uint32_t(col) * SB;
+  auto load = [&](int64_t base, Tile& t) {
+    const uint32_t n = rows_left(base);
+    const auto rk = dev::buffer_rsrc(a.kc + (row0 + base) * KREC, n * KREC);
+#pragma unroll
+    for (int k = 0; k < KW / 4; ++k) {
+      const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rk, ko0, 16 * k, 0);
+      t.kw[4 * k] = q4[0]; t.kw[4 * k + 1] = q4[1]; t.kw[4 * k + 2] = q4[2];
+      t.kw[4 * k + 3] = q4[3];
+    }
+    const uint8_t* kn_p = static_cast<const uint8_t*>(a.kn) + (row0 + base) * nb;
+    const uint8_t* vn_p = static_cast<const uint8_t*>(a.vn) + (row0 + base) * nb;
+    if constexpr (NF16) {
+      t.kn = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(kn_p, n * nb), no0, 0, 0);
+      t.vn = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(vn_p, n * nb), no0, 0, 0);
+    } else {
+      t.kn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(kn_p, n * nb), no0, 0, 0);
+      t.vn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(vn_p, n * nb), no0, 0, 0);
+    }
+    const auto rv = dev::buffer_rsrc(a.vc + (row0 + base) * VREC, n * VREC);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int so = (16 * (i >> 2) + (i & 3)) * VREC;
+      if constexpr (SB == 8) {
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rv, vo0, so, 0);
+        t.vx[i][0] = v2[0];
+        t.vx[i][Tile::SW - 1] = v2[1];
+      } else if constexpr (SB == 4) {
+        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo0, so, 0);
+      } else {
+        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b16(rv, vo0, so, 0);
+      }
+    }
+  };
+
+  float m_run[GK], lpart[GK];
+  mx_f4 acc[VJ];
+#pragma unroll
+  for (int g = 0; g < GK; ++g) {
+    m_run[g] = -INFINITY;
+    lpart[g] = 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < VJ; ++j) acc[j] = mx_f4{0.f, 0.f, 0.f, 0.f};
+
+  auto process = [&](int64_t base, uint32_t* px, const Tile& cur) {
+    // ---------------- scores: lane = token, 4 coordinates per MFMA
+    const bool valid = base + lane < t_end;
+    mx_f4 sk[2] = {mx_f4{0.f, 0.f, 0.f, 0.f}, mx_f4{0.f, 0.f, 0.f, 0.f}};
+    dev::static_for<0, D / 4>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const uint32_t ka0 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j) | rl4;
+      const uint32_t ka1 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j + 1) | rl4;
+      mx_u2 kb;
+      kb[0] = *reinterpret_cast<const uint32_t*>(tabs + ka0);
+      kb[1] = *reinterpret_cast<const uint32_t*>(tabs + ka1);
+      sk[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+          __builtin_bit_cast(mx_h4, qa[j / 16]), __builtin_bit_cast(mx_h4, kb), sk[j & 1], 4,
+          j % 16, 0);
+    });
+    const float knrm = NF16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
+    const float vnrm = NF16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn);
+    const float ks = knrm * a.kscale;
+    const float nv = vnrm * a.vscale;
+
+    // ---------------- online softmax with a lazily raised running max
+    uint16_t* p16 = reinterpret_cast<uint16_t*>(px);
+#pragma unroll
+    for (int g = 0; g < GK; ++g) {
+      const float s = (sk[0][g] + sk[1][g]) * ks;
+      if (__ballot(valid && s > m_run[g] + kRescale)) {        // wave-uniform
+        const float mx = dev::dpp_wave_max(valid ? s : -INFINITY);
+        const float m_new = fmaxf(m_run[g], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+        m_run[g] = m_new;
+        lpart[g] *= alpha;
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) acc[j][g] *= alpha;
+      }
+      // branch-free: rows past the split have zero norms and weight 0
+      const float e = __builtin_amdgcn_exp2f(s - m_run[g]);
+      const float p = valid ? e : 0.f;
+      lpart[g] += p;
+      p16[g * TW + lane] = __builtin_bit_cast(uint16_t, _Float16(p * nv));
+    }
+    // the weights written above are read back by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---------------- values: 16 tokens per MFMA, lane = (kq, column)
+    const bool arow = col < GK;
+    const uint16_t* prow = p16 + (arow ? col : 0) * TW + 4 * kq;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      mx_u2 pw = *reinterpret_cast<const mx_u2*>(prow + 16 * blk);
+      if (!arow) pw = mx_u2{0u, 0u};
+      const mx_h4 pa = __builtin_bit_cast(mx_h4, pw);
+#pragma unroll
+      for (int grp = 0; grp < VJ / 8; ++grp) {
+        uint32_t x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = cur.vx[4 * blk + i][BV == 4 ? grp : 0];
+          x[i] = (BV == 2 && grp == 1) ? (w >> 16) : w;
+        }
+        uint32_t lo01, hi01, lo23, hi23;
+        mx_pair_words<BV>(x[0], x[1], &lo01, &hi01);
+        mx_pair_words<BV>(x[2], x[3], &lo23, &hi23);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8;
+          const uint32_t va01 = __builtin_amdgcn_perm((e & 1) ? hi01 : lo01, vl4, sel);
+          const uint32_t va23 = __builtin_amdgcn_perm((e & 1) ? hi23 : lo23, vl4, sel);
+          mx_u2 vb;
+          vb[0] = *reinterpret_cast<const uint32_t*>(vtab + va01);
+          vb[1] = *reinterpret_cast<const uint32_t*>(vtab + va23);
+          acc[8 * grp + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              pa, __builtin_bit_cast(mx_h4, vb), acc[8 * grp + e], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  {
+    const int64_t wb = t_begin + int64_t(wave) * TW;
+    uint32_t* px0 = pex[wave][0];
+    uint32_t* px1 = pex[wave][1];
+    Tile ta, tb;
+    load(wb, ta);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int it = 0; it < iters; it += 2) {
+      const int64_t base = wb + int64_t(it) * T;
+      load(base + T, tb);
+      process(base, px0, ta);
+      if (it + 1 >= iters) break;
+      load(base + 2 * T, ta);
+      process(base + T, px1, tb);
+    }
+  }
+
+  // ---------------- combine the waves, then R^T of the weighted sum
+  float lw[GK];
+#pragma unroll
+  for (int g = 0; g < GK; ++g) lw[g] = dev::wave_sum(lpart[g]);
+  __syncthreads();                       // tables are dead: reuse them below
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < GK; ++g) {
+      mlx[wave][g][0] = m_run[g];
+      mlx[wave][g][1] = lw[g];
+    }
+  }
+  __syncthreads();
+  float* slab = reinterpret_cast<float*>(tabs);          // [W][GK][D]
+  float M[GK];
+#pragma unroll
+  for (int g = 0; g < GK; ++g) {
+    M[g] = mlx[0][g][0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) M[g] = fmaxf(M[g], mlx[w][g][0]);
+    const float f = m_run[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - M[g]);
+    if (lane < 16) {
+#pragma unroll
+      for (int j = 0; j < VJ; ++j) slab[(wave * GK + g) * D + VJ * lane + j] = acc[j][g] * f;
+    }
+  }
+  __syncthreads();
+  float* obuf = reinterpret_cast<float*>(pex);            // [GK][D]
+  static_assert(sizeof(pex) >= GK * D * 4, "output staging fits the weight slots");
+  for (int i = tid; i < GK * D; i += NT) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) sum += slab[w * GK * D + i];
+    obuf[i] = sum;
+  }
+  __syncthreads();
+  if (tid < GK) {
+    float l = 0.f;
+    for (int w = 0; w < W; ++w) {
+      const float mw = mlx[w][tid][0];
+      if (mw != -INFINITY) l += mlx[w][tid][1] * __builtin_amdgcn_exp2f(mw - M[tid]);
+    }
+    float* ml = a.ml + ((head0 + tid) * a.S + split) * 2;
+    ml[0] = M[tid];
+    ml[1] = l;
+  }
+  if (tid < 16 * GK) {
+    constexpr int E = D / 16;
+    const int g = tid >> 4, l16 = tid & 15;
+    float v[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = obuf[g * D + l16 * E + i];
+    dev::fwht16<E, float>(v, l16);
+    const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
+    const float nn = 1.0f / sqrtf(float(D));
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = (smask >> i & 1) ? -v[i] * nn : v[i] * nn;
+    float4* dst = reinterpret_cast<float4*>(a.acc + ((head0 + g) * a.S + split) * D + l16 * E);
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k)
+      dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge of split partials (exact log-sum-exp in a fixed order) and 1/l.
 // The partials are already in the original frame, so every coordinate is
 // independent: grid (query head, block of 32 coordinates), 256 threads =

@@ -77,16 +77,19 @@ def test_split_plan_and_workspace():
     s = tq.tq_num_splits(cfg, 1, 32, 8, 524288)
     assert s >= 8
     assert tq.tq_num_splits(cfg, 1, 32, 8, 1) == 1
-    # clamped to tiles: the wide kernel's workgroup rounds are 64 tokens per
-    # wave, 16 waves at d 128 and 8 at d 256; the other formats use
+    # clamped to tiles: workgroup rounds are 64 tokens per wave; the
+    # matrix-core kernel (2/4-bit values, no QJL) runs 8 waves, the VALU
+    # wave-private kernel with QJL 12 at d 128; the other formats use
     # 256-token tiles (d 128)
     assert tq.tq_num_splits(cfg, 1, 32, 8, 300, splits=7) == 1
-    assert tq.tq_num_splits(cfg, 1, 32, 8, 2100, splits=7) == 3
+    assert tq.tq_num_splits(cfg, 1, 32, 8, 2100, splits=7) == 5
+    cfgq = tq.Config(d=128, bits_k=3, bits_v=4, qjl=True)
+    assert tq.tq_num_splits(cfgq, 1, 32, 8, 2100, splits=7) == 3
     cfg256 = tq.Config(d=256, bits_k=2, bits_v=2)
     assert tq.tq_num_splits(cfg256, 8, 16, 4, 1100, splits=7) == 3
     cfg3 = tq.Config(d=128, bits_k=3, bits_v=3)
     assert tq.tq_num_splits(cfg3, 1, 32, 8, 300, splits=7) == 2
-    # default: one round of ~256 workgroups for the wide kernel
+    # default: one round of ~256 workgroups for the wave-private kernels
     assert s == 32
     ws = tq.tq_workspace_bytes(cfg, 1, 32, 8, 524288)
     assert ws >= 32 * 128 * 4 + 32 * s * (128 + 2) * 4
