@@ -137,7 +137,12 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
   da.seed = seed;
   (void)rotate;
   qa.qq_pairs = p.wide != 0;
-  int st1 = launch_qprep(d, qa, st);
+  da.q_raw = qa.q;
+  da.q_dtype = qa.q_dtype;
+  da.qmult = qa.mult;
+  int st1 = TQ_OK;
+  // the matrix-core kernel rotates its own query rows
+  if (p.wide != 2) st1 = launch_qprep(d, qa, st);
   if (st1 != TQ_OK) return st1;
   DecodeLauncher fn = decode_launcher(d, bk);
   if (!fn) return TQ_ERR_UNSUPPORTED;

@@ -80,6 +80,9 @@ struct DecodeArgs {
   float cbk[16];          // alpha_k * key centroids (exact in fp16 to ~1e-4)
   float cbv[16];          // alpha_v * value centroids
   uint64_t seed;          // rotation seed: partials are rotated back (R^T)
+  const void* q_raw;      // [B*Hq][D] queries, for kernels that rotate them themselves
+  int q_dtype;
+  float qmult;            // scale * log2(e)
 };
 
 struct MergeArgs {
@@ -1682,7 +1685,23 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
         dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
   }
   const uint8_t* vtab = tabs + KT_BYTES;
-  for (int i = tid; i < GK * (D / 2); i += NT) qs[i] = qp2_all[head0 * (D / 2) + i];
+  // the GK query rows, rotated and scaled here (one 16-lane group per head):
+  // R q * scale * log2(e), as fp16 pairs
+  (void)qp2_all;
+  if (tid < 16 * GK) {
+    constexpr int E = D / 16;
+    const int g = tid >> 4, l16 = tid & 15;
+    float v[E];
+    dev::load_row_part<E>(a.q_raw, a.q_dtype, (head0 + g) * D + l16 * E, v);
+    const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
+#pragma unroll
+    for (int i = 0; i < E; ++i) if (smask >> i & 1) v[i] = -v[i];
+    dev::fwht16<E, float>(v, l16);
+    const float mult = a.qmult / sqrtf(float(D));
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i)
+      qs[g * (D / 2) + l16 * (E / 2) + i] = dev::pack_f16x2(v[2 * i] * mult, v[2 * i + 1] * mult);
+  }
   __syncthreads();
 
   // query quads for the broadcast A operand: lane (block lane/4, row lane%4)
@@ -1764,16 +1783,33 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     // ---------------- scores: lane = token, 4 coordinates per MFMA
     const bool valid = base + lane < t_end;
     mx_f4 sk[2] = {mx_f4{0.f, 0.f, 0.f, 0.f}, mx_f4{0.f, 0.f, 0.f, 0.f}};
-    dev::static_for<0, D / 4>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const uint32_t ka0 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j) | rl4;
-      const uint32_t ka1 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j + 1) | rl4;
-      mx_u2 kb;
-      kb[0] = *reinterpret_cast<const uint32_t*>(tabs + ka0);
-      kb[1] = *reinterpret_cast<const uint32_t*>(tabs + ka1);
-      sk[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
-          __builtin_bit_cast(mx_h4, qa[j / 16]), __builtin_bit_cast(mx_h4, kb), sk[j & 1], 4,
-          j % 16, 0);
+    // software pipeline over batches of KB instructions: the lookups of
+    // batch n + 1 are issued before the MFMAs of batch n, so the LDS latency
+    // overlaps matrix work instead of stalling the wave
+    constexpr int KB = 4;
+    mx_u2 kb[2][KB];
+    auto k_issue = [&](auto nc, mx_u2(&dst)[KB]) {
+      constexpr int n = decltype(nc)::value;
+      dev::static_for<0, KB>([&](auto ic) {
+        constexpr int j = n * KB + decltype(ic)::value;
+        const uint32_t ka0 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j) | rl4;
+        const uint32_t ka1 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j + 1) | rl4;
+        dst[decltype(ic)::value][0] = *reinterpret_cast<const uint32_t*>(tabs + ka0);
+        dst[decltype(ic)::value][1] = *reinterpret_cast<const uint32_t*>(tabs + ka1);
+      });
+    };
+    k_issue(std::integral_constant<int, 0>{}, kb[0]);
+    dev::static_for<0, D / 4 / KB>([&](auto nc) {
+      constexpr int n = decltype(nc)::value;
+      if constexpr (n + 1 < D / 4 / KB) k_issue(std::integral_constant<int, n + 1>{}, kb[(n + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      dev::static_for<0, KB>([&](auto ic) {
+        constexpr int j = n * KB + decltype(ic)::value;
+        sk[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+            __builtin_bit_cast(mx_h4, qa[j / 16]),
+            __builtin_bit_cast(mx_h4, kb[n & 1][decltype(ic)::value]), sk[j & 1], 4, j % 16, 0);
+      });
+      __builtin_amdgcn_sched_barrier(0);
     });
     const float knrm = NF16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
     const float vnrm = NF16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn);
@@ -1808,35 +1844,51 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     // ---------------- values: 16 tokens per MFMA, lane = (kq, column)
     const bool arow = col < GK;
     const uint16_t* prow = p16 + (arow ? col : 0) * TW + 4 * kq;
+    // the same pipeline over (block, group of 8 coordinates) steps: the
+    // lookups of step n + 1 are in flight during the MFMAs of step n
+    constexpr int NG = VJ / 8;
+    constexpr int NS = 4 * NG;
+    mx_u2 vb[2][8];
+    auto v_issue = [&](auto nc, mx_u2(&dst)[8]) {
+      constexpr int n = decltype(nc)::value;
+      constexpr int blk = n / NG, grp = n % NG;
+      uint32_t x[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = cur.vx[4 * blk + i][BV == 4 ? grp : 0];
+        x[i] = (BV == 2 && grp == 1) ? (w >> 16) : w;
+      }
+      uint32_t lo01, hi01, lo23, hi23;
+      mx_pair_words<BV>(x[0], x[1], &lo01, &hi01);
+      mx_pair_words<BV>(x[2], x[3], &lo23, &hi23);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8;
+        const uint32_t va01 = __builtin_amdgcn_perm((e & 1) ? hi01 : lo01, vl4, sel);
+        const uint32_t va23 = __builtin_amdgcn_perm((e & 1) ? hi23 : lo23, vl4, sel);
+        dst[e][0] = *reinterpret_cast<const uint32_t*>(vtab + va01);
+        dst[e][1] = *reinterpret_cast<const uint32_t*>(vtab + va23);
+      }
+    };
+    mx_h4 pa[4];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       mx_u2 pw = *reinterpret_cast<const mx_u2*>(prow + 16 * blk);
       if (!arow) pw = mx_u2{0u, 0u};
-      const mx_h4 pa = __builtin_bit_cast(mx_h4, pw);
-#pragma unroll
-      for (int grp = 0; grp < VJ / 8; ++grp) {
-        uint32_t x[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = cur.vx[4 * blk + i][BV == 4 ? grp : 0];
-          x[i] = (BV == 2 && grp == 1) ? (w >> 16) : w;
-        }
-        uint32_t lo01, hi01, lo23, hi23;
-        mx_pair_words<BV>(x[0], x[1], &lo01, &hi01);
-        mx_pair_words<BV>(x[2], x[3], &lo23, &hi23);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8;
-          const uint32_t va01 = __builtin_amdgcn_perm((e & 1) ? hi01 : lo01, vl4, sel);
-          const uint32_t va23 = __builtin_amdgcn_perm((e & 1) ? hi23 : lo23, vl4, sel);
-          mx_u2 vb;
-          vb[0] = *reinterpret_cast<const uint32_t*>(vtab + va01);
-          vb[1] = *reinterpret_cast<const uint32_t*>(vtab + va23);
-          acc[8 * grp + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              pa, __builtin_bit_cast(mx_h4, vb), acc[8 * grp + e], 0, 0, 0);
-        }
-      }
+      pa[blk] = __builtin_bit_cast(mx_h4, pw);
     }
+    v_issue(std::integral_constant<int, 0>{}, vb[0]);
+    dev::static_for<0, NS>([&](auto nc) {
+      constexpr int n = decltype(nc)::value;
+      constexpr int blk = n / NG, grp = n % NG;
+      if constexpr (n + 1 < NS) v_issue(std::integral_constant<int, n + 1>{}, vb[(n + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        acc[8 * grp + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+            pa[blk], __builtin_bit_cast(mx_h4, vb[n & 1][e]), acc[8 * grp + e], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   {
