@@ -1984,49 +1984,58 @@ constexpr int kMaxSplits = 4096;
 template <int D>
 __global__ void __launch_bounds__(256) k_merge(MergeArgs a) {
   __shared__ float wts[kMaxSplits];
-  __shared__ float red[256];
+  __shared__ float red[2][4];
   __shared__ float part[8][32];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int64_t head = blockIdx.x;
   const int cb = blockIdx.y;
-  const float* ml = a.ml + head * a.S * 2;
-
-  float mx = -INFINITY;
-  for (int s = tid; s < a.S; s += 256) mx = fmaxf(mx, ml[2 * s]);
-  red[tid] = mx;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  const float M = red[0];
-  __syncthreads();
-  float l = 0.f;
-  for (int s = tid; s < a.S; s += 256) {
-    const float w = exp2f(ml[2 * s] - M);
-    wts[s] = w;
-    l = fmaf(ml[2 * s + 1], w, l);
-  }
-  red[tid] = l;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] += red[tid + o];
-    __syncthreads();
-  }
-  const float inv_l = 1.f / red[0];
-
+  const float2* ml = reinterpret_cast<const float2*>(a.ml + head * a.S * 2);
   const int c = tid & 31, sg = tid >> 5;
   const float* col = a.acc + head * int64_t(a.S) * D + cb * 32 + c;
+
+  // the first U partials of this (coordinate, split group) are loaded
+  // before the reductions, so both memory round trips overlap
+  constexpr int U = 8;
+  float v0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int sp = sg + 8 * u;
+    v0[u] = sp < a.S ? col[int64_t(sp) * D] : 0.f;
+  }
+  float mx = -INFINITY;
+  for (int sp = tid; sp < a.S; sp += 256) mx = fmaxf(mx, ml[sp].x);
+  mx = dev::wave_max(mx);
+  if (lane == 0) red[0][wv] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  float l = 0.f;
+  for (int sp = tid; sp < a.S; sp += 256) {
+    const float2 m2 = ml[sp];
+    const float w = exp2f(m2.x - M);
+    wts[sp] = w;
+    l = fmaf(m2.y, w, l);
+  }
+  l = dev::wave_sum(l);
+  if (lane == 0) red[1][wv] = l;
+  __syncthreads();
+  const float inv_l = 1.f / ((red[1][0] + red[1][1]) + (red[1][2] + red[1][3]));
+
   float sum = 0.f;
-  int s = sg;
-  for (; s + 7 * 8 < a.S; s += 8 * 8) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int sp = sg + 8 * u;
+    if (sp < a.S) sum = fmaf(wts[sp], v0[u], sum);
+  }
+  int sp = sg + 8 * U;
+  for (; sp + 7 * 8 < a.S; sp += 8 * 8) {
     float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = col[int64_t(s + 8 * u) * D];
+    for (int u = 0; u < 8; ++u) v[u] = col[int64_t(sp + 8 * u) * D];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sum = fmaf(wts[s + 8 * u], v[u], sum);
+    for (int u = 0; u < 8; ++u) sum = fmaf(wts[sp + 8 * u], v[u], sum);
   }
-  for (; s < a.S; s += 8) sum = fmaf(wts[s], col[int64_t(s) * D], sum);
+  for (; sp < a.S; sp += 8) sum = fmaf(wts[sp], col[int64_t(sp) * D], sum);
   part[sg][c] = sum;
   __syncthreads();
   if (tid < 32) {

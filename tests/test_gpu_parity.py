@@ -90,6 +90,32 @@ def test_split_count_invariance_and_determinism():
     assert np.array_equal(again, gpu_decode(w, cfg, cache, q, w.N))
 
 
+def test_workspace_reuse_across_calls():
+    """One workspace, sized for the largest call, serves calls with different
+    split counts and context lengths back to back; each result equals the
+    same call on a fresh workspace (the output is poisoned before every
+    call, so a merge that did not run shows up)."""
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.small_workload(B=1, Hq=8, Hkv=2, N=3000, bits_k=3, bits_v=4, wid=128)
+    cfg, cache = gpu_encode(w)
+    qraw, _ = si.queries(w)
+    q = to_device(qraw, w.in_dtype)
+    calls = [(3000, 0), (3000, 5), (1700, 2), (3000, 1), (900, 0), (3000, 12), (3000, 5)]
+    nbytes = max(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, n, s) for n, s in calls)
+    ws = tq.workspace(nbytes)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    for n, s in calls:
+        out.fill_(float("nan"))
+        tq.tq_attend_decode(cfg, q, cache, n, out, ws, splits=s)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        fresh = gpu_decode(w, cfg, cache, q, n, splits=s)
+        log(f"n_ctx={n} splits={s}: reused workspace equals a fresh one")
+        assert np.isfinite(got).all()
+        assert np.array_equal(got, fresh), (n, s)
+
+
 @pytest.mark.parametrize("splits,scale", [(1, 0.0), (3, 0.0), (1, 0.35), (2, 0.35)])
 def test_many_tiles_per_split(splits, scale):
     """Long splits (up to 10 tiles of 512 tokens in one workgroup, every
