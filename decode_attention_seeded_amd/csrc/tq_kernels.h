@@ -1623,6 +1623,10 @@ __device__ __forceinline__ void mx_pair_words(uint32_t x, uint32_t y, uint32_t* 
   }
 }
 
+// tiles each wave loads ahead of the one it processes (1 or 2): two where
+// three tile buffers still fit the register budget without spilling
+constexpr int mx_prefetch(int d, int bk) { return d == 128 && bk < 4 ? 2 : 1; }
+
 template <int D, int BK, int BV, int GK, bool NF16>
 __global__ void __launch_bounds__(64 * mx_waves(D))
     __attribute__((amdgpu_waves_per_eu(mx_waves(D) / 4)))
@@ -1783,33 +1787,16 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     // ---------------- scores: lane = token, 4 coordinates per MFMA
     const bool valid = base + lane < t_end;
     mx_f4 sk[2] = {mx_f4{0.f, 0.f, 0.f, 0.f}, mx_f4{0.f, 0.f, 0.f, 0.f}};
-    // software pipeline over batches of KB instructions: the lookups of
-    // batch n + 1 are issued before the MFMAs of batch n, so the LDS latency
-    // overlaps matrix work instead of stalling the wave
-    constexpr int KB = 4;
-    mx_u2 kb[2][KB];
-    auto k_issue = [&](auto nc, mx_u2(&dst)[KB]) {
-      constexpr int n = decltype(nc)::value;
-      dev::static_for<0, KB>([&](auto ic) {
-        constexpr int j = n * KB + decltype(ic)::value;
-        const uint32_t ka0 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j) | rl4;
-        const uint32_t ka1 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j + 1) | rl4;
-        dst[decltype(ic)::value][0] = *reinterpret_cast<const uint32_t*>(tabs + ka0);
-        dst[decltype(ic)::value][1] = *reinterpret_cast<const uint32_t*>(tabs + ka1);
-      });
-    };
-    k_issue(std::integral_constant<int, 0>{}, kb[0]);
-    dev::static_for<0, D / 4 / KB>([&](auto nc) {
-      constexpr int n = decltype(nc)::value;
-      if constexpr (n + 1 < D / 4 / KB) k_issue(std::integral_constant<int, n + 1>{}, kb[(n + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
-      dev::static_for<0, KB>([&](auto ic) {
-        constexpr int j = n * KB + decltype(ic)::value;
-        sk[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
-            __builtin_bit_cast(mx_h4, qa[j / 16]),
-            __builtin_bit_cast(mx_h4, kb[n & 1][decltype(ic)::value]), sk[j & 1], 4, j % 16, 0);
-      });
-      __builtin_amdgcn_sched_barrier(0);
+    dev::static_for<0, D / 4>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const uint32_t ka0 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j) | rl4;
+      const uint32_t ka1 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j + 1) | rl4;
+      mx_u2 kb;
+      kb[0] = *reinterpret_cast<const uint32_t*>(tabs + ka0);
+      kb[1] = *reinterpret_cast<const uint32_t*>(tabs + ka1);
+      sk[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+          __builtin_bit_cast(mx_h4, qa[j / 16]), __builtin_bit_cast(mx_h4, kb), sk[j & 1], 4,
+          j % 16, 0);
     });
     const float knrm = NF16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
     const float vnrm = NF16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn);
@@ -1844,67 +1831,70 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     // ---------------- values: 16 tokens per MFMA, lane = (kq, column)
     const bool arow = col < GK;
     const uint16_t* prow = p16 + (arow ? col : 0) * TW + 4 * kq;
-    // the same pipeline over (block, group of 8 coordinates) steps: the
-    // lookups of step n + 1 are in flight during the MFMAs of step n
-    constexpr int NG = VJ / 8;
-    constexpr int NS = 4 * NG;
-    mx_u2 vb[2][8];
-    auto v_issue = [&](auto nc, mx_u2(&dst)[8]) {
-      constexpr int n = decltype(nc)::value;
-      constexpr int blk = n / NG, grp = n % NG;
-      uint32_t x[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = cur.vx[4 * blk + i][BV == 4 ? grp : 0];
-        x[i] = (BV == 2 && grp == 1) ? (w >> 16) : w;
-      }
-      uint32_t lo01, hi01, lo23, hi23;
-      mx_pair_words<BV>(x[0], x[1], &lo01, &hi01);
-      mx_pair_words<BV>(x[2], x[3], &lo23, &hi23);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8;
-        const uint32_t va01 = __builtin_amdgcn_perm((e & 1) ? hi01 : lo01, vl4, sel);
-        const uint32_t va23 = __builtin_amdgcn_perm((e & 1) ? hi23 : lo23, vl4, sel);
-        dst[e][0] = *reinterpret_cast<const uint32_t*>(vtab + va01);
-        dst[e][1] = *reinterpret_cast<const uint32_t*>(vtab + va23);
-      }
-    };
-    mx_h4 pa[4];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
       mx_u2 pw = *reinterpret_cast<const mx_u2*>(prow + 16 * blk);
       if (!arow) pw = mx_u2{0u, 0u};
-      pa[blk] = __builtin_bit_cast(mx_h4, pw);
-    }
-    v_issue(std::integral_constant<int, 0>{}, vb[0]);
-    dev::static_for<0, NS>([&](auto nc) {
-      constexpr int n = decltype(nc)::value;
-      constexpr int blk = n / NG, grp = n % NG;
-      if constexpr (n + 1 < NS) v_issue(std::integral_constant<int, n + 1>{}, vb[(n + 1) & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+      const mx_h4 pa = __builtin_bit_cast(mx_h4, pw);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        acc[8 * grp + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-            pa[blk], __builtin_bit_cast(mx_h4, vb[n & 1][e]), acc[8 * grp + e], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    });
+      for (int grp = 0; grp < VJ / 8; ++grp) {
+        uint32_t x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w = cur.vx[4 * blk + i][BV == 4 ? grp : 0];
+          x[i] = (BV == 2 && grp == 1) ? (w >> 16) : w;
+        }
+        uint32_t lo01, hi01, lo23, hi23;
+        mx_pair_words<BV>(x[0], x[1], &lo01, &hi01);
+        mx_pair_words<BV>(x[2], x[3], &lo23, &hi23);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8;
+          const uint32_t va01 = __builtin_amdgcn_perm((e & 1) ? hi01 : lo01, vl4, sel);
+          const uint32_t va23 = __builtin_amdgcn_perm((e & 1) ? hi23 : lo23, vl4, sel);
+          mx_u2 vb;
+          vb[0] = *reinterpret_cast<const uint32_t*>(vtab + va01);
+          vb[1] = *reinterpret_cast<const uint32_t*>(vtab + va23);
+          acc[8 * grp + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              pa, __builtin_bit_cast(mx_h4, vb), acc[8 * grp + e], 0, 0, 0);
+        }
+      }
+    }
   };
 
   {
     const int64_t wb = t_begin + int64_t(wave) * TW;
     uint32_t* px0 = pex[wave][0];
     uint32_t* px1 = pex[wave][1];
-    Tile ta, tb;
-    load(wb, ta);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int it = 0; it < iters; it += 2) {
-      const int64_t base = wb + int64_t(it) * T;
-      load(base + T, tb);
-      process(base, px0, ta);
-      if (it + 1 >= iters) break;
-      load(base + 2 * T, ta);
-      process(base + T, px1, tb);
+    if constexpr (mx_prefetch(D, BK) == 1) {
+      Tile ta, tb;
+      load(wb, ta);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int it = 0; it < iters; it += 2) {
+        const int64_t base = wb + int64_t(it) * T;
+        load(base + T, tb);
+        process(base, px0, ta);
+        if (it + 1 >= iters) break;
+        load(base + 2 * T, ta);
+        process(base + T, px1, tb);
+      }
+    } else {
+      Tile ta, tb, tc;
+      load(wb, ta);
+      __builtin_amdgcn_sched_barrier(0);
+      load(wb + T, tb);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int it = 0; it < iters; it += 3) {
+        const int64_t base = wb + int64_t(it) * T;
+        load(base + 2 * T, tc);
+        process(base, px0, ta);
+        if (it + 1 >= iters) break;
+        load(base + 3 * T, ta);
+        process(base + T, px1, tb);
+        if (it + 2 >= iters) break;
+        load(base + 4 * T, tb);
+        process(base + 2 * T, px0, tc);
+      }
     }
   }
 

@@ -40,6 +40,12 @@ SMALL = {
     # last DPP dot of the K phase closely (dot-result wait states)
     "d128_k3v4_f32norm_g1": dict(B=2, Hq=2, Hkv=2, N=1500, bits_k=3, bits_v=4,
                                  norm_dtype="f32", wid=111),
+    # matrix-core decode formats not covered above: d = 256 with 4-bit values
+    # (two-dword value slices), 2-bit keys at d = 128, 4-bit keys at d = 256
+    "d256_k3v4_g2": dict(B=1, Hq=4, Hkv=2, d=256, N=700, bits_k=3, bits_v=4, wid=112),
+    "d256_k4v2_f32norm_g4": dict(B=1, Hq=4, Hkv=1, d=256, N=650, bits_k=4, bits_v=2,
+                                 norm_dtype="f32", wid=113),
+    "d128_k2v4_g4": dict(B=1, Hq=8, Hkv=2, N=800, bits_k=2, bits_v=4, wid=114),
 }
 
 
