@@ -223,6 +223,34 @@ def main():
         torch.cuda.synchronize()
         enc_us = a.elapsed_time(b) * 1e3 / 20
 
+    # single-token generation step (append token N-1, attend over N): the
+    # fused entry point against the two calls it replaces, on the same cache
+    k1, v1 = K[:, :, w.N - 1:].contiguous(), V[:, :, w.N - 1:].contiguous()
+
+    def time_calls(fn, n=20):
+        for _ in range(3):
+            fn()
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    def two_calls():
+        tq.tq_encode_kv(cfg, k1, v1, w.N - 1, cache)
+        tq.tq_attend_decode(cfg, q, cache, w.N, out, ws)
+
+    single = {
+        "two_calls_us": round(time_calls(two_calls), 2),
+        "fused_us": round(time_calls(
+            lambda: tq.tq_append_attend_decode(cfg, k1, v1, q, cache, w.N, out, ws)), 2),
+    }
+    log(f"single-token step: encode + decode {single['two_calls_us']} us, "
+        f"fused {single['fused_us']} us")
+
     # algorithmic bytes of one decode call: every packed plane over N tokens,
     # plus q in and out
     cache_bytes, _ = tq.tq_cache_bytes(cfg, w.B, w.Hkv, w.N)
@@ -289,6 +317,7 @@ def main():
         "decode_call_us": round(dec_avg_us, 2),
         "decode_kv_tokens_per_s": round(w.B * w.N / (dec_avg_us * 1e-6), 1),
         "append_encode_us": round(enc_us, 2) if enc_us else None,
+        "single_token_step": single,
         "bulk_encode_ms": round(bulk_ms, 3),
         "algorithmic_bytes_per_decode": alg_bytes,
         "dense_bf16": dense,

@@ -2,13 +2,15 @@
 
 The work happens in libtq.so (hand-written HIP, C ABI in include/tq.h); this
 package is its thin ctypes binding. See binding.py for the entry points:
-tq_rht, tq_encode_kv, tq_qjl_sketch, tq_attend_decode (+ host helpers).
+tq_rht, tq_encode_kv, tq_qjl_sketch, tq_attend_decode, tq_append_attend_decode
+(+ host helpers).
 """
 
 from .binding import (  # noqa: F401
     EXPORTS, LIB_PATH, TQ_BF16, TQ_ERR_ALIGN, TQ_ERR_ARG, TQ_ERR_CAPACITY,
     TQ_ERR_HIP, TQ_ERR_NO_DEVICE, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_F16,
-    TQ_F32, TQ_OK, Config, PackedCache, TqError, lib, tq_attend_decode,
+    TQ_F32, TQ_OK, Config, PackedCache, TqError, lib, tq_append_attend_decode,
+    tq_attend_decode,
     tq_bits_split, tq_cache_bytes, tq_codebook, tq_config, tq_cache,
     tq_dense_decode_bf16, tq_dense_workspace_bytes, tq_encode_kv, tq_num_splits,
     tq_qjl_sketch, tq_rht, tq_signs, tq_strerror, tq_workspace_bytes, workspace,

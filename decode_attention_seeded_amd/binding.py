@@ -31,7 +31,8 @@ TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 EXPORTS = (
     "tq_bits_split", "tq_codebook", "tq_signs", "tq_cache_bytes", "tq_rht",
     "tq_encode_kv", "tq_qjl_sketch", "tq_num_splits", "tq_workspace_bytes",
-    "tq_attend_decode", "tq_dense_workspace_bytes", "tq_dense_decode_bf16",
+    "tq_attend_decode", "tq_append_attend_decode", "tq_dense_workspace_bytes",
+    "tq_dense_decode_bf16",
     "tq_strerror",
 )
 
@@ -80,6 +81,8 @@ def _lib():
             "tq_num_splits": (I, [CFG, I, I, I, I64, I]),
             "tq_workspace_bytes": (I64, [CFG, I, I, I, I64, I]),
             "tq_attend_decode": (I, [CFG, P, I, I, I, CACHE, I64, F, I, P, P, SZ, P]),
+            "tq_append_attend_decode": (I, [CFG, P, P, I, P, I, I, I, CACHE, I64, F, I, P, P,
+                                            SZ, P]),
             "tq_dense_workspace_bytes": (I64, [I, I, I, I, I64, I]),
             "tq_dense_decode_bf16": (I, [P, P, P, I, I, I, I, I64, F, I, P, P, SZ, P]),
             "tq_strerror": (ctypes.c_char_p, [I]),
@@ -283,6 +286,25 @@ def tq_dense_decode_bf16(q, k, v, out, ws, scale: float = 0.0, splits: int = 0, 
                                        float(scale), splits, _ptr(out), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream(stream)),
            "tq_dense_decode_bf16")
+
+
+def tq_append_attend_decode(cfg: Config, k_new, v_new, q, cache: PackedCache, n_ctx: int, out,
+                            ws, scale: float = 0.0, splits: int = 0, stream=None):
+    """Encode token n_ctx - 1 from k_new, v_new [B][Hkv][1][d], then attend
+    like tq_attend_decode (one launch for 2/4-bit values without QJL)."""
+    B, Hq, d = q.shape
+    if d != cfg.d or not q.is_contiguous() or tuple(out.shape) != (B, Hq, d):
+        raise TqError(TQ_ERR_ARG, "tq_append_attend_decode: q/out must be [B][Hq][d] contiguous")
+    for t in (k_new, v_new):
+        if tuple(t.shape) != (cache.B, cache.Hkv, 1, d) or not t.is_contiguous():
+            raise TqError(TQ_ERR_ARG, "tq_append_attend_decode: k_new/v_new must be [B][Hkv][1][d]")
+    if k_new.dtype != v_new.dtype:
+        raise TqError(TQ_ERR_ARG, "tq_append_attend_decode: k_new and v_new dtypes differ")
+    c = cache.c()
+    _check(_lib().tq_append_attend_decode(
+        ctypes.byref(cfg.c()), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(q),
+        _dtype_code(q), B, Hq, ctypes.byref(c), n_ctx, float(scale), splits, _ptr(out), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)), "tq_append_attend_decode")
 
 
 def workspace(nbytes: int, device="cuda"):

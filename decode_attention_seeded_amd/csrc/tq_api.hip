@@ -116,6 +116,32 @@ int launch_merge(int d, const MergeArgs& a, hipStream_t st) {
   return last_launch();
 }
 
+// Kernel arguments of the encode of rows [offset, offset + n_new) of every
+// (batch, KV head) from k, v: [B*Hkv][n_new][d] of in_dtype.
+void fill_encode_args(const tq_config* cfg, const void* k, const void* v, int in_dtype,
+                      int64_t offset, int64_t n_new, const tq_cache* cache, EncodeArgs* a) {
+  a->x[0] = k;
+  a->x[1] = v;
+  a->codes[0] = static_cast<uint8_t*>(cache->kc);
+  a->codes[1] = static_cast<uint8_t*>(cache->vc);
+  a->norms[0] = cache->kn;
+  a->norms[1] = cache->vn;
+  a->qbits = static_cast<uint8_t*>(cache->kq);
+  a->rnorm = static_cast<uint16_t*>(cache->kr);
+  a->n_new = n_new;
+  a->offset = offset;
+  a->capacity = cache->capacity;
+  a->BH = cache->B * cache->Hkv;
+  a->in_dtype = in_dtype;
+  a->norm_f16 = cfg->norm_dtype == TQ_F16;
+  sign_bitmap(cfg->seed, cfg->d, a->sbits);
+  sign_bitmap(cfg->qjl_seed, cfg->d, a->qsbits);
+  fill_positive_thresholds(cfg->bits_k, a->tpos[0]);
+  fill_positive_thresholds(cfg->bits_v, a->tpos[1]);
+  double thr_unused[15];
+  fill_codebook_f64(cfg->bits_k, thr_unused, a->cen_k);
+}
+
 // Shared tail of the packed and dense decode paths: q preparation, split-K
 // kernel, merge.
 int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs da,
@@ -156,6 +182,74 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
   ma.heads = int64_t(B) * Hq;
   ma.S = p.splits;
   return launch_merge(d, ma, st);
+}
+
+// Decode attention over the first n_ctx tokens; with `app`, token n_ctx - 1
+// is first encoded from app's rows (fused into the decode launch when the
+// matrix-core kernel runs, else one encode launch before it).
+int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
+           const tq_cache* cache, int64_t n_ctx, float scale, int splits, float* out, void* ws,
+           size_t ws_bytes, hipStream_t stream, const EncodeArgs* app) {
+  int st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  st = check_cache(cfg, cache);
+  if (st != TQ_OK) return st;
+  if (!valid_in_dtype(q_dtype)) return TQ_ERR_UNSUPPORTED;
+  if (B != cache->B || Hq < 1 || Hq % cache->Hkv != 0 || splits < 0) return TQ_ERR_ARG;
+  if (!std::isfinite(scale)) return TQ_ERR_ARG;
+  if (n_ctx < 1) return TQ_ERR_ARG;
+  if (n_ctx > cache->capacity) return TQ_ERR_CAPACITY;
+  if (B == 0) return TQ_OK;
+  if (!q || !out || !ws) return TQ_ERR_ARG;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return TQ_ERR_ALIGN;
+  DecodePlan p;
+  st = plan_decode(cfg->d, cfg->bits_v, cfg->qjl, B, Hq, cache->Hkv, n_ctx, splits, &p);
+  if (st != TQ_OK) return st;
+  if (ws_bytes < p.total) return TQ_ERR_WORKSPACE;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+  if (app && p.wide != 2) {
+    EncodeLauncher efn = encode_launcher(cfg->d, cfg->bits_k);
+    if (!efn) return TQ_ERR_UNSUPPORTED;
+    st = efn(cfg->bits_v, cfg->qjl != 0, *app, stream);
+    if (st != TQ_OK) return st;
+    app = nullptr;
+  }
+
+  const float tau = scale == 0.f ? 1.0f / std::sqrt(float(cfg->d)) : scale;
+  QPrepArgs qa{};
+  qa.q = q;
+  qa.heads = int64_t(B) * Hq;
+  qa.q_dtype = q_dtype;
+  qa.rotate = 1;
+  qa.pairs = 1;
+  qa.qjl = cfg->qjl;
+  qa.mult = tau * dev::kLog2e;
+  qa.seed = cfg->seed;
+  qa.qjl_seed = cfg->qjl_seed;
+
+  DecodeArgs da{};
+  da.kc = static_cast<const uint8_t*>(cache->kc);
+  da.vc = static_cast<const uint8_t*>(cache->vc);
+  da.kn = cache->kn;
+  da.vn = cache->vn;
+  da.kq = static_cast<const uint32_t*>(cache->kq);
+  da.kr = static_cast<const uint16_t*>(cache->kr);
+  da.capacity = cache->capacity;
+  da.n_ctx = n_ctx;
+  da.norm_f16 = cfg->norm_dtype == TQ_F16;
+  da.inv_sqrt_d = float(1.0 / std::sqrt(double(cfg->d)));
+  da.qjl_c = float(std::sqrt(M_PI / (2.0 * cfg->d)));
+  const double ak = fill_codebook_f32(cfg->bits_k, da.cbk);
+  const double av = fill_codebook_f32(cfg->bits_v, da.cbv);
+  da.kscale = float(1.0 / (std::sqrt(double(cfg->d)) * ak));
+  da.vscale = float(1.0 / (std::sqrt(double(cfg->d)) * av));
+  if (app) {
+    da.append = 1;
+    da.enc = *app;
+  }
+  return run_decode(cfg->d, cfg->bits_k, cfg->bits_v, cfg->qjl, p, da, qa, B, Hq, cache->Hkv,
+                    ws, out, 1, cfg->seed, stream);
 }
 
 }  // namespace
@@ -200,26 +294,7 @@ int tq_encode_kv(const tq_config* cfg, const void* k, const void* v, int in_dtyp
   if (st != TQ_OK) return st;
 
   EncodeArgs a{};
-  a.x[0] = k;
-  a.x[1] = v;
-  a.codes[0] = static_cast<uint8_t*>(cache->kc);
-  a.codes[1] = static_cast<uint8_t*>(cache->vc);
-  a.norms[0] = cache->kn;
-  a.norms[1] = cache->vn;
-  a.qbits = static_cast<uint8_t*>(cache->kq);
-  a.rnorm = static_cast<uint16_t*>(cache->kr);
-  a.n_new = n_new;
-  a.offset = offset;
-  a.capacity = cache->capacity;
-  a.BH = cache->B * cache->Hkv;
-  a.in_dtype = in_dtype;
-  a.norm_f16 = cfg->norm_dtype == TQ_F16;
-  sign_bitmap(cfg->seed, cfg->d, a.sbits);
-  sign_bitmap(cfg->qjl_seed, cfg->d, a.qsbits);
-  fill_positive_thresholds(cfg->bits_k, a.tpos[0]);
-  fill_positive_thresholds(cfg->bits_v, a.tpos[1]);
-  double thr_unused[15];
-  fill_codebook_f64(cfg->bits_k, thr_unused, a.cen_k);
+  fill_encode_args(cfg, k, v, in_dtype, offset, n_new, cache, &a);
   EncodeLauncher fn = encode_launcher(cfg->d, cfg->bits_k);
   if (!fn) return TQ_ERR_UNSUPPORTED;
   return fn(cfg->bits_v, cfg->qjl != 0, a, stream);
@@ -245,55 +320,29 @@ int tq_qjl_sketch(const float* r, int64_t rows, int d, uint64_t qjl_seed, uint32
 int tq_attend_decode(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
                      const tq_cache* cache, int64_t n_ctx, float scale, int splits, float* out,
                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  return attend(cfg, q, q_dtype, B, Hq, cache, n_ctx, scale, splits, out, ws, ws_bytes, stream,
+                nullptr);
+}
+
+int tq_append_attend_decode(const tq_config* cfg, const void* k_new, const void* v_new,
+                            int in_dtype, const void* q, int q_dtype, int B, int Hq,
+                            const tq_cache* cache, int64_t n_ctx, float scale, int splits,
+                            float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_config(cfg);
   if (st != TQ_OK) return st;
   st = check_cache(cfg, cache);
   if (st != TQ_OK) return st;
-  if (!valid_in_dtype(q_dtype)) return TQ_ERR_UNSUPPORTED;
-  if (B != cache->B || Hq < 1 || Hq % cache->Hkv != 0 || splits < 0) return TQ_ERR_ARG;
-  if (!std::isfinite(scale)) return TQ_ERR_ARG;
+  if (!valid_in_dtype(in_dtype)) return TQ_ERR_UNSUPPORTED;
   if (n_ctx < 1) return TQ_ERR_ARG;
   if (n_ctx > cache->capacity) return TQ_ERR_CAPACITY;
+  if (B != cache->B) return TQ_ERR_ARG;
   if (B == 0) return TQ_OK;
-  if (!q || !out || !ws) return TQ_ERR_ARG;
-  if (!aligned16(q) || !aligned16(out) || !aligned16(ws)) return TQ_ERR_ALIGN;
-  DecodePlan p;
-  st = plan_decode(cfg->d, cfg->bits_v, cfg->qjl, B, Hq, cache->Hkv, n_ctx, splits, &p);
-  if (st != TQ_OK) return st;
-  if (ws_bytes < p.total) return TQ_ERR_WORKSPACE;
-  st = device_ready();
-  if (st != TQ_OK) return st;
-
-  const float tau = scale == 0.f ? 1.0f / std::sqrt(float(cfg->d)) : scale;
-  QPrepArgs qa{};
-  qa.q = q;
-  qa.heads = int64_t(B) * Hq;
-  qa.q_dtype = q_dtype;
-  qa.rotate = 1;
-  qa.pairs = 1;
-  qa.qjl = cfg->qjl;
-  qa.mult = tau * dev::kLog2e;
-  qa.seed = cfg->seed;
-  qa.qjl_seed = cfg->qjl_seed;
-
-  DecodeArgs da{};
-  da.kc = static_cast<const uint8_t*>(cache->kc);
-  da.vc = static_cast<const uint8_t*>(cache->vc);
-  da.kn = cache->kn;
-  da.vn = cache->vn;
-  da.kq = static_cast<const uint32_t*>(cache->kq);
-  da.kr = static_cast<const uint16_t*>(cache->kr);
-  da.capacity = cache->capacity;
-  da.n_ctx = n_ctx;
-  da.norm_f16 = cfg->norm_dtype == TQ_F16;
-  da.inv_sqrt_d = float(1.0 / std::sqrt(double(cfg->d)));
-  da.qjl_c = float(std::sqrt(M_PI / (2.0 * cfg->d)));
-  const double ak = fill_codebook_f32(cfg->bits_k, da.cbk);
-  const double av = fill_codebook_f32(cfg->bits_v, da.cbv);
-  da.kscale = float(1.0 / (std::sqrt(double(cfg->d)) * ak));
-  da.vscale = float(1.0 / (std::sqrt(double(cfg->d)) * av));
-  return run_decode(cfg->d, cfg->bits_k, cfg->bits_v, cfg->qjl, p, da, qa, B, Hq, cache->Hkv,
-                    ws, out, 1, cfg->seed, stream);
+  if (!k_new || !v_new) return TQ_ERR_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return TQ_ERR_ALIGN;
+  EncodeArgs e{};
+  fill_encode_args(cfg, k_new, v_new, in_dtype, n_ctx - 1, 1, cache, &e);
+  return attend(cfg, q, q_dtype, B, Hq, cache, n_ctx, scale, splits, out, ws, ws_bytes, stream,
+                &e);
 }
 
 int tq_dense_decode_bf16(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,

@@ -83,6 +83,8 @@ struct DecodeArgs {
   const void* q_raw;      // [B*Hq][D] queries, for kernels that rotate them themselves
   int q_dtype;
   float qmult;            // scale * log2(e)
+  int append;             // 1: the last split first encodes token n_ctx - 1 (enc)
+  EncodeArgs enc;         // that token's K/V rows and the cache planes
 };
 
 struct MergeArgs {
@@ -356,6 +358,40 @@ __device__ __forceinline__ void encode_row(const EncodeArgs& a, int bh, int64_t 
   }
 }
 
+template <int IW, bool QJL>
+__device__ __forceinline__ EncodeLane<IW> make_encode_lane(const EncodeArgs& a, int lp) {
+  EncodeLane<IW> el;
+  el.lp = lp;
+  el.smask = pick8(a.sbits, lp);
+  el.qmask = QJL ? pick8(a.qsbits, lp) : 0u;
+  if constexpr (IW == 2) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      el.pm[j] = ((el.smask >> (2 * j) & 1u) << 15) | ((el.smask >> (2 * j + 1) & 1u) << 31);
+  }
+#pragma unroll
+  for (int s = 0; s < 3; ++s) el.sg[s] = (lp >> s & 1) ? -1.0 : 1.0;
+  return el;
+}
+
+// Encodes token 0 of the (single-token) append in `e` for row bh: lanes
+// [0, D/32) the key, lanes [D/32, D/16) the value (no QJL).
+template <int D, int BK, int BV, int DT>
+__device__ __forceinline__ void encode_append_row(const EncodeArgs& e, int bh, int lane) {
+  constexpr int IW = DT == 0 ? 4 : 2;
+  constexpr int P = D / 32;
+  const int z = lane / P;
+  const EncodeLane<IW> el = make_encode_lane<IW, false>(e, lane % P);
+  RowWords<IW> rw;
+  load_words<D, IW>(e, z, bh, 0, el.lp, rw);
+  double u[32];
+  const double ss = words_to_f64<DT>(rw, el, u);
+  if (z == 0)
+    encode_row<D, BK, false, 0, IW>(e, bh, 0, true, el, u, ss);
+  else
+    encode_row<D, BV, false, 1, IW>(e, bh, 0, true, el, u, ss);
+}
+
 // Persistent encode of K and V: a work item is 64/P consecutive rows (one
 // wave) of one (tensor, batch*KV head) pair, numbered
 // (tensor * BH + bh) * groups + group. Each wave walks the items with the
@@ -375,17 +411,7 @@ __global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
                   uint32_t(__builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)));
   if (item >= items) return;
 
-  EncodeLane<IW> el;
-  el.lp = lane & (P - 1);
-  el.smask = pick8(a.sbits, el.lp);
-  el.qmask = QJL ? pick8(a.qsbits, el.lp) : 0u;
-  if constexpr (IW == 2) {
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      el.pm[j] = ((el.smask >> (2 * j) & 1u) << 15) | ((el.smask >> (2 * j + 1) & 1u) << 31);
-  }
-#pragma unroll
-  for (int s = 0; s < 3; ++s) el.sg[s] = (el.lp >> s & 1) ? -1.0 : 1.0;
+  const EncodeLane<IW> el = make_encode_lane<IW, QJL>(a, lane & (P - 1));
   const int rl = lane / P;
 
   struct Where { int z, bh; int64_t t; };
@@ -1689,6 +1715,18 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
         dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
   }
   const uint8_t* vtab = tabs + KT_BYTES;
+  // fused single-token append: the workgroup that owns the last split (the
+  // one that reads token n_ctx - 1) encodes that token's K and V rows into
+  // the cache first; the barrier below makes the stores visible to its
+  // waves' loads. Other head chunks of the same KV head write the same bytes.
+  if (a.append && split == a.S - 1 && wave == 0 && lane < D / 16) {
+    if (a.enc.in_dtype == 0)
+      encode_append_row<D, BK, BV, 0>(a.enc, bkv, lane);
+    else if (a.enc.in_dtype == 1)
+      encode_append_row<D, BK, BV, 1>(a.enc, bkv, lane);
+    else
+      encode_append_row<D, BK, BV, 2>(a.enc, bkv, lane);
+  }
   // the GK query rows, rotated and scaled here (one 16-lane group per head):
   // R q * scale * log2(e), as fp16 pairs
   (void)qp2_all;

@@ -197,6 +197,28 @@ int tq_attend_decode(const tq_config* cfg, const void* q, int q_dtype, int B,
                      hipStream_t stream);
 
 /*
+ * One generation step: append the newest token, then attend (README, "How it
+ * plugs in": the cache stores the new rotated key and value, then the
+ * patched scaled_dot_product_attention runs on the rotated query; API page,
+ * "Implementation Details: Cache Substitution"). Same result, cache bytes
+ * and output, as
+ *   tq_encode_kv(cfg, k_new, v_new, in_dtype, n_ctx - 1, 1, cache, stream);
+ *   tq_attend_decode(cfg, q, q_dtype, B, Hq, cache, n_ctx, ...);
+ *   k_new, v_new: [B][Hkv][1][d] of in_dtype (device), 16-byte aligned: the
+ *                 rows of token n_ctx - 1.
+ * The other arguments, the workspace and the errors are those of
+ * tq_attend_decode; all arguments are checked before any work is queued.
+ * For formats with 2- or 4-bit values and no QJL this is one launch: the
+ * workgroup that owns the last split encodes the token before its first
+ * tile. The other formats queue the encode and the decode back to back.
+ */
+int tq_append_attend_decode(const tq_config* cfg, const void* k_new,
+                            const void* v_new, int in_dtype, const void* q,
+                            int q_dtype, int B, int Hq, const tq_cache* cache,
+                            int64_t n_ctx, float scale, int splits, float* out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Dense bf16 decode attention for comparison on the same GPU (not part of
  * the method): out = softmax(scale q K^T) V over k, v: [B][Hkv][n_ctx][d]
  * bf16, q: [B][Hq][d] bf16, out fp32. Same workspace rules

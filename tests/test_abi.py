@@ -182,6 +182,37 @@ def test_decode_validation():
     assert _dec(B=0, cache=_cache(B=0)) == tq.TQ_OK    # empty batch: no-op
 
 
+def _app(cfg=None, k=A, v=A, dt=tq.TQ_BF16, q=A, qdt=tq.TQ_BF16, B=1, Hq=4, cache=None,
+         n_ctx=10, scale=0.0, splits=0, out=A, ws=A, ws_bytes=1 << 30):
+    lib = tq.lib()
+    cfg = _cfg() if cfg is None else cfg
+    cache = _cache() if cache is None else cache
+    return lib.tq_append_attend_decode(ctypes.byref(cfg) if cfg != "null" else None, k, v, dt,
+                                       q, qdt, B, Hq, ctypes.byref(cache), n_ctx, scale, splits,
+                                       out, ws, ws_bytes, None)
+
+
+def test_append_attend_validation():
+    """Both halves of the fused step are checked before anything is queued:
+    the encode side (rows, dtype, alignment) and the decode side."""
+    assert _app(cfg="null") == tq.TQ_ERR_ARG
+    assert _app(cfg=_cfg(bits_v=1)) == tq.TQ_ERR_UNSUPPORTED
+    assert _app(cache=_cache(vc=None)) == tq.TQ_ERR_ARG
+    assert _app(dt=7) == tq.TQ_ERR_UNSUPPORTED
+    assert _app(k=None) == tq.TQ_ERR_ARG
+    assert _app(v=MIS) == tq.TQ_ERR_ALIGN
+    assert _app(n_ctx=0) == tq.TQ_ERR_ARG
+    assert _app(n_ctx=65) == tq.TQ_ERR_CAPACITY
+    assert _app(B=2) == tq.TQ_ERR_ARG
+    assert _app(qdt=5) == tq.TQ_ERR_UNSUPPORTED
+    assert _app(Hq=3) == tq.TQ_ERR_ARG
+    assert _app(q=None) == tq.TQ_ERR_ARG
+    assert _app(out=MIS) == tq.TQ_ERR_ALIGN
+    assert _app(ws_bytes=64) == tq.TQ_ERR_WORKSPACE
+    assert _app(cfg=_cfg(qjl=1), cache=_cache(kq=None)) == tq.TQ_ERR_ARG
+    assert _app(B=0, cache=_cache(B=0)) == tq.TQ_OK    # empty batch: no-op
+
+
 def test_rht_qjl_dense_validation():
     lib = tq.lib()
     assert lib.tq_rht(A, tq.TQ_F32, A, -1, 128, 0, 0, None) == tq.TQ_ERR_ARG

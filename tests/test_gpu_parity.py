@@ -122,6 +122,51 @@ def test_workspace_reuse_across_calls():
         assert np.array_equal(got, fresh), (n, s)
 
 
+APPEND_CASES = ["d128_k3v4_gqa4", "d256_k2v2_outlier", "d128_k4v2_g8", "d128_n1",
+                "d128_k4v4_f32norm_f32in_g1", "d128_k3qjl_v4_corr", "d128_k2v3_g2_f16in"]
+
+
+@pytest.mark.parametrize("name", APPEND_CASES)
+def test_append_attend_matches_encode_then_decode(name):
+    """tq_append_attend_decode (one launch for 2/4-bit values without QJL,
+    encode then decode for the other formats) leaves the same cache bytes
+    and the same output as tq_encode_kv of token N-1 followed by
+    tq_attend_decode, and the output matches the oracle; split counts 0 and
+    3 (the appended token sits in the last split either way)."""
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.small_workload(**SMALL[name])
+    log(f"case {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} N={w.N} K{w.bits_k}/V{w.bits_v} "
+        f"qjl={w.qjl}")
+    n0 = w.N - 1
+    rk, rv, _, _ = kv_host(w, n0, w.N)
+    k1, v1 = to_device(rk, w.in_dtype), to_device(rv, w.in_dtype)
+    qraw, qf = si.queries(w)
+    q = to_device(qraw, w.in_dtype)
+    ref = oracle_encode(w)
+    want = o.attend(qf.astype(np.float64), ref, w.N, d=w.d, seed=w.seed, bits_k=w.bits_k,
+                    bits_v=w.bits_v, Hkv=w.Hkv, qjl=w.qjl, qjl_seed=w.qjl_seed)
+    for splits in (0, 3):
+        cfg, two = gpu_encode(w, chunks=[(0, n0)] if n0 > 0 else [], capacity=w.N)
+        _, one = gpu_encode(w, chunks=[(0, n0)] if n0 > 0 else [], capacity=w.N)
+        tq.tq_encode_kv(cfg, k1, v1, n0, two)
+        ref_out = gpu_decode(w, cfg, two, q, w.N, splits=splits)
+        out = torch.full((w.B, w.Hq, w.d), float("nan"), dtype=torch.float32, device="cuda")
+        ws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N, splits))
+        tq.tq_append_attend_decode(cfg, k1, v1, q, one, w.N, out, ws, splits=splits)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        for plane in ("kc", "vc", "kn", "vn", "kq", "kr"):
+            a, b = getattr(one, plane), getattr(two, plane)
+            if a is None:
+                continue
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), plane
+        assert np.array_equal(got, ref_out)
+        err, _ = rel_err(got, want)
+        log(f"  splits={splits}: fused step equals encode + decode; error vs oracle {err:.2e}")
+        assert err <= TOL
+
+
 @pytest.mark.parametrize("splits,scale", [(1, 0.0), (3, 0.0), (1, 0.35), (2, 0.35)])
 def test_many_tiles_per_split(splits, scale):
     """Long splits (up to 10 tiles of 512 tokens in one workgroup, every
