@@ -208,7 +208,7 @@ int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
   if (ws_bytes < p.total) return TQ_ERR_WORKSPACE;
   st = device_ready();
   if (st != TQ_OK) return st;
-  if (app && p.wide != 2) {
+  if (app && (p.wide != 2 || cfg->qjl)) {
     EncodeLauncher efn = encode_launcher(cfg->d, cfg->bits_k);
     if (!efn) return TQ_ERR_UNSUPPORTED;
     st = efn(cfg->bits_v, cfg->qjl != 0, *app, stream);
@@ -240,6 +240,7 @@ int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
   da.norm_f16 = cfg->norm_dtype == TQ_F16;
   da.inv_sqrt_d = float(1.0 / std::sqrt(double(cfg->d)));
   da.qjl_c = float(std::sqrt(M_PI / (2.0 * cfg->d)));
+  da.qjl_seed = cfg->qjl_seed;
   const double ak = fill_codebook_f32(cfg->bits_k, da.cbk);
   const double av = fill_codebook_f32(cfg->bits_v, da.cbv);
   da.kscale = float(1.0 / (std::sqrt(double(cfg->d)) * ak));

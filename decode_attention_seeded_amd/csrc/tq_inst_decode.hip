@@ -27,13 +27,14 @@ static int go(int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
 #else
   if constexpr (BV == 2 || BV == 4) {
     if (wide == 2) {
-      if constexpr (QJL) return TQ_ERR_UNSUPPORTED;
       const uint32_t* qp2 = reinterpret_cast<const uint32_t*>(a.qp);
       const dim3 block(64 * mx_waves(TQ_D));
       if (a.norm_f16)
-        hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, true>), grid, block, 0, st, a, qp2);
+        hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, QJL, true>), grid, block, 0, st, a,
+                           qp2);
       else
-        hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, false>), grid, block, 0, st, a, qp2);
+        hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, QJL, false>), grid, block, 0, st, a,
+                           qp2);
       return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
     }
     if (wide) {

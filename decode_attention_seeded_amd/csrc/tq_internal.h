@@ -81,9 +81,9 @@ inline bool use_wide(int d, int bits_v, int qjl) {
 }
 
 // Waves per workgroup of the matrix-core decode kernel, and whether a format
-// runs it (2- or 4-bit values, no QJL correction).
+// runs it (2- or 4-bit values, with or without the QJL correction).
 constexpr int mx_waves(int d) { return 8 + 0 * d; }
-inline bool use_mx(int d, int bits_v, int qjl) { return use_wide(d, bits_v, qjl) && !qjl; }
+inline bool use_mx(int d, int bits_v, int qjl) { return use_wide(d, bits_v, qjl); }
 
 // Fills a plan; returns TQ_OK or a negative status.
 int plan_decode(int d, int bits_v, int qjl, int B, int Hq, int Hkv, int64_t n_ctx,

@@ -77,6 +77,7 @@ struct DecodeArgs {
   float kscale;           // 1 / (sqrt(d) * alpha_k): fp32 part of the key scale
   float vscale;           // 1 / (sqrt(d) * alpha_v)
   float qjl_c;            // sqrt(pi / (2 d))
+  uint64_t qjl_seed;      // QJL rotation seed (kernels that rotate the query)
   float cbk[16];          // alpha_k * key centroids (exact in fp16 to ~1e-4)
   float cbv[16];          // alpha_v * value centroids
   uint64_t seed;          // rotation seed: partials are rotated back (R^T)
@@ -1601,8 +1602,8 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 }
 
 // ---------------------------------------------------------------------------
-// Split-K decode on the matrix cores, d = 128 or 256 with 2- or 4-bit values
-// and no QJL correction. Workgroup, tile and softmax structure are those of
+// Split-K decode on the matrix cores, d = 128 or 256 with 2- or 4-bit values,
+// with or without the QJL score correction. Workgroup, tile and softmax structure are those of
 // k_decode_wide (W waves, each with its own online-softmax pass over
 // interleaved 64-token tiles, combined once at the end); the two
 // contractions of a tile run as MFMAs on fp16 operands dequantized through
@@ -1619,19 +1620,24 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 //           holds tokens 4kq .. 4kq + 3 of the block for coordinates
 //           VJ*n .. VJ*n + VJ - 1, one instruction per offset j < VJ. The
 //           sums land in lanes 0..15 (register g = head g).
+//   QJL     the sign dot sum_i q''_i sigma_i is a second chain of the same
+//           4x4x4 blocks: B = the key's 4 signs of quad j as fp16 +-1 (one
+//           8-byte lookup of a 16-entry table), A = the quad of R_2 q'.
 // ---------------------------------------------------------------------------
 
 typedef _Float16 mx_h4 __attribute__((ext_vector_type(4)));
 typedef float mx_f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t mx_u2 __attribute__((ext_vector_type(2)));
 
-template <int D, int BK, int BV>
+template <int D, int BK, int BV, bool QJL>
 struct MxTile {
   static constexpr int SB = D * BV / 128;       // value bytes per (token, lane column)
   static constexpr int SW = (SB + 3) / 4;
   uint32_t kw[D * BK / 32];     // key row of the lane's token
   uint32_t kn, vn;              // its key and value norms (f16 or f32 bits)
   uint32_t vx[16][SW];          // value slices: token 16*(i/4) + 4*kq + i%4
+  uint32_t sw[QJL ? D / 32 : 1];  // QJL sign bits of the key (bit set: negative)
+  uint32_t kr;                  // QJL residual norm (f16 bits)
 };
 
 // For two tokens' slices x, y of 8 coordinates: byte b of *lo is the value
@@ -1651,9 +1657,9 @@ __device__ __forceinline__ void mx_pair_words(uint32_t x, uint32_t y, uint32_t* 
 
 // tiles each wave loads ahead of the one it processes (1 or 2): two where
 // three tile buffers still fit the register budget without spilling
-constexpr int mx_prefetch(int d, int bk) { return d == 128 && bk < 4 ? 2 : 1; }
+constexpr int mx_prefetch(int d, int bk, bool qjl) { return d == 128 && bk < 4 ? 2 + 0 * qjl : 1; }
 
-template <int D, int BK, int BV, int GK, bool NF16>
+template <int D, int BK, int BV, int GK, bool QJL, bool NF16>
 __global__ void __launch_bounds__(64 * mx_waves(D))
     __attribute__((amdgpu_waves_per_eu(mx_waves(D) / 4)))
 k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
@@ -1668,7 +1674,7 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
   constexpr int VREC = D * BV / 8;
   constexpr int KW = D * BK / 32;
   constexpr int VJ = D / 16;                   // coordinates per lane column
-  constexpr int SB = MxTile<D, BK, BV>::SB;
+  constexpr int SB = MxTile<D, BK, BV, QJL>::SB;
   constexpr int KE = 1 << (2 * BK);
   constexpr int VE = 1 << (2 * BV);
   constexpr int KT_BYTES = KE * 128;           // 32 copies, 128-B entry stride
@@ -1676,16 +1682,18 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
   constexpr int NQ = D / 64;                   // query quads kept per lane
   constexpr int PX = GK * TW / 2;              // weight dwords per wave tile
   constexpr float kRescale = 8.0f;
-  using Tile = MxTile<D, BK, BV>;
+  constexpr int ST_BYTES = QJL ? 16 * 512 : 0; // QJL sign quads: 64 copies of 8 B
+  using Tile = MxTile<D, BK, BV, QJL>;
   static_assert(KW % 4 == 0, "key rows are whole 16-byte loads");
   static_assert(SB == 2 || SB == 4 || SB == 8, "value slice width");
 
   constexpr int SLAB_BYTES = W * GK * D * 4;   // per-wave partials, after the loop
-  constexpr int TAB_BYTES = KT_BYTES + VT_BYTES;
+  constexpr int TAB_BYTES = KT_BYTES + VT_BYTES + ST_BYTES;
   __shared__ __attribute__((aligned(16)))
   uint8_t tabs[TAB_BYTES > SLAB_BYTES ? TAB_BYTES : SLAB_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t pex[W][2][PX];
   __shared__ uint32_t qs[GK * (D / 2)];
+  __shared__ uint32_t qs2[QJL ? GK * (D / 2) : 1];
   __shared__ float mlx[W][GK][2];
 
   const int tid = threadIdx.x;
@@ -1715,11 +1723,24 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
         dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
   }
   const uint8_t* vtab = tabs + KT_BYTES;
+  const uint8_t* stab = tabs + KT_BYTES + VT_BYTES;
+  if constexpr (QJL) {
+    // entry e: the fp16 pairs (s0, s1), (s2, s3) with s_k = -1 where bit k
+    // of e is set, else +1; lane l reads copy l (entry stride 512 B)
+    for (int i = tid; i < 16 * 64; i += NT) {
+      const int e = i >> 6;
+      const float s0 = (e & 1) ? -1.f : 1.f, s1 = (e & 2) ? -1.f : 1.f;
+      const float s2 = (e & 4) ? -1.f : 1.f, s3 = (e & 8) ? -1.f : 1.f;
+      *reinterpret_cast<uint2*>(tabs + KT_BYTES + VT_BYTES + (e << 9) + ((i & 63) << 3)) =
+          make_uint2(dev::pack_f16x2(s0, s1), dev::pack_f16x2(s2, s3));
+    }
+  }
   // fused single-token append: the workgroup that owns the last split (the
   // one that reads token n_ctx - 1) encodes that token's K and V rows into
   // the cache first; the barrier below makes the stores visible to its
   // waves' loads. Other head chunks of the same KV head write the same bytes.
-  if (a.append && split == a.S - 1 && wave == 0 && lane < D / 16) {
+  // (Formats with the QJL sketch encode the token in a launch of its own.)
+  if (!QJL && a.append && split == a.S - 1 && wave == 0 && lane < D / 16) {
     if (a.enc.in_dtype == 0)
       encode_append_row<D, BK, BV, 0>(a.enc, bkv, lane);
     else if (a.enc.in_dtype == 1)
@@ -1741,14 +1762,27 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     dev::fwht16<E, float>(v, l16);
     const float mult = a.qmult / sqrtf(float(D));
 #pragma unroll
+    for (int i = 0; i < E; ++i) v[i] *= mult;
+#pragma unroll
     for (int i = 0; i < E / 2; ++i)
-      qs[g * (D / 2) + l16 * (E / 2) + i] = dev::pack_f16x2(v[2 * i] * mult, v[2 * i + 1] * mult);
+      qs[g * (D / 2) + l16 * (E / 2) + i] = dev::pack_f16x2(v[2 * i], v[2 * i + 1]);
+    if constexpr (QJL) {
+      // q'' = R_2 q' from the fp32 q'
+      const uint32_t qmask = dev::sign_mask(a.qjl_seed, l16 * E, E);
+#pragma unroll
+      for (int i = 0; i < E; ++i) if (qmask >> i & 1) v[i] = -v[i];
+      dev::fwht16<E, float>(v, l16);
+      const float nn = 1.0f / sqrtf(float(D));
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i)
+        qs2[g * (D / 2) + l16 * (E / 2) + i] = dev::pack_f16x2(v[2 * i] * nn, v[2 * i + 1] * nn);
+    }
   }
   __syncthreads();
 
   // query quads for the broadcast A operand: lane (block lane/4, row lane%4)
   // keeps coordinates 4j .. 4j+3 of head lane%4 for j = lane/4 + 16*i
-  mx_u2 qa[NQ];
+  mx_u2 qa[NQ], qa2[QJL ? NQ : 1];
   {
     const int qm = lane & 3, qb = lane >> 2;
 #pragma unroll
@@ -1757,12 +1791,18 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
       if (qm < GK) {
         qa[i][0] = qs[qm * (D / 2) + 2 * j];
         qa[i][1] = qs[qm * (D / 2) + 2 * j + 1];
+        if constexpr (QJL) {
+          qa2[i][0] = qs2[qm * (D / 2) + 2 * j];
+          qa2[i][1] = qs2[qm * (D / 2) + 2 * j + 1];
+        }
       } else {
         qa[i][0] = 0u;
         qa[i][1] = 0u;
+        if constexpr (QJL) qa2[i] = mx_u2{0u, 0u};
       }
     }
   }
+  const uint32_t sl8 = uint32_t(lane) << 3;
 
   const int64_t t_begin = int64_t(split) * a.tps;
   const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
@@ -1795,6 +1835,19 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
       t.kn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(kn_p, n * nb), no0, 0, 0);
       t.vn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(vn_p, n * nb), no0, 0, 0);
     }
+    if constexpr (QJL) {
+      const auto rs = dev::buffer_rsrc(reinterpret_cast<const uint8_t*>(a.kq) +
+                                           (row0 + base) * (D / 8), n * (D / 8));
+#pragma unroll
+      for (int k = 0; k < D / 128; ++k) {
+        const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rs, uint32_t(lane) * (D / 8),
+                                                              16 * k, 0);
+        t.sw[4 * k] = q4[0]; t.sw[4 * k + 1] = q4[1]; t.sw[4 * k + 2] = q4[2];
+        t.sw[4 * k + 3] = q4[3];
+      }
+      t.kr = __builtin_amdgcn_raw_buffer_load_b16(
+          dev::buffer_rsrc(a.kr + (row0 + base), n * 2), uint32_t(lane) * 2, 0, 0);
+    }
     const auto rv = dev::buffer_rsrc(a.vc + (row0 + base) * VREC, n * VREC);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -1825,6 +1878,8 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     // ---------------- scores: lane = token, 4 coordinates per MFMA
     const bool valid = base + lane < t_end;
     mx_f4 sk[2] = {mx_f4{0.f, 0.f, 0.f, 0.f}, mx_f4{0.f, 0.f, 0.f, 0.f}};
+    mx_f4 sq[QJL ? 2 : 1];
+    if constexpr (QJL) sq[0] = sq[1] = mx_f4{0.f, 0.f, 0.f, 0.f};
     dev::static_for<0, D / 4>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       const uint32_t ka0 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j) | rl4;
@@ -1835,17 +1890,27 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
       sk[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
           __builtin_bit_cast(mx_h4, qa[j / 16]), __builtin_bit_cast(mx_h4, kb), sk[j & 1], 4,
           j % 16, 0);
+      if constexpr (QJL) {
+        const uint32_t sa = dev::field_at<4, 9>(cur.sw, j) | sl8;
+        const uint2 sp = *reinterpret_cast<const uint2*>(stab + sa);
+        const mx_u2 sb = {sp.x, sp.y};
+        sq[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+            __builtin_bit_cast(mx_h4, qa2[j / 16]), __builtin_bit_cast(mx_h4, sb), sq[j & 1], 4,
+            j % 16, 0);
+      }
     });
     const float knrm = NF16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
     const float vnrm = NF16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn);
     const float ks = knrm * a.kscale;
     const float nv = vnrm * a.vscale;
+    const float rho = QJL ? dev::f16_to_f32(cur.kr) * a.qjl_c : 0.f;
 
     // ---------------- online softmax with a lazily raised running max
     uint16_t* p16 = reinterpret_cast<uint16_t*>(px);
 #pragma unroll
     for (int g = 0; g < GK; ++g) {
-      const float s = (sk[0][g] + sk[1][g]) * ks;
+      float s = (sk[0][g] + sk[1][g]) * ks;
+      if constexpr (QJL) s = fmaf(rho, sq[0][g] + sq[1][g], s);
       if (__ballot(valid && s > m_run[g] + kRescale)) {        // wave-uniform
         const float mx = dev::dpp_wave_max(valid ? s : -INFINITY);
         const float m_new = fmaxf(m_run[g], mx);
@@ -1904,7 +1969,7 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     const int64_t wb = t_begin + int64_t(wave) * TW;
     uint32_t* px0 = pex[wave][0];
     uint32_t* px1 = pex[wave][1];
-    if constexpr (mx_prefetch(D, BK) == 1) {
+    if constexpr (mx_prefetch(D, BK, QJL) == 1) {
       Tile ta, tb;
       load(wb, ta);
       __builtin_amdgcn_sched_barrier(0);

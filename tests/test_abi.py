@@ -78,13 +78,12 @@ def test_split_plan_and_workspace():
     assert s >= 8
     assert tq.tq_num_splits(cfg, 1, 32, 8, 1) == 1
     # clamped to tiles: workgroup rounds are 64 tokens per wave; the
-    # matrix-core kernel (2/4-bit values, no QJL) runs 8 waves, the VALU
-    # wave-private kernel with QJL 12 at d 128; the other formats use
-    # 256-token tiles (d 128)
+    # matrix-core kernel (2/4-bit values, with or without QJL) runs 8 waves;
+    # the other formats use 256-token tiles (d 128)
     assert tq.tq_num_splits(cfg, 1, 32, 8, 300, splits=7) == 1
     assert tq.tq_num_splits(cfg, 1, 32, 8, 2100, splits=7) == 5
     cfgq = tq.Config(d=128, bits_k=3, bits_v=4, qjl=True)
-    assert tq.tq_num_splits(cfgq, 1, 32, 8, 2100, splits=7) == 3
+    assert tq.tq_num_splits(cfgq, 1, 32, 8, 2100, splits=7) == 5
     cfg256 = tq.Config(d=256, bits_k=2, bits_v=2)
     assert tq.tq_num_splits(cfg256, 8, 16, 4, 1100, splits=7) == 3
     cfg3 = tq.Config(d=128, bits_k=3, bits_v=3)
