@@ -227,6 +227,8 @@ int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
   qa.mult = tau * dev::kLog2e;
   qa.seed = cfg->seed;
   qa.qjl_seed = cfg->qjl_seed;
+  sign_bitmap(cfg->seed, cfg->d, qa.sbits);
+  sign_bitmap(cfg->qjl_seed, cfg->d, qa.qsbits);
 
   DecodeArgs da{};
   da.kc = static_cast<const uint8_t*>(cache->kc);
@@ -241,6 +243,10 @@ int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
   da.inv_sqrt_d = float(1.0 / std::sqrt(double(cfg->d)));
   da.qjl_c = float(std::sqrt(M_PI / (2.0 * cfg->d)));
   da.qjl_seed = cfg->qjl_seed;
+  for (int k = 0; k < 8; ++k) {
+    da.sbits[k] = qa.sbits[k];
+    da.qsbits[k] = qa.qsbits[k];
+  }
   const double ak = fill_codebook_f32(cfg->bits_k, da.cbk);
   const double av = fill_codebook_f32(cfg->bits_v, da.cbv);
   da.kscale = float(1.0 / (std::sqrt(double(cfg->d)) * ak));

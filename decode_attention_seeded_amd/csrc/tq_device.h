@@ -103,6 +103,17 @@ __device__ __forceinline__ uint32_t sign_mask(uint64_t seed, int first, int n) {
   return m;
 }
 
+// The same n bits (n <= 32, not crossing a 32-bit word) taken from a sign
+// bitmap that the host filled from that stream (kernel argument, 8 words).
+__device__ __forceinline__ uint32_t bitmap_bits(const uint32_t (&w)[8], int first, int n) {
+  const int wi = first >> 5;
+  uint32_t x = w[0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) x = wi == k ? w[k] : x;
+  x >>= (first & 31);
+  return n == 32 ? x : (x & ((1u << n) - 1u));
+}
+
 // ---------------------------------------------------------------------------
 // Walsh-Hadamard transform of one row held by a group of 16 consecutive
 // lanes, E consecutive elements per lane (row length 16*E). Element index

@@ -57,6 +57,8 @@ struct QPrepArgs {
   int qq_pairs;           // 1: write qq as fp16 pairs too (wide decode)
   float mult;             // scale * log2(e)
   uint64_t seed, qjl_seed;
+  uint32_t sbits[8];      // rotation signs, bit i set when sign i is negative
+  uint32_t qsbits[8];     // QJL rotation signs, same layout
 };
 
 struct DecodeArgs {
@@ -84,6 +86,8 @@ struct DecodeArgs {
   const void* q_raw;      // [B*Hq][D] queries, for kernels that rotate them themselves
   int q_dtype;
   float qmult;            // scale * log2(e)
+  uint32_t sbits[8];      // rotation signs, bit i set when sign i is negative
+  uint32_t qsbits[8];     // QJL rotation signs, same layout
   int append;             // 1: the last split first encodes token n_ctx - 1 (enc)
   EncodeArgs enc;         // that token's K/V rows and the cache planes
 };
@@ -497,7 +501,7 @@ __global__ void __launch_bounds__(256) k_qprep(QPrepArgs a) {
   float v[E];
   dev::load_row_part<E>(a.q, a.q_dtype, row * D + l16 * E, v);
   if (a.rotate) {
-    const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
+    const uint32_t smask = dev::bitmap_bits(a.sbits, l16 * E, E);
 #pragma unroll
     for (int i = 0; i < E; ++i) if (smask >> i & 1) v[i] = -v[i];
     dev::fwht16<E, float>(v, l16);
@@ -522,7 +526,7 @@ __global__ void __launch_bounds__(256) k_qprep(QPrepArgs a) {
       dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
   }
   if (a.qjl) {
-    const uint32_t qmask = dev::sign_mask(a.qjl_seed, l16 * E, E);
+    const uint32_t qmask = dev::bitmap_bits(a.qsbits, l16 * E, E);
 #pragma unroll
     for (int i = 0; i < E; ++i) if (qmask >> i & 1) v[i] = -v[i];
     dev::fwht16<E, float>(v, l16);
@@ -1157,7 +1161,7 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = obuf[g * D + l16 * E + i];
     dev::fwht16<E, float>(v, l16);
-    const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
+    const uint32_t smask = dev::bitmap_bits(a.sbits, l16 * E, E);
     const float nn = 1.0f / sqrtf(float(D));
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = (smask >> i & 1) ? -v[i] * nn : v[i] * nn;
@@ -1590,7 +1594,7 @@ k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = obuf[g * D + l16 * E + i];
     dev::fwht16<E, float>(v, l16);
-    const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
+    const uint32_t smask = dev::bitmap_bits(a.sbits, l16 * E, E);
     const float nn = 1.0f / sqrtf(float(D));
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = (smask >> i & 1) ? -v[i] * nn : v[i] * nn;
@@ -1712,98 +1716,6 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
   const int h0 = kvh * a.G + chunk * GK;
   const int64_t head0 = int64_t(b) * a.Hq + h0;
 
-  for (int i = tid; i < KE * 32; i += NT) {
-    const int e = i >> 5;
-    *reinterpret_cast<uint32_t*>(tabs + (e << 7) + ((i & 31) << 2)) =
-        dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
-  }
-  for (int i = tid; i < VE * 64; i += NT) {
-    const int e = i >> 6;
-    *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << 8) + ((i & 63) << 2)) =
-        dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
-  }
-  const uint8_t* vtab = tabs + KT_BYTES;
-  const uint8_t* stab = tabs + KT_BYTES + VT_BYTES;
-  if constexpr (QJL) {
-    // entry e: the fp16 pairs (s0, s1), (s2, s3) with s_k = -1 where bit k
-    // of e is set, else +1; lane l reads copy l (entry stride 512 B)
-    for (int i = tid; i < 16 * 64; i += NT) {
-      const int e = i >> 6;
-      const float s0 = (e & 1) ? -1.f : 1.f, s1 = (e & 2) ? -1.f : 1.f;
-      const float s2 = (e & 4) ? -1.f : 1.f, s3 = (e & 8) ? -1.f : 1.f;
-      *reinterpret_cast<uint2*>(tabs + KT_BYTES + VT_BYTES + (e << 9) + ((i & 63) << 3)) =
-          make_uint2(dev::pack_f16x2(s0, s1), dev::pack_f16x2(s2, s3));
-    }
-  }
-  // fused single-token append: the workgroup that owns the last split (the
-  // one that reads token n_ctx - 1) encodes that token's K and V rows into
-  // the cache first; the barrier below makes the stores visible to its
-  // waves' loads. Other head chunks of the same KV head write the same bytes.
-  // (Formats with the QJL sketch encode the token in a launch of its own.)
-  if (!QJL && a.append && split == a.S - 1 && wave == 0 && lane < D / 16) {
-    if (a.enc.in_dtype == 0)
-      encode_append_row<D, BK, BV, 0>(a.enc, bkv, lane);
-    else if (a.enc.in_dtype == 1)
-      encode_append_row<D, BK, BV, 1>(a.enc, bkv, lane);
-    else
-      encode_append_row<D, BK, BV, 2>(a.enc, bkv, lane);
-  }
-  // the GK query rows, rotated and scaled here (one 16-lane group per head):
-  // R q * scale * log2(e), as fp16 pairs
-  (void)qp2_all;
-  if (tid < 16 * GK) {
-    constexpr int E = D / 16;
-    const int g = tid >> 4, l16 = tid & 15;
-    float v[E];
-    dev::load_row_part<E>(a.q_raw, a.q_dtype, (head0 + g) * D + l16 * E, v);
-    const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
-#pragma unroll
-    for (int i = 0; i < E; ++i) if (smask >> i & 1) v[i] = -v[i];
-    dev::fwht16<E, float>(v, l16);
-    const float mult = a.qmult / sqrtf(float(D));
-#pragma unroll
-    for (int i = 0; i < E; ++i) v[i] *= mult;
-#pragma unroll
-    for (int i = 0; i < E / 2; ++i)
-      qs[g * (D / 2) + l16 * (E / 2) + i] = dev::pack_f16x2(v[2 * i], v[2 * i + 1]);
-    if constexpr (QJL) {
-      // q'' = R_2 q' from the fp32 q'
-      const uint32_t qmask = dev::sign_mask(a.qjl_seed, l16 * E, E);
-#pragma unroll
-      for (int i = 0; i < E; ++i) if (qmask >> i & 1) v[i] = -v[i];
-      dev::fwht16<E, float>(v, l16);
-      const float nn = 1.0f / sqrtf(float(D));
-#pragma unroll
-      for (int i = 0; i < E / 2; ++i)
-        qs2[g * (D / 2) + l16 * (E / 2) + i] = dev::pack_f16x2(v[2 * i] * nn, v[2 * i + 1] * nn);
-    }
-  }
-  __syncthreads();
-
-  // query quads for the broadcast A operand: lane (block lane/4, row lane%4)
-  // keeps coordinates 4j .. 4j+3 of head lane%4 for j = lane/4 + 16*i
-  mx_u2 qa[NQ], qa2[QJL ? NQ : 1];
-  {
-    const int qm = lane & 3, qb = lane >> 2;
-#pragma unroll
-    for (int i = 0; i < NQ; ++i) {
-      const int j = qb + 16 * i;
-      if (qm < GK) {
-        qa[i][0] = qs[qm * (D / 2) + 2 * j];
-        qa[i][1] = qs[qm * (D / 2) + 2 * j + 1];
-        if constexpr (QJL) {
-          qa2[i][0] = qs2[qm * (D / 2) + 2 * j];
-          qa2[i][1] = qs2[qm * (D / 2) + 2 * j + 1];
-        }
-      } else {
-        qa[i][0] = 0u;
-        qa[i][1] = 0u;
-        if constexpr (QJL) qa2[i] = mx_u2{0u, 0u};
-      }
-    }
-  }
-  const uint32_t sl8 = uint32_t(lane) << 3;
-
   const int64_t t_begin = int64_t(split) * a.tps;
   const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
   const int64_t row0 = int64_t(bkv) * a.capacity;
@@ -1863,6 +1775,117 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
       }
     }
   };
+
+
+  // the first tiles of each wave are requested before the tables and the
+  // query are set up, so the start-up latency of the stream overlaps that
+  // work (not with a fused append, whose row must be stored first)
+  constexpr int PF = mx_prefetch(D, BK, QJL);
+  const int64_t wb = t_begin + int64_t(wave) * TW;
+  const bool early = !a.append;
+  Tile ta, tb, tc;
+  if (early) {
+    load(wb, ta);
+    if constexpr (PF == 2) load(wb + T, tb);
+  }
+
+  // pair tables: each wave writes whole entries (entry index uniform across
+  // the wave, so the centroids are scalar loads), one copy per lane
+#pragma unroll
+  for (int k = 0; k < KE / W; ++k) {
+    const int e = wave + k * W;
+    if (lane < 32)
+      *reinterpret_cast<uint32_t*>(tabs + (e << 7) + (lane << 2)) =
+          dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
+  }
+#pragma unroll 8
+  for (int k = 0; k < VE / W; ++k) {
+    const int e = wave + k * W;
+    *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << 8) + (lane << 2)) =
+        dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
+  }
+  static_assert(KE % W == 0 && VE % W == 0, "table entries split evenly over the waves");
+  const uint8_t* vtab = tabs + KT_BYTES;
+  const uint8_t* stab = tabs + KT_BYTES + VT_BYTES;
+  if constexpr (QJL) {
+    // entry e: the fp16 pairs (s0, s1), (s2, s3) with s_k = -1 where bit k
+    // of e is set, else +1; lane l reads copy l (entry stride 512 B)
+    for (int i = tid; i < 16 * 64; i += NT) {
+      const int e = i >> 6;
+      const float s0 = (e & 1) ? -1.f : 1.f, s1 = (e & 2) ? -1.f : 1.f;
+      const float s2 = (e & 4) ? -1.f : 1.f, s3 = (e & 8) ? -1.f : 1.f;
+      *reinterpret_cast<uint2*>(tabs + KT_BYTES + VT_BYTES + (e << 9) + ((i & 63) << 3)) =
+          make_uint2(dev::pack_f16x2(s0, s1), dev::pack_f16x2(s2, s3));
+    }
+  }
+  // fused single-token append: the workgroup that owns the last split (the
+  // one that reads token n_ctx - 1) encodes that token's K and V rows into
+  // the cache first; the barrier below makes the stores visible to its
+  // waves' loads. Other head chunks of the same KV head write the same bytes.
+  // (Formats with the QJL sketch encode the token in a launch of its own.)
+  if (!QJL && a.append && split == a.S - 1 && wave == 0 && lane < D / 16) {
+    if (a.enc.in_dtype == 0)
+      encode_append_row<D, BK, BV, 0>(a.enc, bkv, lane);
+    else if (a.enc.in_dtype == 1)
+      encode_append_row<D, BK, BV, 1>(a.enc, bkv, lane);
+    else
+      encode_append_row<D, BK, BV, 2>(a.enc, bkv, lane);
+  }
+  // the GK query rows, rotated and scaled here (one 16-lane group per head):
+  // R q * scale * log2(e), as fp16 pairs
+  (void)qp2_all;
+  if (tid < 16 * GK) {
+    constexpr int E = D / 16;
+    const int g = tid >> 4, l16 = tid & 15;
+    float v[E];
+    dev::load_row_part<E>(a.q_raw, a.q_dtype, (head0 + g) * D + l16 * E, v);
+    const uint32_t smask = dev::bitmap_bits(a.sbits, l16 * E, E);
+#pragma unroll
+    for (int i = 0; i < E; ++i) if (smask >> i & 1) v[i] = -v[i];
+    dev::fwht16<E, float>(v, l16);
+    const float mult = a.qmult / sqrtf(float(D));
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] *= mult;
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i)
+      qs[g * (D / 2) + l16 * (E / 2) + i] = dev::pack_f16x2(v[2 * i], v[2 * i + 1]);
+    if constexpr (QJL) {
+      // q'' = R_2 q' from the fp32 q'
+      const uint32_t qmask = dev::bitmap_bits(a.qsbits, l16 * E, E);
+#pragma unroll
+      for (int i = 0; i < E; ++i) if (qmask >> i & 1) v[i] = -v[i];
+      dev::fwht16<E, float>(v, l16);
+      const float nn = 1.0f / sqrtf(float(D));
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i)
+        qs2[g * (D / 2) + l16 * (E / 2) + i] = dev::pack_f16x2(v[2 * i] * nn, v[2 * i + 1] * nn);
+    }
+  }
+  __syncthreads();
+
+  // query quads for the broadcast A operand: lane (block lane/4, row lane%4)
+  // keeps coordinates 4j .. 4j+3 of head lane%4 for j = lane/4 + 16*i
+  mx_u2 qa[NQ], qa2[QJL ? NQ : 1];
+  {
+    const int qm = lane & 3, qb = lane >> 2;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int j = qb + 16 * i;
+      if (qm < GK) {
+        qa[i][0] = qs[qm * (D / 2) + 2 * j];
+        qa[i][1] = qs[qm * (D / 2) + 2 * j + 1];
+        if constexpr (QJL) {
+          qa2[i][0] = qs2[qm * (D / 2) + 2 * j];
+          qa2[i][1] = qs2[qm * (D / 2) + 2 * j + 1];
+        }
+      } else {
+        qa[i][0] = 0u;
+        qa[i][1] = 0u;
+        if constexpr (QJL) qa2[i] = mx_u2{0u, 0u};
+      }
+    }
+  }
+  const uint32_t sl8 = uint32_t(lane) << 3;
 
   float m_run[GK], lpart[GK];
   mx_f4 acc[VJ];
@@ -1966,12 +1989,10 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
   };
 
   {
-    const int64_t wb = t_begin + int64_t(wave) * TW;
     uint32_t* px0 = pex[wave][0];
     uint32_t* px1 = pex[wave][1];
-    if constexpr (mx_prefetch(D, BK, QJL) == 1) {
-      Tile ta, tb;
-      load(wb, ta);
+    if constexpr (PF == 1) {
+      if (!early) load(wb, ta);
       __builtin_amdgcn_sched_barrier(0);
       for (int it = 0; it < iters; it += 2) {
         const int64_t base = wb + int64_t(it) * T;
@@ -1982,10 +2003,11 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
         process(base + T, px1, tb);
       }
     } else {
-      Tile ta, tb, tc;
-      load(wb, ta);
-      __builtin_amdgcn_sched_barrier(0);
-      load(wb + T, tb);
+      if (!early) {
+        load(wb, ta);
+        __builtin_amdgcn_sched_barrier(0);
+        load(wb + T, tb);
+      }
       __builtin_amdgcn_sched_barrier(0);
       for (int it = 0; it < iters; it += 3) {
         const int64_t base = wb + int64_t(it) * T;
@@ -2054,7 +2076,7 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = obuf[g * D + l16 * E + i];
     dev::fwht16<E, float>(v, l16);
-    const uint32_t smask = dev::sign_mask(a.seed, l16 * E, E);
+    const uint32_t smask = dev::bitmap_bits(a.sbits, l16 * E, E);
     const float nn = 1.0f / sqrtf(float(D));
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = (smask >> i & 1) ? -v[i] * nn : v[i] * nn;
