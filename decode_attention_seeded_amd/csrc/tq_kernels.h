@@ -1681,8 +1681,12 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
   constexpr int SB = MxTile<D, BK, BV, QJL>::SB;
   constexpr int KE = 1 << (2 * BK);
   constexpr int VE = 1 << (2 * BV);
-  constexpr int KT_BYTES = KE * 128;           // 32 copies, 128-B entry stride
-  constexpr int VT_BYTES = VE * 256;           // 64 copies, 256-B entry stride
+  // 2-bit codes: one lookup per four codes (a byte indexes a table of fp16
+  // quads: 256 entries, 32 copies of 8 B); wider codes: pair tables
+  constexpr bool KQ4 = BK == 2;
+  constexpr bool VQ4 = BV == 2;
+  constexpr int KT_BYTES = KQ4 ? 256 * 256 : KE * 128;   // pairs: 32 copies, 128-B stride
+  constexpr int VT_BYTES = VQ4 ? 256 * 256 : VE * 256;   // pairs: 64 copies, 256-B stride
   constexpr int NQ = D / 64;                   // query quads kept per lane
   constexpr int PX = GK * TW / 2;              // weight dwords per wave tile
   constexpr float kRescale = 8.0f;
@@ -1707,6 +1711,7 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
   const int kq = lane >> 4;                    // V phase: token quad
   const uint32_t rl4 = uint32_t(lane & 31) << 2;
   const uint32_t vl4 = uint32_t(lane) << 2;
+  const uint32_t l8 = uint32_t(lane & 31) << 3;   // quad tables: the lane's copy
   const int split = blockIdx.x;
   const int unit = blockIdx.y;
   const int chunk = unit % a.chunks;
@@ -1791,20 +1796,44 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
 
   // pair tables: each wave writes whole entries (entry index uniform across
   // the wave, so the centroids are scalar loads), one copy per lane
-#pragma unroll
-  for (int k = 0; k < KE / W; ++k) {
-    const int e = wave + k * W;
-    if (lane < 32)
-      *reinterpret_cast<uint32_t*>(tabs + (e << 7) + (lane << 2)) =
-          dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
-  }
+  // (quad entry e: codes e & 3, e >> 2 & 3, e >> 4 & 3, e >> 6; lane l of
+  // the wave writes dword l & 1 of copy l / 2)
+  if constexpr (KQ4) {
 #pragma unroll 8
-  for (int k = 0; k < VE / W; ++k) {
-    const int e = wave + k * W;
-    *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << 8) + (lane << 2)) =
-        dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
+    for (int k = 0; k < 256 / W; ++k) {
+      const int e = wave + k * W;
+      const uint32_t lo = dev::pack_f16x2(a.cbk[e & 3], a.cbk[(e >> 2) & 3]);
+      const uint32_t hi = dev::pack_f16x2(a.cbk[(e >> 4) & 3], a.cbk[e >> 6]);
+      *reinterpret_cast<uint32_t*>(tabs + (e << 8) + (lane << 2)) = (lane & 1) ? hi : lo;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < KE / W; ++k) {
+      const int e = wave + k * W;
+      if (lane < 32)
+        *reinterpret_cast<uint32_t*>(tabs + (e << 7) + (lane << 2)) =
+            dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
+    }
   }
-  static_assert(KE % W == 0 && VE % W == 0, "table entries split evenly over the waves");
+  if constexpr (VQ4) {
+#pragma unroll 8
+    for (int k = 0; k < 256 / W; ++k) {
+      const int e = wave + k * W;
+      const uint32_t lo = dev::pack_f16x2(a.cbv[e & 3], a.cbv[(e >> 2) & 3]);
+      const uint32_t hi = dev::pack_f16x2(a.cbv[(e >> 4) & 3], a.cbv[e >> 6]);
+      *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << 8) + (lane << 2)) =
+          (lane & 1) ? hi : lo;
+    }
+  } else {
+#pragma unroll 8
+    for (int k = 0; k < VE / W; ++k) {
+      const int e = wave + k * W;
+      *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << 8) + (lane << 2)) =
+          dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
+    }
+  }
+  static_assert(KE % W == 0 && VE % W == 0 && 256 % W == 0,
+                "table entries split evenly over the waves");
   const uint8_t* vtab = tabs + KT_BYTES;
   const uint8_t* stab = tabs + KT_BYTES + VT_BYTES;
   if constexpr (QJL) {
@@ -1905,11 +1934,18 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     if constexpr (QJL) sq[0] = sq[1] = mx_f4{0.f, 0.f, 0.f, 0.f};
     dev::static_for<0, D / 4>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      const uint32_t ka0 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j) | rl4;
-      const uint32_t ka1 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j + 1) | rl4;
       mx_u2 kb;
-      kb[0] = *reinterpret_cast<const uint32_t*>(tabs + ka0);
-      kb[1] = *reinterpret_cast<const uint32_t*>(tabs + ka1);
+      if constexpr (KQ4) {
+        // byte j of the row = the codes of coordinates 4j .. 4j + 3
+        const uint32_t ka = __builtin_amdgcn_perm(cur.kw[j >> 2], l8,
+                                                  0x0C0C0000u | uint32_t(4 + (j & 3)) << 8);
+        kb = *reinterpret_cast<const mx_u2*>(tabs + ka);
+      } else {
+        const uint32_t ka0 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j) | rl4;
+        const uint32_t ka1 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j + 1) | rl4;
+        kb[0] = *reinterpret_cast<const uint32_t*>(tabs + ka0);
+        kb[1] = *reinterpret_cast<const uint32_t*>(tabs + ka1);
+      }
       sk[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
           __builtin_bit_cast(mx_h4, qa[j / 16]), __builtin_bit_cast(mx_h4, kb), sk[j & 1], 4,
           j % 16, 0);
@@ -1962,6 +1998,34 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
       mx_u2 pw = *reinterpret_cast<const mx_u2*>(prow + 16 * blk);
       if (!arow) pw = mx_u2{0u, 0u};
       const mx_h4 pa = __builtin_bit_cast(mx_h4, pw);
+      if constexpr (VQ4) {
+        // the lane's 4 tokens hold VJ <= 16 two-bit codes each (code c at
+        // bits 2c); gather, per coordinate c, the byte t0 | t1<<2 | t2<<4 |
+        // t3<<6 of its 4 tokens' codes: byte b of P, R, Q, S is coordinate
+        // 4b, 4b + 1, 4b + 2, 4b + 3
+        const uint32_t x0 = cur.vx[4 * blk][0], x1 = cur.vx[4 * blk + 1][0];
+        const uint32_t x2 = cur.vx[4 * blk + 2][0], x3 = cur.vx[4 * blk + 3][0];
+        constexpr uint32_t kEven = 0x33333333u, kOdd = 0xCCCCCCCCu, kLo = 0x0F0F0F0Fu;
+        // nibble k: (t0, t1) codes of coordinate 2k (A, C) or 2k + 1 (B, D)
+        const uint32_t A = (x0 & kEven) | ((x1 << 2) & kOdd);
+        const uint32_t B = (x1 & kOdd) | ((x0 >> 2) & kEven);
+        const uint32_t C = (x2 & kEven) | ((x3 << 2) & kOdd);
+        const uint32_t Dw = (x3 & kOdd) | ((x2 >> 2) & kEven);
+        const uint32_t P = (A & kLo) | ((C << 4) & ~kLo);
+        const uint32_t Q = ((A >> 4) & kLo) | (C & ~kLo);
+        const uint32_t R = (B & kLo) | ((Dw << 4) & ~kLo);
+        const uint32_t S = ((B >> 4) & kLo) | (Dw & ~kLo);
+        const uint32_t quad[4] = {P, R, Q, S};
+#pragma unroll
+        for (int c = 0; c < VJ; ++c) {
+          const uint32_t va = __builtin_amdgcn_perm(quad[c & 3], l8,
+                                                    0x0C0C0000u | uint32_t(4 + (c >> 2)) << 8);
+          const mx_u2 vb = *reinterpret_cast<const mx_u2*>(vtab + va);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(mx_h4, vb),
+                                                         acc[c], 0, 0, 0);
+        }
+        continue;
+      }
 #pragma unroll
       for (int grp = 0; grp < VJ / 8; ++grp) {
         uint32_t x[4];
