@@ -162,7 +162,6 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
   da.S = p.splits;
   da.seed = seed;
   (void)rotate;
-  qa.qq_pairs = p.wide != 0;
   da.q_raw = qa.q;
   da.q_dtype = qa.q_dtype;
   da.qmult = qa.mult;

@@ -152,12 +152,10 @@ int plan_decode(int d, int bits_v, int qjl, int B, int Hq, int Hkv, int64_t n_ct
   p->G = Hq / Hkv;
   p->gk = (p->G % 4 == 0) ? 4 : (p->G % 2 == 0) ? 2 : 1;
   p->chunks = p->G / p->gk;
-  p->wide = use_mx(d, bits_v, qjl) ? 2 : use_wide(d, bits_v, qjl) ? 1 : 0;
+  p->wide = use_mx(d, bits_v, qjl) ? 2 : 0;
   const int64_t units = int64_t(B) * Hkv * p->chunks;
   if (p->wide == 2)
     finish_plan(n_ctx, splits, units, 64 * mx_waves(d), 256, p);
-  else if (p->wide)
-    finish_plan(n_ctx, splits, units, 64 * wide_waves(d, bits_v, qjl), 256, p);
   else
     finish_plan(n_ctx, splits, units, decode_tile(d), 2048, p);
   const size_t heads = size_t(B) * Hq;

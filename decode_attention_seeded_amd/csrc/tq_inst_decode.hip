@@ -1,7 +1,7 @@
 // Instantiates the split-K decode kernel for one (D, key bits) pair, chosen
 // at compile time with -DTQ_D=... -DTQ_BK=... (BK = 16: dense bf16 baseline),
 // and exposes one launcher that dispatches over value bits, heads per
-// workgroup, QJL and the wide (8-wave) variant.
+// workgroup, QJL and the matrix-core variant.
 #include "tq_internal.h"
 #include "tq_kernels.h"
 
@@ -37,17 +37,7 @@ static int go(int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
                            qp2);
       return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
     }
-    if (wide) {
-      const uint32_t* qp2 = reinterpret_cast<const uint32_t*>(a.qp);
-      const dim3 block(64 * wide_waves(TQ_D, BV, QJL));
-      if (a.norm_f16)
-        hipLaunchKernelGGL((k_decode_wide<TQ_D, TQ_BK, BV, GK, QJL, true>), grid, block, 0, st,
-                           a, qp2, a.qq);
-      else
-        hipLaunchKernelGGL((k_decode_wide<TQ_D, TQ_BK, BV, GK, QJL, false>), grid, block, 0, st,
-                           a, qp2, a.qq);
-      return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
-    }
+    if (wide) return TQ_ERR_UNSUPPORTED;
   } else {
     if (wide) return TQ_ERR_UNSUPPORTED;
   }

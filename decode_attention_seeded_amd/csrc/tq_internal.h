@@ -58,32 +58,20 @@ inline int norm_bytes(const tq_config* cfg) { return cfg->norm_dtype == TQ_F16 ?
 //   tps:    tokens per split (multiple of tile)
 struct DecodePlan {
   int G = 0, gk = 0, chunks = 0, tile = 0, splits = 0;
-  int wide = 0;      // 1: wave-private kernel on the VALU, 2: on the matrix cores
+  int wide = 0;      // 2: the matrix-core kernel, 0: the workgroup-tile kernel
   int64_t tps = 0;
   // workspace section offsets (bytes)
   size_t off_qp = 0, off_qq = 0, off_ml = 0, off_acc = 0, total = 0;
 };
 
-// Waves per workgroup of the wide decode kernel (one workgroup holds a
-// compute unit; a workgroup round covers 64 tokens per wave). d = 256 keeps
-// twice the accumulators per lane and QJL adds the sign words, so those run
-// fewer waves with more registers each.
-constexpr int wide_waves(int d, int bits_v, int qjl) {
-  return d == 256 ? 8 : (qjl ? 12 : 16 + 0 * bits_v);
-}
-// Tiles each wave loads ahead of the one it processes (1 or 2).
-constexpr int wide_prefetch(int d, int bits_v) { return 1 + 0 * (d + bits_v); }
-
-// Whether the packed decode runs the wide kernel for this format.
-inline bool use_wide(int d, int bits_v, int qjl) {
+// Waves per workgroup of the matrix-core decode kernel (one workgroup holds a
+// compute unit; a workgroup round covers 64 tokens per wave), and whether a
+// format runs it (d 128 or 256, 2- or 4-bit values, with or without QJL).
+constexpr int mx_waves(int d) { return 8 + 0 * d; }
+inline bool use_mx(int d, int bits_v, int qjl) {
   (void)qjl;
   return (d == 128 || d == 256) && (bits_v == 2 || bits_v == 4);
 }
-
-// Waves per workgroup of the matrix-core decode kernel, and whether a format
-// runs it (2- or 4-bit values, with or without the QJL correction).
-constexpr int mx_waves(int d) { return 8 + 0 * d; }
-inline bool use_mx(int d, int bits_v, int qjl) { return use_wide(d, bits_v, qjl); }
 
 // Fills a plan; returns TQ_OK or a negative status.
 int plan_decode(int d, int bits_v, int qjl, int B, int Hq, int Hkv, int64_t n_ctx,

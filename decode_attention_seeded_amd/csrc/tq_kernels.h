@@ -54,7 +54,6 @@ struct QPrepArgs {
   int rotate;             // 0: dense baseline, no rotation
   int pairs;              // 1: write qp as fp16 pairs (packed decode)
   int qjl;
-  int qq_pairs;           // 1: write qq as fp16 pairs too (wide decode)
   float mult;             // scale * log2(e)
   uint64_t seed, qjl_seed;
   uint32_t sbits[8];      // rotation signs, bit i set when sign i is negative
@@ -533,21 +532,10 @@ __global__ void __launch_bounds__(256) k_qprep(QPrepArgs a) {
     const float nn = 1.0f / sqrtf(float(D));
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] *= nn;
-    if (a.qq_pairs) {
-      uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint32_t*>(a.qq) + row * (D / 2) +
-                                            l16 * (E / 2));
+    float4* dq = reinterpret_cast<float4*>(a.qq + row * D + l16 * E);
 #pragma unroll
-      for (int k = 0; k < E / 8; ++k)
-        dst[k] = make_uint4(dev::pack_f16x2(v[8 * k], v[8 * k + 1]),
-                            dev::pack_f16x2(v[8 * k + 2], v[8 * k + 3]),
-                            dev::pack_f16x2(v[8 * k + 4], v[8 * k + 5]),
-                            dev::pack_f16x2(v[8 * k + 6], v[8 * k + 7]));
-    } else {
-      float4* dq = reinterpret_cast<float4*>(a.qq + row * D + l16 * E);
-#pragma unroll
-      for (int k = 0; k < E / 4; ++k)
-        dq[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-    }
+    for (int k = 0; k < E / 4; ++k)
+      dq[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
   }
 }
 
@@ -1173,443 +1161,10 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 }
 
 // ---------------------------------------------------------------------------
-// Split-K decode, wave-private variant for d = 128 or 256 with 2- or 4-bit
-// values, with or without the QJL score correction. One workgroup of W waves (wide_waves) holds a compute
-// unit and shares the codebook pair tables in LDS; each wave runs its own
-// online-softmax pass over interleaved 64-token tiles of the split (wave w
-// takes tiles w, w+W, ...), so the tile loop has no workgroup barrier. The
-// waves' partial results are combined once, at the end.
-//   K phase: lane = token; the key row is in VGPRs, each coordinate pair is
-//            one LDS pair-table lookup feeding GK DPP-broadcast dot2s.
-//   V phase: lane = (row class q = lane & 3, coordinate slice d = lane >> 2):
-//            the lane holds rows 8k+q and 8k+q+4 (k = 0..7) of its CPL =
-//            D/16 coordinates, so each lookup yields a (token, token) value
-//            pair for one coordinate, weighted by the matching fp16 weight
-//            pair. Weights move from the K layout to the V layout through a
-//            wave-private LDS slot.
-//   Loads: key rows, norms and value slices of the next tiles are fetched
-//          while the current one is processed (PF + 1 register buffers used
-//          in rotation), through buffer descriptors whose range ends at the
-//          split's last token (rows past it read as zero).
-//   Softmax: the running max is raised only when some lane's score exceeds
-//            it by more than 8 (log2 units): then a DPP wave max, a rescale
-//            of that head's accumulators, and the weights use the new max.
-// ---------------------------------------------------------------------------
-
-template <int D, int BK, int BV, bool QJL>
-struct WvTile {
-  static constexpr int SW = (D / 16 * BV + 31) / 32;   // dwords per value slice
-  uint32_t kw[D * BK / 32];     // key row of the lane's token
-  uint32_t kn, vn;              // its key and value norms (f16 or f32 bits)
-  uint32_t vx[16][SW];          // value slices: row 4i+q, coordinates CPL*d ..
-  uint32_t sw[QJL ? D / 32 : 1];  // QJL sign bits of the key (bit set: negative)
-  uint32_t kr;                  // QJL residual norm (f16 bits)
-};
-
-// Spreads the eight 2-bit fields of the low 16 bits of x to the low two bits
-// of eight nibbles.
-__device__ __forceinline__ uint32_t spread2to4(uint32_t x) {
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  x = (x | (x << 2)) & 0x33333333u;
-  return x;
-}
-
-template <int D, int BK, int BV, int GK, bool QJL, bool NF16>
-__global__ void __launch_bounds__(64 * wide_waves(D, BV, QJL))
-    __attribute__((amdgpu_waves_per_eu(wide_waves(D, BV, QJL) / 4)))
-k_decode_wide(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
-              const float* __restrict__ qq_all) {
-  static_assert(D == 128 || D == 256, "wave-private decode: d 128 or 256");
-  static_assert(BV == 2 || BV == 4, "wave-private decode: 2- or 4-bit values");
-  constexpr int W = wide_waves(D, BV, QJL);    // waves per workgroup
-  constexpr int PF = wide_prefetch(D, BV);     // tiles loaded ahead
-  constexpr int TW = 64;                       // tokens per wave tile
-  constexpr int T = W * TW;                    // tokens per workgroup round
-  constexpr int NT = 64 * W;                   // threads
-  constexpr int CPL = D / 16;                  // value coordinates per lane
-  constexpr int KREC = D * BK / 8;
-  constexpr int VREC = D * BV / 8;
-  constexpr int KW = D * BK / 32;
-  constexpr int SBYTES = CPL * BV / 8;         // bytes per value slice
-  constexpr int SW = (SBYTES + 3) / 4;
-  constexpr int KE = 1 << (2 * BK);
-  constexpr int VE = 1 << (2 * BV);
-  constexpr int KT_BYTES = KE * 128;           // 32 copies, 128-B entry stride
-  constexpr int VT_BYTES = VE * 256;           // 64 copies, 256-B entry stride
-  constexpr int ST_BYTES = QJL ? 16 * 512 : 0; // QJL sign quads: 64 copies of 8 B
-  constexpr int PX = TW / 2 * GK;              // weight pairs per wave tile
-  constexpr float kRescale = 8.0f;
-  using Tile = WvTile<D, BK, BV, QJL>;
-  static_assert(KW % 4 == 0, "key rows are whole 16-byte loads");
-  static_assert(SBYTES == 2 || SBYTES == 4 || SBYTES == 8, "value slice width");
-
-  constexpr int SLAB_BYTES = W * GK * D * 4;   // per-wave partials, after the loop
-  constexpr int TAB_BYTES = KT_BYTES + VT_BYTES + ST_BYTES;
-  __shared__ __attribute__((aligned(16)))
-  uint8_t tabs[TAB_BYTES > SLAB_BYTES ? TAB_BYTES : SLAB_BYTES];
-  __shared__ __attribute__((aligned(16))) uint32_t pex[W][2][PX];
-  __shared__ uint32_t qs[GK * (D / 2)];
-  __shared__ uint32_t qs2[QJL ? GK * (D / 2) : 1];
-  __shared__ float mlx[W][GK][2];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  // wave index as a scalar, so tile bases and buffer descriptors stay in SGPRs
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int q = lane & 3;
-  const int dsl = lane >> 2;
-  const uint32_t rl4 = uint32_t(lane & 31) << 2;
-  const uint32_t vl4 = uint32_t(lane) << 2;
-  const int split = blockIdx.x;
-  const int unit = blockIdx.y;
-  const int chunk = unit % a.chunks;
-  const int bkv = unit / a.chunks;
-  const int b = bkv / a.Hkv;
-  const int kvh = bkv - b * a.Hkv;
-  const int h0 = kvh * a.G + chunk * GK;
-  const int64_t head0 = int64_t(b) * a.Hq + h0;
-
-  for (int i = tid; i < KE * 32; i += NT) {
-    const int e = i >> 5;
-    *reinterpret_cast<uint32_t*>(tabs + (e << 7) + ((i & 31) << 2)) =
-        dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
-  }
-  for (int i = tid; i < VE * 64; i += NT) {
-    const int e = i >> 6;
-    *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << 8) + ((i & 63) << 2)) =
-        dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
-  }
-  const uint8_t* vtab = tabs + KT_BYTES;
-  const uint8_t* stab = tabs + KT_BYTES + VT_BYTES;
-  if constexpr (QJL) {
-    // entry e: the fp16 pairs (s0, s1), (s2, s3) with s_k = -1 where bit k
-    // of e is set, else +1
-    for (int i = tid; i < 16 * 64; i += NT) {
-      const int e = i >> 6;
-      const float s0 = (e & 1) ? -1.f : 1.f, s1 = (e & 2) ? -1.f : 1.f;
-      const float s2 = (e & 4) ? -1.f : 1.f, s3 = (e & 8) ? -1.f : 1.f;
-      *reinterpret_cast<uint2*>(tabs + KT_BYTES + VT_BYTES + (e << 9) + ((i & 63) << 3)) =
-          make_uint2(dev::pack_f16x2(s0, s1), dev::pack_f16x2(s2, s3));
-    }
-  }
-  // query fp16 pairs of the GK heads (and the QJL query R_2 q'); each K-phase
-  // chunk reads its 16 pairs per head into VGPRs for the DPP broadcast
-  for (int i = tid; i < GK * (D / 2); i += NT) {
-    qs[i] = qp2_all[head0 * (D / 2) + i];
-    if constexpr (QJL) qs2[i] = reinterpret_cast<const uint32_t*>(qq_all)[head0 * (D / 2) + i];
-  }
-  const uint32_t* qrow = qs + (lane & 15);
-  const uint32_t* qrow2 = qs2 + (lane & 15);
-  const uint32_t sl8 = uint32_t(lane) << 3;
-
-  const int64_t t_begin = int64_t(split) * a.tps;
-  const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
-  const int64_t row0 = int64_t(bkv) * a.capacity;
-  constexpr int nb = NF16 ? 2 : 4;
-  const int iters = int((t_end - t_begin + T - 1) / T);
-
-  auto rows_left = [&](int64_t base) -> uint32_t {
-    const int64_t n = t_end - base;
-    return uint32_t(n <= 0 ? 0 : (n < TW ? n : TW));
-  };
-  // voffsets: the lane's key row, its norms, and its value slices (row q,
-  // coordinates CPL*dsl .. CPL*dsl + CPL - 1)
-  const uint32_t ko0 = uint32_t(lane) * KREC;
-  const uint32_t no0 = uint32_t(lane) * nb;
-  const uint32_t vo0 = uint32_t(q) * VREC + uint32_t(dsl) * SBYTES;
-  const uint32_t so0 = uint32_t(lane) * (D / 8);
-  // per-load constants go in the scalar offset operand, so they cost neither
-  // VALU work nor loop-invariant VGPRs
-  auto load = [&](int64_t base, Tile& t) {
-    const uint32_t n = rows_left(base);
-    const auto rk = dev::buffer_rsrc(a.kc + (row0 + base) * KREC, n * KREC);
-#pragma unroll
-    for (int k = 0; k < KW / 4; ++k) {
-      const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rk, ko0, 16 * k, 0);
-      t.kw[4 * k] = q4[0]; t.kw[4 * k + 1] = q4[1]; t.kw[4 * k + 2] = q4[2];
-      t.kw[4 * k + 3] = q4[3];
-    }
-    const uint8_t* kn_p = static_cast<const uint8_t*>(a.kn) + (row0 + base) * nb;
-    const uint8_t* vn_p = static_cast<const uint8_t*>(a.vn) + (row0 + base) * nb;
-    if constexpr (NF16) {
-      t.kn = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(kn_p, n * nb), no0, 0, 0);
-      t.vn = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(vn_p, n * nb), no0, 0, 0);
-    } else {
-      t.kn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(kn_p, n * nb), no0, 0, 0);
-      t.vn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(vn_p, n * nb), no0, 0, 0);
-    }
-    if constexpr (QJL) {
-      const auto rs = dev::buffer_rsrc(reinterpret_cast<const uint8_t*>(a.kq) +
-                                           (row0 + base) * (D / 8), n * (D / 8));
-#pragma unroll
-      for (int k = 0; k < D / 128; ++k) {
-        const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rs, so0, 16 * k, 0);
-        t.sw[4 * k] = q4[0]; t.sw[4 * k + 1] = q4[1]; t.sw[4 * k + 2] = q4[2];
-        t.sw[4 * k + 3] = q4[3];
-      }
-      t.kr = __builtin_amdgcn_raw_buffer_load_b16(
-          dev::buffer_rsrc(a.kr + (row0 + base), n * 2), uint32_t(lane) * 2, 0, 0);
-    }
-    const auto rv = dev::buffer_rsrc(a.vc + (row0 + base) * VREC, n * VREC);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if constexpr (SBYTES == 8) {
-        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rv, vo0, i * 4 * VREC, 0);
-        t.vx[i][0] = v2[0];
-        t.vx[i][SW - 1] = v2[1];
-      } else if constexpr (SBYTES == 4) {
-        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo0, i * 4 * VREC, 0);
-      } else {
-        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b16(rv, vo0, i * 4 * VREC, 0);
-      }
-    }
-  };
-
-  float m_run[GK], lpart[GK];
-  float acc[GK][CPL];
-#pragma unroll
-  for (int g = 0; g < GK; ++g) {
-    m_run[g] = -INFINITY;
-    lpart[g] = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[g][c] = 0.f;
-  }
-
-  auto process = [&](int64_t base, uint32_t* px, const Tile& cur) {
-    // ---------------- K phase: lane = token (EXEC full for the DPP)
-    const bool valid = base + lane < t_end;
-    float s[GK];
-#pragma unroll
-    for (int g = 0; g < GK; ++g) s[g] = 0.f;
-#pragma unroll
-    for (int ch = 0; ch < D / 32; ++ch) {
-      uint32_t qg[GK];
-#pragma unroll
-      for (int g = 0; g < GK; ++g) qg[g] = qrow[g * (D / 2) + ch * 16];
-      dev::static_for<0, 16>([&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        const uint32_t ka = dev::field_at<2 * BK, 7>(cur.kw, ch * 16 + m) | rl4;
-        const uint32_t cp = *reinterpret_cast<const uint32_t*>(tabs + ka);
-        dev::dot2_bcast<m, GK, m == 15>(s, qg, cp);
-        if constexpr (m == 7) __builtin_amdgcn_sched_barrier(0);
-      });
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // QJL: sum of +-q'' over the key's sign bits, four signs per lookup
-    float tq[QJL ? GK : 1];
-    if constexpr (QJL) {
-#pragma unroll
-      for (int g = 0; g < GK; ++g) tq[g] = 0.f;
-#pragma unroll
-      for (int ch = 0; ch < D / 32; ++ch) {
-        uint32_t qg[GK];
-#pragma unroll
-        for (int g = 0; g < GK; ++g) qg[g] = qrow2[g * (D / 2) + ch * 16];
-        dev::static_for<0, 8>([&](auto jc) {
-          constexpr int j = decltype(jc)::value;
-          const uint32_t sa = dev::field_at<4, 9>(cur.sw, ch * 8 + j) | sl8;
-          const uint2 sp = *reinterpret_cast<const uint2*>(stab + sa);
-          dev::dot2_bcast<2 * j, GK>(tq, qg, sp.x);
-          dev::dot2_bcast<2 * j + 1, GK, j == 7>(tq, qg, sp.y);
-        });
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    const float knrm = NF16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
-    const float vnrm = NF16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn);
-    const float ks = knrm * a.kscale;
-    const float nv = vnrm * a.vscale;
-    const float rho = QJL ? dev::f16_to_f32(cur.kr) * a.qjl_c : 0.f;
-
-    // ---------------- online softmax with a lazily raised running max
-    uint16_t* p16 = reinterpret_cast<uint16_t*>(px);
-    const int pslot = (((lane >> 3) * 4 + (lane & 3)) * GK) * 2 + ((lane >> 2) & 1);
-#pragma unroll
-    for (int g = 0; g < GK; ++g) {
-      s[g] *= ks;
-      if constexpr (QJL) s[g] = fmaf(rho, tq[g], s[g]);
-      if (__ballot(valid && s[g] > m_run[g] + kRescale)) {     // wave-uniform
-        const float mx = dev::dpp_wave_max(valid ? s[g] : -INFINITY);
-        const float m_new = fmaxf(m_run[g], mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-        m_run[g] = m_new;
-        lpart[g] *= alpha;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[g][c] *= alpha;
-      }
-      // branch-free: rows past the split have s = 0 and zero norms
-      const float e = __builtin_amdgcn_exp2f(s[g] - m_run[g]);
-      const float p = valid ? e : 0.f;
-      lpart[g] += p;
-      p16[pslot + 2 * g] = __builtin_bit_cast(uint16_t, _Float16(p * nv));
-    }
-    // the weights written above are read back by other lanes of this wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---------------- V phase: lane = (row class q, coordinate slice dsl)
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t p2[GK];
-      const uint32_t* pp = px + (k * 4 + q) * GK;
-      if constexpr (GK == 4) {
-        const uint4 v4 = *reinterpret_cast<const uint4*>(pp);
-        p2[0] = v4.x; p2[1] = v4.y; p2[2] = v4.z; p2[3] = v4.w;
-      } else if constexpr (GK == 2) {
-        const uint2 v2 = *reinterpret_cast<const uint2*>(pp);
-        p2[0] = v2.x; p2[1] = v2.y;
-      } else {
-        p2[0] = pp[0];
-      }
-#pragma unroll
-      for (int hw = 0; hw < CPL / 8; ++hw) {   // coordinates 8hw .. 8hw+7 of the slice
-        uint32_t lo, hi;  // byte b: (x code, y code) of coordinate 2b (lo), 2b+1 (hi)
-        if constexpr (BV == 4) {
-          const uint32_t x = cur.vx[2 * k][hw], y = cur.vx[2 * k + 1][hw];  // rows 8k+q, +4
-          lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
-          hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
-        } else {
-          const uint32_t x = (cur.vx[2 * k][0] >> (16 * hw)) & 0xFFFFu;
-          const uint32_t y = (cur.vx[2 * k + 1][0] >> (16 * hw)) & 0xFFFFu;
-          const uint32_t w = spread2to4(x) | (spread2to4(y) << 2);   // nibble c: coord c
-          lo = w & 0x0F0F0F0Fu;
-          hi = (w >> 4) & 0x0F0F0F0Fu;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t word = (e & 1) ? hi : lo;
-          const uint32_t va =
-              __builtin_amdgcn_perm(word, vl4, 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8);
-          const uint32_t vp = *reinterpret_cast<const uint32_t*>(vtab + va);
-#pragma unroll
-          for (int g = 0; g < GK; ++g)
-            acc[g][8 * hw + e] = dev::dot2(p2[g], vp, acc[g][8 * hw + e]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  // tiles are loaded PF tiles ahead of the one being processed (register
-  // buffers used in rotation, loop unrolled PF + 1 times); all waves run
-  // `iters` rounds (tiles past the split read as zero, zero weight)
-  __syncthreads();
-  {
-    const int64_t wb = t_begin + int64_t(wave) * TW;
-    uint32_t* px0 = pex[wave][0];
-    uint32_t* px1 = pex[wave][1];
-    if constexpr (PF == 1) {
-      Tile ta, tb;
-      load(wb, ta);
-      __builtin_amdgcn_sched_barrier(0);
-      for (int it = 0; it < iters; it += 2) {
-        const int64_t base = wb + int64_t(it) * T;
-        load(base + T, tb);
-        process(base, px0, ta);
-        if (it + 1 >= iters) break;
-        load(base + 2 * T, ta);
-        process(base + T, px1, tb);
-      }
-    } else {
-      static_assert(PF == 2, "prefetch depth 1 or 2");
-      Tile ta, tb, tc;
-      // issue order matters: the loop's waits count loads issued after ta
-      load(wb, ta);
-      __builtin_amdgcn_sched_barrier(0);
-      load(wb + T, tb);
-      __builtin_amdgcn_sched_barrier(0);
-      for (int it = 0; it < iters; it += 3) {
-        const int64_t base = wb + int64_t(it) * T;
-        load(base + 2 * T, tc);
-        process(base, px0, ta);
-        if (it + 1 >= iters) break;
-        load(base + 3 * T, ta);
-        process(base + T, px1, tb);
-        if (it + 2 >= iters) break;
-        load(base + 4 * T, tb);
-        process(base + 2 * T, px0, tc);
-      }
-    }
-  }
-
-  // ---------------- combine the waves, then R^T of the weighted sum
-  float lw[GK];
-#pragma unroll
-  for (int g = 0; g < GK; ++g) {
-    lw[g] = dev::wave_sum(lpart[g]);
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      acc[g][c] += __shfl_xor(acc[g][c], 1);
-      acc[g][c] += __shfl_xor(acc[g][c], 2);
-    }
-  }
-  __syncthreads();                       // tables are dead: reuse them below
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < GK; ++g) {
-      mlx[wave][g][0] = m_run[g];
-      mlx[wave][g][1] = lw[g];
-    }
-  }
-  __syncthreads();
-  float* slab = reinterpret_cast<float*>(tabs);          // [W][GK][D]
-  float M[GK];
-#pragma unroll
-  for (int g = 0; g < GK; ++g) {
-    M[g] = mlx[0][g][0];
-#pragma unroll
-    for (int w = 1; w < W; ++w) M[g] = fmaxf(M[g], mlx[w][g][0]);
-    const float f = m_run[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - M[g]);
-    if (q == 0) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) slab[(wave * GK + g) * D + dsl * CPL + c] = acc[g][c] * f;
-    }
-  }
-  __syncthreads();
-  float* obuf = reinterpret_cast<float*>(pex);            // [GK][D]
-  static_assert(sizeof(pex) >= GK * D * 4, "output staging fits the weight slots");
-  for (int i = tid; i < GK * D; i += NT) {
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) sum += slab[w * GK * D + i];
-    obuf[i] = sum;
-  }
-  __syncthreads();
-  if (tid < GK) {
-    float l = 0.f;
-    for (int w = 0; w < W; ++w) {
-      const float mw = mlx[w][tid][0];
-      if (mw != -INFINITY) l += mlx[w][tid][1] * __builtin_amdgcn_exp2f(mw - M[tid]);
-    }
-    float* ml = a.ml + ((head0 + tid) * a.S + split) * 2;
-    ml[0] = M[tid];
-    ml[1] = l;
-  }
-  if (tid < 16 * GK) {
-    constexpr int E = D / 16;
-    const int g = tid >> 4, l16 = tid & 15;
-    float v[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = obuf[g * D + l16 * E + i];
-    dev::fwht16<E, float>(v, l16);
-    const uint32_t smask = dev::bitmap_bits(a.sbits, l16 * E, E);
-    const float nn = 1.0f / sqrtf(float(D));
-#pragma unroll
-    for (int i = 0; i < E; ++i) v[i] = (smask >> i & 1) ? -v[i] * nn : v[i] * nn;
-    float4* dst = reinterpret_cast<float4*>(a.acc + ((head0 + g) * a.S + split) * D + l16 * E);
-#pragma unroll
-    for (int k = 0; k < E / 4; ++k)
-      dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Split-K decode on the matrix cores, d = 128 or 256 with 2- or 4-bit values,
-// with or without the QJL score correction. Workgroup, tile and softmax structure are those of
-// k_decode_wide (W waves, each with its own online-softmax pass over
-// interleaved 64-token tiles, combined once at the end); the two
+// with or without the QJL score correction. W waves per workgroup (one
+// workgroup per compute unit), each with its own online-softmax pass over
+// interleaved 64-token tiles, combined once at the end; the two
 // contractions of a tile run as MFMAs on fp16 operands dequantized through
 // the pair tables:
 //   scores  S[g][t] = q_g . k_t with v_mfma_f32_4x4x4_16b_f16: 16 blocks of
@@ -1644,19 +1199,12 @@ struct MxTile {
   uint32_t kr;                  // QJL residual norm (f16 bits)
 };
 
-// For two tokens' slices x, y of 8 coordinates: byte b of *lo is the value
-// pair-table index (x code, y code) of coordinate 2b, of *hi of 2b + 1.
-template <int BV>
+// For two tokens' 4-bit slices x, y of 8 coordinates: byte b of *lo is the
+// value pair-table index (x code, y code) of coordinate 2b, of *hi of 2b + 1.
 __device__ __forceinline__ void mx_pair_words(uint32_t x, uint32_t y, uint32_t* lo,
                                               uint32_t* hi) {
-  if constexpr (BV == 4) {
-    *lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
-    *hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
-  } else {
-    const uint32_t w = spread2to4(x & 0xFFFFu) | (spread2to4(y & 0xFFFFu) << 2);
-    *lo = w & 0x0F0F0F0Fu;
-    *hi = (w >> 4) & 0x0F0F0F0Fu;
-  }
+  *lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
+  *hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
 }
 
 // tiles each wave loads ahead of the one it processes (1 or 2): two where
@@ -2024,19 +1572,15 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
           acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(mx_h4, vb),
                                                          acc[c], 0, 0, 0);
         }
-        continue;
-      }
+      } else {
 #pragma unroll
       for (int grp = 0; grp < VJ / 8; ++grp) {
         uint32_t x[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t w = cur.vx[4 * blk + i][BV == 4 ? grp : 0];
-          x[i] = (BV == 2 && grp == 1) ? (w >> 16) : w;
-        }
+        for (int i = 0; i < 4; ++i) x[i] = cur.vx[4 * blk + i][grp];
         uint32_t lo01, hi01, lo23, hi23;
-        mx_pair_words<BV>(x[0], x[1], &lo01, &hi01);
-        mx_pair_words<BV>(x[2], x[3], &lo23, &hi23);
+        mx_pair_words(x[0], x[1], &lo01, &hi01);
+        mx_pair_words(x[2], x[3], &lo23, &hi23);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8;
@@ -2048,6 +1592,7 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
           acc[8 * grp + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
               pa, __builtin_bit_cast(mx_h4, vb), acc[8 * grp + e], 0, 0, 0);
         }
+      }
       }
     }
   };
