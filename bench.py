@@ -57,6 +57,13 @@ def traffic_from_profile(wid):
     return t.get("hbm_bytes_per_launch")
 
 
+def alg_bytes_of(tq, cfg, w, q):
+    """Algorithmic bytes of one decode call: every packed plane over the
+    context, the queries in and the fp32 outputs."""
+    cache_bytes, _ = tq.tq_cache_bytes(cfg, w.B, w.Hkv, w.N)
+    return cache_bytes + q.numel() * q.element_size() + w.B * w.Hq * w.d * 4
+
+
 def to_dev_bf16(torch, raw):
     import numpy as np
     return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).cuda()
@@ -215,6 +222,35 @@ def main():
     log(f"step {ms_per_step * 1e3:.1f} us; decode call avg {dec_avg_us:.1f} us "
         f"(p10 {np.percentile(dec_us, 10):.1f}, p90 {np.percentile(dec_us, 90):.1f})")
 
+    # streaming-read probe over as many bytes as one decode call reads, and
+    # decode calls after a 1 GiB read has evicted the 256 MB last-level cache
+    probe_bytes = (alg_bytes_of(tq, cfg, w, q) + 15) // 16 * 16
+    pbuf = torch.empty(probe_bytes, dtype=torch.uint8, device="cuda")
+    sink = tq.tq_read_probe(pbuf)
+    a, b = ev(), ev()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(20):
+        tq.tq_read_probe(pbuf, sink)
+    b.record()
+    torch.cuda.synchronize()
+    probe_us = a.elapsed_time(b) * 1e3 / 20
+    del pbuf
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    fsink = tq.tq_read_probe(flush)
+    cold_us = []
+    for _ in range(20):
+        tq.tq_read_probe(flush, fsink)
+        c0, c1 = ev(), ev()
+        c0.record()
+        tq.tq_attend_decode(cfg, q, cache, w.N, out, ws)
+        c1.record()
+        torch.cuda.synchronize()
+        cold_us.append(c0.elapsed_time(c1) * 1e3)
+    del flush
+    log(f"read probe {probe_bytes / probe_us / 1e3:.1f} GB/s over {probe_bytes} B; cold decode "
+        f"median {np.median(cold_us):.1f} us")
+
     # append-encode alone
     enc_us = None
     if A:
@@ -256,9 +292,8 @@ def main():
 
     # algorithmic bytes of one decode call: every packed plane over N tokens,
     # plus q in and out
-    cache_bytes, _ = tq.tq_cache_bytes(cfg, w.B, w.Hkv, w.N)
+    alg_bytes = alg_bytes_of(tq, cfg, w, q)
     qbytes = q.numel() * q.element_size()
-    alg_bytes = cache_bytes + qbytes + out.numel() * 4
     achieved = alg_bytes / (dec_avg_us * 1e-6) / 1e9
     traffic = traffic_from_profile(w.wid)
 
@@ -318,6 +353,19 @@ def main():
         },
         "cpu_baseline": cpu,
         "decode_call_us": round(dec_avg_us, 2),
+        "decode_call_percentiles_us": {
+            "p10": round(float(np.percentile(dec_us, 10)), 2),
+            "median": round(float(np.median(dec_us)), 2),
+            "p90": round(float(np.percentile(dec_us, 90)), 2)},
+        "decode_call_cold_us": {
+            "note": "each call after a 1 GiB streaming read (last-level cache evicted)",
+            "p10": round(float(np.percentile(cold_us, 10)), 2),
+            "median": round(float(np.median(cold_us)), 2),
+            "p90": round(float(np.percentile(cold_us, 90)), 2)},
+        "read_probe": {
+            "bytes": probe_bytes, "us": round(probe_us, 2),
+            "gbps": round(probe_bytes / probe_us / 1e3, 1),
+            "decode_frac_of_probe": round(achieved / (probe_bytes / probe_us / 1e3), 4)},
         "decode_kv_tokens_per_s": round(w.B * w.N / (dec_avg_us * 1e-6), 1),
         "append_encode_us": round(enc_us, 2) if enc_us else None,
         "single_token_step": single,

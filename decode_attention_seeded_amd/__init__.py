@@ -13,5 +13,6 @@ from .binding import (  # noqa: F401
     tq_attend_decode,
     tq_bits_split, tq_cache_bytes, tq_codebook, tq_config, tq_cache,
     tq_dense_decode_bf16, tq_dense_workspace_bytes, tq_encode_kv, tq_num_splits,
-    tq_qjl_sketch, tq_rht, tq_signs, tq_strerror, tq_workspace_bytes, workspace,
+    tq_qjl_sketch, tq_read_probe, tq_rht, tq_signs, tq_strerror, tq_workspace_bytes,
+    workspace,
 )

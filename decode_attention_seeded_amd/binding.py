@@ -32,7 +32,7 @@ EXPORTS = (
     "tq_bits_split", "tq_codebook", "tq_signs", "tq_cache_bytes", "tq_rht",
     "tq_encode_kv", "tq_qjl_sketch", "tq_num_splits", "tq_workspace_bytes",
     "tq_attend_decode", "tq_append_attend_decode", "tq_dense_workspace_bytes",
-    "tq_dense_decode_bf16",
+    "tq_dense_decode_bf16", "tq_read_probe_sink_words", "tq_read_probe",
     "tq_strerror",
 )
 
@@ -85,6 +85,8 @@ def _lib():
                                             SZ, P]),
             "tq_dense_workspace_bytes": (I64, [I, I, I, I, I64, I]),
             "tq_dense_decode_bf16": (I, [P, P, P, I, I, I, I, I64, F, I, P, P, SZ, P]),
+            "tq_read_probe_sink_words": (I64, [I64]),
+            "tq_read_probe": (I, [P, I64, P, P]),
             "tq_strerror": (ctypes.c_char_p, [I]),
         }
         for name, (res, args) in sig.items():
@@ -305,6 +307,20 @@ def tq_append_attend_decode(cfg: Config, k_new, v_new, q, cache: PackedCache, n_
         ctypes.byref(cfg.c()), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(q),
         _dtype_code(q), B, Hq, ctypes.byref(c), n_ctx, float(scale), splits, _ptr(out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)), "tq_append_attend_decode")
+
+
+def tq_read_probe(src, sink=None, stream=None):
+    """Streaming read of every byte of the device tensor `src` (bandwidth
+    probe); returns the sink tensor (one XOR word per wave)."""
+    import torch
+    nbytes = src.numel() * src.element_size()
+    if not src.is_contiguous():
+        raise TqError(TQ_ERR_ARG, "tq_read_probe: src must be contiguous")
+    words = _check(_lib().tq_read_probe_sink_words(nbytes), "tq_read_probe_sink_words")
+    if sink is None:
+        sink = torch.empty(max(words, 1), dtype=torch.int32, device=src.device)
+    _check(_lib().tq_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "tq_read_probe")
+    return sink
 
 
 def workspace(nbytes: int, device="cuda"):

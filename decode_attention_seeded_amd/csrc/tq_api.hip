@@ -259,6 +259,37 @@ int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
 }
 
 }  // namespace
+// ---------------------------------------------------------------------------
+// Streaming-read probe: every 16-byte chunk of the buffer is loaded once
+// with nontemporal (streaming) loads, four chunks in flight per lane,
+// XOR-folded; one word per wave is written.
+// ---------------------------------------------------------------------------
+
+constexpr int kProbeBlocks = 16384;
+
+__global__ void __launch_bounds__(256) k_read_probe(const uint4* __restrict__ p, int64_t n16,
+                                                    uint32_t* __restrict__ sink) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const v4u* q = reinterpret_cast<const v4u*>(p);
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    v4u a[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = __builtin_nontemporal_load(q + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x ^= a[u][0] ^ a[u][1] ^ a[u][2] ^ a[u][3];
+  }
+  for (; i < n16; i += stride) {
+    const v4u a = __builtin_nontemporal_load(q + i);
+    x ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x ^= __shfl_xor(x, m);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = x;
+}
+
 }  // namespace tq
 
 using namespace tq;
@@ -384,6 +415,26 @@ int tq_dense_decode_bf16(const void* q, const void* k, const void* v, int B, int
   da.capacity = n_ctx;
   da.n_ctx = n_ctx;
   return run_decode(d, 16, 16, 0, p, da, qa, B, Hq, Hkv, ws, out, 0, 0, stream);
+}
+
+int64_t tq_read_probe_sink_words(int64_t bytes) {
+  if (bytes < 0) return TQ_ERR_ARG;
+  const int64_t n16 = bytes / 16;
+  const int64_t blocks = (n16 + 255) / 256;
+  return 4 * (blocks < kProbeBlocks ? blocks : kProbeBlocks);
+}
+
+int tq_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (bytes < 0 || bytes % 16 != 0) return TQ_ERR_ARG;
+  if (bytes == 0) return TQ_OK;
+  if (!src || !sink) return TQ_ERR_ARG;
+  if (!aligned16(src)) return TQ_ERR_ALIGN;
+  int st = device_ready();
+  if (st != TQ_OK) return st;
+  const unsigned blocks = unsigned(tq_read_probe_sink_words(bytes) / 4);
+  hipLaunchKernelGGL(k_read_probe, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const uint4*>(src), bytes / 16, sink);
+  return last_launch();
 }
 
 }  // extern "C"

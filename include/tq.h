@@ -231,6 +231,18 @@ int tq_dense_decode_bf16(const void* q, const void* k, const void* v, int B,
                          int splits, float* out, void* ws, size_t ws_bytes,
                          hipStream_t stream);
 
+/*
+ * Streaming-read probe for bandwidth measurement (not part of the method):
+ * reads `bytes` bytes at `src` once with 16-byte nontemporal loads and writes the XOR of
+ * every 32-bit word a wave read to sink[w], one word per wave of the launch
+ * (the XOR of all of sink[0 .. tq_read_probe_sink_words(bytes)) is the XOR of
+ * every word of the buffer). src: device, 16-byte aligned, bytes a multiple
+ * of 16; sink: device, caller-owned. Returns TQ_ERR_ARG / TQ_ERR_ALIGN
+ * before queueing anything when these do not hold.
+ */
+int64_t tq_read_probe_sink_words(int64_t bytes);
+int tq_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Human-readable name of a tq_status. Never NULL. */
 const char* tq_strerror(int status);
 

@@ -234,3 +234,17 @@ def test_rht_qjl_dense_validation():
     assert lib.tq_dense_decode_bf16(*small) == tq.TQ_ERR_WORKSPACE
     mis = (A, MIS, A, 1, 4, 2, 128, 10, 0.0, 0, A, A, 1 << 30, None)
     assert lib.tq_dense_decode_bf16(*mis) == tq.TQ_ERR_ALIGN
+
+
+def test_read_probe_validation():
+    lib = tq.lib()
+    assert lib.tq_read_probe(A, -16, A, None) == tq.TQ_ERR_ARG
+    assert lib.tq_read_probe(A, 24, A, None) == tq.TQ_ERR_ARG
+    assert lib.tq_read_probe(None, 32, A, None) == tq.TQ_ERR_ARG
+    assert lib.tq_read_probe(A, 32, None, None) == tq.TQ_ERR_ARG
+    assert lib.tq_read_probe(MIS, 32, A, None) == tq.TQ_ERR_ALIGN
+    assert lib.tq_read_probe(A, 0, A, None) == tq.TQ_OK
+    # one word per wave: 4 per 256-thread block, at most 16384 blocks
+    assert lib.tq_read_probe_sink_words(16) == 4
+    assert lib.tq_read_probe_sink_words(16 * 256 * 3) == 12
+    assert lib.tq_read_probe_sink_words(1 << 40) == 4 * 16384

@@ -299,3 +299,19 @@ def test_dense_bf16_baseline_matches_fp64_attention():
             want[b, h] = (p / p.sum()) @ fv[b, h // G]
     err, _ = rel_err(out.cpu().numpy().astype(np.float64), want)
     assert err <= 1e-4
+
+
+def test_read_probe_reads_every_word():
+    # the XOR of the per-wave words equals the XOR of every 32-bit word of
+    # the buffer: each 16-byte chunk was loaded exactly once
+    torch = torch_cuda()
+    import decode_attention_seeded_amd as tq
+    rng = np.random.default_rng(7)
+    for nbytes in (16, 4096 + 48, (3 << 20) + 16 * 37):
+        host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
+        dev = torch.from_numpy(host.view(np.int32)).cuda()
+        log(f"read probe: {nbytes} bytes")
+        sink = tq.tq_read_probe(dev)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(host), nbytes
