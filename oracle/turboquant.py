@@ -55,7 +55,7 @@ __all__ = [
     "attend", "attend_dense", "attend_rotated_blocked", "QJL_CONST",
     "turboquant_enabled", "bits_split", "tq_bytes_per_token",
     "affine_bytes_per_token", "fp16_bytes_per_token", "boundary_mask",
-    "qjl_boundary_mask", "merge_partials",
+    "qjl_boundary_mask", "merge_partials", "attend_prefill",
 ]
 
 MASK64 = (1 << 64) - 1
@@ -518,6 +518,49 @@ def attend(q, cache, n_ctx, *, d, seed, bits_k, bits_v, Hkv, scale=None,
                                   seed=seed, bits_k=bits_k, bits_v=bits_v,
                                   scale=scale, qjl=qjl, qjl_seed=qjl_seed,
                                   block=block)
+
+
+def attend_prefill(q, cache, n_ctx, *, d, seed, bits_k, bits_v, Hkv, scale=None,
+                   qjl=False, qjl_seed=None):
+    """Causal multi-query attention of a prefill chunk over the packed cache.
+
+    The chunk's n_q tokens are the last n_q of the first n_ctx cache rows
+    (they were appended before the call); query i sits at position
+    p_i = n_ctx - n_q + i and attends to tokens 0..p_i. This is the same
+    score, softmax and value sum as `attend_dense` (the API page's patched
+    attention: the query rotated into the cache's frame, the QJL term added),
+    with the causal mask of a prefill step.
+
+    q: [B][Hq][n_q][d]. Returns [B][Hq][n_q][d] float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, n_q, _ = q.shape
+    G = Hq // Hkv
+    tau = 1.0 / math.sqrt(d) if not scale else scale
+    qs = seed + 1 if qjl_seed is None else qjl_seed
+    pos = n_ctx - n_q + np.arange(n_q)
+    future = np.arange(n_ctx)[None, :] > pos[:, None]         # [n_q][n_ctx]
+    out = np.zeros((B, Hq, n_q, d))
+    for b in range(B):
+        for g in range(Hkv):
+            kc = unpack_codes(cache["kc"][b, g, :n_ctx], bits_k, d)
+            vc = unpack_codes(cache["vc"][b, g, :n_ctx], bits_v, d)
+            k_hat = rht_inverse(dequant_rot(kc, cache["kn"][b, g, :n_ctx], bits_k), seed)
+            v_hat = rht_inverse(dequant_rot(vc, cache["vn"][b, g, :n_ctx], bits_v), seed)
+            if qjl:
+                sigma = 1.0 - 2.0 * unpack_signs(cache["kq"][b, g, :n_ctx], d)
+            for h in range(g * G, (g + 1) * G):
+                logits = tau * (q[b, h] @ k_hat.T)                 # [n_q][n_ctx]
+                if qjl:
+                    qq = rht(rht(q[b, h], seed), qs)
+                    logits = logits + tau * math.sqrt(QJL_CONST / d) * \
+                        (qq @ sigma.T) * cache["kr"][b, g, :n_ctx][None, :]
+                logits = np.where(future, -np.inf, logits)
+                logits = logits - logits.max(axis=1, keepdims=True)
+                p = np.exp(logits)
+                p /= p.sum(axis=1, keepdims=True)
+                out[b, h] = p @ v_hat
+    return out
 
 
 # ---------------------------------------------------------------------------

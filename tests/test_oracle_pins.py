@@ -385,6 +385,46 @@ def test_attention_scale_and_merge():
     np.testing.assert_allclose(a, dense, atol=1e-13)
 
 
+@pytest.mark.parametrize("qjl", [False, True])
+def test_prefill_rows_equal_brute_force_over_their_prefix(qjl):
+    """Causal prefill: query i of the chunk sits at position n_ctx - n_q + i
+    and equals brute-force attention over tokens 0..that position."""
+    d, B, Hq, Hkv, N, n_q = 16, 1, 4, 2, 21, 7
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((B, Hq, n_q, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    cache = o.encode_kv(k, v, seed=3, bits_k=3, bits_v=4, norm_dtype="f16", qjl=qjl,
+                        qjl_seed=11)
+    got = o.attend_prefill(q, cache, N, d=d, seed=3, bits_k=3, bits_v=4, Hkv=Hkv, qjl=qjl,
+                           qjl_seed=11)
+    tau = 1 / math.sqrt(d)
+    for i in range(n_q):
+        p = N - n_q + i
+        want = _brute_attention(q[:, :, i], k[:, :, :p + 1], v[:, :, :p + 1], 3, 3, 4, "f16",
+                                Hkv, tau, qjl, 11)
+        np.testing.assert_allclose(got[:, :, i], want, atol=1e-12, rtol=0)
+
+
+def test_prefill_special_cases():
+    """The chunk's first query of a fresh cache sees token 0 only (output =
+    v_hat_0); a one-query chunk is the decode step."""
+    d, N = 32, 12
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 2, N, d))
+    k = rng.standard_normal((1, 1, N, d))
+    v = rng.standard_normal((1, 1, N, d))
+    cache = o.encode_kv(k, v, seed=0, bits_k=2, bits_v=3, norm_dtype="f32")
+    vhat = o.rht_inverse(o.dequant_rot(o.unpack_codes(cache["vc"][0, 0], 3, d),
+                                       cache["vn"][0, 0], 3), 0)
+    out = o.attend_prefill(q, cache, N, d=d, seed=0, bits_k=2, bits_v=3, Hkv=1)
+    np.testing.assert_allclose(out[0, :, 0], np.repeat(vhat[:1], 2, axis=0), atol=1e-14)
+    one = o.attend_prefill(q[:, :, 5:6], cache, N, d=d, seed=0, bits_k=2, bits_v=3, Hkv=1,
+                           scale=0.3)
+    dec = o.attend(q[:, :, 5], cache, N, d=d, seed=0, bits_k=2, bits_v=3, Hkv=1, scale=0.3)
+    np.testing.assert_allclose(one[:, :, 0], dec, atol=1e-13)
+
+
 def test_rotation_flattens_outliers():
     """P10 (outlier workload): rotation cuts max|z| and the 2-bit z-distortion."""
     w = si.WORKLOADS[3]
