@@ -32,7 +32,8 @@ EXPORTS = (
     "tq_bits_split", "tq_codebook", "tq_signs", "tq_cache_bytes", "tq_rht",
     "tq_encode_kv", "tq_qjl_sketch", "tq_num_splits", "tq_workspace_bytes",
     "tq_attend_decode", "tq_append_attend_decode", "tq_dense_workspace_bytes",
-    "tq_dense_decode_bf16", "tq_read_probe_sink_words", "tq_read_probe",
+    "tq_dense_decode_bf16", "tq_attend_prefill", "tq_read_probe_sink_words",
+    "tq_read_probe",
     "tq_strerror",
 )
 
@@ -85,6 +86,7 @@ def _lib():
                                             SZ, P]),
             "tq_dense_workspace_bytes": (I64, [I, I, I, I, I64, I]),
             "tq_dense_decode_bf16": (I, [P, P, P, I, I, I, I, I64, F, I, P, P, SZ, P]),
+            "tq_attend_prefill": (I, [CFG, P, I, I, I, I64, CACHE, I64, F, P, P]),
             "tq_read_probe_sink_words": (I64, [I64]),
             "tq_read_probe": (I, [P, I64, P, P]),
             "tq_strerror": (ctypes.c_char_p, [I]),
@@ -307,6 +309,21 @@ def tq_append_attend_decode(cfg: Config, k_new, v_new, q, cache: PackedCache, n_
         ctypes.byref(cfg.c()), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(q),
         _dtype_code(q), B, Hq, ctypes.byref(c), n_ctx, float(scale), splits, _ptr(out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)), "tq_append_attend_decode")
+
+
+def tq_attend_prefill(cfg: Config, q, cache: PackedCache, n_ctx: int, out, scale: float = 0.0,
+                      stream=None):
+    """Causal attention of the chunk q [B][Hq][n_q][d] (its tokens already at
+    cache positions n_ctx - n_q .. n_ctx - 1) over the packed cache; out is
+    [B][Hq][n_q][d] float32."""
+    if q.dim() != 4 or q.shape[0] != cache.B or q.shape[3] != cfg.d or not q.is_contiguous():
+        raise TqError(TQ_ERR_ARG, "tq_attend_prefill: q must be contiguous [B][Hq][n_q][d]")
+    if tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise TqError(TQ_ERR_ARG, "tq_attend_prefill: out must be contiguous, shaped like q")
+    c = cache.c()
+    _check(_lib().tq_attend_prefill(ctypes.byref(cfg.c()), _ptr(q), _dtype_code(q), q.shape[0],
+                                    q.shape[1], q.shape[2], ctypes.byref(c), n_ctx, scale,
+                                    _ptr(out), _stream(stream)), "tq_attend_prefill")
 
 
 def tq_read_probe(src, sink=None, stream=None):

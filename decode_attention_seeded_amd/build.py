@@ -46,6 +46,10 @@ def _jobs():
         jobs.append((f"tq_decode_d{d}_k{bk}.o",
                      [HIPCC, *HIP_FLAGS, f"-DTQ_D={d}", f"-DTQ_BK={bk}",
                       "-c", os.path.join(CSRC, "tq_inst_decode.hip")]))
+    for d in (128, 256):
+        jobs.append((f"tq_prefill_d{d}.o",
+                     [HIPCC, *HIP_FLAGS, f"-DTQ_D={d}",
+                      "-c", os.path.join(CSRC, "tq_inst_prefill.hip")]))
     for d, bk in ENCODE_VARIANTS:
         jobs.append((f"tq_encode_d{d}_k{bk}.o",
                      [HIPCC, *HIP_FLAGS, f"-DTQ_D={d}", f"-DTQ_BK={bk}",

@@ -5,6 +5,7 @@
 
 #include "tq_internal.h"
 #include "tq_kernels.h"
+#include "tq_prefill.h"
 
 namespace tq {
 
@@ -17,6 +18,9 @@ int launch_decode_d256_k2(int, int, int, int, const DecodeArgs&, dim3, hipStream
 int launch_decode_d256_k3(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
 int launch_decode_d256_k4(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
 int launch_decode_d256_k16(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
+
+int launch_prefill_d128(int, int, const PrefillArgs&, dim3, hipStream_t);
+int launch_prefill_d256(int, int, const PrefillArgs&, dim3, hipStream_t);
 
 using EncodeLauncher = int (*)(int, bool, const EncodeArgs&, hipStream_t);
 int launch_encode_d128_k2(int, bool, const EncodeArgs&, hipStream_t);
@@ -415,6 +419,55 @@ int tq_dense_decode_bf16(const void* q, const void* k, const void* v, int B, int
   da.capacity = n_ctx;
   da.n_ctx = n_ctx;
   return run_decode(d, 16, 16, 0, p, da, qa, B, Hq, Hkv, ws, out, 0, 0, stream);
+}
+
+int tq_attend_prefill(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
+                      int64_t n_q, const tq_cache* cache, int64_t n_ctx, float scale, float* out,
+                      hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  st = check_cache(cfg, cache);
+  if (st != TQ_OK) return st;
+  if (cfg->qjl) return TQ_ERR_UNSUPPORTED;
+  if (!valid_in_dtype(q_dtype)) return TQ_ERR_UNSUPPORTED;
+  if (B != cache->B || Hq < 1 || Hq % cache->Hkv != 0) return TQ_ERR_ARG;
+  if (!std::isfinite(scale)) return TQ_ERR_ARG;
+  if (n_q < 1 || n_ctx < n_q) return TQ_ERR_ARG;
+  if (n_ctx > cache->capacity) return TQ_ERR_CAPACITY;
+  const int G = Hq / cache->Hkv;
+  const int64_t tiles = (n_q * G + 63) / 64;
+  if (tiles > (int64_t(1) << 31) - 1 || int64_t(B) * cache->Hkv > 65535) return TQ_ERR_ARG;
+  if (B == 0) return TQ_OK;
+  if (!q || !out) return TQ_ERR_ARG;
+  if (!aligned16(q) || !aligned16(out)) return TQ_ERR_ALIGN;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+
+  const float tau = scale == 0.f ? 1.0f / std::sqrt(float(cfg->d)) : scale;
+  PrefillArgs a{};
+  a.kc = static_cast<const uint8_t*>(cache->kc);
+  a.vc = static_cast<const uint8_t*>(cache->vc);
+  a.kn = cache->kn;
+  a.vn = cache->vn;
+  a.q = q;
+  a.out = out;
+  a.capacity = cache->capacity;
+  a.n_ctx = n_ctx;
+  a.n_q = n_q;
+  a.Hkv = cache->Hkv;
+  a.Hq = Hq;
+  a.G = G;
+  a.q_dtype = q_dtype;
+  a.norm_f16 = cfg->norm_dtype == TQ_F16;
+  const double ak = fill_codebook_f32(cfg->bits_k, a.cbk);
+  const double av = fill_codebook_f32(cfg->bits_v, a.cbv);
+  a.kscale = float(1.0 / (std::sqrt(double(cfg->d)) * ak));
+  a.vscale = float(1.0 / (std::sqrt(double(cfg->d)) * av));
+  a.qmult = tau * dev::kLog2e;
+  sign_bitmap(cfg->seed, cfg->d, a.sbits);
+  const dim3 grid(unsigned(tiles), unsigned(int64_t(B) * cache->Hkv));
+  return cfg->d == 128 ? launch_prefill_d128(cfg->bits_k, cfg->bits_v, a, grid, stream)
+                       : launch_prefill_d256(cfg->bits_k, cfg->bits_v, a, grid, stream);
 }
 
 int64_t tq_read_probe_sink_words(int64_t bytes) {

@@ -219,6 +219,28 @@ int tq_append_attend_decode(const tq_config* cfg, const void* k_new,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Causal multi-query attention of a prefill chunk over the packed cache
+ * (the time-to-first-token path of the performance page's "Memory Benefits
+ * and Trade-offs"; the API page's patched attention, "Implementation
+ * Details: Cache Substitution", rotates the queries into the cache's frame).
+ * The chunk's n_q tokens must already be in the cache (tq_encode_kv at
+ * offset n_ctx - n_q); query i of the chunk sits at position
+ * n_ctx - n_q + i and attends to cache tokens 0 .. that position:
+ *   out[b][h][i] = sum_{j <= n_ctx-n_q+i} softmax_j(scale <q[b][h][i], k_hat_j>)
+ *                  v_hat_j,   KV head of h = h / (Hq / Hkv)
+ *   q   : [B][Hq][n_q][d] of q_dtype (device, 16-byte aligned)
+ *   out : [B][Hq][n_q][d] fp32 (device, caller-owned, 16-byte aligned)
+ *   scale: 0 selects 1/sqrt(d). No workspace.
+ * Errors (before any work is queued): TQ_ERR_ARG (1 <= n_q <= n_ctx
+ * violated, Hq not a multiple of Hkv, B != cache B, null pointers),
+ * TQ_ERR_CAPACITY (n_ctx > capacity), TQ_ERR_ALIGN, TQ_ERR_UNSUPPORTED (QJL
+ * formats: the correction term is not implemented on this path).
+ */
+int tq_attend_prefill(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
+                      int64_t n_q, const tq_cache* cache, int64_t n_ctx, float scale,
+                      float* out, hipStream_t stream);
+
+/*
  * Dense bf16 decode attention for comparison on the same GPU (not part of
  * the method): out = softmax(scale q K^T) V over k, v: [B][Hkv][n_ctx][d]
  * bf16, q: [B][Hq][d] bf16, out fp32. Same workspace rules

@@ -156,6 +156,14 @@ def queries(w: Workload, data_seed=DATA_SEED):
     return _round_input(x, w.in_dtype)
 
 
+def chunk_queries(w: Workload, n_q: int, data_seed=DATA_SEED):
+    """Queries of a prefill chunk, q [B][Hq][n_q][d] iid N(0,1) in the
+    workload's input dtype, as (raw, f32)."""
+    x = _gen(data_seed, w.wid, T_Q, 1, n_q, 0).standard_normal(
+        (w.B, w.Hq, n_q, w.d), dtype=np.float32)
+    return _round_input(x, w.in_dtype)
+
+
 def correlated_tokens(w: Workload, data_seed=DATA_SEED):
     """Token index j per (b, query head) for the correlated-query workload."""
     return _gen(data_seed, w.wid, T_QJ, 0, 0, 0).integers(0, w.N, size=(w.B, w.Hq))

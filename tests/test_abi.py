@@ -248,3 +248,26 @@ def test_read_probe_validation():
     assert lib.tq_read_probe_sink_words(16) == 4
     assert lib.tq_read_probe_sink_words(16 * 256 * 3) == 12
     assert lib.tq_read_probe_sink_words(1 << 40) == 4 * 16384
+
+
+def test_prefill_validation():
+    lib = tq.lib()
+
+    def call(cfg=None, q=A, qdt=tq.TQ_BF16, B=1, Hq=4, n_q=8, cache=None, n_ctx=16, out=A):
+        cfg = _cfg() if cfg is None else cfg
+        cache = _cache() if cache is None else cache
+        return lib.tq_attend_prefill(ctypes.byref(cfg), q, qdt, B, Hq, n_q, ctypes.byref(cache),
+                                     n_ctx, 0.0, out, None)
+
+    assert call(cfg=_cfg(qjl=1)) == tq.TQ_ERR_UNSUPPORTED
+    assert call(cfg=_cfg(d=64)) == tq.TQ_ERR_UNSUPPORTED
+    assert call(qdt=7) == tq.TQ_ERR_UNSUPPORTED
+    assert call(n_q=0) == tq.TQ_ERR_ARG
+    assert call(n_q=17) == tq.TQ_ERR_ARG                  # more queries than positions
+    assert call(Hq=3) == tq.TQ_ERR_ARG                    # not a multiple of Hkv
+    assert call(B=2) == tq.TQ_ERR_ARG                     # cache holds B = 1
+    assert call(n_ctx=65) == tq.TQ_ERR_CAPACITY
+    assert call(q=None) == tq.TQ_ERR_ARG
+    assert call(q=MIS) == tq.TQ_ERR_ALIGN
+    assert call(out=MIS) == tq.TQ_ERR_ALIGN
+    assert call(B=0, cache=_cache(B=0)) == tq.TQ_OK
