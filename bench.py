@@ -124,6 +124,7 @@ def main():
     ap.add_argument("--workload", type=int, default=4, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="context tokens of the CPU-oracle sample (0: the whole context "
                          "of one KV head)")
@@ -290,6 +291,34 @@ def main():
     log(f"single-token step: encode + decode {single['two_calls_us']} us, "
         f"fused {single['fused_us']} us")
 
+    # causal prefill of a chunk at the end of the context (the appended
+    # chunk, else the last 1024 tokens) over the packed cache, on the
+    # matrix cores; algorithmic flops = 4 d per (query row, visible token)
+    prefill = None
+    if not args.no_prefill and not w.qjl:
+        nq = A if A else min(1024, w.N)
+        qc_raw, _ = si.chunk_queries(w, nq)
+        qc = to_dev_bf16(torch, qc_raw) if w.in_dtype == "bf16" else \
+            torch.from_numpy(qc_raw).cuda()
+        pout = torch.empty((w.B, w.Hq, nq, w.d), dtype=torch.float32, device="cuda")
+        tq.tq_attend_prefill(cfg, qc, cache, w.N, pout)
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(3):
+            tq.tq_attend_prefill(cfg, qc, cache, w.N, pout)
+        b.record()
+        torch.cuda.synchronize()
+        pms = a.elapsed_time(b) / 3
+        visible = nq * (w.N - nq) + nq * (nq + 1) // 2
+        flops = 4 * w.d * w.B * w.Hq * visible
+        prefill = {"chunk_tokens": nq, "context": w.N, "ms": round(pms, 3),
+                   "tflops": round(flops / (pms * 1e-3) / 1e12, 1),
+                   "frac_of_fp16_dense_peak": round(flops / (pms * 1e-3) / 2.5e15, 4),
+                   "flops": flops}
+        del qc, pout
+        log(f"prefill of {nq} tokens over {w.N}: {pms:.2f} ms, {prefill['tflops']} TFLOP/s")
+
     # algorithmic bytes of one decode call: every packed plane over N tokens,
     # plus q in and out
     alg_bytes = alg_bytes_of(tq, cfg, w, q)
@@ -372,6 +401,7 @@ def main():
         "bulk_encode_ms": round(bulk_ms, 3),
         "algorithmic_bytes_per_decode": alg_bytes,
         "dense_bf16": dense,
+        "prefill": prefill,
         "source_hash": source_hash(),
     }
     print(json.dumps(rec), flush=True)

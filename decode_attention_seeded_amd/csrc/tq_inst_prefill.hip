@@ -16,7 +16,7 @@ namespace tq {
 
 template <int BK, int BV>
 static int go(const PrefillArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_prefill<TQ_D, BK, BV>), grid, dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_prefill<TQ_D, BK, BV>), grid, dim3(64 * pf_waves(TQ_D)), 0, st, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 

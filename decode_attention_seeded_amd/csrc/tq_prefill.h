@@ -5,23 +5,30 @@
 // chunk sits at position n_ctx - n_q + i and attends to tokens 0 .. that
 // position. With G query heads per KV head this is a dense contraction of
 // (n_q * G) query rows against the dequantized cache, so both products run
-// as v_mfma_f32_16x16x16_f16 on fp16 operands with fp32 accumulation.
+// as v_mfma_f32_16x16x32_f16 on fp16 operands with fp32 accumulation (lane
+// (kq, r) of an operand holds k-values 8kq .. 8kq + 7 of row/column r; the
+// output lane (kq, c) holds rows 4kq .. 4kq + 3 of column c).
 //
-// Workgroup: 4 waves, 64 query rows (row r = i * G + g of one KV head), wave
-// w owns rows 16w .. 16w + 15. Per 64-token tile:
-//   dequant  all 256 threads: thread (token t = tid / 4, part = tid % 4)
-//            decodes coordinates [part * d/4, (part + 1) * d/4) of token t's
-//            key (pair-table lookups, row-major fp16 tile) and value
-//            (transposed fp16 tile), and the per-token scales.
-//   scores   S^T = K_hat Q'^T per 16-token block: A = 4 coordinates of a
-//            key row (8-byte LDS read), B = the lane's query row quad (held
-//            in VGPRs). The output layout (lane (kq, col) holds tokens
-//            4kq .. 4kq + 3 of query row col) is exactly the A layout of
-//            P V_hat, so the weights never leave the registers.
+// Workgroup: W waves (8 at d = 128, 4 at d = 256), 16 W query rows (row
+// r = i * G + g of one KV head), wave w owns rows 16w .. 16w + 15. Per
+// 64-token tile, double-buffered in LDS so that the next tile's dequant
+// overlaps this tile's products (one barrier per tile):
+//   dequant  lane = token; a wave decodes one quarter of the coordinates
+//            of every token's key (pair-table lookups, row-major fp16 tile)
+//            or value (transposed fp16 tile, one row store per coordinate),
+//            and the per-token scales. With 8 waves, waves 0-3 take the
+//            keys and 4-7 the values; with 4, each wave both.
+//   scores   S^T = K_hat Q'^T per 16-token block: A = 8 coordinates of a key
+//            row (16-byte LDS read), B = the lane's query row (VGPRs). The
+//            output lane (kq, col) holds tokens 4kq .. 4kq + 3 of the block
+//            for query row col.
 //   softmax  online, in exp2 units, per query row over the 4 lanes that
 //            hold it; tokens past the row's position are masked.
-//   values   O += P V_hat: A = the lane's 4 weights (times the value norm),
-//            B = 4 tokens of one coordinate from the transposed tile.
+//   values   O += P V_hat per 32 tokens: the lane's 8 weights (times the
+//            value norm) of blocks 2b and 2b + 1 are the A operand as they
+//            are; the value tile stores its token columns in that order
+//            (token 32b + 16h + 4q + i at column 32b + 8q + 4h + i), so the
+//            B operand is one 16-byte read.
 // Epilogue: O / l, staged per row in LDS, rotated back (R^T) with 16 lanes
 // per row and stored as fp32.
 #pragma once
@@ -49,16 +56,22 @@ struct PrefillArgs {
   uint32_t sbits[8];      // rotation signs, bit i set when sign i is negative
 };
 
-typedef _Float16 pf_h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 pf_h8 __attribute__((ext_vector_type(8)));
 typedef float pf_f4 __attribute__((ext_vector_type(4)));
 
 constexpr int pf_max(int a, int b) { return a > b ? a : b; }
 
+constexpr int pf_waves(int d) { return d == 128 ? 8 : 4; }
+
 template <int D, int BK, int BV>
-__global__ void __launch_bounds__(256) k_prefill(PrefillArgs a) {
+__global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   static_assert(D == 128 || D == 256, "prefill: d 128 or 256");
+  constexpr int W = pf_waves(D);           // waves; 16 query rows each
+  constexpr int NR = 16 * W;               // query rows per workgroup
+  constexpr int NT = 64 * W;
   constexpr int TT = 64;                   // tokens per tile
-  constexpr int NS = D / 16;               // score k-steps = value coordinate tiles
+  constexpr int NS = D / 16;               // value coordinate tiles of 16
+  constexpr int NK = D / 32;               // score k-steps of 32 coordinates
   constexpr int KS = D + 8;                // key tile row stride (halves)
   constexpr int VS = TT + 8;               // transposed value tile row stride (halves)
   constexpr int CPT = D / 4;               // coordinates per dequant thread
@@ -69,16 +82,18 @@ __global__ void __launch_bounds__(256) k_prefill(PrefillArgs a) {
   constexpr int KE = 1 << (2 * BK);
   constexpr int VE = 1 << BV;
   constexpr int E = D / 16;                // row elements per lane (16 lanes per row)
-  constexpr int TILE_BYTES = TT * KS * 2 + D * VS * 2;
-  constexpr int SMEM = pf_max(TILE_BYTES, 64 * D * 4);
-  static_assert(64 * KS * 2 <= SMEM, "query staging fits");
+  constexpr int KT_BYTES = TT * KS * 2;
+  constexpr int TILE_BYTES = KT_BYTES + D * VS * 2;
+  constexpr int SMEM = pf_max(2 * TILE_BYTES, pf_max(NR * D * 4, NR * KS * 2));
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
-  __shared__ __attribute__((aligned(16))) float tks[TT];
-  __shared__ __attribute__((aligned(16))) float tnv[TT];
+  __shared__ __attribute__((aligned(16))) float tks[2][TT];
+  __shared__ __attribute__((aligned(16))) float tnv[2][TT];
   __shared__ uint32_t kpair[KE];
   __shared__ uint16_t vone[VE];
-  _Float16* ktile = reinterpret_cast<_Float16*>(smem);
-  _Float16* vtile = reinterpret_cast<_Float16*>(smem + TT * KS * 2);
+  auto ktile = [&](int buf) { return reinterpret_cast<_Float16*>(smem + buf * TILE_BYTES); };
+  auto vtile = [&](int buf) {
+    return reinterpret_cast<_Float16*>(smem + buf * TILE_BYTES + KT_BYTES);
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -89,13 +104,13 @@ __global__ void __launch_bounds__(256) k_prefill(PrefillArgs a) {
   const int b = unit / a.Hkv;
   const int kvh = unit - b * a.Hkv;
   const int64_t R = a.n_q * a.G;
-  const int64_t r0 = int64_t(blockIdx.x) * 64;
+  const int64_t r0 = int64_t(blockIdx.x) * NR;
   const int64_t rec0 = int64_t(unit) * a.capacity;
   const int64_t pos0 = a.n_ctx - a.n_q;
 
-  for (int e = tid; e < KE; e += 256)
+  for (int e = tid; e < KE; e += NT)
     kpair[e] = dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
-  for (int e = tid; e < VE; e += 256)
+  for (int e = tid; e < VE; e += NT)
     vone[e] = __builtin_bit_cast(uint16_t, _Float16(a.cbv[e]));
 
   // ---------------- the wave's 16 query rows: R q * scale * log2(e), fp16
@@ -124,48 +139,52 @@ __global__ void __launch_bounds__(256) k_prefill(PrefillArgs a) {
     }
   }
   __syncthreads();
-  pf_h4 qb[NS];
+  pf_h8 qb[NK];
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    qb[s] = *reinterpret_cast<const pf_h4*>(qst + (16 * wave + col) * KS + 16 * s + 4 * kq);
+  for (int s = 0; s < NK; ++s)
+    qb[s] = *reinterpret_cast<const pf_h8*>(qst + (16 * wave + col) * KS + 32 * s + 8 * kq);
 
   // the lane's query row (score layout) and its position
   const int64_t my_r = r0 + 16 * wave + col;
   const int64_t my_pos = my_r < R ? pos0 + my_r / a.G : -1;
-  const int64_t r_last = (r0 + 63 < R ? r0 + 63 : R - 1);
+  const int64_t r_last = (r0 + NR - 1 < R ? r0 + NR - 1 : R - 1);
   const int64_t p_max = pos0 + r_last / a.G;
   const int ntiles = int(p_max / TT) + 1;
 
-  // ---------------- dequant role: token t of the tile, coordinate part
-  const int dt = tid >> 2, dpart = tid & 3;
+  // ---------------- dequant role: lane = token of the tile, wave = quarter
+  // of the coordinates (of the keys, the values, or both)
+  const int dt = lane;
+  const int dpart = W == 8 ? (wave & 3) : wave;
+  const bool do_k = W == 4 || wave < 4;
+  const bool do_v = W == 4 || wave >= 4;     // wave-uniform
   uint32_t kw[KWD], vw[VWD];
   uint32_t knb = 0, vnb = 0;
   auto fetch = [&](int n) {
     const int64_t tok = int64_t(n) * TT + dt;
     const bool ok = tok < a.n_ctx;
-    const uint32_t* kp =
-        reinterpret_cast<const uint32_t*>(a.kc + (rec0 + tok) * KREC) + dpart * KWD;
-    const uint32_t* vp =
-        reinterpret_cast<const uint32_t*>(a.vc + (rec0 + tok) * VREC) + dpart * VWD;
 #pragma unroll
     for (int j = 0; j < KWD; ++j) kw[j] = 0u;
 #pragma unroll
     for (int j = 0; j < VWD; ++j) vw[j] = 0u;
     knb = vnb = 0u;
-    if (ok) {                            // rows past the context are never read
+    if (!ok) return;                     // rows past the context are never read
+    if (do_k) {
+      const uint32_t* kp =
+          reinterpret_cast<const uint32_t*>(a.kc + (rec0 + tok) * KREC) + dpart * KWD;
 #pragma unroll
       for (int j = 0; j < KWD; ++j) kw[j] = kp[j];
+      if (dpart == 0)
+        knb = a.norm_f16 ? uint32_t(static_cast<const uint16_t*>(a.kn)[rec0 + tok])
+                         : static_cast<const uint32_t*>(a.kn)[rec0 + tok];
+    }
+    if (do_v) {
+      const uint32_t* vp =
+          reinterpret_cast<const uint32_t*>(a.vc + (rec0 + tok) * VREC) + dpart * VWD;
 #pragma unroll
       for (int j = 0; j < VWD; ++j) vw[j] = vp[j];
-      if (dpart == 0) {
-        if (a.norm_f16) {
-          knb = static_cast<const uint16_t*>(a.kn)[rec0 + tok];
-          vnb = static_cast<const uint16_t*>(a.vn)[rec0 + tok];
-        } else {
-          knb = static_cast<const uint32_t*>(a.kn)[rec0 + tok];
-          vnb = static_cast<const uint32_t*>(a.vn)[rec0 + tok];
-        }
-      }
+      if (dpart == 0)
+        vnb = a.norm_f16 ? uint32_t(static_cast<const uint16_t*>(a.vn)[rec0 + tok])
+                         : static_cast<const uint32_t*>(a.vn)[rec0 + tok];
     }
   };
 
@@ -174,27 +193,45 @@ __global__ void __launch_bounds__(256) k_prefill(PrefillArgs a) {
 #pragma unroll
   for (int j = 0; j < NS; ++j) o[j] = pf_f4{0.f, 0.f, 0.f, 0.f};
 
-  fetch(0);
-  for (int n = 0; n < ntiles; ++n) {
-    __syncthreads();                    // the previous tile (or q staging) is consumed
-    {
+  // dequantized tile of the fetched words into LDS buffer `buf`
+  auto put = [&](int buf) {
+    if (do_k) {
       uint32_t pk[CPT / 2];
 #pragma unroll
       for (int c = 0; c < CPT / 2; ++c) pk[c] = kpair[dev::field<2 * BK>(kw, c)];
-      uint4* kd = reinterpret_cast<uint4*>(ktile + dt * KS + dpart * CPT);
+      uint4* kd = reinterpret_cast<uint4*>(ktile(buf) + dt * KS + dpart * CPT);
 #pragma unroll
       for (int c = 0; c < CPT / 8; ++c)
         kd[c] = make_uint4(pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]);
-      uint16_t* vt = reinterpret_cast<uint16_t*>(vtile);
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) vt[(dpart * CPT + c) * VS + dt] = vone[dev::field<BV>(vw, c)];
-      if (dpart == 0) {
-        tks[dt] = (a.norm_f16 ? dev::f16_to_f32(knb) : __uint_as_float(knb)) * a.kscale;
-        tnv[dt] = (a.norm_f16 ? dev::f16_to_f32(vnb) : __uint_as_float(vnb)) * a.vscale;
-      }
+      if (dpart == 0)
+        tks[buf][dt] = (a.norm_f16 ? dev::f16_to_f32(knb) : __uint_as_float(knb)) * a.kscale;
     }
-    if (n + 1 < ntiles) fetch(n + 1);
-    __syncthreads();
+    if (do_v) {
+      uint16_t* vt = reinterpret_cast<uint16_t*>(vtile(buf));
+      const int vcol = (dt & 32) | ((dt >> 2) & 3) << 3 | ((dt >> 4) & 1) << 2 | (dt & 3);
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+        vt[(dpart * CPT + c) * VS + vcol] = vone[dev::field<BV>(vw, c)];
+      if (dpart == 0)
+        tnv[buf][dt] = (a.norm_f16 ? dev::f16_to_f32(vnb) : __uint_as_float(vnb)) * a.vscale;
+    }
+  };
+
+  fetch(0);
+  __syncthreads();                      // every wave has its query rows: staging is free
+  put(0);
+  if (ntiles > 1) fetch(1);
+  __syncthreads();                      // tile 0 is in place
+  for (int n = 0; n < ntiles; ++n) {
+    const int buf = n & 1;
+    // the next tile goes to the other buffer, whose last readers finished
+    // before the barrier that ended the previous iteration
+    if (n + 1 < ntiles) {
+      put(buf ^ 1);
+      if (n + 2 < ntiles) fetch(n + 2);
+    }
+    const _Float16* kt = ktile(buf);
+    const _Float16* vtl = vtile(buf);
 
     // ---------------- scores S^T (tokens x rows), scaled and masked
     float sc[4][4];
@@ -203,12 +240,12 @@ __global__ void __launch_bounds__(256) k_prefill(PrefillArgs a) {
     for (int tb = 0; tb < 4; ++tb) {
       pf_f4 acc = pf_f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const pf_h4 ka =
-            *reinterpret_cast<const pf_h4*>(ktile + (16 * tb + col) * KS + 16 * s + 4 * kq);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(ka, qb[s], acc, 0, 0, 0);
+      for (int s = 0; s < NK; ++s) {
+        const pf_h8 ka =
+            *reinterpret_cast<const pf_h8*>(kt + (16 * tb + col) * KS + 32 * s + 8 * kq);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[s], acc, 0, 0, 0);
       }
-      const float4 ks = *reinterpret_cast<const float4*>(tks + 16 * tb + 4 * kq);
+      const float4 ks = *reinterpret_cast<const float4*>(&tks[buf][16 * tb + 4 * kq]);
       const float kss[4] = {ks.x, ks.y, ks.z, ks.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -222,17 +259,17 @@ __global__ void __launch_bounds__(256) k_prefill(PrefillArgs a) {
     const float m_new = fmaxf(m_run, mt);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
-    pf_h4 pa[4];
+    pf_h8 pa[2];
     float ls = 0.f;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      const float4 nv = *reinterpret_cast<const float4*>(tnv + 16 * tb + 4 * kq);
+      const float4 nv = *reinterpret_cast<const float4*>(&tnv[buf][16 * tb + 4 * kq]);
       const float nvs[4] = {nv.x, nv.y, nv.z, nv.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = __builtin_amdgcn_exp2f(sc[tb][i] - m_new);
         ls += p;
-        pa[tb][i] = _Float16(p * nvs[i]);
+        pa[tb >> 1][4 * (tb & 1) + i] = _Float16(p * nvs[i]);
       }
     }
     ls += __shfl_xor(ls, 16);
@@ -248,14 +285,15 @@ __global__ void __launch_bounds__(256) k_prefill(PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) o[j][i] *= al[i];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+    for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
-        const pf_h4 vb =
-            *reinterpret_cast<const pf_h4*>(vtile + (16 * j + col) * VS + 16 * tb + 4 * kq);
-        o[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[tb], vb, o[j], 0, 0, 0);
+        const pf_h8 vb =
+            *reinterpret_cast<const pf_h8*>(vtl + (16 * j + col) * VS + 32 * hb + 8 * kq);
+        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[hb], vb, o[j], 0, 0, 0);
       }
     }
+    __syncthreads();
   }
 
   // ---------------- O / l, then R^T per row, fp32 out
