@@ -435,7 +435,7 @@ int tq_attend_prefill(const tq_config* cfg, const void* q, int q_dtype, int B, i
   if (n_q < 1 || n_ctx < n_q) return TQ_ERR_ARG;
   if (n_ctx > cache->capacity) return TQ_ERR_CAPACITY;
   const int G = Hq / cache->Hkv;
-  const int64_t rows = 16 * pf_waves(cfg->d);
+  const int64_t rows = pf_rows(cfg->d);
   const int64_t tiles = (n_q * G + rows - 1) / rows;
   if (tiles > (int64_t(1) << 31) - 1 || int64_t(B) * cache->Hkv > 65535) return TQ_ERR_ARG;
   if (B == 0) return TQ_OK;

@@ -9,8 +9,11 @@
 // (kq, r) of an operand holds k-values 8kq .. 8kq + 7 of row/column r; the
 // output lane (kq, c) holds rows 4kq .. 4kq + 3 of column c).
 //
-// Workgroup: W waves (8 at d = 128, 4 at d = 256), 16 W query rows (row
-// r = i * G + g of one KV head), wave w owns rows 16w .. 16w + 15. Per
+// Workgroup: W waves (8 at d = 128, 4 at d = 256), each owning RB blocks of
+// 16 query rows (RB = 2 at d = 128, 1 at d = 256; row r = i * G + g of one
+// KV head; wave w owns rows 16 RB w .. 16 RB (w + 1) - 1), so every
+// dequantized tile serves 16 RB W rows and each operand read serves RB
+// blocks. Per
 // 64-token tile, double-buffered in LDS so that the next tile's dequant
 // overlaps this tile's products (one barrier per tile):
 //   dequant  lane = token; a wave decodes one quarter of the coordinates
@@ -62,12 +65,15 @@ typedef float pf_f4 __attribute__((ext_vector_type(4)));
 constexpr int pf_max(int a, int b) { return a > b ? a : b; }
 
 constexpr int pf_waves(int d) { return d == 128 ? 8 : 4; }
+constexpr int pf_row_blocks(int d) { return d == 128 ? 2 : 1; }
+constexpr int pf_rows(int d) { return 16 * pf_waves(d) * pf_row_blocks(d); }
 
 template <int D, int BK, int BV>
 __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   static_assert(D == 128 || D == 256, "prefill: d 128 or 256");
-  constexpr int W = pf_waves(D);           // waves; 16 query rows each
-  constexpr int NR = 16 * W;               // query rows per workgroup
+  constexpr int W = pf_waves(D);           // waves
+  constexpr int RB = pf_row_blocks(D);     // blocks of 16 query rows per wave
+  constexpr int NR = pf_rows(D);           // query rows per workgroup
   constexpr int NT = 64 * W;
   constexpr int TT = 64;                   // tokens per tile
   constexpr int NS = D / 16;               // value coordinate tiles of 16
@@ -120,8 +126,8 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
     const uint32_t smask = dev::bitmap_bits(a.sbits, l16 * E, E);
     const float mult = a.qmult / sqrtf(float(D));
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int m = 16 * wave + 4 * pass + (lane >> 4);
+    for (int pass = 0; pass < 4 * RB; ++pass) {
+      const int m = 16 * RB * wave + 4 * pass + (lane >> 4);
       const int64_t r = r0 + m;
       float v[E];
 #pragma unroll
@@ -139,14 +145,16 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
     }
   }
   __syncthreads();
-  pf_h8 qb[NK];
+  pf_h8 qb[RB][NK];
+  int64_t my_pos[RB];                   // the lane's query rows (score layout)
 #pragma unroll
-  for (int s = 0; s < NK; ++s)
-    qb[s] = *reinterpret_cast<const pf_h8*>(qst + (16 * wave + col) * KS + 32 * s + 8 * kq);
-
-  // the lane's query row (score layout) and its position
-  const int64_t my_r = r0 + 16 * wave + col;
-  const int64_t my_pos = my_r < R ? pos0 + my_r / a.G : -1;
+  for (int rb = 0; rb < RB; ++rb) {
+    const int m = 16 * (RB * wave + rb) + col;
+#pragma unroll
+    for (int s = 0; s < NK; ++s)
+      qb[rb][s] = *reinterpret_cast<const pf_h8*>(qst + m * KS + 32 * s + 8 * kq);
+    my_pos[rb] = r0 + m < R ? pos0 + (r0 + m) / a.G : -1;
+  }
   const int64_t r_last = (r0 + NR - 1 < R ? r0 + NR - 1 : R - 1);
   const int64_t p_max = pos0 + r_last / a.G;
   const int ntiles = int(p_max / TT) + 1;
@@ -188,10 +196,15 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
     }
   };
 
-  float m_run = -1e30f, l_run = 0.f;
-  pf_f4 o[NS];
+  float m_run[RB], l_run[RB];
+  pf_f4 o[RB][NS];
 #pragma unroll
-  for (int j = 0; j < NS; ++j) o[j] = pf_f4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -1e30f;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) o[rb][j] = pf_f4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // dequantized tile of the fetched words into LDS buffer `buf`
   auto put = [&](int buf) {
@@ -234,89 +247,117 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
     const _Float16* vtl = vtile(buf);
 
     // ---------------- scores S^T (tokens x rows), scaled and masked
-    float sc[4][4];
-    float mt = -INFINITY;
+    float sc[RB][4][4];
+    float mt[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) mt[rb] = -INFINITY;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      pf_f4 acc = pf_f4{0.f, 0.f, 0.f, 0.f};
+      pf_f4 acc[RB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = pf_f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
         const pf_h8 ka =
             *reinterpret_cast<const pf_h8*>(kt + (16 * tb + col) * KS + 32 * s + 8 * kq);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[s], acc, 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[rb][s], acc[rb], 0, 0, 0);
       }
       const float4 ks = *reinterpret_cast<const float4*>(&tks[buf][16 * tb + 4 * kq]);
       const float kss[4] = {ks.x, ks.y, ks.z, ks.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t tok = int64_t(n) * TT + 16 * tb + 4 * kq + i;
-        sc[tb][i] = tok <= my_pos ? acc[i] * kss[i] : -INFINITY;
-        mt = fmaxf(mt, sc[tb][i]);
-      }
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t tok = int64_t(n) * TT + 16 * tb + 4 * kq + i;
+          sc[rb][tb][i] = tok <= my_pos[rb] ? acc[rb][i] * kss[i] : -INFINITY;
+          mt[rb] = fmaxf(mt[rb], sc[rb][tb][i]);
+        }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    pf_h8 pa[2];
-    float ls = 0.f;
+    float alpha[RB];
+    pf_h8 pa[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      mt[rb] = fmaxf(mt[rb], __shfl_xor(mt[rb], 16));
+      mt[rb] = fmaxf(mt[rb], __shfl_xor(mt[rb], 32));
+      const float m_new = fmaxf(m_run[rb], mt[rb]);
+      alpha[rb] = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+      m_run[rb] = m_new;
+    }
+    float ls[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) ls[rb] = 0.f;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const float4 nv = *reinterpret_cast<const float4*>(&tnv[buf][16 * tb + 4 * kq]);
       const float nvs[4] = {nv.x, nv.y, nv.z, nv.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sc[tb][i] - m_new);
-        ls += p;
-        pa[tb >> 1][4 * (tb & 1) + i] = _Float16(p * nvs[i]);
-      }
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(sc[rb][tb][i] - m_run[rb]);
+          ls[rb] += p;
+          pa[rb][tb >> 1][4 * (tb & 1) + i] = _Float16(p * nvs[i]);
+        }
     }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
-    l_run = l_run * alpha + ls;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      ls[rb] += __shfl_xor(ls[rb], 16);
+      ls[rb] += __shfl_xor(ls[rb], 32);
+      l_run[rb] = l_run[rb] * alpha[rb] + ls[rb];
+    }
 
-    // ---------------- O = O * alpha + P V_hat (rows 4kq + i of the wave)
-    float al[4];
+    // ---------------- O = O * alpha + P V_hat (rows 4kq + i of each block)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kq + i);
+    for (int rb = 0; rb < RB; ++rb) {
+      float al[4];
 #pragma unroll
-    for (int j = 0; j < NS; ++j)
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha[rb], 4 * kq + i);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[j][i] *= al[i];
+      for (int j = 0; j < NS; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[rb][j][i] *= al[i];
+    }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
       for (int j = 0; j < NS; ++j) {
         const pf_h8 vb =
             *reinterpret_cast<const pf_h8*>(vtl + (16 * j + col) * VS + 32 * hb + 8 * kq);
-        o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[hb], vb, o[j], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          o[rb][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[rb][hb], vb, o[rb][j], 0, 0, 0);
       }
     }
     __syncthreads();
   }
 
   // ---------------- O / l, then R^T per row, fp32 out
-  float il[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float l = __shfl(l_run, 4 * kq + i);
-    il[i] = l > 0.f ? 1.f / l : 0.f;
-  }
   __syncthreads();                      // the tiles are dead: stage rows there
   float* ost = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int j = 0; j < NS; ++j)
+  for (int rb = 0; rb < RB; ++rb) {
+    float il[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ost[(16 * wave + 4 * kq + i) * D + 16 * j + col] = o[j][i] * il[i];
+    for (int i = 0; i < 4; ++i) {
+      const float l = __shfl(l_run[rb], 4 * kq + i);
+      il[i] = l > 0.f ? 1.f / l : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < NS; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ost[(16 * (RB * wave + rb) + 4 * kq + i) * D + 16 * j + col] = o[rb][j][i] * il[i];
+  }
   __syncthreads();
   {
     const int l16 = lane & 15;
     const uint32_t smask = dev::bitmap_bits(a.sbits, l16 * E, E);
     const float nn = 1.0f / sqrtf(float(D));
 #pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int m = 16 * wave + 4 * pass + (lane >> 4);
+    for (int pass = 0; pass < 4 * RB; ++pass) {
+      const int m = 16 * RB * wave + 4 * pass + (lane >> 4);
       const int64_t r = r0 + m;
       float v[E];
 #pragma unroll
