@@ -220,9 +220,9 @@ int tq_append_attend_decode(const tq_config* cfg, const void* k_new,
 
 /*
  * Causal multi-query attention of a prefill chunk over the packed cache
- * (the time-to-first-token path of the performance page's "Memory Benefits
- * and Trade-offs"; the API page's patched attention, "Implementation
- * Details: Cache Substitution", rotates the queries into the cache's frame).
+ * (the time-to-first-token path the README times in "Throughput, latency &
+ * memory"; the API page's patched attention, "Implementation Details: Cache
+ * Substitution", rotates the queries into the cache's frame).
  * The chunk's n_q tokens must already be in the cache (tq_encode_kv at
  * offset n_ctx - n_q); query i of the chunk sits at position
  * n_ctx - n_q + i and attends to cache tokens 0 .. that position:
