@@ -55,7 +55,7 @@ __all__ = [
     "attend", "attend_dense", "attend_rotated_blocked", "QJL_CONST",
     "turboquant_enabled", "bits_split", "tq_bytes_per_token",
     "affine_bytes_per_token", "fp16_bytes_per_token", "boundary_mask",
-    "qjl_boundary_mask", "merge_partials", "attend_prefill",
+    "qjl_boundary_mask", "merge_partials", "attend_prefill", "sphere_density",
 ]
 
 MASK64 = (1 << 64) - 1
@@ -166,14 +166,62 @@ def _cell_mean(a: float, b: float) -> float:
     return (_phi(a) - _phi(b)) / (_upper_tail(a) - _upper_tail(b))
 
 
-def lloyd_max(bits: int):
+def lloyd_max(bits: int, sphere_d: int | None = None):
     """Centroids (ascending, 2^bits) and thresholds (2^bits - 1) in float64.
 
     Lloyd iteration on the positive half-line, then mirrored, so the codebook
     is exactly antisymmetric and the middle threshold is exactly 0.
+    sphere_d=None: the quantizer of N(0,1), the near-Gaussian marginal the
+    pages name. sphere_d=d: the quantizer of the exact finite-d marginal of
+    z = sqrt(d) u, u one coordinate of a uniformly random unit vector in R^d
+    (density proportional to (1 - z^2/d)^((d-3)/2) on |z| < sqrt(d)); the
+    roadmap variant for small head dimensions.
     """
-    c, t = _lloyd_max_cached(bits)
+    c, t = _lloyd_max_cached(bits) if sphere_d is None else _sphere_lloyd_cached(bits, sphere_d)
     return np.array(c), np.array(t)
+
+
+def sphere_density(z, d: int):
+    """Unnormalized density of z = sqrt(d) u for u a coordinate of a uniform
+    unit vector in R^d: (1 - z^2/d)^((d-3)/2) on |z| < sqrt(d)."""
+    z = np.asarray(z, dtype=np.float64)
+    inside = np.abs(z) < math.sqrt(d)
+    return np.where(inside, np.clip(1.0 - z * z / d, 0.0, None) ** ((d - 3) / 2.0), 0.0)
+
+
+@functools.lru_cache(maxsize=None)
+def _sphere_lloyd_cached(bits: int, d: int, tol: float = 1e-13, max_iter: int = 100000):
+    import scipy.integrate
+    if bits < 1 or d < 4:
+        raise ValueError("bits >= 1 and d >= 4")
+    m = 1 << (bits - 1)
+    k = (d - 3) / 2.0
+    zmax = math.sqrt(d)
+
+    def base(z):
+        return max(0.0, 1.0 - z * z / d)   # 0 at the end point sqrt(d)
+
+    def mass(a, b):
+        return scipy.integrate.quad(lambda z: base(z) ** k, a, b,
+                                    epsabs=1e-300, epsrel=1e-13, limit=400)[0]
+
+    def first(a, b):
+        # integral of z (1 - z^2/d)^k, in closed form
+        return d / (2.0 * (k + 1.0)) * (base(a) ** (k + 1.0) - base(b) ** (k + 1.0))
+
+    c = [min(v, 0.9 * zmax) for v in _lloyd_max_cached(bits)[0][m:]]
+    for _ in range(max_iter):
+        edges = [0.0] + [(c[i - 1] + c[i]) / 2.0 for i in range(1, m)] + [zmax]
+        new = [first(edges[i], edges[i + 1]) / mass(edges[i], edges[i + 1]) for i in range(m)]
+        delta = max(abs(u - v) for u, v in zip(new, c))
+        c = new
+        if delta < tol:
+            break
+    pos = list(c)
+    inner = [(pos[i - 1] + pos[i]) / 2.0 for i in range(1, m)]
+    centroids = [-v for v in reversed(pos)] + pos
+    thresholds = [-v for v in reversed(inner)] + [0.0] + inner
+    return tuple(centroids), tuple(thresholds)
 
 
 @functools.lru_cache(maxsize=None)
@@ -269,7 +317,7 @@ def norm_ambiguous(n: np.ndarray, norm_dtype: str, rel: float = 1e-6):
 # Encode (performance page "What Is TurboQuant?": rotation then MSE codebook).
 # ---------------------------------------------------------------------------
 
-def encode_vectors(x: np.ndarray, seed: int, bits: int, norm_dtype: str):
+def encode_vectors(x: np.ndarray, seed: int, bits: int, norm_dtype: str, sphere: bool = False):
     """Encode rows x[..., d].
 
     Returns dict with codes (uint8, ascending-codebook indices), norm (rounded,
@@ -278,7 +326,7 @@ def encode_vectors(x: np.ndarray, seed: int, bits: int, norm_dtype: str):
     """
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
-    _, thr = lloyd_max(bits)
+    _, thr = lloyd_max(bits, x.shape[-1] if sphere else None)
     n = np.sqrt((x * x).sum(axis=-1))
     y = rht(x, seed)
     safe = np.where(n > 0, n, 1.0)
@@ -292,9 +340,10 @@ def encode_vectors(x: np.ndarray, seed: int, bits: int, norm_dtype: str):
     }
 
 
-def dequant_rot(codes: np.ndarray, norm: np.ndarray, bits: int) -> np.ndarray:
+def dequant_rot(codes: np.ndarray, norm: np.ndarray, bits: int,
+                sphere: bool = False) -> np.ndarray:
     """x_hat in the rotated frame: norm * c[code] / sqrt(d)."""
-    c, _ = lloyd_max(bits)
+    c, _ = lloyd_max(bits, np.shape(codes)[-1] if sphere else None)
     codes = np.asarray(codes)
     d = codes.shape[-1]
     return np.asarray(norm, dtype=np.float64)[..., None] * c[codes] / math.sqrt(d)
@@ -360,12 +409,12 @@ def qjl_boundary_mask(w: np.ndarray, rnorm_exact: np.ndarray, rel: float = 1e-6)
     return np.abs(w) < rel * np.asarray(rnorm_exact)[..., None]
 
 
-def qjl_from_encoding(enc: dict, bits: int, qjl_seed: int):
+def qjl_from_encoding(enc: dict, bits: int, qjl_seed: int, sphere: bool = False):
     """Residual of an encoded key in the rotated frame, then its sketch.
 
     r = R k - k_hat_rot with k_hat_rot built from the STORED (rounded) norm.
     """
-    r = enc["y"] - dequant_rot(enc["codes"], enc["norm"], bits)
+    r = enc["y"] - dequant_rot(enc["codes"], enc["norm"], bits, sphere)
     out = qjl_sketch(r, qjl_seed)
     out["r"] = r
     return out
@@ -375,10 +424,12 @@ def qjl_from_encoding(enc: dict, bits: int, qjl_seed: int):
 # Whole-cache encode: planes laid out [B][Hkv][n][bytes].
 # ---------------------------------------------------------------------------
 
-def encode_kv(k, v, *, seed, bits_k, bits_v, norm_dtype, qjl=False, qjl_seed=None):
-    """Encode K and V rows [B][Hkv][n][d] into packed planes (numpy arrays)."""
-    ek = encode_vectors(k, seed, bits_k, norm_dtype)
-    ev = encode_vectors(v, seed, bits_v, norm_dtype)
+def encode_kv(k, v, *, seed, bits_k, bits_v, norm_dtype, qjl=False, qjl_seed=None,
+              sphere=False):
+    """Encode K and V rows [B][Hkv][n][d] into packed planes (numpy arrays).
+    sphere: use the finite-d marginal codebook (lloyd_max(bits, d))."""
+    ek = encode_vectors(k, seed, bits_k, norm_dtype, sphere)
+    ev = encode_vectors(v, seed, bits_v, norm_dtype, sphere)
     out = {
         "kc": pack_codes(ek["codes"], bits_k),
         "vc": pack_codes(ev["codes"], bits_v),
@@ -386,7 +437,7 @@ def encode_kv(k, v, *, seed, bits_k, bits_v, norm_dtype, qjl=False, qjl_seed=Non
         "k_enc": ek, "v_enc": ev,
     }
     if qjl:
-        sk = qjl_from_encoding(ek, bits_k, seed + 1 if qjl_seed is None else qjl_seed)
+        sk = qjl_from_encoding(ek, bits_k, seed + 1 if qjl_seed is None else qjl_seed, sphere)
         out["kq"] = sk["packed"]
         out["kr"] = sk["rnorm"]
         out["k_qjl"] = sk
@@ -399,9 +450,9 @@ def encode_kv(k, v, *, seed, bits_k, bits_v, norm_dtype, qjl=False, qjl_seed=Non
 # in": the query is rotated, and the QJL correction is added to the score).
 # ---------------------------------------------------------------------------
 
-def _scores_rot(qr, kcodes, knorm, bits_k, tau, qjl=None):
+def _scores_rot(qr, kcodes, knorm, bits_k, tau, qjl=None, sphere=False):
     """tau * <R q, k_hat_rot> (+ QJL term), qr = R q [Hg][d] -> [Hg][n]."""
-    khat = dequant_rot(kcodes, knorm, bits_k)            # [n][d]
+    khat = dequant_rot(kcodes, knorm, bits_k, sphere)    # [n][d]
     s = qr @ khat.T
     if qjl is not None:
         qq, sigma, rnorm = qjl                           # qq = R2 R q [Hg][d]
@@ -411,7 +462,7 @@ def _scores_rot(qr, kcodes, knorm, bits_k, tau, qjl=None):
 
 
 def attend_dense(q, cache, *, d, seed, bits_k, bits_v, Hkv, scale=None,
-                 qjl=False, qjl_seed=None):
+                 qjl=False, qjl_seed=None, sphere=False):
     """Dense mode: dequantize K and V to the original frame, then
     softmax(q K_hat^T tau [+ QJL]) V_hat in float64.
 
@@ -428,8 +479,8 @@ def attend_dense(q, cache, *, d, seed, bits_k, bits_v, Hkv, scale=None,
         for g in range(Hkv):
             kc = unpack_codes(cache["kc"][b, g], bits_k, d)
             vc = unpack_codes(cache["vc"][b, g], bits_v, d)
-            k_hat = rht_inverse(dequant_rot(kc, cache["kn"][b, g], bits_k), seed)
-            v_hat = rht_inverse(dequant_rot(vc, cache["vn"][b, g], bits_v), seed)
+            k_hat = rht_inverse(dequant_rot(kc, cache["kn"][b, g], bits_k, sphere), seed)
+            v_hat = rht_inverse(dequant_rot(vc, cache["vn"][b, g], bits_v, sphere), seed)
             qh = q[b, g * G:(g + 1) * G]                 # [G][d]
             logits = tau * (qh @ k_hat.T)
             if qjl:
@@ -454,7 +505,7 @@ def merge_partials(ms, ls, accs):
 
 def attend_rotated_blocked(q, kv_block_fn, n_ctx, *, B, Hq, Hkv, d, seed,
                            bits_k, bits_v, scale=None, qjl=False,
-                           qjl_seed=None, block=65536, heads=None):
+                           qjl_seed=None, block=65536, heads=None, sphere=False):
     """Rotated-frame mode for long contexts.
 
     kv_block_fn(b, g, t0, t1) returns a dict with unpacked arrays for tokens
@@ -482,10 +533,10 @@ def attend_rotated_blocked(q, kv_block_fn, n_ctx, *, B, Hq, Hkv, d, seed,
             qj = None
             if qjl:
                 qj = (qq, 1.0 - 2.0 * blk["ksig"].astype(np.float64), blk["kr"])
-            lg = _scores_rot(qr, blk["kcodes"], blk["kn"], bits_k, tau, qj)
+            lg = _scores_rot(qr, blk["kcodes"], blk["kn"], bits_k, tau, qj, sphere)
             m = lg.max(axis=1)
             p = np.exp(lg - m[:, None])
-            vhat = dequant_rot(blk["vcodes"], blk["vn"], bits_v)
+            vhat = dequant_rot(blk["vcodes"], blk["vn"], bits_v, sphere)
             ms.append(m)
             ls.append(p.sum(axis=1))
             accs.append(p @ vhat)
@@ -497,7 +548,7 @@ def attend_rotated_blocked(q, kv_block_fn, n_ctx, *, B, Hq, Hkv, d, seed,
 
 
 def attend(q, cache, n_ctx, *, d, seed, bits_k, bits_v, Hkv, scale=None,
-           qjl=False, qjl_seed=None, block=65536):
+           qjl=False, qjl_seed=None, block=65536, sphere=False):
     """Rotated-blocked attention over an in-memory cache (first n_ctx tokens)."""
     q = np.asarray(q, dtype=np.float64)
     B, Hq, _ = q.shape
@@ -517,11 +568,11 @@ def attend(q, cache, n_ctx, *, d, seed, bits_k, bits_v, Hkv, scale=None,
     return attend_rotated_blocked(q, fn, n_ctx, B=B, Hq=Hq, Hkv=Hkv, d=d,
                                   seed=seed, bits_k=bits_k, bits_v=bits_v,
                                   scale=scale, qjl=qjl, qjl_seed=qjl_seed,
-                                  block=block)
+                                  block=block, sphere=sphere)
 
 
 def attend_prefill(q, cache, n_ctx, *, d, seed, bits_k, bits_v, Hkv, scale=None,
-                   qjl=False, qjl_seed=None):
+                   qjl=False, qjl_seed=None, sphere=False):
     """Causal multi-query attention of a prefill chunk over the packed cache.
 
     The chunk's n_q tokens are the last n_q of the first n_ctx cache rows
@@ -545,8 +596,8 @@ def attend_prefill(q, cache, n_ctx, *, d, seed, bits_k, bits_v, Hkv, scale=None,
         for g in range(Hkv):
             kc = unpack_codes(cache["kc"][b, g, :n_ctx], bits_k, d)
             vc = unpack_codes(cache["vc"][b, g, :n_ctx], bits_v, d)
-            k_hat = rht_inverse(dequant_rot(kc, cache["kn"][b, g, :n_ctx], bits_k), seed)
-            v_hat = rht_inverse(dequant_rot(vc, cache["vn"][b, g, :n_ctx], bits_v), seed)
+            k_hat = rht_inverse(dequant_rot(kc, cache["kn"][b, g, :n_ctx], bits_k, sphere), seed)
+            v_hat = rht_inverse(dequant_rot(vc, cache["vn"][b, g, :n_ctx], bits_v, sphere), seed)
             if qjl:
                 sigma = 1.0 - 2.0 * unpack_signs(cache["kq"][b, g, :n_ctx], d)
             for h in range(g * G, (g + 1) * G):

@@ -425,6 +425,54 @@ def test_prefill_special_cases():
     np.testing.assert_allclose(one[:, :, 0], dec, atol=1e-13)
 
 
+@pytest.mark.parametrize("d", [16, 128, 256])
+def test_sphere_density_has_unit_variance(d):
+    """z = sqrt(d) u for u a coordinate of a uniform unit vector: E[z^2] =
+    d E[u^2] = 1 exactly, which fixes the exponent (d-3)/2 of the density."""
+    r = math.sqrt(d)
+    z0 = scipy.integrate.quad(lambda z: o.sphere_density(z, d), -r, r, epsabs=1e-14)[0]
+    z2 = scipy.integrate.quad(lambda z: z * z * o.sphere_density(z, d), -r, r, epsabs=1e-14)[0]
+    assert abs(z2 / z0 - 1.0) < 1e-10
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d", [128, 256])
+def test_sphere_codebook_lloyd_max_conditions(bits, d):
+    """Centroid condition by quadrature of the density itself (not the
+    closed-form first moment the iteration uses), midpoint condition,
+    antisymmetry, zero middle threshold."""
+    c, t = o.lloyd_max(bits, d)
+    L = 1 << bits
+    assert len(c) == L and len(t) == L - 1
+    np.testing.assert_allclose(c, -c[::-1], atol=0)
+    assert t[L // 2 - 1] == 0.0
+    np.testing.assert_allclose(t, (c[:-1] + c[1:]) / 2, atol=1e-15)
+    edges = [-math.sqrt(d)] + list(t) + [math.sqrt(d)]
+    for k in range(L):
+        a, b = edges[k], edges[k + 1]
+        m0 = scipy.integrate.quad(lambda z: o.sphere_density(z, d), a, b, epsabs=1e-14)[0]
+        m1 = scipy.integrate.quad(lambda z: z * o.sphere_density(z, d), a, b, epsabs=1e-14)[0]
+        assert abs(m1 / m0 - c[k]) < 1e-9
+
+
+def test_sphere_codebook_limits_and_optimality():
+    """Large d gives the N(0,1) codebook; on samples of the exact marginal
+    (first coordinate of a uniform unit vector, drawn as g0 / sqrt(g0^2 +
+    chi2_{d-1})) the finite-d codebook has the lower distortion."""
+    # the finite-d correction shrinks like 1/d (4-bit: 0.044 at d 128)
+    for bits in (2, 3, 4):
+        np.testing.assert_allclose(o.lloyd_max(bits, 4096)[0], o.lloyd_max(bits)[0],
+                                   atol=2e-3)
+    d, n = 128, 4_000_000
+    rng = np.random.default_rng(0)
+    g0 = rng.standard_normal(n)
+    z = math.sqrt(d) * g0 / np.sqrt(g0 * g0 + rng.chisquare(d - 1, n))
+    cs, ts = o.lloyd_max(4, d)
+    cg, tg = o.lloyd_max(4)
+    diff = (z - cg[o.quantize(z, tg)]) ** 2 - (z - cs[o.quantize(z, ts)]) ** 2
+    assert diff.mean() > 3 * diff.std() / math.sqrt(n)
+
+
 def test_rotation_flattens_outliers():
     """P10 (outlier workload): rotation cuts max|z| and the 2-bit z-distortion."""
     w = si.WORKLOADS[3]
