@@ -11,7 +11,8 @@ from .binding import (  # noqa: F401
     TQ_ERR_HIP, TQ_ERR_NO_DEVICE, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_F16,
     TQ_F32, TQ_OK, Config, PackedCache, TqError, lib, tq_append_attend_decode,
     tq_attend_decode, tq_attend_prefill,
-    tq_bits_split, tq_cache_bytes, tq_codebook, tq_config, tq_cache,
+    tq_bits_split, tq_cache_bytes, tq_codebook, tq_codebook_ex, tq_config, tq_cache,
+    TQ_CODEBOOK_GAUSS, TQ_CODEBOOK_SPHERE,
     tq_dense_decode_bf16, tq_dense_workspace_bytes, tq_encode_kv, tq_num_splits,
     tq_qjl_sketch, tq_read_probe, tq_rht, tq_signs, tq_strerror, tq_workspace_bytes,
     workspace,

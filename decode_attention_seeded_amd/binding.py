@@ -26,10 +26,11 @@ TQ_ERR_NO_DEVICE = -6
 TQ_ERR_HIP = -7
 
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
+TQ_CODEBOOK_GAUSS, TQ_CODEBOOK_SPHERE = 0, 1
 
 # every symbol include/tq.h declares
 EXPORTS = (
-    "tq_bits_split", "tq_codebook", "tq_signs", "tq_cache_bytes", "tq_rht",
+    "tq_bits_split", "tq_codebook", "tq_codebook_ex", "tq_signs", "tq_cache_bytes", "tq_rht",
     "tq_encode_kv", "tq_qjl_sketch", "tq_num_splits", "tq_workspace_bytes",
     "tq_attend_decode", "tq_append_attend_decode", "tq_dense_workspace_bytes",
     "tq_dense_decode_bf16", "tq_attend_prefill", "tq_read_probe_sink_words",
@@ -47,7 +48,8 @@ class TqError(RuntimeError):
 class tq_config(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int), ("bits_k", ctypes.c_int), ("bits_v", ctypes.c_int),
                 ("norm_dtype", ctypes.c_int), ("qjl", ctypes.c_int),
-                ("seed", ctypes.c_uint64), ("qjl_seed", ctypes.c_uint64)]
+                ("seed", ctypes.c_uint64), ("qjl_seed", ctypes.c_uint64),
+                ("codebook", ctypes.c_int)]
 
 
 class tq_cache(ctypes.Structure):
@@ -74,6 +76,7 @@ def _lib():
         sig = {
             "tq_bits_split": (I, [D, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)]),
             "tq_codebook": (I, [I, P, P]),
+            "tq_codebook_ex": (I, [I, I, I, P, P]),
             "tq_signs": (I, [U64, I, P]),
             "tq_cache_bytes": (I64, [CFG, I, I, I64, P]),
             "tq_rht": (I, [P, I, P, I64, I, U64, I, P]),
@@ -123,11 +126,13 @@ class Config:
     qjl: bool = False
     seed: int = 0
     qjl_seed: int = 1
+    codebook: str = "gauss"       # "gauss" | "sphere" (exact finite-d marginal)
 
     def c(self) -> tq_config:
         return tq_config(self.d, self.bits_k, self.bits_v,
                          TQ_F16 if self.norm_dtype == "f16" else TQ_F32,
-                         int(self.qjl), self.seed, self.qjl_seed)
+                         int(self.qjl), self.seed, self.qjl_seed,
+                         TQ_CODEBOOK_SPHERE if self.codebook == "sphere" else TQ_CODEBOOK_GAUSS)
 
 
 def _dtype_code(t):
@@ -171,6 +176,18 @@ def tq_codebook(bits: int):
     t = (ctypes.c_double * max(L - 1, 1))()
     _check(_lib().tq_codebook(bits, ctypes.cast(c, ctypes.c_void_p),
                               ctypes.cast(t, ctypes.c_void_p)), "tq_codebook")
+    return list(c), list(t)[:L - 1]
+
+
+def tq_codebook_ex(bits: int, kind: str = "gauss", d: int = 128):
+    """The codebook a config selects ("gauss" or "sphere" at head dim d), as
+    (centroids, thresholds) Python float lists."""
+    L = 1 << bits
+    c = (ctypes.c_double * L)()
+    t = (ctypes.c_double * max(L - 1, 1))()
+    k = TQ_CODEBOOK_SPHERE if kind == "sphere" else TQ_CODEBOOK_GAUSS
+    _check(_lib().tq_codebook_ex(bits, k, d, ctypes.cast(c, ctypes.c_void_p),
+                                 ctypes.cast(t, ctypes.c_void_p)), "tq_codebook_ex")
     return list(c), list(t)[:L - 1]
 
 

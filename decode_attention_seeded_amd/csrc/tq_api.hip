@@ -81,22 +81,22 @@ void sign_bitmap(uint64_t seed, int d, uint32_t (&w)[8]) {
 }
 
 // t_{L/2} .. t_{L-2}: the positive thresholds of the antisymmetric codebook.
-void fill_positive_thresholds(int bits, double* tpos) {
-  const Codebook& cb = codebook(bits);
+void fill_positive_thresholds(const tq_config* cfg, int bits, double* tpos) {
+  const Codebook& cb = codebook(bits, cfg->codebook, cfg->d);
   const int H = 1 << (bits - 1);
   for (int j = 0; j < 7; ++j) tpos[j] = j < H - 1 ? cb.t[H + j] : INFINITY;
 }
 
-void fill_codebook_f64(int bits, double* thr, double* cen) {
-  const Codebook& cb = codebook(bits);
+void fill_codebook_f64(const tq_config* cfg, int bits, double* thr, double* cen) {
+  const Codebook& cb = codebook(bits, cfg->codebook, cfg->d);
   const int L = 1 << bits;
   for (int k = 0; k < 15; ++k) thr[k] = k < L - 1 ? cb.t[k] : INFINITY;
   for (int k = 0; k < 16; ++k) cen[k] = k < L ? cb.c[k] : 0.0;
 }
 
 // alpha * centroids for the fp16 decode tables; returns alpha.
-double fill_codebook_f32(int bits, float* cen) {
-  const Codebook& cb = codebook(bits);
+double fill_codebook_f32(const tq_config* cfg, int bits, float* cen) {
+  const Codebook& cb = codebook(bits, cfg->codebook, cfg->d);
   const int L = 1 << bits;
   for (int k = 0; k < 16; ++k) cen[k] = k < L ? float(cb.alpha * cb.c[k]) : 0.f;
   return cb.alpha;
@@ -140,10 +140,10 @@ void fill_encode_args(const tq_config* cfg, const void* k, const void* v, int in
   a->norm_f16 = cfg->norm_dtype == TQ_F16;
   sign_bitmap(cfg->seed, cfg->d, a->sbits);
   sign_bitmap(cfg->qjl_seed, cfg->d, a->qsbits);
-  fill_positive_thresholds(cfg->bits_k, a->tpos[0]);
-  fill_positive_thresholds(cfg->bits_v, a->tpos[1]);
+  fill_positive_thresholds(cfg, cfg->bits_k, a->tpos[0]);
+  fill_positive_thresholds(cfg, cfg->bits_v, a->tpos[1]);
   double thr_unused[15];
-  fill_codebook_f64(cfg->bits_k, thr_unused, a->cen_k);
+  fill_codebook_f64(cfg, cfg->bits_k, thr_unused, a->cen_k);
 }
 
 // Shared tail of the packed and dense decode paths: q preparation, split-K
@@ -250,8 +250,8 @@ int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
     da.sbits[k] = qa.sbits[k];
     da.qsbits[k] = qa.qsbits[k];
   }
-  const double ak = fill_codebook_f32(cfg->bits_k, da.cbk);
-  const double av = fill_codebook_f32(cfg->bits_v, da.cbv);
+  const double ak = fill_codebook_f32(cfg, cfg->bits_k, da.cbk);
+  const double av = fill_codebook_f32(cfg, cfg->bits_v, da.cbv);
   da.kscale = float(1.0 / (std::sqrt(double(cfg->d)) * ak));
   da.vscale = float(1.0 / (std::sqrt(double(cfg->d)) * av));
   if (app) {
@@ -460,8 +460,8 @@ int tq_attend_prefill(const tq_config* cfg, const void* q, int q_dtype, int B, i
   a.G = G;
   a.q_dtype = q_dtype;
   a.norm_f16 = cfg->norm_dtype == TQ_F16;
-  const double ak = fill_codebook_f32(cfg->bits_k, a.cbk);
-  const double av = fill_codebook_f32(cfg->bits_v, a.cbv);
+  const double ak = fill_codebook_f32(cfg, cfg->bits_k, a.cbk);
+  const double av = fill_codebook_f32(cfg, cfg->bits_v, a.cbv);
   a.kscale = float(1.0 / (std::sqrt(double(cfg->d)) * ak));
   a.vscale = float(1.0 / (std::sqrt(double(cfg->d)) * av));
   a.qmult = tau * dev::kLog2e;

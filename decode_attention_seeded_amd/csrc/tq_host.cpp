@@ -53,6 +53,59 @@ Codebook build_codebook(int bits) {
   return cb;
 }
 
+// Lloyd iteration for the exact marginal of z = sqrt(d) u, u one coordinate
+// of a uniformly random unit vector in R^d: density proportional to
+// (1 - z^2/d)^((d-3)/2) on |z| < sqrt(d). Cell mass by Simpson's rule in
+// theta (z = sqrt(d) sin(theta), integrand sqrt(d) cos^(d-2)(theta)); the
+// first moment in closed form, d/(d-1) [(1 - a^2/d)^((d-1)/2) - (1 -
+// b^2/d)^((d-1)/2)]. Positive half iterated, then mirrored, as above.
+Codebook build_sphere_codebook(int bits, int d) {
+  const Codebook g = build_codebook(bits);
+  Codebook cb;
+  cb.bits = bits;
+  const int m = 1 << (bits - 1);
+  const double rd = std::sqrt(double(d));
+  auto base = [&](double z) { return std::fmax(0.0, 1.0 - z * z / d); };
+  auto mass = [&](double a, double b) {
+    const double ta = std::asin(std::fmin(1.0, a / rd)), tb = std::asin(std::fmin(1.0, b / rd));
+    const int n = 4096;                       // even
+    const double h = (tb - ta) / n;
+    double acc = 0.0;
+    for (int i = 0; i <= n; ++i) {
+      const double w = (i == 0 || i == n) ? 1.0 : (i & 1) ? 4.0 : 2.0;
+      acc += w * std::pow(std::cos(ta + i * h), d - 2);
+    }
+    return rd * acc * h / 3.0;
+  };
+  auto first = [&](double a, double b) {
+    const double e = 0.5 * (d - 1);
+    return d / double(d - 1) * (std::pow(base(a), e) - std::pow(base(b), e));
+  };
+  double pos[kMaxLevels / 2];
+  for (int k = 0; k < m; ++k) pos[k] = std::fmin(g.c[m + k], 0.9 * rd);
+  for (int it = 0; it < 100000; ++it) {
+    double edge[kMaxLevels / 2 + 1];
+    edge[0] = 0.0;
+    for (int k = 1; k < m; ++k) edge[k] = 0.5 * (pos[k - 1] + pos[k]);
+    edge[m] = rd;
+    double change = 0.0;
+    for (int k = 0; k < m; ++k) {
+      const double mean = first(edge[k], edge[k + 1]) / mass(edge[k], edge[k + 1]);
+      change = std::fmax(change, std::fabs(mean - pos[k]));
+      pos[k] = mean;
+    }
+    if (change < 1e-14) break;
+  }
+  const int L = 2 * m;
+  for (int k = 0; k < m; ++k) {
+    cb.c[m + k] = pos[k];
+    cb.c[m - 1 - k] = -pos[k];
+  }
+  for (int k = 1; k < L; ++k) cb.t[k - 1] = 0.5 * (cb.c[k - 1] + cb.c[k]);
+  cb.t[m - 1] = 0.0;
+  return cb;
+}
+
 // Nearest-even rounding of a positive double to binary16, returned as a
 // double (normal range only; the centroids here are in [0.1, 3]).
 double round_f16(double x) {
@@ -85,6 +138,9 @@ void fit_alpha(Codebook& cb) {
 
 std::once_flag g_once[5];
 Codebook g_cb[5];
+std::mutex g_sphere_mu;
+Codebook g_sphere[5][2];                 // [bits][d == 256]
+bool g_sphere_ok[5][2];
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -98,12 +154,26 @@ const Codebook& codebook(int bits) {
   return g_cb[bits];
 }
 
+const Codebook& codebook(int bits, int kind, int d) {
+  if (kind != TQ_CODEBOOK_SPHERE) return codebook(bits);
+  const int j = d == 256 ? 1 : 0;
+  std::lock_guard<std::mutex> lock(g_sphere_mu);
+  if (!g_sphere_ok[bits][j]) {
+    g_sphere[bits][j] = build_sphere_codebook(bits, d);
+    fit_alpha(g_sphere[bits][j]);
+    g_sphere_ok[bits][j] = true;
+  }
+  return g_sphere[bits][j];
+}
+
 int check_config(const tq_config* cfg) {
   if (!cfg) return TQ_ERR_ARG;
   if (!valid_d(cfg->d) || !valid_bits(cfg->bits_k) || !valid_bits(cfg->bits_v))
     return TQ_ERR_UNSUPPORTED;
   if (cfg->norm_dtype != TQ_F16 && cfg->norm_dtype != TQ_F32) return TQ_ERR_UNSUPPORTED;
   if (cfg->qjl != 0 && cfg->qjl != 1) return TQ_ERR_ARG;
+  if (cfg->codebook != TQ_CODEBOOK_GAUSS && cfg->codebook != TQ_CODEBOOK_SPHERE)
+    return TQ_ERR_UNSUPPORTED;
   return TQ_OK;
 }
 
@@ -219,6 +289,17 @@ int tq_bits_split(double kv_bits, int force_turboquant, int* enabled, int* bits_
 int tq_codebook(int bits, double* centroids, double* thresholds) {
   if (bits < 1 || bits > 4) return TQ_ERR_UNSUPPORTED;
   const Codebook& cb = codebook(bits);
+  const int L = 1 << bits;
+  if (centroids) std::memcpy(centroids, cb.c, sizeof(double) * L);
+  if (thresholds) std::memcpy(thresholds, cb.t, sizeof(double) * (L - 1));
+  return TQ_OK;
+}
+
+int tq_codebook_ex(int bits, int kind, int d, double* centroids, double* thresholds) {
+  if (bits < 1 || bits > 4) return TQ_ERR_UNSUPPORTED;
+  if (kind != TQ_CODEBOOK_GAUSS && kind != TQ_CODEBOOK_SPHERE) return TQ_ERR_UNSUPPORTED;
+  if (kind == TQ_CODEBOOK_SPHERE && !valid_d(d)) return TQ_ERR_UNSUPPORTED;
+  const Codebook& cb = codebook(bits, kind, d);
   const int L = 1 << bits;
   if (centroids) std::memcpy(centroids, cb.c, sizeof(double) * L);
   if (thresholds) std::memcpy(thresholds, cb.t, sizeof(double) * (L - 1));

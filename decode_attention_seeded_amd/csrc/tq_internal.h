@@ -26,6 +26,9 @@ struct Codebook {
 
 // Lloyd-Max codebook for N(0,1), cached per bit width (thread-safe).
 const Codebook& codebook(int bits);
+// The codebook a config selects: N(0,1) (TQ_CODEBOOK_GAUSS) or the exact
+// finite-d marginal (TQ_CODEBOOK_SPHERE, d 128 or 256); cached, thread-safe.
+const Codebook& codebook(int bits, int kind, int d);
 
 // SplitMix64 output i (0-based) of the stream started at state `seed`.
 inline uint64_t splitmix64_at(uint64_t seed, uint64_t i) {

@@ -57,6 +57,7 @@ typedef enum {
 
 /* Element types of inputs (q, k, v, x) and of the per-row norms. */
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+typedef enum { TQ_CODEBOOK_GAUSS = 0, TQ_CODEBOOK_SPHERE = 1 } tq_codebook_kind;
 
 /* Static description of one quantized cache format. */
 typedef struct {
@@ -67,6 +68,12 @@ typedef struct {
   int qjl;            /* 1: keys also carry the 1-bit QJL residual sketch     */
   uint64_t seed;      /* SplitMix64 seed of the rotation signs s              */
   uint64_t qjl_seed;  /* SplitMix64 seed of the QJL rotation R_2              */
+  int codebook;       /* TQ_CODEBOOK_GAUSS (0): Lloyd-Max for N(0,1);
+                         TQ_CODEBOOK_SPHERE (1): Lloyd-Max for the exact
+                         finite-d marginal of sqrt(d) * a coordinate of a
+                         uniform unit vector, density proportional to
+                         (1 - z^2/d)^((d-3)/2): the exact law whose shape
+                         the README's introduction calls near-Gaussian   */
 } tq_config;
 
 /*
@@ -117,6 +124,11 @@ int tq_bits_split(double kv_bits, int force_turboquant, int* enabled,
  * (host arrays, either may be NULL). Computed in double on the host.
  */
 int tq_codebook(int bits, double* centroids, double* thresholds);
+
+/* The codebook a tq_config's `codebook` field selects, in the layout of
+ * tq_codebook: kind TQ_CODEBOOK_GAUSS (d ignored) or TQ_CODEBOOK_SPHERE
+ * (d 128 or 256). TQ_ERR_UNSUPPORTED for other bits, kinds or d. */
+int tq_codebook_ex(int bits, int kind, int d, double* centroids, double* thresholds);
 
 /* The +-1 rotation signs for (seed, d) as int8 (host array of d). Host only. */
 int tq_signs(uint64_t seed, int d, int8_t* out);

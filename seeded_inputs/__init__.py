@@ -56,6 +56,7 @@ class Workload:
     append: int = 0          # tokens appended at the end of the context
     seed: int = 0            # RHT sign seed
     qjl_seed: int = 1
+    codebook: str = "gauss"  # "gauss" | "sphere"
 
     @property
     def G(self):
@@ -195,8 +196,8 @@ def kv_full(w: Workload, tensor: int, data_seed=DATA_SEED, workers=None):
 
 def small_workload(B=1, Hq=4, Hkv=2, d=128, N=300, bits_k=3, bits_v=4,
                    norm_dtype="f16", qjl=False, in_dtype="bf16",
-                   structure="iid", wid=100, seed=0, qjl_seed=1):
+                   structure="iid", wid=100, seed=0, qjl_seed=1, codebook="gauss"):
     """A small workload for parity tests (several tiles and a ragged tail)."""
     return Workload(wid, f"small-{wid}", B, Hq, Hkv, d, N, bits_k, bits_v,
                     norm_dtype, qjl, in_dtype, structure, seed=seed,
-                    qjl_seed=qjl_seed)
+                    qjl_seed=qjl_seed, codebook=codebook)

@@ -54,7 +54,7 @@ def kv_host(w: si.Workload, t0: int, t1: int):
 def config_of(w: si.Workload):
     import decode_attention_seeded_amd as tq
     return tq.Config(d=w.d, bits_k=w.bits_k, bits_v=w.bits_v, norm_dtype=w.norm_dtype,
-                     qjl=w.qjl, seed=w.seed, qjl_seed=w.qjl_seed)
+                     qjl=w.qjl, seed=w.seed, qjl_seed=w.qjl_seed, codebook=w.codebook)
 
 
 def gpu_encode(w: si.Workload, chunks=None, capacity=None):
@@ -76,7 +76,8 @@ def oracle_encode(w: si.Workload, t0=0, t1=None):
     t1 = w.N if t1 is None else t1
     _, _, fk, fv = kv_host(w, t0, t1)
     return o.encode_kv(fk, fv, seed=w.seed, bits_k=w.bits_k, bits_v=w.bits_v,
-                       norm_dtype=w.norm_dtype, qjl=w.qjl, qjl_seed=w.qjl_seed)
+                       norm_dtype=w.norm_dtype, qjl=w.qjl, qjl_seed=w.qjl_seed,
+                       sphere=w.codebook == "sphere")
 
 
 def compare_codes(w, cache, ref, t0=0, t1=None):
@@ -88,7 +89,7 @@ def compare_codes(w, cache, ref, t0=0, t1=None):
     for side, bits in (("k", w.bits_k), ("v", w.bits_v)):
         enc = ref[f"{side}_enc"]
         got = o.unpack_codes(getattr(cache, f"{side}c")[sl].cpu().numpy(), bits, w.d)
-        _, thr = o.lloyd_max(bits)
+        _, thr = o.lloyd_max(bits, w.d if w.codebook == "sphere" else None)
         bnd = o.boundary_mask(enc["z"], thr)
         bad = (got != enc["codes"]) & ~bnd
         assert not bad.any(), f"{side} codes differ at {np.argwhere(bad)[:5]}"
@@ -104,7 +105,7 @@ def compare_codes(w, cache, ref, t0=0, t1=None):
         got = o.unpack_signs(cache.kq[sl].cpu().numpy(), w.d)
         bnd = o.qjl_boundary_mask(sk["w"], sk["rnorm_exact"])
         # a row whose codes flipped at a boundary has a different residual
-        _, thr = o.lloyd_max(w.bits_k)
+        _, thr = o.lloyd_max(w.bits_k, w.d if w.codebook == "sphere" else None)
         row_flip = (o.boundary_mask(ref["k_enc"]["z"], thr)).any(-1, keepdims=True)
         bad = (got != sk["bits"]) & ~bnd & ~row_flip
         assert not bad.any(), f"qjl bits differ at {np.argwhere(bad)[:5]}"

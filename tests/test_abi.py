@@ -39,6 +39,23 @@ def test_host_codebook_matches_oracle(bits):
     assert t[len(t) // 2] == 0.0
 
 
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_host_sphere_codebook_matches_oracle(bits, d):
+    c, t = tq.tq_codebook_ex(bits, "sphere", d)
+    oc, ot = o.lloyd_max(bits, d)
+    # both sides stop a linearly converging Lloyd iteration at a step of
+    # ~1e-13 (different quadratures), which leaves them ~1e-10 apart: far
+    # inside the 1e-6 decision-boundary band of every code comparison
+    np.testing.assert_allclose(c, oc, atol=1e-9, rtol=0)
+    np.testing.assert_allclose(t, ot, atol=1e-9, rtol=0)
+    assert t[len(t) // 2] == 0.0
+    g, _ = tq.tq_codebook_ex(bits, "gauss", d)
+    assert g == tq.tq_codebook(bits)[0]
+    with pytest.raises(tq.TqError):
+        tq.tq_codebook_ex(bits, "sphere", 64)
+
+
 @pytest.mark.parametrize("seed,d", [(0, 128), (1, 256), (12345, 128)])
 def test_host_signs_match_oracle(seed, d):
     assert tq.tq_signs(seed, d) == list(o.signs(seed, d).astype(int))
@@ -130,6 +147,11 @@ def _enc(cfg=None, k=A, v=A, dt=tq.TQ_BF16, off=0, n=4, cache=None):
     cache = _cache() if cache is None else cache
     return lib.tq_encode_kv(ctypes.byref(cfg) if cfg != "null" else None, k, v, dt, off, n,
                             ctypes.byref(cache) if cache != "null" else None, None)
+
+
+def test_codebook_kind_validation():
+    assert _enc(cfg=_cfg(codebook=2)) == tq.TQ_ERR_UNSUPPORTED
+    assert _enc(cfg=_cfg(codebook=1), n=0) == tq.TQ_OK
 
 
 def test_encode_validation():

@@ -46,13 +46,20 @@ SMALL = {
     "d256_k4v2_f32norm_g4": dict(B=1, Hq=4, Hkv=1, d=256, N=650, bits_k=4, bits_v=2,
                                  norm_dtype="f32", wid=113),
     "d128_k2v4_g4": dict(B=1, Hq=8, Hkv=2, N=800, bits_k=2, bits_v=4, wid=114),
+    # the exact finite-d marginal codebook (encode thresholds, decode tables,
+    # QJL residual centroids)
+    "d128_k3v4_sphere": dict(B=1, Hq=8, Hkv=2, N=900, bits_k=3, bits_v=4, codebook="sphere",
+                             wid=115),
+    "d256_k2v2_sphere_qjl": dict(B=1, Hq=4, Hkv=2, d=256, N=520, bits_k=2, bits_v=2, qjl=True,
+                                 codebook="sphere", wid=116),
 }
 
 
 def _run_case(w, scale=0.0, splits=0):
     torch_cuda()
     log(f"case {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} N={w.N} "
-        f"K{w.bits_k}/V{w.bits_v} qjl={w.qjl} norm={w.norm_dtype} in={w.in_dtype}")
+        f"K{w.bits_k}/V{w.bits_v} qjl={w.qjl} norm={w.norm_dtype} in={w.in_dtype} "
+        f"codebook={w.codebook}")
     cfg, cache = gpu_encode(w)
     ref = oracle_encode(w)
     stats = compare_codes(w, cache, ref)
@@ -61,7 +68,7 @@ def _run_case(w, scale=0.0, splits=0):
                      splits=splits)
     want = o.attend(qf.astype(np.float64), ref, w.N, d=w.d, seed=w.seed, bits_k=w.bits_k,
                     bits_v=w.bits_v, Hkv=w.Hkv, scale=scale, qjl=w.qjl,
-                    qjl_seed=w.qjl_seed)
+                    qjl_seed=w.qjl_seed, sphere=w.codebook == "sphere")
     err, abs_err = rel_err(got, want)
     log(f"  boundary stats {stats}; max row-relative error {err:.3e} (abs {abs_err:.3e})")
     assert np.isfinite(got).all()

@@ -24,6 +24,8 @@ CASES = {
     "d256_k3v4_g2_f16in": (dict(B=1, Hq=4, Hkv=2, d=256, N=190, bits_k=3, bits_v=4,
                                 in_dtype="f16", wid=144), 64),
     "d128_k3v4_g8_whole": (dict(B=1, Hq=8, Hkv=1, N=200, bits_k=3, bits_v=4, wid=145), 200),
+    "d128_k3v4_sphere": (dict(B=1, Hq=8, Hkv=2, N=400, bits_k=3, bits_v=4, codebook="sphere",
+                              wid=149), 90),
 }
 
 
@@ -46,7 +48,8 @@ def _run(w, n_q, scale=0.0):
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     ref = o.attend_prefill(f32.astype(np.float64), _planes(cache, w.N), w.N, d=w.d, seed=w.seed,
-                           bits_k=w.bits_k, bits_v=w.bits_v, Hkv=w.Hkv, scale=scale or None)
+                           bits_k=w.bits_k, bits_v=w.bits_v, Hkv=w.Hkv, scale=scale or None,
+                           sphere=w.codebook == "sphere")
     err, abs_err = rel_err(got, ref)
     log(f"  max row-relative error {err:.2e} (abs {abs_err:.2e})")
     assert err <= TOL
