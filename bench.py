@@ -295,7 +295,7 @@ def main():
     # chunk, else the last 1024 tokens) over the packed cache, on the
     # matrix cores; algorithmic flops = 4 d per (query row, visible token)
     prefill = None
-    if not args.no_prefill and not w.qjl:
+    if not args.no_prefill:
         nq = A if A else min(1024, w.N)
         qc_raw, _ = si.chunk_queries(w, nq)
         qc = to_dev_bf16(torch, qc_raw) if w.in_dtype == "bf16" else \

@@ -19,8 +19,8 @@ int launch_decode_d256_k3(int, int, int, int, const DecodeArgs&, dim3, hipStream
 int launch_decode_d256_k4(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
 int launch_decode_d256_k16(int, int, int, int, const DecodeArgs&, dim3, hipStream_t);
 
-int launch_prefill_d128(int, int, const PrefillArgs&, dim3, hipStream_t);
-int launch_prefill_d256(int, int, const PrefillArgs&, dim3, hipStream_t);
+int launch_prefill_d128(int, int, int, const PrefillArgs&, dim3, hipStream_t);
+int launch_prefill_d256(int, int, int, const PrefillArgs&, dim3, hipStream_t);
 
 using EncodeLauncher = int (*)(int, bool, const EncodeArgs&, hipStream_t);
 int launch_encode_d128_k2(int, bool, const EncodeArgs&, hipStream_t);
@@ -428,14 +428,13 @@ int tq_attend_prefill(const tq_config* cfg, const void* q, int q_dtype, int B, i
   if (st != TQ_OK) return st;
   st = check_cache(cfg, cache);
   if (st != TQ_OK) return st;
-  if (cfg->qjl) return TQ_ERR_UNSUPPORTED;
   if (!valid_in_dtype(q_dtype)) return TQ_ERR_UNSUPPORTED;
   if (B != cache->B || Hq < 1 || Hq % cache->Hkv != 0) return TQ_ERR_ARG;
   if (!std::isfinite(scale)) return TQ_ERR_ARG;
   if (n_q < 1 || n_ctx < n_q) return TQ_ERR_ARG;
   if (n_ctx > cache->capacity) return TQ_ERR_CAPACITY;
   const int G = Hq / cache->Hkv;
-  const int64_t rows = pf_rows(cfg->d);
+  const int64_t rows = pf_rows(cfg->d, cfg->qjl != 0);
   const int64_t tiles = (n_q * G + rows - 1) / rows;
   if (tiles > (int64_t(1) << 31) - 1 || int64_t(B) * cache->Hkv > 65535) return TQ_ERR_ARG;
   if (B == 0) return TQ_OK;
@@ -466,9 +465,14 @@ int tq_attend_prefill(const tq_config* cfg, const void* q, int q_dtype, int B, i
   a.vscale = float(1.0 / (std::sqrt(double(cfg->d)) * av));
   a.qmult = tau * dev::kLog2e;
   sign_bitmap(cfg->seed, cfg->d, a.sbits);
+  a.kq = static_cast<const uint32_t*>(cache->kq);
+  a.kr = static_cast<const uint16_t*>(cache->kr);
+  a.qjl_c = float(std::sqrt(M_PI / (2.0 * cfg->d)));
+  sign_bitmap(cfg->qjl_seed, cfg->d, a.qsbits);
   const dim3 grid(unsigned(tiles), unsigned(int64_t(B) * cache->Hkv));
-  return cfg->d == 128 ? launch_prefill_d128(cfg->bits_k, cfg->bits_v, a, grid, stream)
-                       : launch_prefill_d256(cfg->bits_k, cfg->bits_v, a, grid, stream);
+  return cfg->d == 128
+             ? launch_prefill_d128(cfg->bits_k, cfg->bits_v, cfg->qjl, a, grid, stream)
+             : launch_prefill_d256(cfg->bits_k, cfg->bits_v, cfg->qjl, a, grid, stream);
 }
 
 int64_t tq_read_probe_sink_words(int64_t bytes) {

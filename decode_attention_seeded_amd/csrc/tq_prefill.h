@@ -57,6 +57,10 @@ struct PrefillArgs {
   float cbk[16];          // alpha_k * key centroids
   float cbv[16];          // alpha_v * value centroids
   uint32_t sbits[8];      // rotation signs, bit i set when sign i is negative
+  const uint32_t* kq;     // QJL sign plane (d/32 words per record), QJL only
+  const uint16_t* kr;     // QJL residual norms (fp16), QJL only
+  float qjl_c;            // sqrt(pi / (2 d))
+  uint32_t qsbits[8];     // QJL rotation signs, same layout
 };
 
 typedef _Float16 pf_h8 __attribute__((ext_vector_type(8)));
@@ -65,15 +69,19 @@ typedef float pf_f4 __attribute__((ext_vector_type(4)));
 constexpr int pf_max(int a, int b) { return a > b ? a : b; }
 
 constexpr int pf_waves(int d) { return d == 128 ? 8 : 4; }
-constexpr int pf_row_blocks(int d) { return d == 128 ? 2 : 1; }
-constexpr int pf_rows(int d) { return 16 * pf_waves(d) * pf_row_blocks(d); }
+constexpr int pf_row_blocks(int d, bool qjl) { return d == 128 && !qjl ? 2 : 1; }
+constexpr int pf_rows(int d, bool qjl) { return 16 * pf_waves(d) * pf_row_blocks(d, qjl); }
 
-template <int D, int BK, int BV>
+// QJL: the sign dot sum_i q''_i sigma_i of every (row, token) is a second
+// score product of the same shape, A = the key's signs as fp16 +-1 (a third
+// LDS tile written with the keys), B = the row's q'' = R_2 q'; the score is
+// ks_t * S + rho_t * S_qjl with rho_t = ||r_t|| sqrt(pi / (2d)).
+template <int D, int BK, int BV, bool QJL>
 __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   static_assert(D == 128 || D == 256, "prefill: d 128 or 256");
   constexpr int W = pf_waves(D);           // waves
-  constexpr int RB = pf_row_blocks(D);     // blocks of 16 query rows per wave
-  constexpr int NR = pf_rows(D);           // query rows per workgroup
+  constexpr int RB = pf_row_blocks(D, QJL);  // blocks of 16 query rows per wave
+  constexpr int NR = pf_rows(D, QJL);      // query rows per workgroup
   constexpr int NT = 64 * W;
   constexpr int TT = 64;                   // tokens per tile
   constexpr int NS = D / 16;               // value coordinate tiles of 16
@@ -89,16 +97,25 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   constexpr int VE = 1 << BV;
   constexpr int E = D / 16;                // row elements per lane (16 lanes per row)
   constexpr int KT_BYTES = TT * KS * 2;
-  constexpr int TILE_BYTES = KT_BYTES + D * VS * 2;
-  constexpr int SMEM = pf_max(2 * TILE_BYTES, pf_max(NR * D * 4, NR * KS * 2));
+  constexpr int VT_BYTES = D * VS * 2;
+  constexpr int TILE_BYTES = KT_BYTES + VT_BYTES + (QJL ? KT_BYTES : 0);
+  constexpr int QST_BYTES = NR * KS * 2 * (QJL ? 2 : 1);
+  // two tile buffers (the next tile is decoded while this one is used)
+  // where they fit, else one with a barrier on each side of the decode
+  constexpr int NBUF = 2 * TILE_BYTES + 4096 <= 152 * 1024 ? 2 : 1;
+  constexpr int SMEM = pf_max(NBUF * TILE_BYTES, pf_max(NR * D * 4, QST_BYTES));
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
   __shared__ __attribute__((aligned(16))) float tks[2][TT];
   __shared__ __attribute__((aligned(16))) float tnv[2][TT];
+  __shared__ __attribute__((aligned(16))) float trho[QJL ? 2 : 1][TT];
   __shared__ uint32_t kpair[KE];
   __shared__ uint16_t vone[VE];
   auto ktile = [&](int buf) { return reinterpret_cast<_Float16*>(smem + buf * TILE_BYTES); };
   auto vtile = [&](int buf) {
     return reinterpret_cast<_Float16*>(smem + buf * TILE_BYTES + KT_BYTES);
+  };
+  auto stile = [&](int buf) {
+    return reinterpret_cast<_Float16*>(smem + buf * TILE_BYTES + KT_BYTES + VT_BYTES);
   };
 
   const int tid = threadIdx.x;
@@ -141,18 +158,35 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
       for (int i = 0; i < E; ++i) if (smask >> i & 1) v[i] = -v[i];
       dev::fwht16<E, float>(v, l16);
 #pragma unroll
-      for (int i = 0; i < E; ++i) qst[m * KS + l16 * E + i] = _Float16(v[i] * mult);
+      for (int i = 0; i < E; ++i) {
+        v[i] *= mult;
+        qst[m * KS + l16 * E + i] = _Float16(v[i]);
+      }
+      if constexpr (QJL) {
+        // q'' = R_2 q' from the fp32 q'
+        const uint32_t qmask = dev::bitmap_bits(a.qsbits, l16 * E, E);
+#pragma unroll
+        for (int i = 0; i < E; ++i) if (qmask >> i & 1) v[i] = -v[i];
+        dev::fwht16<E, float>(v, l16);
+        const float nn = 1.0f / sqrtf(float(D));
+#pragma unroll
+        for (int i = 0; i < E; ++i) qst[(NR + m) * KS + l16 * E + i] = _Float16(v[i] * nn);
+      }
     }
   }
   __syncthreads();
   pf_h8 qb[RB][NK];
+  pf_h8 qb2[QJL ? RB : 1][QJL ? NK : 1];
   int64_t my_pos[RB];                   // the lane's query rows (score layout)
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int m = 16 * (RB * wave + rb) + col;
 #pragma unroll
-    for (int s = 0; s < NK; ++s)
+    for (int s = 0; s < NK; ++s) {
       qb[rb][s] = *reinterpret_cast<const pf_h8*>(qst + m * KS + 32 * s + 8 * kq);
+      if constexpr (QJL)
+        qb2[rb][s] = *reinterpret_cast<const pf_h8*>(qst + (NR + m) * KS + 32 * s + 8 * kq);
+    }
     my_pos[rb] = r0 + m < R ? pos0 + (r0 + m) / a.G : -1;
   }
   const int64_t r_last = (r0 + NR - 1 < R ? r0 + NR - 1 : R - 1);
@@ -165,8 +199,9 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   const int dpart = W == 8 ? (wave & 3) : wave;
   const bool do_k = W == 4 || wave < 4;
   const bool do_v = W == 4 || wave >= 4;     // wave-uniform
-  uint32_t kw[KWD], vw[VWD];
-  uint32_t knb = 0, vnb = 0;
+  constexpr int SWD = QJL ? CPT / 32 : 1;   // QJL sign words per dequant lane
+  uint32_t kw[KWD], vw[VWD], sw[SWD];
+  uint32_t knb = 0, vnb = 0, rnb = 0;
   auto fetch = [&](int n) {
     const int64_t tok = int64_t(n) * TT + dt;
     const bool ok = tok < a.n_ctx;
@@ -174,7 +209,9 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
     for (int j = 0; j < KWD; ++j) kw[j] = 0u;
 #pragma unroll
     for (int j = 0; j < VWD; ++j) vw[j] = 0u;
-    knb = vnb = 0u;
+#pragma unroll
+    for (int j = 0; j < SWD; ++j) sw[j] = 0u;
+    knb = vnb = rnb = 0u;
     if (!ok) return;                     // rows past the context are never read
     if (do_k) {
       const uint32_t* kp =
@@ -184,6 +221,12 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
       if (dpart == 0)
         knb = a.norm_f16 ? uint32_t(static_cast<const uint16_t*>(a.kn)[rec0 + tok])
                          : static_cast<const uint32_t*>(a.kn)[rec0 + tok];
+      if constexpr (QJL) {
+        const uint32_t* sp = a.kq + (rec0 + tok) * (D / 32) + dpart * SWD;
+#pragma unroll
+        for (int j = 0; j < SWD; ++j) sw[j] = sp[j];
+        if (dpart == 0) rnb = a.kr[rec0 + tok];
+      }
     }
     if (do_v) {
       const uint32_t* vp =
@@ -218,6 +261,20 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
         kd[c] = make_uint4(pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]);
       if (dpart == 0)
         tks[buf][dt] = (a.norm_f16 ? dev::f16_to_f32(knb) : __uint_as_float(knb)) * a.kscale;
+      if constexpr (QJL) {
+        // sign bit set -> -1: the fp16 pair 0x3C00 | bit << 15 per coordinate
+        uint32_t ps[CPT / 2];
+#pragma unroll
+        for (int c = 0; c < CPT / 2; ++c) {
+          const uint32_t two = (sw[c >> 4] >> (2 * (c & 15))) & 3u;
+          ps[c] = 0x3C003C00u | (two & 1u) << 15 | (two & 2u) << 30;
+        }
+        uint4* sd = reinterpret_cast<uint4*>(stile(buf) + dt * KS + dpart * CPT);
+#pragma unroll
+        for (int c = 0; c < CPT / 8; ++c)
+          sd[c] = make_uint4(ps[4 * c], ps[4 * c + 1], ps[4 * c + 2], ps[4 * c + 3]);
+        if (dpart == 0) trho[buf][dt] = dev::f16_to_f32(rnb) * a.qjl_c;
+      }
     }
     if (do_v) {
       uint16_t* vt = reinterpret_cast<uint16_t*>(vtile(buf));
@@ -236,15 +293,16 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   if (ntiles > 1) fetch(1);
   __syncthreads();                      // tile 0 is in place
   for (int n = 0; n < ntiles; ++n) {
-    const int buf = n & 1;
+    const int buf = NBUF == 2 ? (n & 1) : 0;
     // the next tile goes to the other buffer, whose last readers finished
     // before the barrier that ended the previous iteration
-    if (n + 1 < ntiles) {
+    if (NBUF == 2 && n + 1 < ntiles) {
       put(buf ^ 1);
       if (n + 2 < ntiles) fetch(n + 2);
     }
     const _Float16* kt = ktile(buf);
     const _Float16* vtl = vtile(buf);
+    const _Float16* stl = stile(buf);
 
     // ---------------- scores S^T (tokens x rows), scaled and masked
     float sc[RB][4][4];
@@ -253,9 +311,12 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
     for (int rb = 0; rb < RB; ++rb) mt[rb] = -INFINITY;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
-      pf_f4 acc[RB];
+      pf_f4 acc[RB], acq[QJL ? RB : 1];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) acc[rb] = pf_f4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < RB; ++rb) {
+        acc[rb] = pf_f4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (QJL) acq[rb] = pf_f4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
         const pf_h8 ka =
@@ -263,15 +324,29 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[rb][s], acc[rb], 0, 0, 0);
+        if constexpr (QJL) {
+          const pf_h8 sa =
+              *reinterpret_cast<const pf_h8*>(stl + (16 * tb + col) * KS + 32 * s + 8 * kq);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            acq[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, qb2[rb][s], acq[rb], 0, 0, 0);
+        }
       }
       const float4 ks = *reinterpret_cast<const float4*>(&tks[buf][16 * tb + 4 * kq]);
       const float kss[4] = {ks.x, ks.y, ks.z, ks.w};
+      float rhs[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (QJL) {
+        const float4 rh = *reinterpret_cast<const float4*>(&trho[buf][16 * tb + 4 * kq]);
+        rhs[0] = rh.x; rhs[1] = rh.y; rhs[2] = rh.z; rhs[3] = rh.w;
+      }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int64_t tok = int64_t(n) * TT + 16 * tb + 4 * kq + i;
-          sc[rb][tb][i] = tok <= my_pos[rb] ? acc[rb][i] * kss[i] : -INFINITY;
+          float v = acc[rb][i] * kss[i];
+          if constexpr (QJL) v = fmaf(acq[rb][i], rhs[i], v);
+          sc[rb][tb][i] = tok <= my_pos[rb] ? v : -INFINITY;
           mt[rb] = fmaxf(mt[rb], sc[rb][tb][i]);
         }
     }
@@ -331,6 +406,11 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
       }
     }
     __syncthreads();
+    if (NBUF == 1 && n + 1 < ntiles) {  // one buffer: decode between two barriers
+      put(0);
+      if (n + 2 < ntiles) fetch(n + 2);
+      __syncthreads();
+    }
   }
 
   // ---------------- O / l, then R^T per row, fp32 out

@@ -243,10 +243,11 @@ int tq_append_attend_decode(const tq_config* cfg, const void* k_new,
  *   q   : [B][Hq][n_q][d] of q_dtype (device, 16-byte aligned)
  *   out : [B][Hq][n_q][d] fp32 (device, caller-owned, 16-byte aligned)
  *   scale: 0 selects 1/sqrt(d). No workspace.
+ * With cfg->qjl the QJL term of tq_attend_decode is added to every score.
  * Errors (before any work is queued): TQ_ERR_ARG (1 <= n_q <= n_ctx
  * violated, Hq not a multiple of Hkv, B != cache B, null pointers),
- * TQ_ERR_CAPACITY (n_ctx > capacity), TQ_ERR_ALIGN, TQ_ERR_UNSUPPORTED (QJL
- * formats: the correction term is not implemented on this path).
+ * TQ_ERR_CAPACITY (n_ctx > capacity), TQ_ERR_ALIGN, TQ_ERR_UNSUPPORTED
+ * (d, bit widths, codebook or q dtype).
  */
 int tq_attend_prefill(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
                       int64_t n_q, const tq_cache* cache, int64_t n_ctx, float scale,

@@ -281,7 +281,8 @@ def test_prefill_validation():
         return lib.tq_attend_prefill(ctypes.byref(cfg), q, qdt, B, Hq, n_q, ctypes.byref(cache),
                                      n_ctx, 0.0, out, None)
 
-    assert call(cfg=_cfg(qjl=1)) == tq.TQ_ERR_UNSUPPORTED
+    assert call(cfg=_cfg(qjl=1), cache=_cache(kr=MIS)) == tq.TQ_ERR_ALIGN
+    assert call(cfg=_cfg(qjl=1), cache=_cache(kq=None)) == tq.TQ_ERR_ARG
     assert call(cfg=_cfg(d=64)) == tq.TQ_ERR_UNSUPPORTED
     assert call(qdt=7) == tq.TQ_ERR_UNSUPPORTED
     assert call(n_q=0) == tq.TQ_ERR_ARG

@@ -2,7 +2,7 @@
 ABI) against the CPU oracle's attend_prefill on the same seeded inputs.
 
 The cache is encoded on the GPU and the oracle attends over the GPU's own
-planes (encode parity is covered by the decode tests), so the comparison
+planes (codes, norms, QJL sign bits and residual norms) (encode parity is covered by the decode tests), so the comparison
 isolates the attention kernel: max row-relative error <= 2e-3."""
 
 import numpy as np
@@ -26,20 +26,33 @@ CASES = {
     "d128_k3v4_g8_whole": (dict(B=1, Hq=8, Hkv=1, N=200, bits_k=3, bits_v=4, wid=145), 200),
     "d128_k3v4_sphere": (dict(B=1, Hq=8, Hkv=2, N=400, bits_k=3, bits_v=4, codebook="sphere",
                               wid=149), 90),
+    # QJL: the sign dot is a second score product (one row block per wave;
+    # d 256 runs with one tile buffer)
+    "d128_k3qjl_v4_g4": (dict(B=2, Hq=8, Hkv=2, N=600, bits_k=3, bits_v=4, qjl=True, wid=150),
+                         130),
+    "d256_k3qjl_v4_g2": (dict(B=1, Hq=4, Hkv=2, d=256, N=330, bits_k=3, bits_v=4, qjl=True,
+                              wid=151), 75),
+    "d128_k2qjl_v2_g1_sphere": (dict(B=1, Hq=2, Hkv=2, N=250, bits_k=2, bits_v=2, qjl=True,
+                                     codebook="sphere", wid=152), 40),
 }
 
 
-def _planes(cache, n):
-    return {k: getattr(cache, k)[:, :, :n].cpu().numpy() for k in ("kc", "vc")} | {
+def _planes(cache, n, qjl=False):
+    p = {k: getattr(cache, k)[:, :, :n].cpu().numpy() for k in ("kc", "vc")} | {
         k: getattr(cache, k)[:, :, :n].float().cpu().numpy().astype(np.float64)
         for k in ("kn", "vn")}
+    if qjl:
+        p["kq"] = cache.kq[:, :, :n].cpu().numpy()
+        p["kr"] = cache.kr[:, :, :n].float().cpu().numpy().astype(np.float64)
+    return p
 
 
 def _run(w, n_q, scale=0.0):
     import decode_attention_seeded_amd as tq
     torch = torch_cuda()
     log(f"prefill case wid={w.wid} B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} N={w.N} n_q={n_q} "
-        f"K{w.bits_k}/V{w.bits_v} norm={w.norm_dtype} in={w.in_dtype}")
+        f"K{w.bits_k}/V{w.bits_v} qjl={w.qjl} norm={w.norm_dtype} in={w.in_dtype} "
+        f"codebook={w.codebook}")
     cfg, cache = gpu_encode(w)
     raw, f32 = si.chunk_queries(w, n_q)
     q = to_device(raw, w.in_dtype)
@@ -47,8 +60,9 @@ def _run(w, n_q, scale=0.0):
     tq.tq_attend_prefill(cfg, q, cache, w.N, out, scale=scale)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
-    ref = o.attend_prefill(f32.astype(np.float64), _planes(cache, w.N), w.N, d=w.d, seed=w.seed,
-                           bits_k=w.bits_k, bits_v=w.bits_v, Hkv=w.Hkv, scale=scale or None,
+    ref = o.attend_prefill(f32.astype(np.float64), _planes(cache, w.N, w.qjl), w.N, d=w.d,
+                           seed=w.seed, bits_k=w.bits_k, bits_v=w.bits_v, Hkv=w.Hkv,
+                           scale=scale or None, qjl=w.qjl, qjl_seed=w.qjl_seed,
                            sphere=w.codebook == "sphere")
     err, abs_err = rel_err(got, ref)
     log(f"  max row-relative error {err:.2e} (abs {abs_err:.2e})")
@@ -76,16 +90,11 @@ def test_prefill_explicit_scale_and_one_query_equals_decode():
     assert err <= TOL
 
 
-def test_prefill_rejects_qjl_and_bad_chunks():
+def test_prefill_rejects_bad_chunks():
     import decode_attention_seeded_amd as tq
     torch = torch_cuda()
-    w = si.small_workload(B=1, Hq=4, Hkv=2, N=64, bits_k=3, bits_v=4, qjl=True, wid=147)
-    cfg, cache = gpu_encode(w)
-    q = torch.zeros((1, 4, 8, w.d), dtype=torch.bfloat16, device="cuda")
-    out = torch.empty((1, 4, 8, w.d), dtype=torch.float32, device="cuda")
-    with pytest.raises(tq.TqError) as e:
-        tq.tq_attend_prefill(cfg, q, cache, w.N, out)
-    assert e.value.status == tq.TQ_ERR_UNSUPPORTED
+    q = torch.zeros((1, 4, 8, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((1, 4, 8, 128), dtype=torch.float32, device="cuda")
     w2 = si.small_workload(B=1, Hq=4, Hkv=2, N=64, bits_k=3, bits_v=4, wid=148)
     cfg2, cache2 = gpu_encode(w2)
     with pytest.raises(tq.TqError) as e:
