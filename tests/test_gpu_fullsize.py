@@ -142,3 +142,52 @@ def test_full_size_workload(wid):
         log(f"  head (b={b}, h={h}): max relative error {err:.3e}")
         worst = max(worst, err)
     assert worst <= TOL
+
+
+@pytest.mark.timeout(300)
+def test_full_size_prefill_sampled_rows():
+    """The causal prefill bench.py times: the 4096 appended tokens of the
+    long-context workload attend over its 524288-token cache. Sampled query
+    rows (chunk start, middle and end; first and last head of KV head 0 and
+    the last head overall) against the oracle's streamed attention over each
+    row's own prefix."""
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.WORKLOADS[4]
+    n_q = w.append
+    log(f"prefill: {n_q} chunk tokens over {w.name}")
+    cfg, cache = _encode_full(w)
+    qraw, qf = si.chunk_queries(w, n_q)
+    out = torch.empty((w.B, w.Hq, n_q, w.d), dtype=torch.float32, device="cuda")
+    tq.tq_attend_prefill(cfg, to_device(qraw, w.in_dtype), cache, w.N, out)
+    torch.cuda.synchronize()
+    memo = {}
+
+    def block(bb, gg, t0, t1):
+        base = t0 - t0 % si.BLOCK
+        key = (bb, gg, base)
+        if key not in memo:
+            end = min(w.N, base + si.BLOCK)
+            _, fk = si.kv_rows(w, si.T_K, bb, gg, base, end)
+            _, fv = si.kv_rows(w, si.T_V, bb, gg, base, end)
+            ek = o.encode_vectors(fk.astype(np.float64), w.seed, w.bits_k, w.norm_dtype)
+            ev = o.encode_vectors(fv.astype(np.float64), w.seed, w.bits_v, w.norm_dtype)
+            memo[key] = {"kcodes": ek["codes"], "kn": ek["norm"], "vcodes": ev["codes"],
+                         "vn": ev["norm"]}
+        full = memo[key]
+        return {k: v[t0 - base:t1 - base] for k, v in full.items()}
+
+    samples = [(0, [0, w.G - 1]), (n_q // 2 - 1, [0, w.G - 1]), (n_q - 1, [0, w.G - 1, w.Hq - 1])]
+    worst = 0.0
+    for i, hs in samples:
+        n_ctx = w.N - n_q + i + 1
+        want = o.attend_rotated_blocked(qf[:, :, i].astype(np.float64), block, n_ctx, B=w.B,
+                                        Hq=w.Hq, Hkv=w.Hkv, d=w.d, seed=w.seed, bits_k=w.bits_k,
+                                        bits_v=w.bits_v, heads=[(0, h) for h in hs])
+        for h in hs:
+            got = out[0, h, i].cpu().numpy().astype(np.float64)
+            assert np.isfinite(got).all()
+            err, _ = rel_err(got[None], want[0, h][None])
+            log(f"  query {i} (position {n_ctx - 1}), head {h}: max relative error {err:.3e}")
+            worst = max(worst, err)
+    assert worst <= TOL
