@@ -1173,20 +1173,22 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 //           token t. The query is the A operand, broadcast from one block
 //           (CBSZ 4, ABID j mod 16): lane (block b, row m) keeps only the
 //           quads j = b, b + 16, ... of head m.
-//   values  O[g][c] += sum_t p[g][t] v_t[c] with v_mfma_f32_16x16x16_f16 per
-//           16 tokens: A = weights (row = head, rows past GK zero), B =
-//           value pair lookups; lane (kq = lane / 16, column n = lane % 16)
-//           holds tokens 4kq .. 4kq + 3 of the block for coordinates
-//           VJ*n .. VJ*n + VJ - 1, one instruction per offset j < VJ. The
-//           sums land in lanes 0..15 (register g = head g).
+//   values  O[g][c] += sum_t p[g][t] v_t[c] with v_mfma_f32_16x16x32_f16 per
+//           32 tokens (two 16-token blocks): A = weights (row = head, rows
+//           past GK zero), B = value lookups; lane (kq = lane / 16, column
+//           n = lane % 16) holds tokens 4kq .. 4kq + 3 of each block for
+//           coordinates VJ*n .. VJ*n + VJ - 1, one instruction per offset
+//           j < VJ. The sums land in lanes 0..15 (register g = head g).
 //   QJL     the sign dot sum_i q''_i sigma_i is a second chain of the same
 //           4x4x4 blocks: B = the key's 4 signs of quad j as fp16 +-1 (one
 //           8-byte lookup of a 16-entry table), A = the quad of R_2 q'.
 // ---------------------------------------------------------------------------
 
 typedef _Float16 mx_h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 mx_h8 __attribute__((ext_vector_type(8)));
 typedef float mx_f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t mx_u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t mx_u4 __attribute__((ext_vector_type(4)));
 
 template <int D, int BK, int BV, bool QJL>
 struct MxTile {
@@ -1538,61 +1540,73 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---------------- values: 16 tokens per MFMA, lane = (kq, column)
+    // ---------------- values: 32 tokens (two 16-token blocks) per MFMA,
+    // lane = (kq, column); the lane's k-values 8kq .. 8kq + 7 are tokens
+    // 4kq .. 4kq + 3 of the first block, then of the second
     const bool arow = col < GK;
     const uint16_t* prow = p16 + (arow ? col : 0) * TW + 4 * kq;
+    // B operand (4 tokens of one coordinate) of block blk, coordinate c
+    auto vquad = [&](int blk, uint32_t (&quad)[4]) {
+      // 2-bit values: byte b of P, R, Q, S is the 4-token code byte of
+      // coordinate 4b, 4b + 1, 4b + 2, 4b + 3 (code c of a token at bits 2c)
+      const uint32_t x0 = cur.vx[4 * blk][0], x1 = cur.vx[4 * blk + 1][0];
+      const uint32_t x2 = cur.vx[4 * blk + 2][0], x3 = cur.vx[4 * blk + 3][0];
+      constexpr uint32_t kEven = 0x33333333u, kOdd = 0xCCCCCCCCu, kLo = 0x0F0F0F0Fu;
+      // nibble k: (t0, t1) codes of coordinate 2k (A, C) or 2k + 1 (B, D)
+      const uint32_t A = (x0 & kEven) | ((x1 << 2) & kOdd);
+      const uint32_t B = (x1 & kOdd) | ((x0 >> 2) & kEven);
+      const uint32_t C = (x2 & kEven) | ((x3 << 2) & kOdd);
+      const uint32_t Dw = (x3 & kOdd) | ((x2 >> 2) & kEven);
+      quad[0] = (A & kLo) | ((C << 4) & ~kLo);
+      quad[1] = (B & kLo) | ((Dw << 4) & ~kLo);
+      quad[2] = ((A >> 4) & kLo) | (C & ~kLo);
+      quad[3] = ((B >> 4) & kLo) | (Dw & ~kLo);
+    };
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      mx_u2 pw = *reinterpret_cast<const mx_u2*>(prow + 16 * blk);
-      if (!arow) pw = mx_u2{0u, 0u};
-      const mx_h4 pa = __builtin_bit_cast(mx_h4, pw);
+    for (int bp = 0; bp < 2; ++bp) {
+      mx_u2 pw0 = *reinterpret_cast<const mx_u2*>(prow + 32 * bp);
+      mx_u2 pw1 = *reinterpret_cast<const mx_u2*>(prow + 32 * bp + 16);
+      if (!arow) pw0 = pw1 = mx_u2{0u, 0u};
+      const mx_h8 pa = __builtin_bit_cast(mx_h8, mx_u4{pw0[0], pw0[1], pw1[0], pw1[1]});
       if constexpr (VQ4) {
-        // the lane's 4 tokens hold VJ <= 16 two-bit codes each (code c at
-        // bits 2c); gather, per coordinate c, the byte t0 | t1<<2 | t2<<4 |
-        // t3<<6 of its 4 tokens' codes: byte b of P, R, Q, S is coordinate
-        // 4b, 4b + 1, 4b + 2, 4b + 3
-        const uint32_t x0 = cur.vx[4 * blk][0], x1 = cur.vx[4 * blk + 1][0];
-        const uint32_t x2 = cur.vx[4 * blk + 2][0], x3 = cur.vx[4 * blk + 3][0];
-        constexpr uint32_t kEven = 0x33333333u, kOdd = 0xCCCCCCCCu, kLo = 0x0F0F0F0Fu;
-        // nibble k: (t0, t1) codes of coordinate 2k (A, C) or 2k + 1 (B, D)
-        const uint32_t A = (x0 & kEven) | ((x1 << 2) & kOdd);
-        const uint32_t B = (x1 & kOdd) | ((x0 >> 2) & kEven);
-        const uint32_t C = (x2 & kEven) | ((x3 << 2) & kOdd);
-        const uint32_t Dw = (x3 & kOdd) | ((x2 >> 2) & kEven);
-        const uint32_t P = (A & kLo) | ((C << 4) & ~kLo);
-        const uint32_t Q = ((A >> 4) & kLo) | (C & ~kLo);
-        const uint32_t R = (B & kLo) | ((Dw << 4) & ~kLo);
-        const uint32_t S = ((B >> 4) & kLo) | (Dw & ~kLo);
-        const uint32_t quad[4] = {P, R, Q, S};
+        uint32_t q0[4], q1[4];
+        vquad(2 * bp, q0);
+        vquad(2 * bp + 1, q1);
 #pragma unroll
         for (int c = 0; c < VJ; ++c) {
-          const uint32_t va = __builtin_amdgcn_perm(quad[c & 3], l8,
-                                                    0x0C0C0000u | uint32_t(4 + (c >> 2)) << 8);
-          const mx_u2 vb = *reinterpret_cast<const mx_u2*>(vtab + va);
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, __builtin_bit_cast(mx_h4, vb),
-                                                         acc[c], 0, 0, 0);
+          const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (c >> 2)) << 8;
+          const mx_u2 v0 = *reinterpret_cast<const mx_u2*>(
+              vtab + __builtin_amdgcn_perm(q0[c & 3], l8, sel));
+          const mx_u2 v1 = *reinterpret_cast<const mx_u2*>(
+              vtab + __builtin_amdgcn_perm(q1[c & 3], l8, sel));
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              pa, __builtin_bit_cast(mx_h8, mx_u4{v0[0], v0[1], v1[0], v1[1]}), acc[c], 0, 0, 0);
         }
       } else {
 #pragma unroll
-      for (int grp = 0; grp < VJ / 8; ++grp) {
-        uint32_t x[4];
+        for (int grp = 0; grp < VJ / 8; ++grp) {
+          uint32_t lo[2][2], hi[2][2];     // [block][token pair]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = cur.vx[4 * blk + i][grp];
-        uint32_t lo01, hi01, lo23, hi23;
-        mx_pair_words(x[0], x[1], &lo01, &hi01);
-        mx_pair_words(x[2], x[3], &lo23, &hi23);
+          for (int h = 0; h < 2; ++h) {
+            const int blk = 2 * bp + h;
+            mx_pair_words(cur.vx[4 * blk][grp], cur.vx[4 * blk + 1][grp], &lo[h][0], &hi[h][0]);
+            mx_pair_words(cur.vx[4 * blk + 2][grp], cur.vx[4 * blk + 3][grp], &lo[h][1],
+                          &hi[h][1]);
+          }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8;
-          const uint32_t va01 = __builtin_amdgcn_perm((e & 1) ? hi01 : lo01, vl4, sel);
-          const uint32_t va23 = __builtin_amdgcn_perm((e & 1) ? hi23 : lo23, vl4, sel);
-          mx_u2 vb;
-          vb[0] = *reinterpret_cast<const uint32_t*>(vtab + va01);
-          vb[1] = *reinterpret_cast<const uint32_t*>(vtab + va23);
-          acc[8 * grp + e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              pa, __builtin_bit_cast(mx_h4, vb), acc[8 * grp + e], 0, 0, 0);
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8;
+            mx_u4 vb;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int t = 0; t < 2; ++t)
+                vb[2 * h + t] = *reinterpret_cast<const uint32_t*>(
+                    vtab + __builtin_amdgcn_perm((e & 1) ? hi[h][t] : lo[h][t], vl4, sel));
+            acc[8 * grp + e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                pa, __builtin_bit_cast(mx_h8, vb), acc[8 * grp + e], 0, 0, 0);
+          }
         }
-      }
       }
     }
   };
