@@ -127,7 +127,9 @@ int tq_codebook(int bits, double* centroids, double* thresholds);
 
 /* The codebook a tq_config's `codebook` field selects, in the layout of
  * tq_codebook: kind TQ_CODEBOOK_GAUSS (d ignored) or TQ_CODEBOOK_SPHERE
- * (d 128 or 256). TQ_ERR_UNSUPPORTED for other bits, kinds or d. */
+ * (d 128 or 256). TQ_ERR_UNSUPPORTED for other bits, kinds or d. Each
+ * codebook is computed on the host at its first use (a finite-d one takes
+ * up to about a second) and cached for the life of the process. */
 int tq_codebook_ex(int bits, int kind, int d, double* centroids, double* thresholds);
 
 /* The +-1 rotation signs for (seed, d) as int8 (host array of d). Host only. */
