@@ -103,3 +103,26 @@ def test_prefill_rejects_bad_chunks():
     with pytest.raises(tq.TqError) as e:
         tq.tq_attend_prefill(cfg2, q, cache2, 65, out)      # beyond capacity
     assert e.value.status == tq.TQ_ERR_CAPACITY
+
+
+def test_prefill_context_shorter_than_capacity():
+    # the cache has room for more tokens than the context holds: rows past
+    # n_ctx (never written) must not be read
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.small_workload(B=1, Hq=8, Hkv=2, N=300, bits_k=3, bits_v=4, wid=153)
+    log(f"prefill with capacity 1000 > n_ctx {w.N}")
+    cfg, cache = gpu_encode(w, capacity=1000)
+    for name in ("kc", "vc", "kn", "vn"):                  # garbage past the context
+        getattr(cache, name)[:, :, w.N:].fill_(0x7b if name in ("kc", "vc") else 1e4)
+    n_q = 50
+    raw, f32 = si.chunk_queries(w, n_q)
+    out = torch.empty((w.B, w.Hq, n_q, w.d), dtype=torch.float32, device="cuda")
+    tq.tq_attend_prefill(cfg, to_device(raw, w.in_dtype), cache, w.N, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = o.attend_prefill(f32.astype(np.float64), _planes(cache, w.N), w.N, d=w.d, seed=w.seed,
+                           bits_k=w.bits_k, bits_v=w.bits_v, Hkv=w.Hkv)
+    err, _ = rel_err(got, ref)
+    log(f"  max row-relative error {err:.2e}")
+    assert err <= TOL
