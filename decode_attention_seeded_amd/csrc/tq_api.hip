@@ -171,12 +171,12 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
   da.qmult = qa.mult;
   int st1 = TQ_OK;
   // the matrix-core kernel rotates its own query rows
-  if (p.wide != 2) st1 = launch_qprep(d, qa, st);
+  if (!p.mx) st1 = launch_qprep(d, qa, st);
   if (st1 != TQ_OK) return st1;
   DecodeLauncher fn = decode_launcher(d, bk);
   if (!fn) return TQ_ERR_UNSUPPORTED;
   dim3 grid(unsigned(p.splits), unsigned(int64_t(B) * Hkv * p.chunks));
-  st1 = fn(bv, p.gk, qjl, p.wide, da, grid, st);
+  st1 = fn(bv, p.gk, qjl, p.mx, da, grid, st);
   if (st1 != TQ_OK) return st1;
   MergeArgs ma;
   ma.ml = da.ml;
@@ -211,7 +211,7 @@ int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
   if (ws_bytes < p.total) return TQ_ERR_WORKSPACE;
   st = device_ready();
   if (st != TQ_OK) return st;
-  if (app && (p.wide != 2 || cfg->qjl)) {
+  if (app && (!p.mx || cfg->qjl)) {
     EncodeLauncher efn = encode_launcher(cfg->d, cfg->bits_k);
     if (!efn) return TQ_ERR_UNSUPPORTED;
     st = efn(cfg->bits_v, cfg->qjl != 0, *app, stream);

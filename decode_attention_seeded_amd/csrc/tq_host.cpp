@@ -191,7 +191,7 @@ int check_cache(const tq_config* cfg, const tq_cache* c) {
 static int decode_tile(int d) { return d == 128 ? 256 : 512; }
 
 // Default split count: about `target` workgroups over the chip (256 CUs).
-// The wide kernel holds a whole compute unit per workgroup, so it aims at one
+// The matrix-core kernel holds a whole compute unit per workgroup, so it aims at one
 // round of 256 workgroups; the narrow kernels at ~8 workgroups per CU.
 static int finish_plan(int64_t n_ctx, int splits, int64_t units, int tile, int64_t target,
                        DecodePlan* p) {
@@ -222,9 +222,9 @@ int plan_decode(int d, int bits_v, int qjl, int B, int Hq, int Hkv, int64_t n_ct
   p->G = Hq / Hkv;
   p->gk = (p->G % 4 == 0) ? 4 : (p->G % 2 == 0) ? 2 : 1;
   p->chunks = p->G / p->gk;
-  p->wide = use_mx(d, bits_v, qjl) ? 2 : 0;
+  p->mx = use_mx(d, bits_v, qjl) ? 1 : 0;
   const int64_t units = int64_t(B) * Hkv * p->chunks;
-  if (p->wide == 2)
+  if (p->mx)
     finish_plan(n_ctx, splits, units, 64 * mx_waves(d), 256, p);
   else
     finish_plan(n_ctx, splits, units, decode_tile(d), 2048, p);

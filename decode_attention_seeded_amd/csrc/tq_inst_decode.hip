@@ -19,14 +19,14 @@
 namespace tq {
 
 template <int BV, int GK, bool QJL>
-static int go(int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static int go(int mx, const DecodeArgs& a, dim3 grid, hipStream_t st) {
 #if TQ_BK == 16
-  if (wide) return TQ_ERR_UNSUPPORTED;
+  if (mx) return TQ_ERR_UNSUPPORTED;
   hipLaunchKernelGGL((k_decode<TQ_D, TQ_BK, BV, GK, QJL>), grid, dim3(TQ_D / 32 * 64), 0, st,
                      a, a.qp, a.qq);
 #else
   if constexpr (BV == 2 || BV == 4) {
-    if (wide == 2) {
+    if (mx) {
       const uint32_t* qp2 = reinterpret_cast<const uint32_t*>(a.qp);
       const dim3 block(64 * mx_waves(TQ_D));
       if (a.norm_f16)
@@ -37,9 +37,9 @@ static int go(int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
                            qp2);
       return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
     }
-    if (wide) return TQ_ERR_UNSUPPORTED;
+    if (mx) return TQ_ERR_UNSUPPORTED;
   } else {
-    if (wide) return TQ_ERR_UNSUPPORTED;
+    if (mx) return TQ_ERR_UNSUPPORTED;
   }
   hipLaunchKernelGGL((k_decode_pk<TQ_D, TQ_BK, BV, GK, QJL>), grid, dim3(TQ_D / 32 * 64), 0,
                      st, a, reinterpret_cast<const uint32_t*>(a.qp), a.qq);
@@ -48,34 +48,34 @@ static int go(int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
 }
 
 template <int BV, int GK>
-static int go_q(int qjl, int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static int go_q(int qjl, int mx, const DecodeArgs& a, dim3 grid, hipStream_t st) {
 #if TQ_BK == 16
   (void)qjl;
-  return go<BV, GK, false>(wide, a, grid, st);
+  return go<BV, GK, false>(mx, a, grid, st);
 #else
-  return qjl ? go<BV, GK, true>(wide, a, grid, st) : go<BV, GK, false>(wide, a, grid, st);
+  return qjl ? go<BV, GK, true>(mx, a, grid, st) : go<BV, GK, false>(mx, a, grid, st);
 #endif
 }
 
 template <int BV>
-static int go_g(int gk, int qjl, int wide, const DecodeArgs& a, dim3 grid, hipStream_t st) {
+static int go_g(int gk, int qjl, int mx, const DecodeArgs& a, dim3 grid, hipStream_t st) {
   switch (gk) {
-    case 1: return go_q<BV, 1>(qjl, wide, a, grid, st);
-    case 2: return go_q<BV, 2>(qjl, wide, a, grid, st);
-    case 4: return go_q<BV, 4>(qjl, wide, a, grid, st);
+    case 1: return go_q<BV, 1>(qjl, mx, a, grid, st);
+    case 2: return go_q<BV, 2>(qjl, mx, a, grid, st);
+    case 4: return go_q<BV, 4>(qjl, mx, a, grid, st);
     default: return TQ_ERR_UNSUPPORTED;
   }
 }
 
-int TQ_LAUNCHER(int bv, int gk, int qjl, int wide, const DecodeArgs& a, dim3 grid,
+int TQ_LAUNCHER(int bv, int gk, int qjl, int mx, const DecodeArgs& a, dim3 grid,
                 hipStream_t st) {
 #if TQ_BK == 16
-  return bv == 16 ? go_g<16>(gk, 0, wide, a, grid, st) : TQ_ERR_UNSUPPORTED;
+  return bv == 16 ? go_g<16>(gk, 0, mx, a, grid, st) : TQ_ERR_UNSUPPORTED;
 #else
   switch (bv) {
-    case 2: return go_g<2>(gk, qjl, wide, a, grid, st);
-    case 3: return go_g<3>(gk, qjl, wide, a, grid, st);
-    case 4: return go_g<4>(gk, qjl, wide, a, grid, st);
+    case 2: return go_g<2>(gk, qjl, mx, a, grid, st);
+    case 3: return go_g<3>(gk, qjl, mx, a, grid, st);
+    case 4: return go_g<4>(gk, qjl, mx, a, grid, st);
     default: return TQ_ERR_UNSUPPORTED;
   }
 #endif

@@ -61,7 +61,7 @@ inline int norm_bytes(const tq_config* cfg) { return cfg->norm_dtype == TQ_F16 ?
 //   tps:    tokens per split (multiple of tile)
 struct DecodePlan {
   int G = 0, gk = 0, chunks = 0, tile = 0, splits = 0;
-  int wide = 0;      // 2: the matrix-core kernel, 0: the workgroup-tile kernel
+  int mx = 0;        // 1: the matrix-core kernel, 0: the workgroup-tile kernel
   int64_t tps = 0;
   // workspace section offsets (bytes)
   size_t off_qp = 0, off_qq = 0, off_ml = 0, off_acc = 0, total = 0;
