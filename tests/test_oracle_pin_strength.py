@@ -1,0 +1,62 @@
+"""The oracle's pins catch plausible mistakes: each test plants one mistake
+in an oracle function (monkeypatched, CPU only, undone after the test) and
+checks that the pin guarding that function fails."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as o
+import oracle.turboquant as ot
+import test_oracle_pins as pins
+
+
+def _fails(pin, *args):
+    with pytest.raises(AssertionError):
+        pin(*args)
+
+
+def test_off_by_one_causal_position_is_caught(monkeypatch):
+    right = o.attend_prefill
+
+    def one_early(q, cache, n_ctx, **kw):   # every query one position too early
+        return right(q, cache, n_ctx - 1, **kw)
+
+    monkeypatch.setattr(o, "attend_prefill", one_early)
+    _fails(pins.test_prefill_rows_equal_brute_force_over_their_prefix, False)
+
+
+def test_wrong_sphere_exponent_is_caught(monkeypatch):
+    def density(z, d):                      # (d-2)/2 instead of (d-3)/2
+        z = np.asarray(z, dtype=np.float64)
+        inside = np.abs(z) < math.sqrt(d)
+        return np.where(inside, np.clip(1.0 - z * z / d, 0.0, None) ** ((d - 2) / 2.0), 0.0)
+
+    monkeypatch.setattr(o, "sphere_density", density)
+    _fails(pins.test_sphere_density_has_unit_variance, 128)
+
+
+def test_other_reading_of_qjl_constant_is_caught(monkeypatch):
+    # sqrt(pi d / 2) in place of sqrt(pi / (2 d)): the factor grows by d
+    monkeypatch.setattr(o, "QJL_CONST", math.pi * 128 * 128 / 2.0)
+    _fails(pins.test_qjl_constant_gaussian_projection_unbiased)
+
+
+def test_rotation_without_sign_flip_is_caught(monkeypatch):
+    def no_signs(x, seed):
+        x = np.asarray(x, dtype=np.float64)
+        return o.fwht(x) / math.sqrt(x.shape[-1])
+
+    monkeypatch.setattr(o, "rht", no_signs)
+    _fails(pins.test_rht_is_orthogonal_and_matches_dense, 128, 0)
+
+
+def test_dropped_qjl_term_is_caught(monkeypatch):
+    right = ot._scores_rot
+
+    def without_qjl(qr, kcodes, knorm, bits_k, tau, qjl=None, sphere=False):
+        return right(qr, kcodes, knorm, bits_k, tau, None, sphere)
+
+    monkeypatch.setattr(ot, "_scores_rot", without_qjl)
+    _fails(pins.test_attention_matches_brute_force, 5, True)
