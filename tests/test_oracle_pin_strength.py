@@ -60,3 +60,36 @@ def test_dropped_qjl_term_is_caught(monkeypatch):
 
     monkeypatch.setattr(ot, "_scores_rot", without_qjl)
     _fails(pins.test_attention_matches_brute_force, 5, True)
+
+
+def test_ties_going_down_are_caught(monkeypatch):
+    def strict(z, thresholds):              # z > t instead of z >= t
+        z = np.asarray(z, dtype=np.float64)
+        return (z[..., None] > thresholds).sum(axis=-1).astype(np.uint8)
+
+    monkeypatch.setattr(o, "quantize", strict)
+    _fails(pins.test_quantize_is_nearest_centroid, 3)
+
+
+def test_truncated_norm_is_caught(monkeypatch):
+    def truncate(n, norm_dtype):            # round toward zero, not to nearest even
+        n = np.asarray(n, dtype=np.float64)
+        r = n.astype(ot._NORM_TYPES[norm_dtype]).astype(np.float64)
+        down = np.nextafter(r.astype(ot._NORM_TYPES[norm_dtype]),
+                            np.zeros_like(r).astype(ot._NORM_TYPES[norm_dtype]))
+        return np.where(r > n, down.astype(np.float64), r)
+
+    monkeypatch.setattr(ot, "round_norm", truncate)
+    _fails(pins.test_encode_zero_vector_and_norm_rounding)
+
+
+def test_msb_first_packing_is_caught(monkeypatch):
+    def msb_first(codes, bits):
+        codes = np.asarray(codes, dtype=np.uint8)
+        d = codes.shape[-1]
+        planes = (codes[..., :, None] >> np.arange(bits, dtype=np.uint8)) & 1
+        stream = planes.reshape(codes.shape[:-1] + (d * bits,))
+        return np.packbits(stream, axis=-1, bitorder="big")
+
+    monkeypatch.setattr(o, "pack_codes", msb_first)
+    _fails(pins.test_pack_hand_worked_examples)
