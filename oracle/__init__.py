@@ -20,3 +20,4 @@ No function here is "parity unpinned".
 """
 
 from .turboquant import *  # noqa: F401,F403
+from .affine import *  # noqa: F401,F403

@@ -93,3 +93,30 @@ def test_msb_first_packing_is_caught(monkeypatch):
 
     monkeypatch.setattr(o, "pack_codes", msb_first)
     _fails(pins.test_pack_hand_worked_examples)
+
+
+def test_affine_bias_at_group_max_is_caught(monkeypatch):
+    import oracle.affine as oa
+
+    def top_bias(y, bits, group=64):                # bias = max, scale negative
+        y = np.asarray(y, dtype=np.float64)
+        d = y.shape[-1]
+        L = (1 << bits) - 1
+        yg = y.reshape(y.shape[:-1] + (d // group, group))
+        hi, lo = yg.max(-1), yg.min(-1)
+        s = ((lo - hi) / L).astype(np.float16).astype(np.float64)
+        b = hi.astype(np.float16).astype(np.float64)
+        u = (yg - b[..., None]) / np.where(s == 0, 1.0, s)[..., None]
+        return np.clip(np.rint(u), 0, L).astype(np.uint8).reshape(y.shape), s, b
+
+    monkeypatch.setattr(oa, "affine_quantize_group_rows", top_bias)
+    monkeypatch.setattr(o, "affine_quantize_group_rows", top_bias)
+    import test_oracle_affine_pins as ap
+    _fails(ap.test_affine_code_is_nearest_level_of_stored_grid, 4)
+
+
+def test_affine_query_rotated_the_wrong_way_is_caught(monkeypatch):
+    import oracle.affine as oa
+    monkeypatch.setattr(oa, "rht", o.rht_inverse)
+    import test_oracle_affine_pins as ap
+    _fails(ap.test_affine_attention_equals_dense_softmax_in_original_frame, 1)
