@@ -2,8 +2,9 @@
 
 The work happens in libtq.so (hand-written HIP, C ABI in include/tq.h); this
 package is its thin ctypes binding. See binding.py for the entry points:
-tq_rht, tq_encode_kv, tq_qjl_sketch, tq_attend_decode, tq_append_attend_decode
-(+ host helpers).
+tq_rht, tq_encode_kv, tq_qjl_sketch, tq_attend_decode, tq_append_attend_decode,
+tq_attend_prefill, the group-affine variant tq_affine_encode_kv /
+tq_affine_attend_decode (+ host helpers).
 """
 
 from .binding import (  # noqa: F401
@@ -15,5 +16,7 @@ from .binding import (  # noqa: F401
     TQ_CODEBOOK_GAUSS, TQ_CODEBOOK_SPHERE,
     tq_dense_decode_bf16, tq_dense_workspace_bytes, tq_encode_kv, tq_num_splits,
     tq_qjl_sketch, tq_read_probe, tq_rht, tq_signs, tq_strerror, tq_workspace_bytes,
-    workspace,
+    workspace, AffineCache, AffineConfig, tq_affine_attend_decode, tq_affine_cache_bytes,
+    tq_affine_config, tq_affine_cache, tq_affine_encode_kv, tq_affine_num_splits,
+    tq_affine_workspace_bytes,
 )

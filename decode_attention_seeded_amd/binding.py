@@ -34,7 +34,8 @@ EXPORTS = (
     "tq_encode_kv", "tq_qjl_sketch", "tq_num_splits", "tq_workspace_bytes",
     "tq_attend_decode", "tq_append_attend_decode", "tq_dense_workspace_bytes",
     "tq_dense_decode_bf16", "tq_attend_prefill", "tq_read_probe_sink_words",
-    "tq_read_probe",
+    "tq_read_probe", "tq_affine_cache_bytes", "tq_affine_encode_kv", "tq_affine_num_splits",
+    "tq_affine_workspace_bytes", "tq_affine_attend_decode",
     "tq_strerror",
 )
 
@@ -58,6 +59,17 @@ class tq_cache(ctypes.Structure):
                 ("B", ctypes.c_int), ("Hkv", ctypes.c_int), ("capacity", ctypes.c_int64)]
 
 
+class tq_affine_config(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int), ("bits_k", ctypes.c_int), ("bits_v", ctypes.c_int),
+                ("group", ctypes.c_int), ("seed", ctypes.c_uint64)]
+
+
+class tq_affine_cache(ctypes.Structure):
+    _fields_ = [("kc", ctypes.c_void_p), ("vc", ctypes.c_void_p), ("ks", ctypes.c_void_p),
+                ("kb", ctypes.c_void_p), ("vs", ctypes.c_void_p), ("vb", ctypes.c_void_p),
+                ("B", ctypes.c_int), ("Hkv", ctypes.c_int), ("capacity", ctypes.c_int64)]
+
+
 _LIB = None
 
 
@@ -73,6 +85,7 @@ def _lib():
                                     ctypes.c_uint64, ctypes.c_float, ctypes.c_double,
                                     ctypes.c_size_t)
         CFG, CACHE = ctypes.POINTER(tq_config), ctypes.POINTER(tq_cache)
+        ACFG, ACACHE = ctypes.POINTER(tq_affine_config), ctypes.POINTER(tq_affine_cache)
         sig = {
             "tq_bits_split": (I, [D, I, ctypes.POINTER(I), ctypes.POINTER(I), ctypes.POINTER(I)]),
             "tq_codebook": (I, [I, P, P]),
@@ -92,6 +105,11 @@ def _lib():
             "tq_attend_prefill": (I, [CFG, P, I, I, I, I64, CACHE, I64, F, P, P]),
             "tq_read_probe_sink_words": (I64, [I64]),
             "tq_read_probe": (I, [P, I64, P, P]),
+            "tq_affine_cache_bytes": (I64, [ACFG, I, I, I64, P]),
+            "tq_affine_encode_kv": (I, [ACFG, P, P, I, I64, I64, ACACHE, P]),
+            "tq_affine_num_splits": (I, [ACFG, I, I, I, I64, I]),
+            "tq_affine_workspace_bytes": (I64, [ACFG, I, I, I, I64, I]),
+            "tq_affine_attend_decode": (I, [ACFG, P, I, I, I, ACACHE, I64, F, I, P, P, SZ, P]),
             "tq_strerror": (ctypes.c_char_p, [I]),
         }
         for name, (res, args) in sig.items():
@@ -365,3 +383,92 @@ def workspace(nbytes: int, device="cuda"):
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+# ---------------------------------------------------------------------------
+# Group-affine variant (rotated keys, group 64, fp16 scale and bias)
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class AffineConfig:
+    d: int = 128
+    bits_k: int = 4
+    bits_v: int = 4
+    group: int = 64
+    seed: int = 0
+
+    def c(self) -> tq_affine_config:
+        return tq_affine_config(self.d, self.bits_k, self.bits_v, self.group, self.seed)
+
+
+def tq_affine_cache_bytes(cfg: AffineConfig, B: int, Hkv: int, capacity: int):
+    planes = (ctypes.c_int64 * 6)()
+    total = _check(_lib().tq_affine_cache_bytes(ctypes.byref(cfg.c()), B, Hkv, capacity,
+                                                ctypes.cast(planes, ctypes.c_void_p)),
+                   "tq_affine_cache_bytes")
+    return total, list(planes)
+
+
+class AffineCache:
+    """Device planes of an affine cache [B][Hkv][capacity]; see tq_affine_cache in tq.h."""
+
+    def __init__(self, cfg: AffineConfig, B: int, Hkv: int, capacity: int, device="cuda"):
+        import torch
+        self.cfg, self.B, self.Hkv, self.capacity = cfg, B, Hkv, capacity
+        _, p = tq_affine_cache_bytes(cfg, B, Hkv, capacity)
+        shape = (B, Hkv, capacity)
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.kc = torch.empty(shape + (cfg.d * cfg.bits_k // 8,), **u8)
+        self.vc = torch.empty(shape + (cfg.d * cfg.bits_v // 8,), **u8)
+        f16 = dict(dtype=torch.float16, device=device)
+        ng = cfg.d // cfg.group
+        self.ks, self.kb, self.vs, self.vb = (torch.empty(shape + (ng,), **f16) for _ in range(4))
+        assert self.kc.numel() == p[0] and self.vc.numel() == p[1]
+        assert all(t.numel() * 2 == p[2 + i]
+                   for i, t in enumerate((self.ks, self.kb, self.vs, self.vb)))
+
+    def c(self) -> tq_affine_cache:
+        return tq_affine_cache(*(t.data_ptr() for t in
+                                 (self.kc, self.vc, self.ks, self.kb, self.vs, self.vb)),
+                               self.B, self.Hkv, self.capacity)
+
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in
+                   (self.kc, self.vc, self.ks, self.kb, self.vs, self.vb))
+
+
+def tq_affine_encode_kv(cfg: AffineConfig, k, v, offset: int, cache: AffineCache, stream=None):
+    """Encode k, v [B][Hkv][n_new][d] at token positions [offset, offset+n_new)."""
+    if k.shape != v.shape or k.dtype != v.dtype:
+        raise TqError(TQ_ERR_ARG, "tq_affine_encode_kv: k and v differ in shape or dtype")
+    if k.dim() != 4 or k.shape[0] != cache.B or k.shape[1] != cache.Hkv or k.shape[3] != cfg.d:
+        raise TqError(TQ_ERR_ARG, "tq_affine_encode_kv: k must be [B][Hkv][n_new][d]")
+    if not (k.is_contiguous() and v.is_contiguous()):
+        raise TqError(TQ_ERR_ARG, "tq_affine_encode_kv: k and v must be contiguous")
+    c = cache.c()
+    _check(_lib().tq_affine_encode_kv(ctypes.byref(cfg.c()), _ptr(k), _ptr(v), _dtype_code(k),
+                                      offset, k.shape[2], ctypes.byref(c), _stream(stream)),
+           "tq_affine_encode_kv")
+
+
+def tq_affine_num_splits(cfg: AffineConfig, B, Hq, Hkv, n_ctx, splits=0):
+    return _check(_lib().tq_affine_num_splits(ctypes.byref(cfg.c()), B, Hq, Hkv, n_ctx, splits),
+                  "tq_affine_num_splits")
+
+
+def tq_affine_workspace_bytes(cfg: AffineConfig, B, Hq, Hkv, n_ctx, splits=0):
+    return _check(_lib().tq_affine_workspace_bytes(ctypes.byref(cfg.c()), B, Hq, Hkv, n_ctx,
+                                                   splits), "tq_affine_workspace_bytes")
+
+
+def tq_affine_attend_decode(cfg: AffineConfig, q, cache: AffineCache, n_ctx: int, out, ws,
+                            scale: float = 0.0, splits: int = 0, stream=None):
+    """out [B][Hq][d] fp32 = attention of q [B][Hq][d] over the first n_ctx affine tokens."""
+    B, Hq, d = q.shape
+    if d != cfg.d or not q.is_contiguous() or tuple(out.shape) != (B, Hq, d):
+        raise TqError(TQ_ERR_ARG, "tq_affine_attend_decode: q/out must be [B][Hq][d] contiguous")
+    c = cache.c()
+    _check(_lib().tq_affine_attend_decode(ctypes.byref(cfg.c()), _ptr(q), _dtype_code(q), B, Hq,
+                                          ctypes.byref(c), n_ctx, float(scale), splits,
+                                          _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                          _stream(stream)), "tq_affine_attend_decode")

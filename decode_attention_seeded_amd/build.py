@@ -41,6 +41,7 @@ def _jobs():
                        "-I", os.path.join(ROCM, "include"), "-I", os.path.join(ROOT, "include"),
                        "-c", os.path.join(CSRC, "tq_host.cpp")]),
         ("tq_api.o", [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "tq_api.hip")]),
+        ("tq_affine.o", [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "tq_affine.hip")]),
     ]
     for d, bk in DECODE_VARIANTS:
         jobs.append((f"tq_decode_d{d}_k{bk}.o",

@@ -280,6 +280,68 @@ int tq_dense_decode_bf16(const void* q, const void* k, const void* v, int B,
 int64_t tq_read_probe_sink_words(int64_t bytes);
 int tq_read_probe(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
+/*
+ * Group-affine variant (mlx-turboquant README: "Quantize the KV cache" with
+ * kv_group_size = 64; "How it plugs in": the cache is mlx-lm's group-affine
+ * quantized cache with the keys rotated and the query rotated at attention
+ * time; "Memory footprint over long context": the same bytes per token as
+ * the 4-bit codebook cache). Per token and KV head: d codes of b bits
+ * (LSB-first bitstream, as the codebook cache) and, per group of 64
+ * coordinates, an fp16 scale and an fp16 bias. Keys are rotated by R (seed)
+ * first, values are stored in their own frame. Encoding a group y: bias =
+ * fp16(min y), scale = fp16((max y - min y) / (2^b - 1)), code =
+ * round-half-even((y - bias) / scale) clamped to [0, 2^b - 1] (0 when scale
+ * is 0), all in double precision; dequantized value scale * code + bias.
+ */
+typedef struct {
+  int d;              /* head dimension: 128 or 256                           */
+  int bits_k;         /* key code width: 2, 3 or 4                            */
+  int bits_v;         /* value code width: 2, 3 or 4                          */
+  int group;          /* coordinates per scale and bias: must be 64           */
+  uint64_t seed;      /* SplitMix64 seed of the key rotation signs            */
+} tq_affine_config;
+
+/* Device planes (caller-owned, 16-byte aligned), rows [B][Hkv][capacity]:
+ * kc, vc: d*bits/8 bytes per row; ks, kb, vs, vb: d/64 fp16 per row. */
+typedef struct {
+  void* kc;
+  void* vc;
+  void* ks;
+  void* kb;
+  void* vs;
+  void* vb;
+  int B;
+  int Hkv;
+  int64_t capacity;
+} tq_affine_cache;
+
+/* Total bytes of the six planes; plane_bytes[6] (kc, vc, ks, kb, vs, vb) may
+ * be NULL. Negative tq_status on bad arguments. Host only. */
+int64_t tq_affine_cache_bytes(const tq_affine_config* cfg, int B, int Hkv,
+                              int64_t capacity, int64_t* plane_bytes);
+
+/* Encode n_new tokens of K and V into rows [offset, offset + n_new) of every
+ * (b, h); k, v: [B][Hkv][n_new][d] of in_dtype, 16-byte aligned. Same
+ * argument rules and errors as tq_encode_kv. */
+int tq_affine_encode_kv(const tq_affine_config* cfg, const void* k, const void* v,
+                        int in_dtype, int64_t offset, int64_t n_new,
+                        const tq_affine_cache* cache, hipStream_t stream);
+
+/* Split count and workspace bytes of tq_affine_attend_decode. */
+int tq_affine_num_splits(const tq_affine_config* cfg, int B, int Hq, int Hkv,
+                         int64_t n_ctx, int splits);
+int64_t tq_affine_workspace_bytes(const tq_affine_config* cfg, int B, int Hq,
+                                  int Hkv, int64_t n_ctx, int splits);
+
+/* Decode attention over the first n_ctx tokens of an affine cache:
+ * out[b][h] = sum_j softmax_j(scale * <R q, y_hat_j>) v_hat_j, fp32, with
+ * y_hat the dequantized rotated keys and v_hat the dequantized values.
+ * Arguments, workspace and errors as tq_attend_decode. */
+int tq_affine_attend_decode(const tq_affine_config* cfg, const void* q, int q_dtype,
+                            int B, int Hq, const tq_affine_cache* cache,
+                            int64_t n_ctx, float scale, int splits, float* out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Human-readable name of a tq_status. Never NULL. */
 const char* tq_strerror(int status);
 

@@ -294,3 +294,34 @@ def test_prefill_validation():
     assert call(q=MIS) == tq.TQ_ERR_ALIGN
     assert call(out=MIS) == tq.TQ_ERR_ALIGN
     assert call(B=0, cache=_cache(B=0)) == tq.TQ_OK
+
+
+def test_affine_sizes_and_validation():
+    cfg = tq.AffineConfig(d=128, bits_k=4, bits_v=4, group=64, seed=3)
+    total, planes = tq.tq_affine_cache_bytes(cfg, 2, 8, 100)
+    assert planes == [2 * 8 * 100 * 64, 2 * 8 * 100 * 64] + [2 * 8 * 100 * 2 * 2] * 4
+    assert total == 2 * 8 * 100 * o.affine_cache_bytes_per_token(128, 4, 4)
+    lib = tq.lib()
+    for bad in (dict(group=32), dict(bits_k=5), dict(bits_v=1), dict(d=64)):
+        c = tq.AffineConfig(**{**dict(d=128, bits_k=4, bits_v=4, group=64), **bad})
+        assert lib.tq_affine_cache_bytes(ctypes.byref(c.c()), 1, 1, 1, None) == tq.TQ_ERR_UNSUPPORTED
+    c = ctypes.byref(cfg.c())
+    assert lib.tq_affine_num_splits(c, 1, 32, 8, 524288, 0) >= 1
+    assert lib.tq_affine_num_splits(c, 1, 30, 8, 1000, 0) == tq.TQ_ERR_ARG      # Hq % Hkv
+    assert lib.tq_affine_workspace_bytes(c, 1, 8, 8, 0, 0) == tq.TQ_ERR_ARG     # n_ctx 0
+    # splits never exceed one per 256 tokens; tokens per split are whole tiles
+    assert lib.tq_affine_num_splits(c, 1, 8, 8, 300, 1000) == 2
+    cache = tq.tq_affine_cache(16, 16, 16, 16, 16, 16, 1, 1, 10)
+    q = out = ws = ctypes.c_void_p(16)
+    st = lib.tq_affine_attend_decode(c, q, 0, 1, 1, ctypes.byref(cache), 11, 0.0, 0, out, ws,
+                                     1 << 20, None)
+    assert st == tq.TQ_ERR_CAPACITY
+    st = lib.tq_affine_attend_decode(c, q, 0, 1, 1, ctypes.byref(cache), 10, 0.0, 0, out, ws,
+                                     16, None)
+    assert st == tq.TQ_ERR_WORKSPACE
+    st = lib.tq_affine_encode_kv(c, q, q, 0, 5, 6, ctypes.byref(cache), None)
+    assert st == tq.TQ_ERR_CAPACITY
+    bad_align = tq.tq_affine_cache(16, 17, 16, 16, 16, 16, 1, 1, 10)
+    st = lib.tq_affine_encode_kv(c, q, q, 0, 0, 1, ctypes.byref(bad_align), None)
+    assert st == tq.TQ_ERR_ALIGN
+    assert lib.tq_affine_encode_kv(c, q, q, 0, 0, 0, ctypes.byref(cache), None) == tq.TQ_OK
