@@ -125,6 +125,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-affine", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0,
                     help="context tokens of the CPU-oracle sample (0: the whole context "
                          "of one KV head)")
@@ -319,6 +320,37 @@ def main():
         del qc, pout
         log(f"prefill of {nq} tokens over {w.N}: {pms:.2f} ms, {prefill['tflops']} TFLOP/s")
 
+    # the group-affine variant (group 64, fp16 scale and bias, rotated keys)
+    # at 4 bits, the README's iso-byte comparison format, on the same K/V
+    # and query; bytes = its six planes over N tokens plus q in and out
+    affine = None
+    if not args.no_affine:
+        acfg = tq.AffineConfig(d=w.d, bits_k=4, bits_v=4, group=64, seed=w.seed)
+        acache = tq.AffineCache(acfg, w.B, w.Hkv, w.N)
+        tq.tq_affine_encode_kv(acfg, K, V, 0, acache)
+        aws = tq.workspace(tq.tq_affine_workspace_bytes(acfg, w.B, w.Hq, w.Hkv, w.N))
+        aout = torch.empty_like(out)
+        for _ in range(3):
+            tq.tq_affine_attend_decode(acfg, q, acache, w.N, aout, aws)
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(20):
+            tq.tq_affine_attend_decode(acfg, q, acache, w.N, aout, aws)
+        b.record()
+        torch.cuda.synchronize()
+        aus = a.elapsed_time(b) / 20 * 1e3
+        abytes = acache.nbytes() + q.numel() * q.element_size() + aout.numel() * 4
+        affine = {"format": "K4/V4 group-64 affine, fp16 scale and bias, rotated keys",
+                  "us_per_call": round(aus, 2),
+                  "kv_tokens_per_s": round(w.B * w.N / (aus * 1e-6), 1),
+                  "algorithmic_bytes": abytes,
+                  "gbps": round(abytes / aus / 1e3, 1),
+                  "frac_of_hbm_peak": round(abytes / aus / 1e3 / HBM_PEAK_GBPS, 4),
+                  "finite": bool(torch.isfinite(aout).all())}
+        del acache, aws, aout
+        log(f"affine K4V4 decode: {aus:.1f} us/call, {affine['gbps']} GB/s")
+
     # algorithmic bytes of one decode call: every packed plane over N tokens,
     # plus q in and out
     alg_bytes = alg_bytes_of(tq, cfg, w, q)
@@ -402,6 +434,7 @@ def main():
         "algorithmic_bytes_per_decode": alg_bytes,
         "dense_bf16": dense,
         "prefill": prefill,
+        "affine": affine,
         "source_hash": source_hash(),
     }
     print(json.dumps(rec), flush=True)
