@@ -15,9 +15,10 @@
 // partials are merged by the codebook path's log-sum-exp merge kernel.
 //   scores  lane = token: s_g = sum_grp scale_grp * (q'_g . codes)_grp
 //           + bias_grp * (sum of q'_g over the group), q' = R q * tau * log2 e
-//   values  lane = d/64 consecutive coordinates: the wave's 64 value rows are
-//           staged in its own LDS slot and each lane reads its bits of
-//           every row; o_c = sum_t p_t scale_t code_tc + sum_t p_t bias_t.
+//   values  lane = (quarter of the tile's tokens, d/16 consecutive
+//           coordinates): the wave's 64 value rows are staged in its own LDS
+//           slot and each lane reads its bits of its 16 rows; o_c = sum_t
+//           p_t scale_t code_tc + sum_t p_t bias_t, quarters summed at the end.
 #include <algorithm>
 #include <cmath>
 
@@ -143,8 +144,9 @@ __global__ void __launch_bounds__(64 * kAffWaves) k_affine_decode(AffDecodeArgs 
   constexpr int KW = KREC / 4;
   constexpr int VLD = VREC / 16;               // 16-byte value loads per lane
   constexpr int VS = VREC + 16;                // staged row stride (bytes)
-  constexpr int CPL = D / 64;                  // value coordinates per lane
-  constexpr int LB = CPL * BV;                 // value bits per lane and row
+  constexpr int CPL = D / 16;                  // value coordinates per lane
+  constexpr int LB = CPL * BV;                 // value bits per lane and row (<= 64)
+  constexpr int TQ = kAffTile / 4;             // tokens per lane quarter
   static_assert(KREC % 16 == 0 && VREC % 16 == 0, "records are whole 16-byte loads");
 
   __shared__ __attribute__((aligned(16))) float qs[GK][D];
@@ -245,7 +247,10 @@ __global__ void __launch_bounds__(64 * kAffWaves) k_affine_decode(AffDecodeArgs 
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
   uint8_t* my_v = vst[wave];
-  const int vgrp = (lane * CPL) / kAffGroup;        // the lane's value group
+  // value phase: lane = (token quarter lane / 16, coordinates
+  // CPL * (lane % 16) .. + CPL - 1); the quarters are summed at the end
+  const int vcg = lane & 15, vtq = lane >> 4;
+  const int vgrp = (vcg * CPL) / kAffGroup;          // the lane's value group
   const float* qrow = qs[hg];
 
   auto process = [&](int64_t base, const Tile& t) {
@@ -295,26 +300,24 @@ __global__ void __launch_bounds__(64 * kAffWaves) k_affine_decode(AffDecodeArgs 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- values: lane = CPL consecutive coordinates
-    const uint32_t bit0 = uint32_t(lane) * LB;
+    // ---- values: the lane's CPL coordinates over its 16 tokens
+    const uint32_t bit0 = uint32_t(vcg) * LB;
     const uint32_t wsel = (bit0 >> 5) * 4, sh = bit0 & 31;
-#pragma unroll 4
-    for (int j = 0; j < kAffTile; ++j) {
+#pragma unroll 2
+    for (int jj = 0; jj < TQ; ++jj) {
+      const int j = vtq * TQ + jj;
       const uint8_t* rowp = my_v + j * VS + wsel;
-      uint32_t x = *reinterpret_cast<const uint32_t*>(rowp);
-      if (sh + LB > 32) {
-        const uint32_t y = *reinterpret_cast<const uint32_t*>(rowp + 4);
-        x = __builtin_amdgcn_alignbit(y, x, sh);
-      } else {
-        x >>= sh;
-      }
+      uint64_t x = *reinterpret_cast<const uint32_t*>(rowp);
+      if (sh + LB > 32) x |= uint64_t(*reinterpret_cast<const uint32_t*>(rowp + 4)) << 32;
+      x >>= sh;
+      if (sh + LB > 64) x |= uint64_t(*reinterpret_cast<const uint32_t*>(rowp + 8)) << (64 - sh);
       const float2 sb = vsb[wave][j][vgrp];
       const float pj = pw[wave][j];
       const float ws = pj * sb.x;
       accb = fmaf(pj, sb.y, accb);
 #pragma unroll
       for (int c = 0; c < CPL; ++c)
-        acc[c] = fmaf(ws, float((x >> (c * BV)) & ((1u << BV) - 1u)), acc[c]);
+        acc[c] = fmaf(ws, float(uint32_t(x >> (c * BV)) & ((1u << BV) - 1u)), acc[c]);
     }
     // the slot is rewritten by the next tile of this wave
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -351,9 +354,19 @@ __global__ void __launch_bounds__(64 * kAffWaves) k_affine_decode(AffDecodeArgs 
 #pragma unroll
   for (int w = hg; w < W; w += GK) M = fmaxf(M, mlx[w][0]);
   {
-    const float f = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+    // sum the four token quarters (lanes vcg, vcg + 16, vcg + 32, vcg + 48)
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) slab[wave][lane * CPL + c] = (acc[c] + accb) * f;
+    for (int c = 0; c < CPL; ++c) {
+      acc[c] += __shfl_xor(acc[c], 16);
+      acc[c] += __shfl_xor(acc[c], 32);
+    }
+    accb += __shfl_xor(accb, 16);
+    accb += __shfl_xor(accb, 32);
+    const float f = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+    if (vtq == 0) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) slab[wave][vcg * CPL + c] = (acc[c] + accb) * f;
+    }
   }
   __syncthreads();
   for (int i = tid; i < GK * D; i += 64 * W) {
