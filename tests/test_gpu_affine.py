@@ -67,14 +67,14 @@ def _compare_encode(w, cache, ref, fv, n):
     log(f"encode parity: {int(bad_k.sum())} key rows in the band, {differ} plane rows differ there")
 
 
-def _decode(w, cfg, cache, n_ctx, splits=0):
+def _decode(w, cfg, cache, n_ctx, splits=0, scale=0.0):
     import decode_attention_seeded_amd as tq
     torch = torch_cuda()
     qraw, qf = si.queries(w)
     q = to_device(qraw, w.in_dtype)
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
     ws = tq.workspace(tq.tq_affine_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, n_ctx, splits))
-    tq.tq_affine_attend_decode(cfg, q, cache, n_ctx, out, ws, splits=splits)
+    tq.tq_affine_attend_decode(cfg, q, cache, n_ctx, out, ws, scale=scale, splits=splits)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.float64), np.asarray(qf, np.float64)
 
@@ -137,3 +137,25 @@ def test_affine_long_context_sampled_heads():
     err, abs_err = rel_err(got, want)
     log(f"  row-relative {err:.2e} (abs {abs_err:.2e})")
     assert err <= TOL
+
+
+def test_affine_explicit_scale_and_split_counts():
+    # an explicit softmax scale, and requested split counts from 1 to far
+    # more than the context has tiles (the library clamps them); every
+    # result against the oracle and all split counts against each other
+    w = si.small_workload(wid=340, B=1, Hq=8, Hkv=4, d=128, N=2000, bits_k=4, bits_v=3)
+    log("affine scale/splits: B=1 Hq=8 Hkv=4 d=128 N=2000 K4V3, scale 0.2, splits 1..5000")
+    cfg, cache = _gpu_encode(w)
+    ref, _, _ = _oracle_cache(w)
+    planes = {k: ref[k] for k in ("kc", "vc", "ks", "kb", "vs", "vb")}
+    outs = []
+    for splits in (1, 3, 8, 5000):
+        got, qf = _decode(w, cfg, cache, w.N, splits=splits, scale=0.2)
+        want = o.affine_attend(qf, planes, w.N, d=w.d, seed=w.seed, bits_k=4, bits_v=3,
+                               Hkv=w.Hkv, scale=0.2)
+        err, _ = rel_err(got, want)
+        log(f"  splits={splits}: row-relative {err:.2e}")
+        assert err <= TOL
+        outs.append(got)
+    for g in outs[1:]:
+        assert rel_err(g, outs[0])[0] < 1e-5
