@@ -151,6 +151,9 @@ __global__ void __launch_bounds__(64 * kAffWaves) k_affine_decode(AffDecodeArgs 
 
   __shared__ __attribute__((aligned(16))) float qs[GK][D];
   __shared__ float qsum[GK][NG];
+  // 4-bit keys: q' as fp16 pairs in the order of the nibble-pair extraction
+  // (pair 4k + m = coordinates 8k + m and 8k + m + 4)
+  __shared__ __attribute__((aligned(16))) uint32_t qh[GK][D / 2];
   __shared__ __attribute__((aligned(16))) uint8_t vst[W][kAffTile * VS];
   __shared__ float2 vsb[W][kAffTile][NG];
   __shared__ float pw[W][kAffTile];
@@ -190,6 +193,12 @@ __global__ void __launch_bounds__(64 * kAffWaves) k_affine_decode(AffDecodeArgs 
       v[i] *= mult;
       qs[g][l16 * E + i] = v[i];
       part += v[i];
+    }
+#pragma unroll
+    for (int kk = 0; kk < E / 8; ++kk) {
+      const int k = l16 * (E / 8) + kk;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) qh[g][4 * k + m] = dev::pack_f16x2(v[8 * kk + m], v[8 * kk + m + 4]);
     }
     // lanes l16 .. of one group: 64 / E consecutive lanes
     constexpr int LPG = kAffGroup / E;
@@ -259,14 +268,34 @@ __global__ void __launch_bounds__(64 * kAffWaves) k_affine_decode(AffDecodeArgs 
     float dots[NG];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) dots[gi] = 0.f;
+    if constexpr (BK == 4) {
+      // two codes per fp16 pair: (nibble | 0x6400) is 1024 + code in fp16,
+      // a packed fp16 subtract leaves the exact codes, and v_dot2 against
+      // the fp16 query pair accumulates in fp32
+      const uint32_t* qhr = qh[hg];
 #pragma unroll
-    for (int i4 = 0; i4 < D / 4; ++i4) {
-      const int gi = (4 * i4) / kAffGroup;
-      const float4 qv = *reinterpret_cast<const float4*>(qrow + 4 * i4);
-      dots[gi] = fmaf(qv.x, float(dev::field<BK>(t.kw, 4 * i4)), dots[gi]);
-      dots[gi] = fmaf(qv.y, float(dev::field<BK>(t.kw, 4 * i4 + 1)), dots[gi]);
-      dots[gi] = fmaf(qv.z, float(dev::field<BK>(t.kw, 4 * i4 + 2)), dots[gi]);
-      dots[gi] = fmaf(qv.w, float(dev::field<BK>(t.kw, 4 * i4 + 3)), dots[gi]);
+      for (int k = 0; k < KW; ++k) {
+        const int gi = (8 * k) / kAffGroup;
+        const uint4 qq = *reinterpret_cast<const uint4*>(qhr + 4 * k);
+        const uint32_t qm[4] = {qq.x, qq.y, qq.z, qq.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t cp = ((t.kw[k] >> (4 * m)) & 0x000F000Fu) | 0x64006400u;
+          const dev::half2_t ch =
+              __builtin_bit_cast(dev::half2_t, cp) - dev::half2_t{_Float16(1024.f), _Float16(1024.f)};
+          dots[gi] = dev::dot2(qm[m], __builtin_bit_cast(uint32_t, ch), dots[gi]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i4 = 0; i4 < D / 4; ++i4) {
+        const int gi = (4 * i4) / kAffGroup;
+        const float4 qv = *reinterpret_cast<const float4*>(qrow + 4 * i4);
+        dots[gi] = fmaf(qv.x, float(dev::field<BK>(t.kw, 4 * i4)), dots[gi]);
+        dots[gi] = fmaf(qv.y, float(dev::field<BK>(t.kw, 4 * i4 + 1)), dots[gi]);
+        dots[gi] = fmaf(qv.z, float(dev::field<BK>(t.kw, 4 * i4 + 2)), dots[gi]);
+        dots[gi] = fmaf(qv.w, float(dev::field<BK>(t.kw, 4 * i4 + 3)), dots[gi]);
+      }
     }
     // ---- stage the value tile and its scales in this wave's LDS slot
 #pragma unroll
