@@ -475,7 +475,9 @@ int aff_plan(const tq_affine_config* c, int B, int Hq, int Hkv, int64_t n_ctx, i
   const int64_t units = int64_t(B) * Hkv * p->chunks;
   const int64_t round = int64_t(kAffWaves) * kAffTile;
   const int64_t max_s = std::min<int64_t>(kMaxSplitCount, (n_ctx + round - 1) / round);
-  int64_t S = splits > 0 ? splits : (1024 + units - 1) / units;
+  // about 2048 workgroups by default (8 per compute unit, two resident at
+  // a time): measured fastest for long contexts
+  int64_t S = splits > 0 ? splits : (2048 + units - 1) / units;
   S = std::max<int64_t>(1, std::min(S, max_s));
   int64_t tps = (n_ctx + S - 1) / S;
   tps = (tps + kAffTile - 1) / kAffTile * kAffTile;
