@@ -4,8 +4,9 @@ workload bulk encode followed by the 4096-token append).
 
 The oracle cannot redo whole contexts element by element, so it checks
 * the packed codes, norms and QJL bits of a random sample of rows, and
-* the attention output of sampled query heads over the FULL context, from
-  the oracle's own streamed encode of that KV head (blocks of 65536 tokens,
+* the attention output over the FULL context of every query head of two KV
+  heads (the first of batch 0, the last of the last batch), from the
+  oracle's own streamed encode of each KV head (blocks of 65536 tokens,
   rotated frame, exact log-sum-exp merge).
 Bars as in test_gpu_parity.py."""
 
@@ -133,8 +134,10 @@ def test_full_size_workload(wid):
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
-    # first and last query head of KV head 0 (one oracle pass), last head overall
-    heads = sorted({(0, 0), (0, w.G - 1), (w.B - 1, w.Hq - 1)})
+    # every query head of KV head 0 of batch 0 and of the last KV head of the
+    # last batch (one oracle pass per KV head)
+    heads = sorted({(0, h) for h in range(w.G)} |
+                   {(w.B - 1, h) for h in range(w.Hq - w.G, w.Hq)})
     want = _oracle_heads(w, qf, heads)
     worst = 0.0
     for b, h in heads:
@@ -148,9 +151,9 @@ def test_full_size_workload(wid):
 def test_full_size_prefill_sampled_rows():
     """The causal prefill bench.py times: the 4096 appended tokens of the
     long-context workload attend over its 524288-token cache. Sampled query
-    rows (chunk start, middle and end; first and last head of KV head 0 and
-    the last head overall) against the oracle's streamed attention over each
-    row's own prefix."""
+    rows (chunk start, middle and end) against the oracle's streamed attention over each
+    row's own prefix. Every query head of KV head 0 and of the last KV head
+    at each sampled row."""
     import decode_attention_seeded_amd as tq
     torch = torch_cuda()
     w = si.WORKLOADS[4]
@@ -177,7 +180,8 @@ def test_full_size_prefill_sampled_rows():
         full = memo[key]
         return {k: v[t0 - base:t1 - base] for k, v in full.items()}
 
-    samples = [(0, [0, w.G - 1]), (n_q // 2 - 1, [0, w.G - 1]), (n_q - 1, [0, w.G - 1, w.Hq - 1])]
+    hs_all = list(range(w.G)) + list(range(w.Hq - w.G, w.Hq))
+    samples = [(0, hs_all), (n_q // 2 - 1, hs_all), (n_q - 1, hs_all)]
     worst = 0.0
     for i, hs in samples:
         n_ctx = w.N - n_q + i + 1

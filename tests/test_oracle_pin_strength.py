@@ -120,3 +120,49 @@ def test_affine_query_rotated_the_wrong_way_is_caught(monkeypatch):
     monkeypatch.setattr(oa, "rht", o.rht_inverse)
     import test_oracle_affine_pins as ap
     _fails(ap.test_affine_attention_equals_dense_softmax_in_original_frame, 1)
+
+
+def test_boundary_band_too_wide_is_caught(monkeypatch):
+    right = o.boundary_mask
+
+    def wide(z, thresholds, eps=1e-6):                  # eps 1e4 times too wide
+        return right(z, thresholds, eps * 1e4)
+
+    monkeypatch.setattr(o, "boundary_mask", wide)
+    _fails(pins.test_boundary_mask_is_the_1e6_band_in_z_units, 3)
+
+
+def test_boundary_band_relative_to_threshold_is_caught(monkeypatch):
+    def relative(z, thresholds, eps=1e-6):              # eps * |t_k|: no band at t = 0
+        z = np.asarray(z, dtype=np.float64)
+        return (np.abs(z[..., None] - thresholds) < eps * np.abs(thresholds)).any(axis=-1)
+
+    monkeypatch.setattr(o, "boundary_mask", relative)
+    _fails(pins.test_boundary_mask_is_the_1e6_band_in_z_units, 3)
+
+
+def test_boundary_band_in_rotated_units_is_caught(monkeypatch):
+    def rotated_units(z, thresholds, eps=1e-6):         # |y - t/sqrt(d)| < eps, d = 128
+        z = np.asarray(z, dtype=np.float64) / math.sqrt(128)
+        return (np.abs(z[..., None] - thresholds / math.sqrt(128)) < eps).any(axis=-1)
+
+    monkeypatch.setattr(o, "boundary_mask", rotated_units)
+    _fails(pins.test_boundary_mask_is_the_1e6_band_in_z_units, 4)
+
+
+def test_qjl_band_too_wide_is_caught(monkeypatch):
+    right = o.qjl_boundary_mask
+
+    def wide(w, rnorm_exact, rel=1e-6):
+        return right(w, rnorm_exact, rel * 1e4)
+
+    monkeypatch.setattr(o, "qjl_boundary_mask", wide)
+    _fails(pins.test_qjl_boundary_mask_is_the_band_relative_to_the_residual_norm)
+
+
+def test_qjl_band_not_scaled_by_residual_norm_is_caught(monkeypatch):
+    def absolute(w, rnorm_exact, rel=1e-6):             # |w| < 1e-6, ignoring ||r||
+        return np.abs(w) < rel
+
+    monkeypatch.setattr(o, "qjl_boundary_mask", absolute)
+    _fails(pins.test_qjl_boundary_mask_is_the_band_relative_to_the_residual_norm)

@@ -139,6 +139,49 @@ def test_quantize_is_nearest_centroid(bits):
     assert o.quantize(np.array([0.0]), t)[0] == 2 ** (bits - 1)
 
 
+# ------------------------------------------------------ decision bands
+# The parity tests accept either adjacent code for a coordinate whose
+# scaled rotated value z lies within 1e-6 of a threshold (z units), and
+# either sign bit for a QJL coordinate with |w| < 1e-6 ||r||. These pins tie
+# the two band helpers to that definition: fixed points just inside and
+# outside the band, and the band equals the set where moving z (or w) by
+# the band half-width changes the pinned quantizer's code (or the sign).
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_boundary_mask_is_the_1e6_band_in_z_units(bits):
+    c, t = o.lloyd_max(bits)
+    inside = np.concatenate([t - 5e-7, t + 5e-7])
+    outside = np.concatenate([t - 2e-6, t + 2e-6])
+    assert o.boundary_mask(inside, t).all()
+    assert not o.boundary_mask(outside, t).any()
+    assert not o.boundary_mask(c, t).any()               # cell centres
+    assert o.boundary_mask(np.array([0.0, -3e-7, 9e-7]), t).all()   # t_mid = 0
+    rng = np.random.default_rng(40 + bits)
+    z = np.concatenate([t[rng.integers(0, len(t), 20000)] + rng.uniform(-4e-6, 4e-6, 20000),
+                        rng.standard_normal(20000) * 1.5])
+    eps = 1e-6
+    moved = o.quantize(z + eps, t) != o.quantize(z - eps, t)
+    assert np.array_equal(o.boundary_mask(z, t), moved)
+    assert 0.1 < moved.mean() < 0.9
+    # a [rows][d] array is flagged per coordinate
+    zz = z[:1280].reshape(10, 128)
+    assert np.array_equal(o.boundary_mask(zz, t), moved[:1280].reshape(10, 128))
+
+
+def test_qjl_boundary_mask_is_the_band_relative_to_the_residual_norm():
+    rn = np.array([1e-3, 1.0, 50.0])                     # ||r|| per row
+    inside = np.array([[0.5e-6, -0.5e-6, 0.0, 0.9e-6]]) * rn[:, None]
+    outside = np.array([[2e-6, -2e-6, 1.1e-6, -5.0]]) * rn[:, None]
+    assert o.qjl_boundary_mask(inside, rn).all()
+    assert not o.qjl_boundary_mask(outside, rn).any()
+    rng = np.random.default_rng(44)
+    w = rng.uniform(-4e-6, 4e-6, (3, 4096)) * rn[:, None]
+    band = 1e-6 * rn[:, None]
+    flips = (w + band < 0) != (w - band < 0)
+    assert np.array_equal(o.qjl_boundary_mask(w, rn), flips)
+    assert 0.1 < flips.mean() < 0.9
+
+
 # ------------------------------------------------------------------ encode
 
 @pytest.mark.parametrize("bits,d", [(2, 256), (3, 128), (4, 128)])
