@@ -9,7 +9,6 @@ decode_attention_seeded_amd.build`); there is no fallback path.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 
@@ -376,13 +375,11 @@ def tq_read_probe(src, sink=None, stream=None):
 
 
 def workspace(nbytes: int, device="cuda"):
-    """A device byte buffer of at least nbytes (16-byte aligned by torch)."""
+    """A zeroed device byte buffer of at least nbytes (16-byte aligned by
+    torch). Decode workspaces must be zero before their first use; the
+    library leaves them that way after every call."""
     import torch
-    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
-
-
-def default_scale(d: int) -> float:
-    return 1.0 / math.sqrt(d)
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------------------

@@ -149,8 +149,8 @@ void fill_encode_args(const tq_config* cfg, const void* k, const void* v, int in
 // Shared tail of the packed and dense decode paths: q preparation, split-K
 // kernel, merge.
 int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs da,
-               QPrepArgs qa, int B, int Hq, int Hkv, void* ws, float* out, int rotate,
-               uint64_t seed, hipStream_t st) {
+               QPrepArgs qa, int B, int Hq, int Hkv, void* ws, float* out, uint64_t seed,
+               hipStream_t st) {
   char* w = static_cast<char*>(ws);
   qa.qp = reinterpret_cast<float*>(w + p.off_qp);
   qa.qq = qjl ? reinterpret_cast<float*>(w + p.off_qq) : nullptr;
@@ -158,6 +158,8 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
   da.qq = qa.qq;
   da.ml = reinterpret_cast<float*>(w + p.off_ml);
   da.acc = reinterpret_cast<float*>(w + p.off_acc);
+  da.cnt = reinterpret_cast<uint32_t*>(w + p.off_cnt);
+  da.out = out;
   da.tps = p.tps;
   da.Hkv = Hkv;
   da.Hq = Hq;
@@ -165,7 +167,6 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
   da.chunks = p.chunks;
   da.S = p.splits;
   da.seed = seed;
-  (void)rotate;
   da.q_raw = qa.q;
   da.q_dtype = qa.q_dtype;
   da.qmult = qa.mult;
@@ -178,6 +179,8 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
   dim3 grid(unsigned(p.splits), unsigned(int64_t(B) * Hkv * p.chunks));
   st1 = fn(bv, p.gk, qjl, p.mx, da, grid, st);
   if (st1 != TQ_OK) return st1;
+  // the matrix-core kernel merges its own splits (last workgroup per row)
+  if (p.mx) return TQ_OK;
   MergeArgs ma;
   ma.ml = da.ml;
   ma.acc = da.acc;
@@ -259,7 +262,7 @@ int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
     da.enc = *app;
   }
   return run_decode(cfg->d, cfg->bits_k, cfg->bits_v, cfg->qjl, p, da, qa, B, Hq, cache->Hkv,
-                    ws, out, 1, cfg->seed, stream);
+                    ws, out, cfg->seed, stream);
 }
 
 }  // namespace
@@ -418,7 +421,7 @@ int tq_dense_decode_bf16(const void* q, const void* k, const void* v, int B, int
   da.vc = static_cast<const uint8_t*>(v);
   da.capacity = n_ctx;
   da.n_ctx = n_ctx;
-  return run_decode(d, 16, 16, 0, p, da, qa, B, Hq, Hkv, ws, out, 0, 0, stream);
+  return run_decode(d, 16, 16, 0, p, da, qa, B, Hq, Hkv, ws, out, 0, stream);
 }
 
 int tq_attend_prefill(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,

@@ -207,6 +207,30 @@ __device__ __forceinline__ uint32_t field_at(const uint32_t (&w)[NW], int i) {
   return x & (((1u << BITS) - 1u) << P);
 }
 
+// Device-scope (agent) stores and loads of fp32 values: the stores write
+// through this XCD's L2 and the loads do not hit a stale L2 line, so data a
+// workgroup stores before an arrival count is read correctly by whichever
+// workgroup, on whichever XCD, observes the count.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev2(float* p, float x, float y) {
+  const uint64_t v = uint64_t(__float_as_uint(x)) | (uint64_t(__float_as_uint(y)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void load_dev2(const float* p, float* x, float* y) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  *x = __uint_as_float(uint32_t(v));
+  *y = __uint_as_float(uint32_t(v >> 32));
+}
+
 // Raw buffer descriptor over [p, p + bytes): loads at byte offsets past the
 // range return zero without touching memory (stride 0, 32-bit data format).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {

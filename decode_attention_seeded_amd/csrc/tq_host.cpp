@@ -229,7 +229,12 @@ int plan_decode(int d, int bits_v, int qjl, int B, int Hq, int Hkv, int64_t n_ct
   else
     finish_plan(n_ctx, splits, units, decode_tile(d), 2048, p);
   const size_t heads = size_t(B) * Hq;
+  if (units > kMaxDecodeRows) return TQ_ERR_ARG;
+  // arrival counters first, at a fixed offset and size, so that they never
+  // move or overlap another section when one workspace serves calls of
+  // different shapes
   size_t off = 0;
+  p->off_cnt = off; off = align256(off + size_t(kMaxDecodeRows) * sizeof(uint32_t));
   p->off_qp = off;  off = align256(off + heads * d * sizeof(float));
   p->off_qq = off;  if (qjl) off = align256(off + heads * d * sizeof(float));
   p->off_ml = off;  off = align256(off + heads * p->splits * 2 * sizeof(float));

@@ -27,17 +27,13 @@ static int go(int mx, const DecodeArgs& a, dim3 grid, hipStream_t st) {
 #else
   if constexpr (BV == 2 || BV == 4) {
     if (mx) {
-      const uint32_t* qp2 = reinterpret_cast<const uint32_t*>(a.qp);
       const dim3 block(64 * mx_waves(TQ_D));
       if (a.norm_f16)
-        hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, QJL, true>), grid, block, 0, st, a,
-                           qp2);
+        hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, QJL, true>), grid, block, 0, st, a);
       else
-        hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, QJL, false>), grid, block, 0, st, a,
-                           qp2);
+        hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, QJL, false>), grid, block, 0, st, a);
       return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
     }
-    if (mx) return TQ_ERR_UNSUPPORTED;
   } else {
     if (mx) return TQ_ERR_UNSUPPORTED;
   }

@@ -11,6 +11,7 @@ namespace tq {
 
 constexpr int kMaxLevels = 16;  // 2^4
 constexpr int kMaxSplitCount = 4096;  // split-K partials per query head
+constexpr int kMaxDecodeRows = 65535; // decode workgroup rows (B * Hkv * head groups)
 
 // Codebook tables in the precisions the kernels consume.
 struct Codebook {
@@ -63,8 +64,9 @@ struct DecodePlan {
   int G = 0, gk = 0, chunks = 0, tile = 0, splits = 0;
   int mx = 0;        // 1: the matrix-core kernel, 0: the workgroup-tile kernel
   int64_t tps = 0;
-  // workspace section offsets (bytes)
-  size_t off_qp = 0, off_qq = 0, off_ml = 0, off_acc = 0, total = 0;
+  // workspace section offsets (bytes); off_cnt: the matrix-core kernel's
+  // arrival counters (kMaxDecodeRows words at offset 0, zero between calls)
+  size_t off_qp = 0, off_qq = 0, off_ml = 0, off_acc = 0, off_cnt = 0, total = 0;
 };
 
 // Waves per workgroup of the matrix-core decode kernel (one workgroup holds a

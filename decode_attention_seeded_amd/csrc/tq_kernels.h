@@ -89,6 +89,8 @@ struct DecodeArgs {
   uint32_t qsbits[8];     // QJL rotation signs, same layout
   int append;             // 1: the last split first encodes token n_ctx - 1 (enc)
   EncodeArgs enc;         // that token's K/V rows and the cache planes
+  uint32_t* cnt;          // [grid.y] arrival counters (zero between calls)
+  float* out;             // [B*Hq][D] output of kernels that merge their splits
 };
 
 struct MergeArgs {
@@ -1216,7 +1218,7 @@ constexpr int mx_prefetch(int d, int bk, bool qjl) { return d == 128 && bk < 4 ?
 template <int D, int BK, int BV, int GK, bool QJL, bool NF16>
 __global__ void __launch_bounds__(64 * mx_waves(D))
     __attribute__((amdgpu_waves_per_eu(mx_waves(D) / 4)))
-k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
+k_decode_mx(DecodeArgs a) {
   static_assert(D == 128 || D == 256, "matrix-core decode: d 128 or 256");
   static_assert(BV == 2 || BV == 4, "matrix-core decode: 2- or 4-bit values");
   static_assert(GK == 1 || GK == 2 || GK == 4, "heads per workgroup");
@@ -1253,6 +1255,7 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
   __shared__ uint32_t qs[GK * (D / 2)];
   __shared__ uint32_t qs2[QJL ? GK * (D / 2) : 1];
   __shared__ float mlx[W][GK][2];
+  __shared__ bool last_arrival;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1283,7 +1286,12 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
   };
   const uint32_t ko0 = uint32_t(lane) * KREC;
   const uint32_t no0 = uint32_t(lane) * nb;
-  const uint32_t vo0 = uint32_t(4 * kq) * VREC + uint32_t(col) * SB;
+  // value slice i of a lane is token 16 (i / 4) + 4 (i % 4) + kq, so one load
+  // instruction covers four consecutive rows (whole cache lines) and the
+  // value, norm and sign-plane loads can stream past the caches (nontemporal)
+  const uint32_t vo0 = uint32_t(kq) * VREC + uint32_t(col) * SB;
+  constexpr int kNT = 2;                       // cache policy: nontemporal
+  constexpr int kSignNT = D / 8 == 16 ? kNT : 0;   // sign rows of 16 B: whole lines
   auto load = [&](int64_t base, Tile& t) {
     const uint32_t n = rows_left(base);
     const auto rk = dev::buffer_rsrc(a.kc + (row0 + base) * KREC, n * KREC);
@@ -1296,11 +1304,11 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     const uint8_t* kn_p = static_cast<const uint8_t*>(a.kn) + (row0 + base) * nb;
     const uint8_t* vn_p = static_cast<const uint8_t*>(a.vn) + (row0 + base) * nb;
     if constexpr (NF16) {
-      t.kn = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(kn_p, n * nb), no0, 0, 0);
-      t.vn = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(vn_p, n * nb), no0, 0, 0);
+      t.kn = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(kn_p, n * nb), no0, 0, kNT);
+      t.vn = __builtin_amdgcn_raw_buffer_load_b16(dev::buffer_rsrc(vn_p, n * nb), no0, 0, kNT);
     } else {
-      t.kn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(kn_p, n * nb), no0, 0, 0);
-      t.vn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(vn_p, n * nb), no0, 0, 0);
+      t.kn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(kn_p, n * nb), no0, 0, kNT);
+      t.vn = __builtin_amdgcn_raw_buffer_load_b32(dev::buffer_rsrc(vn_p, n * nb), no0, 0, kNT);
     }
     if constexpr (QJL) {
       const auto rs = dev::buffer_rsrc(reinterpret_cast<const uint8_t*>(a.kq) +
@@ -1308,25 +1316,25 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
 #pragma unroll
       for (int k = 0; k < D / 128; ++k) {
         const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rs, uint32_t(lane) * (D / 8),
-                                                              16 * k, 0);
+                                                              16 * k, kSignNT);
         t.sw[4 * k] = q4[0]; t.sw[4 * k + 1] = q4[1]; t.sw[4 * k + 2] = q4[2];
         t.sw[4 * k + 3] = q4[3];
       }
       t.kr = __builtin_amdgcn_raw_buffer_load_b16(
-          dev::buffer_rsrc(a.kr + (row0 + base), n * 2), uint32_t(lane) * 2, 0, 0);
+          dev::buffer_rsrc(a.kr + (row0 + base), n * 2), uint32_t(lane) * 2, 0, kNT);
     }
     const auto rv = dev::buffer_rsrc(a.vc + (row0 + base) * VREC, n * VREC);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int so = (16 * (i >> 2) + (i & 3)) * VREC;
+      const int so = (16 * (i >> 2) + 4 * (i & 3)) * VREC;
       if constexpr (SB == 8) {
-        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rv, vo0, so, 0);
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rv, vo0, so, kNT);
         t.vx[i][0] = v2[0];
         t.vx[i][Tile::SW - 1] = v2[1];
       } else if constexpr (SB == 4) {
-        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo0, so, 0);
+        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo0, so, kNT);
       } else {
-        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b16(rv, vo0, so, 0);
+        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b16(rv, vo0, so, kNT);
       }
     }
   };
@@ -1412,7 +1420,6 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
   }
   // the GK query rows, rotated and scaled here (one 16-lane group per head):
   // R q * scale * log2(e), as fp16 pairs
-  (void)qp2_all;
   if (tid < 16 * GK) {
     constexpr int E = D / 16;
     const int g = tid >> 4, l16 = tid & 15;
@@ -1465,6 +1472,9 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     }
   }
   const uint32_t sl8 = uint32_t(lane) << 3;
+  // weight slot of this lane's token t = 16 blk + 4 j + kq in the value
+  // product's K order (slot 16 blk + 4 kq + j, matching the value slices)
+  const int pslot = (lane & 0x30) | ((lane & 3) << 2) | ((lane >> 2) & 3);
 
   float m_run[GK], lpart[GK];
   mx_f4 acc[VJ];
@@ -1533,7 +1543,7 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
       const float e = __builtin_amdgcn_exp2f(s - m_run[g]);
       const float p = valid ? e : 0.f;
       lpart[g] += p;
-      p16[g * TW + lane] = __builtin_bit_cast(uint16_t, _Float16(p * nv));
+      p16[g * TW + pslot] = __builtin_bit_cast(uint16_t, _Float16(p * nv));
     }
     // the weights written above are read back by other lanes of this wave
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1646,7 +1656,7 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     }
   }
 
-  // ---------------- combine the waves, then R^T of the weighted sum
+  // ---------------- combine the waves of this split (rotated frame)
   float lw[GK];
 #pragma unroll
   for (int g = 0; g < GK; ++g) lw[g] = dev::wave_sum(lpart[g]);
@@ -1673,25 +1683,67 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     }
   }
   __syncthreads();
-  float* obuf = reinterpret_cast<float*>(pex);            // [GK][D]
-  static_assert(sizeof(pex) >= GK * D * 4, "output staging fits the weight slots");
+  // This split's partial, (max, sum) per head and the weighted value sum in
+  // the rotated frame, goes out with device-scope stores: they write through
+  // this XCD's L2, so the workgroup that merges the unit (on any XCD) reads
+  // them without an L2 write-back here.
   for (int i = tid; i < GK * D; i += NT) {
     float sum = 0.f;
 #pragma unroll
     for (int w = 0; w < W; ++w) sum += slab[w * GK * D + i];
-    obuf[i] = sum;
+    const int g = i / D;
+    dev::store_dev(a.acc + ((head0 + g) * a.S + split) * D + (i - g * D), sum);
   }
-  __syncthreads();
   if (tid < GK) {
     float l = 0.f;
     for (int w = 0; w < W; ++w) {
       const float mw = mlx[w][tid][0];
       if (mw != -INFINITY) l += mlx[w][tid][1] * __builtin_amdgcn_exp2f(mw - M[tid]);
     }
-    float* ml = a.ml + ((head0 + tid) * a.S + split) * 2;
-    ml[0] = M[tid];
-    ml[1] = l;
+    dev::store_dev2(a.ml + ((head0 + tid) * a.S + split) * 2, M[tid], l);
   }
+  // every store of this workgroup has completed before the arrival count
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    last_arrival = __hip_atomic_fetch_add(a.cnt + unit, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == uint32_t(a.S - 1);
+  __syncthreads();
+  if (!last_arrival) return;
+
+  // ---------------- last split of the unit: merge the S partials of each
+  // head in split order (online log-sum-exp), then R^T, then the output
+  float* obuf = reinterpret_cast<float*>(pex);            // [GK][D]
+  static_assert(sizeof(pex) >= GK * D * 4, "output staging fits the weight slots");
+  for (int i = tid; i < GK * D; i += NT) {
+    const int g = i / D;
+    const float* pm = a.ml + (head0 + g) * a.S * 2;
+    const float* pa = a.acc + (head0 + g) * a.S * D + (i - g * D);
+    float Mx = -INFINITY, L = 0.f, sum = 0.f;
+    constexpr int U = 16;
+    for (int s0 = 0; s0 < a.S; s0 += U) {
+      float mv[U], lv[U], av[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int sp = s0 + u < a.S ? s0 + u : a.S - 1;
+        dev::load_dev2(pm + 2 * sp, &mv[u], &lv[u]);
+        av[u] = dev::load_dev(pa + int64_t(sp) * D);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (s0 + u < a.S && mv[u] != -INFINITY) {
+          const float nm = fmaxf(Mx, mv[u]);
+          const float a1 = __builtin_amdgcn_exp2f(Mx - nm);
+          const float a2 = __builtin_amdgcn_exp2f(mv[u] - nm);
+          sum = fmaf(av[u], a2, sum * a1);
+          L = fmaf(lv[u], a2, L * a1);
+          Mx = nm;
+        }
+      }
+    }
+    obuf[i] = sum / L;
+  }
+  __syncthreads();
   if (tid < 16 * GK) {
     constexpr int E = D / 16;
     const int g = tid >> 4, l16 = tid & 15;
@@ -1703,11 +1755,13 @@ k_decode_mx(DecodeArgs a, const uint32_t* __restrict__ qp2_all) {
     const float nn = 1.0f / sqrtf(float(D));
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = (smask >> i & 1) ? -v[i] * nn : v[i] * nn;
-    float4* dst = reinterpret_cast<float4*>(a.acc + ((head0 + g) * a.S + split) * D + l16 * E);
+    float4* dst = reinterpret_cast<float4*>(a.out + (head0 + g) * D + l16 * E);
 #pragma unroll
     for (int k = 0; k < E / 4; ++k)
       dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
   }
+  // the counter goes back to zero for the next call on this workspace
+  if (tid == 0) __hip_atomic_store(a.cnt + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------

@@ -185,7 +185,16 @@ int tq_qjl_sketch(const float* r, int64_t rows, int d, uint64_t qjl_seed,
 int tq_num_splits(const tq_config* cfg, int B, int Hq, int Hkv, int64_t n_ctx,
                   int splits);
 
-/* Workspace bytes tq_attend_decode needs; negative tq_status on bad args. */
+/* Workspace bytes tq_attend_decode needs; negative tq_status on bad args
+ * (TQ_ERR_ARG also when B * Hkv * head groups exceeds 65535).
+ * The workspace starts with 65535 arrival counters (256 KB, one per
+ * (batch, KV head, head group) row of the decode grid): for the formats with
+ * 2- or 4-bit values the last workgroup of each row to finish merges the
+ * row's split partials, which follow the counters. The counters must read
+ * zero when a call starts: zero the buffer once before its first use. Every
+ * call leaves them at zero again, so the same buffer serves later calls of
+ * any shape that fits. Two calls that share a workspace must not run at the
+ * same time. */
 int64_t tq_workspace_bytes(const tq_config* cfg, int B, int Hq, int Hkv,
                            int64_t n_ctx, int splits);
 
@@ -201,7 +210,8 @@ int64_t tq_workspace_bytes(const tq_config* cfg, int B, int Hq, int Hkv,
  *        with k_hat / v_hat the dequantized rows in the original frame.
  *   scale: 0 selects 1/sqrt(d).
  *   splits: 0 lets the library choose (see tq_num_splits).
- *   ws:  device workspace of at least tq_workspace_bytes() bytes.
+ *   ws:  device workspace of at least tq_workspace_bytes() bytes, zero before
+ *        its first use (see tq_workspace_bytes).
  * n_ctx must be in [1, capacity]. The result does not depend on host
  * threads or on timing: partials are merged in a fixed order.
  */
