@@ -7,17 +7,25 @@ default workload is the long-context decode: batch 1, 32 query / 8 KV heads,
 d = 128, 524288-token context, 3-bit keys / 4-bit values with fp16 norms,
 4096 tokens appended per step, bf16 N(0,1) inputs.
 
+The timed steps replay a HIP graph of the step (one graph launch per step, so
+that the host's per-call Python and argument set-up cannot starve the GPU);
+the same steps launched eagerly are reported as `step_eager_us`. Decode and
+encode rates are measured on back-to-back launches bracketed by one pair of
+HIP events on the launch stream (no per-call markers inside the timed
+region).
+
 Prints ONE JSON line on stdout (progress goes to stderr):
-  value     KV-tokens/s of the whole step (B * N / step time)
-  roofline  the decode call's algorithmic bytes / its measured duration
-            against the 8 TB/s HBM peak
-  cpu_baseline  the CPU oracle timed on a bounded sample, scaled
+  value         KV-tokens/s of the whole step (B * N / step time)
+  roofline      the decode kernel's algorithmic bytes per launch / its average
+                launch duration, against the 8 TB/s HBM peak
+  cpu_baseline  the CPU oracle on the host cores, one process per
+                (batch, KV head) unit, the step's append encode and decode
+  other_workloads  decode rate and roofline of the two other 128k+ contexts
 """
 
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -26,7 +34,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+FP16_DENSE_PEAK_TFLOPS = 2500.0
 METRIC = "packed decode-attention KV-tokens/s and achieved HBM GB/s as % of peak"
+DECODE_KERNEL = "k_decode_mx"
 
 
 def log(msg):
@@ -44,17 +54,15 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(wid):
-    """HBM bytes per decode launch from the committed counter summary, if it
-    was taken on the current kernel sources; else None."""
-    p = os.path.join(ROOT, "profiles", f"decode_hbm_traffic_workload{wid}.json")
+def profile_summary(name):
+    """A committed profile summary (JSON under profiles/) if it was taken on
+    the current kernel sources, else None."""
+    p = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    if t.get("source_hash") != source_hash():
-        return None
-    return t.get("hbm_bytes_per_launch")
+    return t if t.get("source_hash") == source_hash() else None
 
 
 def alg_bytes_of(tq, cfg, w, q):
@@ -64,56 +72,187 @@ def alg_bytes_of(tq, cfg, w, q):
     return cache_bytes + q.numel() * q.element_size() + w.B * w.Hq * w.d * 4
 
 
-def to_dev_bf16(torch, raw):
+def to_dev(torch, raw, in_dtype):
     import numpy as np
-    return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16).cuda()
+    if in_dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(
+            torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(raw)).cuda()
 
 
-def cpu_baseline(w, sample_tokens):
-    """The oracle (NumPy fp64, as it stands) on a bounded sample of the same
-    step: the append-encode of the newest tokens for one KV head and the
-    decode of that KV head's query heads over `sample_tokens` tokens; both
-    scaled linearly to the whole step."""
+def timed(torch, fn, n, warm=3):
+    """Average microseconds of fn() over n back-to-back calls (one event pair
+    around the loop, on the current stream)."""
+    for _ in range(warm):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / n
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline: one spawned process per (batch, KV head) unit.
+# --------------------------------------------------------------------------
+
+_BARRIER = None
+
+
+def _cpu_init(barrier):
+    global _BARRIER
+    _BARRIER = barrier
+
+
+def _cpu_unit(job):
+    """Worker: the oracle's encode of one unit's context (set-up, untimed),
+    then the step for that unit (append encode of the newest tokens, decode
+    of its G query heads over the whole context), timed. With a barrier the
+    units start their timed phase together."""
+    wid, b, h, threads = job
+    os.environ["OMP_NUM_THREADS"] = str(threads)
     import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(threads)
+    except Exception:
+        pass
     import oracle as o
     import seeded_inputs as si
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    n = min(sample_tokens, w.N) if sample_tokens > 0 else w.N
-    A = min(w.append or 4096, n)
-    _, fk = si.kv_rows(w, si.T_K, 0, 0, 0, n)
-    _, fv = si.kv_rows(w, si.T_V, 0, 0, 0, n)
+    w = si.WORKLOADS[wid]
+    A = w.append or 0
+    _, fk = si.kv_rows(w, si.T_K, b, h, 0, w.N)
+    _, fv = si.kv_rows(w, si.T_V, b, h, 0, w.N)
     fk = fk.astype(np.float64)[None, None]
     fv = fv.astype(np.float64)[None, None]
     kw = dict(seed=w.seed, bits_k=w.bits_k, bits_v=w.bits_v, norm_dtype=w.norm_dtype,
               qjl=w.qjl, qjl_seed=w.qjl_seed)
     t0 = time.perf_counter()
-    cache = o.encode_kv(fk, fv, **kw)                      # setup, untimed
-    t_setup = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    o.encode_kv(fk[:, :, n - A:], fv[:, :, n - A:], **kw)  # the step's append
-    t_enc = time.perf_counter() - t0
+    cache = o.encode_kv(fk[:, :, :w.N - A], fv[:, :, :w.N - A], **kw)
+    for key in ("k_enc", "v_enc", "k_qjl"):     # the encode's intermediates
+        cache.pop(key, None)
+    setup = time.perf_counter() - t0
     _, qf = si.queries(w)
-    q = qf[:1, :w.G].astype(np.float64)
+    q = qf[b:b + 1, h * w.G:(h + 1) * w.G].astype(np.float64)
+    if _BARRIER is not None:
+        _BARRIER.wait()
     t0 = time.perf_counter()
-    o.attend(q, cache, n, d=w.d, seed=w.seed, bits_k=w.bits_k, bits_v=w.bits_v, Hkv=1,
+    if A:
+        app = o.encode_kv(fk[:, :, w.N - A:], fv[:, :, w.N - A:], **kw)
+        for key in ("kc", "vc", "kn", "vn", "kq", "kr"):
+            if key in cache:
+                cache[key] = np.concatenate([cache[key], app[key]], axis=2)
+    o.attend(q, cache, w.N, d=w.d, seed=w.seed, bits_k=w.bits_k, bits_v=w.bits_v, Hkv=1,
              qjl=w.qjl, qjl_seed=w.qjl_seed)
-    t_dec = time.perf_counter() - t0
-    units = w.B * w.Hkv
-    step_s = t_enc * units * (w.append or A) / A + t_dec * units * w.N / n
+    step = time.perf_counter() - t0
+    return setup, step
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, max_units):
+    """The oracle (NumPy fp64, as it stands) on the host's cores: one spawned
+    process per (batch, KV head) unit, each unit's share of the step run on
+    its whole context; the units run side by side and start their timed
+    phase together (a barrier after each unit's set-up). Covers min(units,
+    max_units) units and scales by units / covered."""
+    import multiprocessing as mp
+    cores = len(os.sched_getaffinity(0))
+    units = [(b, h) for b in range(w.B) for h in range(w.Hkv)][:max_units]
+    procs = min(len(units), cores)
+    threads = max(1, cores // procs)
+    ctx = mp.get_context("spawn")
+    barrier = ctx.Barrier(procs) if len(units) == procs else None
+    t0 = time.perf_counter()
+    with ctx.Pool(procs, initializer=_cpu_init, initargs=(barrier,)) as pool:
+        res = pool.map(_cpu_unit, [(w.wid, b, h, threads) for b, h in units], chunksize=1)
+    wall = time.perf_counter() - t0
+    rounds = (len(units) + procs - 1) // procs
+    step_s = max(r[1] for r in res) * rounds * (w.B * w.Hkv) / len(units)
     return {
         "value": w.B * w.N / step_s,
         "unit": "KV-tokens/s",
-        "cores": threads,
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"1 of {units} KV heads: {A}-token append encode ({t_enc:.2f} s) and "
-                   f"decode of {w.G} query heads over {n} of {w.N} tokens ({t_dec:.2f} s), "
-                   f"scaled linearly to the full step ({step_s:.1f} s); encoding the "
-                   f"sample's cache first took {t_setup:.1f} s (not part of the step)"),
+        "cpu_model": cpu_model(),
+        "processes": procs,
+        "threads_per_process": threads,
+        "sample": (f"{len(units)} of {w.B * w.Hkv} (batch, KV head) units, one process each "
+                   f"({procs} side by side, {threads} BLAS thread(s) each): "
+                   f"{w.append or 0}-token append encode and decode of {w.G} query heads over "
+                   f"all {w.N} tokens; slowest unit {max(r[1] for r in res):.2f} s, scaled by "
+                   f"units/processes to the whole step ({step_s:.2f} s); encoding each "
+                   f"unit's cache first took up to {max(r[0] for r in res):.1f} s (not part of "
+                   f"the step); {wall:.0f} s wall"),
     }
+
+
+# --------------------------------------------------------------------------
+# Decode of one workload: encode, back-to-back and cold decode calls.
+# --------------------------------------------------------------------------
+
+def decode_record(torch, tq, si, w, n_calls, flush, fsink):
+    k_host = si.kv_full(w, si.T_K)
+    v_host = si.kv_full(w, si.T_V)
+    q_raw, _ = si.queries(w)
+    K, V, q = (to_dev(torch, k_host, w.in_dtype), to_dev(torch, v_host, w.in_dtype),
+               to_dev(torch, q_raw, w.in_dtype))
+    del k_host, v_host
+    cfg = tq.Config(d=w.d, bits_k=w.bits_k, bits_v=w.bits_v, norm_dtype=w.norm_dtype,
+                    qjl=w.qjl, seed=w.seed, qjl_seed=w.qjl_seed)
+    cache = tq.PackedCache(cfg, w.B, w.Hkv, w.N)
+    tq.tq_encode_kv(cfg, K[:, :, :1].contiguous(), V[:, :, :1].contiguous(), 0, cache)
+    torch.cuda.synchronize()
+    enc_us = timed(torch, lambda: tq.tq_encode_kv(cfg, K, V, 0, cache), 3, warm=1)
+    in_bytes = (K.numel() + V.numel()) * K.element_size()
+    out_bytes = tq.tq_cache_bytes(cfg, w.B, w.Hkv, w.N)[0]
+    del K, V
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    ws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N))
+    dec = lambda: tq.tq_attend_decode(cfg, q, cache, w.N, out, ws)
+    us = timed(torch, dec, n_calls, warm=5)
+    cold = []
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    for _ in range(10):
+        tq.tq_read_probe(flush, fsink)
+        c0, c1 = ev(), ev()
+        c0.record()
+        dec()
+        c1.record()
+        torch.cuda.synchronize()
+        cold.append(c0.elapsed_time(c1) * 1e3)
+    import numpy as np
+    alg = alg_bytes_of(tq, cfg, w, q)
+    bf16_kv = 2 * w.B * w.Hkv * w.N * w.d * 2
+    rec = {
+        "workload": w.name,
+        "decode_call_us": round(us, 2),
+        "decode_call_cold_median_us": round(float(np.median(cold)), 2),
+        "kv_tokens_per_s": round(w.B * w.N / (us * 1e-6), 1),
+        "algorithmic_bytes": alg,
+        "achieved_gbps": round(alg / us / 1e3, 1),
+        "frac_of_hbm_peak": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4),
+        "splits": tq.tq_num_splits(cfg, w.B, w.Hq, w.Hkv, w.N),
+        "kv_bytes_vs_bf16": round(out_bytes / bf16_kv, 4),
+        "encode": {"tokens": w.N, "us": round(enc_us, 1), "bytes_in": in_bytes,
+                   "bytes_out": out_bytes,
+                   "frac_of_hbm_peak": round((in_bytes + out_bytes) / enc_us / 1e3 /
+                                             HBM_PEAK_GBPS, 4)},
+    }
+    del cache, ws, out, q
+    return rec
 
 
 def main():
@@ -126,9 +265,10 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-affine", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=0,
-                    help="context tokens of the CPU-oracle sample (0: the whole context "
-                         "of one KV head)")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the decode records of the other 128k+ workloads")
+    ap.add_argument("--cpu-units", type=int, default=8,
+                    help="(batch, KV head) units the CPU oracle runs (scaled to all)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="copy a buffer of this many MiB once before timing (a kernel of "
                          "known traffic, for calibrating HBM byte counters)")
@@ -148,6 +288,7 @@ def main():
     A = w.append if w.append else 0
     log(f"workload {w.wid}: {w.name}")
     torch.cuda.set_device(0)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
 
     # ---------------- inputs (seeded, host-generated, uploaded once)
     t0 = time.time()
@@ -155,12 +296,8 @@ def main():
     v_host = si.kv_full(w, si.T_V)
     q_raw, _ = si.queries(w)
     log(f"generated inputs in {time.time() - t0:.1f} s")
-    if w.in_dtype == "bf16":
-        K, V, q = to_dev_bf16(torch, k_host), to_dev_bf16(torch, v_host), to_dev_bf16(torch, q_raw)
-    else:
-        K = torch.from_numpy(k_host).cuda()
-        V = torch.from_numpy(v_host).cuda()
-        q = torch.from_numpy(q_raw).cuda()
+    K, V = to_dev(torch, k_host, w.in_dtype), to_dev(torch, v_host, w.in_dtype)
+    q = to_dev(torch, q_raw, w.in_dtype)
     del k_host, v_host
 
     cfg = tq.Config(d=w.d, bits_k=w.bits_k, bits_v=w.bits_v, norm_dtype=w.norm_dtype,
@@ -173,28 +310,20 @@ def main():
     splits = tq.tq_num_splits(cfg, w.B, w.Hq, w.Hkv, w.N)
     ws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N))
 
-    ev = lambda: torch.cuda.Event(enable_timing=True)
-    # one-token encode first, so the timed bulk encode excludes code-object
-    # loading and the host's one-time codebook set-up
+    # bulk encode (after a one-token encode that loads the code object)
     tq.tq_encode_kv(cfg, k_bulk[:, :, :1].contiguous(), v_bulk[:, :, :1].contiguous(), 0, cache)
     torch.cuda.synchronize()
-    e0, e1 = ev(), ev()
-    e0.record()
-    tq.tq_encode_kv(cfg, k_bulk, v_bulk, 0, cache)
-    e1.record()
-    torch.cuda.synchronize()
-    bulk_ms = e0.elapsed_time(e1)
+    bulk_us = timed(torch, lambda: tq.tq_encode_kv(cfg, k_bulk, v_bulk, 0, cache), 3, warm=1)
+    bulk_in = (k_bulk.numel() + v_bulk.numel()) * k_bulk.element_size()
+    bulk_out = tq.tq_cache_bytes(cfg, w.B, w.Hkv, n_bulk)[0]
     del k_bulk, v_bulk
-    log(f"bulk encode of {n_bulk} tokens x {w.B * w.Hkv} heads: {bulk_ms:.3f} ms")
+    log(f"bulk encode of {n_bulk} tokens x {w.B * w.Hkv} heads: {bulk_us:.1f} us "
+        f"({(bulk_in + bulk_out) / bulk_us / 1e3:.0f} GB/s in + out)")
 
-    def step(dec_events=None):
+    def step():
         if A:
             tq.tq_encode_kv(cfg, k_app, v_app, n_bulk, cache)
-        if dec_events:
-            dec_events[0].record()
         tq.tq_attend_decode(cfg, q, cache, w.N, out, ws)
-        if dec_events:
-            dec_events[1].record()
 
     if args.copy_probe_mb:
         src = torch.empty(args.copy_probe_mb << 20, dtype=torch.uint8, device="cuda")
@@ -204,39 +333,52 @@ def main():
         del src, dst
         log(f"copy probe: {args.copy_probe_mb} MiB read + written")
 
-    for _ in range(args.warmup):
+    # ---------------- the step as a HIP graph (one launch per step)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
         step()
     torch.cuda.synchronize()
-    log(f"warmup {args.warmup} steps done; timing {args.steps} steps")
-
-    dec_ev = [(ev(), ev()) for _ in range(args.steps)]
+    ref_out = out.clone()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done; timing {args.steps} steps (graph replays)")
     s0, s1 = ev(), ev()
     torch.cuda.synchronize()
     s0.record()
-    for i in range(args.steps):
-        step(dec_ev[i])
+    for _ in range(args.steps):
+        graph.replay()
     s1.record()
     torch.cuda.synchronize()
-    total_ms = s0.elapsed_time(s1)
-    ms_per_step = total_ms / args.steps
-    dec_us = [a.elapsed_time(b) * 1e3 for a, b in dec_ev]
-    dec_avg_us = float(np.mean(dec_us))
-    log(f"step {ms_per_step * 1e3:.1f} us; decode call avg {dec_avg_us:.1f} us "
-        f"(p10 {np.percentile(dec_us, 10):.1f}, p90 {np.percentile(dec_us, 90):.1f})")
+    ms_per_step = s0.elapsed_time(s1) / args.steps
+    replay_equal = bool(torch.equal(out, ref_out))
+    step_eager_us = timed(torch, step, args.steps, warm=3)
+    log(f"step {ms_per_step * 1e3:.1f} us (graph), {step_eager_us:.1f} us eager; graph output "
+        f"equals the eager step: {replay_equal}")
+
+    # ---------------- decode alone: back-to-back launches
+    alg_bytes = alg_bytes_of(tq, cfg, w, q)
+    n_dec = max(args.steps, 50)
+    dec_us = timed(torch, lambda: tq.tq_attend_decode(cfg, q, cache, w.N, out, ws), n_dec)
+    achieved = alg_bytes / dec_us / 1e3
+    log(f"decode call {dec_us:.2f} us over {n_dec} back-to-back calls = {achieved:.0f} GB/s "
+        f"({achieved / HBM_PEAK_GBPS:.3f} of peak)")
 
     # streaming-read probe over as many bytes as one decode call reads, and
     # decode calls after a 1 GiB read has evicted the 256 MB last-level cache
-    probe_bytes = (alg_bytes_of(tq, cfg, w, q) + 15) // 16 * 16
+    probe_bytes = (alg_bytes + 15) // 16 * 16
     pbuf = torch.empty(probe_bytes, dtype=torch.uint8, device="cuda")
+    pbuf.random_(0, 255)
     sink = tq.tq_read_probe(pbuf)
-    a, b = ev(), ev()
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(20):
-        tq.tq_read_probe(pbuf, sink)
-    b.record()
-    torch.cuda.synchronize()
-    probe_us = a.elapsed_time(b) * 1e3 / 20
+    probe_us = timed(torch, lambda: tq.tq_read_probe(pbuf, sink), 20)
+    probe_gbps = probe_bytes / probe_us / 1e3
     del pbuf
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     fsink = tq.tq_read_probe(flush)
@@ -249,45 +391,26 @@ def main():
         c1.record()
         torch.cuda.synchronize()
         cold_us.append(c0.elapsed_time(c1) * 1e3)
-    del flush
-    log(f"read probe {probe_bytes / probe_us / 1e3:.1f} GB/s over {probe_bytes} B; cold decode "
-        f"median {np.median(cold_us):.1f} us")
+    log(f"read probe {probe_gbps:.1f} GB/s over {probe_bytes} B; cold decode median "
+        f"{np.median(cold_us):.1f} us")
 
     # append-encode alone
     enc_us = None
     if A:
-        a, b = ev(), ev()
-        a.record()
-        for _ in range(20):
-            tq.tq_encode_kv(cfg, k_app, v_app, n_bulk, cache)
-        b.record()
-        torch.cuda.synchronize()
-        enc_us = a.elapsed_time(b) * 1e3 / 20
+        enc_us = timed(torch, lambda: tq.tq_encode_kv(cfg, k_app, v_app, n_bulk, cache), 20)
 
     # single-token generation step (append token N-1, attend over N): the
     # fused entry point against the two calls it replaces, on the same cache
     k1, v1 = K[:, :, w.N - 1:].contiguous(), V[:, :, w.N - 1:].contiguous()
-
-    def time_calls(fn, n=20):
-        for _ in range(3):
-            fn()
-        a, b = ev(), ev()
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(n):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / n
 
     def two_calls():
         tq.tq_encode_kv(cfg, k1, v1, w.N - 1, cache)
         tq.tq_attend_decode(cfg, q, cache, w.N, out, ws)
 
     single = {
-        "two_calls_us": round(time_calls(two_calls), 2),
-        "fused_us": round(time_calls(
-            lambda: tq.tq_append_attend_decode(cfg, k1, v1, q, cache, w.N, out, ws)), 2),
+        "two_calls_us": round(timed(torch, two_calls, 50), 2),
+        "fused_us": round(timed(torch, lambda: tq.tq_append_attend_decode(
+            cfg, k1, v1, q, cache, w.N, out, ws), 50), 2),
     }
     log(f"single-token step: encode + decode {single['two_calls_us']} us, "
         f"fused {single['fused_us']} us")
@@ -299,26 +422,18 @@ def main():
     if not args.no_prefill:
         nq = A if A else min(1024, w.N)
         qc_raw, _ = si.chunk_queries(w, nq)
-        qc = to_dev_bf16(torch, qc_raw) if w.in_dtype == "bf16" else \
-            torch.from_numpy(qc_raw).cuda()
+        qc = to_dev(torch, qc_raw, w.in_dtype)
         pout = torch.empty((w.B, w.Hq, nq, w.d), dtype=torch.float32, device="cuda")
-        tq.tq_attend_prefill(cfg, qc, cache, w.N, pout)
-        a, b = ev(), ev()
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(3):
-            tq.tq_attend_prefill(cfg, qc, cache, w.N, pout)
-        b.record()
-        torch.cuda.synchronize()
-        pms = a.elapsed_time(b) / 3
+        pus = timed(torch, lambda: tq.tq_attend_prefill(cfg, qc, cache, w.N, pout), 3, warm=1)
         visible = nq * (w.N - nq) + nq * (nq + 1) // 2
         flops = 4 * w.d * w.B * w.Hq * visible
-        prefill = {"chunk_tokens": nq, "context": w.N, "ms": round(pms, 3),
-                   "tflops": round(flops / (pms * 1e-3) / 1e12, 1),
-                   "frac_of_fp16_dense_peak": round(flops / (pms * 1e-3) / 2.5e15, 4),
+        tflops = flops / (pus * 1e-6) / 1e12
+        prefill = {"chunk_tokens": nq, "context": w.N, "ms": round(pus / 1e3, 3),
+                   "tflops": round(tflops, 1),
+                   "frac_of_fp16_dense_peak": round(tflops / FP16_DENSE_PEAK_TFLOPS, 4),
                    "flops": flops}
         del qc, pout
-        log(f"prefill of {nq} tokens over {w.N}: {pms:.2f} ms, {prefill['tflops']} TFLOP/s")
+        log(f"prefill of {nq} tokens over {w.N}: {pus / 1e3:.2f} ms, {tflops:.1f} TFLOP/s")
 
     # the group-affine variant (group 64, fp16 scale and bias, rotated keys)
     # at 4 bits, the README's iso-byte comparison format, on the same K/V
@@ -330,16 +445,8 @@ def main():
         tq.tq_affine_encode_kv(acfg, K, V, 0, acache)
         aws = tq.workspace(tq.tq_affine_workspace_bytes(acfg, w.B, w.Hq, w.Hkv, w.N))
         aout = torch.empty_like(out)
-        for _ in range(3):
-            tq.tq_affine_attend_decode(acfg, q, acache, w.N, aout, aws)
-        a, b = ev(), ev()
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(20):
-            tq.tq_affine_attend_decode(acfg, q, acache, w.N, aout, aws)
-        b.record()
-        torch.cuda.synchronize()
-        aus = a.elapsed_time(b) / 20 * 1e3
+        aus = timed(torch, lambda: tq.tq_affine_attend_decode(acfg, q, acache, w.N, aout, aws),
+                    20)
         abytes = acache.nbytes() + q.numel() * q.element_size() + aout.numel() * 4
         affine = {"format": "K4/V4 group-64 affine, fp16 scale and bias, rotated keys",
                   "us_per_call": round(aus, 2),
@@ -351,44 +458,59 @@ def main():
         del acache, aws, aout
         log(f"affine K4V4 decode: {aus:.1f} us/call, {affine['gbps']} GB/s")
 
-    # algorithmic bytes of one decode call: every packed plane over N tokens,
-    # plus q in and out
-    alg_bytes = alg_bytes_of(tq, cfg, w, q)
-    qbytes = q.numel() * q.element_size()
-    achieved = alg_bytes / (dec_avg_us * 1e-6) / 1e9
-    traffic = traffic_from_profile(w.wid)
-
     # dense bf16 decode on the same GPU (same split-K skeleton, bf16 rows)
+    qbytes = q.numel() * q.element_size()
     dense = None
     if not args.no_dense and w.in_dtype == "bf16":
         dws = tq.workspace(tq.tq_dense_workspace_bytes(w.B, w.Hq, w.Hkv, w.d, w.N))
         dout = torch.empty_like(out)
-        for _ in range(3):
-            tq.tq_dense_decode_bf16(q, K, V, dout, dws)
-        a, b = ev(), ev()
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(20):
-            tq.tq_dense_decode_bf16(q, K, V, dout, dws)
-        b.record()
-        torch.cuda.synchronize()
-        dus = a.elapsed_time(b) * 1e3 / 20
+        dus = timed(torch, lambda: tq.tq_dense_decode_bf16(q, K, V, dout, dws), 20)
         dbytes = 2 * K.numel() * 2 + qbytes + out.numel() * 4
-        dense = {"decode_us": round(dus, 2), "achieved_gbps": round(dbytes / dus / 1e3, 1),
-                 "packed_speedup": round(dus / dec_avg_us, 3)}
-        log(f"dense bf16 decode {dus:.1f} us ({dense['achieved_gbps']} GB/s)")
+        dgbps = dbytes / dus / 1e3
+        probe_bound_us = dbytes / probe_gbps / 1e3
+        dense = {"decode_us": round(dus, 2), "achieved_gbps": round(dgbps, 1),
+                 "frac_of_hbm_peak": round(dgbps / HBM_PEAK_GBPS, 4),
+                 "frac_of_read_probe": round(dgbps / probe_gbps, 4),
+                 "packed_speedup": round(dus / dec_us, 3),
+                 "read_probe_bound_us": round(probe_bound_us, 2),
+                 "packed_speedup_vs_probe_bound_dense": round(probe_bound_us / dec_us, 3),
+                 "ideal_byte_ratio": round(dbytes / alg_bytes, 3)}
+        log(f"dense bf16 decode {dus:.1f} us ({dgbps:.1f} GB/s, {dgbps / probe_gbps:.2f} of the "
+            f"read probe); at the probe rate it would take {probe_bound_us:.1f} us")
+    del K, V
+
+    # the other two 128k+ contexts (outlier keys d 256 K2/V2; QJL K3/V4)
+    others = None
+    if not args.no_others and args.workload == 4:
+        del cache, ws
+        others = {}
+        for wid in (3, 5):
+            log(f"workload {wid}: {si.WORKLOADS[wid].name}")
+            rec = decode_record(torch, tq, si, si.WORKLOADS[wid], 50, flush, fsink)
+            others[str(wid)] = rec
+            log(f"  decode {rec['decode_call_us']} us = {rec['achieved_gbps']} GB/s "
+                f"({rec['frac_of_hbm_peak']} of peak); cold median "
+                f"{rec['decode_call_cold_median_us']} us")
+    del flush
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(w, args.cpu_sample_tokens)
+        log("timing the CPU oracle on the host cores")
+        cpu = cpu_baseline(w, args.cpu_units)
         log(f"oracle: {cpu['value']:.3e} KV-tokens/s ({cpu['sample']})")
 
+    trace = profile_summary("decode_long_context_kernel_trace.json") \
+        if args.workload == 4 else None
+    traffic = profile_summary(f"decode_hbm_traffic_workload{w.wid}.json")
+    kernel_us = trace.get("kernel_avg_us") if trace else None
+    bf16_kv = 2 * w.B * w.Hkv * w.N * w.d * 2
+    fp16_kv = bf16_kv
+    cache_bytes = tq.tq_cache_bytes(cfg, w.B, w.Hkv, w.N)[0]
     cfg_desc = {
         "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d,
         "context": w.N, "bits_k": w.bits_k, "bits_v": w.bits_v, "norms": w.norm_dtype,
         "qjl": w.qjl, "append_tokens_per_step": A, "inputs": f"{w.in_dtype} seeded synthetic",
-        "splits": splits,
+        "splits": splits, "launch": "step captured as a HIP graph, one replay per step",
     }
     rec = {
         "metric": METRIC,
@@ -401,40 +523,54 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16 operands, f32 accumulate",
+        "dtype_note": ("decode products on fp16 operands (rotated query, scaled centroids, "
+                       "softmax weight times value norm) with fp32 accumulation; encode in fp64"),
         "data": "synthetic",
         "config": cfg_desc,
         "roofline": {
             "bound": "hbm",
+            "kernel": DECODE_KERNEL,
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
+            "traffic": traffic.get("hbm_bytes_per_launch") if traffic else None,
+            "bytes_per_launch": alg_bytes,
+            "launch_us": round(dec_us, 2),
+            "measured": f"{n_dec} back-to-back launches between two HIP events",
+            "kernel_trace_avg_us": kernel_us,
+            "frac_kernel_trace": (round(alg_bytes / kernel_us / 1e3 / HBM_PEAK_GBPS, 4)
+                                  if kernel_us else None),
+            "frac_of_read_probe": round(achieved / probe_gbps, 4),
         },
         "cpu_baseline": cpu,
-        "decode_call_us": round(dec_avg_us, 2),
-        "decode_call_percentiles_us": {
-            "p10": round(float(np.percentile(dec_us, 10)), 2),
-            "median": round(float(np.median(dec_us)), 2),
-            "p90": round(float(np.percentile(dec_us, 90)), 2)},
+        "decode_call_us": round(dec_us, 2),
+        "decode_kv_tokens_per_s": round(w.B * w.N / (dec_us * 1e-6), 1),
         "decode_call_cold_us": {
             "note": "each call after a 1 GiB streaming read (last-level cache evicted)",
             "p10": round(float(np.percentile(cold_us, 10)), 2),
             "median": round(float(np.median(cold_us)), 2),
             "p90": round(float(np.percentile(cold_us, 90)), 2)},
-        "read_probe": {
-            "bytes": probe_bytes, "us": round(probe_us, 2),
-            "gbps": round(probe_bytes / probe_us / 1e3, 1),
-            "decode_frac_of_probe": round(achieved / (probe_bytes / probe_us / 1e3), 4)},
-        "decode_kv_tokens_per_s": round(w.B * w.N / (dec_avg_us * 1e-6), 1),
+        "step_eager_us": round(step_eager_us, 2),
+        "graph_replay_equals_eager": replay_equal,
+        "read_probe": {"bytes": probe_bytes, "us": round(probe_us, 2),
+                       "gbps": round(probe_gbps, 1)},
+        "kv_cache": {"packed_bytes": cache_bytes, "bf16_bytes": bf16_kv,
+                     "reduction_vs_bf16": round(1 - cache_bytes / bf16_kv, 4),
+                     "reduction_vs_fp16": round(1 - cache_bytes / fp16_kv, 4)},
         "append_encode_us": round(enc_us, 2) if enc_us else None,
+        "bulk_encode": {"tokens": n_bulk, "us": round(bulk_us, 1), "bytes_in": bulk_in,
+                        "bytes_out": bulk_out,
+                        "gbps": round((bulk_in + bulk_out) / bulk_us / 1e3, 1),
+                        "frac_of_hbm_peak": round((bulk_in + bulk_out) / bulk_us / 1e3 /
+                                                  HBM_PEAK_GBPS, 4)},
         "single_token_step": single,
-        "bulk_encode_ms": round(bulk_ms, 3),
         "algorithmic_bytes_per_decode": alg_bytes,
         "dense_bf16": dense,
         "prefill": prefill,
         "affine": affine,
+        "other_workloads": others,
         "source_hash": source_hash(),
     }
     print(json.dumps(rec), flush=True)
