@@ -178,6 +178,48 @@ __device__ __forceinline__ void load_row_part(const void* p, int dt, int64_t idx
   }
 }
 
+// The raw 16-byte words of E consecutive elements of dtype dt (0 f32, 1
+// bf16, 2 f16) at element idx (E / 4 words for f32, E / 8 for 16-bit
+// types), and their conversion to floats: the load and the conversion can
+// then sit far apart.
+template <int E>
+__device__ __forceinline__ void load_row_raw(const void* p, int dt, int64_t idx,
+                                             uint4 (&r)[E / 4]) {
+  static_assert(E % 8 == 0, "whole 16-byte words");
+  if (dt == 0) {
+    const uint4* s = reinterpret_cast<const uint4*>(static_cast<const float*>(p) + idx);
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k) r[k] = s[k];
+  } else {
+    const uint4* s = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + idx);
+#pragma unroll
+    for (int k = 0; k < E / 8; ++k) r[k] = s[k];
+  }
+}
+template <int E>
+__device__ __forceinline__ void convert_row_raw(const uint4 (&r)[E / 4], int dt, float (&f)[E]) {
+  if (dt == 0) {
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k) {
+      f[4 * k] = __uint_as_float(r[k].x);
+      f[4 * k + 1] = __uint_as_float(r[k].y);
+      f[4 * k + 2] = __uint_as_float(r[k].z);
+      f[4 * k + 3] = __uint_as_float(r[k].w);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < E / 8; ++k) {
+      const uint32_t w[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = w[j] & 0xFFFFu, hi = w[j] >> 16;
+        f[8 * k + 2 * j] = dt == 1 ? bf16_to_f32(lo) : f16_to_f32(lo);
+        f[8 * k + 2 * j + 1] = dt == 1 ? bf16_to_f32(hi) : f16_to_f32(hi);
+      }
+    }
+  }
+}
+
 // Field i (width BITS) of a little-endian bitstream held in dwords w[].
 template <int BITS, int NW>
 __device__ __forceinline__ uint32_t field(const uint32_t (&w)[NW], int i) {

@@ -1340,56 +1340,111 @@ k_decode_mx(DecodeArgs a) {
   };
 
 
-  // the first tiles of each wave are requested before the tables and the
-  // query are set up, so the start-up latency of the stream overlaps that
-  // work (not with a fused append, whose row must be stored first)
+  // The query rows of this workgroup's heads are loaded, rotated and scaled
+  // by wave 0 before it requests any tile: a query load queued behind the
+  // whole chip's first round of tile traffic would arrive only after it. The
+  // other waves request their first tiles at once, so the stream starts
+  // while the query and the tables are set up (not with a fused append,
+  // whose row must be stored first).
+  constexpr int QE = D / 16;                   // query elements per lane (16 lanes per head)
+  if (tid < 16 * GK) {
+    const int g = tid >> 4, l16 = tid & 15;
+    float v[QE];
+    {
+      uint4 qraw[QE / 4];
+      dev::load_row_raw<QE>(a.q_raw, a.q_dtype, (head0 + g) * D + l16 * QE, qraw);
+      dev::convert_row_raw<QE>(qraw, a.q_dtype, v);
+    }
+    const uint32_t smask = dev::bitmap_bits(a.sbits, l16 * QE, QE);
+#pragma unroll
+    for (int i = 0; i < QE; ++i) if (smask >> i & 1) v[i] = -v[i];
+    dev::fwht16<QE, float>(v, l16);
+    const float mult = a.qmult / sqrtf(float(D));
+#pragma unroll
+    for (int i = 0; i < QE; ++i) v[i] *= mult;
+#pragma unroll
+    for (int i = 0; i < QE / 2; ++i)
+      qs[g * (D / 2) + l16 * (QE / 2) + i] = dev::pack_f16x2(v[2 * i], v[2 * i + 1]);
+    if constexpr (QJL) {
+      // q'' = R_2 q' from the fp32 q'
+      const uint32_t qmask = dev::bitmap_bits(a.qsbits, l16 * QE, QE);
+#pragma unroll
+      for (int i = 0; i < QE; ++i) if (qmask >> i & 1) v[i] = -v[i];
+      dev::fwht16<QE, float>(v, l16);
+      const float nn = 1.0f / sqrtf(float(D));
+#pragma unroll
+      for (int i = 0; i < QE / 2; ++i)
+        qs2[g * (D / 2) + l16 * (QE / 2) + i] = dev::pack_f16x2(v[2 * i] * nn, v[2 * i + 1] * nn);
+    }
+  }
   constexpr int PF = mx_prefetch(D, BK, QJL);
   const int64_t wb = t_begin + int64_t(wave) * TW;
   const bool early = !a.append;
+  // PF + 1 tile buffers, all requested before the set-up; in the loop a
+  // buffer is refilled right after it has been processed
   Tile ta, tb, tc;
-  if (early) {
+  auto load_first = [&]() {
     load(wb, ta);
-    if constexpr (PF == 2) load(wb + T, tb);
-  }
+    __builtin_amdgcn_sched_barrier(0);
+    load(wb + T, tb);
+    if constexpr (PF == 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(wb + 2 * T, tc);
+    }
+  };
+  if (early) load_first();
 
-  // pair tables: each wave writes whole entries (entry index uniform across
-  // the wave, so the centroids are scalar loads), one copy per lane
-  // (quad entry e: codes e & 3, e >> 2 & 3, e >> 4 & 3, e >> 6; lane l of
-  // the wave writes dword l & 1 of copy l / 2)
-  if constexpr (KQ4) {
-#pragma unroll 8
-    for (int k = 0; k < 256 / W; ++k) {
-      const int e = wave + k * W;
-      const uint32_t lo = dev::pack_f16x2(a.cbk[e & 3], a.cbk[(e >> 2) & 3]);
-      const uint32_t hi = dev::pack_f16x2(a.cbk[(e >> 4) & 3], a.cbk[e >> 6]);
-      *reinterpret_cast<uint32_t*>(tabs + (e << 8) + (lane << 2)) = (lane & 1) ? hi : lo;
-    }
-  } else {
+  // Lookup tables. Each wave writes whole entries with a wave-uniform high
+  // code and compile-time low codes, from centroids loaded once (scalar
+  // loads of the kernel arguments); one copy per lane.
+  constexpr int LK = 1 << BK, LV = 1 << BV;
+  float ck[LK], cv[LV];
 #pragma unroll
-    for (int k = 0; k < KE / W; ++k) {
-      const int e = wave + k * W;
-      if (lane < 32)
-        *reinterpret_cast<uint32_t*>(tabs + (e << 7) + (lane << 2)) =
-            dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
+  for (int j = 0; j < LK; ++j) ck[j] = a.cbk[j];
+#pragma unroll
+  for (int j = 0; j < LV; ++j) cv[j] = a.cbv[j];
+  // quad entry e: codes e & 3, e >> 2 & 3, e >> 4 & 3, e >> 6; wave w writes
+  // the 32 entries with e >> 5 == w (c0, c1 from the low bits, compile-time;
+  // c2, c3 uniform); lane l writes dword l & 1 of copy l / 2
+  auto quad_table = [&](uint8_t* base, const float (&c)[4], const float* cu) {
+    static_assert(W == 8, "quad tables: 8 waves x 32 entries");
+    const float c3 = cu[wave >> 1];
+    const uint32_t hi0 = dev::pack_f16x2(cu[(2 * wave) & 3], c3);
+    const uint32_t hi1 = dev::pack_f16x2(cu[(2 * wave + 1) & 3], c3);
+    dev::static_for<0, 32>([&](auto rc) {
+      constexpr int r = decltype(rc)::value;
+      const uint32_t lo = dev::pack_f16x2(c[r & 3], c[(r >> 2) & 3]);
+      *reinterpret_cast<uint32_t*>(base + ((32 * wave + r) << 8) + (lane << 2)) =
+          (lane & 1) ? (r < 16 ? hi0 : hi1) : lo;
+    });
+  };
+  // pair entry e = hi << B | lo: (c[lo], c[hi]); wave w writes the entries
+  // with hi = w, w + 8; COPIES lanes write one copy each at stride SH bytes
+  auto pair_table = [&](uint8_t* base, const auto& c, const float* cu, auto bits_c,
+                        auto copies_c) {
+    constexpr int B = decltype(bits_c)::value, COPIES = decltype(copies_c)::value;
+    constexpr int L = 1 << B;
+    constexpr int SH = COPIES == 64 ? 8 : 7;
+#pragma unroll
+    for (int hi0 = 0; hi0 < L; hi0 += W) {
+      const int hi = hi0 + wave;
+      if (hi < L) {
+        const float ch = cu[hi];             // wave-uniform: a scalar load
+        dev::static_for<0, L>([&](auto lc) {
+          constexpr int lo = decltype(lc)::value;
+          if (COPIES == 64 || lane < 32)
+            *reinterpret_cast<uint32_t*>(base + (((hi << B) | lo) << SH) + (lane << 2)) =
+                dev::pack_f16x2(c[lo], ch);
+        });
+      }
     }
-  }
-  if constexpr (VQ4) {
-#pragma unroll 8
-    for (int k = 0; k < 256 / W; ++k) {
-      const int e = wave + k * W;
-      const uint32_t lo = dev::pack_f16x2(a.cbv[e & 3], a.cbv[(e >> 2) & 3]);
-      const uint32_t hi = dev::pack_f16x2(a.cbv[(e >> 4) & 3], a.cbv[e >> 6]);
-      *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << 8) + (lane << 2)) =
-          (lane & 1) ? hi : lo;
-    }
-  } else {
-#pragma unroll 8
-    for (int k = 0; k < VE / W; ++k) {
-      const int e = wave + k * W;
-      *reinterpret_cast<uint32_t*>(tabs + KT_BYTES + (e << 8) + (lane << 2)) =
-          dev::pack_f16x2(a.cbv[e & ((1 << BV) - 1)], a.cbv[e >> BV]);
-    }
-  }
+  };
+  if constexpr (KQ4) quad_table(tabs, ck, a.cbk);
+  else pair_table(tabs, ck, a.cbk, std::integral_constant<int, BK>{},
+                  std::integral_constant<int, 32>{});
+  if constexpr (VQ4) quad_table(tabs + KT_BYTES, cv, a.cbv);
+  else pair_table(tabs + KT_BYTES, cv, a.cbv, std::integral_constant<int, BV>{},
+                  std::integral_constant<int, 64>{});
   static_assert(KE % W == 0 && VE % W == 0 && 256 % W == 0,
                 "table entries split evenly over the waves");
   const uint8_t* vtab = tabs + KT_BYTES;
@@ -1417,35 +1472,6 @@ k_decode_mx(DecodeArgs a) {
       encode_append_row<D, BK, BV, 1>(a.enc, bkv, lane);
     else
       encode_append_row<D, BK, BV, 2>(a.enc, bkv, lane);
-  }
-  // the GK query rows, rotated and scaled here (one 16-lane group per head):
-  // R q * scale * log2(e), as fp16 pairs
-  if (tid < 16 * GK) {
-    constexpr int E = D / 16;
-    const int g = tid >> 4, l16 = tid & 15;
-    float v[E];
-    dev::load_row_part<E>(a.q_raw, a.q_dtype, (head0 + g) * D + l16 * E, v);
-    const uint32_t smask = dev::bitmap_bits(a.sbits, l16 * E, E);
-#pragma unroll
-    for (int i = 0; i < E; ++i) if (smask >> i & 1) v[i] = -v[i];
-    dev::fwht16<E, float>(v, l16);
-    const float mult = a.qmult / sqrtf(float(D));
-#pragma unroll
-    for (int i = 0; i < E; ++i) v[i] *= mult;
-#pragma unroll
-    for (int i = 0; i < E / 2; ++i)
-      qs[g * (D / 2) + l16 * (E / 2) + i] = dev::pack_f16x2(v[2 * i], v[2 * i + 1]);
-    if constexpr (QJL) {
-      // q'' = R_2 q' from the fp32 q'
-      const uint32_t qmask = dev::bitmap_bits(a.qsbits, l16 * E, E);
-#pragma unroll
-      for (int i = 0; i < E; ++i) if (qmask >> i & 1) v[i] = -v[i];
-      dev::fwht16<E, float>(v, l16);
-      const float nn = 1.0f / sqrtf(float(D));
-#pragma unroll
-      for (int i = 0; i < E / 2; ++i)
-        qs2[g * (D / 2) + l16 * (E / 2) + i] = dev::pack_f16x2(v[2 * i] * nn, v[2 * i + 1] * nn);
-    }
   }
   __syncthreads();
 
@@ -1624,27 +1650,21 @@ k_decode_mx(DecodeArgs a) {
   {
     uint32_t* px0 = pex[wave][0];
     uint32_t* px1 = pex[wave][1];
+    if (!early) load_first();
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (PF == 1) {
-      if (!early) load(wb, ta);
-      __builtin_amdgcn_sched_barrier(0);
       for (int it = 0; it < iters; it += 2) {
         const int64_t base = wb + int64_t(it) * T;
-        load(base + T, tb);
         process(base, px0, ta);
         if (it + 1 >= iters) break;
         load(base + 2 * T, ta);
         process(base + T, px1, tb);
+        if (it + 2 >= iters) break;
+        load(base + 3 * T, tb);
       }
     } else {
-      if (!early) {
-        load(wb, ta);
-        __builtin_amdgcn_sched_barrier(0);
-        load(wb + T, tb);
-      }
-      __builtin_amdgcn_sched_barrier(0);
       for (int it = 0; it < iters; it += 3) {
         const int64_t base = wb + int64_t(it) * T;
-        load(base + 2 * T, tc);
         process(base, px0, ta);
         if (it + 1 >= iters) break;
         load(base + 3 * T, ta);
@@ -1652,15 +1672,20 @@ k_decode_mx(DecodeArgs a) {
         if (it + 2 >= iters) break;
         load(base + 4 * T, tb);
         process(base + 2 * T, px0, tc);
+        if (it + 3 >= iters) break;
+        load(base + 5 * T, tc);
       }
     }
   }
 
-  // ---------------- combine the waves of this split (rotated frame)
+  // ---------------- combine the waves of this split (rotated frame): each
+  // wave leaves (max, sum) and its unscaled weighted sums in LDS, then every
+  // thread rescales and adds the W waves' values of its coordinate
   float lw[GK];
 #pragma unroll
   for (int g = 0; g < GK; ++g) lw[g] = dev::wave_sum(lpart[g]);
   __syncthreads();                       // tables are dead: reuse them below
+  float* slab = reinterpret_cast<float*>(tabs);          // [W][GK][D]
   if (lane == 0) {
 #pragma unroll
     for (int g = 0; g < GK; ++g) {
@@ -1668,19 +1693,11 @@ k_decode_mx(DecodeArgs a) {
       mlx[wave][g][1] = lw[g];
     }
   }
-  __syncthreads();
-  float* slab = reinterpret_cast<float*>(tabs);          // [W][GK][D]
-  float M[GK];
+  if (lane < 16) {
 #pragma unroll
-  for (int g = 0; g < GK; ++g) {
-    M[g] = mlx[0][g][0];
+    for (int g = 0; g < GK; ++g)
 #pragma unroll
-    for (int w = 1; w < W; ++w) M[g] = fmaxf(M[g], mlx[w][g][0]);
-    const float f = m_run[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[g] - M[g]);
-    if (lane < 16) {
-#pragma unroll
-      for (int j = 0; j < VJ; ++j) slab[(wave * GK + g) * D + VJ * lane + j] = acc[j][g] * f;
-    }
+      for (int j = 0; j < VJ; ++j) slab[(wave * GK + g) * D + VJ * lane + j] = acc[j][g];
   }
   __syncthreads();
   // This split's partial, (max, sum) per head and the weighted value sum in
@@ -1688,19 +1705,20 @@ k_decode_mx(DecodeArgs a) {
   // this XCD's L2, so the workgroup that merges the unit (on any XCD) reads
   // them without an L2 write-back here.
   for (int i = tid; i < GK * D; i += NT) {
-    float sum = 0.f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) sum += slab[w * GK * D + i];
     const int g = i / D;
-    dev::store_dev(a.acc + ((head0 + g) * a.S + split) * D + (i - g * D), sum);
-  }
-  if (tid < GK) {
-    float l = 0.f;
+    float Mg = mlx[0][g][0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) Mg = fmaxf(Mg, mlx[w][g][0]);
+    float sum = 0.f, l = 0.f;
+#pragma unroll
     for (int w = 0; w < W; ++w) {
-      const float mw = mlx[w][tid][0];
-      if (mw != -INFINITY) l += mlx[w][tid][1] * __builtin_amdgcn_exp2f(mw - M[tid]);
+      const float mw = mlx[w][g][0];
+      const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - Mg);
+      sum = fmaf(slab[w * GK * D + i], f, sum);
+      l = fmaf(mlx[w][g][1], f, l);
     }
-    dev::store_dev2(a.ml + ((head0 + tid) * a.S + split) * 2, M[tid], l);
+    dev::store_dev(a.acc + ((head0 + g) * a.S + split) * D + (i - g * D), sum);
+    if (i - g * D == 0) dev::store_dev2(a.ml + ((head0 + g) * a.S + split) * 2, Mg, l);
   }
   // every store of this workgroup has completed before the arrival count
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1712,36 +1730,73 @@ k_decode_mx(DecodeArgs a) {
   if (!last_arrival) return;
 
   // ---------------- last split of the unit: merge the S partials of each
-  // head in split order (online log-sum-exp), then R^T, then the output
+  // head (online log-sum-exp), then R^T, then the output. Thread (sg, item)
+  // merges splits sg, sg + SG, ... of four coordinates (one 16-byte load per
+  // split, device-scope so that no stale L2 line is read); the SG partial
+  // merges of an item are then combined in split-group order through LDS.
+  constexpr int ITEMS = GK * D / 4;
+  constexpr int SG = NT / ITEMS;
+  static_assert(NT % ITEMS == 0 && SG >= 1, "merge work split");
   float* obuf = reinterpret_cast<float*>(pex);            // [GK][D]
+  float* mpart = reinterpret_cast<float*>(tabs);          // [SG][ITEMS][6]
+  static_assert(sizeof(tabs) >= NT * 6 * 4, "merge partials fit the table space");
   static_assert(sizeof(pex) >= GK * D * 4, "output staging fits the weight slots");
-  for (int i = tid; i < GK * D; i += NT) {
-    const int g = i / D;
-    const float* pm = a.ml + (head0 + g) * a.S * 2;
-    const float* pa = a.acc + (head0 + g) * a.S * D + (i - g * D);
-    float Mx = -INFINITY, L = 0.f, sum = 0.f;
-    constexpr int U = 16;
-    for (int s0 = 0; s0 < a.S; s0 += U) {
-      float mv[U], lv[U], av[U];
+  {
+    const int item = tid % ITEMS, sg = tid / ITEMS;
+    const int g = item / (D / 4), c4 = item % (D / 4);
+    // one descriptor per plane over this unit's GK heads (wave-uniform base);
+    // a split past S is masked below (past the last head it reads as zero)
+    const auto racc = dev::buffer_rsrc(a.acc + head0 * a.S * D, uint32_t(GK * a.S) * D * 4);
+    const auto rml = dev::buffer_rsrc(a.ml + head0 * a.S * 2, uint32_t(GK * a.S) * 8);
+    float Mx = -INFINITY, L = 0.f, sum[4] = {0.f, 0.f, 0.f, 0.f};
+    constexpr int U = 8;
+    constexpr int kDev = 16;                 // cache policy: device scope (sc1)
+    for (int s0 = sg; s0 < a.S; s0 += U * SG) {
+      mx_u4 av[U];
+      mx_u2 mv[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int sp = s0 + u < a.S ? s0 + u : a.S - 1;
-        dev::load_dev2(pm + 2 * sp, &mv[u], &lv[u]);
-        av[u] = dev::load_dev(pa + int64_t(sp) * D);
+        const uint32_t sp = uint32_t(g * a.S + s0 + u * SG);
+        av[u] = __builtin_amdgcn_raw_buffer_load_b128(racc, sp * (D * 4) + c4 * 16, 0, kDev);
+        mv[u] = __builtin_amdgcn_raw_buffer_load_b64(rml, sp * 8, 0, kDev);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if (s0 + u < a.S && mv[u] != -INFINITY) {
-          const float nm = fmaxf(Mx, mv[u]);
+        const float m = __uint_as_float(mv[u][0]);
+        if (s0 + u * SG < a.S && m != -INFINITY) {
+          const float nm = fmaxf(Mx, m);
           const float a1 = __builtin_amdgcn_exp2f(Mx - nm);
-          const float a2 = __builtin_amdgcn_exp2f(mv[u] - nm);
-          sum = fmaf(av[u], a2, sum * a1);
-          L = fmaf(lv[u], a2, L * a1);
+          const float a2 = __builtin_amdgcn_exp2f(m - nm);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) sum[k] = fmaf(__uint_as_float(av[u][k]), a2, sum[k] * a1);
+          L = fmaf(__uint_as_float(mv[u][1]), a2, L * a1);
           Mx = nm;
         }
       }
     }
-    obuf[i] = sum / L;
+    float* mp = mpart + (sg * ITEMS + item) * 6;
+    mp[0] = Mx;
+    mp[1] = L;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mp[2 + k] = sum[k];
+  }
+  __syncthreads();
+  if (tid < ITEMS) {
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < SG; ++q) Mx = fmaxf(Mx, mpart[(q * ITEMS + tid) * 6]);
+    float L = 0.f, sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < SG; ++q) {
+      const float* mp = mpart + (q * ITEMS + tid) * 6;
+      const float f = mp[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp[0] - Mx);
+      L = fmaf(mp[1], f, L);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) sum[k] = fmaf(mp[2 + k], f, sum[k]);
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) obuf[4 * tid + k] = sum[k] * inv;
   }
   __syncthreads();
   if (tid < 16 * GK) {
