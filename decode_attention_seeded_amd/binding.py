@@ -31,7 +31,8 @@ TQ_CODEBOOK_GAUSS, TQ_CODEBOOK_SPHERE = 0, 1
 EXPORTS = (
     "tq_bits_split", "tq_codebook", "tq_codebook_ex", "tq_signs", "tq_cache_bytes", "tq_rht",
     "tq_encode_kv", "tq_qjl_sketch", "tq_num_splits", "tq_workspace_bytes",
-    "tq_attend_decode", "tq_append_attend_decode", "tq_dense_workspace_bytes",
+    "tq_attend_decode", "tq_attend_decode_noalloc", "tq_append_attend_decode",
+    "tq_dense_workspace_bytes",
     "tq_dense_decode_bf16", "tq_attend_prefill", "tq_read_probe_sink_words",
     "tq_read_probe", "tq_affine_cache_bytes", "tq_affine_encode_kv", "tq_affine_num_splits",
     "tq_affine_workspace_bytes", "tq_affine_attend_decode",
@@ -97,6 +98,7 @@ def _lib():
             "tq_num_splits": (I, [CFG, I, I, I, I64, I]),
             "tq_workspace_bytes": (I64, [CFG, I, I, I, I64, I]),
             "tq_attend_decode": (I, [CFG, P, I, I, I, CACHE, I64, F, I, P, P, SZ, P]),
+            "tq_attend_decode_noalloc": (I, [CFG, P, I, I, I, CACHE, I64, F, I, P, P]),
             "tq_append_attend_decode": (I, [CFG, P, P, I, P, I, I, I, CACHE, I64, F, I, P, P,
                                             SZ, P]),
             "tq_dense_workspace_bytes": (I64, [I, I, I, I, I64, I]),
@@ -314,6 +316,20 @@ def tq_attend_decode(cfg: Config, q, cache: PackedCache, n_ctx: int, out, ws,
                                    ctypes.byref(c), n_ctx, float(scale), splits, _ptr(out),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "tq_attend_decode")
+
+
+def tq_attend_decode_noalloc(cfg: Config, q, cache: PackedCache, n_ctx: int, out,
+                             scale: float = 0.0, splits: int = 0, stream=None):
+    """tq_attend_decode without a workspace: the library's static per-GPU
+    scratch buffer holds the split partials (calls must not overlap on one
+    GPU)."""
+    B, Hq, d = q.shape
+    if d != cfg.d or not q.is_contiguous() or tuple(out.shape) != (B, Hq, d):
+        raise TqError(TQ_ERR_ARG, "tq_attend_decode_noalloc: q/out must be [B][Hq][d] contiguous")
+    c = cache.c()
+    _check(_lib().tq_attend_decode_noalloc(ctypes.byref(cfg.c()), _ptr(q), _dtype_code(q), B, Hq,
+                                           ctypes.byref(c), n_ctx, float(scale), splits, _ptr(out),
+                                           _stream(stream)), "tq_attend_decode_noalloc")
 
 
 def tq_dense_decode_bf16(q, k, v, out, ws, scale: float = 0.0, splits: int = 0, stream=None):

@@ -2,6 +2,7 @@
 // kernel launches. Every argument is checked before the first HIP call.
 
 #include <cmath>
+#include <mutex>
 
 #include "tq_internal.h"
 #include "tq_kernels.h"
@@ -266,6 +267,43 @@ int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
 }
 
 }  // namespace
+}  // namespace tq
+
+// ---------------------------------------------------------------------------
+// Allocation-free decode: the split partials and the arrival counters live in
+// this file-scope device array instead of a caller workspace. Each GPU the
+// library runs on holds its own copy until the process ends; it starts zeroed
+// and every decode leaves its counters at zero again. Host code must use the
+// per-device address from hipGetSymbolAddress, never the array's name.
+// ---------------------------------------------------------------------------
+
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace tq {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up once per device with
+// that device current.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TQ_ERR_NO_DEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return TQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TQ_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return TQ_OK;
+}
+
+}  // namespace
 // ---------------------------------------------------------------------------
 // Streaming-read probe: every 16-byte chunk of the buffer is loaded once
 // with nontemporal (streaming) loads, four chunks in flight per lane,
@@ -366,6 +404,30 @@ int tq_attend_decode(const tq_config* cfg, const void* q, int q_dtype, int B, in
                      void* ws, size_t ws_bytes, hipStream_t stream) {
   return attend(cfg, q, q_dtype, B, Hq, cache, n_ctx, scale, splits, out, ws, ws_bytes, stream,
                 nullptr);
+}
+
+int tq_attend_decode_noalloc(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
+                             const tq_cache* cache, int64_t n_ctx, float scale, int splits,
+                             float* out, hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  st = check_cache(cfg, cache);
+  if (st != TQ_OK) return st;
+  if (B != cache->B || Hq < 1 || Hq % cache->Hkv != 0 || splits < 0 || n_ctx < 1)
+    return TQ_ERR_ARG;
+  if (n_ctx > cache->capacity) return TQ_ERR_CAPACITY;
+  if (B == 0) return TQ_OK;
+  DecodePlan p;
+  st = plan_decode(cfg->d, cfg->bits_v, cfg->qjl, B, Hq, cache->Hkv, n_ctx, splits, &p);
+  if (st != TQ_OK) return st;
+  if (p.total > kScratchBytes) return TQ_ERR_WORKSPACE;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != TQ_OK) return st;
+  return attend(cfg, q, q_dtype, B, Hq, cache, n_ctx, scale, splits, out, ws, kScratchBytes,
+                stream, nullptr);
 }
 
 int tq_append_attend_decode(const tq_config* cfg, const void* k_new, const void* v_new,

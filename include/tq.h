@@ -221,6 +221,22 @@ int tq_attend_decode(const tq_config* cfg, const void* q, int q_dtype, int B,
                      hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as tq_attend_decode, with the same arguments minus the workspace.
+ * The split partials and arrival counters live in a static 8 MiB device
+ * buffer inside the library, one per GPU, held until the process ends; the
+ * library allocates and frees nothing. Returns TQ_ERR_WORKSPACE, before any
+ * HIP call, when the call needs more than 8 MiB (tq_workspace_bytes() of the
+ * same arguments), e.g. B * Hq * splits * (d + 2) * 4 bytes beyond ~7.7 MiB.
+ * Every call on one GPU shares that buffer: calls that overlap in time on the
+ * same GPU (two streams, two host threads) race and must not be issued.
+ */
+int tq_attend_decode_noalloc(const tq_config* cfg, const void* q, int q_dtype, int B,
+                             int Hq, const tq_cache* cache, int64_t n_ctx, float scale,
+                             int splits, float* out, hipStream_t stream);
+
+/*
  * One generation step: append the newest token, then attend (README, "How it
  * plugs in": the cache stores the new rotated key and value, then the
  * patched scaled_dot_product_attention runs on the rotated query; API page,
