@@ -143,6 +143,12 @@ __device__ __forceinline__ void fwht16(T (&v)[E], int l16) {
   }
 }
 
+__device__ __forceinline__ float group_max16(float x) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 16));
+  return x;
+}
+
 template <typename T>
 __device__ __forceinline__ T group16_sum(T x) {
 #pragma unroll

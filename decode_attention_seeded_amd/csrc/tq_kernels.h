@@ -511,15 +511,24 @@ __global__ void __launch_bounds__(256) k_qprep(QPrepArgs a) {
 #pragma unroll
   for (int i = 0; i < E; ++i) v[i] *= mult;
   if (a.pairs) {
-    // fp16 pairs (v_2m, v_2m+1), D/2 dwords per head
+    // fp16 pairs (v_2m, v_2m+1), D/2 dwords per head, scaled by a power of
+    // two 2^-e that puts the head's largest element near 2^10 (no fp16
+    // overflow or subnormals); e follows the pairs of all heads as one int
+    // per head (read by the decode kernel, which undoes it in fp32)
+    float vmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) vmax = fmaxf(vmax, fabsf(v[i]));
+    vmax = dev::group_max16(vmax);
+    const int qe = vmax > 0.f ? ilogbf(vmax) - 10 : 0;
     uint4* dst = reinterpret_cast<uint4*>(reinterpret_cast<uint32_t*>(a.qp) + row * (D / 2) +
                                           l16 * (E / 2));
 #pragma unroll
     for (int k = 0; k < E / 8; ++k)
-      dst[k] = make_uint4(dev::pack_f16x2(v[8 * k], v[8 * k + 1]),
-                          dev::pack_f16x2(v[8 * k + 2], v[8 * k + 3]),
-                          dev::pack_f16x2(v[8 * k + 4], v[8 * k + 5]),
-                          dev::pack_f16x2(v[8 * k + 6], v[8 * k + 7]));
+      dst[k] = make_uint4(dev::pack_f16x2(ldexpf(v[8 * k], -qe), ldexpf(v[8 * k + 1], -qe)),
+                          dev::pack_f16x2(ldexpf(v[8 * k + 2], -qe), ldexpf(v[8 * k + 3], -qe)),
+                          dev::pack_f16x2(ldexpf(v[8 * k + 4], -qe), ldexpf(v[8 * k + 5], -qe)),
+                          dev::pack_f16x2(ldexpf(v[8 * k + 6], -qe), ldexpf(v[8 * k + 7], -qe)));
+    if (l16 == 0) reinterpret_cast<int*>(a.qp)[a.heads * (D / 2) + row] = qe;
   } else {
     float4* dst = reinterpret_cast<float4*>(a.qp + row * D + l16 * E);
 #pragma unroll
@@ -847,7 +856,7 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 
   __shared__ __attribute__((aligned(16))) uint8_t tabs[KT_BYTES + VT_BYTES];
   __shared__ uint32_t pv2[(T / 2) * GK];
-  __shared__ float red[W * GK];
+  __shared__ float red[W * (GK + 1)];           // per-wave maxima: scores, then nv
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -881,6 +890,20 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   const int64_t row0 = int64_t(bkv) * a.capacity;
   const float* qq_base = QJL ? qq_all + head0 * D : nullptr;
   const bool nf16 = a.norm_f16 != 0;
+  // key scale per head with the query pairs' power of two undone (the
+  // exponents follow the pairs of all B * Hq heads)
+  float ksg[GK];
+  {
+    const int64_t heads_total = int64_t(gridDim.y / (a.Hkv * a.chunks)) * a.Hq;
+    const int* qexp = reinterpret_cast<const int*>(qp2_all) + heads_total * (D / 2) + head0;
+#pragma unroll
+    for (int g = 0; g < GK; ++g) ksg[g] = ldexpf(a.kscale, qexp[g]);
+  }
+  // value weights p * nv go to fp16 with p <= 2^8; nv carries a
+  // workgroup-uniform power of two 2^-vexp that keeps each tile's largest
+  // value norm within [2^-6, 2^6] (moved only when a tile leaves that band)
+  float vsc = a.vscale;
+  int vexp = 0;
 
   // The GK x D/2 rotated query pairs stay in VGPRs for the whole split:
   // register r of lane l holds pair 16 r + (l & 15), so every 16-lane row
@@ -992,10 +1015,9 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
     }
     if (valid) {
       const float knrm = nf16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
-      const float ks = knrm * a.kscale;
 #pragma unroll
-      for (int g = 0; g < GK; ++g) s[g] *= ks;
-      nv = (nf16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn)) * a.vscale;
+      for (int g = 0; g < GK; ++g) s[g] *= knrm * ksg[g];
+      nv = (nf16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn)) * vsc;
       if constexpr (QJL) {
         const dev::const_f32_ptr qq = dev::as_const(qqr);
         float tq[GK];
@@ -1019,7 +1041,26 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
       const float mx = dev::dpp_wave_max(valid ? s[g] : -INFINITY);
       if (lane == 0) red[wave * GK + g] = mx;
     }
+    {
+      const float nvm = dev::dpp_wave_max(nv);
+      if (lane == 0) red[W * GK + wave] = nvm;
+    }
     __syncthreads();
+    {
+      float tnv = red[W * GK];
+#pragma unroll
+      for (int w = 1; w < W; ++w) tnv = fmaxf(tnv, red[W * GK + w]);
+      if (tnv > 64.f || (tnv > 0.f && tnv < 0.015625f)) {   // uniform, rare
+        const int sh = ilogbf(tnv) - 4;
+        vsc = ldexpf(vsc, -sh);
+        vexp += sh;
+        nv = ldexpf(nv, -sh);
+#pragma unroll
+        for (int g = 0; g < GK; ++g)
+#pragma unroll
+          for (int c = 0; c < CW; ++c) acc[g][c] = ldexpf(acc[g][c], -sh);
+      }
+    }
     uint16_t* pv16 = reinterpret_cast<uint16_t*>(pv2);
     const int pslot = ((tid >> 7) * 64 + (tid & 63)) * GK;
     const int phalf = (tid >> 6) & 1;
@@ -1134,7 +1175,7 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
   for (int i = 0; i < dev::reduce_kept<NV>(); ++i) {
     bool writer;
     const int idx = dev::reduce_index<NV>(lane, i, &writer);
-    if (writer) obuf[(idx / CW) * D + wave * CW + idx % CW] = flat[i];
+    if (writer) obuf[(idx / CW) * D + wave * CW + idx % CW] = ldexpf(flat[i], vexp);
   }
   __syncthreads();
   if (tid < GK) {
@@ -1255,6 +1296,8 @@ k_decode_mx(DecodeArgs a) {
   __shared__ uint32_t qs[GK * (D / 2)];
   __shared__ uint32_t qs2[QJL ? GK * (D / 2) : 1];
   __shared__ float mlx[W][GK][2];
+  __shared__ int vexp_w[W];                    // each wave's value exponent (below)
+  __shared__ int qexp;                         // the query's power-of-two scale
   __shared__ bool last_arrival;
 
   const int tid = threadIdx.x;
@@ -1362,19 +1405,40 @@ k_decode_mx(DecodeArgs a) {
     const float mult = a.qmult / sqrtf(float(D));
 #pragma unroll
     for (int i = 0; i < QE; ++i) v[i] *= mult;
+    float v2[QJL ? QE : 1];
+    float vmax = 0.f;
 #pragma unroll
-    for (int i = 0; i < QE / 2; ++i)
-      qs[g * (D / 2) + l16 * (QE / 2) + i] = dev::pack_f16x2(v[2 * i], v[2 * i + 1]);
+    for (int i = 0; i < QE; ++i) vmax = fmaxf(vmax, fabsf(v[i]));
     if constexpr (QJL) {
       // q'' = R_2 q' from the fp32 q'
       const uint32_t qmask = dev::bitmap_bits(a.qsbits, l16 * QE, QE);
 #pragma unroll
-      for (int i = 0; i < QE; ++i) if (qmask >> i & 1) v[i] = -v[i];
-      dev::fwht16<QE, float>(v, l16);
+      for (int i = 0; i < QE; ++i) v2[i] = (qmask >> i & 1) ? -v[i] : v[i];
+      dev::fwht16<QE, float>(v2, l16);
       const float nn = 1.0f / sqrtf(float(D));
 #pragma unroll
+      for (int i = 0; i < QE; ++i) {
+        v2[i] *= nn;
+        vmax = fmaxf(vmax, fabsf(v2[i]));
+      }
+    }
+    // one power of two for the GK rows (q' and q'') puts their largest
+    // element near 2^10, so the fp16 operands neither overflow nor lose
+    // small elements to subnormals; it is undone in fp32 with the key scale
+    vmax = dev::group_max16(vmax);
+    if constexpr (GK >= 2) vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+    if constexpr (GK >= 4) vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+    const int qe = vmax > 0.f ? ilogbf(vmax) - 10 : 0;
+    if (tid == 0) qexp = qe;
+#pragma unroll
+    for (int i = 0; i < QE / 2; ++i)
+      qs[g * (D / 2) + l16 * (QE / 2) + i] =
+          dev::pack_f16x2(ldexpf(v[2 * i], -qe), ldexpf(v[2 * i + 1], -qe));
+    if constexpr (QJL) {
+#pragma unroll
       for (int i = 0; i < QE / 2; ++i)
-        qs2[g * (D / 2) + l16 * (QE / 2) + i] = dev::pack_f16x2(v[2 * i] * nn, v[2 * i + 1] * nn);
+        qs2[g * (D / 2) + l16 * (QE / 2) + i] =
+            dev::pack_f16x2(ldexpf(v2[2 * i], -qe), ldexpf(v2[2 * i + 1], -qe));
     }
   }
   constexpr int PF = mx_prefetch(D, BK, QJL);
@@ -1503,6 +1567,16 @@ k_decode_mx(DecodeArgs a) {
   const int pslot = (lane & 0x30) | ((lane & 3) << 2) | ((lane >> 2) & 3);
 
   float m_run[GK], lpart[GK];
+  // key and QJL scales with the query's power of two undone (fp32)
+  const float kscale = ldexpf(a.kscale, qexp);
+  const float qjl_c = ldexpf(a.qjl_c, qexp);
+  // The weights p * nv enter the value product as fp16, with p <= 2^8 (the
+  // lazily raised max). nv carries a wave-uniform power of two 2^-vexp that
+  // keeps the tile's value norms within [2^-6, 2^6]: only when a tile leaves
+  // that band is it moved (and the accumulators with it), so large or tiny
+  // value norms neither overflow fp16 nor fall into its subnormals.
+  float vsc = a.vscale;                        // a.vscale * 2^-vexp
+  int vexp = 0;
   mx_f4 acc[VJ];
 #pragma unroll
   for (int g = 0; g < GK; ++g) {
@@ -1546,9 +1620,23 @@ k_decode_mx(DecodeArgs a) {
     });
     const float knrm = NF16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
     const float vnrm = NF16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn);
-    const float ks = knrm * a.kscale;
-    const float nv = vnrm * a.vscale;
-    const float rho = QJL ? dev::f16_to_f32(cur.kr) * a.qjl_c : 0.f;
+    const float ks = knrm * kscale;
+    float nv = vnrm * vsc;
+    const float rho = QJL ? dev::f16_to_f32(cur.kr) * qjl_c : 0.f;
+    {
+      const bool high = __ballot(nv > 64.f) != 0;
+      const bool low = __ballot(nv >= 0.015625f) == 0 && __ballot(nv > 0.f) != 0;
+      if (high || low) {                      // wave-uniform, rare
+        const int sh = ilogbf(dev::dpp_wave_max(nv)) - 4;
+        vsc = ldexpf(vsc, -sh);
+        vexp += sh;
+        nv = ldexpf(nv, -sh);
+#pragma unroll
+        for (int j = 0; j < VJ; ++j)
+#pragma unroll
+          for (int g = 0; g < GK; ++g) acc[j][g] = ldexpf(acc[j][g], -sh);
+      }
+    }
 
     // ---------------- online softmax with a lazily raised running max
     uint16_t* p16 = reinterpret_cast<uint16_t*>(px);
@@ -1692,6 +1780,7 @@ k_decode_mx(DecodeArgs a) {
       mlx[wave][g][0] = m_run[g];
       mlx[wave][g][1] = lw[g];
     }
+    vexp_w[wave] = vexp;
   }
   if (lane < 16) {
 #pragma unroll
@@ -1714,7 +1803,7 @@ k_decode_mx(DecodeArgs a) {
     for (int w = 0; w < W; ++w) {
       const float mw = mlx[w][g][0];
       const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - Mg);
-      sum = fmaf(slab[w * GK * D + i], f, sum);
+      sum = fmaf(slab[w * GK * D + i], ldexpf(f, vexp_w[w]), sum);
       l = fmaf(mlx[w][g][1], f, l);
     }
     dev::store_dev(a.acc + ((head0 + g) * a.S + split) * D + (i - g * D), sum);

@@ -136,17 +136,18 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   for (int e = tid; e < VE; e += NT)
     vone[e] = __builtin_bit_cast(uint16_t, _Float16(a.cbv[e]));
 
-  // ---------------- the wave's 16 query rows: R q * scale * log2(e), fp16
+  // ---------------- the wave's 16 query rows: R q * scale * log2(e), fp16.
+  // A first pass finds the largest element of the wave's rows (q' and q''),
+  // the second stores them scaled by one power of two 2^-qe that puts it
+  // near 2^10 (no fp16 overflow or subnormals); the scores undo it in fp32.
   _Float16* qst = reinterpret_cast<_Float16*>(smem);
+  int qe = 0;
   {
     const int l16 = lane & 15;
     const uint32_t smask = dev::bitmap_bits(a.sbits, l16 * E, E);
     const float mult = a.qmult / sqrtf(float(D));
-#pragma unroll
-    for (int pass = 0; pass < 4 * RB; ++pass) {
-      const int m = 16 * RB * wave + 4 * pass + (lane >> 4);
-      const int64_t r = r0 + m;
-      float v[E];
+    auto row = [&](int pass, float (&v)[E], float (&v2)[E]) {
+      const int64_t r = r0 + 16 * RB * wave + 4 * pass + (lane >> 4);
 #pragma unroll
       for (int i = 0; i < E; ++i) v[i] = 0.f;
       if (r < R) {
@@ -158,22 +159,44 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
       for (int i = 0; i < E; ++i) if (smask >> i & 1) v[i] = -v[i];
       dev::fwht16<E, float>(v, l16);
 #pragma unroll
-      for (int i = 0; i < E; ++i) {
-        v[i] *= mult;
-        qst[m * KS + l16 * E + i] = _Float16(v[i]);
-      }
+      for (int i = 0; i < E; ++i) v[i] *= mult;
       if constexpr (QJL) {
         // q'' = R_2 q' from the fp32 q'
         const uint32_t qmask = dev::bitmap_bits(a.qsbits, l16 * E, E);
 #pragma unroll
-        for (int i = 0; i < E; ++i) if (qmask >> i & 1) v[i] = -v[i];
-        dev::fwht16<E, float>(v, l16);
+        for (int i = 0; i < E; ++i) v2[i] = (qmask >> i & 1) ? -v[i] : v[i];
+        dev::fwht16<E, float>(v2, l16);
         const float nn = 1.0f / sqrtf(float(D));
 #pragma unroll
-        for (int i = 0; i < E; ++i) qst[(NR + m) * KS + l16 * E + i] = _Float16(v[i] * nn);
+        for (int i = 0; i < E; ++i) v2[i] *= nn;
+      }
+    };
+    float vmax = 0.f;
+#pragma unroll 1
+    for (int pass = 0; pass < 4 * RB; ++pass) {
+      float v[E], v2[E];
+      row(pass, v, v2);
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        vmax = fmaxf(vmax, fabsf(v[i]));
+        if constexpr (QJL) vmax = fmaxf(vmax, fabsf(v2[i]));
+      }
+    }
+    vmax = dev::wave_max(vmax);
+    qe = vmax > 0.f ? ilogbf(vmax) - 10 : 0;
+#pragma unroll 1
+    for (int pass = 0; pass < 4 * RB; ++pass) {
+      const int m = 16 * RB * wave + 4 * pass + (lane >> 4);
+      float v[E], v2[E];
+      row(pass, v, v2);
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        qst[m * KS + l16 * E + i] = _Float16(ldexpf(v[i], -qe));
+        if constexpr (QJL) qst[(NR + m) * KS + l16 * E + i] = _Float16(ldexpf(v2[i], -qe));
       }
     }
   }
+  const float qsc = ldexpf(1.f, qe);     // undoes the query rows' power of two
   __syncthreads();
   pf_h8 qb[RB][NK];
   pf_h8 qb2[QJL ? RB : 1][QJL ? NK : 1];
@@ -240,6 +263,7 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   };
 
   float m_run[RB], l_run[RB];
+  int vexp = 0;                         // value norms carry 2^-vexp (below)
   pf_f4 o[RB][NS];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -333,11 +357,11 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
         }
       }
       const float4 ks = *reinterpret_cast<const float4*>(&tks[buf][16 * tb + 4 * kq]);
-      const float kss[4] = {ks.x, ks.y, ks.z, ks.w};
+      const float kss[4] = {ks.x * qsc, ks.y * qsc, ks.z * qsc, ks.w * qsc};
       float rhs[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (QJL) {
         const float4 rh = *reinterpret_cast<const float4*>(&trho[buf][16 * tb + 4 * kq]);
-        rhs[0] = rh.x; rhs[1] = rh.y; rhs[2] = rh.z; rhs[3] = rh.w;
+        rhs[0] = rh.x * qsc; rhs[1] = rh.y * qsc; rhs[2] = rh.z * qsc; rhs[3] = rh.w * qsc;
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
@@ -363,10 +387,40 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
     float ls[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) ls[rb] = 0.f;
+    // the weights p * nv (p <= 1) go to fp16: nv carries a workgroup-uniform
+    // power of two 2^-vexp that keeps the tile's largest value norm within
+    // [2^-6, 2^6], moved (with the accumulators) only when a tile leaves it
+    float nvt[4][4];
+    float nvmax = 0.f;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const float4 nv = *reinterpret_cast<const float4*>(&tnv[buf][16 * tb + 4 * kq]);
-      const float nvs[4] = {nv.x, nv.y, nv.z, nv.w};
+      nvt[tb][0] = ldexpf(nv.x, -vexp);
+      nvt[tb][1] = ldexpf(nv.y, -vexp);
+      nvt[tb][2] = ldexpf(nv.z, -vexp);
+      nvt[tb][3] = ldexpf(nv.w, -vexp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nvmax = fmaxf(nvmax, nvt[tb][i]);
+    }
+    nvmax = fmaxf(nvmax, __shfl_xor(nvmax, 16));
+    nvmax = fmaxf(nvmax, __shfl_xor(nvmax, 32));
+    if (nvmax > 64.f || (nvmax > 0.f && nvmax < 0.015625f)) {   // uniform, rare
+      const int sh = ilogbf(nvmax) - 4;
+      vexp += sh;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nvt[tb][i] = ldexpf(nvt[tb][i], -sh);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[rb][j][i] = ldexpf(o[rb][j][i], -sh);
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      const float (&nvs)[4] = nvt[tb];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -422,7 +476,7 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float l = __shfl(l_run[rb], 4 * kq + i);
-      il[i] = l > 0.f ? 1.f / l : 0.f;
+      il[i] = l > 0.f ? ldexpf(1.f / l, vexp) : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < NS; ++j)

@@ -214,6 +214,15 @@ int64_t tq_workspace_bytes(const tq_config* cfg, int B, int Hq, int Hkv,
  *        its first use (see tq_workspace_bytes).
  * n_ctx must be in [1, capacity]. The result does not depend on host
  * threads or on timing: partials are merged in a fixed order.
+ * Precision and range: products run on fp16 operands with fp32
+ * accumulation. The rotated query and the softmax weights times the value
+ * norms are scaled by powers of two (undone in fp32) that keep them inside
+ * fp16's normal range for any finite input, so large or tiny values and
+ * queries neither overflow nor flush to zero. The query is rounded to fp16
+ * (relative 2^-11 per element), so a score's error grows with |q| |k|: the
+ * output's max row-relative error against fp64 is about 5e-4 for
+ * unit-variance q and k (scores spanning a few log2 units) and about 2e-3
+ * when q is 10x larger.
  */
 int tq_attend_decode(const tq_config* cfg, const void* q, int q_dtype, int B,
                      int Hq, const tq_cache* cache, int64_t n_ctx, float scale,
