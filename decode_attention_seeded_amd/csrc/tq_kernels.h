@@ -1216,12 +1216,15 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 //           token t. The query is the A operand, broadcast from one block
 //           (CBSZ 4, ABID j mod 16): lane (block b, row m) keeps only the
 //           quads j = b, b + 16, ... of head m.
-//   values  O[g][c] += sum_t p[g][t] v_t[c] with v_mfma_f32_16x16x32_f16 per
-//           32 tokens (two 16-token blocks): A = weights (row = head, rows
-//           past GK zero), B = value lookups; lane (kq = lane / 16, column
-//           n = lane % 16) holds tokens 4kq .. 4kq + 3 of each block for
-//           coordinates VJ*n .. VJ*n + VJ - 1, one instruction per offset
-//           j < VJ. The sums land in lanes 0..15 (register g = head g).
+//   values  O[g][c] += sum_t p[g][t] v_t[c] with v_mfma_f32_16x16x32_f16:
+//           one byte of a token's value row codes 2 (4-bit) or 4 (2-bit)
+//           consecutive coordinates and is looked up as an fp16 pair or
+//           quad; the K dimension is (token slot, coordinate j within the
+//           byte): 16 tokens x 2 or 8 tokens x 4. Lane (kq, column n)
+//           supplies byte cb of its slice of each of its tokens (B), and row
+//           g + 4 j of A holds head g's weights in element j only, so row
+//           g + 4 j of C is head g at coordinate j of byte cb of column n's
+//           slice: one accumulator per byte of the slice.
 //   QJL     the sign dot sum_i q''_i sigma_i is a second chain of the same
 //           4x4x4 blocks: B = the key's 4 signs of quad j as fp16 +-1 (one
 //           8-byte lookup of a 16-entry table), A = the quad of R_2 q'.
@@ -1244,14 +1247,6 @@ struct MxTile {
   uint32_t kr;                  // QJL residual norm (f16 bits)
 };
 
-// For two tokens' 4-bit slices x, y of 8 coordinates: byte b of *lo is the
-// value pair-table index (x code, y code) of coordinate 2b, of *hi of 2b + 1.
-__device__ __forceinline__ void mx_pair_words(uint32_t x, uint32_t y, uint32_t* lo,
-                                              uint32_t* hi) {
-  *lo = (x & 0x0F0F0F0Fu) | ((y << 4) & 0xF0F0F0F0u);
-  *hi = ((x >> 4) & 0x0F0F0F0Fu) | (y & 0xF0F0F0F0u);
-}
-
 // tiles each wave loads ahead of the one it processes (1 or 2): two where
 // three tile buffers still fit the register budget without spilling
 constexpr int mx_prefetch(int d, int bk, bool qjl) { return d == 128 && bk < 4 ? 2 + 0 * qjl : 1; }
@@ -1270,7 +1265,6 @@ k_decode_mx(DecodeArgs a) {
   constexpr int KREC = D * BK / 8;
   constexpr int VREC = D * BV / 8;
   constexpr int KW = D * BK / 32;
-  constexpr int VJ = D / 16;                   // coordinates per lane column
   constexpr int SB = MxTile<D, BK, BV, QJL>::SB;
   constexpr int KE = 1 << (2 * BK);
   constexpr int VE = 1 << (2 * BV);
@@ -1562,9 +1556,41 @@ k_decode_mx(DecodeArgs a) {
     }
   }
   const uint32_t sl8 = uint32_t(lane) << 3;
-  // weight slot of this lane's token t = 16 blk + 4 j + kq in the value
-  // product's K order (slot 16 blk + 4 kq + j, matching the value slices)
-  const int pslot = (lane & 0x30) | ((lane & 3) << 2) | ((lane >> 2) & 3);
+  // Value product (see the kernel comment): the weight slot of this lane's
+  // token in the product's K order. 4-bit values: token 16 G + 4 u + kq of
+  // 16-token group G sits in slot 16 G + 4 kq + u; 2-bit values: token
+  // 8 G + 4 u + kq of 8-token group G in slot 8 G + 2 kq + u.
+  const int pslot = VQ4 ? (lane & 0x38) | ((lane & 3) << 1) | ((lane >> 2) & 1)
+                        : (lane & 0x30) | ((lane & 3) << 2) | ((lane >> 2) & 3);
+  // A-operand selectors: row col = g + 4 j of the product holds head g's
+  // weights in half j of each pair (4-bit) or element j of each quad (2-bit)
+  // of the K dimension; rows of heads >= GK (and rows >= 8 with 4-bit values)
+  // are zero. v_perm selectors on the dword X = (p_slot0, p_slot1): 0x0C
+  // gives a zero byte, 0x0100 / 0x0302 the low / high fp16 of X.
+  uint32_t asel[4];
+  {
+    const int ga = col & 3, ja = col >> 2;
+    const bool live = ga < GK && (VQ4 || ja < 2);
+    constexpr uint32_t kZ = 0x0C0C0C0Cu;
+    if constexpr (VQ4) {
+      // dwords: (slot 0, j' 0-1), (slot 0, j' 2-3), (slot 1, j' 0-1), (slot 1, j' 2-3)
+      const uint32_t lo = (ja & 1) ? 0x01000C0Cu : 0x0C0C0100u;
+      const uint32_t hi = (ja & 1) ? 0x03020C0Cu : 0x0C0C0302u;
+      asel[0] = live && ja < 2 ? lo : kZ;
+      asel[1] = live && ja >= 2 ? lo : kZ;
+      asel[2] = live && ja < 2 ? hi : kZ;
+      asel[3] = live && ja >= 2 ? hi : kZ;
+    } else {
+      // dwords: slots 0 .. 3 of the group, weight in half ja
+      const uint32_t lo = ja ? 0x01000C0Cu : 0x0C0C0100u;
+      const uint32_t hi = ja ? 0x03020C0Cu : 0x0C0C0302u;
+      asel[0] = live ? lo : kZ;
+      asel[1] = live ? hi : kZ;
+      asel[2] = asel[0];
+      asel[3] = asel[1];
+    }
+  }
+  const int arow_head = (col & 3) < GK ? (col & 3) : 0;
 
   float m_run[GK], lpart[GK];
   // key and QJL scales with the query's power of two undone (fp32)
@@ -1577,14 +1603,14 @@ k_decode_mx(DecodeArgs a) {
   // value norms neither overflow fp16 nor fall into its subnormals.
   float vsc = a.vscale;                        // a.vscale * 2^-vexp
   int vexp = 0;
-  mx_f4 acc[VJ];
+  mx_f4 acc[SB];                               // SB = value bytes per (token, column)
 #pragma unroll
   for (int g = 0; g < GK; ++g) {
     m_run[g] = -INFINITY;
     lpart[g] = 0.f;
   }
 #pragma unroll
-  for (int j = 0; j < VJ; ++j) acc[j] = mx_f4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < SB; ++j) acc[j] = mx_f4{0.f, 0.f, 0.f, 0.f};
 
   auto process = [&](int64_t base, uint32_t* px, const Tile& cur) {
     // ---------------- scores: lane = token, 4 coordinates per MFMA
@@ -1632,7 +1658,7 @@ k_decode_mx(DecodeArgs a) {
         vexp += sh;
         nv = ldexpf(nv, -sh);
 #pragma unroll
-        for (int j = 0; j < VJ; ++j)
+        for (int j = 0; j < SB; ++j)
 #pragma unroll
           for (int g = 0; g < GK; ++g) acc[j][g] = ldexpf(acc[j][g], -sh);
       }
@@ -1651,7 +1677,7 @@ k_decode_mx(DecodeArgs a) {
         m_run[g] = m_new;
         lpart[g] *= alpha;
 #pragma unroll
-        for (int j = 0; j < VJ; ++j) acc[j][g] *= alpha;
+        for (int j = 0; j < SB; ++j) acc[j][g] *= alpha;
       }
       // branch-free: rows past the split have zero norms and weight 0
       const float e = __builtin_amdgcn_exp2f(s - m_run[g]);
@@ -1664,72 +1690,55 @@ k_decode_mx(DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---------------- values: 32 tokens (two 16-token blocks) per MFMA,
-    // lane = (kq, column); the lane's k-values 8kq .. 8kq + 7 are tokens
-    // 4kq .. 4kq + 3 of the first block, then of the second
-    const bool arow = col < GK;
-    const uint16_t* prow = p16 + (arow ? col : 0) * TW + 4 * kq;
-    // B operand (4 tokens of one coordinate) of block blk, coordinate c
-    auto vquad = [&](int blk, uint32_t (&quad)[4]) {
-      // 2-bit values: byte b of P, R, Q, S is the 4-token code byte of
-      // coordinate 4b, 4b + 1, 4b + 2, 4b + 3 (code c of a token at bits 2c)
-      const uint32_t x0 = cur.vx[4 * blk][0], x1 = cur.vx[4 * blk + 1][0];
-      const uint32_t x2 = cur.vx[4 * blk + 2][0], x3 = cur.vx[4 * blk + 3][0];
-      constexpr uint32_t kEven = 0x33333333u, kOdd = 0xCCCCCCCCu, kLo = 0x0F0F0F0Fu;
-      // nibble k: (t0, t1) codes of coordinate 2k (A, C) or 2k + 1 (B, D)
-      const uint32_t A = (x0 & kEven) | ((x1 << 2) & kOdd);
-      const uint32_t B = (x1 & kOdd) | ((x0 >> 2) & kEven);
-      const uint32_t C = (x2 & kEven) | ((x3 << 2) & kOdd);
-      const uint32_t Dw = (x3 & kOdd) | ((x2 >> 2) & kEven);
-      quad[0] = (A & kLo) | ((C << 4) & ~kLo);
-      quad[1] = (B & kLo) | ((Dw << 4) & ~kLo);
-      quad[2] = ((A >> 4) & kLo) | (C & ~kLo);
-      quad[3] = ((B >> 4) & kLo) | (Dw & ~kLo);
-    };
+    // ---------------- values: one 16x16x32 MFMA per (token group, value
+    // byte of the lane's slice); the byte of a token holds the codes of two
+    // (4-bit) or four (2-bit) consecutive coordinates, looked up as an fp16
+    // pair or quad, and the coordinate within the byte is the product's row
+    // half / quad element: row g + 4 j of A carries head g's weights in
+    // element j only, so row g + 4 j of C is head g at coordinate j of the
+    // byte. Column n = the lane's slice of the rows.
+    if constexpr (!VQ4) {
+      // 16-token groups G: the lane's slots 4 kq + u are tokens 16 G + 4 u + kq
+      const uint16_t* pr = p16 + arow_head * TW + 4 * kq;
 #pragma unroll
-    for (int bp = 0; bp < 2; ++bp) {
-      mx_u2 pw0 = *reinterpret_cast<const mx_u2*>(prow + 32 * bp);
-      mx_u2 pw1 = *reinterpret_cast<const mx_u2*>(prow + 32 * bp + 16);
-      if (!arow) pw0 = pw1 = mx_u2{0u, 0u};
-      const mx_h8 pa = __builtin_bit_cast(mx_h8, mx_u4{pw0[0], pw0[1], pw1[0], pw1[1]});
-      if constexpr (VQ4) {
-        uint32_t q0[4], q1[4];
-        vquad(2 * bp, q0);
-        vquad(2 * bp + 1, q1);
+      for (int G = 0; G < 4; ++G) {
+        const mx_u2 X = *reinterpret_cast<const mx_u2*>(pr + 16 * G);
+        const mx_u4 aw = {__builtin_amdgcn_perm(X[0], X[0], asel[0]),
+                          __builtin_amdgcn_perm(X[0], X[0], asel[1]),
+                          __builtin_amdgcn_perm(X[1], X[1], asel[0]),
+                          __builtin_amdgcn_perm(X[1], X[1], asel[1])};
+        const mx_h8 pa = __builtin_bit_cast(mx_h8, aw);
 #pragma unroll
-        for (int c = 0; c < VJ; ++c) {
-          const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (c >> 2)) << 8;
-          const mx_u2 v0 = *reinterpret_cast<const mx_u2*>(
-              vtab + __builtin_amdgcn_perm(q0[c & 3], l8, sel));
-          const mx_u2 v1 = *reinterpret_cast<const mx_u2*>(
-              vtab + __builtin_amdgcn_perm(q1[c & 3], l8, sel));
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              pa, __builtin_bit_cast(mx_h8, mx_u4{v0[0], v0[1], v1[0], v1[1]}), acc[c], 0, 0, 0);
+        for (int cb = 0; cb < SB; ++cb) {
+          const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (cb & 3)) << 8;
+          mx_u4 vb;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            vb[u] = *reinterpret_cast<const uint32_t*>(
+                vtab + __builtin_amdgcn_perm(cur.vx[4 * G + u][cb >> 2], vl4, sel));
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(mx_h8, vb),
+                                                           acc[cb], 0, 0, 0);
         }
-      } else {
+      }
+    } else {
+      // 8-token groups G: the lane's slots 2 kq + u are tokens 8 G + 4 u + kq
+      const uint16_t* pr = p16 + arow_head * TW + 2 * kq;
 #pragma unroll
-        for (int grp = 0; grp < VJ / 8; ++grp) {
-          uint32_t lo[2][2], hi[2][2];     // [block][token pair]
+      for (int G = 0; G < 8; ++G) {
+        const uint32_t X = *reinterpret_cast<const uint32_t*>(pr + 8 * G);
+        const mx_u4 aw = {__builtin_amdgcn_perm(X, X, asel[0]), __builtin_amdgcn_perm(X, X, asel[1]),
+                          __builtin_amdgcn_perm(X, X, asel[2]), __builtin_amdgcn_perm(X, X, asel[3])};
+        const mx_h8 pa = __builtin_bit_cast(mx_h8, aw);
+        const int i0 = 4 * (G >> 1) + 2 * (G & 1);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int blk = 2 * bp + h;
-            mx_pair_words(cur.vx[4 * blk][grp], cur.vx[4 * blk + 1][grp], &lo[h][0], &hi[h][0]);
-            mx_pair_words(cur.vx[4 * blk + 2][grp], cur.vx[4 * blk + 3][grp], &lo[h][1],
-                          &hi[h][1]);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (e >> 1)) << 8;
-            mx_u4 vb;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int t = 0; t < 2; ++t)
-                vb[2 * h + t] = *reinterpret_cast<const uint32_t*>(
-                    vtab + __builtin_amdgcn_perm((e & 1) ? hi[h][t] : lo[h][t], vl4, sel));
-            acc[8 * grp + e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                pa, __builtin_bit_cast(mx_h8, vb), acc[8 * grp + e], 0, 0, 0);
-          }
+        for (int cb = 0; cb < SB; ++cb) {
+          const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (cb & 3)) << 8;
+          const mx_u2 q0 = *reinterpret_cast<const mx_u2*>(
+              vtab + __builtin_amdgcn_perm(cur.vx[i0][cb >> 2], l8, sel));
+          const mx_u2 q1 = *reinterpret_cast<const mx_u2*>(
+              vtab + __builtin_amdgcn_perm(cur.vx[i0 + 1][cb >> 2], l8, sel));
+          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              pa, __builtin_bit_cast(mx_h8, mx_u4{q0[0], q0[1], q1[0], q1[1]}), acc[cb], 0, 0, 0);
         }
       }
     }
@@ -1782,11 +1791,15 @@ k_decode_mx(DecodeArgs a) {
     }
     vexp_w[wave] = vexp;
   }
-  if (lane < 16) {
+  // C row g + 4 j of lane (col, kq = j) is head g at coordinate
+  // (bits / 2 ... ) j of value byte cb of column col's slice
+  constexpr int CPB = VQ4 ? 4 : 2;             // coordinates per value byte
+  if (kq < CPB) {
 #pragma unroll
     for (int g = 0; g < GK; ++g)
 #pragma unroll
-      for (int j = 0; j < VJ; ++j) slab[(wave * GK + g) * D + VJ * lane + j] = acc[j][g];
+      for (int cb = 0; cb < SB; ++cb)
+        slab[(wave * GK + g) * D + CPB * (SB * col + cb) + kq] = acc[cb][g];
   }
   __syncthreads();
   // This split's partial, (max, sum) per head and the weighted value sum in
