@@ -1286,7 +1286,7 @@ k_decode_mx(DecodeArgs a) {
   constexpr int TAB_BYTES = KT_BYTES + VT_BYTES + ST_BYTES;
   __shared__ __attribute__((aligned(16)))
   uint8_t tabs[TAB_BYTES > SLAB_BYTES ? TAB_BYTES : SLAB_BYTES];
-  __shared__ __attribute__((aligned(16))) uint32_t pex[W][2][PX];
+  __shared__ __attribute__((aligned(16))) uint32_t pex[W][3][PX];
   __shared__ uint32_t qs[GK * (D / 2)];
   __shared__ uint32_t qs2[QJL ? GK * (D / 2) : 1];
   __shared__ float mlx[W][GK][2];
@@ -1612,38 +1612,155 @@ k_decode_mx(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < SB; ++j) acc[j] = mx_f4{0.f, 0.f, 0.f, 0.f};
 
-  auto process = [&](int64_t base, uint32_t* px, const Tile& cur) {
-    // ---------------- scores: lane = token, 4 coordinates per MFMA
-    const bool valid = base + lane < t_end;
-    mx_f4 sk[2] = {mx_f4{0.f, 0.f, 0.f, 0.f}, mx_f4{0.f, 0.f, 0.f, 0.f}};
+  // A tile goes through three steps: scores (key lookups and the score
+  // products), softmax (running max, weights into LDS) and values (value
+  // lookups and the value product). The loop below takes the values of tile
+  // k together with the scores of tile k + 1, in one software pipeline: its
+  // stage i is value step i and score steps 2i, 2i + 1 (there are D / 8
+  // value steps and D / 4 score steps), and the lookups of stage i + 1 are
+  // issued before the products of stage i, so that table reads stay in
+  // flight while the products run.
+  struct Scores {
+    mx_f4 sk[2];
     mx_f4 sq[QJL ? 2 : 1];
-    if constexpr (QJL) sq[0] = sq[1] = mx_f4{0.f, 0.f, 0.f, 0.f};
-    dev::static_for<0, D / 4>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      mx_u2 kb;
-      if constexpr (KQ4) {
-        // byte j of the row = the codes of coordinates 4j .. 4j + 3
-        const uint32_t ka = __builtin_amdgcn_perm(cur.kw[j >> 2], l8,
-                                                  0x0C0C0000u | uint32_t(4 + (j & 3)) << 8);
-        kb = *reinterpret_cast<const mx_u2*>(tabs + ka);
-      } else {
-        const uint32_t ka0 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j) | rl4;
-        const uint32_t ka1 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j + 1) | rl4;
-        kb[0] = *reinterpret_cast<const uint32_t*>(tabs + ka0);
-        kb[1] = *reinterpret_cast<const uint32_t*>(tabs + ka1);
-      }
-      sk[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
-          __builtin_bit_cast(mx_h4, qa[j / 16]), __builtin_bit_cast(mx_h4, kb), sk[j & 1], 4,
+  };
+  struct KLook {
+    mx_u2 kb;                                  // fp16 centroids of 4 coordinates
+    mx_u2 sb;                                  // their QJL signs (+-1)
+  };
+  // score step j: coordinates 4j .. 4j + 3 of the lane's token
+  auto k_issue = [&](auto jc, const Tile& cur) {
+    constexpr int j = decltype(jc)::value;
+    KLook l;
+    if constexpr (KQ4) {
+      // byte j of the row = the codes of coordinates 4j .. 4j + 3
+      const uint32_t ka = __builtin_amdgcn_perm(cur.kw[j >> 2], l8,
+                                                0x0C0C0000u | uint32_t(4 + (j & 3)) << 8);
+      l.kb = *reinterpret_cast<const mx_u2*>(tabs + ka);
+    } else {
+      const uint32_t ka0 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j) | rl4;
+      const uint32_t ka1 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j + 1) | rl4;
+      l.kb[0] = *reinterpret_cast<const uint32_t*>(tabs + ka0);
+      l.kb[1] = *reinterpret_cast<const uint32_t*>(tabs + ka1);
+    }
+    if constexpr (QJL) {
+      const uint32_t sa = dev::field_at<4, 9>(cur.sw, j) | sl8;
+      const uint2 sp = *reinterpret_cast<const uint2*>(stab + sa);
+      l.sb = mx_u2{sp.x, sp.y};
+    }
+    return l;
+  };
+  // scores: lane = token, 4 coordinates per MFMA, query block j % 16 broadcast
+  auto k_take = [&](auto jc, const KLook& l, Scores& r) {
+    constexpr int j = decltype(jc)::value;
+    r.sk[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+        __builtin_bit_cast(mx_h4, qa[j / 16]), __builtin_bit_cast(mx_h4, l.kb), r.sk[j & 1], 4,
+        j % 16, 0);
+    if constexpr (QJL)
+      r.sq[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+          __builtin_bit_cast(mx_h4, qa2[j / 16]), __builtin_bit_cast(mx_h4, l.sb), r.sq[j & 1], 4,
           j % 16, 0);
-      if constexpr (QJL) {
-        const uint32_t sa = dev::field_at<4, 9>(cur.sw, j) | sl8;
-        const uint2 sp = *reinterpret_cast<const uint2*>(stab + sa);
-        const mx_u2 sb = {sp.x, sp.y};
-        sq[j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
-            __builtin_bit_cast(mx_h4, qa2[j / 16]), __builtin_bit_cast(mx_h4, sb), sq[j & 1], 4,
-            j % 16, 0);
+  };
+  // Values: one 16x16x32 MFMA per (token group G, value byte cb of the
+  // lane's slice); a token's byte holds the codes of two (4-bit) or four
+  // (2-bit) consecutive coordinates, looked up as an fp16 pair or quad, and
+  // the coordinate within the byte is the product's row half / quad element:
+  // row g + 4 j of A carries head g's weights in element j only, so row
+  // g + 4 j of C is head g at coordinate j of the byte. Column n = the lane's
+  // slice of the rows. 4-bit values: 16-token groups, the lane's slots
+  // 4 kq + u are tokens 16 G + 4 u + kq; 2-bit values: 8-token groups, slots
+  // 2 kq + u are tokens 8 G + 4 u + kq. Value step i is (G, cb) = (i / SB,
+  // i % SB).
+  constexpr int NV = D / 8;
+  constexpr int NG = VQ4 ? 8 : 4;
+  static_assert(NV == NG * SB, "value steps");
+  auto v_issue = [&](auto ic, const Tile& cur) {
+    constexpr int i = decltype(ic)::value, G = i / SB, cb = i % SB;
+    constexpr uint32_t sel = 0x0C0C0000u | uint32_t(4 + (cb & 3)) << 8;
+    mx_u4 vb;
+    if constexpr (!VQ4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        vb[u] = *reinterpret_cast<const uint32_t*>(
+            vtab + __builtin_amdgcn_perm(cur.vx[4 * G + u][cb >> 2], vl4, sel));
+    } else {
+      constexpr int i0 = 4 * (G >> 1) + 2 * (G & 1);
+      const mx_u2 q0 = *reinterpret_cast<const mx_u2*>(
+          vtab + __builtin_amdgcn_perm(cur.vx[i0][cb >> 2], l8, sel));
+      const mx_u2 q1 = *reinterpret_cast<const mx_u2*>(
+          vtab + __builtin_amdgcn_perm(cur.vx[i0 + 1][cb >> 2], l8, sel));
+      vb = mx_u4{q0[0], q0[1], q1[0], q1[1]};
+    }
+    return vb;
+  };
+  // the weights of group G as the A operand (v_perm into the head's rows)
+  using WX = std::conditional_t<VQ4, uint32_t, mx_u2>;
+  auto w_operand = [&](const WX& X) {
+    mx_u4 aw;
+    if constexpr (!VQ4)
+      aw = mx_u4{__builtin_amdgcn_perm(X[0], X[0], asel[0]),
+                 __builtin_amdgcn_perm(X[0], X[0], asel[1]),
+                 __builtin_amdgcn_perm(X[1], X[1], asel[0]),
+                 __builtin_amdgcn_perm(X[1], X[1], asel[1])};
+    else
+      aw = mx_u4{__builtin_amdgcn_perm(X, X, asel[0]), __builtin_amdgcn_perm(X, X, asel[1]),
+                 __builtin_amdgcn_perm(X, X, asel[2]), __builtin_amdgcn_perm(X, X, asel[3])};
+    return __builtin_bit_cast(mx_h8, aw);
+  };
+  // The pipeline: the values of the tile in vt with its weights in px (when
+  // WV) and the scores of the tile in kt.
+  auto pipeline = [&](auto wv_c, const uint32_t* px, const Tile& vt, const Tile& kt) {
+    constexpr bool WV = decltype(wv_c)::value;
+    Scores r;
+    r.sk[0] = r.sk[1] = mx_f4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (QJL) r.sq[0] = r.sq[1] = mx_f4{0.f, 0.f, 0.f, 0.f};
+    WX X[WV ? NG : 1];
+    if constexpr (WV) {
+      const uint16_t* pr = reinterpret_cast<const uint16_t*>(px) + arow_head * TW +
+                           (VQ4 ? 2 : 4) * kq;
+#pragma unroll
+      for (int G = 0; G < NG; ++G)
+        X[G] = *reinterpret_cast<const WX*>(pr + (VQ4 ? 8 : 16) * G);
+    }
+    KLook kl[2][2];
+    mx_u4 vl[2];
+    mx_h8 pa;
+    kl[0][0] = k_issue(std::integral_constant<int, 0>{}, kt);
+    kl[0][1] = k_issue(std::integral_constant<int, 1>{}, kt);
+    if constexpr (WV) vl[0] = v_issue(std::integral_constant<int, 0>{}, vt);
+    dev::static_for<0, NV>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i + 1 < NV) {
+        kl[(i + 1) & 1][0] = k_issue(std::integral_constant<int, 2 * i + 2>{}, kt);
+        kl[(i + 1) & 1][1] = k_issue(std::integral_constant<int, 2 * i + 3>{}, kt);
+        if constexpr (WV) vl[(i + 1) & 1] = v_issue(std::integral_constant<int, i + 1>{}, vt);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (WV) {
+        if constexpr (i % SB == 0) pa = w_operand(X[i / SB]);
+        acc[i % SB] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            pa, __builtin_bit_cast(mx_h8, vl[i & 1]), acc[i % SB], 0, 0, 0);
+      }
+      k_take(std::integral_constant<int, 2 * i>{}, kl[i & 1][0], r);
+      k_take(std::integral_constant<int, 2 * i + 1>{}, kl[i & 1][1], r);
+      __builtin_amdgcn_sched_barrier(0);
     });
+    // computed here, not on the path past the loop exit that follows
+#pragma unroll
+    for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(r.sk[i]));
+    if constexpr (QJL) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) asm volatile("" : "+v"(r.sq[i]));
+    }
+    return r;
+  };
+  const std::true_type with_values{};
+  const std::false_type scores_only{};
+
+  auto softmax = [&](int64_t base, uint32_t* px, const Tile& cur, const Scores& sc) {
+    const bool valid = base + lane < t_end;
+    const mx_f4 (&sk)[2] = sc.sk;
+    const mx_f4 (&sq)[QJL ? 2 : 1] = sc.sq;
     const float knrm = NF16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);
     const float vnrm = NF16 ? dev::f16_to_f32(cur.vn) : __uint_as_float(cur.vn);
     const float ks = knrm * kscale;
@@ -1689,88 +1806,44 @@ k_decode_mx(DecodeArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---------------- values: one 16x16x32 MFMA per (token group, value
-    // byte of the lane's slice); the byte of a token holds the codes of two
-    // (4-bit) or four (2-bit) consecutive coordinates, looked up as an fp16
-    // pair or quad, and the coordinate within the byte is the product's row
-    // half / quad element: row g + 4 j of A carries head g's weights in
-    // element j only, so row g + 4 j of C is head g at coordinate j of the
-    // byte. Column n = the lane's slice of the rows.
-    if constexpr (!VQ4) {
-      // 16-token groups G: the lane's slots 4 kq + u are tokens 16 G + 4 u + kq
-      const uint16_t* pr = p16 + arow_head * TW + 4 * kq;
-#pragma unroll
-      for (int G = 0; G < 4; ++G) {
-        const mx_u2 X = *reinterpret_cast<const mx_u2*>(pr + 16 * G);
-        const mx_u4 aw = {__builtin_amdgcn_perm(X[0], X[0], asel[0]),
-                          __builtin_amdgcn_perm(X[0], X[0], asel[1]),
-                          __builtin_amdgcn_perm(X[1], X[1], asel[0]),
-                          __builtin_amdgcn_perm(X[1], X[1], asel[1])};
-        const mx_h8 pa = __builtin_bit_cast(mx_h8, aw);
-#pragma unroll
-        for (int cb = 0; cb < SB; ++cb) {
-          const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (cb & 3)) << 8;
-          mx_u4 vb;
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            vb[u] = *reinterpret_cast<const uint32_t*>(
-                vtab + __builtin_amdgcn_perm(cur.vx[4 * G + u][cb >> 2], vl4, sel));
-          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(mx_h8, vb),
-                                                           acc[cb], 0, 0, 0);
-        }
-      }
-    } else {
-      // 8-token groups G: the lane's slots 2 kq + u are tokens 8 G + 4 u + kq
-      const uint16_t* pr = p16 + arow_head * TW + 2 * kq;
-#pragma unroll
-      for (int G = 0; G < 8; ++G) {
-        const uint32_t X = *reinterpret_cast<const uint32_t*>(pr + 8 * G);
-        const mx_u4 aw = {__builtin_amdgcn_perm(X, X, asel[0]), __builtin_amdgcn_perm(X, X, asel[1]),
-                          __builtin_amdgcn_perm(X, X, asel[2]), __builtin_amdgcn_perm(X, X, asel[3])};
-        const mx_h8 pa = __builtin_bit_cast(mx_h8, aw);
-        const int i0 = 4 * (G >> 1) + 2 * (G & 1);
-#pragma unroll
-        for (int cb = 0; cb < SB; ++cb) {
-          const uint32_t sel = 0x0C0C0000u | uint32_t(4 + (cb & 3)) << 8;
-          const mx_u2 q0 = *reinterpret_cast<const mx_u2*>(
-              vtab + __builtin_amdgcn_perm(cur.vx[i0][cb >> 2], l8, sel));
-          const mx_u2 q1 = *reinterpret_cast<const mx_u2*>(
-              vtab + __builtin_amdgcn_perm(cur.vx[i0 + 1][cb >> 2], l8, sel));
-          acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-              pa, __builtin_bit_cast(mx_h8, mx_u4{q0[0], q0[1], q1[0], q1[1]}), acc[cb], 0, 0, 0);
-        }
-      }
-    }
   };
 
   {
     uint32_t* px0 = pex[wave][0];
     uint32_t* px1 = pex[wave][1];
+    uint32_t* px2 = pex[wave][2];
     if (!early) load_first();
     __builtin_amdgcn_sched_barrier(0);
+    // tile k is in buffer k mod (PF + 1) with its weights in slot k mod
+    // (PF + 1); a buffer is refilled once its values have been taken
+    softmax(wb, px0, ta, pipeline(scores_only, nullptr, ta, ta));
     if constexpr (PF == 1) {
       for (int it = 0; it < iters; it += 2) {
         const int64_t base = wb + int64_t(it) * T;
-        process(base, px0, ta);
+        Scores sc = pipeline(with_values, px0, ta, tb);
         if (it + 1 >= iters) break;
         load(base + 2 * T, ta);
-        process(base + T, px1, tb);
+        softmax(base + T, px1, tb, sc);
+        sc = pipeline(with_values, px1, tb, ta);
         if (it + 2 >= iters) break;
         load(base + 3 * T, tb);
+        softmax(base + 2 * T, px0, ta, sc);
       }
     } else {
       for (int it = 0; it < iters; it += 3) {
         const int64_t base = wb + int64_t(it) * T;
-        process(base, px0, ta);
+        Scores sc = pipeline(with_values, px0, ta, tb);
         if (it + 1 >= iters) break;
         load(base + 3 * T, ta);
-        process(base + T, px1, tb);
+        softmax(base + T, px1, tb, sc);
+        sc = pipeline(with_values, px1, tb, tc);
         if (it + 2 >= iters) break;
         load(base + 4 * T, tb);
-        process(base + 2 * T, px0, tc);
+        softmax(base + 2 * T, px2, tc, sc);
+        sc = pipeline(with_values, px2, tc, ta);
         if (it + 3 >= iters) break;
         load(base + 5 * T, tc);
+        softmax(base + 3 * T, px0, ta, sc);
       }
     }
   }
