@@ -26,6 +26,7 @@ Prints ONE JSON line on stdout (progress goes to stderr):
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -255,6 +256,90 @@ def decode_record(torch, tq, si, w, n_calls, flush, fsink):
     return rec
 
 
+def _exact_attention(q, k, v, G, scale):
+    """softmax(scale q K^T) V in float64 from the rounded inputs [B][H][n][d]."""
+    import numpy as np
+    heads = np.arange(q.shape[1]) // G
+    s = scale * np.einsum("bhd,bhtd->bht", q, k[:, heads])
+    s -= s.max(-1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(-1, keepdims=True)
+    return np.einsum("bht,bhtd->bhd", p, v[:, heads])
+
+
+def accuracy_report(torch, tq, si):
+    """The method's accuracy on the GPU's own outputs (small seeded cases).
+
+    p13: relative L2 error of the decode output against unquantized fp64
+    attention softmax(q K^T / sqrt(d)) V, per format, iid and correlated
+    queries (README, "Measured results"). qjl_score_bias: mean error of the
+    score difference s_j - s_other over two-token contexts with queries
+    correlated to token j, MSE-only against QJL-corrected (README, "The 1-bit
+    QJL residual"); the kernel's score difference is read back from its
+    output o = p0 v0 + (1 - p0) v1, with v0 and v1 the dequantized values
+    (one-token decodes of the same codes).
+    """
+    import numpy as np
+    def run(w, q_raw, n_ctx, scale=0.0, swap=False):
+        cfg = tq.Config(d=w.d, bits_k=w.bits_k, bits_v=w.bits_v, norm_dtype=w.norm_dtype,
+                        qjl=w.qjl, seed=w.seed, qjl_seed=w.qjl_seed)
+        kr, vr = si.kv_full(w, si.T_K), si.kv_full(w, si.T_V)
+        if swap:
+            kr, vr = kr[:, :, ::-1].copy(), vr[:, :, ::-1].copy()
+        cache = tq.PackedCache(cfg, w.B, w.Hkv, w.N)
+        tq.tq_encode_kv(cfg, to_dev(torch, kr, w.in_dtype), to_dev(torch, vr, w.in_dtype), 0,
+                        cache)
+        out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+        ws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, n_ctx))
+        tq.tq_attend_decode(cfg, to_dev(torch, q_raw, w.in_dtype), cache, n_ctx, out, ws,
+                            scale=scale)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64)
+
+    f64 = lambda raw, w: (si.bf16_bits_to_f32(raw) if w.in_dtype == "bf16"
+                          else raw.astype(np.float32)).astype(np.float64)
+    p13 = {}
+    for structure in ("iid", "correlated"):
+        rows = {}
+        for bk, bv in ((2, 2), (3, 3), (4, 4), (3, 4)):
+            for qjl in (False, True):
+                w = si.small_workload(B=1, Hq=32, Hkv=8, d=128, N=4096, bits_k=bk, bits_v=bv,
+                                      norm_dtype="f16", qjl=qjl, in_dtype="bf16",
+                                      structure=structure, wid=301)
+                q_raw, qf = si.queries(w)
+                got = run(w, q_raw, w.N)
+                ref = _exact_attention(qf.astype(np.float64), f64(si.kv_full(w, si.T_K), w),
+                                       f64(si.kv_full(w, si.T_V), w), w.G, 1 / math.sqrt(w.d))
+                e = np.linalg.norm(got - ref, axis=-1) / np.linalg.norm(ref, axis=-1)
+                rows[f"K{bk}{'+QJL' if qjl else ''}/V{bv}"] = {
+                    "mean": round(float(e.mean()), 5), "max": round(float(e.max()), 5)}
+        p13[f"{structure}_queries"] = rows
+    bias = {}
+    scale = 1.0 / 128
+    for qjl in (False, True):
+        w = si.small_workload(B=64, Hq=32, Hkv=8, d=128, N=2, bits_k=3, bits_v=4,
+                              norm_dtype="f16", qjl=qjl, in_dtype="bf16",
+                              structure="correlated", wid=300)
+        q_raw, qf = si.queries(w)
+        o2 = run(w, q_raw, 2, scale)
+        v0 = run(w, q_raw, 1, scale)
+        v1 = run(w, q_raw, 1, scale, swap=True)
+        dv = v0 - v1
+        p0 = np.clip(((o2 - v1) * dv).sum(-1) / (dv * dv).sum(-1), 1e-9, 1 - 1e-9)
+        heads = np.arange(w.Hq) // w.G
+        s = scale * np.einsum("bhd,bhtd->bht", qf.astype(np.float64),
+                              f64(si.kv_full(w, si.T_K), w)[:, heads])
+        sign = np.where(si.correlated_tokens(w) == 0, 1.0, -1.0)
+        err = (np.log(p0 / (1 - p0)) - (s[..., 0] - s[..., 1])) * sign
+        bias["qjl" if qjl else "mse_only"] = round(float(err.mean()), 5)
+        bias[("qjl" if qjl else "mse_only") + "_sem"] = round(
+            float(err.std() / math.sqrt(err.size)), 5)
+        bias["mean_true_difference"] = round(float(((s[..., 0] - s[..., 1]) * sign).mean()), 5)
+        bias["pairs"] = int(err.size)
+    bias["format"] = "K3/V4 (+QJL), d 128, scale 1/128, q = 0.8 k_j + 0.6 eps"
+    return {"p13_rel_l2_error_vs_fp64_attention": p13, "qjl_score_bias": bias}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +350,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-affine", action="store_true")
+    ap.add_argument("--no-accuracy", action="store_true",
+                    help="skip the accuracy report (P13 errors, QJL score bias)")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the decode records of the other 128k+ workloads")
     ap.add_argument("--cpu-units", type=int, default=8,
@@ -493,6 +580,11 @@ def main():
                 f"{rec['decode_call_cold_median_us']} us")
     del flush
 
+    accuracy = None
+    if not args.no_accuracy:
+        accuracy = accuracy_report(torch, tq, si)
+        log(f"accuracy: QJL score bias {accuracy['qjl_score_bias']}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the host cores")
@@ -571,6 +663,7 @@ def main():
         "prefill": prefill,
         "affine": affine,
         "other_workloads": others,
+        "accuracy": accuracy,
         "source_hash": source_hash(),
     }
     print(json.dumps(rec), flush=True)

@@ -1785,9 +1785,15 @@ k_decode_mx(DecodeArgs a) {
     uint16_t* p16 = reinterpret_cast<uint16_t*>(px);
 #pragma unroll
     for (int g = 0; g < GK; ++g) {
-      float s = (sk[0][g] + sk[1][g]) * ks;
-      if constexpr (QJL) s = fmaf(rho, sq[0][g] + sq[1][g], s);
-      if (__ballot(valid && s > m_run[g] + kRescale)) {        // wave-uniform
+      // t = score - running max, in one step; the branch rebuilds the score
+      // itself (the running max starts at -inf)
+      const float dk = sk[0][g] + sk[1][g];
+      const float dq = QJL ? sq[0][g] + sq[1][g] : 0.f;
+      float t = fmaf(dk, ks, -m_run[g]);
+      if constexpr (QJL) t = fmaf(rho, dq, t);
+      if (__ballot(valid && t > kRescale)) {              // wave-uniform, rare
+        float s = dk * ks;
+        if constexpr (QJL) s = fmaf(rho, dq, s);
         const float mx = dev::dpp_wave_max(valid ? s : -INFINITY);
         const float m_new = fmaxf(m_run[g], mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
@@ -1795,9 +1801,10 @@ k_decode_mx(DecodeArgs a) {
         lpart[g] *= alpha;
 #pragma unroll
         for (int j = 0; j < SB; ++j) acc[j][g] *= alpha;
+        t = s - m_new;
       }
       // branch-free: rows past the split have zero norms and weight 0
-      const float e = __builtin_amdgcn_exp2f(s - m_run[g]);
+      const float e = __builtin_amdgcn_exp2f(t);
       const float p = valid ? e : 0.f;
       lpart[g] += p;
       p16[g * TW + pslot] = __builtin_bit_cast(uint16_t, _Float16(p * nv));
