@@ -236,13 +236,10 @@ __device__ __forceinline__ uint32_t field(const uint32_t (&w)[NW], int i) {
   return BITS == 32 ? x : (x & ((1u << BITS) - 1u));
 }
 
-// Field i (width BITS) of the bitstream w[], already shifted left by P
-// (result = field << P). Two VALU ops: one shift (or a funnel shift when the
-// field straddles two dwords) and the mask. Needs P <= 32 - BITS... the
-// straddling case needs the field to start at bit >= P of its dword.
+// The BITS-bit field that starts at bit `bit` of the words w (LSB-first),
+// shifted left by P.
 template <int BITS, int P, int NW>
-__device__ __forceinline__ uint32_t field_at(const uint32_t (&w)[NW], int i) {
-  const int bit = i * BITS;
+__device__ __forceinline__ uint32_t bits_at(const uint32_t (&w)[NW], int bit) {
   const int wi = bit >> 5, sh = bit & 31;
   uint32_t x;
   if (sh + BITS > 32) {
@@ -253,6 +250,15 @@ __device__ __forceinline__ uint32_t field_at(const uint32_t (&w)[NW], int i) {
     x = w[wi] << (P - sh);
   }
   return x & (((1u << BITS) - 1u) << P);
+}
+
+// Field i (width BITS) of the bitstream w[], already shifted left by P
+// (result = field << P). Two VALU ops: one shift (or a funnel shift when the
+// field straddles two dwords) and the mask. Needs P <= 32 - BITS... the
+// straddling case needs the field to start at bit >= P of its dword.
+template <int BITS, int P, int NW>
+__device__ __forceinline__ uint32_t field_at(const uint32_t (&w)[NW], int i) {
+  return bits_at<BITS, P>(w, i * BITS);
 }
 
 // Device-scope (agent) stores and loads of fp32 values: the stores write

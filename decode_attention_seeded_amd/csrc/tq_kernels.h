@@ -1269,12 +1269,15 @@ k_decode_mx(DecodeArgs a) {
   constexpr int KE = 1 << (2 * BK);
   constexpr int VE = 1 << (2 * BV);
   // 2-bit codes: one lookup per four codes (a byte indexes a table of fp16
-  // quads: 256 entries, 32 copies of 8 B); wider codes: pair tables
+  // quads: 256 entries, 32 copies of 8 B); wider codes: one lookup per two
+  // codes (a table of fp16 pairs, 64 copies of 4 B: entry stride 256 B, so
+  // that the 64 lanes of a lookup hit 64 different banks)
   constexpr bool KQ4 = BK == 2;
   constexpr bool VQ4 = BV == 2;
-  constexpr int KT_BYTES = KQ4 ? 256 * 256 : KE * 128;   // pairs: 32 copies, 128-B stride
-  constexpr int VT_BYTES = VQ4 ? 256 * 256 : VE * 256;   // pairs: 64 copies, 256-B stride
-  constexpr int NQ = D / 64;                   // query quads kept per lane
+  constexpr int KT_BYTES = KQ4 ? 256 * 256 : KE * 256;
+  constexpr int VT_BYTES = VQ4 ? 256 * 256 : VE * 256;
+  constexpr int NS = D / 4;                    // score steps per token
+  constexpr int NQ = NS / 16;                  // query quads kept per lane
   constexpr int PX = GK * TW / 2;              // weight dwords per wave tile
   constexpr float kRescale = 8.0f;
   constexpr int ST_BYTES = QJL ? 16 * 512 : 0; // QJL sign quads: 64 copies of 8 B
@@ -1299,9 +1302,19 @@ k_decode_mx(DecodeArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;                   // V phase: lane column / A row
   const int kq = lane >> 4;                    // V phase: token quad
-  const uint32_t rl4 = uint32_t(lane & 31) << 2;
-  const uint32_t vl4 = uint32_t(lane) << 2;
+  const uint32_t kl4 = uint32_t(lane) << 2;    // pair tables: the lane's copy
+  // LDS table bases: keys at 0, values at VT_OFF, QJL signs at ST_OFF. The
+  // part of a base at or above 64 KB rides in the lane's offset register
+  // (byte 2 of a v_perm-built address, or bits a field never reaches), the
+  // rest in the instruction's 16-bit offset, so that no address needs an
+  // add of its own.
+  constexpr uint32_t VT_OFF = KT_BYTES, ST_OFF = KT_BYTES + VT_BYTES;
+  constexpr uint32_t VT_HI = VT_OFF & 0xFF0000u, VT_LO = VT_OFF & 0xFFFFu;
+  constexpr uint32_t VSEL2 = (VT_HI ? 0x02u : 0x0Cu) << 16;   // byte 2 of a value address
+  static_assert(VT_OFF < 0x1000000u && ST_OFF % 0x2000u == 0, "table bases");
+  const uint32_t vl4 = (uint32_t(lane) << 2) | VT_HI;
   const uint32_t l8 = uint32_t(lane & 31) << 3;   // quad tables: the lane's copy
+  const uint32_t vl8 = l8 | VT_HI;
   const int split = blockIdx.x;
   const int unit = blockIdx.y;
   const int chunk = unit % a.chunks;
@@ -1499,14 +1512,13 @@ k_decode_mx(DecodeArgs a) {
   };
   if constexpr (KQ4) quad_table(tabs, ck, a.cbk);
   else pair_table(tabs, ck, a.cbk, std::integral_constant<int, BK>{},
-                  std::integral_constant<int, 32>{});
+                  std::integral_constant<int, 64>{});
   if constexpr (VQ4) quad_table(tabs + KT_BYTES, cv, a.cbv);
   else pair_table(tabs + KT_BYTES, cv, a.cbv, std::integral_constant<int, BV>{},
                   std::integral_constant<int, 64>{});
   static_assert(KE % W == 0 && VE % W == 0 && 256 % W == 0,
                 "table entries split evenly over the waves");
-  const uint8_t* vtab = tabs + KT_BYTES;
-  const uint8_t* stab = tabs + KT_BYTES + VT_BYTES;
+  const uint8_t* vtab = tabs + VT_LO;          // value addresses carry VT_HI
   if constexpr (QJL) {
     // entry e: the fp16 pairs (s0, s1), (s2, s3) with s_k = -1 where bit k
     // of e is set, else +1; lane l reads copy l (entry stride 512 B)
@@ -1542,12 +1554,8 @@ k_decode_mx(DecodeArgs a) {
     for (int i = 0; i < NQ; ++i) {
       const int j = qb + 16 * i;
       if (qm < GK) {
-        qa[i][0] = qs[qm * (D / 2) + 2 * j];
-        qa[i][1] = qs[qm * (D / 2) + 2 * j + 1];
-        if constexpr (QJL) {
-          qa2[i][0] = qs2[qm * (D / 2) + 2 * j];
-          qa2[i][1] = qs2[qm * (D / 2) + 2 * j + 1];
-        }
+        qa[i] = mx_u2{qs[qm * (D / 2) + 2 * j], qs[qm * (D / 2) + 2 * j + 1]};
+        if constexpr (QJL) qa2[i] = mx_u2{qs2[qm * (D / 2) + 2 * j], qs2[qm * (D / 2) + 2 * j + 1]};
       } else {
         qa[i][0] = 0u;
         qa[i][1] = 0u;
@@ -1555,7 +1563,7 @@ k_decode_mx(DecodeArgs a) {
       }
     }
   }
-  const uint32_t sl8 = uint32_t(lane) << 3;
+  const uint32_t sl8 = (uint32_t(lane) << 3) | ST_OFF;   // QJL signs: copy and table base
   // Value product (see the kernel comment): the weight slot of this lane's
   // token in the product's K order. 4-bit values: token 16 G + 4 u + kq of
   // 16-token group G sits in slot 16 G + 4 kq + u; 2-bit values: token
@@ -1625,7 +1633,7 @@ k_decode_mx(DecodeArgs a) {
     mx_f4 sq[QJL ? 2 : 1];
   };
   struct KLook {
-    mx_u2 kb;                                  // fp16 centroids of 4 coordinates
+    mx_u2 kb;                                  // fp16 centroids of the step's coordinates
     mx_u2 sb;                                  // their QJL signs (+-1)
   };
   // score step j: coordinates 4j .. 4j + 3 of the lane's token
@@ -1638,14 +1646,14 @@ k_decode_mx(DecodeArgs a) {
                                                 0x0C0C0000u | uint32_t(4 + (j & 3)) << 8);
       l.kb = *reinterpret_cast<const mx_u2*>(tabs + ka);
     } else {
-      const uint32_t ka0 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j) | rl4;
-      const uint32_t ka1 = dev::field_at<2 * BK, 7>(cur.kw, 2 * j + 1) | rl4;
+      const uint32_t ka0 = dev::field_at<2 * BK, 8>(cur.kw, 2 * j) | kl4;
+      const uint32_t ka1 = dev::field_at<2 * BK, 8>(cur.kw, 2 * j + 1) | kl4;
       l.kb[0] = *reinterpret_cast<const uint32_t*>(tabs + ka0);
       l.kb[1] = *reinterpret_cast<const uint32_t*>(tabs + ka1);
     }
     if constexpr (QJL) {
       const uint32_t sa = dev::field_at<4, 9>(cur.sw, j) | sl8;
-      const uint2 sp = *reinterpret_cast<const uint2*>(stab + sa);
+      const uint2 sp = *reinterpret_cast<const uint2*>(tabs + sa);
       l.sb = mx_u2{sp.x, sp.y};
     }
     return l;
@@ -1676,7 +1684,7 @@ k_decode_mx(DecodeArgs a) {
   static_assert(NV == NG * SB, "value steps");
   auto v_issue = [&](auto ic, const Tile& cur) {
     constexpr int i = decltype(ic)::value, G = i / SB, cb = i % SB;
-    constexpr uint32_t sel = 0x0C0C0000u | uint32_t(4 + (cb & 3)) << 8;
+    constexpr uint32_t sel = 0x0C000000u | VSEL2 | uint32_t(4 + (cb & 3)) << 8;
     mx_u4 vb;
     if constexpr (!VQ4) {
 #pragma unroll
@@ -1686,9 +1694,9 @@ k_decode_mx(DecodeArgs a) {
     } else {
       constexpr int i0 = 4 * (G >> 1) + 2 * (G & 1);
       const mx_u2 q0 = *reinterpret_cast<const mx_u2*>(
-          vtab + __builtin_amdgcn_perm(cur.vx[i0][cb >> 2], l8, sel));
+          vtab + __builtin_amdgcn_perm(cur.vx[i0][cb >> 2], vl8, sel));
       const mx_u2 q1 = *reinterpret_cast<const mx_u2*>(
-          vtab + __builtin_amdgcn_perm(cur.vx[i0 + 1][cb >> 2], l8, sel));
+          vtab + __builtin_amdgcn_perm(cur.vx[i0 + 1][cb >> 2], vl8, sel));
       vb = mx_u4{q0[0], q0[1], q1[0], q1[1]};
     }
     return vb;
@@ -1722,17 +1730,28 @@ k_decode_mx(DecodeArgs a) {
       for (int G = 0; G < NG; ++G)
         X[G] = *reinterpret_cast<const WX*>(pr + (VQ4 ? 8 : 16) * G);
     }
+    // stage i takes score steps 2i, 2i + 1
+    static_assert(NS == 2 * NV, "two score steps per value step");
     KLook kl[2][2];
     mx_u4 vl[2];
     mx_h8 pa;
-    kl[0][0] = k_issue(std::integral_constant<int, 0>{}, kt);
-    kl[0][1] = k_issue(std::integral_constant<int, 1>{}, kt);
+    auto k_stage = [&](auto sc, auto issue_c) {
+      constexpr int st = decltype(sc)::value;
+      constexpr int a0 = 2 * st, a1 = 2 * st + 2;
+      dev::static_for<a0, a1>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (decltype(issue_c)::value)
+          kl[st & 1][m - a0] = k_issue(std::integral_constant<int, m>{}, kt);
+        else
+          k_take(std::integral_constant<int, m>{}, kl[st & 1][m - a0], r);
+      });
+    };
+    k_stage(std::integral_constant<int, 0>{}, std::true_type{});
     if constexpr (WV) vl[0] = v_issue(std::integral_constant<int, 0>{}, vt);
     dev::static_for<0, NV>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       if constexpr (i + 1 < NV) {
-        kl[(i + 1) & 1][0] = k_issue(std::integral_constant<int, 2 * i + 2>{}, kt);
-        kl[(i + 1) & 1][1] = k_issue(std::integral_constant<int, 2 * i + 3>{}, kt);
+        k_stage(std::integral_constant<int, i + 1>{}, std::true_type{});
         if constexpr (WV) vl[(i + 1) & 1] = v_issue(std::integral_constant<int, i + 1>{}, vt);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1741,8 +1760,7 @@ k_decode_mx(DecodeArgs a) {
         acc[i % SB] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
             pa, __builtin_bit_cast(mx_h8, vl[i & 1]), acc[i % SB], 0, 0, 0);
       }
-      k_take(std::integral_constant<int, 2 * i>{}, kl[i & 1][0], r);
-      k_take(std::integral_constant<int, 2 * i + 1>{}, kl[i & 1][1], r);
+      k_stage(ic, std::false_type{});
       __builtin_amdgcn_sched_barrier(0);
     });
     // computed here, not on the path past the loop exit that follows
