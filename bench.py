@@ -564,6 +564,30 @@ def main():
                  "ideal_byte_ratio": round(dbytes / alg_bytes, 3)}
         log(f"dense bf16 decode {dus:.1f} us ({dgbps:.1f} GB/s, {dgbps / probe_gbps:.2f} of the "
             f"read probe); at the probe rate it would take {probe_bound_us:.1f} us")
+    # other fractional splits on the same K/V and query: K3/V3 and the
+    # 2.5-bit K2/V3 (3-bit values run on the VALU decode kernel)
+    formats = None
+    if not args.no_others and args.workload == 4:
+        formats = {}
+        for bk, bv in ((3, 3), (2, 3)):
+            fcfg = tq.Config(d=w.d, bits_k=bk, bits_v=bv, norm_dtype=w.norm_dtype, qjl=False,
+                             seed=w.seed)
+            fcache = tq.PackedCache(fcfg, w.B, w.Hkv, w.N)
+            tq.tq_encode_kv(fcfg, K, V, 0, fcache)
+            fws = tq.workspace(tq.tq_workspace_bytes(fcfg, w.B, w.Hq, w.Hkv, w.N))
+            fout = torch.empty_like(out)
+            fus = timed(torch, lambda: tq.tq_attend_decode(fcfg, q, fcache, w.N, fout, fws), 50)
+            fb = tq.tq_cache_bytes(fcfg, w.B, w.Hkv, w.N)[0] + qbytes + fout.numel() * 4
+            formats[f"K{bk}/V{bv}"] = {
+                "decode_call_us": round(fus, 2), "algorithmic_bytes": fb,
+                "achieved_gbps": round(fb / fus / 1e3, 1),
+                "frac_of_hbm_peak": round(fb / fus / 1e3 / HBM_PEAK_GBPS, 4),
+                "kernel": "k_decode_pk (VALU; 3-bit values)",
+                "kv_bytes_vs_bf16": round(tq.tq_cache_bytes(fcfg, w.B, w.Hkv, w.N)[0] /
+                                          (2 * K.numel() * 2), 4)}
+            del fcache, fws, fout
+            log(f"K{bk}/V{bv} decode over {w.N} tokens: {fus:.1f} us "
+                f"({formats[f'K{bk}/V{bv}']['frac_of_hbm_peak']} of peak)")
     del K, V
 
     # the other two 128k+ contexts (outlier keys d 256 K2/V2; QJL K3/V4)
@@ -663,6 +687,7 @@ def main():
         "prefill": prefill,
         "affine": affine,
         "other_workloads": others,
+        "other_formats_same_context": formats,
         "accuracy": accuracy,
         "source_hash": source_hash(),
     }
