@@ -565,7 +565,7 @@ def main():
         log(f"dense bf16 decode {dus:.1f} us ({dgbps:.1f} GB/s, {dgbps / probe_gbps:.2f} of the "
             f"read probe); at the probe rate it would take {probe_bound_us:.1f} us")
     # other fractional splits on the same K/V and query: K3/V3 and the
-    # 2.5-bit K2/V3 (3-bit values run on the VALU decode kernel)
+    # 2.5-bit K2/V3, on the same matrix-core kernel
     formats = None
     if not args.no_others and args.workload == 4:
         formats = {}
@@ -582,7 +582,7 @@ def main():
                 "decode_call_us": round(fus, 2), "algorithmic_bytes": fb,
                 "achieved_gbps": round(fb / fus / 1e3, 1),
                 "frac_of_hbm_peak": round(fb / fus / 1e3 / HBM_PEAK_GBPS, 4),
-                "kernel": "k_decode_pk (VALU; 3-bit values)",
+                "kernel": "k_decode_mx (matrix cores)",
                 "kv_bytes_vs_bf16": round(tq.tq_cache_bytes(fcfg, w.B, w.Hkv, w.N)[0] /
                                           (2 * K.numel() * 2), 4)}
             del fcache, fws, fout

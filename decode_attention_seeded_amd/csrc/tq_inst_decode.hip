@@ -25,17 +25,13 @@ static int go(int mx, const DecodeArgs& a, dim3 grid, hipStream_t st) {
   hipLaunchKernelGGL((k_decode<TQ_D, TQ_BK, BV, GK, QJL>), grid, dim3(TQ_D / 32 * 64), 0, st,
                      a, a.qp, a.qq);
 #else
-  if constexpr (BV == 2 || BV == 4) {
-    if (mx) {
-      const dim3 block(64 * mx_waves(TQ_D));
-      if (a.norm_f16)
-        hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, QJL, true>), grid, block, 0, st, a);
-      else
-        hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, QJL, false>), grid, block, 0, st, a);
-      return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
-    }
-  } else {
-    if (mx) return TQ_ERR_UNSUPPORTED;
+  if (mx) {
+    const dim3 block(64 * mx_waves(TQ_D));
+    if (a.norm_f16)
+      hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, QJL, true>), grid, block, 0, st, a);
+    else
+      hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, QJL, false>), grid, block, 0, st, a);
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
   }
   hipLaunchKernelGGL((k_decode_pk<TQ_D, TQ_BK, BV, GK, QJL>), grid, dim3(TQ_D / 32 * 64), 0,
                      st, a, reinterpret_cast<const uint32_t*>(a.qp), a.qq);

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <cstdint>
+#include <cstdlib>
 #include <cstddef>
 
 #include "tq.h"
@@ -71,11 +72,15 @@ struct DecodePlan {
 
 // Waves per workgroup of the matrix-core decode kernel (one workgroup holds a
 // compute unit; a workgroup round covers 64 tokens per wave), and whether a
-// format runs it (d 128 or 256, 2- or 4-bit values, with or without QJL).
+// format runs it (d 128 or 256, 2- to 4-bit values, with or without QJL).
+// Setting TQ_DECODE_VALU=1 in the environment sends every format to the
+// VALU kernel instead (a diagnostic switch, read on every plan).
 constexpr int mx_waves(int d) { return 8 + 0 * d; }
 inline bool use_mx(int d, int bits_v, int qjl) {
   (void)qjl;
-  return (d == 128 || d == 256) && (bits_v == 2 || bits_v == 4);
+  const char* v = std::getenv("TQ_DECODE_VALU");
+  if (v && v[0] == '1') return false;
+  return (d == 128 || d == 256) && bits_v >= 2 && bits_v <= 4;
 }
 
 // Fills a plan; returns TQ_OK or a negative status.

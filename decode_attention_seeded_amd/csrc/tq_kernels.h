@@ -1238,8 +1238,12 @@ typedef uint32_t mx_u4 __attribute__((ext_vector_type(4)));
 
 template <int D, int BK, int BV, bool QJL>
 struct MxTile {
-  static constexpr int SB = D * BV / 128;       // value bytes per (token, lane column)
-  static constexpr int SW = (SB + 3) / 4;
+  // value lookups per (token, lane column): one per byte of 2- or 4-bit codes
+  // (a quad or a pair), one per pair of 3-bit codes
+  static constexpr int SB = BV == 2 ? D / 64 : D / 32;
+  // dwords of value bits kept per token: the column's bytes, or for 3-bit
+  // codes (3 or 6 bytes at any byte offset) the aligned 8 bytes around them
+  static constexpr int SW = BV == 3 ? 2 : (SB + 3) / 4;
   uint32_t kw[D * BK / 32];     // key row of the lane's token
   uint32_t kn, vn;              // its key and value norms (f16 or f32 bits)
   uint32_t vx[16][SW];          // value slices: token 16*(i/4) + 4*kq + i%4
@@ -1249,14 +1253,16 @@ struct MxTile {
 
 // tiles each wave loads ahead of the one it processes (1 or 2): two where
 // three tile buffers still fit the register budget without spilling
-constexpr int mx_prefetch(int d, int bk, bool qjl) { return d == 128 && bk < 4 ? 2 + 0 * qjl : 1; }
+constexpr int mx_prefetch(int d, int bk, int bv, bool qjl) {
+  return d == 128 && bk < 4 && bv != 3 ? 2 + 0 * qjl : 1;
+}
 
 template <int D, int BK, int BV, int GK, bool QJL, bool NF16>
 __global__ void __launch_bounds__(64 * mx_waves(D))
     __attribute__((amdgpu_waves_per_eu(mx_waves(D) / 4)))
 k_decode_mx(DecodeArgs a) {
   static_assert(D == 128 || D == 256, "matrix-core decode: d 128 or 256");
-  static_assert(BV == 2 || BV == 4, "matrix-core decode: 2- or 4-bit values");
+  static_assert(BV >= 2 && BV <= 4, "matrix-core decode: 2- to 4-bit values");
   static_assert(GK == 1 || GK == 2 || GK == 4, "heads per workgroup");
   constexpr int W = mx_waves(D);
   constexpr int TW = 64;                       // tokens per wave tile
@@ -1274,6 +1280,7 @@ k_decode_mx(DecodeArgs a) {
   // that the 64 lanes of a lookup hit 64 different banks)
   constexpr bool KQ4 = BK == 2;
   constexpr bool VQ4 = BV == 2;
+  constexpr bool V3 = BV == 3;                 // 3-bit values: pairs of 6-bit fields
   constexpr int KT_BYTES = KQ4 ? 256 * 256 : KE * 256;
   constexpr int VT_BYTES = VQ4 ? 256 * 256 : VE * 256;
   constexpr int NS = D / 4;                    // score steps per token
@@ -1339,8 +1346,15 @@ k_decode_mx(DecodeArgs a) {
   // value slice i of a lane is token 16 (i / 4) + 4 (i % 4) + kq, so one load
   // instruction covers four consecutive rows (whole cache lines) and the
   // value, norm and sign-plane loads can stream past the caches (nontemporal)
-  const uint32_t vo0 = uint32_t(kq) * VREC + uint32_t(col) * SB;
+  // 3-bit values: the column's 3 D / 128 bytes start at byte vby of the row;
+  // the lane loads the dword-aligned 8 bytes from vby & ~3 and shifts them
+  // down by vsh bits
+  const uint32_t vby = uint32_t(col) * (3 * D / 128);
+  const uint32_t vsh = (vby & 3u) * 8u;
+  const uint32_t vo0 = uint32_t(kq) * VREC + (V3 ? (vby & ~3u) : uint32_t(col) * SB);
   constexpr int kNT = 2;                       // cache policy: nontemporal
+  // overlapping windows of 48-byte rows are not whole lines: normal policy
+  constexpr int kValNT = V3 ? 0 : kNT;
   constexpr int kSignNT = D / 8 == 16 ? kNT : 0;   // sign rows of 16 B: whole lines
   auto load = [&](int64_t base, Tile& t) {
     const uint32_t n = rows_left(base);
@@ -1377,8 +1391,8 @@ k_decode_mx(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int so = (16 * (i >> 2) + 4 * (i & 3)) * VREC;
-      if constexpr (SB == 8) {
-        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rv, vo0, so, kNT);
+      if constexpr (V3 || SB == 8) {
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rv, vo0, so, kValNT);
         t.vx[i][0] = v2[0];
         t.vx[i][Tile::SW - 1] = v2[1];
       } else if constexpr (SB == 4) {
@@ -1448,7 +1462,7 @@ k_decode_mx(DecodeArgs a) {
             dev::pack_f16x2(ldexpf(v2[2 * i], -qe), ldexpf(v2[2 * i + 1], -qe));
     }
   }
-  constexpr int PF = mx_prefetch(D, BK, QJL);
+  constexpr int PF = mx_prefetch(D, BK, BV, QJL);
   const int64_t wb = t_begin + int64_t(wave) * TW;
   const bool early = !a.append;
   // PF + 1 tile buffers, all requested before the set-up; in the loop a
@@ -1682,11 +1696,24 @@ k_decode_mx(DecodeArgs a) {
   constexpr int NV = D / 8;
   constexpr int NG = VQ4 ? 8 : 4;
   static_assert(NV == NG * SB, "value steps");
+  // 3-bit values: the token's bits of the column, shifted to bit 0 (24 or 48
+  // bits), taken once per token when its group starts
+  uint32_t xw[4][2];
   auto v_issue = [&](auto ic, const Tile& cur) {
     constexpr int i = decltype(ic)::value, G = i / SB, cb = i % SB;
     constexpr uint32_t sel = 0x0C000000u | VSEL2 | uint32_t(4 + (cb & 3)) << 8;
     mx_u4 vb;
-    if constexpr (!VQ4) {
+    if constexpr (V3) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (cb == 0) {
+          const uint32_t w0 = cur.vx[4 * G + u][0], w1 = cur.vx[4 * G + u][1];
+          xw[u][0] = __builtin_amdgcn_alignbit(w1, w0, vsh);
+          xw[u][1] = w1 >> vsh;
+        }
+        vb[u] = *reinterpret_cast<const uint32_t*>(vtab + (dev::bits_at<6, 8>(xw[u], 6 * cb) | vl4));
+      }
+    } else if constexpr (!VQ4) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         vb[u] = *reinterpret_cast<const uint32_t*>(

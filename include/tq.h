@@ -188,8 +188,8 @@ int tq_num_splits(const tq_config* cfg, int B, int Hq, int Hkv, int64_t n_ctx,
 /* Workspace bytes tq_attend_decode needs; negative tq_status on bad args
  * (TQ_ERR_ARG also when B * Hkv * head groups exceeds 65535).
  * The workspace starts with 65535 arrival counters (256 KB, one per
- * (batch, KV head, head group) row of the decode grid): for the formats with
- * 2- or 4-bit values the last workgroup of each row to finish merges the
+ * (batch, KV head, head group) row of the decode grid): on the matrix-core
+ * kernel (d 128 or 256) the last workgroup of each row to finish merges the
  * row's split partials, which follow the counters. The counters must read
  * zero when a call starts: zero the buffer once before its first use. Every
  * call leaves them at zero again, so the same buffer serves later calls of
@@ -223,6 +223,9 @@ int64_t tq_workspace_bytes(const tq_config* cfg, int B, int Hq, int Hkv,
  * output's max row-relative error against fp64 is about 5e-4 for
  * unit-variance q and k (scores spanning a few log2 units) and about 2e-3
  * when q is 10x larger.
+ * Kernels: d 128 and 256 run on the matrix cores; other head dims, or every
+ * format when the environment variable TQ_DECODE_VALU is "1" when the call
+ * is planned, run on a vector-ALU kernel with the same results contract.
  */
 int tq_attend_decode(const tq_config* cfg, const void* q, int q_dtype, int B,
                      int Hq, const tq_cache* cache, int64_t n_ctx, float scale,

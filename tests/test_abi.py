@@ -89,14 +89,15 @@ def test_cache_bytes_match_format(bk, bv, nd, qjl, d):
     assert planes[0] == 600 * d * bk // 8 and planes[1] == 600 * d * bv // 8
 
 
-def test_split_plan_and_workspace():
+def test_split_plan_and_workspace(monkeypatch):
     cfg = tq.Config(d=128, bits_k=3, bits_v=4)
     s = tq.tq_num_splits(cfg, 1, 32, 8, 524288)
     assert s >= 8
     assert tq.tq_num_splits(cfg, 1, 32, 8, 1) == 1
     # clamped to tiles: workgroup rounds are 64 tokens per wave; the
-    # matrix-core kernel (2/4-bit values, with or without QJL) runs 8 waves;
-    # the other formats use 256-token tiles (d 128)
+    # matrix-core kernel (d 128 / 256, with or without QJL) runs 8 waves; the
+    # VALU kernel (TQ_DECODE_VALU=1, or other head dims) uses 256-token tiles
+    # at d 128
     assert tq.tq_num_splits(cfg, 1, 32, 8, 300, splits=7) == 1
     assert tq.tq_num_splits(cfg, 1, 32, 8, 2100, splits=7) == 5
     cfgq = tq.Config(d=128, bits_k=3, bits_v=4, qjl=True)
@@ -104,7 +105,11 @@ def test_split_plan_and_workspace():
     cfg256 = tq.Config(d=256, bits_k=2, bits_v=2)
     assert tq.tq_num_splits(cfg256, 8, 16, 4, 1100, splits=7) == 3
     cfg3 = tq.Config(d=128, bits_k=3, bits_v=3)
+    assert tq.tq_num_splits(cfg3, 1, 32, 8, 300, splits=7) == 1
+    monkeypatch.setenv("TQ_DECODE_VALU", "1")
     assert tq.tq_num_splits(cfg3, 1, 32, 8, 300, splits=7) == 2
+    assert tq.tq_num_splits(cfg, 1, 32, 8, 300, splits=7) == 2
+    monkeypatch.delenv("TQ_DECODE_VALU")
     # default: one round of ~256 workgroups for the wave-private kernels
     assert s == 32
     ws = tq.tq_workspace_bytes(cfg, 1, 32, 8, 524288)

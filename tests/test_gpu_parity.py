@@ -52,6 +52,11 @@ SMALL = {
                              wid=115),
     "d256_k2v2_sphere_qjl": dict(B=1, Hq=4, Hkv=2, d=256, N=520, bits_k=2, bits_v=2, qjl=True,
                                  codebook="sphere", wid=116),
+    # 3-bit values on the matrix cores: windows of the column's 3 or 6 bytes
+    # at every byte offset, with QJL, and d = 256 with 2-bit keys
+    "d128_k3qjl_v3_g4": dict(B=2, Hq=8, Hkv=2, N=700, bits_k=3, bits_v=3, qjl=True,
+                             structure="correlated", wid=117),
+    "d256_k2v3_g4": dict(B=1, Hq=4, Hkv=1, d=256, N=900, bits_k=2, bits_v=3, wid=118),
 }
 
 
@@ -78,6 +83,15 @@ def _run_case(w, scale=0.0, splits=0):
 
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_encode_and_decode_match_oracle(name):
+    _run_case(si.small_workload(**SMALL[name]))
+
+
+@pytest.mark.parametrize("name", ["d128_k3v4_gqa4", "d256_k2v2_outlier", "d128_k3v3_g3",
+                                  "d128_k3qjl_v4_corr"])
+def test_valu_decode_kernel_matches_oracle(name, monkeypatch):
+    """TQ_DECODE_VALU=1 sends every format to the VALU decode kernel (no
+    matrix cores); it must meet the same bar."""
+    monkeypatch.setenv("TQ_DECODE_VALU", "1")
     _run_case(si.small_workload(**SMALL[name]))
 
 
