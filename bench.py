@@ -588,6 +588,22 @@ def main():
             del fcache, fws, fout
             log(f"K{bk}/V{bv} decode over {w.N} tokens: {fus:.1f} us "
                 f"({formats[f'K{bk}/V{bv}']['frac_of_hbm_peak']} of peak)")
+    # the headline format on the vector-ALU decode kernel (no matrix cores)
+    valu = None
+    if not args.no_others and args.workload == 4:
+        os.environ["TQ_DECODE_VALU"] = "1"
+        try:
+            vws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N))
+            vout = torch.empty_like(out)
+            vus = timed(torch, lambda: tq.tq_attend_decode(cfg, q, cache, w.N, vout, vws), 30)
+            valu = {"decode_call_us": round(vus, 2),
+                    "frac_of_hbm_peak": round(alg_bytes / vus / 1e3 / HBM_PEAK_GBPS, 4),
+                    "kernel": "k_decode_pk (TQ_DECODE_VALU=1)",
+                    "max_abs_diff_vs_matrix_core": float((vout - out).abs().max())}
+            del vws, vout
+        finally:
+            del os.environ["TQ_DECODE_VALU"]
+        log(f"VALU decode kernel: {valu['decode_call_us']} us ({valu['frac_of_hbm_peak']} of peak)")
     del K, V
 
     # the other two 128k+ contexts (outlier keys d 256 K2/V2; QJL K3/V4)
@@ -688,6 +704,7 @@ def main():
         "affine": affine,
         "other_workloads": others,
         "other_formats_same_context": formats,
+        "valu_decode_kernel": valu,
         "accuracy": accuracy,
         "source_hash": source_hash(),
     }

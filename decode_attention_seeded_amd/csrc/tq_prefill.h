@@ -214,6 +214,7 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   }
   const int64_t r_last = (r0 + NR - 1 < R ? r0 + NR - 1 : R - 1);
   const int64_t p_max = pos0 + r_last / a.G;
+  const int64_t p_min = pos0 + r0 / a.G;  // tiles wholly at or before it need no mask
   const int ntiles = int(p_max / TT) + 1;
 
   // ---------------- dequant role: lane = token of the tile, wave = quarter
@@ -328,11 +329,10 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
     const _Float16* vtl = vtile(buf);
     const _Float16* stl = stile(buf);
 
-    // ---------------- scores S^T (tokens x rows), scaled and masked
+    // ---------------- scores S^T (tokens x rows), scaled (exp2 units) and
+    // masked on the tiles that reach past the workgroup's lowest row position
+    const bool masked = int64_t(n) * TT + TT - 1 > p_min;   // workgroup-uniform
     float sc[RB][4][4];
-    float mt[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) mt[rb] = -INFINITY;
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       pf_f4 acc[RB], acq[QJL ? RB : 1];
@@ -367,22 +367,57 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t tok = int64_t(n) * TT + 16 * tb + 4 * kq + i;
           float v = acc[rb][i] * kss[i];
           if constexpr (QJL) v = fmaf(acq[rb][i], rhs[i], v);
-          sc[rb][tb][i] = tok <= my_pos[rb] ? v : -INFINITY;
-          mt[rb] = fmaxf(mt[rb], sc[rb][tb][i]);
+          sc[rb][tb][i] = v;
         }
     }
-    float alpha[RB];
+    if (masked) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t tok = int64_t(n) * TT + 16 * tb + 4 * kq + i;
+            if (tok > my_pos[rb]) sc[rb][tb][i] = -INFINITY;
+          }
+    }
+    // The running max (per row, the same on its 4 lanes) is raised only when
+    // a score exceeds it by more than 2^8 (weights stay <= 2^8, which with
+    // the value-norm band below keeps the fp16 operands finite): then the
+    // tile's row maxima are taken and the accumulators rescaled. The branch
+    // is wave-uniform; it always runs on the first tile (m_run = -1e30, so
+    // alpha = 0), and a row masked on every token keeps m_run and weight 0.
     pf_h8 pa[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      mt[rb] = fmaxf(mt[rb], __shfl_xor(mt[rb], 16));
-      mt[rb] = fmaxf(mt[rb], __shfl_xor(mt[rb], 32));
-      const float m_new = fmaxf(m_run[rb], mt[rb]);
-      alpha[rb] = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-      m_run[rb] = m_new;
+      const float lim = m_run[rb] + 8.f;
+      bool up = false;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) up |= sc[rb][tb][i] > lim;
+      if (__ballot(up)) {
+        float mt = -INFINITY;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[rb][tb][i]);
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m_run[rb], mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
+        m_run[rb] = m_new;
+        l_run[rb] *= alpha;
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * kq + i);
+#pragma unroll
+        for (int j = 0; j < NS; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[rb][j][i] *= al[i];
+      }
     }
     float ls[RB];
 #pragma unroll
@@ -430,24 +465,12 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
           pa[rb][tb >> 1][4 * (tb & 1) + i] = _Float16(p * nvs[i]);
         }
     }
+    // the lane's partial row sums (its 16 tokens); the 4 lanes of a row are
+    // added once, after the loop
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      ls[rb] += __shfl_xor(ls[rb], 16);
-      ls[rb] += __shfl_xor(ls[rb], 32);
-      l_run[rb] = l_run[rb] * alpha[rb] + ls[rb];
-    }
+    for (int rb = 0; rb < RB; ++rb) l_run[rb] += ls[rb];
 
-    // ---------------- O = O * alpha + P V_hat (rows 4kq + i of each block)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      float al[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha[rb], 4 * kq + i);
-#pragma unroll
-      for (int j = 0; j < NS; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[rb][j][i] *= al[i];
-    }
+    // ---------------- O += P V_hat (rows 4kq + i of each block)
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
@@ -468,6 +491,11 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   }
 
   // ---------------- O / l, then R^T per row, fp32 out
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    l_run[rb] += __shfl_xor(l_run[rb], 16);
+    l_run[rb] += __shfl_xor(l_run[rb], 32);
+  }
   __syncthreads();                      // the tiles are dead: stage rows there
   float* ost = reinterpret_cast<float*>(smem);
 #pragma unroll
