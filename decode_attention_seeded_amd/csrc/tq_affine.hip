@@ -21,6 +21,7 @@
 //           p_t scale_t code_tc + sum_t p_t bias_t, quarters summed at the end.
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 
 #include "tq_internal.h"
 #include "tq_kernels.h"
@@ -420,6 +421,436 @@ __global__ void __launch_bounds__(64 * kAffWaves) k_affine_decode(AffDecodeArgs 
 }
 
 // ----------------------------------------------------------------------------
+// Matrix-core decode of the 4-bit affine format at d 128 (up to 4 query
+// heads per workgroup; the layout also takes d 256 with up to 2). A 4-bit code c enters the
+// products as the fp16 number 64 + c: low byte c << 4 (a byte's high
+// nibble as it is, or its low nibble shifted up) and high byte 0x54, placed
+// by one v_perm (exact: fp16 spacing is 1/16 in [64, 128), and an offset
+// small enough next to the codes' own contribution that the fp32 sums keep
+// their precision); the offset is taken back out in fp32 per group, from the
+// query's group sums (scores) and from the sum of the rounded weights
+// (values). Per 64-token wave tile:
+//   scores  lane = token, v_mfma_f32_4x4x4_16b_f16 with the query block
+//           broadcast: step j takes 4 coordinates of one key dword, in the
+//           order (0, 2, 1, 3) or (4, 6, 5, 7) of its 8 codes (the even and
+//           the odd nibbles, each masked out with one AND); one accumulator
+//           pair per group of 64 coordinates, then
+//           s = sum_grp ks_grp (dot_grp - 64 qsum16_grp) 2^qe + kb_grp qsum_grp
+//   values  v_mfma_f32_16x16x32_f16: column n = the lane's D/16 coordinates,
+//           K = (token, pair element), and A row g + GK (j + 2 grp) carries
+//           head g's weight p * vscale_grp for pair element j; a column only
+//           keeps the rows of its own group. sum_t p vbias_grp and the
+//           weights' own sum (for the offset) are per-lane fp32 sums.
+// Split partials (original value frame) are merged by k_merge.
+template <int D, int GK>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+k_affine_decode_mx(AffDecodeArgs a) {
+  constexpr int W = 8, TW = 64, T = W * TW;
+  constexpr int NG = D / kAffGroup;            // groups per row
+  constexpr int KREC = D / 2, VREC = D / 2;    // 4-bit rows
+  constexpr int KW = D / 8;                    // key dwords per row (lane = token)
+  constexpr int NS = D / 4;                    // score steps
+  constexpr int NQ = NS / 16;                  // query quads per lane
+  constexpr int SB = D / 32;                   // value slots (pairs) per (token, column)
+  constexpr int VW = D / 128;                  // value dwords per (token, column)
+  constexpr int CPC = D / 16;                  // coordinates per column
+  constexpr int CPG = 16 / NG;                 // columns per group
+  constexpr int NROW = GK * 2 * NG;            // live A rows
+  constexpr int PX = GK * NG * TW / 2;         // weight dwords per wave tile
+  constexpr float kRescale = 8.0f;
+  static_assert(NROW <= 16, "A rows: heads x pair element x group");
+  using mx_h4 = _Float16 __attribute__((ext_vector_type(4)));
+  using mx_h8 = _Float16 __attribute__((ext_vector_type(8)));
+  using mx_f4 = float __attribute__((ext_vector_type(4)));
+  using mx_u2 = uint32_t __attribute__((ext_vector_type(2)));
+  using mx_u4 = uint32_t __attribute__((ext_vector_type(4)));
+
+  __shared__ __attribute__((aligned(16))) uint32_t pex[W][2][PX];
+  __shared__ __attribute__((aligned(16))) uint32_t qs[GK][NS * 2];   // fp16 steps
+  __shared__ float qsum[GK][NG], qsum16[GK][NG];
+  __shared__ int qexp;
+  __shared__ __attribute__((aligned(16))) float slab[W][GK][D];
+  __shared__ float wst[W][GK][2 + 2 * NG];      // m, l, then per group bias and weight sums
+  __shared__ int vexp_w[W];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, kq = lane >> 4;
+  const int split = blockIdx.x;
+  const int unit = blockIdx.y;
+  const int chunk = unit % a.chunks;
+  const int bkv = unit / a.chunks;
+  const int b = bkv / a.Hkv;
+  const int kvh = bkv - b * a.Hkv;
+  const int64_t head0 = int64_t(b) * a.Hq + kvh * a.G + chunk * GK;
+  const int64_t t_begin = int64_t(split) * a.tps;
+  const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
+  const int64_t row0 = int64_t(bkv) * a.capacity;
+  const int iters = int((t_end - t_begin + T - 1) / T);
+
+  // ---- query rows: R q * tau * log2 e, one power of two 2^-qe for the GK
+  // rows (largest element near 2^10), fp16 in score-step order
+  if (tid < 16 * GK) {
+    constexpr int E = D / 16;
+    const int g = tid >> 4, l16 = tid & 15;
+    float v[E];
+    dev::load_row_part<E>(a.q, a.q_dtype, (head0 + g) * D + l16 * E, v);
+    const uint32_t neg = dev::bitmap_bits(a.sbits, l16 * E, E);
+#pragma unroll
+    for (int i = 0; i < E; ++i) if (neg >> i & 1) v[i] = -v[i];
+    dev::fwht16<E, float>(v, l16);
+    const float mult = a.qmult / sqrtf(float(D));
+    float vmax = 0.f;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      v[i] *= mult;
+      vmax = fmaxf(vmax, fabsf(v[i]));
+    }
+    vmax = dev::group_max16(vmax);
+    if constexpr (GK >= 2) vmax = fmaxf(vmax, __shfl_xor(vmax, 16));
+    if constexpr (GK >= 4) vmax = fmaxf(vmax, __shfl_xor(vmax, 32));
+    const int qe = vmax > 0.f ? ilogbf(vmax) - 10 : 0;
+    if (tid == 0) qexp = qe;
+    // the lane's E coordinates l16 E .. are whole key dwords (8 codes):
+    // steps 2k, 2k + 1 of dword k take coordinates (0, 2, 1, 3), (4, 6, 5, 7)
+    float part = 0.f, part16 = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < E / 8; ++kk) {
+      const int k = l16 * (E / 8) + kk;
+      _Float16 h[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        h[e] = _Float16(ldexpf(v[8 * kk + e], -qe));
+        part += v[8 * kk + e];
+        part16 += float(h[e]);
+      }
+      qs[g][4 * k + 0] = __builtin_bit_cast(uint32_t, dev::half2_t{h[0], h[2]});
+      qs[g][4 * k + 1] = __builtin_bit_cast(uint32_t, dev::half2_t{h[1], h[3]});
+      qs[g][4 * k + 2] = __builtin_bit_cast(uint32_t, dev::half2_t{h[4], h[6]});
+      qs[g][4 * k + 3] = __builtin_bit_cast(uint32_t, dev::half2_t{h[5], h[7]});
+    }
+    constexpr int LPG = kAffGroup / E;          // lanes per group
+#pragma unroll
+    for (int m = 1; m < LPG; m <<= 1) {
+      part += __shfl_xor(part, m, 16);
+      part16 += __shfl_xor(part16, m, 16);
+    }
+    if (l16 % LPG == 0) {
+      qsum[g][l16 / LPG] = part;
+      qsum16[g][l16 / LPG] = part16;
+    }
+  }
+
+  // ---- tiles: keys lane = token; values lane = (token kq + 4 (i % 4) +
+  // 16 (i / 4), column col), whole 64-byte rows per four lanes
+  struct Tile {
+    uint32_t kw[KW];
+    uint32_t ks[NG], kb[NG], vs[NG], vb[NG];     // fp16 bits
+    uint32_t vx[16][VW];
+  };
+  auto rows_left = [&](int64_t base) -> uint32_t {
+    const int64_t n = t_end - base;
+    return uint32_t(n <= 0 ? 0 : (n < TW ? n : TW));
+  };
+  constexpr int kNT = 2;                       // nontemporal
+  const uint32_t vo0 = uint32_t(kq) * VREC + uint32_t(col) * (4 * VW);
+  auto load = [&](int64_t base, Tile& t) {
+    const uint32_t n = rows_left(base);
+    const auto rk = dev::buffer_rsrc(a.kc + (row0 + base) * KREC, n * KREC);
+#pragma unroll
+    for (int k = 0; k < KW / 4; ++k) {
+      const auto q4 = __builtin_amdgcn_raw_buffer_load_b128(rk, uint32_t(lane) * KREC, 16 * k, 0);
+      t.kw[4 * k] = q4[0]; t.kw[4 * k + 1] = q4[1]; t.kw[4 * k + 2] = q4[2];
+      t.kw[4 * k + 3] = q4[3];
+    }
+    const uint16_t* pl[4] = {a.ks, a.kb, a.vs, a.vb};
+    uint32_t* dst[4] = {t.ks, t.kb, t.vs, t.vb};
+#pragma unroll
+    for (int pi = 0; pi < 4; ++pi) {
+      const auto rs = dev::buffer_rsrc(pl[pi] + (row0 + base) * NG, n * NG * 2);
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+        dst[pi][gi] = __builtin_amdgcn_raw_buffer_load_b16(rs, uint32_t(lane) * NG * 2 + 2 * gi,
+                                                           0, kNT);
+    }
+    const auto rv = dev::buffer_rsrc(a.vc + (row0 + base) * VREC, n * VREC);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int so = (16 * (i >> 2) + 4 * (i & 3)) * VREC;
+      if constexpr (VW == 2) {
+        const auto v2 = __builtin_amdgcn_raw_buffer_load_b64(rv, vo0, so, kNT);
+        t.vx[i][0] = v2[0];
+        t.vx[i][1] = v2[1];
+      } else {
+        t.vx[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rv, vo0, so, kNT);
+      }
+    }
+  };
+  const int64_t wb = t_begin + int64_t(wave) * TW;
+  Tile ta, tb;
+  load(wb, ta);
+  load(wb + T, tb);
+  __syncthreads();
+
+  // query quads for the broadcast A operand (lane block lane/4 = step j % 16,
+  // row lane % 4 = head)
+  mx_u2 qa[NQ];
+  {
+    const int qm = lane & 3, qb = lane >> 2;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const int j = qb + 16 * i;
+      qa[i] = qm < GK ? mx_u2{qs[qm][2 * j], qs[qm][2 * j + 1]} : mx_u2{0u, 0u};
+    }
+  }
+  const float qsc = ldexpf(1.f, qexp);
+  float qs16[GK][NG], qsf[GK][NG];
+#pragma unroll
+  for (int g = 0; g < GK; ++g)
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      qs16[g][gi] = 64.f * qsum16[g][gi];
+      qsf[g][gi] = qsum[g][gi];
+    }
+
+  // weight slots (token 16 G + 4 u + kq at slot 16 G + 4 kq + u) and the A
+  // operand selectors of the lane's row r = g + GK (j + 2 grp)
+  const int pslot = (lane & 0x30) | ((lane & 3) << 2) | ((lane >> 2) & 3);
+  uint32_t asel[2];
+  int arow = 0;
+  {
+    const int r = col;
+    const bool live = r < NROW;
+    const int rg = r % GK, rj = (r / GK) & 1, rgrp = r / (2 * GK);
+    constexpr uint32_t kZ = 0x0C0C0C0Cu;
+    const uint32_t lo = rj ? 0x01000C0Cu : 0x0C0C0100u;
+    const uint32_t hi = rj ? 0x03020C0Cu : 0x0C0C0302u;
+    asel[0] = live ? lo : kZ;
+    asel[1] = live ? hi : kZ;
+    arow = live ? (rg * NG + rgrp) * TW : 0;
+  }
+  constexpr uint32_t kC54 = 0x54545454u;      // the high byte of 64 + c
+  // halfwords (0x54 << 8 | byte b): bytes 0, 1 or 2, 3 of the nibble source
+  constexpr uint32_t kLo = 0x04010400u, kHi = 0x04030402u;
+
+  float m_run[GK], lpart[GK], bsum[GK][NG], wsum[GK][NG];
+  int vexp = 0;
+  float vsc = 1.f;                             // 2^-vexp
+  mx_f4 acc[SB];
+#pragma unroll
+  for (int g = 0; g < GK; ++g) {
+    m_run[g] = -INFINITY;
+    lpart[g] = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) bsum[g][gi] = wsum[g][gi] = 0.f;
+  }
+#pragma unroll
+  for (int s = 0; s < SB; ++s) acc[s] = mx_f4{0.f, 0.f, 0.f, 0.f};
+
+  auto process = [&](int64_t base, uint32_t* px, const Tile& cur) {
+    const bool valid = base + lane < t_end;
+    // ---- scores
+    mx_f4 sk[NG][2];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) sk[gi][0] = sk[gi][1] = mx_f4{0.f, 0.f, 0.f, 0.f};
+    dev::static_for<0, KW>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      // even codes (low nibbles) and odd codes (high nibbles) as c << 4
+      const uint32_t t0 = (cur.kw[k] << 4) & 0xF0F0F0F0u;
+      const uint32_t t1 = cur.kw[k] & 0xF0F0F0F0u;
+      dev::static_for<0, 2>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        constexpr int j = 2 * k + h;
+        constexpr uint32_t sel = h ? kHi : kLo;
+        const mx_u2 kb = {__builtin_amdgcn_perm(kC54, t0, sel), __builtin_amdgcn_perm(kC54, t1, sel)};
+        constexpr int gi = (4 * j) / kAffGroup;
+        sk[gi][j & 1] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+            __builtin_bit_cast(mx_h4, qa[j / 16]), __builtin_bit_cast(mx_h4, kb), sk[gi][j & 1], 4,
+            j % 16, 0);
+      });
+    });
+    float ksf[NG], kbf[NG], vw[NG];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      ksf[gi] = dev::f16_to_f32(cur.ks[gi]) * qsc;
+      kbf[gi] = dev::f16_to_f32(cur.kb[gi]);
+      vw[gi] = dev::f16_to_f32(cur.vs[gi]) * vsc;
+    }
+    // value weights stay in fp16's normal range: the tile's largest scale
+    // times 2^-vexp within [2^-6, 2^6] (p <= 2^8)
+    {
+      float vm = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) vm = fmaxf(vm, vw[gi]);
+      const bool high = __ballot(vm > 64.f) != 0;
+      const bool low = __ballot(vm >= 0.015625f) == 0 && __ballot(vm > 0.f) != 0;
+      if (high || low) {                       // wave-uniform, rare
+        const int sh = ilogbf(dev::dpp_wave_max(vm)) - 4;
+        vsc = ldexpf(vsc, -sh);
+        vexp += sh;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) vw[gi] = ldexpf(vw[gi], -sh);
+#pragma unroll
+        for (int s = 0; s < SB; ++s)
+#pragma unroll
+          for (int g = 0; g < GK; ++g) acc[s][g] = ldexpf(acc[s][g], -sh);
+        // (the weight sums are rescaled with them: they stay in acc's units)
+#pragma unroll
+        for (int g = 0; g < GK; ++g)
+#pragma unroll
+          for (int gi = 0; gi < NG; ++gi) wsum[g][gi] = ldexpf(wsum[g][gi], -sh);
+      }
+    }
+    // ---- online softmax, lazily raised running max
+    uint16_t* p16 = reinterpret_cast<uint16_t*>(px);
+#pragma unroll
+    for (int g = 0; g < GK; ++g) {
+      float s = 0.f;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+        s = fmaf(ksf[gi], (sk[gi][0][g] + sk[gi][1][g]) - qs16[g][gi], fmaf(kbf[gi], qsf[g][gi], s));
+      if (__ballot(valid && s > m_run[g] + kRescale)) {      // wave-uniform
+        const float mx = dev::dpp_wave_max(valid ? s : -INFINITY);
+        const float m_new = fmaxf(m_run[g], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+        m_run[g] = m_new;
+        lpart[g] *= alpha;
+#pragma unroll
+        for (int s2 = 0; s2 < SB; ++s2) acc[s2][g] *= alpha;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          bsum[g][gi] *= alpha;
+          wsum[g][gi] *= alpha;
+        }
+      }
+      const float e = __builtin_amdgcn_exp2f(s - m_run[g]);
+      const float p = valid ? e : 0.f;
+      lpart[g] += p;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        const _Float16 w16 = _Float16(p * vw[gi]);
+        p16[(g * NG + gi) * TW + pslot] = __builtin_bit_cast(uint16_t, w16);
+        wsum[g][gi] += float(w16);
+        bsum[g][gi] = fmaf(p, dev::f16_to_f32(cur.vb[gi]), bsum[g][gi]);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- values: 16-token groups G; slot s of the column's dword s / 4:
+    // pair (0, 2), (1, 3), (4, 6), (5, 7) of its 8 codes
+    const uint16_t* pr = reinterpret_cast<const uint16_t*>(px) + arow + 4 * kq;
+#pragma unroll
+    for (int G = 0; G < 4; ++G) {
+      const mx_u2 X = *reinterpret_cast<const mx_u2*>(pr + 16 * G);
+      const mx_u4 aw = {__builtin_amdgcn_perm(X[0], X[0], asel[0]),
+                        __builtin_amdgcn_perm(X[0], X[0], asel[1]),
+                        __builtin_amdgcn_perm(X[1], X[1], asel[0]),
+                        __builtin_amdgcn_perm(X[1], X[1], asel[1])};
+      const mx_h8 pa = __builtin_bit_cast(mx_h8, aw);
+      uint32_t t0[4][VW], t1[4][VW];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int d = 0; d < VW; ++d) {
+          t0[u][d] = (cur.vx[4 * G + u][d] << 4) & 0xF0F0F0F0u;
+          t1[u][d] = cur.vx[4 * G + u][d] & 0xF0F0F0F0u;
+        }
+#pragma unroll
+      for (int s = 0; s < SB; ++s) {
+        const int d = s >> 2, m = s & 3;
+        const uint32_t sel = (m & 2) ? kHi : kLo;
+        mx_u4 vb;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          vb[u] = __builtin_amdgcn_perm(kC54, (m & 1) ? t1[u][d] : t0[u][d], sel);
+        acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, __builtin_bit_cast(mx_h8, vb), acc[s],
+                                                        0, 0, 0);
+      }
+    }
+  };
+
+  {
+    uint32_t* px0 = pex[wave][0];
+    uint32_t* px1 = pex[wave][1];
+    for (int it = 0; it < iters; it += 2) {
+      const int64_t base = wb + int64_t(it) * T;
+      process(base, px0, ta);
+      if (it + 1 >= iters) break;
+      load(base + 2 * T, ta);
+      process(base + T, px1, tb);
+      if (it + 2 >= iters) break;
+      load(base + 3 * T, tb);
+    }
+  }
+
+  // ---- this wave's partial: C row r = 4 kq + i is (head r % GK, pair
+  // element (r / GK) & 1, group r / (2 GK)); a column keeps its own group
+  {
+    const int cgrp = col / CPG;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * kq + i;
+      const int rg = r % GK, rj = (r / GK) & 1, rgrp = r / (2 * GK);
+      if (r < NROW && rgrp == cgrp) {
+#pragma unroll
+        for (int s = 0; s < SB; ++s) {
+          const int m = s & 3;
+          const int c = CPC * col + 8 * (s >> 2) + ((m & 1) | ((m & 2) << 1)) + 2 * rj;
+          slab[wave][rg][c] = acc[s][i];
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < GK; ++g) {
+      const float l = dev::wave_sum(lpart[g]);
+      float bs[NG], ws[NG];
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        bs[gi] = dev::wave_sum(bsum[g][gi]);
+        ws[gi] = dev::wave_sum(wsum[g][gi]);
+      }
+      if (lane == 0) {
+        wst[wave][g][0] = m_run[g];
+        wst[wave][g][1] = l;
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          wst[wave][g][2 + gi] = bs[gi];
+          wst[wave][g][2 + NG + gi] = ws[gi];
+        }
+      }
+    }
+    if (lane == 0) vexp_w[wave] = vexp;
+  }
+  __syncthreads();
+  // ---- combine the waves: o_c = sum_w f_w (2^vexp_w (C_w,c - 64 wsum_w)
+  // + bsum_w) with f_w = 2^(m_w - M); unnormalized partial and (M, l) out
+  for (int i = tid; i < GK * D; i += 64 * W) {
+    const int g = i / D, c = i - g * D, gi = c / kAffGroup;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, wst[w][g][0]);
+    float sum = 0.f, l = 0.f;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const float mw = wst[w][g][0];
+      const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      const float v = ldexpf(slab[w][g][c] - 64.f * wst[w][g][2 + NG + gi], vexp_w[w]) +
+                      wst[w][g][2 + gi];
+      sum = fmaf(v, f, sum);
+      l = fmaf(wst[w][g][1], f, l);
+    }
+    a.acc[((head0 + g) * a.S + split) * D + c] = sum;
+    if (c == 0) {
+      float* ml = a.ml + ((head0 + g) * a.S + split) * 2;
+      ml[0] = M;
+      ml[1] = l;
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
 // host side
 
 int aff_device_ready() {
@@ -462,25 +893,39 @@ int aff_check_cache(const tq_affine_config* c, const tq_affine_cache* k) {
 
 struct AffPlan {
   int gk, chunks, S;
+  int mx;              // 1: the matrix-core kernel (4-bit keys and values)
   int64_t tps;
   int64_t acc_bytes, total;
 };
+
+// The matrix-core kernel takes 4-bit keys and values at d 128
+// (TQ_DECODE_VALU=1 in the environment keeps every format on the VALU kernel).
+bool aff_use_mx(const tq_affine_config* c) {
+  const char* v = std::getenv("TQ_DECODE_VALU");
+  if (v && v[0] == '1') return false;
+  return c->bits_k == 4 && c->bits_v == 4 && c->d == 128;
+}
 
 int aff_plan(const tq_affine_config* c, int B, int Hq, int Hkv, int64_t n_ctx, int splits,
              AffPlan* p) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || n_ctx < 1 || splits < 0) return TQ_ERR_ARG;
   const int G = Hq / Hkv;
-  p->gk = G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1);
+  p->mx = aff_use_mx(c) ? 1 : 0;
+  // matrix-core kernel: query heads x 2 x groups <= 16 product rows
+  const int gmax = p->mx && c->d == 256 ? 2 : 4;
+  p->gk = G % 4 == 0 && gmax >= 4 ? 4 : (G % 2 == 0 ? 2 : 1);
   p->chunks = G / p->gk;
   const int64_t units = int64_t(B) * Hkv * p->chunks;
-  const int64_t round = int64_t(kAffWaves) * kAffTile;
+  // tokens per workgroup round: 8 (matrix cores) or 4 waves of 64
+  const int64_t round = p->mx ? 512 : int64_t(kAffWaves) * kAffTile;
   const int64_t max_s = std::min<int64_t>(kMaxSplitCount, (n_ctx + round - 1) / round);
-  // about 2048 workgroups by default (8 per compute unit, two resident at
-  // a time): measured fastest for long contexts
-  int64_t S = splits > 0 ? splits : (2048 + units - 1) / units;
+  // default: one round of ~256 workgroups for the matrix-core kernel (one
+  // per compute unit); ~2048 for the VALU kernel (8 per compute unit, two
+  // resident at a time): measured fastest for long contexts
+  int64_t S = splits > 0 ? splits : ((p->mx ? 256 : 2048) + units - 1) / units;
   S = std::max<int64_t>(1, std::min(S, max_s));
   int64_t tps = (n_ctx + S - 1) / S;
-  tps = (tps + kAffTile - 1) / kAffTile * kAffTile;
+  tps = (tps + round - 1) / round * round;
   S = (n_ctx + tps - 1) / tps;
   if (units * S > (int64_t(1) << 31) - 1 || units > 65535) return TQ_ERR_UNSUPPORTED;
   p->S = int(S);
@@ -648,8 +1093,20 @@ int tq_affine_attend_decode(const tq_affine_config* cfg, const void* q, int q_dt
     if (splitmix64_at(cfg->seed, uint64_t(i)) >> 63) a.sbits[i >> 5] |= 1u << (i & 31);
 
   const dim3 grid(unsigned(p.S), unsigned(int64_t(B) * cache->Hkv * p.chunks));
-  st = cfg->d == 128 ? launch_aff_decode<128>(cfg->bits_k, cfg->bits_v, p.gk, a, grid, stream)
-                     : launch_aff_decode<256>(cfg->bits_k, cfg->bits_v, p.gk, a, grid, stream);
+  if (p.mx) {
+    const dim3 blk(512);
+    if (cfg->d == 128) {
+      if (p.gk == 4) hipLaunchKernelGGL((k_affine_decode_mx<128, 4>), grid, blk, 0, stream, a);
+      else if (p.gk == 2) hipLaunchKernelGGL((k_affine_decode_mx<128, 2>), grid, blk, 0, stream, a);
+      else hipLaunchKernelGGL((k_affine_decode_mx<128, 1>), grid, blk, 0, stream, a);
+    } else {
+      return TQ_ERR_UNSUPPORTED;
+    }
+    st = aff_last_launch();
+  } else {
+    st = cfg->d == 128 ? launch_aff_decode<128>(cfg->bits_k, cfg->bits_v, p.gk, a, grid, stream)
+                       : launch_aff_decode<256>(cfg->bits_k, cfg->bits_v, p.gk, a, grid, stream);
+  }
   if (st != TQ_OK) return st;
   MergeArgs m{};
   m.ml = a.ml;

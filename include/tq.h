@@ -374,7 +374,10 @@ int64_t tq_affine_workspace_bytes(const tq_affine_config* cfg, int B, int Hq,
 /* Decode attention over the first n_ctx tokens of an affine cache:
  * out[b][h] = sum_j softmax_j(scale * <R q, y_hat_j>) v_hat_j, fp32, with
  * y_hat the dequantized rotated keys and v_hat the dequantized values.
- * Arguments, workspace and errors as tq_attend_decode. */
+ * Arguments, workspace and errors as tq_attend_decode. 4-bit keys and values
+ * at d 128 run on the matrix cores (fp16 operands, fp32 accumulation; codes
+ * exact); other formats, or every format when TQ_DECODE_VALU is "1", on a
+ * vector-ALU kernel. */
 int tq_affine_attend_decode(const tq_affine_config* cfg, const void* q, int q_dtype,
                             int B, int Hq, const tq_affine_cache* cache,
                             int64_t n_ctx, float scale, int splits, float* out,

@@ -88,6 +88,11 @@ CASES = {
     "d256_k4v2_outlier": dict(B=1, Hq=4, Hkv=1, d=256, N=650, bits_k=4, bits_v=2,
                               structure="outlier"),
     "d256_k3v4_g2": dict(B=2, Hq=4, Hkv=2, d=256, N=129, bits_k=3, bits_v=4, seed=7),
+    # the matrix-core kernel (4-bit keys and values, d 128) at one and two
+    # query heads per workgroup
+    "d128_k4v4_g1_f16in": dict(B=2, Hq=2, Hkv=2, d=128, N=900, bits_k=4, bits_v=4,
+                               in_dtype="f16"),
+    "d128_k4v4_g2_ragged": dict(B=1, Hq=4, Hkv=2, d=128, N=1531, bits_k=4, bits_v=4),
 }
 
 
@@ -159,3 +164,30 @@ def test_affine_explicit_scale_and_split_counts():
         outs.append(got)
     for g in outs[1:]:
         assert rel_err(g, outs[0])[0] < 1e-5
+
+
+def test_affine_k4v4_split_counts_and_valu_kernel(monkeypatch):
+    # 4-bit keys and values run on the matrix cores: requested split counts
+    # against the oracle, and the VALU kernel (TQ_DECODE_VALU=1) on the same
+    # cache against the oracle and the matrix-core result
+    w = si.small_workload(wid=350, B=1, Hq=8, Hkv=2, d=128, N=3000, bits_k=4, bits_v=4)
+    log("affine K4V4: B=1 Hq=8 Hkv=2 d=128 N=3000, splits 1/3/8, and the VALU kernel")
+    cfg, cache = _gpu_encode(w)
+    ref, _, _ = _oracle_cache(w)
+    planes = {k: ref[k] for k in ("kc", "vc", "ks", "kb", "vs", "vb")}
+    want = None
+    outs = []
+    for splits in (1, 3, 8):
+        got, qf = _decode(w, cfg, cache, w.N, splits=splits)
+        if want is None:
+            want = o.affine_attend(qf, planes, w.N, d=w.d, seed=w.seed, bits_k=4, bits_v=4,
+                                   Hkv=w.Hkv)
+        err, _ = rel_err(got, want)
+        log(f"  matrix cores, splits={splits}: row-relative {err:.2e}")
+        assert err <= TOL
+        outs.append(got)
+    monkeypatch.setenv("TQ_DECODE_VALU", "1")
+    got, _ = _decode(w, cfg, cache, w.N)
+    err, _ = rel_err(got, want)
+    log(f"  VALU kernel: row-relative {err:.2e}; vs matrix cores {rel_err(got, outs[0])[0]:.2e}")
+    assert err <= TOL
