@@ -153,14 +153,21 @@ def _cpu_unit(job):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with its family, model and
+    stepping numbers (virtual machines often report a generic name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break                      # the first processor is enough
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(ids)})" if ids else name
 
 
 def cpu_baseline(w, max_units):

@@ -314,8 +314,13 @@ def test_affine_sizes_and_validation():
     assert lib.tq_affine_num_splits(c, 1, 32, 8, 524288, 0) >= 1
     assert lib.tq_affine_num_splits(c, 1, 30, 8, 1000, 0) == tq.TQ_ERR_ARG      # Hq % Hkv
     assert lib.tq_affine_workspace_bytes(c, 1, 8, 8, 0, 0) == tq.TQ_ERR_ARG     # n_ctx 0
-    # splits never exceed one per 256 tokens; tokens per split are whole tiles
-    assert lib.tq_affine_num_splits(c, 1, 8, 8, 300, 1000) == 2
+    # splits never exceed one per workgroup round (512 tokens on the
+    # matrix-core kernel, which K4/V4 at d 128 runs; 256 on the VALU kernel);
+    # tokens per split are whole rounds
+    assert lib.tq_affine_num_splits(c, 1, 8, 8, 300, 1000) == 1
+    assert lib.tq_affine_num_splits(c, 1, 8, 8, 1100, 1000) == 3
+    c3 = ctypes.byref(tq.AffineConfig(d=128, bits_k=4, bits_v=3, group=64, seed=3).c())
+    assert lib.tq_affine_num_splits(c3, 1, 8, 8, 300, 1000) == 2
     cache = tq.tq_affine_cache(16, 16, 16, 16, 16, 16, 1, 1, 10)
     q = out = ws = ctypes.c_void_p(16)
     st = lib.tq_affine_attend_decode(c, q, 0, 1, 1, ctypes.byref(cache), 11, 0.0, 0, out, ws,

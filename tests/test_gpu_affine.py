@@ -191,3 +191,38 @@ def test_affine_k4v4_split_counts_and_valu_kernel(monkeypatch):
     err, _ = rel_err(got, want)
     log(f"  VALU kernel: row-relative {err:.2e}; vs matrix cores {rel_err(got, outs[0])[0]:.2e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("vs,qs", [(300.0, 1.0), (1e-3, 1.0), (1e4, 1.0), (1.0, 3.0),
+                                   (1.0, 1e-5)])
+def test_affine_k4v4_far_from_unit_scale(vs, qs):
+    # the matrix-core kernel's fp16 operands (query with its power-of-two
+    # scale, weights times the value scale with their band, codes as 64 + c)
+    # on values and queries far from unit scale; fp32 inputs so that both
+    # sides see the same scaled numbers
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.small_workload(wid=360, B=1, Hq=8, Hkv=2, d=128, N=1300, bits_k=4, bits_v=4,
+                          in_dtype="f32")
+    log(f"affine K4V4 range: values x{vs:g}, queries x{qs:g}")
+    _, _, fk, fv = kv_host(w, 0, w.N)
+    fv = fv * vs
+    qf = si.queries(w)[1].astype(np.float64) * qs
+    cfg = _cfg(w)
+    cache = tq.AffineCache(cfg, w.B, w.Hkv, w.N)
+    tq.tq_affine_encode_kv(cfg, torch.from_numpy(fk.astype(np.float32)).cuda(),
+                           torch.from_numpy(fv.astype(np.float32)).cuda(), 0, cache)
+    q = torch.from_numpy(qf.astype(np.float32)).cuda()
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    ws = tq.workspace(tq.tq_affine_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N))
+    tq.tq_affine_attend_decode(cfg, q, cache, w.N, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    ref = o.affine_encode_kv(fk, fv, bits_k=4, bits_v=4, seed=w.seed)
+    want = o.affine_attend(qf.astype(np.float32).astype(np.float64),
+                           {k: ref[k] for k in ("kc", "vc", "ks", "kb", "vs", "vb")}, w.N,
+                           d=w.d, seed=w.seed, bits_k=4, bits_v=4, Hkv=w.Hkv)
+    err, abs_err = rel_err(got, want)
+    log(f"  row-relative {err:.2e} (abs {abs_err:.2e})")
+    assert np.isfinite(got).all()
+    assert err <= TOL
