@@ -16,20 +16,28 @@
 // blocks. Per
 // 64-token tile, double-buffered in LDS so that the next tile's dequant
 // overlaps this tile's products (one barrier per tile):
-//   dequant  lane = token; a wave decodes one quarter of the coordinates
-//            of every token's key (pair-table lookups, row-major fp16 tile)
-//            or value (transposed fp16 tile, one row store per coordinate),
-//            and the per-token scales. With 8 waves, waves 0-3 take the
-//            keys and 4-7 the values; with 4, each wave both.
+//   dequant  keys: lane = token, a wave decodes one quarter of every
+//            token's coordinates (pair-table lookups, 16-byte row stores
+//            into a row-major fp16 tile). Values: lane = 4 consecutive
+//            tokens x 8 coordinates (one octet of their codes); a lookup in
+//            a table of fp16 pairs indexed by the codes of two tokens gives
+//            two tokens' values of one coordinate, so each coordinate of the
+//            4 tokens is one 8-byte store into the transposed tile. Each
+//            value enters the tile times its token's norm (and a per-tile
+//            power of two), each key scale carries the query rows' power of
+//            two. With 8 waves, waves 0-3 take the keys and 4-7 the values;
+//            with 4, each wave both.
 //   scores   S^T = K_hat Q'^T per 16-token block: A = 8 coordinates of a key
 //            row (16-byte LDS read), B = the lane's query row (VGPRs). The
 //            output lane (kq, col) holds tokens 4kq .. 4kq + 3 of the block
 //            for query row col.
 //   softmax  online, in exp2 units, per query row over the 4 lanes that
-//            hold it; tokens past the row's position are masked.
-//   values   O += P V_hat per 32 tokens: the lane's 8 weights (times the
-//            value norm) of blocks 2b and 2b + 1 are the A operand as they
-//            are; the value tile stores its token columns in that order
+//            hold it: one fma gives score minus running max, tokens past
+//            the row's position are masked, the max is raised lazily, and
+//            the fp16 weights 2^t also feed the row sums (dot2).
+//   values   O += P V_hat per 32 tokens: the lane's 8 weights of blocks 2b
+//            and 2b + 1 are the A operand as they are; the value tile
+//            stores its token columns in that order
 //            (token 32b + 16h + 4q + i at column 32b + 8q + 4h + i), so the
 //            B operand is one 16-byte read.
 // Epilogue: O / l, staged per row in LDS, rotated back (R^T) with 16 lanes
@@ -79,6 +87,7 @@ constexpr int pf_rows(int d, bool qjl) { return 16 * pf_waves(d) * pf_row_blocks
 template <int D, int BK, int BV, bool QJL>
 __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   static_assert(D == 128 || D == 256, "prefill: d 128 or 256");
+  static_assert(BV >= 2 && BV <= 4, "prefill: 2 to 4 value bits");
   constexpr int W = pf_waves(D);           // waves
   constexpr int RB = pf_row_blocks(D, QJL);  // blocks of 16 query rows per wave
   constexpr int NR = pf_rows(D, QJL);      // query rows per workgroup
@@ -88,9 +97,8 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   constexpr int NK = D / 32;               // score k-steps of 32 coordinates
   constexpr int KS = D + 8;                // key tile row stride (halves)
   constexpr int VS = TT + 8;               // transposed value tile row stride (halves)
-  constexpr int CPT = D / 4;               // coordinates per dequant thread
-  constexpr int KWD = CPT * BK / 32;       // code dwords per dequant thread
-  constexpr int VWD = CPT * BV / 32;
+  constexpr int CPT = D / 4;               // key coordinates per dequant lane
+  constexpr int KWD = CPT * BK / 32;       // key code dwords per dequant lane
   constexpr int KREC = D * BK / 8;
   constexpr int VREC = D * BV / 8;
   constexpr int KE = 1 << (2 * BK);
@@ -105,11 +113,13 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   constexpr int NBUF = 2 * TILE_BYTES + 4096 <= 152 * 1024 ? 2 : 1;
   constexpr int SMEM = pf_max(NBUF * TILE_BYTES, pf_max(NR * D * 4, QST_BYTES));
   __shared__ __attribute__((aligned(16))) uint8_t smem[SMEM];
-  __shared__ __attribute__((aligned(16))) float tks[2][TT];
-  __shared__ __attribute__((aligned(16))) float tnv[2][TT];
+  __shared__ __attribute__((aligned(16))) float tks[2][TT];     // key scale per token
   __shared__ __attribute__((aligned(16))) float trho[QJL ? 2 : 1][TT];
+  __shared__ int texp[2];                  // the value tile's power of two
+  __shared__ float wmax[W];
   __shared__ uint32_t kpair[KE];
-  __shared__ uint16_t vone[VE];
+  // fp16 values of codes (e & (VE - 1), e >> BV) as one pair, token order
+  __shared__ __attribute__((aligned(16))) uint32_t vpair[VE * VE];
   auto ktile = [&](int buf) { return reinterpret_cast<_Float16*>(smem + buf * TILE_BYTES); };
   auto vtile = [&](int buf) {
     return reinterpret_cast<_Float16*>(smem + buf * TILE_BYTES + KT_BYTES);
@@ -133,13 +143,14 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
 
   for (int e = tid; e < KE; e += NT)
     kpair[e] = dev::pack_f16x2(a.cbk[e & ((1 << BK) - 1)], a.cbk[e >> BK]);
-  for (int e = tid; e < VE; e += NT)
-    vone[e] = __builtin_bit_cast(uint16_t, _Float16(a.cbv[e]));
+  for (int e = tid; e < VE * VE; e += NT)
+    vpair[e] = dev::pack_f16x2(a.cbv[e & (VE - 1)], a.cbv[e >> BV]);
 
-  // ---------------- the wave's 16 query rows: R q * scale * log2(e), fp16.
-  // A first pass finds the largest element of the wave's rows (q' and q''),
-  // the second stores them scaled by one power of two 2^-qe that puts it
-  // near 2^10 (no fp16 overflow or subnormals); the scores undo it in fp32.
+  // ---------------- the wave's 16 RB query rows: R q * scale * log2(e),
+  // fp16. A first pass finds the largest element of the workgroup's rows
+  // (q' and q''); the second stores them scaled by one power of two 2^-qe
+  // that puts it near 2^10 (no fp16 overflow or subnormals). The key scales
+  // carry 2^qe back in fp32.
   _Float16* qst = reinterpret_cast<_Float16*>(smem);
   int qe = 0;
   {
@@ -183,6 +194,10 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
       }
     }
     vmax = dev::wave_max(vmax);
+    if (lane == 0) wmax[wave] = vmax;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < W; ++w) vmax = fmaxf(vmax, wmax[w]);
     qe = vmax > 0.f ? ilogbf(vmax) - 10 : 0;
 #pragma unroll 1
     for (int pass = 0; pass < 4 * RB; ++pass) {
@@ -217,58 +232,74 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
   const int64_t p_min = pos0 + r0 / a.G;  // tiles wholly at or before it need no mask
   const int ntiles = int(p_max / TT) + 1;
 
-  // ---------------- dequant role: lane = token of the tile, wave = quarter
-  // of the coordinates (of the keys, the values, or both)
+  // ---------------- dequant roles. Keys: lane = token of the tile, wave =
+  // quarter of the coordinates. Values: value lane vl (0 .. 255 over the
+  // value waves) takes tokens 4 vq .. 4 vq + 3 and the coordinate octets
+  // vo, vo + 16, ... Tokens past the context load the last token's record
+  // (in bounds; every score they enter is masked).
   const int dt = lane;
   const int dpart = W == 8 ? (wave & 3) : wave;
   const bool do_k = W == 4 || wave < 4;
   const bool do_v = W == 4 || wave >= 4;     // wave-uniform
   constexpr int SWD = QJL ? CPT / 32 : 1;   // QJL sign words per dequant lane
-  uint32_t kw[KWD], vw[VWD], sw[SWD];
-  uint32_t knb = 0, vnb = 0, rnb = 0;
+  constexpr int VO = D / 128;               // value octets per lane
+  constexpr int VXW = BV == 3 ? 2 : 1;      // code dwords per (octet, token)
+  const int vl = (wave & 3) * 64 + lane;
+  const int vq = vl & 15, vo = vl >> 4;
+  const int last = int(a.n_ctx - 1);
+  const uint8_t* kbase = a.kc + rec0 * KREC + dpart * KWD * 4;
+  const uint8_t* vbase = a.vc + rec0 * VREC;
+  uint32_t kw[KWD], sw[SWD], vx[VO][4][VXW];
+  uint32_t knb = 0, rnb = 0, vnb[4];
+  auto norm_at = [&](const void* np, int t) -> uint32_t {
+    return a.norm_f16 ? uint32_t(static_cast<const uint16_t*>(np)[rec0 + t])
+                      : static_cast<const uint32_t*>(np)[rec0 + t];
+  };
   auto fetch = [&](int n) {
-    const int64_t tok = int64_t(n) * TT + dt;
-    const bool ok = tok < a.n_ctx;
-#pragma unroll
-    for (int j = 0; j < KWD; ++j) kw[j] = 0u;
-#pragma unroll
-    for (int j = 0; j < VWD; ++j) vw[j] = 0u;
-#pragma unroll
-    for (int j = 0; j < SWD; ++j) sw[j] = 0u;
-    knb = vnb = rnb = 0u;
-    if (!ok) return;                     // rows past the context are never read
     if (do_k) {
-      const uint32_t* kp =
-          reinterpret_cast<const uint32_t*>(a.kc + (rec0 + tok) * KREC) + dpart * KWD;
+      const int t = min(n * TT + dt, last);
+      const uint32_t* kp = reinterpret_cast<const uint32_t*>(kbase + int64_t(t) * KREC);
 #pragma unroll
       for (int j = 0; j < KWD; ++j) kw[j] = kp[j];
-      if (dpart == 0)
-        knb = a.norm_f16 ? uint32_t(static_cast<const uint16_t*>(a.kn)[rec0 + tok])
-                         : static_cast<const uint32_t*>(a.kn)[rec0 + tok];
+      if (dpart == 0) knb = norm_at(a.kn, t);
       if constexpr (QJL) {
-        const uint32_t* sp = a.kq + (rec0 + tok) * (D / 32) + dpart * SWD;
+        const uint32_t* sp = a.kq + (rec0 + t) * (D / 32) + dpart * SWD;
 #pragma unroll
         for (int j = 0; j < SWD; ++j) sw[j] = sp[j];
-        if (dpart == 0) rnb = a.kr[rec0 + tok];
+        if (dpart == 0) rnb = a.kr[rec0 + t];
       }
     }
     if (do_v) {
-      const uint32_t* vp =
-          reinterpret_cast<const uint32_t*>(a.vc + (rec0 + tok) * VREC) + dpart * VWD;
 #pragma unroll
-      for (int j = 0; j < VWD; ++j) vw[j] = vp[j];
-      if (dpart == 0)
-        vnb = a.norm_f16 ? uint32_t(static_cast<const uint16_t*>(a.vn)[rec0 + tok])
-                         : static_cast<const uint32_t*>(a.vn)[rec0 + tok];
+      for (int u = 0; u < 4; ++u) {
+        const int t = min(n * TT + 4 * vq + u, last);
+        const uint32_t* rp = reinterpret_cast<const uint32_t*>(vbase + int64_t(t) * VREC);
+#pragma unroll
+        for (int o = 0; o < VO; ++o) {
+          const int oct = vo + 16 * o;
+          if constexpr (BV == 3) {
+            // bits 24 oct .. 24 oct + 23: dword i, and i + 1 when they
+            // straddle (i + 1 stays inside the record then)
+            const int i = (3 * oct) >> 2;
+            vx[o][u][0] = rp[i];
+            vx[o][u][1] = rp[i + 1 < VREC / 4 ? i + 1 : i];
+          } else {
+            vx[o][u][0] = rp[BV == 4 ? oct : oct >> 1];
+          }
+        }
+        vnb[u] = norm_at(a.vn, t);
+      }
     }
   };
 
   float m_run[RB], l_run[RB];
-  int vexp = 0;                         // value norms carry 2^-vexp (below)
+  int vexp = 0;                         // accumulators carry 2^-vexp (value tiles)
+  int vexp_d = 0;                       // the value waves' running choice of it
+  float vmul = a.vscale;                // vscale * 2^-vexp_d
   pf_f4 o[RB][NS];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -1e30f;
+    m_run[rb] = 0.f;                    // set by the first tile
     l_run[rb] = 0.f;
 #pragma unroll
     for (int j = 0; j < NS; ++j) o[rb][j] = pf_f4{0.f, 0.f, 0.f, 0.f};
@@ -285,7 +316,8 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
       for (int c = 0; c < CPT / 8; ++c)
         kd[c] = make_uint4(pk[4 * c], pk[4 * c + 1], pk[4 * c + 2], pk[4 * c + 3]);
       if (dpart == 0)
-        tks[buf][dt] = (a.norm_f16 ? dev::f16_to_f32(knb) : __uint_as_float(knb)) * a.kscale;
+        tks[buf][dt] =
+            (a.norm_f16 ? dev::f16_to_f32(knb) : __uint_as_float(knb)) * (a.kscale * qsc);
       if constexpr (QJL) {
         // sign bit set -> -1: the fp16 pair 0x3C00 | bit << 15 per coordinate
         uint32_t ps[CPT / 2];
@@ -298,17 +330,79 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
 #pragma unroll
         for (int c = 0; c < CPT / 8; ++c)
           sd[c] = make_uint4(ps[4 * c], ps[4 * c + 1], ps[4 * c + 2], ps[4 * c + 3]);
-        if (dpart == 0) trho[buf][dt] = dev::f16_to_f32(rnb) * a.qjl_c;
+        if (dpart == 0) trho[buf][dt] = dev::f16_to_f32(rnb) * (a.qjl_c * qsc);
       }
     }
     if (do_v) {
-      uint16_t* vt = reinterpret_cast<uint16_t*>(vtile(buf));
-      const int vcol = (dt & 32) | ((dt >> 2) & 3) << 3 | ((dt >> 4) & 1) << 2 | (dt & 3);
+      // Values enter the tile times their norm: nv * vscale * 2^-vexp_d,
+      // with one power of two per tile that keeps the tile's largest norm
+      // within [2^-6, 2^6] (moved only when a tile leaves that band: a norm
+      // above it, or all below). Every value wave holds all 64 tokens, so
+      // each takes the same decision.
+      float ns[4];
+      bool above = false, inside = false;
 #pragma unroll
-      for (int c = 0; c < CPT; ++c)
-        vt[(dpart * CPT + c) * VS + vcol] = vone[dev::field<BV>(vw, c)];
-      if (dpart == 0)
-        tnv[buf][dt] = (a.norm_f16 ? dev::f16_to_f32(vnb) : __uint_as_float(vnb)) * a.vscale;
+      for (int u = 0; u < 4; ++u) {
+        const float nv = a.norm_f16 ? dev::f16_to_f32(vnb[u]) : __uint_as_float(vnb[u]);
+        ns[u] = nv * vmul;
+        above |= ns[u] > 64.f;
+        inside |= ns[u] >= 0.015625f;
+      }
+      if (__ballot(above) || !__ballot(inside)) {     // wave-uniform, rare
+        float mx = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mx = fmaxf(mx, ldexpf(ns[u], vexp_d));
+        mx = dev::dpp_wave_max(mx);
+        if (mx > 0.f) {
+          const int nexp = ilogbf(mx) - 4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ns[u] = ldexpf(ns[u], vexp_d - nexp);
+          vexp_d = nexp;
+          vmul = ldexpf(a.vscale, -vexp_d);
+        }
+      }
+      if (vl == 0) texp[buf] = vexp_d;
+      const dev::half2_t sc01 = {_Float16(ns[0]), _Float16(ns[1])};
+      const dev::half2_t sc23 = {_Float16(ns[2]), _Float16(ns[3])};
+      // token t sits at column vcol(t); the quad's 4 tokens are adjacent
+      const int t0 = 4 * vq;
+      const int vcol = (t0 & 32) | ((t0 >> 2) & 3) << 3 | ((t0 >> 4) & 1) << 2;
+      // even coordinates 2j: group j (2 BV bits) of ze holds the codes of
+      // the pair's two tokens as one index; odd ones in zo
+      constexpr uint32_t M = BV == 4 ? 0x0F0F0F0Fu : BV == 3 ? 0x71C71C7u : 0x33333333u;
+      const char* vpb = reinterpret_cast<const char*>(vpair);
+#pragma unroll
+      for (int o = 0; o < VO; ++o) {
+        const int oct = vo + 16 * o;
+        uint32_t x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          x[u] = BV == 3   ? __builtin_amdgcn_alignbit(vx[o][u][1], vx[o][u][0],
+                                                       uint32_t(8 * ((3 * oct) & 3)))
+                 : BV == 2 ? vx[o][u][0] >> (16 * (oct & 1))
+                           : vx[o][u][0];
+        uint32_t pv[2][8];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint32_t ze[1] = {(x[2 * p] & M) | ((x[2 * p + 1] << BV) & ~M)};
+          const uint32_t zo[1] = {((x[2 * p] >> BV) & M) | (x[2 * p + 1] & ~M)};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            pv[p][2 * j] = *reinterpret_cast<const uint32_t*>(
+                vpb + dev::bits_at<2 * BV, 2>(ze, 2 * BV * j));
+            pv[p][2 * j + 1] = *reinterpret_cast<const uint32_t*>(
+                vpb + dev::bits_at<2 * BV, 2>(zo, 2 * BV * j));
+          }
+        }
+        uint2* vt = reinterpret_cast<uint2*>(vtile(buf) + 8 * oct * VS + vcol);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const dev::half2_t v01 = __builtin_bit_cast(dev::half2_t, pv[0][k]) * sc01;
+          const dev::half2_t v23 = __builtin_bit_cast(dev::half2_t, pv[1][k]) * sc23;
+          vt[k * (VS / 4)] =
+              make_uint2(__builtin_bit_cast(uint32_t, v01), __builtin_bit_cast(uint32_t, v23));
+        }
+      }
     }
   };
 
@@ -329,8 +423,9 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
     const _Float16* vtl = vtile(buf);
     const _Float16* stl = stile(buf);
 
-    // ---------------- scores S^T (tokens x rows), scaled (exp2 units) and
-    // masked on the tiles that reach past the workgroup's lowest row position
+    // ---------------- scores S^T (tokens x rows) in exp2 units, less the
+    // running max: t = ks_t * S (+ rho_t * S_qjl) - m, masked on the tiles
+    // that reach past the workgroup's lowest row position
     const bool masked = int64_t(n) * TT + TT - 1 > p_min;   // workgroup-uniform
     float sc[RB][4][4];
 #pragma unroll
@@ -357,19 +452,19 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
         }
       }
       const float4 ks = *reinterpret_cast<const float4*>(&tks[buf][16 * tb + 4 * kq]);
-      const float kss[4] = {ks.x * qsc, ks.y * qsc, ks.z * qsc, ks.w * qsc};
+      const float kss[4] = {ks.x, ks.y, ks.z, ks.w};
       float rhs[4] = {0.f, 0.f, 0.f, 0.f};
       if constexpr (QJL) {
         const float4 rh = *reinterpret_cast<const float4*>(&trho[buf][16 * tb + 4 * kq]);
-        rhs[0] = rh.x * qsc; rhs[1] = rh.y * qsc; rhs[2] = rh.z * qsc; rhs[3] = rh.w * qsc;
+        rhs[0] = rh.x; rhs[1] = rh.y; rhs[2] = rh.z; rhs[3] = rh.w;
       }
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float v = acc[rb][i] * kss[i];
-          if constexpr (QJL) v = fmaf(acq[rb][i], rhs[i], v);
-          sc[rb][tb][i] = v;
+          float t = fmaf(acc[rb][i], kss[i], -m_run[rb]);
+          if constexpr (QJL) t = fmaf(acq[rb][i], rhs[i], t);
+          sc[rb][tb][i] = t;
         }
     }
     if (masked) {
@@ -384,31 +479,25 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
           }
     }
     // The running max (per row, the same on its 4 lanes) is raised only when
-    // a score exceeds it by more than 2^8 (weights stay <= 2^8, which with
-    // the value-norm band below keeps the fp16 operands finite): then the
-    // tile's row maxima are taken and the accumulators rescaled. The branch
-    // is wave-uniform; it always runs on the first tile (m_run = -1e30, so
-    // alpha = 0), and a row masked on every token keeps m_run and weight 0.
-    pf_h8 pa[RB][2];
+    // a score exceeds it by more than 2^8, so the weights stay <= 2^8; then
+    // the tile's row maxima are taken and the accumulators rescaled. The
+    // branch is wave-uniform. The first tile always takes it and sets the
+    // max (token 0 is visible to every row; rows past the chunk, masked
+    // everywhere, get a finite max and weight 0).
+    const bool first = n == 0;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float lim = m_run[rb] + 8.f;
-      bool up = false;
+      float tm = sc[rb][0][0];
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) up |= sc[rb][tb][i] > lim;
-      if (__ballot(up)) {
-        float mt = -INFINITY;
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mt = fmaxf(mt, sc[rb][tb][i]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        const float m_new = fmaxf(m_run[rb], mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - m_new);
-        m_run[rb] = m_new;
+        for (int i = 0; i < 4; ++i) tm = fmaxf(tm, sc[rb][tb][i]);
+      if (__ballot(first || tm > 8.f)) {
+        tm = fmaxf(tm, __shfl_xor(tm, 16));
+        tm = fmaxf(tm, __shfl_xor(tm, 32));
+        const float delta = fmaxf(tm, first ? -3.0e38f : 0.f);
+        const float alpha = first ? 1.f : __builtin_amdgcn_exp2f(-delta);
+        m_run[rb] += delta;
         l_run[rb] *= alpha;
         float al[4];
 #pragma unroll
@@ -417,58 +506,44 @@ __global__ void __launch_bounds__(64 * pf_waves(D)) k_prefill(PrefillArgs a) {
         for (int j = 0; j < NS; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) o[rb][j][i] *= al[i];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[rb][tb][i] -= delta;
       }
     }
-    float ls[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) ls[rb] = 0.f;
-    // the weights p * nv (p <= 1) go to fp16: nv carries a workgroup-uniform
-    // power of two 2^-vexp that keeps the tile's largest value norm within
-    // [2^-6, 2^6], moved (with the accumulators) only when a tile leaves it
-    float nvt[4][4];
-    float nvmax = 0.f;
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const float4 nv = *reinterpret_cast<const float4*>(&tnv[buf][16 * tb + 4 * kq]);
-      nvt[tb][0] = ldexpf(nv.x, -vexp);
-      nvt[tb][1] = ldexpf(nv.y, -vexp);
-      nvt[tb][2] = ldexpf(nv.z, -vexp);
-      nvt[tb][3] = ldexpf(nv.w, -vexp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) nvmax = fmaxf(nvmax, nvt[tb][i]);
-    }
-    nvmax = fmaxf(nvmax, __shfl_xor(nvmax, 16));
-    nvmax = fmaxf(nvmax, __shfl_xor(nvmax, 32));
-    if (nvmax > 64.f || (nvmax > 0.f && nvmax < 0.015625f)) {   // uniform, rare
-      const int sh = ilogbf(nvmax) - 4;
-      vexp += sh;
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) nvt[tb][i] = ldexpf(nvt[tb][i], -sh);
+    // the value tile's power of two (the same on every lane)
+    const int te = texp[buf];
+    if (te != vexp) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int j = 0; j < NS; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[rb][j][i] = ldexpf(o[rb][j][i], -sh);
+          for (int i = 0; i < 4; ++i) o[rb][j][i] = ldexpf(o[rb][j][i], vexp - te);
+      vexp = te;
     }
+    // weights p = 2^t as fp16 (p <= 2^8); the row sums add the same fp16
+    // weights (2 per dot), the lane's 16 tokens here and its 4 lanes once
+    // after the loop
+    pf_h8 pa[RB][2];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-      const float (&nvs)[4] = nvt[tb];
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(sc[rb][tb][i] - m_run[rb]);
-          ls[rb] += p;
-          pa[rb][tb >> 1][4 * (tb & 1) + i] = _Float16(p * nvs[i]);
-        }
-    }
-    // the lane's partial row sums (its 16 tokens); the 4 lanes of a row are
-    // added once, after the loop
+        for (int i = 0; i < 4; ++i)
+          pa[rb][tb >> 1][4 * (tb & 1) + i] = _Float16(__builtin_amdgcn_exp2f(sc[rb][tb][i]));
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) l_run[rb] += ls[rb];
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 w4 = __builtin_bit_cast(uint4, pa[rb][h]);
+        l_run[rb] = dev::dot2(w4.x, 0x3C003C00u, l_run[rb]);
+        l_run[rb] = dev::dot2(w4.y, 0x3C003C00u, l_run[rb]);
+        l_run[rb] = dev::dot2(w4.z, 0x3C003C00u, l_run[rb]);
+        l_run[rb] = dev::dot2(w4.w, 0x3C003C00u, l_run[rb]);
+      }
 
     // ---------------- O += P V_hat (rows 4kq + i of each block)
 #pragma unroll
