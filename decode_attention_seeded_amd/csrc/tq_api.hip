@@ -498,6 +498,7 @@ int tq_attend_prefill(const tq_config* cfg, const void* q, int q_dtype, int B, i
   if (!std::isfinite(scale)) return TQ_ERR_ARG;
   if (n_q < 1 || n_ctx < n_q) return TQ_ERR_ARG;
   if (n_ctx > cache->capacity) return TQ_ERR_CAPACITY;
+  if (n_ctx > INT32_MAX) return TQ_ERR_UNSUPPORTED;   // token positions are 32-bit
   const int G = Hq / cache->Hkv;
   const int64_t rows = pf_rows(cfg->d, cfg->qjl != 0);
   const int64_t tiles = (n_q * G + rows - 1) / rows;

@@ -132,13 +132,20 @@ int tq_codebook(int bits, double* centroids, double* thresholds);
  * up to about a second) and cached for the life of the process. */
 int tq_codebook_ex(int bits, int kind, int d, double* centroids, double* thresholds);
 
-/* The +-1 rotation signs for (seed, d) as int8 (host array of d). Host only. */
+/* The +-1 rotation signs for (seed, d) as int8 (host array of d): the random
+ * diagonal of the deterministic rotation (API page, "What is TurboQuant?":
+ * a seeded random rotation before the codebook; README: randomized
+ * Hadamard). Host only. TQ_ERR_ARG for a NULL out or d < 1. */
 int tq_signs(uint64_t seed, int d, int8_t* out);
 
 /*
  * Bytes of each plane of a cache (capacity tokens) written to
- * plane_bytes[6] in the order kc, vc, kn, vn, kq, kr (may be NULL).
- * Returns the total, or a negative tq_status.
+ * plane_bytes[6] in the order kc, vc, kn, vn, kq, kr (may be NULL): the
+ * packed codes at bits_k and bits_v per coordinate plus one norm per row
+ * (performance page, "Aggressive Compression Ratios"), and with QJL one
+ * sign bit per key coordinate plus a residual norm (README, "The 1-bit QJL
+ * residual": +1 bit per channel). Returns the total, or a negative
+ * tq_status.
  */
 int64_t tq_cache_bytes(const tq_config* cfg, int B, int Hkv, int64_t capacity,
                        int64_t* plane_bytes);
@@ -287,7 +294,8 @@ int tq_append_attend_decode(const tq_config* cfg, const void* k_new,
  * Errors (before any work is queued): TQ_ERR_ARG (1 <= n_q <= n_ctx
  * violated, Hq not a multiple of Hkv, B != cache B, null pointers),
  * TQ_ERR_CAPACITY (n_ctx > capacity), TQ_ERR_ALIGN, TQ_ERR_UNSUPPORTED
- * (d, bit widths, codebook or q dtype).
+ * (d, bit widths, codebook or q dtype, or n_ctx above 2^31 - 1: the kernel
+ * holds token positions in 32 bits).
  */
 int tq_attend_prefill(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
                       int64_t n_q, const tq_cache* cache, int64_t n_ctx, float scale,

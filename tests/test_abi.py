@@ -295,6 +295,8 @@ def test_prefill_validation():
     assert call(Hq=3) == tq.TQ_ERR_ARG                    # not a multiple of Hkv
     assert call(B=2) == tq.TQ_ERR_ARG                     # cache holds B = 1
     assert call(n_ctx=65) == tq.TQ_ERR_CAPACITY
+    big = 1 << 31                                        # positions past 32 bits
+    assert call(n_ctx=big, cache=_cache(cap=big)) == tq.TQ_ERR_UNSUPPORTED
     assert call(q=None) == tq.TQ_ERR_ARG
     assert call(q=MIS) == tq.TQ_ERR_ALIGN
     assert call(out=MIS) == tq.TQ_ERR_ALIGN
