@@ -230,7 +230,9 @@ def decode_record(torch, tq, si, w, n_calls, flush, fsink):
     out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
     ws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N))
     dec = lambda: tq.tq_attend_decode(cfg, q, cache, w.N, out, ws)
-    us = timed(torch, dec, n_calls, warm=5)
+    # the inputs are generated on the host for seconds while the GPU idles:
+    # 200 untimed calls (about 20 ms) bring its clocks back before timing
+    us = timed(torch, dec, n_calls, warm=200)
     cold = []
     ev = lambda: torch.cuda.Event(enable_timing=True)
     for _ in range(10):
@@ -620,7 +622,7 @@ def main():
         others = {}
         for wid in (3, 5):
             log(f"workload {wid}: {si.WORKLOADS[wid].name}")
-            rec = decode_record(torch, tq, si, si.WORKLOADS[wid], 50, flush, fsink)
+            rec = decode_record(torch, tq, si, si.WORKLOADS[wid], 100, flush, fsink)
             others[str(wid)] = rec
             log(f"  decode {rec['decode_call_us']} us = {rec['achieved_gbps']} GB/s "
                 f"({rec['frac_of_hbm_peak']} of peak); cold median "
