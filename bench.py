@@ -683,6 +683,11 @@ def main():
             "kernel_trace_avg_us": kernel_us,
             "frac_kernel_trace": (round(alg_bytes / kernel_us / 1e3 / HBM_PEAK_GBPS, 4)
                                   if kernel_us else None),
+            # in the committed traced run: the traced back-to-back calls and
+            # this script's HIP-event time of the same calls
+            "trace_back_to_back_us": trace.get("back_to_back_run_mean_us") if trace else None,
+            "trace_run_launch_us": (trace.get("bench_live_launch_us_in_traced_run")
+                                    if trace else None),
             "frac_of_read_probe": round(achieved / probe_gbps, 4),
         },
         "cpu_baseline": cpu,
