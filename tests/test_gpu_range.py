@@ -18,6 +18,11 @@ is the property that holds at any temperature: a finite output inside the
 per-coordinate range of the dequantized value rows (a convex combination of
 them).
 
+Value norms that change along the context (a ramp over 2^20, a sawtooth of
+2^+-8) make the kernels move their per-tile power of two for the value
+scales, and rescale the accumulators, many times within one call; those
+cases keep the 2e-3 bar.
+
 Inputs are fp32 (so the scaled values reach both sides unrounded); norms are
 fp16 where they fit its range and fp32 for the 1e5 and 1e-6 cases."""
 
@@ -135,3 +140,69 @@ def test_prefill_far_from_unit_scale(fmt, scl):
     want = o.attend_prefill(q.astype(np.float64), ref, w.N, d=w.d, seed=w.seed, bits_k=w.bits_k,
                             bits_v=w.bits_v, Hkv=w.Hkv, qjl=w.qjl, qjl_seed=w.qjl_seed)
     _check(got, want, ref, w, scl)
+
+
+# Value norms that change along the context: the kernels' per-tile power of
+# two for the value scales has to move (a ramp over 2^20: many moves one
+# way; a sawtooth of 2^+-8 with a 37-token period: tiles that mix both and
+# moves both ways), with the accumulators rescaled on every move.
+PROFILES = {
+    "ramp": lambda t, n: np.exp2(-10.0 + 20.0 * t / max(n - 1, 1)),
+    "saw": lambda t, n: np.where((t // 37) % 2 == 0, 2.0 ** 8, 2.0 ** -8),
+}
+
+
+def _profiled_inputs(w, prof, n_q=0):
+    k, v, q = _scaled_inputs(w, 1.0, 1.0, n_q)
+    f = PROFILES[prof](np.arange(w.N), w.N).astype(np.float32)
+    return k, (v * f[None, None, :, None]).astype(np.float32), q
+
+
+@pytest.mark.parametrize("prof", sorted(PROFILES))
+@pytest.mark.parametrize("fmt", ["k3v4", "k3qjl_v4", "d256_k2v2"])
+def test_decode_value_norms_along_the_context(fmt, prof):
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.small_workload(wid=230 + sorted(FORMATS).index(fmt), in_dtype="f32",
+                          norm_dtype="f16", **FORMATS[fmt])
+    log(f"decode {fmt} with value norms along a {prof} profile")
+    k, v, q = _profiled_inputs(w, prof)
+    cfg = config_of(w)
+    cache = tq.PackedCache(cfg, w.B, w.Hkv, w.N)
+    tq.tq_encode_kv(cfg, to_device(k, "f32"), to_device(v, "f32"), 0, cache)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    ws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N))
+    tq.tq_attend_decode(cfg, to_device(q, "f32"), cache, w.N, out, ws)
+    torch.cuda.synchronize()
+    ref = o.encode_kv(k.astype(np.float64), v.astype(np.float64), seed=w.seed, bits_k=w.bits_k,
+                      bits_v=w.bits_v, norm_dtype=w.norm_dtype, qjl=w.qjl, qjl_seed=w.qjl_seed)
+    want = o.attend(q.astype(np.float64), ref, w.N, d=w.d, seed=w.seed, bits_k=w.bits_k,
+                    bits_v=w.bits_v, Hkv=w.Hkv, qjl=w.qjl, qjl_seed=w.qjl_seed)
+    err, abs_err = rel_err(out.cpu().numpy().astype(np.float64), want)
+    log(f"  max row-relative error {err:.2e} (abs {abs_err:.2e})")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("prof", sorted(PROFILES))
+@pytest.mark.parametrize("fmt", ["k3v4", "k3qjl_v4"])
+def test_prefill_value_norms_along_the_context(fmt, prof):
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.small_workload(wid=240 + (fmt == "k3qjl_v4"), in_dtype="f32", norm_dtype="f16",
+                          **FORMATS[fmt])
+    n_q = 130
+    log(f"prefill {fmt} with value norms along a {prof} profile")
+    k, v, q = _profiled_inputs(w, prof, n_q)
+    cfg = config_of(w)
+    cache = tq.PackedCache(cfg, w.B, w.Hkv, w.N)
+    tq.tq_encode_kv(cfg, to_device(k, "f32"), to_device(v, "f32"), 0, cache)
+    out = torch.empty((w.B, w.Hq, n_q, w.d), dtype=torch.float32, device="cuda")
+    tq.tq_attend_prefill(cfg, to_device(q, "f32"), cache, w.N, out)
+    torch.cuda.synchronize()
+    ref = o.encode_kv(k.astype(np.float64), v.astype(np.float64), seed=w.seed, bits_k=w.bits_k,
+                      bits_v=w.bits_v, norm_dtype=w.norm_dtype, qjl=w.qjl, qjl_seed=w.qjl_seed)
+    want = o.attend_prefill(q.astype(np.float64), ref, w.N, d=w.d, seed=w.seed, bits_k=w.bits_k,
+                            bits_v=w.bits_v, Hkv=w.Hkv, qjl=w.qjl, qjl_seed=w.qjl_seed)
+    err, abs_err = rel_err(out.cpu().numpy().astype(np.float64), want)
+    log(f"  max row-relative error {err:.2e} (abs {abs_err:.2e})")
+    assert err <= TOL
