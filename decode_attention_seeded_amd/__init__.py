@@ -3,6 +3,7 @@
 The work happens in libtq.so (hand-written HIP, C ABI in include/tq.h); this
 package is its thin ctypes binding. See binding.py for the entry points:
 tq_rht, tq_encode_kv, tq_qjl_sketch, tq_attend_decode, tq_append_attend_decode,
+tq_append_chunk_attend_decode,
 tq_attend_decode_noalloc (no workspace: a static per-GPU scratch buffer),
 tq_attend_prefill, the group-affine variant tq_affine_encode_kv /
 tq_affine_attend_decode (+ host helpers).
@@ -12,6 +13,7 @@ from .binding import (  # noqa: F401
     EXPORTS, LIB_PATH, TQ_BF16, TQ_ERR_ALIGN, TQ_ERR_ARG, TQ_ERR_CAPACITY,
     TQ_ERR_HIP, TQ_ERR_NO_DEVICE, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_F16,
     TQ_F32, TQ_OK, Config, PackedCache, TqError, lib, tq_append_attend_decode,
+    tq_append_chunk_attend_decode,
     tq_attend_decode, tq_attend_decode_noalloc, tq_attend_prefill,
     tq_bits_split, tq_cache_bytes, tq_codebook, tq_codebook_ex, tq_config, tq_cache,
     TQ_CODEBOOK_GAUSS, TQ_CODEBOOK_SPHERE,

@@ -32,7 +32,7 @@ EXPORTS = (
     "tq_bits_split", "tq_codebook", "tq_codebook_ex", "tq_signs", "tq_cache_bytes", "tq_rht",
     "tq_encode_kv", "tq_qjl_sketch", "tq_num_splits", "tq_workspace_bytes",
     "tq_attend_decode", "tq_attend_decode_noalloc", "tq_append_attend_decode",
-    "tq_dense_workspace_bytes",
+    "tq_append_chunk_attend_decode", "tq_dense_workspace_bytes",
     "tq_dense_decode_bf16", "tq_attend_prefill", "tq_read_probe_sink_words",
     "tq_read_probe", "tq_affine_cache_bytes", "tq_affine_encode_kv", "tq_affine_num_splits",
     "tq_affine_workspace_bytes", "tq_affine_attend_decode",
@@ -101,6 +101,8 @@ def _lib():
             "tq_attend_decode_noalloc": (I, [CFG, P, I, I, I, CACHE, I64, F, I, P, P]),
             "tq_append_attend_decode": (I, [CFG, P, P, I, P, I, I, I, CACHE, I64, F, I, P, P,
                                             SZ, P]),
+            "tq_append_chunk_attend_decode": (I, [CFG, P, P, I, I64, P, I, I, I, CACHE, I64,
+                                                  F, I, P, P, SZ, P]),
             "tq_dense_workspace_bytes": (I64, [I, I, I, I, I64, I]),
             "tq_dense_decode_bf16": (I, [P, P, P, I, I, I, I, I64, F, I, P, P, SZ, P]),
             "tq_attend_prefill": (I, [CFG, P, I, I, I, I64, CACHE, I64, F, P, P]),
@@ -359,6 +361,29 @@ def tq_append_attend_decode(cfg: Config, k_new, v_new, q, cache: PackedCache, n_
         ctypes.byref(cfg.c()), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), _ptr(q),
         _dtype_code(q), B, Hq, ctypes.byref(c), n_ctx, float(scale), splits, _ptr(out), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)), "tq_append_attend_decode")
+
+
+def tq_append_chunk_attend_decode(cfg: Config, k_new, v_new, q, cache: PackedCache, n_ctx: int,
+                                  out, ws, scale: float = 0.0, splits: int = 0, stream=None):
+    """Encode tokens n_ctx - n_new .. n_ctx - 1 from k_new, v_new
+    [B][Hkv][n_new][d], then attend like tq_attend_decode (one launch on the
+    matrix-core decode without QJL)."""
+    B, Hq, d = q.shape
+    if d != cfg.d or not q.is_contiguous() or tuple(out.shape) != (B, Hq, d):
+        raise TqError(TQ_ERR_ARG,
+                      "tq_append_chunk_attend_decode: q/out must be [B][Hq][d] contiguous")
+    n_new = k_new.shape[2] if k_new.dim() == 4 else -1
+    for t in (k_new, v_new):
+        if tuple(t.shape) != (cache.B, cache.Hkv, n_new, d) or not t.is_contiguous():
+            raise TqError(TQ_ERR_ARG, "tq_append_chunk_attend_decode: k_new/v_new must be "
+                                      "contiguous [B][Hkv][n_new][d]")
+    if k_new.dtype != v_new.dtype:
+        raise TqError(TQ_ERR_ARG, "tq_append_chunk_attend_decode: k_new and v_new dtypes differ")
+    c = cache.c()
+    _check(_lib().tq_append_chunk_attend_decode(
+        ctypes.byref(cfg.c()), _ptr(k_new), _ptr(v_new), _dtype_code(k_new), n_new, _ptr(q),
+        _dtype_code(q), B, Hq, ctypes.byref(c), n_ctx, float(scale), splits, _ptr(out), _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(stream)), "tq_append_chunk_attend_decode")
 
 
 def tq_attend_prefill(cfg: Config, q, cache: PackedCache, n_ctx: int, out, scale: float = 0.0,

@@ -196,7 +196,7 @@ int run_decode(int d, int bk, int bv, int qjl, const DecodePlan& p, DecodeArgs d
 // matrix-core kernel runs, else one encode launch before it).
 int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
            const tq_cache* cache, int64_t n_ctx, float scale, int splits, float* out, void* ws,
-           size_t ws_bytes, hipStream_t stream, const EncodeArgs* app) {
+           size_t ws_bytes, hipStream_t stream, const EncodeArgs* app, bool chunk = false) {
   int st = check_config(cfg);
   if (st != TQ_OK) return st;
   st = check_cache(cfg, cache);
@@ -261,6 +261,15 @@ int attend(const tq_config* cfg, const void* q, int q_dtype, int B, int Hq,
   if (app) {
     da.append = 1;
     da.enc = *app;
+    if (chunk) {
+      // every split decodes a share of the old tokens (a multiple of 64)
+      // and of the appended ones, whose rows it encodes first
+      da.append = 2;
+      da.n_old = n_ctx - app->n_new;
+      const int64_t S = p.splits;
+      da.tpo = ((da.n_old + S - 1) / S + 63) / 64 * 64;
+      da.tpn = (app->n_new + S - 1) / S;
+    }
   }
   return run_decode(cfg->d, cfg->bits_k, cfg->bits_v, cfg->qjl, p, da, qa, B, Hq, cache->Hkv,
                     ws, out, cfg->seed, stream);
@@ -449,6 +458,28 @@ int tq_append_attend_decode(const tq_config* cfg, const void* k_new, const void*
   fill_encode_args(cfg, k_new, v_new, in_dtype, n_ctx - 1, 1, cache, &e);
   return attend(cfg, q, q_dtype, B, Hq, cache, n_ctx, scale, splits, out, ws, ws_bytes, stream,
                 &e);
+}
+
+int tq_append_chunk_attend_decode(const tq_config* cfg, const void* k_new, const void* v_new,
+                                  int in_dtype, int64_t n_new, const void* q, int q_dtype, int B,
+                                  int Hq, const tq_cache* cache, int64_t n_ctx, float scale,
+                                  int splits, float* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  int st = check_config(cfg);
+  if (st != TQ_OK) return st;
+  st = check_cache(cfg, cache);
+  if (st != TQ_OK) return st;
+  if (!valid_in_dtype(in_dtype)) return TQ_ERR_UNSUPPORTED;
+  if (n_ctx < 1 || n_new < 1 || n_new > n_ctx) return TQ_ERR_ARG;
+  if (n_ctx > cache->capacity) return TQ_ERR_CAPACITY;
+  if (B != cache->B) return TQ_ERR_ARG;
+  if (B == 0) return TQ_OK;
+  if (!k_new || !v_new) return TQ_ERR_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return TQ_ERR_ALIGN;
+  EncodeArgs e{};
+  fill_encode_args(cfg, k_new, v_new, in_dtype, n_ctx - n_new, n_new, cache, &e);
+  return attend(cfg, q, q_dtype, B, Hq, cache, n_ctx, scale, splits, out, ws, ws_bytes, stream,
+                &e, true);
 }
 
 int tq_dense_decode_bf16(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,

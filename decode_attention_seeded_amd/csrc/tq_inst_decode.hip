@@ -27,6 +27,17 @@ static int go(int mx, const DecodeArgs& a, dim3 grid, hipStream_t st) {
 #else
   if (mx) {
     const dim3 block(64 * mx_waves(TQ_D));
+    if constexpr (!QJL) {
+      if (a.append == 2) {              // chunked append: its own instantiation
+        if (a.norm_f16)
+          hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, false, true, true>), grid, block,
+                             0, st, a);
+        else
+          hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, false, false, true>), grid,
+                             block, 0, st, a);
+        return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+      }
+    }
     if (a.norm_f16)
       hipLaunchKernelGGL((k_decode_mx<TQ_D, TQ_BK, BV, GK, QJL, true>), grid, block, 0, st, a);
     else

@@ -87,8 +87,13 @@ struct DecodeArgs {
   float qmult;            // scale * log2(e)
   uint32_t sbits[8];      // rotation signs, bit i set when sign i is negative
   uint32_t qsbits[8];     // QJL rotation signs, same layout
-  int append;             // 1: the last split first encodes token n_ctx - 1 (enc)
-  EncodeArgs enc;         // that token's K/V rows and the cache planes
+  int append;             // 1: the last split first encodes token n_ctx - 1 (enc);
+                          // 2: every split first encodes its share of the
+                          //    enc.n_new appended tokens (below)
+  EncodeArgs enc;         // the appended K/V rows and the cache planes
+  // append == 2: split s reads old tokens [s tpo, s tpo + tpo) (tpo a multiple
+  // of 64) below n_old, then new tokens [n_old + s tpn, n_old + s tpn + tpn)
+  int64_t n_old, tpo, tpn;
   uint32_t* cnt;          // [grid.y] arrival counters (zero between calls)
   float* out;             // [B*Hq][D] output of kernels that merge their splits
 };
@@ -396,6 +401,33 @@ __device__ __forceinline__ void encode_append_row(const EncodeArgs& e, int bh, i
     encode_row<D, BK, false, 0, IW>(e, bh, 0, true, el, u, ss);
   else
     encode_row<D, BV, false, 1, IW>(e, bh, 0, true, el, u, ss);
+}
+
+// Encodes rows [t0, t0 + n) of the appended tokens in `e`, K and V, for row
+// bh: work items of 64/P rows (one wave each, as in k_encode) taken in turn
+// by the nwaves waves of the workgroup.
+template <int D, int BK, int BV, int DT>
+__device__ __forceinline__ void encode_chunk_rows(const EncodeArgs& e, int bh, int64_t t0,
+                                                  int64_t n, int wave, int nwaves, int lane) {
+  constexpr int IW = DT == 0 ? 4 : 2;
+  constexpr int P = D / 32;
+  constexpr int RPW = 64 / P;
+  const int groups = int((n + RPW - 1) / RPW);
+  if (groups <= 0) return;
+  const EncodeLane<IW> el = make_encode_lane<IW, false>(e, lane & (P - 1));
+  const int rl = lane / P;
+  for (int it = wave; it < 2 * groups; it += nwaves) {
+    const int z = it >= groups ? 1 : 0;
+    const int64_t r = int64_t(it - z * groups) * RPW + rl;
+    RowWords<IW> rw;
+    load_words<D, IW>(e, z, bh, t0 + r, el.lp, rw);
+    double u[32];
+    const double ss = words_to_f64<DT>(rw, el, u);
+    if (z == 0)
+      encode_row<D, BK, false, 0, IW>(e, bh, t0 + r, r < n, el, u, ss);
+    else
+      encode_row<D, BV, false, 1, IW>(e, bh, t0 + r, r < n, el, u, ss);
+  }
 }
 
 // Persistent encode of K and V: a work item is 64/P consecutive rows (one
@@ -1228,6 +1260,11 @@ k_decode_pk(DecodeArgs a, const uint32_t* __restrict__ qp2_all,
 //   QJL     the sign dot sum_i q''_i sigma_i is a second chain of the same
 //           4x4x4 blocks: B = the key's 4 signs of quad j as fp16 +-1 (one
 //           8-byte lookup of a 16-entry table), A = the quad of R_2 q'.
+// CHUNK: the instantiation for a chunked append (formats without QJL): each
+// workgroup first encodes its split's share of the appended tokens (all 8
+// waves, k_encode's row layout), then decodes its older tokens followed by
+// those new ones; a separate instantiation so that the encode's registers
+// do not weigh on the plain decode.
 // ---------------------------------------------------------------------------
 
 typedef _Float16 mx_h4 __attribute__((ext_vector_type(4)));
@@ -1257,13 +1294,14 @@ constexpr int mx_prefetch(int d, int bk, int bv, bool qjl) {
   return d == 128 && bk < 4 && bv != 3 ? 2 + 0 * qjl : 1;
 }
 
-template <int D, int BK, int BV, int GK, bool QJL, bool NF16>
+template <int D, int BK, int BV, int GK, bool QJL, bool NF16, bool CHUNK = false>
 __global__ void __launch_bounds__(64 * mx_waves(D))
     __attribute__((amdgpu_waves_per_eu(mx_waves(D) / 4)))
 k_decode_mx(DecodeArgs a) {
   static_assert(D == 128 || D == 256, "matrix-core decode: d 128 or 256");
   static_assert(BV >= 2 && BV <= 4, "matrix-core decode: 2- to 4-bit values");
   static_assert(GK == 1 || GK == 2 || GK == 4, "heads per workgroup");
+  static_assert(!(CHUNK && QJL), "chunked append: formats without QJL");
   constexpr int W = mx_waves(D);
   constexpr int TW = 64;                       // tokens per wave tile
   constexpr int T = W * TW;                    // tokens per workgroup round
@@ -1331,16 +1369,59 @@ k_decode_mx(DecodeArgs a) {
   const int h0 = kvh * a.G + chunk * GK;
   const int64_t head0 = int64_t(b) * a.Hq + h0;
 
-  const int64_t t_begin = int64_t(split) * a.tps;
-  const int64_t t_end = min(a.n_ctx, t_begin + a.tps);
+  // The split's tokens as positions [0, t_end): its old tokens [0, vlo)
+  // are cache rows obeg + v; with a chunked append (append == 2) its new
+  // tokens follow from the next 64-token boundary vpad, as rows
+  // nbeg + v - vpad (no wave tile holds both).
+  int64_t obeg, vlo, vpad, nbeg, t_end;
+  if (CHUNK) {
+    obeg = int64_t(split) * a.tpo;
+    vlo = max(int64_t(0), min(a.tpo, a.n_old - obeg));
+    vpad = (vlo + TW - 1) / TW * TW;
+    nbeg = a.n_old + int64_t(split) * a.tpn;
+    t_end = vpad + max(int64_t(0), min(a.tpn, a.n_ctx - nbeg));
+  } else {
+    obeg = int64_t(split) * a.tps;
+    vlo = max(int64_t(0), min(a.n_ctx, obeg + a.tps) - obeg);
+    vpad = vlo;
+    nbeg = 0;
+    t_end = vlo;
+  }
+  const int64_t t_begin = 0;
   const int64_t row0 = int64_t(bkv) * a.capacity;
   constexpr int nb = NF16 ? 2 : 4;
   const int iters = int((t_end - t_begin + T - 1) / T);
 
+  // the end of the range the wave tile at position `base` belongs to, and
+  // the cache row of that position (base is wave-uniform)
+  auto vend = [&](int64_t base) -> int64_t {
+    if constexpr (CHUNK) return base < vpad ? vlo : t_end;
+    return t_end;
+  };
+  auto phys = [&](int64_t base) -> int64_t {
+    if constexpr (CHUNK) return base < vpad ? obeg + base : nbeg + (base - vpad);
+    return obeg + base;
+  };
   auto rows_left = [&](int64_t base) -> uint32_t {
-    const int64_t n = t_end - base;
+    const int64_t n = vend(base) - base;
     return uint32_t(n <= 0 ? 0 : (n < TW ? n : TW));
   };
+  // chunked append: every workgroup first encodes its split's new rows
+  // (rows nbeg .. of the cache, t_end - vpad of them) with all its waves,
+  // before anything else is live. Only its own waves read them, so the
+  // workgroup-scope release and acquire of the barrier after the tables make
+  // the stores visible to their loads (no device-wide fence, which would
+  // write back and invalidate the L2). Other head chunks of the same KV head
+  // write the same bytes.
+  if constexpr (CHUNK) {
+    const int64_t t0 = nbeg - a.n_old, n = t_end - vpad;
+    if (a.enc.in_dtype == 0)
+      encode_chunk_rows<D, BK, BV, 0>(a.enc, bkv, t0, n, wave, W, lane);
+    else if (a.enc.in_dtype == 1)
+      encode_chunk_rows<D, BK, BV, 1>(a.enc, bkv, t0, n, wave, W, lane);
+    else
+      encode_chunk_rows<D, BK, BV, 2>(a.enc, bkv, t0, n, wave, W, lane);
+  }
   const uint32_t ko0 = uint32_t(lane) * KREC;
   const uint32_t no0 = uint32_t(lane) * nb;
   // value slice i of a lane is token 16 (i / 4) + 4 (i % 4) + kq, so one load
@@ -1356,8 +1437,9 @@ k_decode_mx(DecodeArgs a) {
   // overlapping windows of 48-byte rows are not whole lines: normal policy
   constexpr int kValNT = V3 ? 0 : kNT;
   constexpr int kSignNT = D / 8 == 16 ? kNT : 0;   // sign rows of 16 B: whole lines
-  auto load = [&](int64_t base, Tile& t) {
-    const uint32_t n = rows_left(base);
+  auto load = [&](int64_t vbase, Tile& t) {
+    const uint32_t n = rows_left(vbase);
+    const int64_t base = phys(vbase);
     const auto rk = dev::buffer_rsrc(a.kc + (row0 + base) * KREC, n * KREC);
 #pragma unroll
     for (int k = 0; k < KW / 4; ++k) {
@@ -1549,7 +1631,7 @@ k_decode_mx(DecodeArgs a) {
   // the cache first; the barrier below makes the stores visible to its
   // waves' loads. Other head chunks of the same KV head write the same bytes.
   // (Formats with the QJL sketch encode the token in a launch of its own.)
-  if (!QJL && a.append && split == a.S - 1 && wave == 0 && lane < D / 16) {
+  if (!QJL && !CHUNK && a.append && split == a.S - 1 && wave == 0 && lane < D / 16) {
     if (a.enc.in_dtype == 0)
       encode_append_row<D, BK, BV, 0>(a.enc, bkv, lane);
     else if (a.enc.in_dtype == 1)
@@ -1803,7 +1885,7 @@ k_decode_mx(DecodeArgs a) {
   const std::false_type scores_only{};
 
   auto softmax = [&](int64_t base, uint32_t* px, const Tile& cur, const Scores& sc) {
-    const bool valid = base + lane < t_end;
+    const bool valid = base + lane < vend(base);
     const mx_f4 (&sk)[2] = sc.sk;
     const mx_f4 (&sq)[QJL ? 2 : 1] = sc.sq;
     const float knrm = NF16 ? dev::f16_to_f32(cur.kn) : __uint_as_float(cur.kn);

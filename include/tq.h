@@ -278,6 +278,30 @@ int tq_append_attend_decode(const tq_config* cfg, const void* k_new,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * One step that appends a chunk of n_new tokens and attends (README, "How
+ * it plugs in": the cache stores the new rotated keys and values, then
+ * attention runs on the rotated query; API page, "Implementation Details:
+ * Cache Substitution"). Same result (up to the order of the sums) and the
+ * same cache bytes as
+ *   tq_encode_kv(cfg, k_new, v_new, in_dtype, n_ctx - n_new, n_new, cache, stream);
+ *   tq_attend_decode(cfg, q, q_dtype, B, Hq, cache, n_ctx, ...);
+ *   k_new, v_new: [B][Hkv][n_new][d] of in_dtype (device), 16-byte aligned:
+ *                 the rows of tokens n_ctx - n_new .. n_ctx - 1.
+ * 1 <= n_new <= n_ctx (else TQ_ERR_ARG); the other arguments, the workspace
+ * and the errors are those of tq_attend_decode; all arguments are checked
+ * before any work is queued. On the matrix-core decode without QJL this is
+ * one launch: every split decodes a share of the older tokens and a share
+ * of the new ones, and its workgroup encodes its new rows first. Other
+ * formats queue the encode and the decode back to back.
+ */
+int tq_append_chunk_attend_decode(const tq_config* cfg, const void* k_new,
+                                  const void* v_new, int in_dtype, int64_t n_new,
+                                  const void* q, int q_dtype, int B, int Hq,
+                                  const tq_cache* cache, int64_t n_ctx, float scale,
+                                  int splits, float* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/*
  * Causal multi-query attention of a prefill chunk over the packed cache
  * (the time-to-first-token path the README times in "Throughput, latency &
  * memory"; the API page's patched attention, "Implementation Details: Cache

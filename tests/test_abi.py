@@ -239,6 +239,38 @@ def test_append_attend_validation():
     assert _app(B=0, cache=_cache(B=0)) == tq.TQ_OK    # empty batch: no-op
 
 
+def _chunk(cfg=None, k=A, v=A, dt=tq.TQ_BF16, n_new=4, q=A, qdt=tq.TQ_BF16, B=1, Hq=4,
+           cache=None, n_ctx=10, scale=0.0, splits=0, out=A, ws=A, ws_bytes=1 << 30):
+    lib = tq.lib()
+    cfg = _cfg() if cfg is None else cfg
+    cache = _cache() if cache is None else cache
+    return lib.tq_append_chunk_attend_decode(ctypes.byref(cfg) if cfg != "null" else None, k, v,
+                                             dt, n_new, q, qdt, B, Hq, ctypes.byref(cache),
+                                             n_ctx, scale, splits, out, ws, ws_bytes, None)
+
+
+def test_append_chunk_attend_validation():
+    """The chunked step checks the chunk (1 <= n_new <= n_ctx, rows, dtype,
+    alignment) and the decode side before anything is queued."""
+    assert _chunk(cfg="null") == tq.TQ_ERR_ARG
+    assert _chunk(cfg=_cfg(bits_k=5)) == tq.TQ_ERR_UNSUPPORTED
+    assert _chunk(cache=_cache(kc=None)) == tq.TQ_ERR_ARG
+    assert _chunk(dt=7) == tq.TQ_ERR_UNSUPPORTED
+    assert _chunk(n_new=0) == tq.TQ_ERR_ARG
+    assert _chunk(n_new=11) == tq.TQ_ERR_ARG              # more new tokens than the context
+    assert _chunk(n_ctx=0) == tq.TQ_ERR_ARG
+    assert _chunk(n_ctx=65, n_new=4) == tq.TQ_ERR_CAPACITY
+    assert _chunk(k=None) == tq.TQ_ERR_ARG
+    assert _chunk(v=MIS) == tq.TQ_ERR_ALIGN
+    assert _chunk(B=2) == tq.TQ_ERR_ARG
+    assert _chunk(qdt=5) == tq.TQ_ERR_UNSUPPORTED
+    assert _chunk(Hq=3) == tq.TQ_ERR_ARG
+    assert _chunk(q=None) == tq.TQ_ERR_ARG
+    assert _chunk(out=MIS) == tq.TQ_ERR_ALIGN
+    assert _chunk(ws_bytes=64) == tq.TQ_ERR_WORKSPACE
+    assert _chunk(B=0, cache=_cache(B=0)) == tq.TQ_OK    # empty batch: no-op
+
+
 def test_rht_qjl_dense_validation():
     lib = tq.lib()
     assert lib.tq_rht(A, tq.TQ_F32, A, -1, 128, 0, 0, None) == tq.TQ_ERR_ARG

@@ -195,3 +195,48 @@ def test_full_size_prefill_sampled_rows():
             log(f"  query {i} (position {n_ctx - 1}), head {h}: max relative error {err:.3e}")
             worst = max(worst, err)
     assert worst <= TOL
+
+
+@pytest.mark.timeout(300)
+def test_full_size_chunk_append_step():
+    """The long-context step as one call: tq_append_chunk_attend_decode of the
+    4096 newest tokens onto the bulk-encoded 520192 (default split count).
+    The appended rows are sampled against the oracle, the output of every
+    query head of two KV heads against the oracle over the full context, and
+    the whole output against tq_attend_decode on the resulting cache."""
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.WORKLOADS[4]
+    cfg = config_of(w)
+    k_host = si.kv_full(w, si.T_K)
+    v_host = si.kv_full(w, si.T_V)
+    K, V = to_device(k_host, w.in_dtype), to_device(v_host, w.in_dtype)
+    del k_host, v_host
+    n_bulk = w.N - w.append
+    log(f"chunk step: {w.append} tokens appended onto {n_bulk} ({w.name})")
+    cache = tq.PackedCache(cfg, w.B, w.Hkv, w.N)
+    tq.tq_encode_kv(cfg, K[:, :, :n_bulk].contiguous(), V[:, :, :n_bulk].contiguous(), 0, cache)
+    kc, vc = K[:, :, n_bulk:].contiguous(), V[:, :, n_bulk:].contiguous()
+    del K, V
+    qraw, qf = si.queries(w)
+    q = to_device(qraw, w.in_dtype)
+    out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device="cuda")
+    ws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N))
+    tq.tq_append_chunk_attend_decode(cfg, kc, vc, q, cache, w.N, out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    counts = _check_sampled_rows(w, cache)
+    log(f"  sampled rows: codes/norms exact off boundaries; boundary coords {counts}")
+    out2 = torch.empty_like(out)
+    tq.tq_attend_decode(cfg, q, cache, w.N, out2, ws)
+    torch.cuda.synchronize()
+    diff, _ = rel_err(got, out2.cpu().numpy().astype(np.float64))
+    log(f"  against tq_attend_decode on the same cache: {diff:.2e}")
+    assert diff <= TOL
+    heads = sorted({(0, h) for h in range(w.G)} |
+                   {(w.B - 1, h) for h in range(w.Hq - w.G, w.Hq)})
+    want = _oracle_heads(w, qf, heads)
+    worst = max(rel_err(got[b, h][None], want[b, h][None])[0] for b, h in heads)
+    log(f"  worst head against the oracle: {worst:.3e}")
+    assert worst <= TOL

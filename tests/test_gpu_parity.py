@@ -197,6 +197,64 @@ def test_many_tiles_per_split(splits, scale):
                                 structure="correlated", wid=127), scale=scale, splits=splits)
 
 
+CHUNK_CASES = ["d128_k3v4_gqa4", "d256_k2v2_outlier", "d128_k3v3_g3",
+               "d128_k4v4_f32norm_f32in_g1", "d128_k3qjl_v4_corr", "d128_n1"]
+
+
+@pytest.mark.parametrize("name", CHUNK_CASES)
+def test_append_chunk_attend_matches_encode_then_decode(name):
+    """tq_append_chunk_attend_decode (one launch on the matrix-core decode
+    without QJL: every split encodes and reads a share of the new tokens;
+    encode then decode otherwise) leaves the same cache bytes as tq_encode_kv
+    of the chunk, and its output matches the oracle and the two-call result
+    (bit for bit when it makes the two calls): chunks of 1, 37, 300 and all
+    N tokens, split counts 0 and 5."""
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.small_workload(**SMALL[name])
+    fused = not w.qjl
+    log(f"case {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} N={w.N} K{w.bits_k}/V{w.bits_v} "
+        f"qjl={w.qjl} in={w.in_dtype}")
+    qraw, qf = si.queries(w)
+    q = to_device(qraw, w.in_dtype)
+    ref = oracle_encode(w)
+    want = o.attend(qf.astype(np.float64), ref, w.N, d=w.d, seed=w.seed, bits_k=w.bits_k,
+                    bits_v=w.bits_v, Hkv=w.Hkv, qjl=w.qjl, qjl_seed=w.qjl_seed)
+    for n_new in sorted({1, min(37, w.N), min(300, w.N), w.N}):
+        n0 = w.N - n_new
+        rk, rv, _, _ = kv_host(w, n0, w.N)
+        kc, vc = to_device(rk, w.in_dtype), to_device(rv, w.in_dtype)
+        for splits in (0, 5):
+            if n0 > 0:
+                cfg, two = gpu_encode(w, chunks=[(0, n0)], capacity=w.N)
+                _, one = gpu_encode(w, chunks=[(0, n0)], capacity=w.N)
+            else:                         # the chunk is the whole context
+                cfg = config_of(w)
+                two = tq.PackedCache(cfg, w.B, w.Hkv, w.N)
+                one = tq.PackedCache(cfg, w.B, w.Hkv, w.N)
+            tq.tq_encode_kv(cfg, kc, vc, n0, two)
+            ref_out = gpu_decode(w, cfg, two, q, w.N, splits=splits)
+            out = torch.full((w.B, w.Hq, w.d), float("nan"), dtype=torch.float32, device="cuda")
+            ws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N, splits))
+            tq.tq_append_chunk_attend_decode(cfg, kc, vc, q, one, w.N, out, ws, splits=splits)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy().astype(np.float64)
+            for plane in ("kc", "vc", "kn", "vn", "kq", "kr"):
+                a, b = getattr(one, plane), getattr(two, plane)
+                if a is None:
+                    continue
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), plane
+            err, _ = rel_err(got, want)
+            diff, _ = rel_err(got, ref_out)
+            log(f"  n_new={n_new} splits={splits}: error vs oracle {err:.2e}, "
+                f"vs the two calls {diff:.2e}")
+            assert err <= TOL
+            if fused:
+                assert diff <= TOL
+            else:
+                assert np.array_equal(got, ref_out)
+
+
 def test_append_chunks_equal_bulk_encode():
     """Encoding as several appends writes the same planes as one encode."""
     torch = torch_cuda()
