@@ -1,5 +1,6 @@
 """The decode step captured in a HIP graph (torch.cuda.CUDAGraph), as
-bench.py times it: append encode + decode, replayed several times with eager
+bench.py times it: append encode + decode (as two calls, or as the one
+tq_append_chunk_attend_decode call), replayed several times with eager
 calls and synchronizations between the replays. Every replay's output and
 cache bytes must equal the eager step's bit for bit; this also exercises the
 decode's arrival counters, which every call leaves at zero."""
@@ -13,13 +14,14 @@ from gpu_helpers import config_of, kv_host, log, to_device, torch_cuda
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("bits_v,qjl", [(4, False), (2, False), (4, True), (3, False)])
-def test_graph_replays_equal_eager_step(bits_v, qjl):
+def test_graph_replays_equal_eager_step(bits_v, qjl, fused):
     import decode_attention_seeded_amd as tq
     torch = torch_cuda()
     w = si.small_workload(B=2, Hq=8, Hkv=2, N=3000, bits_k=3, bits_v=bits_v, wid=150 + bits_v,
                           qjl=qjl)
-    log(f"graph replay: K3/V{bits_v} qjl={qjl}")
+    log(f"graph replay: K3/V{bits_v} qjl={qjl} fused={fused}")
     cfg = config_of(w)
     rk, rv, _, _ = kv_host(w, 0, w.N)
     K, V = to_device(rk, w.in_dtype), to_device(rv, w.in_dtype)
@@ -33,8 +35,11 @@ def test_graph_replays_equal_eager_step(bits_v, qjl):
     ws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N))
 
     def step():
-        tq.tq_encode_kv(cfg, k_app, v_app, w.N - A, cache)
-        tq.tq_attend_decode(cfg, q, cache, w.N, out, ws)
+        if fused:
+            tq.tq_append_chunk_attend_decode(cfg, k_app, v_app, q, cache, w.N, out, ws)
+        else:
+            tq.tq_encode_kv(cfg, k_app, v_app, w.N - A, cache)
+            tq.tq_attend_decode(cfg, q, cache, w.N, out, ws)
 
     step()
     torch.cuda.synchronize()
