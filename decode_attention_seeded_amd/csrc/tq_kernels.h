@@ -290,9 +290,22 @@ __device__ __forceinline__ double words_to_f64(const RowWords<IW>& r, const Enco
 // u >= 0 and L/2 - 1 - #{j : |u| >= n t_{L/2+j}} for u < 0 (exact ties aside),
 // which needs neither a division nor the negative half of the thresholds.
 // Lanes of rows past the end (valid = false) compute but store nothing.
-template <int D, int BITS, bool QJL, int TS, int IW>
+// Threshold lookup for 4-bit codes (k_encode): bucket b of z = |u| / n
+// covers [b / 32, (b + 1) / 32); c0 counts the positive thresholds at or
+// below b / 32 and tb32 is 32 times the one threshold inside the bucket
+// (+inf when none; the thresholds are more than 1/32 apart). The count is
+// c0 + (32 |u| / n >= tb32): in fp64 it differs from the direct comparisons
+// |u| >= n t_j only within ~1e-16 of a threshold, inside the decision band.
+struct CodeLut {
+  double tb32;
+  uint32_t c0, pad;
+};
+constexpr int kLutBuckets = 256;             // z up to 8; larger z clamps to the last
+
+template <int D, int BITS, bool QJL, int TS, int IW, bool LUT = false>
 __device__ __forceinline__ void encode_row(const EncodeArgs& a, int bh, int64_t t, bool valid,
-                                           const EncodeLane<IW>& el, double (&u)[32], double ss) {
+                                           const EncodeLane<IW>& el, double (&u)[32], double ss,
+                                           const CodeLut* lut = nullptr) {
   constexpr int P = D / 32;
   constexpr int E = 32;
   constexpr int L = 1 << BITS;
@@ -318,9 +331,12 @@ __device__ __forceinline__ void encode_row(const EncodeArgs& a, int bh, int64_t 
   }
 
   // thresholds scaled by the norm; a zero row gets the middle code L/2
+  // (with the lookup: z = 0, bucket 0, count 0)
+  static_assert(!LUT || BITS == 4, "threshold lookup: 4-bit codes");
   double T[H - 1];
 #pragma unroll
   for (int j = 0; j < H - 1; ++j) T[j] = n > 0.0 ? a.tpos[TS][j] * n : INFINITY;
+  const double rn32 = n > 0.0 ? 32.0 / n : 0.0;
   uint32_t w[LW];
 #pragma unroll
   for (int k = 0; k < LW; ++k) w[k] = 0u;
@@ -329,8 +345,15 @@ __device__ __forceinline__ void encode_row(const EncodeArgs& a, int bh, int64_t 
   for (int i = 0; i < E; ++i) {
     const double au = fabs(u[i]);
     uint32_t c = 0;
+    if constexpr (LUT) {
+      const double z32 = au * rn32;
+      const int b = min(int(z32), kLutBuckets - 1);
+      const CodeLut e = lut[b];
+      c = e.c0 + (z32 >= e.tb32 ? 1u : 0u);
+    } else {
 #pragma unroll
-    for (int j = 0; j < H - 1; ++j) c += (au >= T[j]) ? 1u : 0u;
+      for (int j = 0; j < H - 1; ++j) c += (au >= T[j]) ? 1u : 0u;
+    }
     code[i] = u[i] >= 0.0 ? uint32_t(H) + c : uint32_t(H - 1) - c;
     // LSB-first bitstream: code i at bit BITS*i of the lane's LW dwords
     const int pos = BITS * i;
@@ -447,6 +470,27 @@ __global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
   const uint32_t nwave = gridDim.x * (blockDim.x >> 6);
   uint32_t item = blockIdx.x * (blockDim.x >> 6) +
                   uint32_t(__builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)));
+
+  // threshold lookups of the 4-bit tensors (key, value), one per workgroup
+  constexpr bool LK = BK == 4, LV = BV == 4;
+  __shared__ CodeLut lut[(LK && LV) ? 2 : 1][kLutBuckets];
+  if constexpr (LK || LV) {
+    for (int i = threadIdx.x; i < ((LK ? 1 : 0) + (LV ? 1 : 0)) * kLutBuckets;
+         i += blockDim.x) {
+      const int tab = i / kLutBuckets, bkt = i % kLutBuckets;
+      const int ts = LK && tab == 0 ? 0 : 1;
+      const double lo = bkt / 32.0, hi = (bkt + 1) / 32.0;
+      uint32_t c0 = 0;
+      double tb = INFINITY;
+      for (int j = 0; j < 7; ++j) {
+        const double tj = a.tpos[ts][j];
+        if (tj <= lo) ++c0;
+        else if (tj < hi) tb = tj * 32.0;
+      }
+      lut[tab][bkt] = CodeLut{tb, c0, 0u};
+    }
+    __syncthreads();
+  }
   if (item >= items) return;
 
   const EncodeLane<IW> el = make_encode_lane<IW, QJL>(a, lane & (P - 1));
@@ -479,9 +523,9 @@ __global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
     fetch(item, rw);
     const bool valid = w.t < a.n_new;
     if (w.z == 0)
-      encode_row<D, BK, QJL, 0, IW>(a, w.bh, w.t, valid, el, u, ss);
+      encode_row<D, BK, QJL, 0, IW, LK>(a, w.bh, w.t, valid, el, u, ss, lut[0]);
     else
-      encode_row<D, BV, false, 1, IW>(a, w.bh, w.t, valid, el, u, ss);
+      encode_row<D, BV, false, 1, IW, LV>(a, w.bh, w.t, valid, el, u, ss, lut[LK ? 1 : 0]);
     if (item >= items) break;
   }
 }

@@ -56,6 +56,18 @@ def test_host_sphere_codebook_matches_oracle(bits, d):
         tq.tq_codebook_ex(bits, "sphere", 64)
 
 
+@pytest.mark.parametrize("kind,d", [("gauss", 128), ("sphere", 128), ("sphere", 256)])
+def test_4bit_thresholds_fit_the_encode_lookup(kind, d):
+    """The encode finds 4-bit codes through buckets of width 1/32 in
+    z = |u| / n over [0, 8): each bucket may hold at most one positive
+    threshold, and all of them lie below 8."""
+    _, t = tq.tq_codebook_ex(4, kind, d)
+    pos = np.asarray(t[len(t) // 2 + 1:])           # the 7 positive thresholds
+    assert len(pos) == 7 and (pos > 0).all() and (pos < 8).all()
+    buckets = np.floor(pos * 32).astype(int)
+    assert len(set(buckets.tolist())) == len(buckets)
+
+
 @pytest.mark.parametrize("seed,d", [(0, 128), (1, 256), (12345, 128)])
 def test_host_signs_match_oracle(seed, d):
     assert tq.tq_signs(seed, d) == list(o.signs(seed, d).astype(int))
