@@ -166,6 +166,18 @@ const Codebook& codebook(int bits, int kind, int d) {
   return g_sphere[bits][j];
 }
 
+bool codebook_fits_code_lookup(const tq_config* cfg, int bits) {
+  if (bits != 3 && bits != 4) return true;
+  const Codebook& cb = codebook(bits, cfg->codebook, cfg->d);
+  const int L = 1 << bits;
+  const double w = 1.0 / kCodeLutScale, lim = (kCodeLutOff - 1) * w;
+  for (int k = 0; k < L - 1; ++k) {
+    if (!(std::fabs(cb.t[k]) < lim)) return false;
+    if (k > 0 && !(cb.t[k] - cb.t[k - 1] > w)) return false;
+  }
+  return true;
+}
+
 int check_config(const tq_config* cfg) {
   if (!cfg) return TQ_ERR_ARG;
   if (!valid_d(cfg->d) || !valid_bits(cfg->bits_k) || !valid_bits(cfg->bits_v))
@@ -173,6 +185,9 @@ int check_config(const tq_config* cfg) {
   if (cfg->norm_dtype != TQ_F16 && cfg->norm_dtype != TQ_F32) return TQ_ERR_UNSUPPORTED;
   if (cfg->qjl != 0 && cfg->qjl != 1) return TQ_ERR_ARG;
   if (cfg->codebook != TQ_CODEBOOK_GAUSS && cfg->codebook != TQ_CODEBOOK_SPHERE)
+    return TQ_ERR_UNSUPPORTED;
+  // every supported codebook fits; a codebook that did not would get wrong codes
+  if (!codebook_fits_code_lookup(cfg, cfg->bits_k) || !codebook_fits_code_lookup(cfg, cfg->bits_v))
     return TQ_ERR_UNSUPPORTED;
   return TQ_OK;
 }

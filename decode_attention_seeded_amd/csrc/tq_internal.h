@@ -70,6 +70,16 @@ struct DecodePlan {
   size_t off_qp = 0, off_qq = 0, off_ml = 0, off_acc = 0, off_cnt = 0, total = 0;
 };
 
+// Geometry of the bulk encode's code lookup for 3- and 4-bit codes: buckets
+// of width 1 / kCodeLutScale in z, kCodeLutOff of them below z = 0 and as
+// many above, the two end buckets open towards -inf and +inf. A codebook
+// fits it when its thresholds are more than one bucket apart (at most one
+// inside any bucket) and all lie inside the inner buckets.
+constexpr int kCodeLutScale = 4;
+constexpr int kCodeLutOff = 16;
+constexpr int kCodeLutBuckets = 2 * kCodeLutOff;
+bool codebook_fits_code_lookup(const tq_config* cfg, int bits);
+
 // Waves per workgroup of the matrix-core decode kernel (one workgroup holds a
 // compute unit; a workgroup round covers 64 tokens per wave), and whether a
 // format runs it (d 128 or 256, 2- to 4-bit values, with or without QJL).

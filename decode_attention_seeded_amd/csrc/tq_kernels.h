@@ -139,10 +139,11 @@ __global__ void __launch_bounds__(256) k_rht(RhtArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Encode: rotation, norm, quantization and packing of one K or V plane.
-// 16 lanes per row. The transform and the comparisons run in double: the
-// Hadamard sums of bf16 inputs are then exact, so the codes equal the
-// definition except for values lying exactly on a threshold.
+// Encode: rotation, norm, quantization and packing of one K or V plane, a
+// row on P = D/32 lanes with 32 coordinates each. The transform and the
+// comparisons run in double: the Hadamard sums of bf16 inputs are then
+// exact, so the codes equal the definition except for values lying exactly
+// on a threshold.
 // ---------------------------------------------------------------------------
 
 // Dword k (k < 8) of 8 uniform dwords for a lane-dependent k: a select
@@ -215,6 +216,22 @@ __device__ __forceinline__ double group_sum_f64(double x) {
   return x;
 }
 
+// k_encode's strided row layout: with S = 5 - log2(P), lane lp of a row holds
+// the coordinates whose bits [S, 5) equal lp, its register j the one with
+// bits [0, S) = j mod 2^S and bits [5, 5 + log2 P) = j / 2^S. A lane then
+// reads P segments of 2^S consecutive elements, and the butterflies on all
+// bits but [S, 5) stay inside the lane.
+template <int P>
+__host__ __device__ constexpr int enc_seg_bits() {
+  static_assert(P == 4 || P == 8, "rows of 128 or 256 coordinates");
+  return P == 4 ? 3 : 2;
+}
+template <int P>
+__host__ __device__ constexpr int strided_coord(int lp, int j) {
+  return ((j >> enc_seg_bits<P>()) << 5) | (lp << enc_seg_bits<P>()) |
+         (j & ((1 << enc_seg_bits<P>()) - 1));
+}
+
 // One lane's 32 input coordinates as raw 16-byte words: 4 for 16-bit inputs
 // (IW = 2 bytes per element), 8 for fp32.
 template <int IW>
@@ -243,6 +260,36 @@ __device__ __forceinline__ void load_words(const EncodeArgs& a, int z, int bh, i
                                                   (row * D + lp * 32) * IW);
 #pragma unroll
   for (int k = 0; k < 2 * IW; ++k) r.q[k] = s[k];
+}
+
+// The lane's 32 input coordinates in k_encode's strided layout: P segments of
+// 32 IW / P bytes (rows past the end re-read the last one).
+template <int D, int IW>
+__device__ __forceinline__ void load_words_strided(const EncodeArgs& a, int z, int bh, int64_t t,
+                                                   int lp, RowWords<IW>& r) {
+  constexpr int P = D / 32;
+  constexpr int SEG = 32 * IW / P;
+  const int64_t tc = t < a.n_new ? t : a.n_new - 1;
+  const uint8_t* row =
+      static_cast<const uint8_t*>(a.x[z]) + (int64_t(bh) * a.n_new + tc) * (D * IW);
+#pragma unroll
+  for (int g = 0; g < P; ++g) {
+    const uint8_t* src = row + strided_coord<P>(lp, g << enc_seg_bits<P>()) * IW;
+    if constexpr (SEG >= 16) {
+#pragma unroll
+      for (int k = 0; k < SEG / 16; ++k)
+        r.q[g * (SEG / 16) + k] = reinterpret_cast<const uint4*>(src)[k];
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(src);
+      if (g & 1) {
+        r.q[g >> 1].z = w.x;
+        r.q[g >> 1].w = w.y;
+      } else {
+        r.q[g >> 1].x = w.x;
+        r.q[g >> 1].y = w.y;
+      }
+    }
+  }
 }
 
 // Sign-flipped coordinates x_i * s_i as doubles, and sum of squares (DT:
@@ -282,42 +329,198 @@ __device__ __forceinline__ double words_to_f64(const RowWords<IW>& r, const Enco
   return ss;
 }
 
-// One row of tensor TS (0 = K, 1 = V) on P = D/32 lanes, from its
-// sign-flipped coordinates u and their sum of squares: FWHT in fp64 (exact
-// for bf16/fp16 inputs), norm, codes, pack. The code of
-// z = u / n is #{k : z >= t_k}; with the antisymmetric codebook
-// (t_{L/2-1} = 0, t_k = -t_{L-2-k}) it is L/2 + #{j : |u| >= n t_{L/2+j}} for
-// u >= 0 and L/2 - 1 - #{j : |u| >= n t_{L/2+j}} for u < 0 (exact ties aside),
-// which needs neither a division nor the negative half of the thresholds.
-// Lanes of rows past the end (valid = false) compute but store nothing.
-// Threshold lookup for 4-bit codes (k_encode): bucket b of z = |u| / n
-// covers [b / 32, (b + 1) / 32); c0 counts the positive thresholds at or
-// below b / 32 and tb32 is 32 times the one threshold inside the bucket
-// (+inf when none; the thresholds are more than 1/32 apart). The count is
-// c0 + (32 |u| / n >= tb32): in fp64 it differs from the direct comparisons
-// |u| >= n t_j only within ~1e-16 of a threshold, inside the decision band.
-struct CodeLut {
-  double tb32;
-  uint32_t c0, pad;
+// LDS cells (16 bytes: two doubles) of the transpose from the strided to the
+// contiguous layout, for one wave's 64/P rows. It runs in two rounds, one
+// per value of coordinate bit 1, each moving half of every row; chunk c of
+// a round is coordinate >> 2, and (row r, chunk c) lives in cell
+// r RS + (r >> 1) E1 + c + (c >> 3) p3. The padding keeps every write and
+// read instruction free of bank conflicts (16-lane groups over 64 banks and
+// 8-lane groups over 32) and makes each address a per-lane base plus a
+// per-instruction constant (checked below).
+template <int P>
+struct XposeLayout;
+template <>
+struct XposeLayout<4> {
+  static constexpr int RS = 41, E1 = 6, p3 = 2, cells = 695;
 };
-constexpr int kLutBuckets = 256;             // z up to 8; larger z clamps to the last
+template <>
+struct XposeLayout<8> {
+  static constexpr int RS = 72, E1 = 0, p3 = 1, cells = 575;
+};
+template <int P>
+__host__ __device__ constexpr int xpose_cell(int r, int c) {
+  return r * XposeLayout<P>::RS + (r >> 1) * XposeLayout<P>::E1 + c + (c >> 3) * XposeLayout<P>::p3;
+}
+// chunk written from register pair j (strided) and read into pair k (contiguous)
+template <int P>
+__host__ __device__ constexpr int xpose_wchunk(int lp, int j) {
+  return strided_coord<P>(lp, j) >> 2;
+}
+__host__ __device__ constexpr int xpose_rchunk(int lp, int k) { return (32 * lp + k) >> 2; }
 
-template <int D, int BITS, bool QJL, int TS, int IW, bool LUT = false>
-__device__ __forceinline__ void encode_row(const EncodeArgs& a, int bh, int64_t t, bool valid,
-                                           const EncodeLane<IW>& el, double (&u)[32], double ss,
-                                           const CodeLut* lut = nullptr) {
+template <int P>
+constexpr bool xpose_layout_ok() {
+  constexpr int R = 64 / P, C = 8 * P, N = XposeLayout<P>::cells;
+  bool seen[N] = {};
+  for (int r = 0; r < R; ++r)
+    for (int c = 0; c < C; ++c) {
+      const int x = xpose_cell<P>(r, c);
+      if (x < 0 || x >= N || seen[x]) return false;
+      seen[x] = true;
+    }
+  for (int r = 0; r < R; ++r)
+    for (int lp = 0; lp < P; ++lp)
+      for (int j = 0; j < 32; j += 2) {
+        const int dw = xpose_cell<P>(r, xpose_wchunk<P>(lp, j)) - xpose_cell<P>(r, xpose_wchunk<P>(lp, 0));
+        const int dr = xpose_cell<P>(r, xpose_rchunk(lp, j)) - xpose_cell<P>(r, xpose_rchunk(lp, 0));
+        if (dw != xpose_cell<P>(0, xpose_wchunk<P>(0, j)) - xpose_cell<P>(0, xpose_wchunk<P>(0, 0)) ||
+            dr != xpose_cell<P>(0, xpose_rchunk(0, j)) - xpose_cell<P>(0, xpose_rchunk(0, 0)))
+          return false;
+      }
+  return true;
+}
+static_assert(xpose_layout_ok<4>() && xpose_layout_ok<8>(), "transpose layout");
+
+// FWHT (unnormalized) of a row held in the strided layout, which it leaves in
+// the contiguous one (register k of lane lp = coordinate 32 lp + k): the
+// butterflies on the register bits, the transpose through the wave's LDS
+// cells xb, whose first write and read cells are at byte offsets wb and rb
+// for this lane, then the butterflies on bits [S, 5). The cells are private
+// to the wave, whose LDS operations complete in order: a wave-scope fence
+// only keeps the compiler from moving them.
+template <int P>
+__device__ __forceinline__ void fwht_strided(double (&v)[32], char* xb, int wb, int rb) {
+  constexpr int S = enc_seg_bits<P>();
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (!(i & h)) {
+        const double x = v[i], y = v[i + h];
+        v[i] = x + y;
+        v[i + h] = x - y;
+      }
+    }
+  }
+#pragma unroll
+  for (int hr = 0; hr < 2; ++hr) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int j = 4 * m + 2 * hr;
+      const int off = 16 * (xpose_cell<P>(0, xpose_wchunk<P>(0, j)) - xpose_cell<P>(0, xpose_wchunk<P>(0, 0)));
+      *reinterpret_cast<double2*>(xb + wb + off) = make_double2(v[j], v[j + 1]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int k = 4 * m + 2 * hr;
+      const int off = 16 * (xpose_cell<P>(0, xpose_rchunk(0, k)) - xpose_cell<P>(0, xpose_rchunk(0, 0)));
+      const double2 t = *reinterpret_cast<const double2*>(xb + rb + off);
+      v[k] = t.x;
+      v[k + 1] = t.y;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+#pragma unroll
+  for (int h = 1 << S; h < 32; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if (!(i & h)) {
+        const double x = v[i], y = v[i + h];
+        v[i] = x + y;
+        v[i + h] = x - y;
+      }
+    }
+  }
+}
+
+// Code lookup of k_encode (3- and 4-bit codes): with S = kCodeLutScale and
+// OFF = kCodeLutOff, bucket b covers z = u / n in [(b - OFF) / S,
+// (b + 1 - OFF) / S), the first one extended down to -inf and the last one up
+// to +inf; the host admits only codebooks whose thresholds are more than 1/S
+// apart and inside the inner buckets. Entry b is the double S t + OFF of the
+// one threshold t inside the bucket (2^60 when there is none), with its low
+// BITS mantissa bits replaced by the number of thresholds at or below the
+// bucket's lower edge. The code is that number plus (S z + OFF >= entry): the
+// replaced bits move the threshold by less than 2^-46 in z, and the rounding
+// of S z + OFF is below 2^-50, both far inside the decision band. The 32
+// entries of a table lie in distinct LDS banks, so its reads never conflict.
+// Packs the low BITS bits of each of 32 codes LSB-first into BITS dwords
+// with one funnel shift per code (two for a code that straddles dwords):
+// bits above BITS in a code are ignored.
+template <int BITS>
+__device__ __forceinline__ void pack_codes_funnel(const uint32_t (&code)[32], uint32_t (&w)[BITS]) {
+#pragma unroll
+  for (int k = 0; k < BITS; ++k) {
+    const int hi = 32 * k + 32;
+    const int i0 = 32 * k / BITS, i1 = (hi - 1) / BITS;
+    uint32_t x = 0u;
+#pragma unroll
+    for (int i = i0; i <= i1; ++i)
+      x = __builtin_amdgcn_alignbit(code[i], x, uint32_t(i == i1 ? hi - BITS * i : BITS));
+    w[k] = x;
+  }
+}
+
+// Codes of 32 rotated coordinates u through a code lookup table lut (3- and
+// 4-bit codes, above): z = u / n enters scaled by rns = kCodeLutScale / n (0
+// for a zero row, which gets z = 0, the middle code L/2; a row with an
+// infinite or NaN element gets unspecified codes). The low BITS bits of
+// each result are the code; the bits above are not.
+__device__ __forceinline__ void lookup_codes(const double (&u)[32], double rns, const double* lut,
+                                             uint32_t (&code)[32]) {
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const double z = fma(u[i], rns, double(kCodeLutOff));
+    const double e = lut[min(max(int(z), 0), kCodeLutBuckets - 1)];
+    code[i] = uint32_t(__double_as_longlong(e)) + (z >= e ? 1u : 0u);
+  }
+}
+
+// Codes of 32 rotated coordinates u of a row of norm n by comparison. The
+// code of z = u / n is #{k : z >= t_k}; with the antisymmetric codebook
+// (t_{L/2-1} = 0, t_k = -t_{L-2-k}) it is L/2 + #{j : |u| >= n t_{L/2+j}}
+// for u >= 0 and L/2 - 1 - #{j : |u| >= n t_{L/2+j}} for u < 0 (exact ties
+// aside), which needs neither a division nor the negative half of the
+// thresholds. A zero row gets the middle code L/2.
+template <int BITS, int TS>
+__device__ __forceinline__ void direct_codes(const EncodeArgs& a, const double (&u)[32], double n,
+                                             uint32_t (&code)[32]) {
+  constexpr int H = 1 << (BITS - 1);
+  double T[H - 1];
+#pragma unroll
+  for (int j = 0; j < H - 1; ++j) T[j] = n > 0.0 ? a.tpos[TS][j] * n : INFINITY;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const double au = fabs(u[i]);
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < H - 1; ++j) c += (au >= T[j]) ? 1u : 0u;
+    code[i] = u[i] >= 0.0 ? uint32_t(H) + c : uint32_t(H - 1) - c;
+  }
+}
+
+// Stores one row of tensor TS (0 = K, 1 = V) held on P = D/32 lanes: its norm
+// n, its codes (low BITS bits of code[i] for the lane's coordinate i, packed
+// LSB-first), and with QJL the sign sketch of the residual of the rotated
+// coordinates u. Lanes of rows past the end (valid = false) compute but store
+// nothing.
+template <int D, int BITS, bool QJL, int TS, int IW>
+__device__ __forceinline__ void store_encoded_row(const EncodeArgs& a, int bh, int64_t t,
+                                                  bool valid, const EncodeLane<IW>& el,
+                                                  const double (&u)[32], double n,
+                                                  const uint32_t (&code)[32]) {
   constexpr int P = D / 32;
   constexpr int E = 32;
   constexpr int L = 1 << BITS;
-  constexpr int H = L / 2;
   constexpr int REC = D * BITS / 8;          // bytes per packed row
   constexpr int LW = BITS;                    // dwords of the row per lane (32 codes)
   const int lp = el.lp;
   const int64_t rec = int64_t(bh) * a.capacity + a.offset + t;
-
-  fwht32xP<P>(u, el.sg);
-  ss = group_sum_f64<P>(ss);
-  const double n = sqrt(ss);
 
   double nstored;
   if (a.norm_f16) {
@@ -330,36 +533,8 @@ __device__ __forceinline__ void encode_row(const EncodeArgs& a, int bh, int64_t 
     if (valid && lp == 0) static_cast<float*>(a.norms[TS])[rec] = nf;
   }
 
-  // thresholds scaled by the norm; a zero row gets the middle code L/2
-  // (with the lookup: z = 0, bucket 0, count 0)
-  static_assert(!LUT || BITS == 4, "threshold lookup: 4-bit codes");
-  double T[H - 1];
-#pragma unroll
-  for (int j = 0; j < H - 1; ++j) T[j] = n > 0.0 ? a.tpos[TS][j] * n : INFINITY;
-  const double rn32 = n > 0.0 ? 32.0 / n : 0.0;
   uint32_t w[LW];
-#pragma unroll
-  for (int k = 0; k < LW; ++k) w[k] = 0u;
-  uint32_t code[E];
-#pragma unroll
-  for (int i = 0; i < E; ++i) {
-    const double au = fabs(u[i]);
-    uint32_t c = 0;
-    if constexpr (LUT) {
-      const double z32 = au * rn32;
-      const int b = min(int(z32), kLutBuckets - 1);
-      const CodeLut e = lut[b];
-      c = e.c0 + (z32 >= e.tb32 ? 1u : 0u);
-    } else {
-#pragma unroll
-      for (int j = 0; j < H - 1; ++j) c += (au >= T[j]) ? 1u : 0u;
-    }
-    code[i] = u[i] >= 0.0 ? uint32_t(H) + c : uint32_t(H - 1) - c;
-    // LSB-first bitstream: code i at bit BITS*i of the lane's LW dwords
-    const int pos = BITS * i;
-    w[pos >> 5] |= code[i] << (pos & 31);
-    if ((pos & 31) + BITS > 32) w[(pos >> 5) + 1] |= code[i] >> (32 - (pos & 31));
-  }
+  pack_codes_funnel<BITS>(code, w);
   if (valid) {
     uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes[TS] + rec * REC + lp * (4 * LW));
 #pragma unroll
@@ -373,9 +548,10 @@ __device__ __forceinline__ void encode_row(const EncodeArgs& a, int bh, int64_t 
     double rr = 0.0;
 #pragma unroll
     for (int i = 0; i < E; ++i) {
+      const uint32_t ck = code[i] & uint32_t(L - 1);
       double ci = 0.0;
 #pragma unroll
-      for (int k = 0; k < L; ++k) ci = (code[i] == uint32_t(k)) ? a.cen_k[k] : ci;
+      for (int k = 0; k < L; ++k) ci = (ck == uint32_t(k)) ? a.cen_k[k] : ci;
       const double ri = (u[i] - nstored * ci) * inv_sqrt_d;
       rr += ri * ri;
       r[i] = (el.qmask >> i & 1) ? -ri : ri;
@@ -392,11 +568,36 @@ __device__ __forceinline__ void encode_row(const EncodeArgs& a, int bh, int64_t 
   }
 }
 
-template <int IW, bool QJL>
+// One row of the decode kernels' appends, in the contiguous layout, from its
+// sign-flipped coordinates u and the lane's share ss of its sum of squares:
+// FWHT, norm, codes by comparison, stores.
+template <int D, int BITS, bool QJL, int TS, int IW>
+__device__ __forceinline__ void encode_row(const EncodeArgs& a, int bh, int64_t t, bool valid,
+                                           const EncodeLane<IW>& el, double (&u)[32], double ss) {
+  const double n = sqrt(group_sum_f64<D / 32>(ss));
+  fwht32xP<D / 32>(u, el.sg);
+  uint32_t code[32];
+  direct_codes<BITS, TS>(a, u, n, code);
+  store_encoded_row<D, BITS, QJL, TS, IW>(a, bh, t, valid, el, u, n, code);
+}
+
+// The lane's constants. SP = P selects the sign masks of k_encode's strided
+// layout of P lanes per row, SP = 0 those of the contiguous one; the QJL
+// signs are always contiguous (the residual is rotated after the FWHT).
+template <int IW, bool QJL, int SP = 0>
 __device__ __forceinline__ EncodeLane<IW> make_encode_lane(const EncodeArgs& a, int lp) {
   EncodeLane<IW> el;
   el.lp = lp;
-  el.smask = pick8(a.sbits, lp);
+  if constexpr (SP > 0) {
+    constexpr int S = enc_seg_bits<SP>();
+    uint32_t m = 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      m |= (a.sbits[j >> S] >> ((lp << S) | (j & ((1 << S) - 1))) & 1u) << j;
+    el.smask = m;
+  } else {
+    el.smask = pick8(a.sbits, lp);
+  }
   el.qmask = QJL ? pick8(a.qsbits, lp) : 0u;
   if constexpr (IW == 2) {
 #pragma unroll
@@ -457,44 +658,58 @@ __device__ __forceinline__ void encode_chunk_rows(const EncodeArgs& e, int bh, i
 // wave) of one (tensor, batch*KV head) pair, numbered
 // (tensor * BH + bh) * groups + group. Each wave walks the items with the
 // grid's wave count as stride and loads the next item's input while it
-// encodes the current one.
+// encodes the current one. Rows are loaded in the strided layout and
+// transposed through LDS in the middle of the FWHT; 3- and 4-bit codes come
+// from the per-workgroup lookup tables.
 template <int D, int BK, int BV, bool QJL, int DT>
 __global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
   constexpr int IW = DT == 0 ? 4 : 2;        // input bytes per coordinate
   constexpr int P = D / 32;
   constexpr int RPW = 64 / P;                // rows per work item
+  constexpr int WPB = 4;                     // waves per workgroup
   const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const uint32_t groups = uint32_t((a.n_new + RPW - 1) / RPW);
   const uint32_t per_tensor = uint32_t(a.BH) * groups;
   const uint32_t items = 2 * per_tensor;
-  const uint32_t nwave = gridDim.x * (blockDim.x >> 6);
-  uint32_t item = blockIdx.x * (blockDim.x >> 6) +
-                  uint32_t(__builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)));
+  const uint32_t nwave = gridDim.x * WPB;
+  uint32_t item = blockIdx.x * WPB + uint32_t(wave);
 
-  // threshold lookups of the 4-bit tensors (key, value), one per workgroup
-  constexpr bool LK = BK == 4, LV = BV == 4;
-  __shared__ CodeLut lut[(LK && LV) ? 2 : 1][kLutBuckets];
+  // code lookups of the 3- and 4-bit tensors (key, value), one per workgroup
+  constexpr bool LK = BK == 3 || BK == 4, LV = BV == 3 || BV == 4;
+  constexpr int OFF = kCodeLutOff;
+  constexpr int NB = kCodeLutBuckets;
+  __shared__ double lut[(LK && LV) ? 2 : 1][NB];
+  __shared__ double2 xpose[WPB][XposeLayout<P>::cells];
   if constexpr (LK || LV) {
-    for (int i = threadIdx.x; i < ((LK ? 1 : 0) + (LV ? 1 : 0)) * kLutBuckets;
-         i += blockDim.x) {
-      const int tab = i / kLutBuckets, bkt = i % kLutBuckets;
+    for (int i = threadIdx.x; i < ((LK ? 1 : 0) + (LV ? 1 : 0)) * NB; i += blockDim.x) {
+      const int tab = i / NB, bkt = i % NB;
       const int ts = LK && tab == 0 ? 0 : 1;
-      const double lo = bkt / 32.0, hi = (bkt + 1) / 32.0;
+      const int bits = ts == 0 ? BK : BV;
+      const double lo = double(bkt - OFF) / kCodeLutScale, hi = double(bkt + 1 - OFF) / kCodeLutScale;
       uint32_t c0 = 0;
-      double tb = INFINITY;
-      for (int j = 0; j < 7; ++j) {
-        const double tj = a.tpos[ts][j];
-        if (tj <= lo) ++c0;
-        else if (tj < hi) tb = tj * 32.0;
+      double tb = 0x1p60;
+      // the L - 1 thresholds: 0 and +-t_{L/2+j}
+      for (int j = -1; j < (1 << (bits - 1)) - 1; ++j) {
+        for (int sgn = 0; sgn < (j < 0 ? 1 : 2); ++sgn) {
+          const double tj = j < 0 ? 0.0 : (sgn ? -a.tpos[ts][j] : a.tpos[ts][j]);
+          if (tj <= lo) ++c0;
+          else if (tj < hi) tb = kCodeLutScale * tj + OFF;
+        }
       }
-      lut[tab][bkt] = CodeLut{tb, c0, 0u};
+      const uint64_t mask = (uint64_t(1) << bits) - 1;
+      lut[tab][bkt] = __longlong_as_double(
+          int64_t((uint64_t(__double_as_longlong(tb)) & ~mask) | c0));
     }
     __syncthreads();
   }
   if (item >= items) return;
 
-  const EncodeLane<IW> el = make_encode_lane<IW, QJL>(a, lane & (P - 1));
-  const int rl = lane / P;
+  const int lp = lane & (P - 1), rl = lane / P;
+  const EncodeLane<IW> el = make_encode_lane<IW, QJL, P>(a, lp);
+  char* xb = reinterpret_cast<char*>(&xpose[wave][0]);
+  const int wb = 16 * xpose_cell<P>(rl, xpose_wchunk<P>(lp, 0));
+  const int rb = 16 * xpose_cell<P>(rl, xpose_rchunk(lp, 0));
 
   struct Where { int z, bh; int64_t t; };
   auto where = [&](uint32_t it) {
@@ -508,7 +723,7 @@ __global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
   auto fetch = [&](uint32_t it, RowWords<IW>& rw) {
     const uint32_t c = it < items ? it : items - 1;    // past the last item: reload it
     const Where w = where(c);
-    load_words<D, IW>(a, w.z, w.bh, w.t, el.lp, rw);
+    load_words_strided<D, IW>(a, w.z, w.bh, w.t, lp, rw);
   };
 
   // one input buffer: it is converted to doubles before the next item's
@@ -521,11 +736,24 @@ __global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
     const Where w = where(item);
     item += nwave;
     fetch(item, rw);
+    // the row norm and the lookup scale first: their latency overlaps the FWHT
+    const double n = sqrt(group_sum_f64<P>(ss));
+    const double rns = n > 0.0 ? double(kCodeLutScale) / n : 0.0;
+    fwht_strided<P>(u, xb, wb, rb);
     const bool valid = w.t < a.n_new;
-    if (w.z == 0)
-      encode_row<D, BK, QJL, 0, IW, LK>(a, w.bh, w.t, valid, el, u, ss, lut[0]);
-    else
-      encode_row<D, BV, false, 1, IW, LV>(a, w.bh, w.t, valid, el, u, ss, lut[LK ? 1 : 0]);
+    uint32_t code[32];
+    // with lookups for both tensors the codes are found before the branch,
+    // in the same block as the FWHT, whose work then hides the LDS latency
+    if constexpr (LK && LV) lookup_codes(u, rns, lut[w.z], code);
+    if (w.z == 0) {
+      if constexpr (LK && !LV) lookup_codes(u, rns, lut[0], code);
+      if constexpr (!LK) direct_codes<BK, 0>(a, u, n, code);
+      store_encoded_row<D, BK, QJL, 0, IW>(a, w.bh, w.t, valid, el, u, n, code);
+    } else {
+      if constexpr (LV && !LK) lookup_codes(u, rns, lut[0], code);
+      if constexpr (!LV) direct_codes<BV, 1>(a, u, n, code);
+      store_encoded_row<D, BV, false, 1, IW>(a, w.bh, w.t, valid, el, u, n, code);
+    }
     if (item >= items) break;
   }
 }

@@ -56,16 +56,62 @@ def test_host_sphere_codebook_matches_oracle(bits, d):
         tq.tq_codebook_ex(bits, "sphere", 64)
 
 
-@pytest.mark.parametrize("kind,d", [("gauss", 128), ("sphere", 128), ("sphere", 256)])
-def test_4bit_thresholds_fit_the_encode_lookup(kind, d):
-    """The encode finds 4-bit codes through buckets of width 1/32 in
-    z = |u| / n over [0, 8): each bucket may hold at most one positive
-    threshold, and all of them lie below 8."""
-    _, t = tq.tq_codebook_ex(4, kind, d)
-    pos = np.asarray(t[len(t) // 2 + 1:])           # the 7 positive thresholds
-    assert len(pos) == 7 and (pos > 0).all() and (pos < 8).all()
-    buckets = np.floor(pos * 32).astype(int)
-    assert len(set(buckets.tolist())) == len(buckets)
+LOOKUP_CASES = [(bits, kind, d) for bits in (3, 4)
+                for kind, d in (("gauss", 128), ("gauss", 256), ("sphere", 128), ("sphere", 256))]
+
+
+@pytest.mark.parametrize("bits,kind,d", LOOKUP_CASES)
+def test_thresholds_fit_the_encode_lookup(bits, kind, d):
+    """The bulk encode finds 3- and 4-bit codes through buckets of width
+    1/4 in z = u / n over [-4, 4), the end buckets open: each bucket may hold
+    at most one threshold strictly inside it, so consecutive thresholds must
+    be more than 1/4 apart, and none may lie in an end bucket."""
+    _, t = tq.tq_codebook_ex(bits, kind, d)
+    t = np.asarray(t)
+    assert len(t) == (1 << bits) - 1 and t[len(t) // 2] == 0.0
+    assert (np.diff(t) > 1 / 4).all()
+    np.testing.assert_array_equal(t, -t[::-1])      # antisymmetric
+    assert np.abs(t).max() < 3.75                    # inside the inner buckets
+
+
+def _lookup_codes(t, bits, z):
+    """The encode's lookup rule, restated: bucket b of 4 z + OFF, clamped
+    to [0, 2 OFF), entry 4 t + OFF of the threshold inside it (2^60 if
+    none) with its low bits replaced by the count of thresholds at or below
+    the bucket's edge."""
+    off, scale = 16, 4
+    nb = 2 * off
+    ent = np.empty(nb, dtype=np.uint64)
+    for b in range(nb):
+        lo, hi = (b - off) / scale, (b + 1 - off) / scale
+        c0 = int((t <= lo).sum())
+        inside = t[(t > lo) & (t < hi)]
+        assert len(inside) <= 1
+        tb = scale * inside[0] + off if len(inside) else 2.0 ** 60
+        raw = np.array([tb]).view(np.uint64)[0]
+        ent[b] = (raw & ~np.uint64((1 << bits) - 1)) | np.uint64(c0)
+    zz = scale * z + off
+    idx = np.clip(np.trunc(zz).astype(np.int64), 0, nb - 1)
+    e = ent[idx]
+    low = (e & np.uint64((1 << bits) - 1)).astype(np.int64) + (zz >= e.view(np.float64))
+    return low & ((1 << bits) - 1), low >> bits
+
+
+@pytest.mark.parametrize("bits,kind,d", LOOKUP_CASES)
+def test_encode_lookup_rule_counts_thresholds(bits, kind, d):
+    """The lookup gives #{k : z >= t_k} over the whole range |z| <= sqrt(d)
+    (beyond the table's [-4, 4) through its clamped end buckets), away from
+    the thresholds, and never carries into the bits above the code."""
+    _, t = tq.tq_codebook_ex(bits, kind, d)
+    t = np.asarray(t)
+    rng = np.random.default_rng(bits * 1000 + d)
+    z = np.concatenate([rng.uniform(-np.sqrt(d), np.sqrt(d), 20000),
+                        rng.standard_normal(20000), t - 1e-7, t + 1e-7, [0.0, -1e-9],
+                        np.arange(-20, 21) / 4, [np.sqrt(d), -np.sqrt(d)]])
+    got, carry = _lookup_codes(t, bits, z)
+    want = (z[:, None] >= t[None, :]).sum(1)
+    np.testing.assert_array_equal(got, want)
+    assert not carry.any()
 
 
 @pytest.mark.parametrize("seed,d", [(0, 128), (1, 256), (12345, 128)])

@@ -57,6 +57,12 @@ SMALL = {
     "d128_k3qjl_v3_g4": dict(B=2, Hq=8, Hkv=2, N=700, bits_k=3, bits_v=3, qjl=True,
                              structure="correlated", wid=117),
     "d256_k2v3_g4": dict(B=1, Hq=4, Hkv=1, d=256, N=900, bits_k=2, bits_v=3, wid=118),
+    # the bulk encode's strided loads at d = 256: 16-byte segments of fp32
+    # inputs and 8-byte segments of fp16 ones, ragged against 8-row items
+    "d256_k4v4_f32in_g2": dict(B=1, Hq=4, Hkv=2, d=256, N=333, bits_k=4, bits_v=4,
+                               in_dtype="f32", wid=131),
+    "d256_k3v3_f16in": dict(B=2, Hq=2, Hkv=1, d=256, N=257, bits_k=3, bits_v=3,
+                            in_dtype="f16", wid=132),
 }
 
 
