@@ -627,9 +627,39 @@ __device__ __forceinline__ void encode_append_row(const EncodeArgs& e, int bh, i
     encode_row<D, BV, false, 1, IW>(e, bh, 0, true, el, u, ss);
 }
 
+// Fills the code lookup tables (above) of the 3- and 4-bit tensors among K
+// (BK bits) and V (BV bits), in that order, with threads tid = 0, nthr, ...
+template <int BK, int BV>
+__device__ __forceinline__ void fill_code_luts(const EncodeArgs& a, double (*lut)[kCodeLutBuckets],
+                                               int tid, int nthr) {
+  constexpr bool LK = BK == 3 || BK == 4, LV = BV == 3 || BV == 4;
+  constexpr int OFF = kCodeLutOff, NB = kCodeLutBuckets;
+  for (int i = tid; i < ((LK ? 1 : 0) + (LV ? 1 : 0)) * NB; i += nthr) {
+    const int tab = i / NB, bkt = i % NB;
+    const int ts = LK && tab == 0 ? 0 : 1;
+    const int bits = ts == 0 ? BK : BV;
+    const double lo = double(bkt - OFF) / kCodeLutScale, hi = double(bkt + 1 - OFF) / kCodeLutScale;
+    uint32_t c0 = 0;
+    double tb = 0x1p60;
+    // the L - 1 thresholds: 0 and +-t_{L/2+j}
+    for (int j = -1; j < (1 << (bits - 1)) - 1; ++j) {
+      for (int sgn = 0; sgn < (j < 0 ? 1 : 2); ++sgn) {
+        const double tj = j < 0 ? 0.0 : (sgn ? -a.tpos[ts][j] : a.tpos[ts][j]);
+        if (tj <= lo) ++c0;
+        else if (tj < hi) tb = kCodeLutScale * tj + OFF;
+      }
+    }
+    const uint64_t mask = (uint64_t(1) << bits) - 1;
+    lut[tab][bkt] =
+        __longlong_as_double(int64_t((uint64_t(__double_as_longlong(tb)) & ~mask) | c0));
+  }
+}
+
 // Encodes rows [t0, t0 + n) of the appended tokens in `e`, K and V, for row
 // bh: work items of 64/P rows (one wave each, as in k_encode) taken in turn
-// by the nwaves waves of the workgroup.
+// by the nwaves waves of the workgroup, in the contiguous layout (DPP
+// cross-lane stages, codes by comparison: with few items per wave, a code
+// table's fill, barrier and LDS latency would cost more than they save).
 template <int D, int BK, int BV, int DT>
 __device__ __forceinline__ void encode_chunk_rows(const EncodeArgs& e, int bh, int64_t t0,
                                                   int64_t n, int wave, int nwaves, int lane) {
@@ -677,30 +707,10 @@ __global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
 
   // code lookups of the 3- and 4-bit tensors (key, value), one per workgroup
   constexpr bool LK = BK == 3 || BK == 4, LV = BV == 3 || BV == 4;
-  constexpr int OFF = kCodeLutOff;
-  constexpr int NB = kCodeLutBuckets;
-  __shared__ double lut[(LK && LV) ? 2 : 1][NB];
+  __shared__ double lut[(LK && LV) ? 2 : 1][kCodeLutBuckets];
   __shared__ double2 xpose[WPB][XposeLayout<P>::cells];
   if constexpr (LK || LV) {
-    for (int i = threadIdx.x; i < ((LK ? 1 : 0) + (LV ? 1 : 0)) * NB; i += blockDim.x) {
-      const int tab = i / NB, bkt = i % NB;
-      const int ts = LK && tab == 0 ? 0 : 1;
-      const int bits = ts == 0 ? BK : BV;
-      const double lo = double(bkt - OFF) / kCodeLutScale, hi = double(bkt + 1 - OFF) / kCodeLutScale;
-      uint32_t c0 = 0;
-      double tb = 0x1p60;
-      // the L - 1 thresholds: 0 and +-t_{L/2+j}
-      for (int j = -1; j < (1 << (bits - 1)) - 1; ++j) {
-        for (int sgn = 0; sgn < (j < 0 ? 1 : 2); ++sgn) {
-          const double tj = j < 0 ? 0.0 : (sgn ? -a.tpos[ts][j] : a.tpos[ts][j]);
-          if (tj <= lo) ++c0;
-          else if (tj < hi) tb = kCodeLutScale * tj + OFF;
-        }
-      }
-      const uint64_t mask = (uint64_t(1) << bits) - 1;
-      lut[tab][bkt] = __longlong_as_double(
-          int64_t((uint64_t(__double_as_longlong(tb)) & ~mask) | c0));
-    }
+    fill_code_luts<BK, BV>(a, lut, threadIdx.x, blockDim.x);
     __syncthreads();
   }
   if (item >= items) return;
@@ -1762,8 +1772,10 @@ k_decode_mx(DecodeArgs a) {
   // by wave 0 before it requests any tile: a query load queued behind the
   // whole chip's first round of tile traffic would arrive only after it. The
   // other waves request their first tiles at once, so the stream starts
-  // while the query and the tables are set up (not with a fused append,
-  // whose row must be stored first).
+  // while the query and the tables are set up. With a fused append this
+  // needs the first tiles to hold old rows only: the appended rows are the
+  // last ones of their split, past position vlo - 1 (chunk) or at vlo - 1
+  // (single token), and the first tiles end before position (PF + 1) T.
   constexpr int QE = D / 16;                   // query elements per lane (16 lanes per head)
   if (tid < 16 * GK) {
     const int g = tid >> 4, l16 = tid & 15;
@@ -1818,7 +1830,7 @@ k_decode_mx(DecodeArgs a) {
   }
   constexpr int PF = mx_prefetch(D, BK, BV, QJL);
   const int64_t wb = t_begin + int64_t(wave) * TW;
-  const bool early = !a.append;
+  const bool early = !a.append || int64_t(PF + 1) * T < vlo;
   // PF + 1 tile buffers, all requested before the set-up; in the loop a
   // buffer is refilled right after it has been processed
   Tile ta, tb, tc;
