@@ -63,6 +63,9 @@ SMALL = {
                                in_dtype="f32", wid=131),
     "d256_k3v3_f16in": dict(B=2, Hq=2, Hkv=1, d=256, N=257, bits_k=3, bits_v=3,
                             in_dtype="f16", wid=132),
+    # longer contexts (also the fused appends with long splits, below)
+    "d128_k3v4_long": dict(B=1, Hq=8, Hkv=2, N=4000, bits_k=3, bits_v=4, wid=133),
+    "d256_k2v3_long": dict(B=1, Hq=4, Hkv=1, d=256, N=3500, bits_k=2, bits_v=3, wid=134),
 }
 
 
@@ -192,6 +195,55 @@ def test_append_attend_matches_encode_then_decode(name):
         err, _ = rel_err(got, want)
         log(f"  splits={splits}: fused step equals encode + decode; error vs oracle {err:.2e}")
         assert err <= TOL
+
+
+@pytest.mark.parametrize("name", ["d128_k3v4_long", "d256_k2v3_long"])
+def test_fused_appends_with_long_splits(name):
+    """With one or two splits of about 2000-4000 tokens, each split holds more
+    old tokens than its first tiles ((PF + 1) x 512 tokens), so the fused
+    single-token and chunk steps request those tiles before the set-up and
+    the encode, as the plain decode does. Both steps against encode + decode
+    (cache bytes equal; single token: output bit-identical; chunk: within the
+    tolerance) and against the oracle."""
+    import decode_attention_seeded_amd as tq
+    torch = torch_cuda()
+    w = si.small_workload(**SMALL[name])
+    log(f"case {name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} N={w.N} K{w.bits_k}/V{w.bits_v}")
+    qraw, qf = si.queries(w)
+    q = to_device(qraw, w.in_dtype)
+    ref = oracle_encode(w)
+    want = o.attend(qf.astype(np.float64), ref, w.N, d=w.d, seed=w.seed, bits_k=w.bits_k,
+                    bits_v=w.bits_v, Hkv=w.Hkv)
+    for n_new in (1, 300):
+        n0 = w.N - n_new
+        rk, rv, _, _ = kv_host(w, n0, w.N)
+        kc, vc = to_device(rk, w.in_dtype), to_device(rv, w.in_dtype)
+        for splits in (1, 2):
+            cfg, two = gpu_encode(w, chunks=[(0, n0)], capacity=w.N)
+            _, one = gpu_encode(w, chunks=[(0, n0)], capacity=w.N)
+            tq.tq_encode_kv(cfg, kc, vc, n0, two)
+            ref_out = gpu_decode(w, cfg, two, q, w.N, splits=splits)
+            out = torch.full((w.B, w.Hq, w.d), float("nan"), dtype=torch.float32, device="cuda")
+            ws = tq.workspace(tq.tq_workspace_bytes(cfg, w.B, w.Hq, w.Hkv, w.N, splits))
+            if n_new == 1:
+                tq.tq_append_attend_decode(cfg, kc, vc, q, one, w.N, out, ws, splits=splits)
+            else:
+                tq.tq_append_chunk_attend_decode(cfg, kc, vc, q, one, w.N, out, ws,
+                                                 splits=splits)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy().astype(np.float64)
+            for plane in ("kc", "vc", "kn", "vn"):
+                assert torch.equal(getattr(one, plane).view(torch.uint8),
+                                   getattr(two, plane).view(torch.uint8)), plane
+            err, _ = rel_err(got, want)
+            diff, _ = rel_err(got, ref_out)
+            log(f"  n_new={n_new} splits={splits}: error vs oracle {err:.2e}, "
+                f"vs the two calls {diff:.2e}")
+            assert err <= TOL
+            if n_new == 1:
+                assert np.array_equal(got, ref_out)
+            else:
+                assert diff <= TOL
 
 
 @pytest.mark.parametrize("splits,scale", [(1, 0.0), (3, 0.0), (1, 0.35), (2, 0.35)])
