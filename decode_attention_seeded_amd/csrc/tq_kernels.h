@@ -513,7 +513,8 @@ template <int D, int BITS, bool QJL, int TS, int IW>
 __device__ __forceinline__ void store_encoded_row(const EncodeArgs& a, int bh, int64_t t,
                                                   bool valid, const EncodeLane<IW>& el,
                                                   const double (&u)[32], double n,
-                                                  const uint32_t (&code)[32]) {
+                                                  const uint32_t (&code)[32],
+                                                  const double* cen = nullptr) {
   constexpr int P = D / 32;
   constexpr int E = 32;
   constexpr int L = 1 << BITS;
@@ -548,10 +549,16 @@ __device__ __forceinline__ void store_encoded_row(const EncodeArgs& a, int bh, i
     double rr = 0.0;
 #pragma unroll
     for (int i = 0; i < E; ++i) {
+      // the key centroid of the code: from the LDS copy cen when given,
+      // else through a select chain over the kernel arguments
       const uint32_t ck = code[i] & uint32_t(L - 1);
       double ci = 0.0;
+      if (cen) {
+        ci = cen[ck];
+      } else {
 #pragma unroll
-      for (int k = 0; k < L; ++k) ci = (ck == uint32_t(k)) ? a.cen_k[k] : ci;
+        for (int k = 0; k < L; ++k) ci = (ck == uint32_t(k)) ? a.cen_k[k] : ci;
+      }
       const double ri = (u[i] - nstored * ci) * inv_sqrt_d;
       rr += ri * ri;
       r[i] = (el.qmask >> i & 1) ? -ri : ri;
@@ -709,10 +716,13 @@ __global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
   constexpr bool LK = BK == 3 || BK == 4, LV = BV == 3 || BV == 4;
   __shared__ double lut[(LK && LV) ? 2 : 1][kCodeLutBuckets];
   __shared__ double2 xpose[WPB][XposeLayout<P>::cells];
-  if constexpr (LK || LV) {
-    fill_code_luts<BK, BV>(a, lut, threadIdx.x, blockDim.x);
-    __syncthreads();
+  // QJL: the key centroids for the residual, one LDS read per coordinate
+  __shared__ double cen[QJL ? 16 : 1];
+  if constexpr (LK || LV) fill_code_luts<BK, BV>(a, lut, threadIdx.x, blockDim.x);
+  if constexpr (QJL) {
+    if (threadIdx.x < 16) cen[threadIdx.x] = a.cen_k[threadIdx.x];
   }
+  if constexpr (LK || LV || QJL) __syncthreads();
   if (item >= items) return;
 
   const int lp = lane & (P - 1), rl = lane / P;
@@ -758,7 +768,8 @@ __global__ void __launch_bounds__(256) k_encode(EncodeArgs a) {
     if (w.z == 0) {
       if constexpr (LK && !LV) lookup_codes(u, rns, lut[0], code);
       if constexpr (!LK) direct_codes<BK, 0>(a, u, n, code);
-      store_encoded_row<D, BK, QJL, 0, IW>(a, w.bh, w.t, valid, el, u, n, code);
+      store_encoded_row<D, BK, QJL, 0, IW>(a, w.bh, w.t, valid, el, u, n, code,
+                                           QJL ? cen : nullptr);
     } else {
       if constexpr (LV && !LK) lookup_codes(u, rns, lut[0], code);
       if constexpr (!LV) direct_codes<BV, 1>(a, u, n, code);
