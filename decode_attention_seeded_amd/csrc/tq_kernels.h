@@ -449,6 +449,7 @@ __device__ __forceinline__ void fwht_strided(double (&v)[32], char* xb, int wb, 
 // replaced bits move the threshold by less than 2^-46 in z, and the rounding
 // of S z + OFF is below 2^-50, both far inside the decision band. The 32
 // entries of a table lie in distinct LDS banks, so its reads never conflict.
+
 // Packs the low BITS bits of each of 32 codes LSB-first into BITS dwords
 // with one funnel shift per code (two for a code that straddles dwords):
 // bits above BITS in a code are ignored.
