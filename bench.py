@@ -530,10 +530,20 @@ def main():
         tq.tq_encode_kv(cfg, k1, v1, w.N - 1, cache)
         tq.tq_attend_decode(cfg, q, cache, w.N, out, ws)
 
+    def fused():
+        tq.tq_append_attend_decode(cfg, k1, v1, q, cache, w.N, out, ws)
+
+    # four interleaved rounds of 100 calls each, the median round of each
+    # (one round each was at the mercy of the clocks after the cold-cache
+    # measurements above)
+    rounds = {"two": [], "fused": []}
+    for _ in range(4):
+        rounds["two"].append(timed(torch, two_calls, 100, warm=10))
+        rounds["fused"].append(timed(torch, fused, 100, warm=10))
     single = {
-        "two_calls_us": round(timed(torch, two_calls, 50), 2),
-        "fused_us": round(timed(torch, lambda: tq.tq_append_attend_decode(
-            cfg, k1, v1, q, cache, w.N, out, ws), 50), 2),
+        "two_calls_us": round(float(np.median(rounds["two"])), 2),
+        "fused_us": round(float(np.median(rounds["fused"])), 2),
+        "measured": "median of 4 interleaved rounds of 100 back-to-back calls",
     }
     log(f"single-token step: encode + decode {single['two_calls_us']} us, "
         f"fused {single['fused_us']} us")
